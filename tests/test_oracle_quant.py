@@ -1,0 +1,86 @@
+"""Pins of the oracle's quantisers: the OCP e4m3 bit layout, round-to-nearest-
+even with saturation, torch's CPU float8 cast on in-range values, and the
+int4 group quantiser's grid and error bound."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant as Q
+
+
+def test_e4m3_decode_spec_values():
+    dec = Q.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert dec[0x7E] == 448.0 and dec[0xFE] == -448.0
+    assert dec[0x08] == 2.0 ** -6            # smallest normal
+    assert dec[0x01] == 2.0 ** -9            # smallest subnormal
+    assert dec[0x07] == 7 * 2.0 ** -9        # largest subnormal
+    assert dec[0x38] == 1.0                  # exponent field 7 = bias
+    assert dec[0x3C] == 1.5
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    assert np.sum(np.isnan(dec)) == 2
+    assert dec[0x00] == 0.0 and dec[0x80] == 0.0
+    finite = dec[~np.isnan(dec)]
+    assert np.all(np.isfinite(finite))
+    pos = Q.e4m3_all_values()
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_e4m3_roundtrip_all_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
+    assert np.array_equal(Q.e4m3_encode(Q.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    pos = Q.e4m3_all_values()
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = Q.e4m3_encode(mids).astype(int)
+    lo = np.arange(len(mids))
+    expect = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(enc, expect)
+    assert Q.e4m3_encode(np.array([1e9]))[0] == 0x7E
+    assert Q.e4m3_encode(np.array([-500.0]))[0] == 0xFE
+    assert Q.e4m3_encode(np.array([np.nan]))[0] == 0x7F
+    assert Q.e4m3_encode(np.array([2.0 ** -11]))[0] == 0x00   # below half the smallest subnormal -> 0
+    assert Q.e4m3_encode(np.array([3 * 2.0 ** -11]))[0] == 0x01
+
+
+def test_e4m3_vs_torch_cast():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 1.0, 30.0, 120.0)]).astype(np.float32)
+    x = x[np.abs(x) <= 448.0]
+    ours = Q.e4m3_decode(Q.e4m3_encode(x))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_fp8_tensor_quantiser():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 48)) * 0.02).astype(np.float32)
+    codes, scale, deq = Q.quantise_fp8_tensor(w)
+    assert scale == np.float32(np.max(np.abs(w)) / np.float32(448.0))
+    assert np.max(np.abs(Q.e4m3_decode(codes))) == 448.0       # the amax element maps to the top code
+    rel = np.abs(deq - w) / np.maximum(np.abs(w), 2.0 ** -6 * scale)
+    assert np.max(rel) <= 2.0 ** -4 + 1e-12                     # half an ulp of a 3-bit mantissa
+    z, s0, d0 = Q.quantise_fp8_tensor(np.zeros((4, 4), np.float32))
+    assert s0 == 1.0 and np.all(d0 == 0)
+
+
+def test_w4_quantiser():
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((256, 40)) * 0.02).astype(np.float32)
+    q, s, deq = Q.quantise_w4(w, 128)
+    assert q.dtype == np.int8 and q.min() >= -8 and q.max() <= 7
+    assert s.shape == (2, 40) and s.dtype == np.float16
+    s32 = np.repeat(s.astype(np.float64), 128, axis=0)
+    # rounding error at most half a step; amax/7 rounded to fp16 keeps the clip error below that too
+    assert np.all(np.abs(deq - w) <= s32 / 2 + 1e-12)
+    # values already on the grid round-trip exactly
+    grid = (q.astype(np.float32) * np.repeat(s.astype(np.float32), 128, axis=0)).astype(np.float32)
+    q2, s2, deq2 = Q.quantise_w4(grid, 128)
+    assert np.array_equal(deq2, grid.astype(np.float64))
+    # each group's largest magnitude maps to +-7 (or -8 is never needed for symmetric amax)
+    assert np.all(np.max(np.abs(q.reshape(2, 128, 40)), axis=1) == 7)
+    # an all-zero group gets scale 1 and codes 0
+    w[:128, 3] = 0
+    q3, s3, d3 = Q.quantise_w4(w, 128)
+    assert s3[0, 3] == 1.0 and np.all(q3[:128, 3] == 0)
