@@ -1,0 +1,179 @@
+/*
+ * vfm.h -- C ABI of the MI355X (gfx950) flow-matching action-expert library.
+ *
+ * The library runs the denoise loop of a pi0.5-style action expert: N explicit
+ * Euler steps of a flow-matching velocity field, each step one pass of a small
+ * transformer over the action-chunk tokens that attend to a cached
+ * vision+language prefix KV. The PhyAI summary ("Real-Time Physical AI at the
+ * Edge, Scalable Rollouts in the Cloud", optimisation and profiling paragraphs)
+ * names this ten-step Euler loop of the action expert as the part of pi0.5
+ * whose latency is dominated by many small kernel launches; the FlashRT
+ * walk-through (component 7, graph capture; the exec/ execution contract)
+ * describes the shape of this interface: named device buffers are the only
+ * state, the hot path takes device pointers only, and a replay is launched
+ * on a stream.
+ *
+ * Conventions (all entry points):
+ *  - Every function returns vfm_status; no C++ exception crosses the ABI.
+ *    On failure vfm_last_error() returns a thread-local message.
+ *  - Argument, shape, dtype and bound-state checks run on the host before
+ *    anything is enqueued, so those errors never touch the device.
+ *  - Device pointers are plain HIP device addresses (for instance the
+ *    data_ptr() of a torch tensor on a ROCm device); streams are hipStream_t
+ *    passed as void* (NULL = the default stream).
+ *  - The caller owns every pointer it passes in. Weights are copied and
+ *    repacked at create time, so the caller may free its weight tensors after
+ *    vfm_expert_create returns. Bound buffers must stay alive until they are
+ *    rebound or the expert is destroyed.
+ *  - One expert must not be used from two host threads at once.
+ *  - Device faults surface as VFM_E_HIP at the call that observes them.
+ */
+#ifndef VFM_H_
+#define VFM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VFM_ABI_VERSION 1
+
+typedef struct vfm_expert vfm_expert;   /* opaque; owned by the library */
+
+typedef enum {
+  VFM_OK = 0,
+  VFM_E_INVALID_ARG = 1,   /* NULL where a value is required, bad config field, unknown name */
+  VFM_E_SHAPE = 2,         /* a shape does not match the config / bound buffers */
+  VFM_E_DTYPE = 3,         /* wrong element type for a weight or buffer */
+  VFM_E_UNBOUND = 4,       /* denoise needs a buffer that was never bound */
+  VFM_E_STATE = 5,         /* call not valid in the expert's current state */
+  VFM_E_UNSUPPORTED = 6,   /* valid request this build does not implement */
+  VFM_E_OOM = 7,           /* device allocation failed */
+  VFM_E_HIP = 8            /* a HIP runtime call or a kernel failed */
+} vfm_status;
+
+typedef enum { VFM_F32 = 0, VFM_BF16 = 1, VFM_F16 = 2, VFM_FP8_E4M3 = 3, VFM_I4X2 = 4 } vfm_dtype;
+
+/* Storage precision of the per-layer GEMM weights (q/k/v/o/gate/up/down). */
+typedef enum { VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3 } vfm_wprec;
+
+typedef struct {
+  int32_t abi_version;      /* must equal VFM_ABI_VERSION */
+  int32_t num_layers;       /* L >= 0 */
+  int32_t width;            /* W, multiple of 64 */
+  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads */
+  int32_t num_kv_heads;     /* Hkv >= 1 */
+  int32_t head_dim;         /* d, multiple of 16, <= 256 */
+  int32_t mlp_dim;          /* F, multiple of 64 */
+  int32_t action_horizon;   /* H, 1..64 action tokens per sample */
+  int32_t action_dim;       /* A, 1..64 */
+  int32_t state_dim;        /* S >= 0 (0: no state input) */
+  int32_t time_emb_dim;     /* E, even, >= 4 */
+  int32_t max_prefix_len;   /* upper bound of P over all binds */
+  int32_t max_batch;        /* upper bound of B over all binds */
+  int32_t num_steps;        /* N >= 1 Euler steps, t from 1 to 0 */
+  float rope_base;          /* rotary base, > 0 */
+  float rms_eps;            /* RMSNorm epsilon, > 0 */
+  int32_t weight_precision; /* vfm_wprec */
+  int32_t act_dtype;        /* VFM_F32 (with VFM_W_FP32) or VFM_BF16 (all others) */
+  int32_t w4_group_size;    /* 128 for VFM_W_W4A16, ignored otherwise */
+} vfm_config;
+
+/* A named weight handed to vfm_expert_create. Matrices are row-major
+ * [in][out] (y = x @ W). dtype is the master type: VFM_F32 when
+ * weight_precision is VFM_W_FP32, VFM_BF16 otherwise. */
+typedef struct {
+  const char* name;
+  const void* dev_ptr;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+} vfm_tensor;
+
+/* Returns VFM_ABI_VERSION. */
+int vfm_abi_version(void);
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* vfm_last_error(void);
+
+/* Create an expert from a config and its named weights.
+ * Names: time_mlp_in.{w,b} [E][W],[W]; time_mlp_out.{w,b} [W][W],[W];
+ * in_proj.{w,b} [A][W],[W]; state_proj.{w,b} [S][W],[W] (S > 0 only);
+ * layers.{l}.attn_norm.mod.{w,b} and layers.{l}.mlp_norm.mod.{w,b} [W][3W],[3W]
+ * (columns [scale | shift | gate]); layers.{l}.{q,k,v}.w [W][H*d] (head-major
+ * columns); layers.{l}.o.w [Hq*d][W]; layers.{l}.{gate,up}.w [W][F];
+ * layers.{l}.down.w [F][W]; final_norm.mod.{w,b}; out_proj.{w,b} [W][A],[A].
+ * Synchronous on `stream`: copies, repacks and (for FP8 / W4A16) quantises the
+ * weights on the device and precomputes the time-conditioning table for the
+ * N fixed times t_k = (N-k)/N. All workspace for max_batch / max_prefix_len
+ * is allocated here; denoise never allocates.
+ * Errors: VFM_E_INVALID_ARG (config field out of range, missing or unknown
+ * name), VFM_E_SHAPE, VFM_E_DTYPE, VFM_E_OOM, VFM_E_HIP. On error *out is NULL. */
+vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, int32_t n_weights,
+                             void* stream, vfm_expert** out);
+
+/* Bind a named device buffer. Names and layouts:
+ *   "prefix_k", "prefix_v": [L][B][P][Hkv][d], act_dtype, the cached prefix
+ *      keys (already position-encoded) and values of every layer;
+ *   "noise":   [B][H][A] f32, the sample at t = 1;
+ *   "state":   [B][S] f32 (S > 0 only);
+ *   "actions": [B][H][A] f32, receives the sample at t = 0.
+ * B (1..max_batch) and P (1..max_prefix_len) are taken from the prefix_k
+ * shape; every other buffer must agree. Pointers must be 16-byte aligned.
+ * Host-only validation; nothing is enqueued. Errors: VFM_E_INVALID_ARG,
+ * VFM_E_SHAPE, VFM_E_DTYPE. */
+vfm_status vfm_bind(vfm_expert* ex, const char* name, void* dev_ptr, int32_t dtype, int32_t ndim,
+                    const int64_t* shape);
+
+/* Run the N-step denoise loop on `stream` (asynchronous). noise / state /
+ * actions may be NULL to use the bound buffers; non-NULL pointers replace
+ * the bound ones for this call and must have the bound shapes. actions may
+ * alias noise. Errors: VFM_E_UNBOUND (prefix or a needed buffer not bound),
+ * VFM_E_STATE, VFM_E_HIP (launch failure or a fault seen from an earlier
+ * call). */
+vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, float* actions,
+                       void* stream);
+
+/* Options (string key/value), host-only:
+ *   "launch_mode": "persistent" (default: one cooperative launch per
+ *       denoise with device-wide phase barriers), "graph" (one kernel per
+ *       phase, captured once into a hipGraph and replayed) or "eager" (one
+ *       kernel per phase, launched directly).
+ * Errors: VFM_E_INVALID_ARG for an unknown key or value. */
+vfm_status vfm_set_option(vfm_expert* ex, const char* key, const char* value);
+
+/* FP8 experts: measure the activation amax of every FP8 GEMM input over one
+ * bf16 pass on the bound buffers and set act_scale = amax / 448 per input.
+ * Synchronous on `stream`. VFM_E_STATE on a non-FP8 expert. */
+vfm_status vfm_calibrate(vfm_expert* ex, void* stream);
+
+/* Test hook: set the n = 4 * L FP8 activation scales directly (order per
+ * layer: qkv input, o input, gate/up input, down input). VFM_E_STATE on a
+ * non-FP8 expert, VFM_E_SHAPE if n != 4 * L. */
+vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
+
+/* Copy a tensor the library holds, as float32, to host memory `dst`
+ * (`bytes` must equal 4 * element count):
+ *   a per-layer GEMM weight by its create-time name (e.g. "layers.3.q.w"):
+ *      the value the kernels multiply by, i.e. dequantised for FP8 / W4A16,
+ *      row-major [in][out];
+ *   "mod_table": [N][2L+1][3][W], (scale, shift, gate) of every norm at
+ *      every step (norm order attn_0, mlp_0, ..., final).
+ * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE. */
+vfm_status vfm_export(vfm_expert* ex, const char* name, void* dst, size_t bytes);
+
+/* Wait for `stream` and report any device-side failure of earlier denoise
+ * calls (a launch error, or a phase barrier that timed out and stopped the
+ * persistent kernel early): VFM_E_HIP with a message. */
+vfm_status vfm_check(vfm_expert* ex, void* stream);
+
+/* Synchronise the expert's work and free everything it owns. NULL-safe. */
+vfm_status vfm_expert_destroy(vfm_expert* ex);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VFM_H_ */

@@ -1,0 +1,121 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every entry
+point the header declares, and rejects bad arguments on the host before
+touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from synth import CONFIGS
+from vla_flow_matching_pi0_amd import vfm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "vfm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vfm_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vfm.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(declared) == sorted(vfm.EXPORTS)
+
+
+def test_abi_version(lib):
+    assert lib.vfm_abi_version() == vfm.ABI_VERSION == 1
+
+
+def _create(lib, cfg, weights=None):
+    out = ctypes.c_void_p()
+    if weights is None:
+        arr, n = None, 0
+    else:
+        arr = (vfm.VfmTensor * len(weights))(*weights)
+        n = len(weights)
+    st = lib.vfm_expert_create(ctypes.byref(cfg) if cfg is not None else None, arr, n, None, ctypes.byref(out))
+    return st, out
+
+
+def test_create_rejects_bad_configs(lib):
+    st, out = _create(lib, None)
+    assert vfm.STATUS[st] == "VFM_E_INVALID_ARG" and not out.value
+    good = vfm.make_config(CONFIGS["tiny_fp32"])
+    for field, value in [("abi_version", 7), ("width", 200), ("head_dim", 48), ("num_q_heads", 3),
+                         ("action_horizon", 65), ("num_steps", 0), ("mlp_dim", 100), ("time_emb_dim", 5),
+                         ("max_batch", 0), ("act_dtype", vfm.VFM_BF16), ("weight_precision", 9)]:
+        c = vfm.make_config(CONFIGS["tiny_fp32"])
+        setattr(c, field, value)
+        st, out = _create(lib, c)
+        assert vfm.STATUS[st] == "VFM_E_INVALID_ARG", (field, vfm.STATUS[st])
+        assert lib.vfm_last_error().decode()
+        assert not out.value
+    c = vfm.make_config(CONFIGS["tiny_fp32"])
+    c.rope_base = -1.0
+    assert vfm.STATUS[_create(lib, c)[0]] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[_create(lib, good)[0]] == "VFM_E_INVALID_ARG"      # no weights
+
+
+def _fake_weights(cfg, drop=None, extra=None, bad_shape=None, bad_dtype=None):
+    from synth import param_specs
+    ws = []
+    keep = []
+    for name, shape in param_specs(cfg):
+        if name == drop:
+            continue
+        t = vfm.VfmTensor()
+        b = name.encode()
+        keep.append(b)
+        t.name = b
+        t.dev_ptr = 0x1000        # never dereferenced: validation fails first
+        t.dtype = bad_dtype if name == bad_shape and bad_dtype is not None else (vfm.VFM_F32 if cfg.master_dtype == "f32" else vfm.VFM_BF16)
+        shp = list(shape)
+        if name == bad_shape and bad_dtype is None:
+            shp[0] += 1
+        t.ndim = len(shp)
+        for i, s in enumerate(shp):
+            t.shape[i] = s
+        ws.append(t)
+    if extra:
+        t = vfm.VfmTensor()
+        b = extra.encode()
+        keep.append(b)
+        t.name, t.dev_ptr, t.dtype, t.ndim = b, 0x1000, 0, 1
+        t.shape[0] = 4
+        ws.append(t)
+    return ws, keep
+
+
+def test_create_rejects_bad_weights(lib):
+    cfg = CONFIGS["tiny_fp32"]
+    c = vfm.make_config(cfg)
+    ws, keep = _fake_weights(cfg, drop="layers.1.up.w")
+    st, _ = _create(lib, c, ws)
+    assert vfm.STATUS[st] == "VFM_E_INVALID_ARG" and "layers.1.up.w" in lib.vfm_last_error().decode()
+    ws, keep = _fake_weights(cfg, extra="layers.9.q.w")
+    assert vfm.STATUS[_create(lib, c, ws)[0]] == "VFM_E_INVALID_ARG"
+    ws, keep = _fake_weights(cfg, bad_shape="layers.0.o.w")
+    assert vfm.STATUS[_create(lib, c, ws)[0]] == "VFM_E_SHAPE"
+    ws, keep = _fake_weights(cfg, bad_shape="in_proj.b", bad_dtype=vfm.VFM_BF16)
+    assert vfm.STATUS[_create(lib, c, ws)[0]] == "VFM_E_DTYPE"
+
+
+def test_null_expert_calls(lib):
+    shape = (ctypes.c_int64 * 1)(4)
+    assert vfm.STATUS[lib.vfm_bind(None, b"noise", 0x1000, 0, 1, shape)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_denoise(None, None, None, None, None)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_set_option(None, b"launch_mode", b"graph")] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_calibrate(None, None)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_export(None, b"mod_table", None, 0)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_check(None, None)] == "VFM_E_INVALID_ARG"
+    assert lib.vfm_expert_destroy(None) == 0

@@ -1,0 +1,152 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle on
+the same seeded inputs. Tolerances are relative L2 on the final actions:
+1e-4 for the fp32 expert, 2e-2 for bf16."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import denoise as O
+from synth import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["persistent", "graph", "eager"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from vla_flow_matching_pi0_amd import vfm
+    vfm.load_library()
+
+
+def _gu():
+    import gpu_util
+    return gpu_util
+
+
+_CACHE = {}
+
+
+def pi05_case():
+    """Inputs and oracle actions of the pi0.5 bf16 batch-1 workload (computed once)."""
+    if "pi05" not in _CACHE:
+        cfg = CONFIGS["pi05_bf16_b1"]
+        params, pk, pv, noise, state = make_inputs(cfg)
+        ref = O.denoise(params, noise, state, pk, pv, cfg)
+        _CACHE["pi05"] = (cfg, params, pk, pv, noise, state, ref)
+    return _CACHE["pi05"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_fp32_matches_oracle(mode):
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    print(f"case tiny_fp32 mode={mode}", flush=True)
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    err = gu.rel_l2(got, ref)
+    disp = gu.rel_l2(got - noise, ref - noise)
+    print(f"tiny rel_l2={err:.3e} displacement rel_l2={disp:.3e}")
+    assert err <= 1e-4
+    assert disp <= 1e-3
+
+
+@pytest.mark.parametrize("mode", ["persistent", "graph"])
+def test_pi05_bf16_b1_matches_oracle(mode):
+    gu = _gu()
+    cfg, params, pk, pv, noise, state, ref = pi05_case()
+    print(f"case pi05_bf16_b1 mode={mode}", flush=True)
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode, repeats=2)
+    err = gu.rel_l2(got, ref)
+    disp = gu.rel_l2(got - noise, ref - noise)
+    print(f"pi05 rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("cfgname", ["tiny_fp32", "pi05_bf16_b1"])
+def test_zero_out_projection_keeps_noise_bitwise(cfgname):
+    gu = _gu()
+    cfg = CONFIGS[cfgname]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    params["out_proj.w"] = np.zeros_like(params["out_proj.w"])
+    params["out_proj.b"] = np.zeros_like(params["out_proj.b"])
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+    assert np.array_equal(got, noise)
+
+
+def test_constant_velocity_closed_form():
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    vel = np.linspace(-1.5, 2.0, cfg.action_dim).astype(np.float32)
+    params["out_proj.w"] = np.zeros_like(params["out_proj.w"])
+    params["out_proj.b"] = vel
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+    np.testing.assert_allclose(got, noise.astype(np.float64) - vel, atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("layers,steps", [(0, 1), (0, 3), (1, 1), (1, 2)])
+def test_small_depths(layers, steps):
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"].replace(num_layers=layers, num_steps=steps)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    assert gu.rel_l2(got, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("batch,prefix,horizon", [(3, 37, 8), (2, 5, 13), (1, 130, 50)])
+def test_ragged_shapes(batch, prefix, horizon):
+    """Batch > 1, prefix lengths that are not a multiple of 32, horizons that
+    are not a multiple of 16 (fp32 expert with a state input)."""
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"].replace(batch=batch, prefix_len=prefix, action_horizon=horizon, state_dim=5)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    for mode in ("persistent", "eager"):
+        got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
+        ref = O.denoise(params, noise, state, pk, pv, cfg)
+        assert gu.rel_l2(got, ref) <= 1e-4, mode
+
+
+def test_modulation_table_matches_oracle():
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ex = gu.build_expert(cfg, params)
+    tab = ex.export("mod_table", (cfg.num_steps, 2 * cfg.num_layers + 1, 3, cfg.width))
+    ex.close()
+    ref = O.modulation_table(params, cfg)
+    np.testing.assert_allclose(tab, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("cfgname", ["tiny_fp32", "pi05_bf16_b1"])
+def test_packed_weights_round_trip(cfgname):
+    gu = _gu()
+    cfg = CONFIGS[cfgname].replace(num_layers=1)
+    params, *_ = make_inputs(cfg)
+    ex = gu.build_expert(cfg, params)
+    for n in ("q", "k", "v", "o", "gate", "up", "down"):
+        name = f"layers.0.{n}.w"
+        got = ex.export(name, params[name].shape)
+        assert np.array_equal(got, params[name]), name
+    ex.close()
+
+
+def test_pi05_bf16_b32_sampled():
+    """Batch 32, one prefix per sample; checked on three samples (samples
+    never interact, so the oracle runs them alone)."""
+    gu = _gu()
+    cfg = CONFIGS["pi05_bf16_b32"]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    print("case pi05_bf16_b32", flush=True)
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+    c1 = cfg.replace(batch=1)
+    for b in (0, 31):
+        ref = O.denoise(params, noise[b:b + 1], state[b:b + 1], pk[:, b:b + 1], pv[:, b:b + 1], c1)
+        err = gu.rel_l2(got[b:b + 1], ref)
+        print(f"b32 sample {b}: rel_l2={err:.3e}")
+        assert err <= 2e-2

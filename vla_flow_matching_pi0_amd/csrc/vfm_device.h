@@ -1,0 +1,163 @@
+// vfm_device.h -- device-side building blocks shared by every kernel of the
+// action-expert denoise loop: vector types, the MFMA operand traits, coherent
+// (device-scope) memory helpers and the grid barrier.
+//
+// Memory model used across workgroups inside one launch (measured on MI355X):
+// the per-XCD L2 caches are not coherent with each other for ordinary
+// stores, so every value one workgroup produces for another is written with
+// device-scope (sc1) stores, which write through to the coherence point, and
+// read with device-scope (sc1) loads. A phase boundary is then a wait for the
+// wave's own outstanding memory operations plus a counter barrier made of
+// relaxed device-scope atomics; no L2 writeback/invalidate is needed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vfm {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ MFMA traits
+// Every operand fetch is 16 bytes per lane. For a 16-column tile, lane l
+// (column / row l % 16, group g = l / 16) holds E consecutive k values
+// k = kb * KB + E * g + e; the same mapping is used for both operands, so the
+// hardware's pairing of operand slots always multiplies matching k.
+// The 16x16 output tile: lane l holds rows 4 * g + r (r = 0..3) of column l % 16.
+template <typename T> struct MT;
+template <> struct MT<float> {
+  static constexpr int E = 4;    // elements per 16-byte lane fetch
+  static constexpr int KB = 16;  // k values per 16-byte block (4 MFMAs of K = 4)
+  static __device__ __forceinline__ floatx4 mma(u32x4 a, u32x4 b, floatx4 c) {
+    // whole-vector bit casts: casting single components of an ext_vector is
+    // miscompiled (every component reads as component 0)
+    const floatx4 af = __builtin_bit_cast(floatx4, a), bf = __builtin_bit_cast(floatx4, b);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], bf[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], bf[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], c, 0, 0, 0);
+    return c;
+  }
+};
+template <> struct MT<bf16> {
+  static constexpr int E = 8;
+  static constexpr int KB = 32;  // one 16x16x32 MFMA per block
+  static __device__ __forceinline__ floatx4 mma(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------------ conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// pack two values of T into the low bytes of a word (bf16: one u32; f32: u32x2)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// ------------------------------------------------------------------ coherent memory
+// Buffer-resource based loads/stores with the device-scope (sc1) cache policy.
+// Offsets are bytes from `base` and must stay below 2 GiB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ u32x4 coh_ld16(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ u32x2 coh_ld8(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ uint32_t coh_ld4(const void* base, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void coh_st16(void* base, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void coh_st8(void* base, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rsrc(base), off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void coh_st4(void* base, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, rsrc(base), off, 0, CPOL_SC1);
+}
+// read-only data (weights, prefix KV, tables): ordinary cached loads
+__device__ __forceinline__ u32x4 ro_ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ floatx4 as_f4(u32x4 v) { return __builtin_bit_cast(floatx4, v); }
+__device__ __forceinline__ u32x4 as_u4(floatx4 v) { return __builtin_bit_cast(u32x4, v); }
+
+// ------------------------------------------------------------------ math
+// exp2 via the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// GELU, tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3);
+// tanh(z) = 1 - 2 / (exp(2z) + 1), with exp(2z) = exp2(2 z log2(e)).
+__device__ __forceinline__ float gelu_tanh(float u) {
+  const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
+  const float e = fast_exp2(2.8853900817779268f * z);
+  const float th = 1.0f - 2.0f / (e + 1.0f);
+  return 0.5f * u * (1.0f + th);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Sum over a 256-thread block; `red` is >= 4 floats of LDS.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = warp_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// ------------------------------------------------------------------ grid barrier
+// Layout of the barrier words (uint32): [0] global count of finished groups,
+// [1] error flag, [64 + 64 * g] arrival count of group g (g = block % 8).
+// Counts are monotonic within one launch (zeroed before it). Spins are
+// bounded; on timeout the error flag is raised and every block returns.
+constexpr long BARRIER_SPIN_LIMIT = 1L << 22;
+
+__device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch) {
+  __shared__ unsigned s_ok;
+  ++epoch;
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores (and loads) have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned G = gridDim.x;
+    const unsigned ngroups = G < 8 ? G : 8;
+    const unsigned grp = blockIdx.x % 8;
+    const unsigned gsize = (G - grp + 7) / 8;
+    unsigned ok = 1;
+    const unsigned old = __hip_atomic_fetch_add(&bar[64 + 64 * grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == epoch * gsize) __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    long spins = 0;
+    while (ld_agent(&bar[0]) < epoch * ngroups) {
+      ++spins;
+      if (((spins & 1023) == 0 && ld_agent(&bar[1]) != 0u) || spins > BARRIER_SPIN_LIMIT) {
+        __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+}  // namespace vfm

@@ -1,0 +1,732 @@
+// vfm_runtime.cpp -- host runtime behind the C ABI in include/vfm.h:
+// config and weight validation, create-time packing, the named-buffer
+// registry, launch modes (persistent / graph / eager) and error reporting.
+//
+// Named device buffers as the only state and replay of a captured launch
+// sequence keyed by its shape follow the FlashRT walk-through (exec/: Buffer
+// and Graph objects; component 7, graph capture with pointer-only inputs).
+#include "vfm.h"
+#include "vfm_params.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+using vfm::VP;
+
+namespace {
+
+thread_local std::string g_err;
+
+vfm_status fail(vfm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIPCHK(call)                                                                          \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess) return fail(VFM_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+struct BoundBuf {
+  void* ptr = nullptr;
+  int dtype = -1;
+  int ndim = 0;
+  int64_t shape[5] = {0, 0, 0, 0, 0};
+  bool bound = false;
+};
+
+// Column map of one fused, packed weight: packed column -> (source, column).
+struct ColMap {
+  std::vector<int> src, idx;
+};
+
+}  // namespace
+
+struct vfm_expert {
+  vfm_config cfg{};
+  int act_bf16 = 0;       // activations / packed weights are bf16 (else f32)
+  int src_bf16 = 0;       // master weights are bf16 (else f32)
+  int L = 0, W = 0, Hq = 0, Hkv = 0, d = 0, F = 0, H = 0, A = 0, S = 0, E = 0, N = 0;
+  int maxB = 0, maxP = 0, KSmax = 0;
+  std::vector<void*> allocs;
+  std::vector<uint8_t*> w_qkv, w_o, w_gu, w_down;
+  ColMap map_qkv, map_o, map_gu, map_down;
+  float *in_w = nullptr, *in_b = nullptr, *st_w = nullptr, *st_b = nullptr, *out_w = nullptr, *out_b = nullptr;
+  float* mod = nullptr;
+  float* rope = nullptr;
+  int rope_P = -1;
+  float* s = nullptr;
+  float* h = nullptr;
+  void *xn = nullptr, *q = nullptr, *ks = nullptr, *vs = nullptr, *attn = nullptr, *act = nullptr;
+  float *opart = nullptr, *ml = nullptr;
+  unsigned* bar = nullptr;
+  unsigned* host_flag = nullptr;   // pinned copy of the barrier error word
+  hipEvent_t flag_event = nullptr;
+  bool flag_pending = false;
+  BoundBuf prefix_k, prefix_v, noise, state, actions;
+  int mode = 0;                    // 0 persistent, 1 graph, 2 eager
+  size_t lds = 0;
+  int coop_grid = 0;
+  // graph cache (one entry): key = shape + pointers
+  hipGraphExec_t gexec = nullptr;
+  std::vector<uintptr_t> gkey;
+  hipStream_t cap_stream = nullptr;
+
+  void* dalloc(size_t bytes) {
+    void* p = nullptr;
+    if (bytes == 0) bytes = 16;
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    allocs.push_back(p);
+    return p;
+  }
+};
+
+namespace {
+
+int elem_bytes(int dt) { return dt == VFM_F32 ? 4 : dt == VFM_BF16 || dt == VFM_F16 ? 2 : 1; }
+
+vfm_status validate_config(const vfm_config* c) {
+  if (!c) return fail(VFM_E_INVALID_ARG, "config is NULL");
+  if (c->abi_version != VFM_ABI_VERSION)
+    return fail(VFM_E_INVALID_ARG, "abi_version %d != %d", c->abi_version, VFM_ABI_VERSION);
+  if (c->num_layers < 0 || c->num_layers > vfm::MAX_LAYERS)
+    return fail(VFM_E_INVALID_ARG, "num_layers %d outside [0, %d]", c->num_layers, vfm::MAX_LAYERS);
+  if (c->width < 256 || c->width % 256 != 0 || c->width > 4096)
+    return fail(VFM_E_INVALID_ARG, "width %d must be a multiple of 256 in [256, 4096]", c->width);
+  if (c->num_kv_heads < 1 || c->num_q_heads < 1 || c->num_q_heads % c->num_kv_heads != 0)
+    return fail(VFM_E_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d", c->num_q_heads,
+                c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(VFM_E_INVALID_ARG, "head_dim %d must be 64, 128 or 256", c->head_dim);
+  if ((c->num_q_heads * c->head_dim) % 256 != 0)
+    return fail(VFM_E_INVALID_ARG, "num_q_heads * head_dim must be a multiple of 256");
+  if (c->mlp_dim < 256 || c->mlp_dim % 256 != 0 || c->mlp_dim > 65536)
+    return fail(VFM_E_INVALID_ARG, "mlp_dim %d must be a multiple of 256 in [256, 65536]", c->mlp_dim);
+  if (c->action_horizon < 1 || c->action_horizon > 64)
+    return fail(VFM_E_INVALID_ARG, "action_horizon %d outside [1, 64]", c->action_horizon);
+  if (c->action_dim < 1 || c->action_dim > 64 || 256 % c->action_dim != 0)
+    return fail(VFM_E_INVALID_ARG, "action_dim %d must divide 256", c->action_dim);
+  if (c->state_dim < 0 || c->state_dim > 4096) return fail(VFM_E_INVALID_ARG, "state_dim %d out of range", c->state_dim);
+  if (c->time_emb_dim < 4 || c->time_emb_dim % 2 != 0 || c->time_emb_dim > 8192)
+    return fail(VFM_E_INVALID_ARG, "time_emb_dim %d must be even in [4, 8192]", c->time_emb_dim);
+  if (c->max_prefix_len < 1 || c->max_prefix_len > 65536)
+    return fail(VFM_E_INVALID_ARG, "max_prefix_len %d outside [1, 65536]", c->max_prefix_len);
+  if (c->max_batch < 1 || c->max_batch > 1024) return fail(VFM_E_INVALID_ARG, "max_batch %d outside [1, 1024]", c->max_batch);
+  if (c->num_steps < 1 || c->num_steps > 1000) return fail(VFM_E_INVALID_ARG, "num_steps %d outside [1, 1000]", c->num_steps);
+  if (!(c->rope_base > 0.f)) return fail(VFM_E_INVALID_ARG, "rope_base must be > 0");
+  if (!(c->rms_eps > 0.f)) return fail(VFM_E_INVALID_ARG, "rms_eps must be > 0");
+  if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W4A16)
+    return fail(VFM_E_INVALID_ARG, "weight_precision %d unknown", c->weight_precision);
+  if (c->weight_precision == VFM_W_FP32 && c->act_dtype != VFM_F32)
+    return fail(VFM_E_INVALID_ARG, "fp32 weights need act_dtype VFM_F32");
+  if (c->weight_precision != VFM_W_FP32 && c->act_dtype != VFM_BF16)
+    return fail(VFM_E_INVALID_ARG, "16-bit and quantised weights need act_dtype VFM_BF16");
+  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16)
+    return fail(VFM_E_UNSUPPORTED, "weight precision %d is not built into this library yet", c->weight_precision);
+  return VFM_OK;
+}
+
+struct WeightSpec {
+  std::string name;
+  std::vector<int64_t> shape;
+};
+
+std::vector<WeightSpec> weight_specs(const vfm_expert& x) {
+  std::vector<WeightSpec> v;
+  const int64_t W = x.W, E = x.E, A = x.A, S = x.S, F = x.F, qd = (int64_t)x.Hq * x.d, kd = (int64_t)x.Hkv * x.d;
+  v.push_back({"time_mlp_in.w", {E, W}});
+  v.push_back({"time_mlp_in.b", {W}});
+  v.push_back({"time_mlp_out.w", {W, W}});
+  v.push_back({"time_mlp_out.b", {W}});
+  v.push_back({"in_proj.w", {A, W}});
+  v.push_back({"in_proj.b", {W}});
+  if (S > 0) {
+    v.push_back({"state_proj.w", {S, W}});
+    v.push_back({"state_proj.b", {W}});
+  }
+  for (int l = 0; l < x.L; ++l) {
+    const std::string p = "layers." + std::to_string(l) + ".";
+    v.push_back({p + "attn_norm.mod.w", {W, 3 * W}});
+    v.push_back({p + "attn_norm.mod.b", {3 * W}});
+    v.push_back({p + "q.w", {W, qd}});
+    v.push_back({p + "k.w", {W, kd}});
+    v.push_back({p + "v.w", {W, kd}});
+    v.push_back({p + "o.w", {qd, W}});
+    v.push_back({p + "mlp_norm.mod.w", {W, 3 * W}});
+    v.push_back({p + "mlp_norm.mod.b", {3 * W}});
+    v.push_back({p + "gate.w", {W, F}});
+    v.push_back({p + "up.w", {W, F}});
+    v.push_back({p + "down.w", {F, W}});
+  }
+  v.push_back({"final_norm.mod.w", {W, 3 * W}});
+  v.push_back({"final_norm.mod.b", {3 * W}});
+  v.push_back({"out_proj.w", {W, A}});
+  v.push_back({"out_proj.b", {A}});
+  return v;
+}
+
+// Packed column orders (see the GEMM epilogues in vfm_kernels.hip).
+ColMap qkv_map(int Hq, int Hkv, int d) {
+  ColMap m;
+  const int heads = Hq + 2 * Hkv, hd = d / 2;
+  for (int head = 0; head < heads; ++head) {
+    const int sid = head < Hq ? 0 : head < Hq + Hkv ? 1 : 2;
+    const int base = (head < Hq ? head : head < Hq + Hkv ? head - Hq : head - Hq - Hkv) * d;
+    for (int tt = 0; tt < d / 16; ++tt)
+      for (int g = 0; g < 4; ++g)
+        for (int r = 0; r < 4; ++r) {
+          int col;
+          if (sid < 2) col = tt * 8 + 2 * g + (r & 1) + (r >> 1) * hd;   // rotary pairs in one lane
+          else col = tt * 16 + 4 * g + r;
+          m.src.push_back(sid);
+          m.idx.push_back(base + col);
+        }
+  }
+  return m;
+}
+ColMap gu_map(int F) {
+  ColMap m;
+  for (int t = 0; t < F / 8; ++t)
+    for (int g = 0; g < 4; ++g)
+      for (int r = 0; r < 4; ++r) {
+        m.src.push_back(r & 1);              // gate, up, gate, up
+        m.idx.push_back(t * 8 + 2 * g + (r >> 1));
+      }
+  return m;
+}
+ColMap ident_map(int N) {
+  ColMap m;
+  for (int c = 0; c < N; ++c) {
+    m.src.push_back(0);
+    m.idx.push_back(c);
+  }
+  return m;
+}
+
+void free_all(vfm_expert* x) {
+  if (x->gexec) (void)hipGraphExecDestroy(x->gexec);
+  if (x->cap_stream) (void)hipStreamDestroy(x->cap_stream);
+  if (x->flag_event) (void)hipEventDestroy(x->flag_event);
+  if (x->host_flag) (void)hipHostFree(x->host_flag);
+  for (void* p : x->allocs) (void)hipFree(p);
+  x->allocs.clear();
+}
+
+vfm_status check_prev_flag(vfm_expert* x, bool wait) {
+  if (!x->flag_pending) return VFM_OK;
+  if (wait) {
+    HIPCHK(hipEventSynchronize(x->flag_event));
+  } else if (hipEventQuery(x->flag_event) != hipSuccess) {
+    return VFM_OK;
+  }
+  x->flag_pending = false;
+  if (*x->host_flag != 0u) {
+    *x->host_flag = 0u;
+    return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
+  }
+  return VFM_OK;
+}
+
+vfm_status check_buf(const char* name, const BoundBuf& b, int dtype, std::initializer_list<int64_t> shape) {
+  if (!b.bound) return fail(VFM_E_UNBOUND, "buffer '%s' is not bound", name);
+  if (b.dtype != dtype) return fail(VFM_E_DTYPE, "buffer '%s' has dtype %d, expected %d", name, b.dtype, dtype);
+  if (b.ndim != (int)shape.size()) return fail(VFM_E_SHAPE, "buffer '%s' has %d dims, expected %d", name, b.ndim, (int)shape.size());
+  int i = 0;
+  for (int64_t s : shape) {
+    if (b.shape[i] != s)
+      return fail(VFM_E_SHAPE, "buffer '%s' dim %d is %lld, expected %lld", name, i, (long long)b.shape[i], (long long)s);
+    ++i;
+  }
+  return VFM_OK;
+}
+
+int phase_grid(const VP& p, int phase) {
+  auto cdiv = [](long a, long b) { return (int)((a + b - 1) / b); };
+  const int mt = cdiv(p.M, 64);
+  long units = 1;
+  switch (phase) {
+    case vfm::PH_INIT: units = cdiv(std::max(p.B * p.H * p.A, p.B * p.W), 256); break;
+    case vfm::PH_IN_PROJ: units = cdiv((long)p.M * p.W / 4, 256); break;
+    case vfm::PH_NORM_ATTN:
+    case vfm::PH_NORM_MLP:
+    case vfm::PH_FINAL: units = p.M; break;
+    case vfm::PH_QKV: units = (long)(p.Hq + 2 * p.Hkv) * p.d / 64 * mt; break;
+    case vfm::PH_ATTN: units = (long)p.B * p.Hq * p.KS; break;
+    case vfm::PH_COMBINE: units = cdiv((long)p.M * p.Hq * p.d / 4, 256); break;
+    case vfm::PH_O:
+    case vfm::PH_DOWN: units = (long)p.W / 64 * mt; break;
+    case vfm::PH_GU: units = (long)2 * p.F / 64 * mt; break;
+  }
+  if (units < 1) units = 1;
+  if (units > 4096) units = 4096;
+  return (int)units;
+}
+
+hipError_t enqueue_phases(vfm_expert* x, const VP& p, hipStream_t st) {
+  hipError_t e;
+  auto run = [&](int ph, int k, int l) { return vfm::launch_phase(p, x->act_bf16, 1, ph, k, l, phase_grid(p, ph), x->lds, st); };
+  if ((e = run(vfm::PH_INIT, 0, 0)) != hipSuccess) return e;
+  for (int k = 0; k < p.N; ++k) {
+    if ((e = run(vfm::PH_IN_PROJ, k, 0)) != hipSuccess) return e;
+    for (int l = 0; l < p.L; ++l) {
+      const int seq[] = {vfm::PH_NORM_ATTN, vfm::PH_QKV, vfm::PH_ATTN, vfm::PH_COMBINE,
+                         vfm::PH_O, vfm::PH_NORM_MLP, vfm::PH_GU, vfm::PH_DOWN};
+      for (int ph : seq)
+        if ((e = run(ph, k, l)) != hipSuccess) return e;
+    }
+    if ((e = run(vfm::PH_FINAL, k, 0)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vfm_abi_version(void) { return VFM_ABI_VERSION; }
+
+const char* vfm_last_error(void) { return g_err.c_str(); }
+
+vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, int32_t n_weights, void* stream,
+                             vfm_expert** out) {
+  if (!out) return fail(VFM_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  vfm_status st = validate_config(cfg);
+  if (st != VFM_OK) return st;
+  if (!weights || n_weights <= 0) return fail(VFM_E_INVALID_ARG, "no weights given");
+
+  vfm_expert tmp;
+  tmp.cfg = *cfg;
+  tmp.act_bf16 = cfg->act_dtype == VFM_BF16;
+  tmp.src_bf16 = cfg->weight_precision != VFM_W_FP32;
+  tmp.L = cfg->num_layers; tmp.W = cfg->width; tmp.Hq = cfg->num_q_heads; tmp.Hkv = cfg->num_kv_heads;
+  tmp.d = cfg->head_dim; tmp.F = cfg->mlp_dim; tmp.H = cfg->action_horizon; tmp.A = cfg->action_dim;
+  tmp.S = cfg->state_dim; tmp.E = cfg->time_emb_dim; tmp.N = cfg->num_steps;
+  tmp.maxB = cfg->max_batch; tmp.maxP = cfg->max_prefix_len;
+
+  // ---- weights: every expected name exactly once, right dtype and shape, nothing else
+  const int master_dt = tmp.src_bf16 ? VFM_BF16 : VFM_F32;
+  std::map<std::string, const vfm_tensor*> byname;
+  for (int i = 0; i < n_weights; ++i) {
+    const vfm_tensor& t = weights[i];
+    if (!t.name) return fail(VFM_E_INVALID_ARG, "weight %d has no name", i);
+    if (byname.count(t.name)) return fail(VFM_E_INVALID_ARG, "weight '%s' given twice", t.name);
+    byname[t.name] = &t;
+  }
+  const std::vector<WeightSpec> specs = weight_specs(tmp);
+  std::map<std::string, const void*> ptr;
+  for (const WeightSpec& sp : specs) {
+    auto it = byname.find(sp.name);
+    if (it == byname.end()) return fail(VFM_E_INVALID_ARG, "weight '%s' is missing", sp.name.c_str());
+    const vfm_tensor& t = *it->second;
+    if (!t.dev_ptr) return fail(VFM_E_INVALID_ARG, "weight '%s' has a NULL pointer", sp.name.c_str());
+    if (t.dtype != master_dt) return fail(VFM_E_DTYPE, "weight '%s' has dtype %d, expected %d", sp.name.c_str(), t.dtype, master_dt);
+    if (t.ndim != (int)sp.shape.size()) return fail(VFM_E_SHAPE, "weight '%s' has %d dims, expected %d", sp.name.c_str(), t.ndim, (int)sp.shape.size());
+    for (size_t j = 0; j < sp.shape.size(); ++j)
+      if (t.shape[j] != sp.shape[j])
+        return fail(VFM_E_SHAPE, "weight '%s' dim %zu is %lld, expected %lld", sp.name.c_str(), j, (long long)t.shape[j], (long long)sp.shape[j]);
+    ptr[sp.name] = t.dev_ptr;
+  }
+  if (byname.size() != specs.size()) {
+    for (auto& kv : byname) {
+      bool known = false;
+      for (const WeightSpec& sp : specs) known |= sp.name == kv.first;
+      if (!known) return fail(VFM_E_INVALID_ARG, "unknown weight name '%s'", kv.first.c_str());
+    }
+  }
+
+  // ---- device work
+  vfm_expert* x = new vfm_expert(tmp);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto bail = [&](vfm_status code) { free_all(x); delete x; return code; };
+  const int ab = x->act_bf16 ? 2 : 4;
+  const int L = x->L, W = x->W, Hq = x->Hq, Hkv = x->Hkv, d = x->d, F = x->F, H = x->H, A = x->A, S = x->S;
+  const int n_norms = 2 * L + 1;
+  const int nqkv = (Hq + 2 * Hkv) * d;
+
+  x->map_qkv = qkv_map(Hq, Hkv, d);
+  x->map_o = ident_map(W);
+  x->map_gu = gu_map(F);
+  x->map_down = ident_map(W);
+
+  // upload column maps
+  auto upload_map = [&](const ColMap& m, int** dsrc, int** didx) -> bool {
+    *dsrc = (int*)x->dalloc(m.src.size() * 4);
+    *didx = (int*)x->dalloc(m.idx.size() * 4);
+    if (!*dsrc || !*didx) return false;
+    return hipMemcpy(*dsrc, m.src.data(), m.src.size() * 4, hipMemcpyHostToDevice) == hipSuccess &&
+           hipMemcpy(*didx, m.idx.data(), m.idx.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
+  };
+  int *qs, *qi, *os, *oi, *gs, *gi, *ds, *di;
+  if (!upload_map(x->map_qkv, &qs, &qi) || !upload_map(x->map_o, &os, &oi) || !upload_map(x->map_gu, &gs, &gi) ||
+      !upload_map(x->map_down, &ds, &di)) {
+    fail(VFM_E_OOM, "column map upload failed");
+    return bail(VFM_E_OOM);
+  }
+  for (int l = 0; l < L; ++l) {
+    const std::string p = "layers." + std::to_string(l) + ".";
+    uint8_t* wq = (uint8_t*)x->dalloc((size_t)W * nqkv * ab);
+    uint8_t* wo = (uint8_t*)x->dalloc((size_t)Hq * d * W * ab);
+    uint8_t* wg = (uint8_t*)x->dalloc((size_t)W * 2 * F * ab);
+    uint8_t* wd = (uint8_t*)x->dalloc((size_t)F * W * ab);
+    if (!wq || !wo || !wg || !wd) { fail(VFM_E_OOM, "weight allocation failed"); return bail(VFM_E_OOM); }
+    hipError_t e;
+    if ((e = vfm::pack_weight(wq, W, nqkv, qs, qi, ptr[p + "q.w"], Hq * d, ptr[p + "k.w"], Hkv * d, ptr[p + "v.w"], Hkv * d,
+                              x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+        (e = vfm::pack_weight(wo, Hq * d, W, os, oi, ptr[p + "o.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+        (e = vfm::pack_weight(wg, W, 2 * F, gs, gi, ptr[p + "gate.w"], F, ptr[p + "up.w"], F, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+        (e = vfm::pack_weight(wd, F, W, ds, di, ptr[p + "down.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess) {
+      fail(VFM_E_HIP, "weight packing failed: %s", hipGetErrorString(e));
+      return bail(VFM_E_HIP);
+    }
+    x->w_qkv.push_back(wq); x->w_o.push_back(wo); x->w_gu.push_back(wg); x->w_down.push_back(wd);
+  }
+  // small f32 weights
+  struct Cv { float** dst; const char* name; size_t n; };
+  std::vector<Cv> cvs = {{&x->in_w, "in_proj.w", (size_t)A * W}, {&x->in_b, "in_proj.b", (size_t)W},
+                         {&x->out_w, "out_proj.w", (size_t)W * A}, {&x->out_b, "out_proj.b", (size_t)A}};
+  if (S > 0) {
+    cvs.push_back({&x->st_w, "state_proj.w", (size_t)S * W});
+    cvs.push_back({&x->st_b, "state_proj.b", (size_t)W});
+  }
+  for (const Cv& c : cvs) {
+    *c.dst = (float*)x->dalloc(c.n * 4);
+    if (!*c.dst) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
+    hipError_t e = vfm::to_f32(*c.dst, ptr[c.name], c.n, x->src_bf16, s);
+    if (e != hipSuccess) { fail(VFM_E_HIP, "convert %s: %s", c.name, hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
+  // modulation table
+  x->mod = (float*)x->dalloc((size_t)x->N * n_norms * 3 * W * 4);
+  double* scratch = (double*)x->dalloc(((size_t)x->N * x->E + 2 * (size_t)x->N * W) * 8);
+  if (!x->mod || !scratch) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
+  {
+    std::vector<const void*> mw, mb;
+    for (int l = 0; l < L; ++l) {
+      const std::string p = "layers." + std::to_string(l) + ".";
+      mw.push_back(ptr[p + "attn_norm.mod.w"]); mb.push_back(ptr[p + "attn_norm.mod.b"]);
+      mw.push_back(ptr[p + "mlp_norm.mod.w"]); mb.push_back(ptr[p + "mlp_norm.mod.b"]);
+    }
+    mw.push_back(ptr["final_norm.mod.w"]); mb.push_back(ptr["final_norm.mod.b"]);
+    hipError_t e = vfm::build_mod_table(x->mod, mw.data(), mb.data(), n_norms, ptr["time_mlp_in.w"], ptr["time_mlp_in.b"],
+                                        ptr["time_mlp_out.w"], ptr["time_mlp_out.b"], x->N, x->E, W, x->src_bf16, scratch, s);
+    if (e != hipSuccess) { fail(VFM_E_HIP, "modulation table: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
+  // workspace for max_batch / max_prefix_len
+  const size_t Mmax = (size_t)x->maxB * H;
+  x->KSmax = (x->maxP + H + 63) / 64;
+  x->rope = (float*)x->dalloc((size_t)H * d * 4);
+  x->s = (float*)x->dalloc((size_t)x->maxB * W * 4);
+  x->h = (float*)x->dalloc(Mmax * W * 4);
+  x->xn = x->dalloc(Mmax * W * ab);
+  x->q = x->dalloc((size_t)x->maxB * Hq * H * d * ab);
+  x->ks = x->dalloc((size_t)x->maxB * Hkv * H * d * ab);
+  x->vs = x->dalloc((size_t)x->maxB * Hkv * H * d * ab);
+  x->opart = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * d * 4);
+  x->ml = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * 2 * 4);
+  x->attn = x->dalloc(Mmax * Hq * d * ab);
+  x->act = x->dalloc(Mmax * F * ab);
+  x->bar = (unsigned*)x->dalloc(1024 * 4);
+  if (!x->rope || !x->s || !x->h || !x->xn || !x->q || !x->ks || !x->vs || !x->opart || !x->ml || !x->attn || !x->act || !x->bar) {
+    fail(VFM_E_OOM, "workspace allocation failed");
+    return bail(VFM_E_OOM);
+  }
+  if (hipHostMalloc((void**)&x->host_flag, 4) != hipSuccess) { fail(VFM_E_OOM, "pinned allocation failed"); return bail(VFM_E_OOM); }
+  *x->host_flag = 0u;
+  if (hipEventCreateWithFlags(&x->flag_event, hipEventDisableTiming) != hipSuccess) { fail(VFM_E_HIP, "event"); return bail(VFM_E_HIP); }
+  {
+    VP shape{};
+    shape.d = d;
+    shape.W = W;
+    x->lds = vfm::lds_bytes(shape, ab);
+    hipError_t e = vfm::prepare_kernels(x->act_bf16, d, (int)x->lds);
+    if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
+  if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) {
+    fail(VFM_E_HIP, "create-time device work failed");
+    return bail(VFM_E_HIP);
+  }
+  *out = x;
+  return VFM_OK;
+}
+
+vfm_status vfm_bind(vfm_expert* x, const char* name, void* dev_ptr, int32_t dtype, int32_t ndim, const int64_t* shape) {
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  if (!name) return fail(VFM_E_INVALID_ARG, "name is NULL");
+  if (ndim < 1 || ndim > 5 || !shape) return fail(VFM_E_SHAPE, "buffer '%s': bad ndim %d", name, ndim);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) numel *= shape[i];
+  // an empty buffer (a zero-layer expert's prefix) may have a NULL pointer
+  if (!dev_ptr && numel != 0) return fail(VFM_E_INVALID_ARG, "buffer '%s': NULL pointer", name);
+  if (reinterpret_cast<uintptr_t>(dev_ptr) % 16 != 0) return fail(VFM_E_INVALID_ARG, "buffer '%s': pointer not 16-byte aligned", name);
+  BoundBuf* b = nullptr;
+  const std::string n = name;
+  if (n == "prefix_k") b = &x->prefix_k;
+  else if (n == "prefix_v") b = &x->prefix_v;
+  else if (n == "noise") b = &x->noise;
+  else if (n == "state") b = &x->state;
+  else if (n == "actions") b = &x->actions;
+  else return fail(VFM_E_INVALID_ARG, "unknown buffer name '%s'", name);
+  const int act_dt = x->act_bf16 ? VFM_BF16 : VFM_F32;
+  if (b == &x->prefix_k || b == &x->prefix_v) {
+    if (dtype != act_dt) return fail(VFM_E_DTYPE, "buffer '%s' must have dtype %d", name, act_dt);
+    if (ndim != 5) return fail(VFM_E_SHAPE, "buffer '%s' must be [L][B][P][Hkv][d]", name);
+    if (shape[0] != x->L || shape[3] != x->Hkv || shape[4] != x->d)
+      return fail(VFM_E_SHAPE, "buffer '%s' must be [%d][B][P][%d][%d]", name, x->L, x->Hkv, x->d);
+    if (shape[1] < 1 || shape[1] > x->maxB) return fail(VFM_E_SHAPE, "buffer '%s': batch %lld outside [1, %d]", name, (long long)shape[1], x->maxB);
+    if (shape[2] < 1 || shape[2] > x->maxP) return fail(VFM_E_SHAPE, "buffer '%s': prefix %lld outside [1, %d]", name, (long long)shape[2], x->maxP);
+  } else {
+    if (dtype != VFM_F32) return fail(VFM_E_DTYPE, "buffer '%s' must be f32", name);
+    if (b == &x->state) {
+      if (x->S == 0) return fail(VFM_E_INVALID_ARG, "this expert has no state input");
+      if (ndim != 2 || shape[1] != x->S || shape[0] < 1 || shape[0] > x->maxB)
+        return fail(VFM_E_SHAPE, "buffer 'state' must be [B][%d]", x->S);
+    } else if (ndim != 3 || shape[1] != x->H || shape[2] != x->A || shape[0] < 1 || shape[0] > x->maxB) {
+      return fail(VFM_E_SHAPE, "buffer '%s' must be [B][%d][%d]", name, x->H, x->A);
+    }
+  }
+  b->ptr = dev_ptr;
+  b->dtype = dtype;
+  b->ndim = ndim;
+  for (int i = 0; i < 5; ++i) b->shape[i] = i < ndim ? shape[i] : 0;
+  b->bound = true;
+  return VFM_OK;
+}
+
+vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
+  if (!x || !key || !value) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  const std::string k = key, v = value;
+  if (k == "launch_mode") {
+    if (v == "persistent") x->mode = 0;
+    else if (v == "graph") x->mode = 1;
+    else if (v == "eager") x->mode = 2;
+    else return fail(VFM_E_INVALID_ARG, "launch_mode '%s' unknown", value);
+    return VFM_OK;
+  }
+  return fail(VFM_E_INVALID_ARG, "unknown option '%s'", key);
+}
+
+vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, float* actions, void* stream) {
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  vfm_status st = check_prev_flag(x, false);
+  if (st != VFM_OK) return st;
+  if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
+  const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
+  const int act_dt = x->act_bf16 ? VFM_BF16 : VFM_F32;
+  if ((st = check_buf("prefix_v", x->prefix_v, act_dt, {x->L, B, P, x->Hkv, x->d})) != VFM_OK) return st;
+  if (!noise) {
+    if ((st = check_buf("noise", x->noise, VFM_F32, {B, x->H, x->A})) != VFM_OK) return st;
+    noise = (const float*)x->noise.ptr;
+  }
+  if (!actions) {
+    if ((st = check_buf("actions", x->actions, VFM_F32, {B, x->H, x->A})) != VFM_OK) return st;
+    actions = (float*)x->actions.ptr;
+  }
+  if (x->S > 0 && !state) {
+    if ((st = check_buf("state", x->state, VFM_F32, {B, x->S})) != VFM_OK) return st;
+    state = (const float*)x->state.ptr;
+  }
+  if ((reinterpret_cast<uintptr_t>(noise) | reinterpret_cast<uintptr_t>(actions) | reinterpret_cast<uintptr_t>(state)) % 16)
+    return fail(VFM_E_INVALID_ARG, "noise / state / actions must be 16-byte aligned");
+
+  VP p{};
+  p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
+  p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
+  {
+    const int tot = P + x->H;
+    const int want = std::max(1, 256 / (B * x->Hq));
+    int kps = (tot + want - 1) / want;
+    kps = std::max(64, (kps + 31) / 32 * 32);
+    p.kps = kps;
+    p.KS = (tot + kps - 1) / kps;
+  }
+  p.eps = x->cfg.rms_eps;
+  for (int l = 0; l < x->L; ++l) {
+    p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
+  }
+  p.in_w = x->in_w; p.in_b = x->in_b; p.st_w = x->st_w; p.st_b = x->st_b; p.out_w = x->out_w; p.out_b = x->out_b;
+  p.mod = x->mod; p.rope = x->rope;
+  p.prefix_k = x->prefix_k.ptr; p.prefix_v = x->prefix_v.ptr;
+  p.noise = noise; p.state = state; p.x = actions;
+  p.s = x->s; p.h = x->h; p.xn = x->xn; p.q = x->q; p.ks = x->ks; p.vs = x->vs; p.opart = x->opart; p.ml = x->ml;
+  p.attn = x->attn; p.act = x->act; p.bar = x->bar;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (x->rope_P != P) {
+    HIPCHK(vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s));
+    x->rope_P = P;
+    if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
+  }
+  if (x->mode == 0) {
+    if (x->coop_grid == 0) {
+      HIPCHK(vfm::max_cooperative_grid(x->act_bf16, x->d, x->lds, &x->coop_grid));
+      if (x->coop_grid == 0) return fail(VFM_E_HIP, "persistent kernel does not fit on a compute unit");
+    }
+    HIPCHK(vfm::zero_words(x->bar, 1024, s));
+    HIPCHK(vfm::launch_phase(p, x->act_bf16, 0, 0, 0, 0, x->coop_grid, x->lds, s));
+    HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipEventRecord(x->flag_event, s));
+    x->flag_pending = true;
+    return VFM_OK;
+  }
+  if (x->mode == 2) {
+    HIPCHK(enqueue_phases(x, p, s));
+    return VFM_OK;
+  }
+  // graph mode
+  std::vector<uintptr_t> key = {(uintptr_t)B, (uintptr_t)P, (uintptr_t)noise, (uintptr_t)state, (uintptr_t)actions,
+                                (uintptr_t)p.prefix_k, (uintptr_t)p.prefix_v};
+  if (!x->gexec || key != x->gkey) {
+    if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
+    if (!x->cap_stream) HIPCHK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
+    hipGraph_t g = nullptr;
+    HIPCHK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipError_t e = enqueue_phases(x, p, x->cap_stream);
+    hipError_t e2 = hipStreamEndCapture(x->cap_stream, &g);
+    if (e != hipSuccess || e2 != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      return fail(VFM_E_HIP, "graph capture failed: %s", hipGetErrorString(e != hipSuccess ? e : e2));
+    }
+    e = hipGraphInstantiate(&x->gexec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) { x->gexec = nullptr; return fail(VFM_E_HIP, "graph instantiate: %s", hipGetErrorString(e)); }
+    x->gkey = key;
+  }
+  HIPCHK(hipGraphLaunch(x->gexec, s));
+  return VFM_OK;
+}
+
+vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
+  (void)stream;
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  if (x->cfg.weight_precision != VFM_W_FP8) return fail(VFM_E_STATE, "calibrate applies to FP8 experts only");
+  return fail(VFM_E_UNSUPPORTED, "FP8 is not built into this library yet");
+}
+
+vfm_status vfm_set_act_scales(vfm_expert* x, const float* scales, int32_t n) {
+  (void)scales;
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  if (x->cfg.weight_precision != VFM_W_FP8) return fail(VFM_E_STATE, "activation scales apply to FP8 experts only");
+  if (n != 4 * x->L) return fail(VFM_E_SHAPE, "expected %d scales", 4 * x->L);
+  return fail(VFM_E_UNSUPPORTED, "FP8 is not built into this library yet");
+}
+
+vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) {
+  if (!x || !name || !dst) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  const std::string n = name;
+  if (n == "mod_table") {
+    const size_t cnt = (size_t)x->N * (2 * x->L + 1) * 3 * x->W;
+    if (bytes != cnt * 4) return fail(VFM_E_SHAPE, "mod_table needs %zu bytes", cnt * 4);
+    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(hipMemcpy(dst, x->mod, bytes, hipMemcpyDeviceToHost));
+    return VFM_OK;
+  }
+  // workspace tensors as left by the last denoise call (diagnostics)
+  {
+    const int B = x->prefix_k.bound ? (int)x->prefix_k.shape[1] : x->maxB;
+    const size_t M = (size_t)B * x->H;
+    struct Ws { const char* name; const void* ptr; size_t count; bool act; };
+    const Ws ws[] = {{"ws.h", x->h, M * x->W, false},
+                     {"ws.xn", x->xn, M * x->W, true},
+                     {"ws.q", x->q, (size_t)B * x->Hq * x->H * x->d, true},
+                     {"ws.k", x->ks, (size_t)B * x->Hkv * x->H * x->d, true},
+                     {"ws.v", x->vs, (size_t)B * x->Hkv * x->H * x->d, true},
+                     {"ws.attn", x->attn, M * x->Hq * x->d, true},
+                     {"ws.act", x->act, M * x->F, true}};
+    for (const Ws& w : ws) {
+      if (n != w.name) continue;
+      if (bytes != w.count * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, w.count * 4);
+      HIPCHK(hipDeviceSynchronize());
+      float* out = static_cast<float*>(dst);
+      if (!w.act || !x->act_bf16) {
+        HIPCHK(hipMemcpy(dst, w.ptr, bytes, hipMemcpyDeviceToHost));
+      } else {
+        std::vector<uint16_t> tmp(w.count);
+        HIPCHK(hipMemcpy(tmp.data(), w.ptr, w.count * 2, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < w.count; ++i) {
+          const uint32_t u = (uint32_t)tmp[i] << 16;
+          memcpy(&out[i], &u, 4);
+        }
+      }
+      return VFM_OK;
+    }
+  }
+  // layers.{l}.{q,k,v,o,gate,up,down}.w
+  int l = -1;
+  char what[16] = {0};
+  if (sscanf(name, "layers.%d.%15[a-z].w", &l, what) != 2 || l < 0 || l >= x->L)
+    return fail(VFM_E_INVALID_ARG, "unknown tensor '%s'", name);
+  const std::string w = what;
+  const uint8_t* packed;
+  const ColMap* map;
+  int K, Npk, sid, ncols;
+  if (w == "q" || w == "k" || w == "v") {
+    packed = x->w_qkv[l]; map = &x->map_qkv; K = x->W; Npk = (x->Hq + 2 * x->Hkv) * x->d;
+    sid = w == "q" ? 0 : w == "k" ? 1 : 2; ncols = (w == "q" ? x->Hq : x->Hkv) * x->d;
+  } else if (w == "o") {
+    packed = x->w_o[l]; map = &x->map_o; K = x->Hq * x->d; Npk = x->W; sid = 0; ncols = x->W;
+  } else if (w == "gate" || w == "up") {
+    packed = x->w_gu[l]; map = &x->map_gu; K = x->W; Npk = 2 * x->F; sid = w == "gate" ? 0 : 1; ncols = x->F;
+  } else if (w == "down") {
+    packed = x->w_down[l]; map = &x->map_down; K = x->F; Npk = x->W; sid = 0; ncols = x->W;
+  } else {
+    return fail(VFM_E_INVALID_ARG, "unknown tensor '%s'", name);
+  }
+  if (bytes != (size_t)K * ncols * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, (size_t)K * ncols * 4);
+  const int ab = x->act_bf16 ? 2 : 4;
+  std::vector<uint8_t> host((size_t)K * Npk * ab);
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemcpy(host.data(), packed, host.size(), hipMemcpyDeviceToHost));
+  const int E = 16 / ab, KB = 4 * E, nkb = K / KB;
+  float* out = static_cast<float*>(dst);
+  for (int pc = 0; pc < Npk; ++pc) {
+    if (map->src[pc] != sid) continue;
+    const int col = map->idx[pc];
+    const int t = pc / 16, c16 = pc % 16;
+    for (int k = 0; k < K; ++k) {
+      const int kb = k / KB, rem = k % KB, g = rem / E, e = rem % E;
+      const size_t off = (((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + (size_t)e * ab;
+      float v;
+      if (ab == 4) {
+        memcpy(&v, &host[off], 4);
+      } else {
+        uint16_t hb;
+        memcpy(&hb, &host[off], 2);
+        uint32_t u = (uint32_t)hb << 16;
+        memcpy(&v, &u, 4);
+      }
+      out[(size_t)k * ncols + col] = v;
+    }
+  }
+  return VFM_OK;
+}
+
+vfm_status vfm_check(vfm_expert* x, void* stream) {
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  HIPCHK(hipGetLastError());
+  return check_prev_flag(x, true);
+}
+
+vfm_status vfm_expert_destroy(vfm_expert* x) {
+  if (!x) return VFM_OK;
+  (void)hipDeviceSynchronize();
+  vfm_status st = check_prev_flag(x, true);
+  free_all(x);
+  delete x;
+  return st;
+}
+
+}  // extern "C"

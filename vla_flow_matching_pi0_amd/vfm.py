@@ -1,0 +1,185 @@
+"""ctypes binding of libvfm.so (include/vfm.h).
+
+Argument marshalling only: every step of the denoise loop runs in the HIP
+kernels of the library. PyTorch supplies device memory and streams. There is
+no fallback: if the library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Mapping, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvfm.so")
+
+VFM_F32, VFM_BF16, VFM_F16, VFM_FP8_E4M3, VFM_I4X2 = 0, 1, 2, 3, 4
+WPREC = {"fp32": 0, "bf16": 1, "fp8": 2, "w4a16": 3}
+STATUS = {0: "VFM_OK", 1: "VFM_E_INVALID_ARG", 2: "VFM_E_SHAPE", 3: "VFM_E_DTYPE", 4: "VFM_E_UNBOUND",
+          5: "VFM_E_STATE", 6: "VFM_E_UNSUPPORTED", 7: "VFM_E_OOM", 8: "VFM_E_HIP"}
+ABI_VERSION = 1
+
+# Every entry point include/vfm.h declares.
+EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
+           "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
+           "vfm_expert_destroy"]
+
+
+class VfmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class VfmConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim",
+        "action_horizon", "action_dim", "state_dim", "time_emb_dim", "max_prefix_len", "max_batch",
+        "num_steps")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                         ("weight_precision", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                         ("w4_group_size", ctypes.c_int32)]
+
+
+class VfmTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dev_ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvfm.so and declare the signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m vla_flow_matching_pi0_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+    lib.vfm_abi_version.restype = ctypes.c_int
+    lib.vfm_last_error.restype = ctypes.c_char_p
+    lib.vfm_expert_create.argtypes = [ctypes.POINTER(VfmConfig), ctypes.POINTER(VfmTensor), i32, vp,
+                                      ctypes.POINTER(vp)]
+    lib.vfm_bind.argtypes = [vp, ctypes.c_char_p, vp, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.vfm_denoise.argtypes = [vp, vp, vp, vp, vp]
+    lib.vfm_set_option.argtypes = [vp, ctypes.c_char_p, ctypes.c_char_p]
+    lib.vfm_calibrate.argtypes = [vp, vp]
+    lib.vfm_set_act_scales.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32]
+    lib.vfm_export.argtypes = [vp, ctypes.c_char_p, vp, ctypes.c_size_t]
+    lib.vfm_check.argtypes = [vp, vp]
+    lib.vfm_expert_destroy.argtypes = [vp]
+    for n in EXPORTS[2:]:
+        getattr(lib, n).restype = st
+    if lib.vfm_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libvfm ABI {lib.vfm_abi_version()} != {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = _lib.vfm_last_error().decode(errors="replace")
+        raise VfmError(status, msg)
+
+
+def make_config(cfg, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None) -> VfmConfig:
+    """Build the C config from any object with the expert's fields
+    (num_layers, width, ..., weight_precision in {'fp32','bf16','fp8','w4a16'})."""
+    c = VfmConfig()
+    c.abi_version = ABI_VERSION
+    for n in ("num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim", "action_horizon",
+              "action_dim", "state_dim", "time_emb_dim", "num_steps"):
+        setattr(c, n, int(getattr(cfg, n)))
+    c.max_prefix_len = int(max_prefix_len if max_prefix_len is not None else cfg.prefix_len)
+    c.max_batch = int(max_batch if max_batch is not None else cfg.batch)
+    c.rope_base = float(cfg.rope_base)
+    c.rms_eps = float(cfg.rms_eps)
+    c.weight_precision = WPREC[cfg.weight_precision]
+    c.act_dtype = VFM_F32 if cfg.weight_precision == "fp32" else VFM_BF16
+    c.w4_group_size = int(getattr(cfg, "w4_group", 128))
+    return c
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: VFM_F32, torch.bfloat16: VFM_BF16, torch.float16: VFM_F16}[t.dtype]
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class Expert:
+    """One action expert living on the current HIP device.
+
+    weights: name -> device tensor (row-major [in][out]); fp32 for fp32
+    experts, bf16 otherwise. They may be freed once the constructor returns."""
+
+    def __init__(self, cfg, weights: Mapping[str, "object"], stream=None, max_batch: Optional[int] = None,
+                 max_prefix_len: Optional[int] = None):
+        lib = load_library()
+        self._cfg = cfg
+        self._ccfg = make_config(cfg, max_batch, max_prefix_len)
+        names = list(weights.keys())
+        arr = (VfmTensor * len(names))()
+        self._names = [n.encode() for n in names]
+        for i, n in enumerate(names):
+            t = weights[n]
+            arr[i].name = self._names[i]
+            arr[i].dev_ptr = t.data_ptr()
+            arr[i].dtype = _dtype_code(t)
+            arr[i].ndim = t.dim()
+            for j, s in enumerate(t.shape):
+                arr[i].shape[j] = int(s)
+        h = ctypes.c_void_p()
+        _check(lib.vfm_expert_create(ctypes.byref(self._ccfg), arr, len(names), _stream_ptr(stream), ctypes.byref(h)))
+        self._h = h
+        self._bound: Dict[str, object] = {}
+
+    # -------------------------------------------------------------- buffers
+    def bind(self, name: str, t) -> None:
+        shape = (ctypes.c_int64 * t.dim())(*[int(s) for s in t.shape])
+        _check(_lib.vfm_bind(self._h, name.encode(), t.data_ptr(), _dtype_code(t), t.dim(), shape))
+        self._bound[name] = t            # keep the memory alive while bound
+
+    def set_option(self, key: str, value: str) -> None:
+        _check(_lib.vfm_set_option(self._h, key.encode(), value.encode()))
+
+    def denoise(self, noise=None, state=None, out=None, stream=None):
+        """Run the loop; returns `out` (or the bound actions buffer)."""
+        ptr = lambda t: None if t is None else t.data_ptr()
+        _check(_lib.vfm_denoise(self._h, ptr(noise), ptr(state), ptr(out), _stream_ptr(stream)))
+        return out if out is not None else self._bound.get("actions")
+
+    def check(self, stream=None) -> None:
+        _check(_lib.vfm_check(self._h, _stream_ptr(stream)))
+
+    def calibrate(self, stream=None) -> None:
+        _check(_lib.vfm_calibrate(self._h, _stream_ptr(stream)))
+
+    def set_act_scales(self, scales) -> None:
+        a = np.ascontiguousarray(scales, dtype=np.float32)
+        _check(_lib.vfm_set_act_scales(self._h, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.size))
+
+    def export(self, name: str, shape) -> np.ndarray:
+        out = np.empty(shape, dtype=np.float32)
+        _check(_lib.vfm_export(self._h, name.encode(), out.ctypes.data, out.nbytes))
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            _check(_lib.vfm_expert_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
