@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Benchmark of the action-expert denoise loop on one MI355X.
+
+One "step" is one full denoise call: 10 flow-matching Euler steps of the
+pi0.5-shaped expert (18 layers, width 1024, 8 query heads + 1 KV head of
+dim 256, GeGLU 4096, 50 action tokens of dim 32, state 32, prefix KV of 560
+tokens, bf16 weights and activations) at batch 1, on synthetic seeded
+inputs already resident in HBM. Prints one JSON line.
+
+Roofline: the path streams every per-step GEMM weight plus the prefix KV from
+HBM once per Euler step (the modulation parameters are folded into a
+create-time table and are not counted); achieved GB/s = those algorithmic
+bytes per launch / the measured launch time, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def algorithmic_bytes_per_step(cfg) -> int:
+    """Bytes the method must read from HBM per Euler step: the per-step GEMM
+    weights (q/k/v/o/gate/up/down of every layer, in/out/state projections)
+    plus every layer's prefix K and V."""
+    wb = {"fp32": 4, "bf16": 2}[cfg.weight_precision]
+    W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
+    qkv = W * (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d
+    o = cfg.num_q_heads * d * W
+    per_layer = qkv + o + 2 * W * F + F * W
+    small = cfg.action_dim * W + W * cfg.action_dim + cfg.state_dim * W
+    prefix = 2 * L * cfg.batch * cfg.prefix_len * cfg.num_kv_heads * d
+    act_b = 4 if cfg.weight_precision == "fp32" else 2
+    return (L * per_layer + small) * wb + prefix * act_b
+
+
+def flops_per_chunk(cfg) -> float:
+    """Multiply-adds x 2 of the GEMMs and attention of one chunk."""
+    M = cfg.batch * cfg.action_horizon
+    W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
+    qkv = W * (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d
+    gemm = M * (L * (qkv + cfg.num_q_heads * d * W + 3 * W * F) + 2 * cfg.action_dim * W)
+    attn = L * cfg.batch * cfg.num_q_heads * cfg.action_horizon * (cfg.prefix_len + cfg.action_horizon) * d * 2
+    return 2.0 * (gemm + attn) * cfg.num_steps
+
+
+def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int):
+    """The oracle, untuned, timed on the host cores on a bounded sample:
+    `steps` of the Euler steps of the same chunk, scaled to the full chunk."""
+    from oracle import denoise as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    p64 = O.to_f64(params)
+    t0 = time.perf_counter()
+    O.denoise(p64, noise, state, pk, pv, cfg, num_steps=steps)
+    dt = time.perf_counter() - t0
+    per_chunk_ms = dt * 1e3 * cfg.num_steps / steps
+    return {"value": round(per_chunk_ms, 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} of {cfg.num_steps} Euler steps of the {cfg.name} chunk (float64 numpy), "
+                      f"scaled to {cfg.num_steps} steps; {dt:.1f} s measured"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed denoise calls (chunks)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="pi05_bf16_b1")
+    ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager"])
+    ap.add_argument("--cpu-steps", type=int, default=5, help="Euler steps of the oracle CPU sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoise loop at batch 1 is "
+              "not sharded; a batch would split across GPUs by samples with no communication.", file=sys.stderr)
+        return 2
+
+    import torch
+    from synth import CONFIGS, make_inputs
+    from vla_flow_matching_pi0_amd import vfm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    cfg = CONFIGS[args.workload]
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    wdt = torch.float32 if cfg.weight_precision == "fp32" else torch.bfloat16
+    dev = {k: torch.from_numpy(v).to("cuda").to(wdt) for k, v in params.items()}
+    ex = vfm.Expert(cfg, dev)
+    del dev
+    ex.set_option("launch_mode", args.mode)
+    bufs = {"prefix_k": torch.from_numpy(pk).to("cuda").to(wdt), "prefix_v": torch.from_numpy(pv).to("cuda").to(wdt),
+            "noise": torch.from_numpy(noise).to("cuda"), "actions": torch.empty(noise.shape, device="cuda")}
+    if cfg.state_dim:
+        bufs["state"] = torch.from_numpy(state).to("cuda")
+    for k, v in bufs.items():
+        ex.bind(k, v)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        ex.denoise(stream=stream)
+    ex.check(stream)
+    torch.cuda.synchronize()
+
+    # timed region: per-call HIP events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        ex.denoise(stream=stream)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ex.check(stream)
+    total_ms = t0.elapsed_time(t1)
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_chunk = total_ms / args.steps
+    med = float(np.median(per))
+
+    bytes_step = algorithmic_bytes_per_step(cfg)
+    bytes_launch = bytes_step * cfg.num_steps
+    achieved = bytes_launch / (med * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    cpu = None
+    if args.cpu_steps > 0:
+        print(f"[bench] oracle CPU sample ({args.cpu_steps} steps)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, params, pk, pv, noise, state, args.cpu_steps)
+    tflops = flops_per_chunk(cfg) / (med * 1e-3) / 1e12
+    line = {
+        "metric": "ms per 10-step action chunk @ batch 1; % of HBM weight-stream roofline",
+        "value": round(ms_chunk, 4),
+        "unit": "ms/chunk",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_chunk, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.weight_precision != "fp32" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
+                   "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,
+                   "action_dim": cfg.action_dim, "state_dim": cfg.state_dim, "prefix": cfg.prefix_len,
+                   "batch": cfg.batch, "euler_steps": cfg.num_steps, "launch_mode": args.mode},
+        "chunks_per_s": round(cfg.batch * 1e3 / ms_chunk, 2),
+        "ms_per_chunk_median": round(med, 4),
+        "ms_per_chunk_p99": round(float(np.percentile(per, 99)), 4),
+        "roofline_ms_per_chunk": round(bytes_launch / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+        "algorithmic_bytes_per_launch": int(bytes_launch),
+        "achieved_tflops": round(tflops, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    ex.close()
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -92,6 +92,21 @@ __device__ __forceinline__ void coh_st4(void* base, uint32_t off, uint32_t v) {
 // read-only data (weights, prefix KV, tables): ordinary cached loads
 __device__ __forceinline__ u32x4 ro_ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Predicated loads without branches: a lane whose `ok` is false gets an
+// out-of-range offset, which the buffer unit answers with zeros and no
+// memory access. Loads inside per-lane branches are serialised by the
+// compiler's wait insertion; these are issued back to back.
+constexpr uint32_t OOB = 0xFFFFFFF0u;
+__device__ __forceinline__ u32x4 ld16_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : OOB, 0, 0);
+}
+__device__ __forceinline__ u32x4 coh_ld16_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : OOB, 0, CPOL_SC1);
+}
+__device__ __forceinline__ u32x2 coh_ld8_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, ok ? off : OOB, 0, CPOL_SC1);
+}
+
 __device__ __forceinline__ floatx4 as_f4(u32x4 v) { return __builtin_bit_cast(floatx4, v); }
 __device__ __forceinline__ u32x4 as_u4(floatx4 v) { return __builtin_bit_cast(u32x4, v); }
 
@@ -132,11 +147,13 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch) {
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace = nullptr) {
   __shared__ unsigned s_ok;
   ++epoch;
   __builtin_amdgcn_s_waitcnt(0);   // this wave's stores (and loads) have completed
   __syncthreads();
+  // optional timeline: workgroup 0 stamps (arrive, release) of every barrier
+  if (trace && blockIdx.x == 0 && threadIdx.x == 0) trace[2 * epoch] = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0) {
     const unsigned G = gridDim.x;
     const unsigned ngroups = G < 8 ? G : 8;
@@ -155,6 +172,7 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch) {
       }
     }
     s_ok = ok;
+    if (trace && blockIdx.x == 0) trace[2 * epoch + 1] = __builtin_amdgcn_s_memrealtime();
   }
   __syncthreads();
   return s_ok != 0;

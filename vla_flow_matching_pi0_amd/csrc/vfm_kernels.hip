@@ -10,20 +10,23 @@
 //   * as one kernel launch per phase (eager, or captured into a hipGraph).
 //
 // Phases of one Euler step t_k (dt = -1/N), per layer l:
-//   in_proj   h = x W_in + b_in + s                      (s = state W_s + b_s)
-//   norm      xn = rms(h) * (1 + scale) + shift           (adaRMSNorm, attn)
 //   qkv       [q|k|v] = xn W_qkv, rotary on q, k at P..P+H-1   (fused GEMM)
 //   attn      split-K flash attention of q over prefix KV + chunk KV (GQA)
 //   combine   merge the key splits (log-sum-exp)
-//   o         h += gate * (attn W_o)                      (gated residual)
-//   norm      xn = adaRMSNorm(h) (mlp)
-//   gateup    a = gelu_tanh(xn W_gate) * (xn W_up)         (fused GEMM)
-//   down      h += gate * (a W_down)
-//   final     x += dt * (adaRMSNorm_final(h) W_out + b_out)
+//   o         partial_s = attn[:, K_s] W_o[K_s, :]            (K-split GEMM)
+//   rn_mlp    h += gate * sum_s partial_s; xn = adaRMSNorm(h)  (fused)
+//   gateup    a = gelu_tanh(xn W_gate) * (xn W_up)             (fused GEMM)
+//   down      partial_s = a[:, K_s] W_down[K_s, :]             (K-split GEMM)
+//   rn_attn   h += gate * sum_s partial_s; xn = adaRMSNorm(h)  (next layer)
+// and at a step boundary (one phase, row-owned):
+//   final     h += gate * sum_s partial_s; x += dt (adaRMSNorm_f(h) W_out + b_out)
+//   in_proj   h = x W_in + b_in + s; xn = adaRMSNorm(h) (layer 0)
 // The fusions (QKV as one GEMM, gate/up as one GEMM, residual+norm, RoPE in
 // the projection epilogue) follow the PhyAI optimisation paragraph and the
 // hand-written memory-bound kernels listed in the FlashRT walk-through
-// (component 8, kernel library).
+// (component 8, kernel library). The K-split of the residual GEMMs, whose
+// partial sums the following row-parallel norm phase reduces, is ours: it
+// lets every GEMM phase use all compute units without atomics.
 #include "vfm_device.h"
 #include "vfm_params.h"
 
@@ -31,313 +34,524 @@ namespace vfm {
 
 extern __shared__ __align__(16) char smem[];
 
-// =============================================================== elementwise phases
-// x = noise (skipped when the two alias) and s = state W_s + b_s.
-__device__ void ph_init(const VP& p, int wg, int nwg) {
-  const int nx = p.B * p.H * p.A;
-  if (p.noise != p.x) {
-    for (int i = wg * 256 + threadIdx.x; i < nx; i += nwg * 256)
-      coh_st4(p.x, i * 4, __builtin_bit_cast(uint32_t, p.noise[i]));
-  }
-  if (p.S > 0) {
-    const int ns = p.B * p.W;
-    for (int i = wg * 256 + threadIdx.x; i < ns; i += nwg * 256) {
-      const int b = i / p.W, n = i % p.W;
-      float acc = p.st_b[n];
-      for (int j = 0; j < p.S; ++j) acc += p.state[b * p.S + j] * p.st_w[j * p.W + n];
-      coh_st4(p.s, i * 4, __builtin_bit_cast(uint32_t, acc));
-    }
-  }
+constexpr int NTH = NTHREADS;          // threads per workgroup (8 waves)
+constexpr int NWAVES = NTH / 64;
+
+// Sum over the workgroup; `red` is >= NWAVES floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = warp_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) s += red[i];
+  return s;
 }
 
-// h[m][n] = sum_a x[m][a] W_in[a][n] + b_in[n] + s[b][n]; 4 columns per thread.
-__device__ void ph_in_proj(const VP& p, int wg, int nwg) {
-  const int W4 = p.W / 4, total = p.M * W4;
-  for (int it = wg * 256 + threadIdx.x; it < total; it += nwg * 256) {
-    const int m = it / W4, n = (it % W4) * 4;
-    const int b = m / p.H;
-    floatx4 acc = as_f4(ro_ld16(p.in_b + n));
-    if (p.S > 0) acc += as_f4(coh_ld16(p.s, (b * p.W + n) * 4));
-    for (int a = 0; a < p.A; ++a) {
-      const float xv = __builtin_bit_cast(float, coh_ld4(p.x, (m * p.A + a) * 4));
-      acc += xv * as_f4(ro_ld16(p.in_w + a * p.W + n));
-    }
-    coh_st16(p.h, (m * p.W + n) * 4, as_u4(acc));
-  }
+__device__ __forceinline__ float ldf_coh(const void* base, size_t idx) {
+  return __builtin_bit_cast(float, coh_ld4(base, (uint32_t)(idx * 4)));
+}
+__device__ __forceinline__ void stf_coh(void* base, size_t idx, float v) {
+  coh_st4(base, (uint32_t)(idx * 4), __builtin_bit_cast(uint32_t, v));
 }
 
-// adaRMSNorm of rows of h into xn (act type T); one row per workgroup unit.
+// Activations that many workgroups read (xn, q/k/v, attn, act) live in a
+// ring of per-(step, layer) slabs that are written exactly once per launch,
+// each 128-byte line by one workgroup, and only read after a phase barrier.
+// No L2 of any XCD can then hold a stale copy (the caches start clean at
+// every launch), so readers use ordinary cached loads and an XCD fetches
+// each line from memory once instead of every workgroup going to the
+// coherence point.
+__device__ __forceinline__ uint8_t* slab(const VP& p, int k, int l) { return p.ring + ((size_t)k * p.L + l) * p.slab; }
+
+// q/k/v are stored tile-major, [sample][head][d/16 tiles][64 tokens][16];
+// within a q/k tile the 16 slots hold dims 8t..8t+7, then their rotary
+// partners 8t+d/2..8t+7+d/2. Element offset of (token i, canonical dim e)
+// for a chunk of up to 8 consecutive dims that stays inside one half.
+__device__ __forceinline__ size_t qk_off(int d, size_t head_block, int i, int e) {
+  const int hd = d / 2;
+  const int tt = e < hd ? e / 8 : (e - hd) / 8;
+  const int pos = e < hd ? e % 8 : 8 + (e - hd) % 8;
+  return ((head_block * (d / 16) + tt) * 64 + i) * 16 + pos;
+}
+__device__ __forceinline__ size_t v_off(int d, size_t head_block, int i, int e) {
+  return ((head_block * (d / 16) + e / 16) * 64 + i) * 16 + e % 16;
+}
+
+// ============================================================ row phases
+// Row m of the residual stream is always handled by workgroup m % nwg, in
+// every row phase, so a row of h and x is only ever touched by one workgroup.
+
+// h[m] += gate * sum_s part[s][m]; xn[m] = adaRMSNorm(h[m]) with norm `ni`
+// (ni < 0: no norm). Four columns per thread; W <= 4 * NTH.
 template <typename T>
-__device__ void ph_norm(const VP& p, int step, int ni, int wg, int nwg) {
-  float* red = reinterpret_cast<float*>(smem);
-  const float* mod = p.mod + ((size_t)step * p.n_norms + ni) * 3 * p.W;
+__device__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni, int ni,
+                                  void* xn, float* red) {
   const int W4 = p.W / 4;
-  for (int m = wg; m < p.M; m += nwg) {
-    floatx4 hv[4];
-    float ss = 0.f;
+  const int c = threadIdx.x;
+  floatx4 hv = {0, 0, 0, 0}, sc = {0, 0, 0, 0}, sh = {0, 0, 0, 0};
+  if (c < W4 && ni >= 0) {   // modulation of the norm, fetched with the inputs
+    const float* mod = p.mod + ((size_t)step * p.n_norms + ni) * 3 * p.W;
+    sc = as_f4(ro_ld16(mod + c * 4));
+    sh = as_f4(ro_ld16(mod + p.W + c * 4));
+  }
+  if (c < W4) {
+    hv = as_f4(coh_ld16(p.h, (uint32_t)(((size_t)m * p.W + c * 4) * 4)));
+    if (S > 0) {
+      const auto pr = rsrc(part);
+      u32x4 pv[MAX_KSPLIT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = threadIdx.x + j * 256;
-      hv[j] = c < W4 ? as_f4(coh_ld16(p.h, (m * p.W + c * 4) * 4)) : floatx4{0, 0, 0, 0};
-      ss += hv[j].x * hv[j].x + hv[j].y * hv[j].y + hv[j].z * hv[j].z + hv[j].w * hv[j].w;
+      for (int s = 0; s < MAX_KSPLIT; ++s)
+        pv[s] = coh_ld16_if(pr, (uint32_t)((((size_t)s * p.M + m) * p.W + c * 4) * 4), s < S);
+      floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < MAX_KSPLIT; ++s) acc += as_f4(pv[s]);
+      const floatx4 gate = as_f4(ro_ld16(p.mod + (((size_t)step * p.n_norms + gate_ni) * 3 + 2) * p.W + c * 4));
+      hv += gate * acc;
+      coh_st16(p.h, (uint32_t)(((size_t)m * p.W + c * 4) * 4), as_u4(hv));
     }
-    ss = block_sum256(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
+  }
+  if (ni < 0) return;
+  float ss = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
+  if (c < W4) {
+    const floatx4 y = hv * r * (1.0f + sc) + sh;
+    if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(((size_t)m * p.W + c * 4) * 4), as_u4(y));
+    else coh_st8(xn, (uint32_t)(((size_t)m * p.W + c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+  }
+}
+
+// Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
+// scales the partial sums, ni the norm applied.
+template <typename T>
+__device__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
+  float* red = reinterpret_cast<float*>(smem);
+  const float* part = mlp ? p.part_o : p.part_d;
+  const int S = mlp ? p.S_o : p.S_down;
+  const int gate_ni = mlp ? 2 * layer : 2 * layer - 1, ni = mlp ? 2 * layer + 1 : 2 * layer;
+  void* xn = slab(p, step, layer) + (mlp ? p.off_xnm : p.off_xna);
+  for (int m = wg; m < p.M; m += nwg) {
+    row_residual_norm<T>(p, step, m, part, S, gate_ni, ni, xn, red);
+    __syncthreads();
+  }
+}
+
+// Step boundary for row m: finish step `kp` (if kp >= 0): add the last
+// layer's partials, x += dt * (adaRMSNorm_final(h) W_out + b_out); then
+// start step `kn` (if kn < N): h = x W_in + b_in + s, xn = adaRMSNorm(h).
+// kp = -1 also initialises x from the noise and the state embedding s.
+// Thread c owns columns 4c..4c+3 of the row; every weight load is issued
+// before it is used.
+constexpr int MAX_A = 64;
+template <typename T>
+__device__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
+  float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
+  float* xs = red + NWAVES;                                          // [W]
+  floatx4* part = reinterpret_cast<floatx4*>(xs + p.W);              // [NTH]
+  float* xrow = reinterpret_cast<float*>(part + NTH);                // [MAX_A]
+  const int A = p.A, W = p.W, W4 = W / 4, c = threadIdx.x;
+  const float dt = -1.0f / (float)p.N;
+  const auto wout = rsrc(p.out_w), win = rsrc(p.in_w), wst = rsrc(p.st_w);
+  for (int m = wg; m < p.M; m += nwg) {
+    const int b = m / p.H;
+    if (kp < 0) {
+      if (c < A) {
+        const float v = p.noise[(size_t)m * A + c];
+        xrow[c] = v;
+        if (p.noise != p.x) stf_coh(p.x, (size_t)m * A + c, v);
+      }
+    } else {
+      // h += gate * sum_s partial_s of the last layer, then the final adaRMSNorm into LDS
+      floatx4 hv = {0, 0, 0, 0};
+      if (c < W4) {
+        hv = as_f4(coh_ld16(p.h, (uint32_t)(((size_t)m * W + c * 4) * 4)));
+        if (p.L > 0) {
+          const auto pr = rsrc(p.part_d);
+          u32x4 pv[MAX_KSPLIT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = threadIdx.x + j * 256;
-      if (c >= W4) continue;
-      const floatx4 sc = as_f4(ro_ld16(mod + c * 4));
-      const floatx4 sh = as_f4(ro_ld16(mod + p.W + c * 4));
-      const floatx4 y = hv[j] * r * (1.0f + sc) + sh;
-      if constexpr (sizeof(T) == 4) {
-        coh_st16(p.xn, (m * p.W + c * 4) * 4, as_u4(y));
-      } else {
-        coh_st8(p.xn, (m * p.W + c * 4) * 2, u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+          for (int s = 0; s < MAX_KSPLIT; ++s)
+            pv[s] = coh_ld16_if(pr, (uint32_t)((((size_t)s * p.M + m) * W + c * 4) * 4), s < p.S_down);
+          floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < MAX_KSPLIT; ++s) acc += as_f4(pv[s]);
+          const floatx4 gate = as_f4(ro_ld16(p.mod + (((size_t)kp * p.n_norms + 2 * p.L - 1) * 3 + 2) * W + c * 4));
+          hv += gate * acc;
+        }
+      }
+      const float ss = block_sum(hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w, red);
+      const float r = 1.0f / sqrtf(ss / (float)W + p.eps);
+      if (c < W4) {
+        const float* mod = p.mod + ((size_t)kp * p.n_norms + (p.n_norms - 1)) * 3 * W;
+        const floatx4 y = hv * r * (1.0f + as_f4(ro_ld16(mod + c * 4))) + as_f4(ro_ld16(mod + W + c * 4));
+        *reinterpret_cast<floatx4*>(xs + c * 4) = y;
+      }
+      __syncthreads();
+      // v[4q..4q+3] = sum_n xs[n] W_out[n][4q..4q+3]: thread (q, sub) sums n = sub + nsub * j
+      const int nq = A / 4, nsub = NTH / nq, q = c % nq, sub = c / nq;
+      floatx4 acc = {0, 0, 0, 0};
+      for (int j0 = 0; j0 * nsub < W; j0 += 16) {
+        u32x4 wv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int n = sub + (j0 + j) * nsub;
+          wv[j] = ld16_if(wout, (uint32_t)(((size_t)n * A + 4 * q) * 4), n < W);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int n = sub + (j0 + j) * nsub;
+          acc += (n < W ? xs[n] : 0.f) * as_f4(wv[j]);
+        }
+      }
+      part[c] = acc;
+      __syncthreads();
+      if (c < nq) {
+        floatx4 v = as_f4(ro_ld16(p.out_b + 4 * c));
+        for (int j = 0; j < nsub; ++j) v += part[c + j * nq];
+        const uint32_t off = (uint32_t)(((size_t)m * A + 4 * c) * 4);
+        const floatx4 x = as_f4(coh_ld16(p.x, off)) + dt * v;
+        coh_st16(p.x, off, as_u4(x));
+        *reinterpret_cast<floatx4*>(xrow + 4 * c) = x;
       }
     }
+    __syncthreads();
+    if (kn < p.N) {
+      // h = x W_in + b_in + s, four columns per thread
+      floatx4 hv = {0, 0, 0, 0};
+      if (c < W4) {
+        hv = as_f4(ro_ld16(p.in_b + c * 4));
+        if (p.S > 0) {
+          if (kp < 0) {   // state embedding, computed once per denoise call
+            floatx4 sv = as_f4(ro_ld16(p.st_b + c * 4));
+            for (int j0 = 0; j0 < p.S; j0 += 16) {
+              u32x4 wv[16];
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                wv[j] = ld16_if(wst, (uint32_t)(((size_t)(j0 + j) * W + c * 4) * 4), j0 + j < p.S);
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (j0 + j < p.S) sv += p.state[(size_t)b * p.S + j0 + j] * as_f4(wv[j]);
+            }
+            coh_st16(p.s_emb, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(sv));
+            hv += sv;
+          } else {
+            hv += as_f4(coh_ld16(p.s_emb, (uint32_t)(((size_t)m * W + c * 4) * 4)));
+          }
+        }
+        for (int a0 = 0; a0 < A; a0 += 16) {
+          u32x4 wv[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            wv[j] = ld16_if(win, (uint32_t)(((size_t)(a0 + j) * W + c * 4) * 4), a0 + j < A);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) hv += (a0 + j < A ? xrow[a0 + j] : 0.f) * as_f4(wv[j]);
+        }
+        coh_st16(p.h, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(hv));
+      }
+      if (p.L > 0) {
+        const float ss = block_sum(hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w, red);
+        const float r = 1.0f / sqrtf(ss / (float)W + p.eps);
+        if (c < W4) {
+          const float* mod = p.mod + ((size_t)kn * p.n_norms) * 3 * W;
+          const floatx4 y = hv * r * (1.0f + as_f4(ro_ld16(mod + c * 4))) + as_f4(ro_ld16(mod + W + c * 4));
+          uint8_t* xn = slab(p, kn, 0) + p.off_xna;
+          if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(y));
+          else coh_st8(xn, (uint32_t)(((size_t)m * W + c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
-// =============================================================== skinny GEMM on MFMA
+// ============================================================ skinny GEMM on MFMA
 // C[M x N] = A[M x K] (act type T, row-major, produced by an earlier phase)
 // times a packed weight. Swap-AB: the weight supplies the 16 MFMA rows
 // (output features) and the tokens the 16 MFMA columns, so the 50 tokens of
 // a chunk pad to 64 = 4 column tiles and a lane ends with 4 consecutive
 // output features of one token. Packed weight layout:
 // [N/16 tiles][K/KB blocks][64 lanes][16 bytes], one contiguous 1 KiB block
-// per MFMA step, so a wave streams its tile's weights sequentially.
-// Work unit = 64 output columns (4 waves x 16) x 64 tokens.
+// per MFMA step.
+// Work unit = nt (1 or 2) 16-column tiles x a K range K/S x 64 tokens. The 8
+// waves of the workgroup split the K range; every wave issues all its weight
+// and activation loads of a pass before its MFMAs, and the 8 partial tiles
+// are summed through LDS. Nonlinear epilogues (RoPE, GeGLU) need S = 1; the
+// linear residual GEMMs (o, down) write S partial sums that the next row
+// phase adds.
 enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3 };
+constexpr int GEMM_PASS = 4;     // k blocks loaded per wave per pass
 
 template <typename T, int WHICH>
 __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
-  constexpr int KC = 512 / (int)sizeof(T);        // k per staged chunk (512 bytes of a row)
-  constexpr int LDA = KC + 16 / (int)sizeof(T);   // padded LDS row (elements)
-  constexpr int NBLK = KC / KB;                   // MFMA blocks per chunk (= 8)
-  const void* A;
+  uint8_t* sl = slab(p, step, layer);
+  const T* A;
   const uint8_t* Wp;
   int K, N;
-  if (WHICH == G_QKV) { A = p.xn; K = p.W; N = (p.Hq + 2 * p.Hkv) * p.d; Wp = p.w_qkv[layer]; }
-  else if (WHICH == G_O) { A = p.attn; K = p.Hq * p.d; N = p.W; Wp = p.w_o[layer]; }
-  else if (WHICH == G_GU) { A = p.xn; K = p.W; N = 2 * p.F; Wp = p.w_gu[layer]; }
-  else { A = p.act; K = p.F; N = p.W; Wp = p.w_down[layer]; }
-
-  T* As = reinterpret_cast<T*>(smem);
+  if (WHICH == G_QKV) { A = (const T*)(sl + p.off_xna); K = p.W; N = (p.Hq + 2 * p.Hkv) * p.d; Wp = p.w_qkv[layer]; }
+  else if (WHICH == G_O) { A = (const T*)(sl + p.off_attn); K = p.Hq * p.d; N = p.W; Wp = p.w_o[layer]; }
+  else if (WHICH == G_GU) { A = (const T*)(sl + p.off_xnm); K = p.W; N = 2 * p.F; Wp = p.w_gu[layer]; }
+  else { A = (const T*)(sl + p.off_act); K = p.F; N = p.W; Wp = p.w_down[layer]; }
+  const int nt = p.gp_nt[WHICH], S = p.gp_s[WHICH];
+  const int Mpad = ((p.M + 63) / 64) * 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const int ngroups = N / 64, mtiles = (p.M + 63) / 64, units = ngroups * mtiles;
-  const int nkb = K / KB;
+  const int ngroups = N / (16 * nt), mtiles = (p.M + 63) / 64;
+  const int units = ngroups * S * mtiles;
+  const int nkb = K / KB;                          // k blocks of the whole K
+  const int KR = K / S, nkbw = KR / KB / NWAVES;   // k blocks per wave
+  floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NWAVES][2][4][64]
   for (int u = wg; u < units; u += nwg) {
-    const int ng = u % ngroups, mt = u / ngroups;
-    const int t = ng * 4 + wv;                     // this wave's 16-column tile
-    const int m0 = mt * 64;
-    floatx4 acc[4];
+    const int ng = u % ngroups, rest = u / ngroups, s = rest % S, mt = rest / S;
+    const int t0 = ng * nt, m0 = mt * 64;
+    const int kb0 = (s * KR) / KB + wv * nkbw;
+    floatx4 acc[2][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc[s] = floatx4{0, 0, 0, 0};
-    const uint8_t* wt = Wp + ((size_t)t * nkb * 64 + lane) * 16;
-    for (int k0 = 0; k0 < K; k0 += KC) {
-      u32x4 wreg[NBLK];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < NBLK; ++i) wreg[i] = ro_ld16(wt + ((size_t)(k0 / KB + i) * 64) * 16);
-      __syncthreads();
-      // stage A[m0 .. m0+64)[k0 .. k0+KC) : 64 rows x 32 chunks of 16 bytes
+      for (int st = 0; st < 4; ++st) acc[t][st] = floatx4{0, 0, 0, 0};
+    bool rowok[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int idx = threadIdx.x + i * 256;
-        const int row = idx >> 5, cc = idx & 31;
-        const int gm = m0 + row;
-        u32x4 v = {0, 0, 0, 0};
-        if (gm < p.M) v = coh_ld16(A, (uint32_t)(((size_t)gm * K + k0) * sizeof(T) + cc * 16));
-        *reinterpret_cast<u32x4*>(As + row * LDA + cc * (16 / (int)sizeof(T))) = v;
-      }
-      __syncthreads();
+    for (int st = 0; st < 4; ++st) rowok[st] = m0 + st * 16 + c16 < p.M;
+    const auto wrs = rsrc(Wp), ars = rsrc(A);
+    for (int pb = 0; pb < nkbw; pb += GEMM_PASS) {
+      u32x4 wr[2][GEMM_PASS], ar[4][GEMM_PASS];
 #pragma unroll
-      for (int i = 0; i < NBLK; ++i) {
+      for (int i = 0; i < GEMM_PASS; ++i) {
+        const bool ok = pb + i < nkbw;
+        const int kb = kb0 + pb + i;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 b = *reinterpret_cast<const u32x4*>(As + (s * 16 + c16) * LDA + i * KB + g * E);
-          acc[s] = MT<T>::mma(wreg[i], b, acc[s]);
+        for (int t = 0; t < 2; ++t)
+          wr[t][i] = ld16_if(wrs, (uint32_t)((((size_t)(t0 + t) * nkb + kb) * 64 + lane) * 16), ok && t < nt);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const size_t row = (size_t)(m0 + st * 16 + c16);
+          const int k = kb * KB + g * E;
+          // act is tile-major [K/16][Mpad][16]; the others are row-major [M][K]
+          const size_t off = WHICH == G_DOWN ? ((size_t)(k / 16) * Mpad + row) * 16 + k % 16 : row * K + k;
+          ar[st][i] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
         }
       }
+#pragma unroll
+      for (int i = 0; i < GEMM_PASS; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            if (t < nt) acc[t][st] = MT<T>::mma(wr[t][i], ar[st][i], acc[t][st]);
     }
-    // ---------------- epilogues
+    // sum the 8 waves' partial tiles through LDS
+    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int gm = m0 + s * 16 + c16;
-      if (gm >= p.M) continue;
-      const floatx4 v = acc[s];
-      if (WHICH == G_QKV) {
-        const int d = p.d, hd = d / 2;
-        const int col0 = t * 16;
-        const int head = col0 / d, tt = (col0 % d) / 16;
-        const int b = gm / p.H, i = gm % p.H;
-        if (head < p.Hq + p.Hkv) {
-          // packed lane order (x_j, x_j+1, x_j+d/2, x_j+1+d/2), j = 8 tt + 2 g
-          const int j0 = tt * 8 + 2 * g;
-          const float* rp = p.rope + ((size_t)i * hd + j0) * 2;
-          const float c0 = rp[0], s0 = rp[1], c1 = rp[2], s1 = rp[3];
-          const float y0 = v.x * c0 - v.z * s0, y0h = v.z * c0 + v.x * s0;
-          const float y1 = v.y * c1 - v.w * s1, y1h = v.w * c1 + v.y * s1;
-          void* dst;
-          size_t row;
-          if (head < p.Hq) { dst = p.q; row = ((size_t)b * p.Hq + head) * p.H + i; }
-          else { dst = p.ks; row = ((size_t)b * p.Hkv + (head - p.Hq)) * p.H + i; }
-          const size_t e0 = row * d + j0;
-          if constexpr (sizeof(T) == 4) {
-            coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, y0), __builtin_bit_cast(uint32_t, y1)});
-            coh_st8(dst, (uint32_t)((e0 + hd) * 4), u32x2{__builtin_bit_cast(uint32_t, y0h), __builtin_bit_cast(uint32_t, y1h)});
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        if (t < nt) red[((wv * 2 + t) * 4 + st) * 64 + lane] = acc[t][st];
+    __syncthreads();
+    // epilogue: wave w finalises item w = (tile t, token subtile st)
+    if (wv < nt * 4) {
+      const int t = wv / 4, st = wv % 4;
+      floatx4 v = {0, 0, 0, 0};
+#pragma unroll
+      for (int w2 = 0; w2 < NWAVES; ++w2) v += red[((w2 * 2 + t) * 4 + st) * 64 + lane];
+      const int gm = m0 + st * 16 + c16;
+      const int tile = t0 + t;
+      if (gm < p.M) {
+        if (WHICH == G_QKV) {
+          const int d = p.d, hd = d / 2;
+          const int col0 = tile * 16;
+          const int head = col0 / d, tt = (col0 % d) / 16;
+          const int b = gm / p.H, i = gm % p.H;
+          if (head < p.Hq + p.Hkv) {
+            // packed lane order (x_j, x_j+1, x_j+d/2, x_j+1+d/2), j = 8 tt + 2 g
+            const int j0 = tt * 8 + 2 * g;
+            const float* rp = p.rope + ((size_t)i * hd + j0) * 2;
+            const float c0 = rp[0], s0 = rp[1], c1 = rp[2], s1 = rp[3];
+            const float y0 = v.x * c0 - v.z * s0, y0h = v.z * c0 + v.x * s0;
+            const float y1 = v.y * c1 - v.w * s1, y1h = v.w * c1 + v.y * s1;
+            const bool isq = head < p.Hq;
+            uint8_t* dst = sl + (isq ? p.off_q : p.off_k);
+            const size_t hb = isq ? (size_t)b * p.Hq + head : (size_t)b * p.Hkv + (head - p.Hq);
+            const size_t e0 = ((hb * (d / 16) + tt) * 64 + i) * 16 + 2 * g;   // slots 2g, 2g+1 and 8+2g, 9+2g
+            if constexpr (sizeof(T) == 4) {
+              coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, y0), __builtin_bit_cast(uint32_t, y1)});
+              coh_st8(dst, (uint32_t)((e0 + 8) * 4), u32x2{__builtin_bit_cast(uint32_t, y0h), __builtin_bit_cast(uint32_t, y1h)});
+            } else {
+              coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(y0, y1));
+              coh_st4(dst, (uint32_t)((e0 + 8) * 2), pack_bf16x2(y0h, y1h));
+            }
           } else {
-            coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(y0, y1));
-            coh_st4(dst, (uint32_t)((e0 + hd) * 2), pack_bf16x2(y0h, y1h));
+            const int kvh = head - p.Hq - p.Hkv;
+            const size_t e0 = ((((size_t)b * p.Hkv + kvh) * (d / 16) + tt) * 64 + i) * 16 + 4 * g;
+            uint8_t* dst = sl + p.off_v;
+            if constexpr (sizeof(T) == 4) coh_st16(dst, (uint32_t)(e0 * 4), as_u4(v));
+            else coh_st8(dst, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)});
           }
+        } else if (WHICH == G_GU) {
+          // packed lane order (gate f, up f, gate f+1, up f+1), f = 8 tile + 2 g
+          const int f0 = tile * 8 + 2 * g;
+          const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
+          const size_t e0 = ((size_t)(f0 / 16) * Mpad + gm) * 16 + f0 % 16;   // tile-major [F/16][Mpad][16]
+          uint8_t* dst = sl + p.off_act;
+          if constexpr (sizeof(T) == 4)
+            coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
+          else coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(a0, a1));
         } else {
-          const int kvh = head - p.Hq - p.Hkv;
-          const size_t e0 = (((size_t)b * p.Hkv + kvh) * p.H + i) * d + tt * 16 + 4 * g;
-          if constexpr (sizeof(T) == 4) coh_st16(p.vs, (uint32_t)(e0 * 4), as_u4(v));
-          else coh_st8(p.vs, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)});
+          float* part = WHICH == G_O ? p.part_o : p.part_d;
+          const int n0 = tile * 16 + 4 * g;
+          coh_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(v));
         }
-      } else if (WHICH == G_GU) {
-        // packed lane order (gate f, up f, gate f+1, up f+1), f = 8 t + 2 g
-        const int f0 = t * 8 + 2 * g;
-        const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
-        const size_t e0 = (size_t)gm * p.F + f0;
-        if constexpr (sizeof(T) == 4) coh_st8(p.act, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
-        else coh_st4(p.act, (uint32_t)(e0 * 2), pack_bf16x2(a0, a1));
-      } else {
-        // gated residual: h += gate * v (this lane owns h[gm][n0 .. n0+4))
-        const int ni = WHICH == G_O ? 2 * layer : 2 * layer + 1;
-        const int n0 = t * 16 + 4 * g;
-        const floatx4 gate = as_f4(ro_ld16(p.mod + (((size_t)step * p.n_norms + ni) * 3 + 2) * p.W + n0));
-        const uint32_t off = (uint32_t)(((size_t)gm * p.W + n0) * 4);
-        const floatx4 h = as_f4(coh_ld16(p.h, off));
-        coh_st16(p.h, off, as_u4(h + gate * v));
       }
     }
   }
 }
 
-// =============================================================== attention
+// ============================================================ attention
 // Flash-style attention of one query head over keys [s0, s1) of
-// [prefix (P) ; chunk (H)]. Work unit = (sample b, query head j, key split c).
-// Each wave owns 16 query rows; a 32-key chunk of K (row-major) and V
-// (transposed) is staged in LDS and shared by the 4 waves. Scores are
-// computed transposed, S^T = K Q^T, so a lane holds 8 keys of one query and
-// the row max / sum need only two cross-lane exchanges; the probabilities
-// then feed the PV MFMA directly from registers.
+// [prefix (P) ; chunk (H)], at most 64 keys. Work unit = (sample b, query
+// head j, key split c); the workgroup runs two units at once, one per group
+// of 4 waves. Each wave owns 16 query rows, kept in registers as MFMA
+// operands; the split's K (row-major) and V (transposed) are staged in LDS
+// with every load issued up front, and shared by the group's 4 waves.
+// Scores are computed transposed, S^T = K Q^T, so a lane holds 8 keys of one
+// query and the row max / sum need only two cross-lane exchanges; the
+// probabilities then feed the PV MFMA directly from registers.
+constexpr int ATT_KEYS = 64;   // keys per split
+
 template <typename T, int D>
-__device__ void ph_attn(const VP& p, int layer, int wg, int nwg) {
+__device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
-  constexpr int LDQ = D + 16 / (int)sizeof(T);
-  constexpr int LDV = 32 + 16 / (int)sizeof(T);
-  constexpr int CPR = D * (int)sizeof(T) / 16;    // 16-byte chunks per row
-  T* Qs = reinterpret_cast<T*>(smem);             // [64][LDQ]
-  T* Ks = Qs + 64 * LDQ;                          // [32][LDQ]
-  T* Vt = Ks + 32 * LDQ;                          // [D][LDV]
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const int H = p.H, P = p.P, S_tot = P + H, KS = p.KS, KPS = p.kps;
+  constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+  constexpr int LDK = D + EPC;                       // padded K row (elements)
+  constexpr int LDV = ATT_KEYS + EPC;                // padded V^T row (elements)
+  constexpr int CPR = D / EPC;                       // 16-byte chunks per key row
+  constexpr int GROUP_ELEMS = ATT_KEYS * LDK + D * LDV;
+  constexpr int LOADS = ATT_KEYS * CPR / 256;        // K (and V) chunks per thread
+  const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
+  T* Ks = reinterpret_cast<T*>(smem) + grp * GROUP_ELEMS;   // [64][LDK]
+  T* Vt = Ks + ATT_KEYS * LDK;                              // [D][LDV]
+  const int lane = threadIdx.x & 63, wv = gtid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int H = p.H, P = p.P, S_tot = P + H, KS = p.KS;
   const int group = p.Hq / p.Hkv;
   const int units = p.B * p.Hq * KS;
   const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
-  const T* pk_base = reinterpret_cast<const T*>(p.prefix_k);
-  const T* pv_base = reinterpret_cast<const T*>(p.prefix_v);
-  for (int u = wg; u < units; u += nwg) {
-    const int c = u % KS, bh = u / KS, jh = bh % p.Hq, b = bh / p.Hq;
+  const size_t layer_elems = (size_t)p.B * P * p.Hkv * D;
+  const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
+  const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
+  const uint8_t* sl = slab(p, step, layer);
+  const auto qrs = rsrc(sl + p.off_q), kgr = rsrc(sl + p.off_k), vgr = rsrc(sl + p.off_v);
+  // both groups run the same number of rounds so the block barriers match
+  const int rounds = (units + 2 * nwg - 1) / (2 * nwg);
+  for (int rr = 0; rr < rounds; ++rr) {
+    const int u = (rr * nwg + wg) * 2 + grp;
+    const bool valid = u < units;
+    const int c = valid ? u % KS : 0, bh = valid ? u / KS : 0, jh = bh % p.Hq, b = bh / p.Hq;
     const int kvh = jh / group;
-    const int s0 = c * KPS, s1 = min(S_tot, s0 + KPS);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * CPR; idx += 256) {
-      const int row = idx / CPR, cc = idx % CPR;
-      u32x4 v = {0, 0, 0, 0};
-      if (row < H) v = coh_ld16(p.q, (uint32_t)((((size_t)(b * p.Hq + jh) * H + row) * D) * sizeof(T) + cc * 16));
-      *reinterpret_cast<u32x4*>(Qs + row * LDQ + cc * (16 / (int)sizeof(T))) = v;
+    const int s0 = c * ATT_KEYS, s1 = valid ? min(S_tot, s0 + ATT_KEYS) : s0;
+    const int qrow = wv * 16 + c16;
+    const bool active = valid && wv * 16 < H;
+    // query fragments (B operand of S^T): Q[qrow][kb*KB + g*E .. +E]
+    u32x4 qf[D / KB];
+#pragma unroll
+    for (int kb = 0; kb < D / KB; ++kb)
+      qf[kb] = ld16_if(qrs, (uint32_t)(qk_off(D, (size_t)b * p.Hq + jh, qrow, kb * KB + g * E) * sizeof(T)),
+                       active && qrow < H);
+    // K and V of the split: issue every load (prefix and chunk keys through
+    // two predicated loads, one of which returns zeros), then fill LDS
+    // K: a wave covers whole key rows (contiguous 16-byte LDS stores); V: a
+    // wave covers one 16-byte dim chunk of 64 keys, so its transposed
+    // element stores are consecutive in LDS and free of bank conflicts.
+    u32x4 kreg[LOADS], vreg[LOADS];
+    const size_t hb = (size_t)b * p.Hkv + kvh;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = gtid + j * 256;
+      {
+        const int kk = idx / CPR, e0 = (idx % CPR) * EPC, s = s0 + kk;
+        const bool inp = s < s1 && s < P, inc = s < s1 && s >= P;
+        const uint32_t op = (uint32_t)(((((size_t)b * P + s) * p.Hkv + kvh) * D + e0) * sizeof(T));
+        kreg[j] = ld16_if(pkr, op, inp) | ld16_if(kgr, (uint32_t)(qk_off(D, hb, inc ? s - P : 0, e0) * sizeof(T)), inc);
+      }
+      {
+        const int kk = idx % ATT_KEYS, e0 = (idx / ATT_KEYS) * EPC, s = s0 + kk;
+        const bool inp = s < s1 && s < P, inc = s < s1 && s >= P;
+        const uint32_t op = (uint32_t)(((((size_t)b * P + s) * p.Hkv + kvh) * D + e0) * sizeof(T));
+        vreg[j] = ld16_if(pvr, op, inp) | ld16_if(vgr, (uint32_t)(v_off(D, hb, inc ? s - P : 0, e0) * sizeof(T)), inc);
+      }
     }
+    __syncthreads();   // the previous round's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int idx = gtid + j * 256;
+      *reinterpret_cast<u32x4*>(Ks + (idx / CPR) * LDK + (idx % CPR) * EPC) = kreg[j];
+      const int kk = idx % ATT_KEYS, e0 = (idx / ATT_KEYS) * EPC;
+      const T* ve = reinterpret_cast<const T*>(&vreg[j]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) Vt[(e0 + e) * LDV + kk] = ve[e];
+    }
+    __syncthreads();
     float m_run = -INFINITY, l_run = 0.f;
     floatx4 O[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[dt] = floatx4{0, 0, 0, 0};
-    const bool active = wv * 16 < H;
-    for (int sc = s0; sc < s1; sc += 32) {
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < 32 * CPR; idx += 256) {
-        const int kk = idx / CPR, cc = idx % CPR;
-        const int s = sc + kk;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (s < s1) {
-          if (s < P) {
-            const size_t e = ((((size_t)layer * p.B + b) * P + s) * p.Hkv + kvh) * D;
-            kv = ro_ld16(pk_base + e + cc * (16 / (int)sizeof(T)));
-            vv = ro_ld16(pv_base + e + cc * (16 / (int)sizeof(T)));
-          } else {
-            const uint32_t off = (uint32_t)(((((size_t)b * p.Hkv + kvh) * H + (s - P)) * D) * sizeof(T) + cc * 16);
-            kv = coh_ld16(p.ks, off);
-            vv = coh_ld16(p.vs, off);
+    if (active) {
+#pragma unroll
+      for (int ci = 0; ci < ATT_KEYS / 32; ++ci) {
+        const int sc = s0 + ci * 32;
+        if (sc >= s1) break;
+        floatx4 slo = {0, 0, 0, 0}, shi = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < D / KB; ++kb) {
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + c16) * LDK + kb * KB + g * E);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + 16 + c16) * LDK + kb * KB + g * E);
+          slo = MT<T>::mma(alo, qf[kb], slo);
+          shi = MT<T>::mma(ahi, qf[kb], shi);
+        }
+        float pr[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = (sc + 4 * g + r < s1) ? slo[r] * scale : -INFINITY;
+          pr[4 + r] = (sc + 16 + 4 * g + r < s1) ? shi[r] * scale : -INFINITY;
+        }
+        float cmax = pr[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = fast_exp2(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); psum += pr[e]; }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= alpha;
+        // PV: key order of the k slots is (4g..4g+3, 16+4g..16+4g+3) for both operands
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[e] = (bf16)pr[e];
+          const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const T* vr = Vt + (dt * 16 + c16) * LDV + ci * 32;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * g);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * g);
+            O[dt] = MT<T>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pbu, O[dt]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = ci * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+              O[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f(Vt[(dt * 16 + c16) * LDV + key]), pr[e], O[dt], 0, 0, 0);
           }
         }
-        *reinterpret_cast<u32x4*>(Ks + kk * LDQ + cc * (16 / (int)sizeof(T))) = kv;
-        const T* ve = reinterpret_cast<const T*>(&vv);
-        const int d0 = cc * (16 / (int)sizeof(T));
-#pragma unroll
-        for (int e = 0; e < 16 / (int)sizeof(T); ++e) Vt[(d0 + e) * LDV + kk] = ve[e];
       }
-      __syncthreads();
-      if (!active) continue;
-      floatx4 slo = {0, 0, 0, 0}, shi = {0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < D / KB; ++kb) {
-        const u32x4 bq = *reinterpret_cast<const u32x4*>(Qs + (wv * 16 + c16) * LDQ + kb * KB + g * E);
-        const u32x4 alo = *reinterpret_cast<const u32x4*>(Ks + c16 * LDQ + kb * KB + g * E);
-        const u32x4 ahi = *reinterpret_cast<const u32x4*>(Ks + (16 + c16) * LDQ + kb * KB + g * E);
-        slo = MT<T>::mma(alo, bq, slo);
-        shi = MT<T>::mma(ahi, bq, shi);
-      }
-      float pr[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = (sc + 4 * g + r < s1) ? slo[r] * scale : -INFINITY;
-        pr[4 + r] = (sc + 16 + 4 * g + r < s1) ? shi[r] * scale : -INFINITY;
-      }
-      float cmax = pr[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); psum += pr[e]; }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) O[dt] *= alpha;
-      // PV: key order of the k slots is (4g..4g+3, 16+4g..16+4g+3) for both operands
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)pr[e];
-        const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const T* vr = Vt + (dt * 16 + c16) * LDV;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * g);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * g);
-          O[dt] = MT<T>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pbu, O[dt]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-            O[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f(Vt[(dt * 16 + c16) * LDV + key]), pr[e], O[dt], 0, 0, 0);
-        }
-      }
-    }
-    if (active) {
-      const int qrow = wv * 16 + c16;
       if (qrow < H) {
         const size_t base = ((size_t)(b * p.Hq + jh) * KS + c) * 64 + qrow;
 #pragma unroll
@@ -350,158 +564,148 @@ __device__ void ph_attn(const VP& p, int layer, int wg, int nwg) {
 }
 
 // Merge the key splits: attn[b*H+i][j*d + dd] = sum_c w_c O_c / sum_c w_c l_c,
-// w_c = 2^(m_c - max m). Four head dims per thread.
+// w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
+// c's (max, sum), then every lane merges four head dims over all splits.
 template <typename T>
-__device__ void ph_combine(const VP& p, int wg, int nwg) {
-  const int D = p.d, D4 = D / 4, KS = p.KS;
-  const int total = p.M * p.Hq * D4;
-  for (int it = wg * 256 + threadIdx.x; it < total; it += nwg * 256) {
-    const int d4 = it % D4, r = it / D4, jh = r % p.Hq, gm = r / p.Hq;
+__device__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
+  const int D = p.d, KS = p.KS;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int items = p.M * p.Hq;
+  uint8_t* attn = slab(p, step, layer) + p.off_attn;
+  for (int it = wg * NWAVES + wv; it < items; it += nwg * NWAVES) {
+    const int jh = it % p.Hq, gm = it / p.Hq;
     const int b = gm / p.H, i = gm % p.H;
     const size_t base0 = ((size_t)(b * p.Hq + jh) * KS) * 64 + i;
-    float mx = -INFINITY;
-    for (int c = 0; c < KS; ++c) mx = fmaxf(mx, __builtin_bit_cast(float, coh_ld4(p.ml, (uint32_t)((base0 + c * 64) * 8))));
-    floatx4 num = {0, 0, 0, 0};
-    float den = 0.f;
-    for (int c = 0; c < KS; ++c) {
-      const size_t base = base0 + (size_t)c * 64;
-      const floatx2 ml = __builtin_bit_cast(floatx2, coh_ld8(p.ml, (uint32_t)(base * 8)));
-      const float w = fast_exp2(ml[0] - mx);
-      den += w * ml[1];
-      num += w * as_f4(coh_ld16(p.opart, (uint32_t)((base * D + d4 * 4) * 4)));
+    float mc = -INFINITY, lc = 0.f;
+    if (lane < KS) {
+      const floatx2 ml = __builtin_bit_cast(floatx2, coh_ld8(p.ml, (uint32_t)((base0 + (size_t)lane * 64) * 8)));
+      mc = ml[0];
+      lc = ml[1];
     }
-    const floatx4 o = num / den;
-    const size_t e0 = (size_t)gm * p.Hq * D + jh * D + d4 * 4;
-    if constexpr (sizeof(T) == 4) coh_st16(p.attn, (uint32_t)(e0 * 4), as_u4(o));
-    else coh_st8(p.attn, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
+    float mx = mc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float wc = lane < KS ? fast_exp2(mc - mx) : 0.f;
+    const float den = warp_sum(wc * lc);
+    const auto opr = rsrc(p.opart);
+    for (int d4 = lane; d4 < D / 4; d4 += 64) {
+      floatx4 num = {0, 0, 0, 0};
+      for (int c0 = 0; c0 < KS; c0 += 16) {
+        u32x4 ov[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          ov[j] = coh_ld16_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4), c0 + j < KS);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
+      }
+      const floatx4 o = num / den;
+      const size_t e0 = (size_t)gm * p.Hq * D + jh * D + d4 * 4;
+      if constexpr (sizeof(T) == 4) coh_st16(attn, (uint32_t)(e0 * 4), as_u4(o));
+      else coh_st8(attn, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
+    }
   }
 }
 
-// =============================================================== final norm + out proj + Euler
-// One row per unit: v = adaRMSNorm_final(h[m]) W_out + b_out; x[m] += dt * v.
-__device__ void ph_final(const VP& p, int step, int wg, int nwg) {
-  float* red = reinterpret_cast<float*>(smem);          // [4]
-  float* xs = red + 4;                                   // [W]
-  float* part = xs + p.W;                                // [256]
-  const float* mod = p.mod + ((size_t)step * p.n_norms + (p.n_norms - 1)) * 3 * p.W;
-  const int A = p.A, nsub = 256 / A;
-  const float dt = -1.0f / (float)p.N;
-  for (int m = wg; m < p.M; m += nwg) {
-    float ss = 0.f;
-    for (int n = threadIdx.x; n < p.W; n += 256) {
-      const float v = __builtin_bit_cast(float, coh_ld4(p.h, (m * p.W + n) * 4));
-      xs[n] = v;
-      ss += v * v;
-    }
-    ss = block_sum256(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
-    for (int n = threadIdx.x; n < p.W; n += 256) xs[n] = xs[n] * r * (1.0f + mod[n]) + mod[p.W + n];
-    __syncthreads();
-    float acc = 0.f;
-    const int a = threadIdx.x % A, sub = threadIdx.x / A;
-    if (sub < nsub)
-      for (int n = sub; n < p.W; n += nsub) acc += xs[n] * p.out_w[n * A + a];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x < A) {
-      float v = p.out_b[threadIdx.x];
-      for (int j = 0; j < nsub; ++j) v += part[threadIdx.x + j * A];
-      const uint32_t off = (uint32_t)((m * A + threadIdx.x) * 4);
-      const float x = __builtin_bit_cast(float, coh_ld4(p.x, off));
-      coh_st4(p.x, off, __builtin_bit_cast(uint32_t, x + dt * v));
-    }
-    __syncthreads();
-  }
-}
-
-// =============================================================== kernels
+// ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_persistent(VP p) {
+__global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
   const int wg = blockIdx.x, nwg = gridDim.x;
-#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch)) return; } while (0)
-  ph_init(p, wg, nwg);
+  if (p.trace && wg == 0 && threadIdx.x == 0) p.trace[0] = p.trace[1] = __builtin_amdgcn_s_memrealtime();
+#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace)) return; } while (0)
+  ph_boundary<T>(p, -1, 0, wg, nwg);
   VFM_BAR();
   for (int k = 0; k < p.N; ++k) {
-    ph_in_proj(p, wg, nwg);
-    VFM_BAR();
     for (int l = 0; l < p.L; ++l) {
-      ph_norm<T>(p, k, 2 * l, wg, nwg);
-      VFM_BAR();
+      if (l > 0) {
+        ph_rn<T>(p, k, l, false, wg, nwg);
+        VFM_BAR();
+      }
       ph_gemm<T, G_QKV>(p, k, l, wg, nwg);
       VFM_BAR();
-      ph_attn<T, D>(p, l, wg, nwg);
+      ph_attn<T, D>(p, k, l, wg, nwg);
       VFM_BAR();
-      ph_combine<T>(p, wg, nwg);
+      ph_combine<T>(p, k, l, wg, nwg);
       VFM_BAR();
       ph_gemm<T, G_O>(p, k, l, wg, nwg);
       VFM_BAR();
-      ph_norm<T>(p, k, 2 * l + 1, wg, nwg);
+      ph_rn<T>(p, k, l, true, wg, nwg);
       VFM_BAR();
       ph_gemm<T, G_GU>(p, k, l, wg, nwg);
       VFM_BAR();
       ph_gemm<T, G_DOWN>(p, k, l, wg, nwg);
       VFM_BAR();
     }
-    ph_final(p, k, wg, nwg);
+    ph_boundary<T>(p, k, k + 1, wg, nwg);
     VFM_BAR();
   }
 #undef VFM_BAR
 }
 
-// One phase per launch (eager / graph modes).
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_phase(VP p, int phase, int k, int l) {
+// One phase per launch (eager / graph modes); one kernel symbol per phase so
+// a kernel trace attributes time to phases.
+template <typename T, int D, int PH>
+__global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
   const int wg = blockIdx.x, nwg = gridDim.x;
-  switch (phase) {
-    case PH_INIT: ph_init(p, wg, nwg); break;
-    case PH_IN_PROJ: ph_in_proj(p, wg, nwg); break;
-    case PH_NORM_ATTN: ph_norm<T>(p, k, 2 * l, wg, nwg); break;
-    case PH_QKV: ph_gemm<T, G_QKV>(p, k, l, wg, nwg); break;
-    case PH_ATTN: ph_attn<T, D>(p, l, wg, nwg); break;
-    case PH_COMBINE: ph_combine<T>(p, wg, nwg); break;
-    case PH_O: ph_gemm<T, G_O>(p, k, l, wg, nwg); break;
-    case PH_NORM_MLP: ph_norm<T>(p, k, 2 * l + 1, wg, nwg); break;
-    case PH_GU: ph_gemm<T, G_GU>(p, k, l, wg, nwg); break;
-    case PH_DOWN: ph_gemm<T, G_DOWN>(p, k, l, wg, nwg); break;
-    case PH_FINAL: ph_final(p, k, wg, nwg); break;
-    default: break;
+  if constexpr (PH == PH_BOUNDARY) ph_boundary<T>(p, k - 1, k, wg, nwg);
+  else if constexpr (PH == PH_RN_ATTN) ph_rn<T>(p, k, l, false, wg, nwg);
+  else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_ATTN) ph_attn<T, D>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_COMBINE) ph_combine<T>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_O) ph_gemm<T, G_O>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_RN_MLP) ph_rn<T>(p, k, l, true, wg, nwg);
+  else if constexpr (PH == PH_GU) ph_gemm<T, G_GU>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN>(p, k, l, wg, nwg);
+}
+
+template <typename T, int D>
+__host__ const void* phase_kernel(int ph) {
+  switch (ph) {
+    case PH_BOUNDARY: return (const void*)&k_phase<T, D, PH_BOUNDARY>;
+    case PH_RN_ATTN: return (const void*)&k_phase<T, D, PH_RN_ATTN>;
+    case PH_QKV: return (const void*)&k_phase<T, D, PH_QKV>;
+    case PH_ATTN: return (const void*)&k_phase<T, D, PH_ATTN>;
+    case PH_COMBINE: return (const void*)&k_phase<T, D, PH_COMBINE>;
+    case PH_O: return (const void*)&k_phase<T, D, PH_O>;
+    case PH_RN_MLP: return (const void*)&k_phase<T, D, PH_RN_MLP>;
+    case PH_GU: return (const void*)&k_phase<T, D, PH_GU>;
+    default: return (const void*)&k_phase<T, D, PH_DOWN>;
   }
 }
 
 }  // namespace vfm
 
-// =============================================================== host-side launch table
+// ============================================================ host-side launch table
 namespace vfm {
 
 size_t lds_bytes(const VP& p, int act_bytes) {
-  const size_t gemm = 64 * (512 + 16);
-  const size_t ldq = p.d + 16 / act_bytes, ldv = 32 + 16 / act_bytes;
-  const size_t attn = (96 * ldq + (size_t)p.d * ldv) * act_bytes;
-  const size_t fin = (4 + (size_t)p.W + 256) * 4;
+  const size_t gemm = (size_t)NWAVES * 2 * 4 * 64 * 16;
+  const size_t epc = 16 / act_bytes;
+  const size_t attn = 2 * ((size_t)ATT_KEYS * (p.d + epc) + (size_t)p.d * (ATT_KEYS + epc)) * act_bytes;
+  const size_t row = ((size_t)NWAVES + p.W + 4 * NTH + MAX_A) * 4;
   size_t m = gemm > attn ? gemm : attn;
-  return m > fin ? m : fin;
+  return m > row ? m : row;
 }
 
 template <typename T, int D>
 static hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, size_t lds, hipStream_t st) {
   if (mode == 0) {
     void* args[] = {const_cast<VP*>(&p)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(256), args,
+    return hipLaunchCooperativeKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(NTH), args,
                                       (unsigned)lds, st);
   }
-  hipLaunchKernelGGL((k_phase<T, D>), dim3(grid), dim3(256), lds, st, p, phase, k, l);
-  return hipGetLastError();
+  void* args[] = {const_cast<VP*>(&p), &k, &l};
+  return hipLaunchKernel(phase_kernel<T, D>(phase), dim3(grid), dim3(NTH), args, lds, st);
 }
 
 template <typename T, int D>
 static hipError_t set_lds_limit(int bytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_phase<T, D>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph)
+    e = hipFuncSetAttribute(phase_kernel<T, D>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return e;
 }
 
 hipError_t prepare_kernels(int act_bf16, int d, int lds) {
@@ -533,7 +737,7 @@ hipError_t max_cooperative_grid(int act_bf16, int d, size_t lds, int* grid) {
   if (act_bf16) f = d == 64 ? (const void*)&k_persistent<bf16, 64> : d == 128 ? (const void*)&k_persistent<bf16, 128> : (const void*)&k_persistent<bf16, 256>;
   else f = d == 64 ? (const void*)&k_persistent<float, 64> : d == 128 ? (const void*)&k_persistent<float, 128> : (const void*)&k_persistent<float, 256>;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 256, lds);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, NTH, lds);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 0;
   e = hipGetDevice(&dev);

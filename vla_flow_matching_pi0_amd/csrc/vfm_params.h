@@ -8,15 +8,18 @@
 namespace vfm {
 
 constexpr int MAX_LAYERS = 48;
+constexpr int NTHREADS = 512;      // threads per workgroup
+constexpr int MAX_KSPLIT = 16;     // K splits of the residual GEMMs
 
 enum Phase {
-  PH_INIT = 0, PH_IN_PROJ, PH_NORM_ATTN, PH_QKV, PH_ATTN, PH_COMBINE,
-  PH_O, PH_NORM_MLP, PH_GU, PH_DOWN, PH_FINAL, PH_COUNT
+  PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_COUNT
 };
 
 // Everything a phase needs; passed by value as the kernel argument.
 struct VP {
   int L, W, Hq, Hkv, d, F, H, A, S, N, B, P, M, n_norms, KS, kps;
+  int gp_nt[4], gp_s[4];   // GEMM plan (qkv, o, gateup, down): tiles per unit, K splits
+  int S_o, S_down;         // = gp_s[1], gp_s[3]
   float eps;
   const uint8_t* w_qkv[MAX_LAYERS];   // packed [N/16][K/KB][64][16 B]
   const uint8_t* w_o[MAX_LAYERS];
@@ -30,17 +33,20 @@ struct VP {
   const float* noise;      // [B][H][A]
   const float* state;      // [B][S]
   float* x;                // [B][H][A]  actions, updated in place
-  float* s;                // [B][W]     state embedding
+  float* s_emb;            // [M][W]     state embedding, per action token
   float* h;                // [M][W]     residual stream
-  void* xn;                // [M][W]     normalised activations (act type)
-  void* q;                 // [B][Hq][H][d]
-  void* ks;                // [B][Hkv][H][d]
-  void* vs;
+  // write-once activation ring: one slab per (step, layer) holding, at the
+  // offsets below, xn_attn [M][W], q [B][Hq][d/16][64][16], k and v
+  // [B][Hkv][d/16][64][16], attn [M][Hq*d], xn_mlp [M][W], act [F/16][Mpad][16]
+  uint8_t* ring;
+  size_t slab;
+  size_t off_xna, off_q, off_k, off_v, off_attn, off_xnm, off_act;
   float* opart;            // [B*Hq*KS*64][d]  unnormalised split outputs
   float* ml;               // [B*Hq*KS*64][2]  (max, sum) per split row, log2 domain
-  void* attn;              // [M][Hq*d]
-  void* act;               // [M][F]      GeGLU output
+  float* part_o;           // [S_o][M][W]  K-split partial sums of the o projection
+  float* part_d;           // [S_down][M][W] ... of the down projection
   unsigned* bar;           // grid-barrier words
+  unsigned long long* trace;  // optional phase timeline of the persistent kernel (null: off)
 };
 
 size_t lds_bytes(const VP& p, int act_bytes);

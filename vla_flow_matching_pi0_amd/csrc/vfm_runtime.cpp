@@ -68,11 +68,15 @@ struct vfm_expert {
   float* mod = nullptr;
   float* rope = nullptr;
   int rope_P = -1;
-  float* s = nullptr;
+  float* s_emb = nullptr;
   float* h = nullptr;
-  void *xn = nullptr, *q = nullptr, *ks = nullptr, *vs = nullptr, *attn = nullptr, *act = nullptr;
+  float *part_o = nullptr, *part_d = nullptr;
+  uint8_t* ring = nullptr;     // write-once activation slabs, one per (step, layer)
+  size_t slab = 0, off_xna = 0, off_q = 0, off_k = 0, off_v = 0, off_attn = 0, off_xnm = 0, off_act = 0;
   float *opart = nullptr, *ml = nullptr;
   unsigned* bar = nullptr;
+  unsigned long long* trace = nullptr;   // phase timeline (option "trace")
+  size_t trace_words = 0;
   unsigned* host_flag = nullptr;   // pinned copy of the barrier error word
   hipEvent_t flag_event = nullptr;
   bool flag_pending = false;
@@ -104,26 +108,28 @@ vfm_status validate_config(const vfm_config* c) {
     return fail(VFM_E_INVALID_ARG, "abi_version %d != %d", c->abi_version, VFM_ABI_VERSION);
   if (c->num_layers < 0 || c->num_layers > vfm::MAX_LAYERS)
     return fail(VFM_E_INVALID_ARG, "num_layers %d outside [0, %d]", c->num_layers, vfm::MAX_LAYERS);
-  if (c->width < 256 || c->width % 256 != 0 || c->width > 4096)
-    return fail(VFM_E_INVALID_ARG, "width %d must be a multiple of 256 in [256, 4096]", c->width);
+  if (c->width < 256 || c->width % 256 != 0 || c->width > 2048)
+    return fail(VFM_E_INVALID_ARG, "width %d must be a multiple of 256 in [256, 2048]", c->width);
   if (c->num_kv_heads < 1 || c->num_q_heads < 1 || c->num_q_heads % c->num_kv_heads != 0)
     return fail(VFM_E_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d", c->num_q_heads,
                 c->num_kv_heads);
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
     return fail(VFM_E_INVALID_ARG, "head_dim %d must be 64, 128 or 256", c->head_dim);
+  if (c->act_dtype == VFM_F32 && c->head_dim > 128)
+    return fail(VFM_E_INVALID_ARG, "fp32 experts support head_dim <= 128");
   if ((c->num_q_heads * c->head_dim) % 256 != 0)
     return fail(VFM_E_INVALID_ARG, "num_q_heads * head_dim must be a multiple of 256");
   if (c->mlp_dim < 256 || c->mlp_dim % 256 != 0 || c->mlp_dim > 65536)
     return fail(VFM_E_INVALID_ARG, "mlp_dim %d must be a multiple of 256 in [256, 65536]", c->mlp_dim);
   if (c->action_horizon < 1 || c->action_horizon > 64)
     return fail(VFM_E_INVALID_ARG, "action_horizon %d outside [1, 64]", c->action_horizon);
-  if (c->action_dim < 1 || c->action_dim > 64 || 256 % c->action_dim != 0)
-    return fail(VFM_E_INVALID_ARG, "action_dim %d must divide 256", c->action_dim);
+  if (c->action_dim != 4 && c->action_dim != 8 && c->action_dim != 16 && c->action_dim != 32 && c->action_dim != 64)
+    return fail(VFM_E_INVALID_ARG, "action_dim %d must be 4, 8, 16, 32 or 64", c->action_dim);
   if (c->state_dim < 0 || c->state_dim > 4096) return fail(VFM_E_INVALID_ARG, "state_dim %d out of range", c->state_dim);
   if (c->time_emb_dim < 4 || c->time_emb_dim % 2 != 0 || c->time_emb_dim > 8192)
     return fail(VFM_E_INVALID_ARG, "time_emb_dim %d must be even in [4, 8192]", c->time_emb_dim);
-  if (c->max_prefix_len < 1 || c->max_prefix_len > 65536)
-    return fail(VFM_E_INVALID_ARG, "max_prefix_len %d outside [1, 65536]", c->max_prefix_len);
+  if (c->max_prefix_len < 1 || c->max_prefix_len > 4000)
+    return fail(VFM_E_INVALID_ARG, "max_prefix_len %d outside [1, 4000]", c->max_prefix_len);
   if (c->max_batch < 1 || c->max_batch > 1024) return fail(VFM_E_INVALID_ARG, "max_batch %d outside [1, 1024]", c->max_batch);
   if (c->num_steps < 1 || c->num_steps > 1000) return fail(VFM_E_INVALID_ARG, "num_steps %d outside [1, 1000]", c->num_steps);
   if (!(c->rope_base > 0.f)) return fail(VFM_E_INVALID_ARG, "rope_base must be > 0");
@@ -258,38 +264,48 @@ int phase_grid(const VP& p, int phase) {
   const int mt = cdiv(p.M, 64);
   long units = 1;
   switch (phase) {
-    case vfm::PH_INIT: units = cdiv(std::max(p.B * p.H * p.A, p.B * p.W), 256); break;
-    case vfm::PH_IN_PROJ: units = cdiv((long)p.M * p.W / 4, 256); break;
-    case vfm::PH_NORM_ATTN:
-    case vfm::PH_NORM_MLP:
-    case vfm::PH_FINAL: units = p.M; break;
-    case vfm::PH_QKV: units = (long)(p.Hq + 2 * p.Hkv) * p.d / 64 * mt; break;
-    case vfm::PH_ATTN: units = (long)p.B * p.Hq * p.KS; break;
-    case vfm::PH_COMBINE: units = cdiv((long)p.M * p.Hq * p.d / 4, 256); break;
-    case vfm::PH_O:
-    case vfm::PH_DOWN: units = (long)p.W / 64 * mt; break;
-    case vfm::PH_GU: units = (long)2 * p.F / 64 * mt; break;
+    case vfm::PH_BOUNDARY:
+    case vfm::PH_RN_ATTN:
+    case vfm::PH_RN_MLP: units = p.M; break;
+    case vfm::PH_QKV: units = (long)(p.Hq + 2 * p.Hkv) * p.d / (16 * p.gp_nt[0]) * p.gp_s[0] * mt; break;
+    case vfm::PH_O: units = (long)p.W / (16 * p.gp_nt[1]) * p.gp_s[1] * mt; break;
+    case vfm::PH_GU: units = (long)2 * p.F / (16 * p.gp_nt[2]) * p.gp_s[2] * mt; break;
+    case vfm::PH_DOWN: units = (long)p.W / (16 * p.gp_nt[3]) * p.gp_s[3] * mt; break;
+    case vfm::PH_ATTN: units = cdiv((long)p.B * p.Hq * p.KS, 2); break;
+    case vfm::PH_COMBINE: units = cdiv((long)p.M * p.Hq, vfm::NTHREADS / 64); break;
   }
   if (units < 1) units = 1;
-  if (units > 4096) units = 4096;
+  if (units > 8192) units = 8192;
   return (int)units;
 }
 
 hipError_t enqueue_phases(vfm_expert* x, const VP& p, hipStream_t st) {
   hipError_t e;
   auto run = [&](int ph, int k, int l) { return vfm::launch_phase(p, x->act_bf16, 1, ph, k, l, phase_grid(p, ph), x->lds, st); };
-  if ((e = run(vfm::PH_INIT, 0, 0)) != hipSuccess) return e;
+  if ((e = run(vfm::PH_BOUNDARY, 0, 0)) != hipSuccess) return e;
   for (int k = 0; k < p.N; ++k) {
-    if ((e = run(vfm::PH_IN_PROJ, k, 0)) != hipSuccess) return e;
     for (int l = 0; l < p.L; ++l) {
-      const int seq[] = {vfm::PH_NORM_ATTN, vfm::PH_QKV, vfm::PH_ATTN, vfm::PH_COMBINE,
-                         vfm::PH_O, vfm::PH_NORM_MLP, vfm::PH_GU, vfm::PH_DOWN};
+      if (l > 0 && (e = run(vfm::PH_RN_ATTN, k, l)) != hipSuccess) return e;
+      const int seq[] = {vfm::PH_QKV, vfm::PH_ATTN, vfm::PH_COMBINE, vfm::PH_O, vfm::PH_RN_MLP, vfm::PH_GU, vfm::PH_DOWN};
       for (int ph : seq)
         if ((e = run(ph, k, l)) != hipSuccess) return e;
     }
-    if ((e = run(vfm::PH_FINAL, k, 0)) != hipSuccess) return e;
+    if ((e = run(vfm::PH_BOUNDARY, k + 1, 0)) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// GEMM plan: nt 16-column tiles per work unit and S splits of K, so that a
+// phase has about one unit per workgroup. Only linear epilogues split K.
+void plan_gemm(int M, int N, int K, int KB, int nwg, bool linear, int* nt, int* S) {
+  const int tiles = N / 16, mt = (M + 63) / 64, waves = vfm::NTHREADS / 64;
+  int smax = 1;
+  if (linear)
+    while (smax * 2 <= vfm::MAX_KSPLIT && K % (smax * 2 * KB * waves) == 0) smax *= 2;
+  *nt = (tiles % 2 == 0 && (long)(tiles / 2) * mt * smax >= nwg) ? 2 : 1;
+  int s = 1;
+  while (s * 2 <= smax && (long)(tiles / *nt) * mt * s < nwg) s *= 2;
+  *S = s;
 }
 
 }  // namespace
@@ -428,18 +444,28 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   const size_t Mmax = (size_t)x->maxB * H;
   x->KSmax = (x->maxP + H + 63) / 64;
   x->rope = (float*)x->dalloc((size_t)H * d * 4);
-  x->s = (float*)x->dalloc((size_t)x->maxB * W * 4);
+  x->s_emb = (float*)x->dalloc(Mmax * W * 4);
+  x->part_o = (float*)x->dalloc((size_t)vfm::MAX_KSPLIT * Mmax * W * 4);
+  x->part_d = (float*)x->dalloc((size_t)vfm::MAX_KSPLIT * Mmax * W * 4);
   x->h = (float*)x->dalloc(Mmax * W * 4);
-  x->xn = x->dalloc(Mmax * W * ab);
-  x->q = x->dalloc((size_t)x->maxB * Hq * H * d * ab);
-  x->ks = x->dalloc((size_t)x->maxB * Hkv * H * d * ab);
-  x->vs = x->dalloc((size_t)x->maxB * Hkv * H * d * ab);
+  {
+    auto al = [](size_t b) { return (b + 4095) / 4096 * 4096; };
+    const size_t Mpad = (Mmax + 63) / 64 * 64;
+    size_t off = 0;
+    x->off_xna = off; off += al(Mmax * W * ab);
+    x->off_q = off; off += al((size_t)x->maxB * Hq * d * 64 * ab);
+    x->off_k = off; off += al((size_t)x->maxB * Hkv * d * 64 * ab);
+    x->off_v = off; off += al((size_t)x->maxB * Hkv * d * 64 * ab);
+    x->off_attn = off; off += al(Mmax * Hq * d * ab);
+    x->off_xnm = off; off += al(Mmax * W * ab);
+    x->off_act = off; off += al((size_t)F * Mpad * ab);
+    x->slab = off;
+    x->ring = (uint8_t*)x->dalloc(x->slab * (size_t)x->N * std::max(L, 1));
+  }
   x->opart = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * d * 4);
   x->ml = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * 2 * 4);
-  x->attn = x->dalloc(Mmax * Hq * d * ab);
-  x->act = x->dalloc(Mmax * F * ab);
   x->bar = (unsigned*)x->dalloc(1024 * 4);
-  if (!x->rope || !x->s || !x->h || !x->xn || !x->q || !x->ks || !x->vs || !x->opart || !x->ml || !x->attn || !x->act || !x->bar) {
+  if (!x->rope || !x->s_emb || !x->part_o || !x->part_d || !x->h || !x->ring || !x->opart || !x->ml || !x->bar) {
     fail(VFM_E_OOM, "workspace allocation failed");
     return bail(VFM_E_OOM);
   }
@@ -508,6 +534,18 @@ vfm_status vfm_bind(vfm_expert* x, const char* name, void* dev_ptr, int32_t dtyp
 vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
   if (!x || !key || !value) return fail(VFM_E_INVALID_ARG, "NULL argument");
   const std::string k = key, v = value;
+  if (k == "trace") {
+    if (v == "1" && !x->trace) {
+      x->trace_words = 2 * (size_t)(x->N * (8 * (size_t)x->L + 1) + 4);
+      x->trace = (unsigned long long*)x->dalloc(x->trace_words * 8);
+      if (!x->trace) return fail(VFM_E_OOM, "trace buffer");
+    } else if (v == "0") {
+      x->trace = nullptr;   // the buffer stays owned by the expert
+    } else if (v != "1") {
+      return fail(VFM_E_INVALID_ARG, "trace must be 0 or 1");
+    }
+    return VFM_OK;
+  }
   if (k == "launch_mode") {
     if (v == "persistent") x->mode = 0;
     else if (v == "graph") x->mode = 1;
@@ -544,14 +582,8 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   VP p{};
   p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
   p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
-  {
-    const int tot = P + x->H;
-    const int want = std::max(1, 256 / (B * x->Hq));
-    int kps = (tot + want - 1) / want;
-    kps = std::max(64, (kps + 31) / 32 * 32);
-    p.kps = kps;
-    p.KS = (tot + kps - 1) / kps;
-  }
+  p.kps = 64;                       // keys per attention split
+  p.KS = (P + x->H + 63) / 64;
   p.eps = x->cfg.rms_eps;
   for (int l = 0; l < x->L; ++l) {
     p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
@@ -560,9 +592,25 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   p.mod = x->mod; p.rope = x->rope;
   p.prefix_k = x->prefix_k.ptr; p.prefix_v = x->prefix_v.ptr;
   p.noise = noise; p.state = state; p.x = actions;
-  p.s = x->s; p.h = x->h; p.xn = x->xn; p.q = x->q; p.ks = x->ks; p.vs = x->vs; p.opart = x->opart; p.ml = x->ml;
-  p.attn = x->attn; p.act = x->act; p.bar = x->bar;
+  p.s_emb = x->s_emb; p.h = x->h; p.part_o = x->part_o; p.part_d = x->part_d; p.opart = x->opart; p.ml = x->ml;
+  p.ring = x->ring; p.slab = x->slab; p.off_xna = x->off_xna; p.off_q = x->off_q; p.off_k = x->off_k; p.off_v = x->off_v;
+  p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
+  p.trace = x->mode == 0 ? x->trace : nullptr;
 
+  {
+    int nwg = x->coop_grid;
+    if (nwg == 0) {
+      HIPCHK(vfm::max_cooperative_grid(x->act_bf16, x->d, x->lds, &x->coop_grid));
+      if (x->coop_grid == 0) return fail(VFM_E_HIP, "persistent kernel does not fit on a compute unit");
+      nwg = x->coop_grid;
+    }
+    const int KB = x->act_bf16 ? 32 : 16;
+    const int Ks[4] = {x->W, x->Hq * x->d, x->W, x->F};
+    const int Ns[4] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W};
+    for (int i = 0; i < 4; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i == 1 || i == 3, &p.gp_nt[i], &p.gp_s[i]);
+    p.S_o = p.gp_s[1];
+    p.S_down = p.gp_s[3];
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (x->rope_P != P) {
     HIPCHK(vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s));
@@ -570,10 +618,6 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
   }
   if (x->mode == 0) {
-    if (x->coop_grid == 0) {
-      HIPCHK(vfm::max_cooperative_grid(x->act_bf16, x->d, x->lds, &x->coop_grid));
-      if (x->coop_grid == 0) return fail(VFM_E_HIP, "persistent kernel does not fit on a compute unit");
-    }
     HIPCHK(vfm::zero_words(x->bar, 1024, s));
     HIPCHK(vfm::launch_phase(p, x->act_bf16, 0, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
@@ -638,13 +682,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     const int B = x->prefix_k.bound ? (int)x->prefix_k.shape[1] : x->maxB;
     const size_t M = (size_t)B * x->H;
     struct Ws { const char* name; const void* ptr; size_t count; bool act; };
-    const Ws ws[] = {{"ws.h", x->h, M * x->W, false},
-                     {"ws.xn", x->xn, M * x->W, true},
-                     {"ws.q", x->q, (size_t)B * x->Hq * x->H * x->d, true},
-                     {"ws.k", x->ks, (size_t)B * x->Hkv * x->H * x->d, true},
-                     {"ws.v", x->vs, (size_t)B * x->Hkv * x->H * x->d, true},
-                     {"ws.attn", x->attn, M * x->Hq * x->d, true},
-                     {"ws.act", x->act, M * x->F, true}};
+    const Ws ws[] = {{"ws.h", x->h, M * x->W, false}};
     for (const Ws& w : ws) {
       if (n != w.name) continue;
       if (bytes != w.count * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, w.count * 4);
@@ -662,6 +700,17 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
       }
       return VFM_OK;
     }
+  }
+  if (n == "trace") {
+    // microseconds since kernel start of (arrive, release) of every phase barrier of the last call
+    if (!x->trace) return fail(VFM_E_STATE, "trace is off");
+    if (bytes != x->trace_words * 4) return fail(VFM_E_SHAPE, "'trace' needs %zu bytes", x->trace_words * 4);
+    std::vector<unsigned long long> t(x->trace_words);
+    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(hipMemcpy(t.data(), x->trace, x->trace_words * 8, hipMemcpyDeviceToHost));
+    float* out = static_cast<float*>(dst);
+    for (size_t i = 0; i < x->trace_words; ++i) out[i] = t[i] >= t[0] ? (float)((t[i] - t[0]) / 100.0) : -1.0f;
+    return VFM_OK;
   }
   // layers.{l}.{q,k,v,o,gate,up,down}.w
   int l = -1;
