@@ -37,6 +37,16 @@ extern __shared__ __align__(16) char smem[];
 constexpr int NTH = NTHREADS;          // threads per workgroup (8 waves)
 constexpr int NWAVES = NTH / 64;
 
+// The thread index as an opaque value: every phase derives its lane
+// constants from this, so the compiler cannot hoist them out of the
+// persistent kernel's step/layer loops and keep every phase's constants live
+// at once (which made the fused kernel spill).
+__device__ __forceinline__ int tid_opaque() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
 // Sum over the workgroup; `red` is >= NWAVES floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = warp_sum(v);
@@ -88,8 +98,9 @@ __device__ __forceinline__ size_t v_off(int d, size_t head_block, int i, int e) 
 template <typename T>
 __device__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni, int ni,
                                   void* xn, float* red) {
+  const int tid = tid_opaque();
   const int W4 = p.W / 4;
-  const int c = threadIdx.x;
+  const int c = tid;
   floatx4 hv = {0, 0, 0, 0}, sc = {0, 0, 0, 0}, sh = {0, 0, 0, 0};
   if (c < W4 && ni >= 0) {   // modulation of the norm, fetched with the inputs
     const float* mod = p.mod + ((size_t)step * p.n_norms + ni) * 3 * p.W;
@@ -127,6 +138,7 @@ __device__ void row_residual_norm(const VP& p, int step, int m, const float* par
 // scales the partial sums, ni the norm applied.
 template <typename T>
 __device__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
+  const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
   const float* part = mlp ? p.part_o : p.part_d;
   const int S = mlp ? p.S_o : p.S_down;
@@ -147,11 +159,12 @@ __device__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nw
 constexpr int MAX_A = 64;
 template <typename T>
 __device__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
+  const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
   float* xs = red + NWAVES;                                          // [W]
   floatx4* part = reinterpret_cast<floatx4*>(xs + p.W);              // [NTH]
   float* xrow = reinterpret_cast<float*>(part + NTH);                // [MAX_A]
-  const int A = p.A, W = p.W, W4 = W / 4, c = threadIdx.x;
+  const int A = p.A, W = p.W, W4 = W / 4, c = tid;
   const float dt = -1.0f / (float)p.N;
   const auto wout = rsrc(p.out_w), win = rsrc(p.in_w), wst = rsrc(p.st_w);
   for (int m = wg; m < p.M; m += nwg) {
@@ -284,6 +297,7 @@ constexpr int GEMM_PASS = 4;     // k blocks loaded per wave per pass
 
 template <typename T, int WHICH>
 __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
+  const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   uint8_t* sl = slab(p, step, layer);
   const T* A;
@@ -295,7 +309,7 @@ __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
   else { A = (const T*)(sl + p.off_act); K = p.F; N = p.W; Wp = p.w_down[layer]; }
   const int nt = p.gp_nt[WHICH], S = p.gp_s[WHICH];
   const int Mpad = ((p.M + 63) / 64) * 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int ngroups = N / (16 * nt), mtiles = (p.M + 63) / 64;
   const int units = ngroups * S * mtiles;
   const int nkb = K / KB;                          // k blocks of the whole K
@@ -409,28 +423,67 @@ __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
 // ============================================================ attention
 // Flash-style attention of one query head over keys [s0, s1) of
 // [prefix (P) ; chunk (H)], at most 64 keys. Work unit = (sample b, query
-// head j, key split c); the workgroup runs two units at once, one per group
-// of 4 waves. Each wave owns 16 query rows, kept in registers as MFMA
-// operands; the split's K (row-major) and V (transposed) are staged in LDS
-// with every load issued up front, and shared by the group's 4 waves.
+// head j, key split c), one per workgroup. Each wave owns 16 query rows,
+// kept in registers as MFMA operands; the split's K (row-major) and V
+// (transposed) are staged in LDS with every load issued up front. The two
+// groups of 4 waves both compute the scores (cheap) and each applies P to
+// half of the head dims, so a workgroup reads K and V once.
 // Scores are computed transposed, S^T = K Q^T, so a lane holds 8 keys of one
 // query and the row max / sum need only two cross-lane exchanges; the
 // probabilities then feed the PV MFMA directly from registers.
 constexpr int ATT_KEYS = 64;   // keys per split
 
+template <typename T, int D, int MODE>   // MODE 0: prefix keys only, 1: chunk keys only, 2: both
+__device__ __forceinline__ void attn_load_kv(const VP& p, int tid, int b, int kvh, int s0, int s1,
+                                             __amdgpu_buffer_rsrc_t pkr, __amdgpu_buffer_rsrc_t pvr,
+                                             __amdgpu_buffer_rsrc_t kgr, __amdgpu_buffer_rsrc_t vgr,
+                                             u32x4* kreg, u32x4* vreg) {
+  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC;
+  constexpr int LOADS = ATT_KEYS * CPR / NTH;
+  const int P = p.P;
+  const int hbase = (b * p.Hkv + kvh) * D * 64;                 // chunk k/v block of this head
+  const int pstride = p.Hkv * D;                                // elements between prefix keys
+  const int pbase = ((b * P + s0) * p.Hkv + kvh) * D;           // prefix key s0
+  // K: a wave covers whole key rows; V: a wave covers one dim chunk of 64 keys
+  const int kk0 = tid / CPR, ke0 = (tid % CPR) * EPC;
+  const int ktt = ke0 < D / 2 ? ke0 / 8 : (ke0 - D / 2) / 8;
+  const int kpos = ke0 < D / 2 ? ke0 % 8 : 8 + (ke0 - D / 2) % 8;
+  const int vkk = tid % ATT_KEYS, ve00 = (tid / ATT_KEYS) * EPC;
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int kk = kk0 + j * (NTH / CPR), s = s0 + kk;
+    const int ve0 = ve00 + j * (NTH / ATT_KEYS) * EPC, vs = s0 + vkk;
+    const uint32_t kpo = (uint32_t)((pbase + kk * pstride + ke0) * (int)sizeof(T));
+    const uint32_t vpo = (uint32_t)((pbase + vkk * pstride + ve0) * (int)sizeof(T));
+    const uint32_t kco = (uint32_t)((hbase + (ktt * 64 + (s - P)) * 16 + kpos) * (int)sizeof(T));
+    const uint32_t vco = (uint32_t)((hbase + ((ve0 / 16) * 64 + (vs - P)) * 16 + ve0 % 16) * (int)sizeof(T));
+    if constexpr (MODE == 0) {
+      kreg[j] = ld16_if(pkr, kpo, s < s1);
+      vreg[j] = ld16_if(pvr, vpo, vs < s1);
+    } else if constexpr (MODE == 1) {
+      kreg[j] = ld16_if(kgr, kco, s < s1);
+      vreg[j] = ld16_if(vgr, vco, vs < s1);
+    } else {
+      kreg[j] = ld16_if(pkr, kpo, s < s1 && s < P) | ld16_if(kgr, kco, s < s1 && s >= P);
+      vreg[j] = ld16_if(pvr, vpo, vs < s1 && vs < P) | ld16_if(vgr, vco, vs < s1 && vs >= P);
+    }
+  }
+}
+
 template <typename T, int D>
 __device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
+  const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
   constexpr int LDK = D + EPC;                       // padded K row (elements)
   constexpr int LDV = ATT_KEYS + EPC;                // padded V^T row (elements)
   constexpr int CPR = D / EPC;                       // 16-byte chunks per key row
-  constexpr int GROUP_ELEMS = ATT_KEYS * LDK + D * LDV;
-  constexpr int LOADS = ATT_KEYS * CPR / 256;        // K (and V) chunks per thread
-  const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
-  T* Ks = reinterpret_cast<T*>(smem) + grp * GROUP_ELEMS;   // [64][LDK]
-  T* Vt = Ks + ATT_KEYS * LDK;                              // [D][LDV]
-  const int lane = threadIdx.x & 63, wv = gtid >> 6, g = lane >> 4, c16 = lane & 15;
+  constexpr int LOADS = ATT_KEYS * CPR / NTH;        // K (and V) chunks per thread
+  constexpr int DT = D / 32;                         // dim tiles per group
+  T* Ks = reinterpret_cast<T*>(smem);                // [64][LDK]
+  T* Vt = Ks + ATT_KEYS * LDK;                       // [D][LDV]
+  const int grp = tid >> 8, gtid = tid & 255;
+  const int lane = tid & 63, wv = gtid >> 6, g = lane >> 4, c16 = lane & 15;
   const int H = p.H, P = p.P, S_tot = P + H, KS = p.KS;
   const int group = p.Hq / p.Hkv;
   const int units = p.B * p.Hq * KS;
@@ -440,49 +493,33 @@ __device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
   const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
   const uint8_t* sl = slab(p, step, layer);
   const auto qrs = rsrc(sl + p.off_q), kgr = rsrc(sl + p.off_k), vgr = rsrc(sl + p.off_v);
-  // both groups run the same number of rounds so the block barriers match
-  const int rounds = (units + 2 * nwg - 1) / (2 * nwg);
-  for (int rr = 0; rr < rounds; ++rr) {
-    const int u = (rr * nwg + wg) * 2 + grp;
-    const bool valid = u < units;
-    const int c = valid ? u % KS : 0, bh = valid ? u / KS : 0, jh = bh % p.Hq, b = bh / p.Hq;
+  for (int u = wg; u < units; u += nwg) {
+    const int c = u % KS, bh = u / KS, jh = bh % p.Hq, b = bh / p.Hq;
     const int kvh = jh / group;
-    const int s0 = c * ATT_KEYS, s1 = valid ? min(S_tot, s0 + ATT_KEYS) : s0;
+    const int s0 = c * ATT_KEYS, s1 = min(S_tot, s0 + ATT_KEYS);
     const int qrow = wv * 16 + c16;
-    const bool active = valid && wv * 16 < H;
-    // query fragments (B operand of S^T): Q[qrow][kb*KB + g*E .. +E]
+    const bool active = wv * 16 < H;
+    // query fragments (B operand of S^T): Q[qrow][kb*KB + g*E .. +E]; the
+    // permuted q/k tile layout keeps each 16-byte chunk contiguous
     u32x4 qf[D / KB];
+    {
+      const int qbase = (b * p.Hq + jh) * D * 64;
+      const bool ok = active && qrow < H;
 #pragma unroll
-    for (int kb = 0; kb < D / KB; ++kb)
-      qf[kb] = ld16_if(qrs, (uint32_t)(qk_off(D, (size_t)b * p.Hq + jh, qrow, kb * KB + g * E) * sizeof(T)),
-                       active && qrow < H);
-    // K and V of the split: issue every load (prefix and chunk keys through
-    // two predicated loads, one of which returns zeros), then fill LDS
-    // K: a wave covers whole key rows (contiguous 16-byte LDS stores); V: a
-    // wave covers one 16-byte dim chunk of 64 keys, so its transposed
-    // element stores are consecutive in LDS and free of bank conflicts.
-    u32x4 kreg[LOADS], vreg[LOADS];
-    const size_t hb = (size_t)b * p.Hkv + kvh;
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int idx = gtid + j * 256;
-      {
-        const int kk = idx / CPR, e0 = (idx % CPR) * EPC, s = s0 + kk;
-        const bool inp = s < s1 && s < P, inc = s < s1 && s >= P;
-        const uint32_t op = (uint32_t)(((((size_t)b * P + s) * p.Hkv + kvh) * D + e0) * sizeof(T));
-        kreg[j] = ld16_if(pkr, op, inp) | ld16_if(kgr, (uint32_t)(qk_off(D, hb, inc ? s - P : 0, e0) * sizeof(T)), inc);
-      }
-      {
-        const int kk = idx % ATT_KEYS, e0 = (idx / ATT_KEYS) * EPC, s = s0 + kk;
-        const bool inp = s < s1 && s < P, inc = s < s1 && s >= P;
-        const uint32_t op = (uint32_t)(((((size_t)b * P + s) * p.Hkv + kvh) * D + e0) * sizeof(T));
-        vreg[j] = ld16_if(pvr, op, inp) | ld16_if(vgr, (uint32_t)(v_off(D, hb, inc ? s - P : 0, e0) * sizeof(T)), inc);
+      for (int kb = 0; kb < D / KB; ++kb) {
+        const int e = kb * KB + g * E;
+        const int tt = e < D / 2 ? e / 8 : (e - D / 2) / 8, pos = e < D / 2 ? e % 8 : 8 + (e - D / 2) % 8;
+        qf[kb] = ld16_if(qrs, (uint32_t)((qbase + (tt * 64 + qrow) * 16 + pos) * (int)sizeof(T)), ok);
       }
     }
-    __syncthreads();   // the previous round's LDS reads are done
+    u32x4 kreg[LOADS], vreg[LOADS];
+    if (s1 <= P) attn_load_kv<T, D, 0>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
+    else if (s0 >= P) attn_load_kv<T, D, 1>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
+    else attn_load_kv<T, D, 2>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
+    __syncthreads();   // the previous unit's LDS reads are done
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int idx = gtid + j * 256;
+      const int idx = tid + j * NTH;
       *reinterpret_cast<u32x4*>(Ks + (idx / CPR) * LDK + (idx % CPR) * EPC) = kreg[j];
       const int kk = idx % ATT_KEYS, e0 = (idx / ATT_KEYS) * EPC;
       const T* ve = reinterpret_cast<const T*>(&vreg[j]);
@@ -490,75 +527,85 @@ __device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
       for (int e = 0; e < EPC; ++e) Vt[(e0 + e) * LDV + kk] = ve[e];
     }
     __syncthreads();
+    if (!active) continue;
     float m_run = -INFINITY, l_run = 0.f;
-    floatx4 O[D / 16];
+    floatx4 O[DT];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) O[dt] = floatx4{0, 0, 0, 0};
-    if (active) {
+    for (int dt = 0; dt < DT; ++dt) O[dt] = floatx4{0, 0, 0, 0};
+    const int dbase = grp * (D / 2);
 #pragma unroll
-      for (int ci = 0; ci < ATT_KEYS / 32; ++ci) {
-        const int sc = s0 + ci * 32;
-        if (sc >= s1) break;
-        floatx4 slo = {0, 0, 0, 0}, shi = {0, 0, 0, 0};
+    for (int ci = 0; ci < ATT_KEYS / 32; ++ci) {
+      const int sc = s0 + ci * 32;
+      if (sc >= s1) break;
+      floatx4 slo = {0, 0, 0, 0}, shi = {0, 0, 0, 0};
+      constexpr int KH = D / KB < 4 ? D / KB : 4;     // K fragments read ahead per batch
 #pragma unroll
-        for (int kb = 0; kb < D / KB; ++kb) {
-          const u32x4 alo = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + c16) * LDK + kb * KB + g * E);
-          const u32x4 ahi = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + 16 + c16) * LDK + kb * KB + g * E);
-          slo = MT<T>::mma(alo, qf[kb], slo);
-          shi = MT<T>::mma(ahi, qf[kb], shi);
+      for (int k0 = 0; k0 < D / KB; k0 += KH) {
+        u32x4 alo[KH], ahi[KH];
+#pragma unroll
+        for (int kb = 0; kb < KH; ++kb) {
+          alo[kb] = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + c16) * LDK + (k0 + kb) * KB + g * E);
+          ahi[kb] = *reinterpret_cast<const u32x4*>(Ks + (ci * 32 + 16 + c16) * LDK + (k0 + kb) * KB + g * E);
         }
-        float pr[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[r] = (sc + 4 * g + r < s1) ? slo[r] * scale : -INFINITY;
-          pr[4 + r] = (sc + 16 + 4 * g + r < s1) ? shi[r] * scale : -INFINITY;
-        }
-        float cmax = pr[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); psum += pr[e]; }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= alpha;
-        // PV: key order of the k slots is (4g..4g+3, 16+4g..16+4g+3) for both operands
-        if constexpr (sizeof(T) == 2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = (bf16)pr[e];
-          const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) {
-            const T* vr = Vt + (dt * 16 + c16) * LDV + ci * 32;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * g);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * g);
-            O[dt] = MT<T>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pbu, O[dt]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = ci * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-              O[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f(Vt[(dt * 16 + c16) * LDV + key]), pr[e], O[dt], 0, 0, 0);
-          }
+        for (int kb = 0; kb < KH; ++kb) {
+          slo = MT<T>::mma(alo[kb], qf[k0 + kb], slo);
+          shi = MT<T>::mma(ahi[kb], qf[k0 + kb], shi);
         }
       }
-      if (qrow < H) {
-        const size_t base = ((size_t)(b * p.Hq + jh) * KS + c) * 64 + qrow;
+      float pr[8];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          coh_st16(p.opart, (uint32_t)((base * D + dt * 16 + 4 * g) * 4), as_u4(O[dt]));
-        if (g == 0) coh_st8(p.ml, (uint32_t)(base * 8), u32x2{__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_run)});
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = (sc + 4 * g + r < s1) ? slo[r] * scale : -INFINITY;
+        pr[4 + r] = (sc + 16 + 4 * g + r < s1) ? shi[r] * scale : -INFINITY;
       }
+      float cmax = pr[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); psum += pr[e]; }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+      // PV on this group's dims: key order of the k slots is
+      // (4g..4g+3, 16+4g..16+4g+3) for both operands
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)pr[e];
+        const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const T* vr = Vt + (dbase + dt * 16 + c16) * LDV + ci * 32;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 4 * g);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 + 4 * g);
+          O[dt] = MT<T>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pbu, O[dt]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = ci * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            O[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f(Vt[(dbase + dt * 16 + c16) * LDV + key]), pr[e], O[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (qrow < H) {
+      const size_t base = ((size_t)(b * p.Hq + jh) * KS + c) * 64 + qrow;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        coh_st16(p.opart, (uint32_t)((base * D + dbase + dt * 16 + 4 * g) * 4), as_u4(O[dt]));
+      if (g == 0 && grp == 0)
+        coh_st8(p.ml, (uint32_t)(base * 8), u32x2{__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_run)});
     }
   }
 }
@@ -568,8 +615,9 @@ __device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
 // c's (max, sum), then every lane merges four head dims over all splits.
 template <typename T>
 __device__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
+  const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = tid & 63, wv = tid >> 6;
   const int items = p.M * p.Hq;
   uint8_t* attn = slab(p, step, layer) + p.off_attn;
   for (int it = wg * NWAVES + wv; it < items; it += nwg * NWAVES) {
@@ -682,7 +730,7 @@ namespace vfm {
 size_t lds_bytes(const VP& p, int act_bytes) {
   const size_t gemm = (size_t)NWAVES * 2 * 4 * 64 * 16;
   const size_t epc = 16 / act_bytes;
-  const size_t attn = 2 * ((size_t)ATT_KEYS * (p.d + epc) + (size_t)p.d * (ATT_KEYS + epc)) * act_bytes;
+  const size_t attn = ((size_t)ATT_KEYS * (p.d + epc) + (size_t)p.d * (ATT_KEYS + epc)) * act_bytes;
   const size_t row = ((size_t)NWAVES + p.W + 4 * NTH + MAX_A) * 4;
   size_t m = gemm > attn ? gemm : attn;
   return m > row ? m : row;

@@ -271,7 +271,7 @@ int phase_grid(const VP& p, int phase) {
     case vfm::PH_O: units = (long)p.W / (16 * p.gp_nt[1]) * p.gp_s[1] * mt; break;
     case vfm::PH_GU: units = (long)2 * p.F / (16 * p.gp_nt[2]) * p.gp_s[2] * mt; break;
     case vfm::PH_DOWN: units = (long)p.W / (16 * p.gp_nt[3]) * p.gp_s[3] * mt; break;
-    case vfm::PH_ATTN: units = cdiv((long)p.B * p.Hq * p.KS, 2); break;
+    case vfm::PH_ATTN: units = (long)p.B * p.Hq * p.KS; break;
     case vfm::PH_COMBINE: units = cdiv((long)p.M * p.Hq, vfm::NTHREADS / 64); break;
   }
   if (units < 1) units = 1;
