@@ -147,7 +147,16 @@ __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace = nullptr) {
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// `hook` runs in every thread between this workgroup's arrival and its wait:
+// work that does not depend on the other workgroups (issuing loads of
+// read-only data) overlaps the wait.
+template <typename HOOK = NoHook>
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace = nullptr,
+                                             const HOOK& hook = HOOK()) {
   __shared__ unsigned s_ok;
   ++epoch;
   __builtin_amdgcn_s_waitcnt(0);   // this wave's stores (and loads) have completed
@@ -156,12 +165,15 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
   if (trace && blockIdx.x == 0 && threadIdx.x == 0) trace[2 * epoch] = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0) {
     const unsigned G = gridDim.x;
-    const unsigned ngroups = G < 8 ? G : 8;
     const unsigned grp = blockIdx.x % 8;
     const unsigned gsize = (G - grp + 7) / 8;
-    unsigned ok = 1;
     const unsigned old = __hip_atomic_fetch_add(&bar[64 + 64 * grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old + 1 == epoch * gsize) __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  hook();
+  if (threadIdx.x == 0) {
+    const unsigned ngroups = gridDim.x < 8 ? gridDim.x : 8;
+    unsigned ok = 1;
     long spins = 0;
     while (ld_agent(&bar[0]) < epoch * ngroups) {
       ++spins;

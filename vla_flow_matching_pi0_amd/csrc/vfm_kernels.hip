@@ -96,32 +96,30 @@ __device__ __forceinline__ size_t v_off(int d, size_t head_block, int i, int e) 
 // h[m] += gate * sum_s part[s][m]; xn[m] = adaRMSNorm(h[m]) with norm `ni`
 // (ni < 0: no norm). Four columns per thread; W <= 4 * NTH.
 template <typename T>
-__device__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni, int ni,
-                                  void* xn, float* red) {
+__device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni,
+                                                  int ni, void* xn, float* red) {
   const int tid = tid_opaque();
   const int W4 = p.W / 4;
   const int c = tid;
-  floatx4 hv = {0, 0, 0, 0}, sc = {0, 0, 0, 0}, sh = {0, 0, 0, 0};
-  if (c < W4 && ni >= 0) {   // modulation of the norm, fetched with the inputs
-    const float* mod = p.mod + ((size_t)step * p.n_norms + ni) * 3 * p.W;
-    sc = as_f4(ro_ld16(mod + c * 4));
-    sh = as_f4(ro_ld16(mod + p.W + c * 4));
-  }
-  if (c < W4) {
-    hv = as_f4(coh_ld16(p.h, (uint32_t)(((size_t)m * p.W + c * 4) * 4)));
-    if (S > 0) {
-      const auto pr = rsrc(part);
-      u32x4 pv[MAX_KSPLIT];
+  const bool act = c < W4;
+  const auto mr = rsrc(p.mod);
+  const size_t mrow = ((size_t)step * p.n_norms + (ni >= 0 ? ni : 0)) * 3 * p.W + c * 4;
+  const floatx4 sc = as_f4(ld16_if(mr, (uint32_t)(mrow * 4), act && ni >= 0));
+  const floatx4 sh = as_f4(ld16_if(mr, (uint32_t)((mrow + p.W) * 4), act && ni >= 0));
+  floatx4 hv = as_f4(coh_ld16_if(rsrc(p.h), (uint32_t)(((size_t)m * p.W + c * 4) * 4), act));
+  if (S > 0) {
+    const auto pr = rsrc(part);
+    u32x4 pv[MAX_KSPLIT];
 #pragma unroll
-      for (int s = 0; s < MAX_KSPLIT; ++s)
-        pv[s] = coh_ld16_if(pr, (uint32_t)((((size_t)s * p.M + m) * p.W + c * 4) * 4), s < S);
-      floatx4 acc = {0, 0, 0, 0};
+    for (int s = 0; s < MAX_KSPLIT; ++s)
+      pv[s] = coh_ld16_if(pr, (uint32_t)((((size_t)s * p.M + m) * p.W + c * 4) * 4), act && s < S);
+    const floatx4 gate =
+        as_f4(ld16_if(mr, (uint32_t)(((((size_t)step * p.n_norms + gate_ni) * 3 + 2) * p.W + c * 4) * 4), act));
+    floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < MAX_KSPLIT; ++s) acc += as_f4(pv[s]);
-      const floatx4 gate = as_f4(ro_ld16(p.mod + (((size_t)step * p.n_norms + gate_ni) * 3 + 2) * p.W + c * 4));
-      hv += gate * acc;
-      coh_st16(p.h, (uint32_t)(((size_t)m * p.W + c * 4) * 4), as_u4(hv));
-    }
+    for (int s = 0; s < MAX_KSPLIT; ++s) acc += as_f4(pv[s]);
+    hv += gate * acc;
+    if (act) coh_st16(p.h, (uint32_t)(((size_t)m * p.W + c * 4) * 4), as_u4(hv));
   }
   if (ni < 0) return;
   float ss = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
@@ -137,7 +135,7 @@ __device__ void row_residual_norm(const VP& p, int step, int m, const float* par
 // Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
 // scales the partial sums, ni the norm applied.
 template <typename T>
-__device__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
+__device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
   const float* part = mlp ? p.part_o : p.part_d;
@@ -158,7 +156,7 @@ __device__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nw
 // before it is used.
 constexpr int MAX_A = 64;
 template <typename T>
-__device__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
+__device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
   float* xs = red + NWAVES;                                          // [W]
@@ -295,25 +293,86 @@ __device__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
 enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3 };
 constexpr int GEMM_PASS = 4;     // k blocks loaded per wave per pass
 
+// Weight fragments of one pass of one unit, held in registers. The
+// persistent kernel loads a workgroup's first pass of the next GEMM at the
+// start of the preceding phase, so the weight stream's latency is spent
+// while that phase and the barrier run.
+struct WPre {
+  u32x4 w[2][GEMM_PASS];
+};
+
+struct GemmShape {
+  const uint8_t* Wp;
+  int K, N, nt, S, ngroups, units, nkb, KR, nkbw;
+};
+
 template <typename T, int WHICH>
-__device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
+__device__ __forceinline__ GemmShape gemm_shape(const VP& p, int layer) {
+  constexpr int KB = MT<T>::KB;
+  GemmShape g;
+  if (WHICH == G_QKV) { g.K = p.W; g.N = (p.Hq + 2 * p.Hkv) * p.d; g.Wp = p.w_qkv[layer]; }
+  else if (WHICH == G_O) { g.K = p.Hq * p.d; g.N = p.W; g.Wp = p.w_o[layer]; }
+  else if (WHICH == G_GU) { g.K = p.W; g.N = 2 * p.F; g.Wp = p.w_gu[layer]; }
+  else { g.K = p.F; g.N = p.W; g.Wp = p.w_down[layer]; }
+  g.nt = p.gp_nt[WHICH];
+  g.S = p.gp_s[WHICH];
+  g.ngroups = g.N / (16 * g.nt);
+  g.units = g.ngroups * g.S * ((p.M + 63) / 64);
+  g.nkb = g.K / KB;
+  g.KR = g.K / g.S;
+  g.nkbw = g.KR / KB / NWAVES;
+  return g;
+}
+
+// Weight fragments of pass pb of unit u for this lane (zeros where the pass
+// or the tile does not exist).
+template <typename T, int WHICH>
+__device__ __forceinline__ void gemm_load_weights(const GemmShape& gs, int u, int pb, int tid, WPre& out) {
+  constexpr int KB = MT<T>::KB;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int ng = u % gs.ngroups, s = (u / gs.ngroups) % gs.S;
+  const int t0 = ng * gs.nt;
+  const int kb0 = (s * gs.KR) / KB + wv * gs.nkbw;
+  const auto wrs = rsrc(gs.Wp);
+#pragma unroll
+  for (int i = 0; i < GEMM_PASS; ++i) {
+    const bool ok = pb + i < gs.nkbw;
+    const int kb = kb0 + pb + i;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      out.w[t][i] = ld16_if(wrs, (uint32_t)((((size_t)(t0 + t) * gs.nkb + kb) * 64 + lane) * 16), ok && t < gs.nt);
+  }
+}
+
+template <typename T, int WHICH>
+__device__ __forceinline__ void gemm_prefetch(const VP& p, int layer, int wg, WPre& out) {
+  const GemmShape gs = gemm_shape<T, WHICH>(p, layer);
+  const int tid = tid_opaque();
+  if (wg < gs.units) gemm_load_weights<T, WHICH>(gs, wg, 0, tid, out);
+}
+
+template <typename T, int WHICH>
+struct PrefetchHook {
+  const VP& p;
+  int layer, wg;
+  WPre& out;
+  __device__ __forceinline__ void operator()() const { gemm_prefetch<T, WHICH>(p, layer, wg, out); }
+};
+
+template <typename T, int WHICH, bool PRE>
+__device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg, const WPre& pre) {
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   uint8_t* sl = slab(p, step, layer);
   const T* A;
-  const uint8_t* Wp;
-  int K, N;
-  if (WHICH == G_QKV) { A = (const T*)(sl + p.off_xna); K = p.W; N = (p.Hq + 2 * p.Hkv) * p.d; Wp = p.w_qkv[layer]; }
-  else if (WHICH == G_O) { A = (const T*)(sl + p.off_attn); K = p.Hq * p.d; N = p.W; Wp = p.w_o[layer]; }
-  else if (WHICH == G_GU) { A = (const T*)(sl + p.off_xnm); K = p.W; N = 2 * p.F; Wp = p.w_gu[layer]; }
-  else { A = (const T*)(sl + p.off_act); K = p.F; N = p.W; Wp = p.w_down[layer]; }
-  const int nt = p.gp_nt[WHICH], S = p.gp_s[WHICH];
+  if (WHICH == G_QKV) A = (const T*)(sl + p.off_xna);
+  else if (WHICH == G_O) A = (const T*)(sl + p.off_attn);
+  else if (WHICH == G_GU) A = (const T*)(sl + p.off_xnm);
+  else A = (const T*)(sl + p.off_act);
+  const GemmShape gs = gemm_shape<T, WHICH>(p, layer);
+  const int K = gs.K, nt = gs.nt, S = gs.S, ngroups = gs.ngroups, units = gs.units, KR = gs.KR, nkbw = gs.nkbw;
   const int Mpad = ((p.M + 63) / 64) * 64;
   const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int ngroups = N / (16 * nt), mtiles = (p.M + 63) / 64;
-  const int units = ngroups * S * mtiles;
-  const int nkb = K / KB;                          // k blocks of the whole K
-  const int KR = K / S, nkbw = KR / KB / NWAVES;   // k blocks per wave
   floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NWAVES][2][4][64]
   for (int u = wg; u < units; u += nwg) {
     const int ng = u % ngroups, rest = u / ngroups, s = rest % S, mt = rest / S;
@@ -327,16 +386,16 @@ __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
     bool rowok[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) rowok[st] = m0 + st * 16 + c16 < p.M;
-    const auto wrs = rsrc(Wp), ars = rsrc(A);
+    const auto ars = rsrc(A);
     for (int pb = 0; pb < nkbw; pb += GEMM_PASS) {
-      u32x4 wr[2][GEMM_PASS], ar[4][GEMM_PASS];
+      WPre wl;
+      u32x4 ar[4][GEMM_PASS];
+      if (PRE && u == wg && pb == 0) wl = pre;
+      else gemm_load_weights<T, WHICH>(gs, u, pb, tid, wl);
 #pragma unroll
       for (int i = 0; i < GEMM_PASS; ++i) {
         const bool ok = pb + i < nkbw;
         const int kb = kb0 + pb + i;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          wr[t][i] = ld16_if(wrs, (uint32_t)((((size_t)(t0 + t) * nkb + kb) * 64 + lane) * 16), ok && t < nt);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const size_t row = (size_t)(m0 + st * 16 + c16);
@@ -352,7 +411,7 @@ __device__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int st = 0; st < 4; ++st)
-            if (t < nt) acc[t][st] = MT<T>::mma(wr[t][i], ar[st][i], acc[t][st]);
+            if (t < nt) acc[t][st] = MT<T>::mma(wl.w[t][i], ar[st][i], acc[t][st]);
     }
     // sum the 8 waves' partial tiles through LDS
     __syncthreads();
@@ -471,7 +530,7 @@ __device__ __forceinline__ void attn_load_kv(const VP& p, int tid, int b, int kv
 }
 
 template <typename T, int D>
-__device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
+__device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
@@ -614,7 +673,7 @@ __device__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
 // w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
 // c's (max, sum), then every lane merges four head dims over all splits.
 template <typename T>
-__device__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
+__device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
   const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
   const int lane = tid & 63, wv = tid >> 6;
@@ -662,32 +721,40 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   const int wg = blockIdx.x, nwg = gridDim.x;
   if (p.trace && wg == 0 && threadIdx.x == 0) p.trace[0] = p.trace[1] = __builtin_amdgcn_s_memrealtime();
 #define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace)) return; } while (0)
+  // The next GEMM's first weight pass is loaded while the workgroup waits at
+  // the barrier before it: weights do not depend on the other workgroups.
+#define VFM_BAR_PF(WHICH, LAYER) \
+  do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH>{p, LAYER, wg, pre})) return; } while (0)
+  WPre pre;
   ph_boundary<T>(p, -1, 0, wg, nwg);
-  VFM_BAR();
+  if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
+  else VFM_BAR();
   for (int k = 0; k < p.N; ++k) {
     for (int l = 0; l < p.L; ++l) {
       if (l > 0) {
         ph_rn<T>(p, k, l, false, wg, nwg);
-        VFM_BAR();
+        VFM_BAR_PF(G_QKV, l);
       }
-      ph_gemm<T, G_QKV>(p, k, l, wg, nwg);
+      ph_gemm<T, G_QKV, true>(p, k, l, wg, nwg, pre);
       VFM_BAR();
       ph_attn<T, D>(p, k, l, wg, nwg);
       VFM_BAR();
       ph_combine<T>(p, k, l, wg, nwg);
-      VFM_BAR();
-      ph_gemm<T, G_O>(p, k, l, wg, nwg);
+      VFM_BAR_PF(G_O, l);
+      ph_gemm<T, G_O, true>(p, k, l, wg, nwg, pre);
       VFM_BAR();
       ph_rn<T>(p, k, l, true, wg, nwg);
-      VFM_BAR();
-      ph_gemm<T, G_GU>(p, k, l, wg, nwg);
-      VFM_BAR();
-      ph_gemm<T, G_DOWN>(p, k, l, wg, nwg);
+      VFM_BAR_PF(G_GU, l);
+      ph_gemm<T, G_GU, true>(p, k, l, wg, nwg, pre);
+      VFM_BAR_PF(G_DOWN, l);
+      ph_gemm<T, G_DOWN, true>(p, k, l, wg, nwg, pre);
       VFM_BAR();
     }
     ph_boundary<T>(p, k, k + 1, wg, nwg);
-    VFM_BAR();
+    if (p.L > 0 && k + 1 < p.N) VFM_BAR_PF(G_QKV, 0);
+    else VFM_BAR();
   }
+#undef VFM_BAR_PF
 #undef VFM_BAR
 }
 
@@ -698,13 +765,13 @@ __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
   const int wg = blockIdx.x, nwg = gridDim.x;
   if constexpr (PH == PH_BOUNDARY) ph_boundary<T>(p, k - 1, k, wg, nwg);
   else if constexpr (PH == PH_RN_ATTN) ph_rn<T>(p, k, l, false, wg, nwg);
-  else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV, false>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_ATTN) ph_attn<T, D>(p, k, l, wg, nwg);
   else if constexpr (PH == PH_COMBINE) ph_combine<T>(p, k, l, wg, nwg);
-  else if constexpr (PH == PH_O) ph_gemm<T, G_O>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_O) ph_gemm<T, G_O, false>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_RN_MLP) ph_rn<T>(p, k, l, true, wg, nwg);
-  else if constexpr (PH == PH_GU) ph_gemm<T, G_GU>(p, k, l, wg, nwg);
-  else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_GU) ph_gemm<T, G_GU, false>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN, false>(p, k, l, wg, nwg, WPre{});
 }
 
 template <typename T, int D>
