@@ -15,6 +15,7 @@ bytes per launch / the measured launch time, against 8 TB/s.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,41 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_kernels.hip", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
+                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h"]
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the sources of the timed kernel: a traffic figure taken
+    from counters is only reported while it still describes this code."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, mode: str):
+    """HBM bytes per launch of the timed kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain streaming kernel of
+    known size), or None when there is none for this code and workload."""
+    if mode != "persistent":
+        return None
+    path = os.path.join(ROOT, "profiles", f"k_persistent_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- `"):
+                k, v = line[3:].split("`", 1)[0], line.split(":", 1)[1].strip().strip("`")
+                vals[k] = v
+    if vals.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes_per_step(cfg) -> int:
@@ -54,9 +90,10 @@ def flops_per_chunk(cfg) -> float:
     return 2.0 * (gemm + attn) * cfg.num_steps
 
 
-def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int):
+def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: float = 10.0):
     """The oracle, untuned, timed on the host cores on a bounded sample:
-    `steps` of the Euler steps of the same chunk, scaled to the full chunk."""
+    `steps` Euler steps of the same chunk, repeated until `min_seconds` have
+    passed, scaled to the full chunk."""
     from oracle import denoise as O
     try:
         from threadpoolctl import threadpool_info
@@ -64,12 +101,15 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int):
     except Exception:
         cores = os.cpu_count() or 1
     p64 = O.to_f64(params)
-    t0 = time.perf_counter()
-    O.denoise(p64, noise, state, pk, pv, cfg, num_steps=steps)
-    dt = time.perf_counter() - t0
-    per_chunk_ms = dt * 1e3 * cfg.num_steps / steps
+    reps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        O.denoise(p64, noise, state, pk, pv, cfg, num_steps=steps)
+        dt += time.perf_counter() - t0
+        reps += 1
+    per_chunk_ms = dt * 1e3 * cfg.num_steps / (steps * reps)
     return {"value": round(per_chunk_ms, 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} of {cfg.num_steps} Euler steps of the {cfg.name} chunk (float64 numpy), "
+            "sample": f"{reps} x {steps} of {cfg.num_steps} Euler steps of the {cfg.name} chunk (float64 numpy), "
                       f"scaled to {cfg.num_steps} steps; {dt:.1f} s measured"}
 
 
@@ -80,7 +120,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi05_bf16_b1")
     ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager"])
-    ap.add_argument("--cpu-steps", type=int, default=5, help="Euler steps of the oracle CPU sample (0: skip)")
+    ap.add_argument("--persistent-launch", default="cooperative", choices=["cooperative", "plain"],
+                    help="launch API of the persistent kernel (plain: for profilers that cannot follow "
+                         "cooperative launches)")
+    ap.add_argument("--cpu-steps", type=int, default=10, help="Euler steps of the oracle CPU sample (0: skip)")
+    ap.add_argument("--calib-mib", type=int, default=0,
+                    help="after the timed region, run a plain streaming kernel (negation) over this many MiB "
+                         "of float32, the reference for scaling HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoise loop at batch 1 is "
@@ -102,6 +148,7 @@ def main() -> int:
     ex = vfm.Expert(cfg, dev)
     del dev
     ex.set_option("launch_mode", args.mode)
+    ex.set_option("persistent_launch", args.persistent_launch)
     bufs = {"prefix_k": torch.from_numpy(pk).to("cuda").to(wdt), "prefix_v": torch.from_numpy(pv).to("cuda").to(wdt),
             "noise": torch.from_numpy(noise).to("cuda"), "actions": torch.empty(noise.shape, device="cuda")}
     if cfg.state_dim:
@@ -133,17 +180,26 @@ def main() -> int:
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_chunk = total_ms / args.steps
     med = float(np.median(per))
+    mean = float(np.mean(per))
+    if args.calib_mib > 0:
+        n = args.calib_mib * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     bytes_step = algorithmic_bytes_per_step(cfg)
     bytes_launch = bytes_step * cfg.num_steps
-    achieved = bytes_launch / (med * 1e-3) / 1e9
+    achieved = bytes_launch / (mean * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, args.mode)}
     cpu = None
     if args.cpu_steps > 0:
         print(f"[bench] oracle CPU sample ({args.cpu_steps} steps)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, params, pk, pv, noise, state, args.cpu_steps)
-    tflops = flops_per_chunk(cfg) / (med * 1e-3) / 1e12
+    tflops = flops_per_chunk(cfg) / (mean * 1e-3) / 1e12
     line = {
         "metric": "ms per 10-step action chunk @ batch 1; % of HBM weight-stream roofline",
         "value": round(ms_chunk, 4),
@@ -160,8 +216,10 @@ def main() -> int:
         "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,
                    "action_dim": cfg.action_dim, "state_dim": cfg.state_dim, "prefix": cfg.prefix_len,
-                   "batch": cfg.batch, "euler_steps": cfg.num_steps, "launch_mode": args.mode},
+                   "batch": cfg.batch, "euler_steps": cfg.num_steps, "launch_mode": args.mode,
+                   "persistent_launch": args.persistent_launch},
         "chunks_per_s": round(cfg.batch * 1e3 / ms_chunk, 2),
+        "ms_per_launch_mean": round(mean, 4),
         "ms_per_chunk_median": round(med, 4),
         "ms_per_chunk_p99": round(float(np.percentile(per, 99)), 4),
         "roofline_ms_per_chunk": round(bytes_launch / (HBM_PEAK_GBS * 1e9) * 1e3, 4),

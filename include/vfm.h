@@ -141,6 +141,16 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       denoise with device-wide phase barriers), "graph" (one kernel per
  *       phase, captured once into a hipGraph and replayed) or "eager" (one
  *       kernel per phase, launched directly).
+ *   "persistent_launch": "cooperative" (default) or "plain": how the
+ *       persistent kernel is launched. "plain" is an ordinary launch of the
+ *       same grid (one workgroup per compute unit, from the occupancy query);
+ *       it relies on the device being otherwise idle so that every
+ *       workgroup is resident. If one is not, the device-wide barrier gives
+ *       up after a bounded spin and the next vfm_check / vfm_denoise
+ *       reports VFM_E_HIP. Used where a tool cannot follow cooperative
+ *       launches (kernel profilers).
+ *   "trace": "1" / "0": record a timeline of the persistent kernel's phase
+ *       barriers (workgroup 0), read with vfm_export("trace").
  * Errors: VFM_E_INVALID_ARG for an unknown key or value. */
 vfm_status vfm_set_option(vfm_expert* ex, const char* key, const char* value);
 

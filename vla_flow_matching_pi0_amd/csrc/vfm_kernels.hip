@@ -810,6 +810,10 @@ static hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int
     return hipLaunchCooperativeKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(NTH), args,
                                       (unsigned)lds, st);
   }
+  if (mode == 3) {   // same kernel, ordinary launch (grid sized by the occupancy query)
+    void* args[] = {const_cast<VP*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(NTH), args, lds, st);
+  }
   void* args[] = {const_cast<VP*>(&p), &k, &l};
   return hipLaunchKernel(phase_kernel<T, D>(phase), dim3(grid), dim3(NTH), args, lds, st);
 }

@@ -84,6 +84,7 @@ struct vfm_expert {
   int mode = 0;                    // 0 persistent, 1 graph, 2 eager
   size_t lds = 0;
   int coop_grid = 0;
+  bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
   // graph cache (one entry): key = shape + pointers
   hipGraphExec_t gexec = nullptr;
   std::vector<uintptr_t> gkey;
@@ -546,6 +547,12 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     }
     return VFM_OK;
   }
+  if (k == "persistent_launch") {
+    if (v == "cooperative") x->coop_launch = true;
+    else if (v == "plain") x->coop_launch = false;
+    else return fail(VFM_E_INVALID_ARG, "persistent_launch must be 'cooperative' or 'plain'");
+    return VFM_OK;
+  }
   if (k == "launch_mode") {
     if (v == "persistent") x->mode = 0;
     else if (v == "graph") x->mode = 1;
@@ -619,7 +626,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   }
   if (x->mode == 0) {
     HIPCHK(vfm::zero_words(x->bar, 1024, s));
-    HIPCHK(vfm::launch_phase(p, x->act_bf16, 0, 0, 0, 0, x->coop_grid, x->lds, s));
+    HIPCHK(vfm::launch_phase(p, x->act_bf16, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(x->flag_event, s));
     x->flag_pending = true;
