@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_kernels.hip", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
+KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
                   "vla_flow_matching_pi0_amd/csrc/vfm_params.h"]
 
 
@@ -69,7 +69,6 @@ def algorithmic_bytes_per_step(cfg) -> int:
     """Bytes the method must read from HBM per Euler step: the per-step GEMM
     weights (q/k/v/o/gate/up/down of every layer, in/out/state projections)
     plus every layer's prefix K and V."""
-    wb = {"fp32": 4, "bf16": 2}[cfg.weight_precision]
     W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
     qkv = W * (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d
     o = cfg.num_q_heads * d * W
@@ -77,7 +76,13 @@ def algorithmic_bytes_per_step(cfg) -> int:
     small = cfg.action_dim * W + W * cfg.action_dim + cfg.state_dim * W
     prefix = 2 * L * cfg.batch * cfg.prefix_len * cfg.num_kv_heads * d
     act_b = 4 if cfg.weight_precision == "fp32" else 2
-    return (L * per_layer + small) * wb + prefix * act_b
+    if cfg.weight_precision == "fp8":
+        gemm = L * per_layer                                  # one byte per weight
+    elif cfg.weight_precision == "w4a16":
+        gemm = L * per_layer // 2 + L * per_layer // cfg.w4_group * 2   # nibbles + fp16 group scales
+    else:
+        gemm = L * per_layer * act_b
+    return gemm + small * act_b + prefix * act_b
 
 
 def flops_per_chunk(cfg) -> float:
@@ -134,7 +139,7 @@ def main() -> int:
         return 2
 
     import torch
-    from synth import CONFIGS, make_inputs
+    from synth import CONFIGS, make_calibration_inputs, make_inputs
     from vla_flow_matching_pi0_amd import vfm
 
     if not torch.cuda.is_available():
@@ -143,7 +148,7 @@ def main() -> int:
     cfg = CONFIGS[args.workload]
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     params, pk, pv, noise, state = make_inputs(cfg)
-    wdt = torch.float32 if cfg.weight_precision == "fp32" else torch.bfloat16
+    wdt = torch.float32 if cfg.weight_precision == "fp32" else torch.bfloat16   # masters / activations
     dev = {k: torch.from_numpy(v).to("cuda").to(wdt) for k, v in params.items()}
     ex = vfm.Expert(cfg, dev)
     del dev
@@ -153,9 +158,20 @@ def main() -> int:
             "noise": torch.from_numpy(noise).to("cuda"), "actions": torch.empty(noise.shape, device="cuda")}
     if cfg.state_dim:
         bufs["state"] = torch.from_numpy(state).to("cuda")
+    stream = torch.cuda.current_stream()
+    if cfg.weight_precision == "fp8":
+        # activation scales from one calibration pass over a separate draw
+        cpk, cpv, cnoise, cstate = make_calibration_inputs(cfg)
+        cal = {"prefix_k": torch.from_numpy(cpk).to("cuda").to(wdt), "prefix_v": torch.from_numpy(cpv).to("cuda").to(wdt),
+               "noise": torch.from_numpy(cnoise).to("cuda"), "actions": torch.empty(cnoise.shape, device="cuda")}
+        if cfg.state_dim:
+            cal["state"] = torch.from_numpy(cstate).to("cuda")
+        for k, v in cal.items():
+            ex.bind(k, v)
+        print("[bench] FP8 calibration pass", file=sys.stderr, flush=True)
+        ex.calibrate(stream)
     for k, v in bufs.items():
         ex.bind(k, v)
-    stream = torch.cuda.current_stream()
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         ex.denoise(stream=stream)
@@ -211,7 +227,7 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.weight_precision != "fp32" else "f32",
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8e4m3", "w4a16": "int4/bf16"}[cfg.weight_precision],
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,

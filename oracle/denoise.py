@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = ["sincos_embedding", "silu", "time_conditioning", "modulation", "rms_normalize",
            "ada_rms_norm", "rope", "gqa_attention", "gelu_tanh", "expert_layer",
-           "velocity", "denoise", "modulation_table", "to_f64"]
+           "velocity", "denoise", "gemm_input_amax", "modulation_table", "to_f64"]
 
 
 def to_f64(params: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
@@ -114,14 +114,23 @@ def gelu_tanh(u: np.ndarray) -> np.ndarray:
     return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
 
 
-def expert_layer(p, l: int, h: np.ndarray, c: np.ndarray, pk: np.ndarray, pv: np.ndarray, cfg) -> np.ndarray:
-    """One transformer block over h [B, H, W]; pk/pv [B, P, Hkv, d] for this layer."""
+def _note(record, l: int, i: int, x: np.ndarray) -> None:
+    """Keep the largest |x| of GEMM input i of layer l (0 qkv, 1 o, 2 gate/up, 3 down)."""
+    if record is not None and x.size:
+        record[l, i] = max(record[l, i], float(np.max(np.abs(x))))
+
+
+def expert_layer(p, l: int, h: np.ndarray, c: np.ndarray, pk: np.ndarray, pv: np.ndarray, cfg,
+                 record: Optional[np.ndarray] = None) -> np.ndarray:
+    """One transformer block over h [B, H, W]; pk/pv [B, P, Hkv, d] for this layer.
+    `record` ([L][4], optional) collects the largest |input| of each GEMM."""
     B, T, W = h.shape
     Hq, Hkv, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     P = pk.shape[1]
     pre = f"layers.{l}."
     sc, sh, g = modulation(c, p[pre + "attn_norm.mod.w"], p[pre + "attn_norm.mod.b"])
     xn = ada_rms_norm(h, sc, sh, cfg.rms_eps)
+    _note(record, l, 0, xn)
     q = (xn @ p[pre + "q.w"]).reshape(B, T, Hq, d).transpose(0, 2, 1, 3)
     k = (xn @ p[pre + "k.w"]).reshape(B, T, Hkv, d).transpose(0, 2, 1, 3)
     v = (xn @ p[pre + "v.w"]).reshape(B, T, Hkv, d).transpose(0, 2, 1, 3)
@@ -131,30 +140,35 @@ def expert_layer(p, l: int, h: np.ndarray, c: np.ndarray, pk: np.ndarray, pv: np
     K = np.concatenate([pk.transpose(0, 2, 1, 3), k], axis=2)   # [B, Hkv, P+T, d]
     V = np.concatenate([pv.transpose(0, 2, 1, 3), v], axis=2)
     o = gqa_attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, T, Hq * d)
+    _note(record, l, 1, o)
     h = h + g * (o @ p[pre + "o.w"])
     sc, sh, g = modulation(c, p[pre + "mlp_norm.mod.w"], p[pre + "mlp_norm.mod.b"])
     xn = ada_rms_norm(h, sc, sh, cfg.rms_eps)
+    _note(record, l, 2, xn)
     a = gelu_tanh(xn @ p[pre + "gate.w"]) * (xn @ p[pre + "up.w"])
+    _note(record, l, 3, a)
     return h + g * (a @ p[pre + "down.w"])
 
 
 def velocity(p, x: np.ndarray, s: Optional[np.ndarray], t: float, prefix_k: np.ndarray,
-             prefix_v: np.ndarray, cfg) -> np.ndarray:
+             prefix_v: np.ndarray, cfg, record: Optional[np.ndarray] = None) -> np.ndarray:
     """Velocity field v(x, t) [B, H, A]; prefix_k/v [L, B, P, Hkv, d]."""
     c = time_conditioning(p, t)
     h = x @ p["in_proj.w"] + p["in_proj.b"]
     if s is not None:
         h = h + s[:, None, :]
     for l in range(cfg.num_layers):
-        h = expert_layer(p, l, h, c, prefix_k[l], prefix_v[l], cfg)
+        h = expert_layer(p, l, h, c, prefix_k[l], prefix_v[l], cfg, record)
     sc, sh, _ = modulation(c, p["final_norm.mod.w"], p["final_norm.mod.b"])
     return ada_rms_norm(h, sc, sh, cfg.rms_eps) @ p["out_proj.w"] + p["out_proj.b"]
 
 
 def denoise(params, noise: np.ndarray, state: np.ndarray, prefix_k: np.ndarray,
-            prefix_v: np.ndarray, cfg, num_steps: Optional[int] = None) -> np.ndarray:
+            prefix_v: np.ndarray, cfg, num_steps: Optional[int] = None,
+            record: Optional[np.ndarray] = None) -> np.ndarray:
     """Explicit Euler from t = 1 (x = noise) to t = 0 in N equal steps of dt = -1/N.
-    Returns the action chunk [B, H, A] in float64."""
+    Returns the action chunk [B, H, A] in float64. `record` ([L][4], optional)
+    collects the largest |input| of every GEMM over all steps."""
     p = params if all(v.dtype == np.float64 for v in params.values()) else to_f64(params)
     N = cfg.num_steps if num_steps is None else num_steps
     x = np.asarray(noise, dtype=np.float64).copy()
@@ -166,8 +180,18 @@ def denoise(params, noise: np.ndarray, state: np.ndarray, prefix_k: np.ndarray,
     dt = -1.0 / N
     for k in range(N):
         t = (N - k) / N
-        x = x + dt * velocity(p, x, s, t, pk, pv, cfg)
+        x = x + dt * velocity(p, x, s, t, pk, pv, cfg, record)
     return x
+
+
+def gemm_input_amax(params, noise, state, prefix_k, prefix_v, cfg) -> np.ndarray:
+    """[L][4] largest |input| of the qkv, o, gate/up and down GEMMs of every
+    layer over one full denoise call: what an FP8 calibration pass measures
+    (FlashRT walk-through, component 6: one measurement pass records the amax
+    of every FP8 GEMM input)."""
+    rec = np.zeros((cfg.num_layers, 4))
+    denoise(params, noise, state, prefix_k, prefix_v, cfg, record=rec)
+    return rec
 
 
 def modulation_table(params, cfg, num_steps: Optional[int] = None) -> np.ndarray:

@@ -22,7 +22,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["e4m3_decode", "e4m3_encode", "e4m3_all_values", "quantise_fp8_tensor",
-           "quantise_w4", "E4M3_MAX"]
+           "quantise_w4", "dequantised_expert", "E4M3_MAX"]
 
 E4M3_MAX = 448.0
 
@@ -94,3 +94,37 @@ def quantise_w4(w: np.ndarray, group: int = 128):
     q = np.clip(np.rint((g / s32[:, None, :]).astype(np.float32)), -8, 7).astype(np.int8)
     deq = q.astype(np.float64) * s32[:, None, :].astype(np.float64)
     return q.reshape(K, N), s16, deq.reshape(K, N)
+
+
+def dequantised_expert(params, cfg):
+    """The expert's parameters with every per-layer GEMM weight replaced by
+    the float64 value its quantised form stands for (what the oracle is fed
+    for the FP8 and W4A16 experts). FP8 quantises each fused GEMM tensor as a
+    whole, [q | k | v] and [gate | up] along the output columns, so the
+    fused parts share one scale; int4 scales are per column, so fusion does
+    not matter there. Also returns the FP8 weight scales [L][4] (qkv, o,
+    gate/up, down), or None for W4A16."""
+    out = dict(params)
+    L = cfg.num_layers
+    if cfg.weight_precision == "fp8":
+        scales = np.zeros((L, 4), dtype=np.float32)
+        for l in range(L):
+            pre = f"layers.{l}."
+            groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+            for gi, names in enumerate(groups):
+                mats = [np.asarray(params[pre + n + ".w"], dtype=np.float32) for n in names]
+                _, scale, deq = quantise_fp8_tensor(np.concatenate(mats, axis=1))
+                scales[l, gi] = scale
+                c0 = 0
+                for n, m in zip(names, mats):
+                    out[pre + n + ".w"] = deq[:, c0:c0 + m.shape[1]]
+                    c0 += m.shape[1]
+        return out, scales
+    if cfg.weight_precision == "w4a16":
+        for l in range(L):
+            pre = f"layers.{l}."
+            for n in ("q", "k", "v", "o", "gate", "up", "down"):
+                _, _, deq = quantise_w4(params[pre + n + ".w"], cfg.w4_group)
+                out[pre + n + ".w"] = deq
+        return out, None
+    raise ValueError(f"{cfg.weight_precision} weights are not quantised")

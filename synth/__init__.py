@@ -21,7 +21,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 __all__ = ["ExpertConfig", "CONFIGS", "param_specs", "make_params", "make_inputs",
-           "round_to_bf16", "workload"]
+           "make_calibration_inputs", "round_to_bf16", "workload"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,6 +152,21 @@ def make_inputs(cfg: ExpertConfig, seed: int | None = None):
     noise = rng.standard_normal(size=(cfg.batch, cfg.action_horizon, cfg.action_dim), dtype=np.float32)
     state = rng.standard_normal(size=(cfg.batch, cfg.state_dim), dtype=np.float32)
     return params, pk, pv, noise, state
+
+
+def make_calibration_inputs(cfg: ExpertConfig):
+    """The inputs of an FP8 calibration pass, drawn apart from the evaluation
+    inputs: one ``PCG64(seed + 1000)`` generator, in the order prefix K,
+    prefix V, noise, state (same shapes and distributions as make_inputs)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + 1000))
+    kv_shape = (cfg.num_layers, cfg.batch, cfg.prefix_len, cfg.num_kv_heads, cfg.head_dim)
+    pk = rng.standard_normal(size=kv_shape, dtype=np.float32)
+    pv = rng.standard_normal(size=kv_shape, dtype=np.float32)
+    if cfg.act_dtype == "bf16":
+        pk, pv = round_to_bf16(pk), round_to_bf16(pv)
+    noise = rng.standard_normal(size=(cfg.batch, cfg.action_horizon, cfg.action_dim), dtype=np.float32)
+    state = rng.standard_normal(size=(cfg.batch, cfg.state_dim), dtype=np.float32)
+    return pk, pv, noise, state
 
 
 def make_noise_state(cfg: ExpertConfig, seed: int):

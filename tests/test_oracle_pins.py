@@ -389,3 +389,43 @@ def test_modulation_table_matches_per_step_conditioning():
         c = O.time_conditioning(p, t)
         m = c @ p["layers.1.mlp_norm.mod.w"] + p["layers.1.mlp_norm.mod.b"]
         np.testing.assert_allclose(tab[k, 3].reshape(-1), m, atol=1e-15)
+
+
+def test_gemm_input_amax_records_the_gemm_inputs():
+    """The calibration recorder: at N = 1, L = 1 every GEMM input can be
+    rebuilt from the oracle's public pieces; its largest |value| must be
+    what the recorder keeps."""
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["tiny_fp32"].replace(num_layers=1, num_steps=1)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    p = O.to_f64(params)
+    rec = O.gemm_input_amax(params, noise, state, pk, pv, cfg)
+    c = O.time_conditioning(p, 1.0)
+    h = noise.astype(np.float64) @ p["in_proj.w"] + p["in_proj.b"]
+    sc, sh, g = O.modulation(c, p["layers.0.attn_norm.mod.w"], p["layers.0.attn_norm.mod.b"])
+    xn = O.ada_rms_norm(h, sc, sh, cfg.rms_eps)
+    assert rec[0, 0] == np.max(np.abs(xn))
+    B, T, W = h.shape
+    d, Hq = cfg.head_dim, cfg.num_q_heads
+    q = O.rope((xn @ p["layers.0.q.w"]).reshape(B, T, Hq, d).transpose(0, 2, 1, 3), np.arange(64, 64 + T), 10000.0)
+    k = O.rope((xn @ p["layers.0.k.w"]).reshape(B, T, 1, d).transpose(0, 2, 1, 3), np.arange(64, 64 + T), 10000.0)
+    v = (xn @ p["layers.0.v.w"]).reshape(B, T, 1, d).transpose(0, 2, 1, 3)
+    K = np.concatenate([pk[0].astype(np.float64).transpose(0, 2, 1, 3), k], axis=2)
+    V = np.concatenate([pv[0].astype(np.float64).transpose(0, 2, 1, 3), v], axis=2)
+    o = O.gqa_attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, T, Hq * d)
+    np.testing.assert_allclose(rec[0, 1], np.max(np.abs(o)), rtol=1e-12)
+    h2 = h + g * (o @ p["layers.0.o.w"])
+    sc, sh, g = O.modulation(c, p["layers.0.mlp_norm.mod.w"], p["layers.0.mlp_norm.mod.b"])
+    xn2 = O.ada_rms_norm(h2, sc, sh, cfg.rms_eps)
+    np.testing.assert_allclose(rec[0, 2], np.max(np.abs(xn2)), rtol=1e-12)
+    a = O.gelu_tanh(xn2 @ p["layers.0.gate.w"]) * (xn2 @ p["layers.0.up.w"])
+    np.testing.assert_allclose(rec[0, 3], np.max(np.abs(a)), rtol=1e-12)
+
+
+def test_calibration_inputs_are_a_separate_draw():
+    from synth import CONFIGS, make_calibration_inputs, make_inputs
+    cfg = CONFIGS["tiny_fp32"]
+    _, pk, pv, noise, state = make_inputs(cfg)
+    cpk, cpv, cnoise, cstate = make_calibration_inputs(cfg)
+    assert cpk.shape == pk.shape and cpv.shape == pv.shape and cnoise.shape == noise.shape
+    assert not np.array_equal(cpk, pk) and not np.array_equal(cnoise, noise)

@@ -84,3 +84,39 @@ def test_w4_quantiser():
     w[:128, 3] = 0
     q3, s3, d3 = Q.quantise_w4(w, 128)
     assert s3[0, 3] == 1.0 and np.all(q3[:128, 3] == 0)
+
+
+def test_dequantised_expert_fp8_shares_fused_scales():
+    """FP8 quantises [q | k | v] and [gate | up] as single tensors: every
+    fused part sits on the e4m3 grid of the one scale amax(fused) / 448."""
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["tiny_fp32"].replace(weight_precision="fp8", num_layers=1)
+    params, *_ = make_inputs(cfg)
+    deq, scales = Q.dequantised_expert(params, cfg)
+    grid = np.concatenate([-Q.e4m3_all_values()[::-1], Q.e4m3_all_values()])
+    for gi, names in enumerate([["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]):
+        mats = [params[f"layers.0.{n}.w"].astype(np.float32) for n in names]
+        amax = max(float(np.max(np.abs(m))) for m in mats)
+        assert scales[0, gi] == np.float32(np.float32(amax) / np.float32(448.0))
+        for n in names:
+            codes_val = deq[f"layers.0.{n}.w"] / np.float64(scales[0, gi])
+            assert np.all(np.isin(codes_val, grid)), n
+            # nearest-grid error bound: half a step of the local spacing (<= 1/16 relative above 2^-6),
+            # plus the float32 rounding of the quotient w / scale that is encoded
+            w = params[f"layers.0.{n}.w"].astype(np.float64)
+            err = np.abs(deq[f"layers.0.{n}.w"] - w) / np.float64(scales[0, gi])
+            assert np.all(err <= np.maximum(np.abs(w) / np.float64(scales[0, gi]) / 16.0, 2.0 ** -10) * (1 + 1e-6)), n
+    # the tensor with the largest amax uses its full range
+    assert np.max(np.abs(deq["layers.0.o.w"])) == np.float64(448.0) * np.float64(scales[0, 1])
+
+
+def test_dequantised_expert_w4_is_per_matrix():
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["tiny_fp32"].replace(weight_precision="w4a16", num_layers=1)
+    params, *_ = make_inputs(cfg)
+    deq, scales = Q.dequantised_expert(params, cfg)
+    assert scales is None
+    for n in ("q", "k", "v", "o", "gate", "up", "down"):
+        _, _, d1 = Q.quantise_w4(params[f"layers.0.{n}.w"], 128)
+        assert np.array_equal(deq[f"layers.0.{n}.w"], d1), n
+    assert deq["in_proj.w"] is params["in_proj.w"]

@@ -21,6 +21,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ MFMA traits
 // Every operand fetch is 16 bytes per lane. For a 16-column tile, lane l
@@ -105,6 +106,9 @@ __device__ __forceinline__ u32x4 coh_ld16_if(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 __device__ __forceinline__ u32x2 coh_ld8_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, ok ? off : OOB, 0, CPOL_SC1);
+}
+__device__ __forceinline__ uint32_t ld2_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, ok ? off : OOB, 0, 0);
 }
 
 __device__ __forceinline__ floatx4 as_f4(u32x4 v) { return __builtin_bit_cast(floatx4, v); }

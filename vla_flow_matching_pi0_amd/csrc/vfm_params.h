@@ -45,21 +45,37 @@ struct VP {
   float* ml;               // [B*Hq*KS*64][2]  (max, sum) per split row, log2 domain
   float* part_o;           // [S_o][M][W]  K-split partial sums of the o projection
   float* part_d;           // [S_down][M][W] ... of the down projection
+  const float* qs;         // FP8 weights: [L][4 GEMMs][alpha, 1/act_scale]
+  float* amax;             // calibration: [L][4 GEMMs] largest |input| (null: off)
   unsigned* bar;           // grid-barrier words
   unsigned long long* trace;  // optional phase timeline of the persistent kernel (null: off)
 };
 
+// Kernel sets: activation type x weight format (x calibration).
+enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4 };
+constexpr int ATT_KEYS_HOST = 64;   // keys per attention split (the kernels' ATT_KEYS)
+constexpr int MAX_A_HOST = 64;      // largest action dim (the kernels' MAX_A)
+
 size_t lds_bytes(const VP& p, int act_bytes);
-hipError_t prepare_kernels(int act_bf16, int d, int lds);
-hipError_t launch_phase(const VP& p, int act_bf16, int mode, int phase, int k, int l, int grid, size_t lds,
+hipError_t prepare_kernels(int kset, int d, int lds);
+// mode 0: persistent kernel (cooperative launch), 3: persistent kernel
+// (ordinary launch), otherwise the single phase `phase` at step k, layer l.
+hipError_t launch_phase(const VP& p, int kset, int mode, int phase, int k, int l, int grid, size_t lds,
                         hipStream_t st);
-hipError_t max_cooperative_grid(int act_bf16, int d, size_t lds, int* grid);
+hipError_t max_cooperative_grid(int kset, int d, size_t lds, int* grid);
 
 // create-time preparation (vfm_prep.hip)
 hipError_t pack_weight(uint8_t* dst, int K, int Npk, const int* d_col_src, const int* d_col_idx,
                        const void* s0, int n0, const void* s1, int n1, const void* s2, int n2,
                        int src_bf16, int dst_bf16, hipStream_t st);
 hipError_t to_f32(float* dst, const void* src, size_t n, int src_bf16, hipStream_t st);
+// quantised packing (bf16 masters): fmt 0 = FP8 e4m3 per tensor (scale from
+// *amax), 1 = int4 with fp16 scales per (column, 128-K group)
+hipError_t amax_into(unsigned* out, const void* src, size_t n, int src_bf16, hipStream_t st);
+hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col_src, const int* d_col_idx,
+                         const void* s0, int n0, const void* s1, int n1, const void* s2, int n2, const unsigned* amax,
+                         hipStream_t st);
+hipError_t fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax, hipStream_t st);
 hipError_t build_mod_table(float* tab, const void* const* mod_w, const void* const* mod_b, int n_norms,
                            const void* t1w, const void* t1b, const void* t2w, const void* t2b,
                            int N, int E, int W, int src_bf16, double* scratch, hipStream_t st);

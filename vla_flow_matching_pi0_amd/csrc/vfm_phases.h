@@ -1,4 +1,6 @@
-// vfm_kernels.hip -- HIP kernels (gfx950) of the flow-matching action expert.
+// vfm_phases.h -- HIP kernels (gfx950) of the flow-matching action expert.
+// Included by one translation unit per weight format (vfm_k_*.hip), each of
+// which instantiates the kernels of its format.
 //
 // The denoise loop (PhyAI summary, "Real-Time Physical AI at the Edge,
 // Scalable Rollouts in the Cloud": pi0.5's ten Euler steps of the action
@@ -27,6 +29,7 @@
 // (component 8, kernel library). The K-split of the residual GEMMs, whose
 // partial sums the following row-parallel norm phase reduces, is ours: it
 // lets every GEMM phase use all compute units without atomics.
+#pragma once
 #include "vfm_device.h"
 #include "vfm_params.h"
 
@@ -154,7 +157,7 @@ __device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp
 // kp = -1 also initialises x from the noise and the state embedding s.
 // Thread c owns columns 4c..4c+3 of the row; every weight load is issued
 // before it is used.
-constexpr int MAX_A = 64;
+constexpr int MAX_A = MAX_A_HOST;
 template <typename T>
 __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
   const int tid = tid_opaque();
@@ -291,93 +294,174 @@ __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg,
 // linear residual GEMMs (o, down) write S partial sums that the next row
 // phase adds.
 enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3 };
-constexpr int GEMM_PASS = 4;     // k blocks loaded per wave per pass
+constexpr int GEMM_PASS = 4;     // MFMA k blocks per wave per pass
+
+// Storage format of the per-layer GEMM weights. A lane's 16-byte weight load
+// ("weight block") feeds R MFMA k blocks of K = MT<T>::KB each:
+//   WF_NATIVE  weights in the activation type (fp32 or bf16), R = 1;
+//   WF_FP8     OCP e4m3 codes with a per-tensor scale, R = 2: bytes 8r..8r+7
+//              are the fp8 operand of block r, the activations are quantised
+//              to e4m3 with the calibrated activation scale as they are
+//              loaded, and alpha = act_scale * weight_scale scales the
+//              accumulator (FlashRT walk-through, component 6, calibration);
+//   WF_W4      symmetric int4 with an fp16 scale per (column, 128-K group),
+//              R = 4: word r holds the 8 nibbles of block r, dequantised to
+//              bf16 in registers before the MFMA (the W4A16 variant of the
+//              PhyAI optimisation paragraph).
+enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2 };
+template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : WF == WF_FP8 ? 2 : 4; };
 
 // Weight fragments of one pass of one unit, held in registers. The
-// persistent kernel loads a workgroup's first pass of the next GEMM at the
-// start of the preceding phase, so the weight stream's latency is spent
-// while that phase and the barrier run.
+// persistent kernel loads a workgroup's first pass of the next GEMM while it
+// waits at the barrier before that GEMM.
 struct WPre {
   u32x4 w[2][GEMM_PASS];
+  uint32_t sc[2];          // WF_W4: the fp16 group scale of each tile's column
 };
 
 struct GemmShape {
   const uint8_t* Wp;
+  const uint8_t* Ws;       // WF_W4: scales [N/16][K/128][16] fp16, after the codes
   int K, N, nt, S, ngroups, units, nkb, KR, nkbw;
 };
 
-template <typename T, int WHICH>
+template <typename T, int WHICH, int WF>
 __device__ __forceinline__ GemmShape gemm_shape(const VP& p, int layer) {
-  constexpr int KB = MT<T>::KB;
+  constexpr int KW = MT<T>::KB * WFmt<WF>::R;   // K per weight block
   GemmShape g;
   if (WHICH == G_QKV) { g.K = p.W; g.N = (p.Hq + 2 * p.Hkv) * p.d; g.Wp = p.w_qkv[layer]; }
   else if (WHICH == G_O) { g.K = p.Hq * p.d; g.N = p.W; g.Wp = p.w_o[layer]; }
   else if (WHICH == G_GU) { g.K = p.W; g.N = 2 * p.F; g.Wp = p.w_gu[layer]; }
   else { g.K = p.F; g.N = p.W; g.Wp = p.w_down[layer]; }
+  g.Ws = g.Wp + (size_t)g.N * g.K / 2;
   g.nt = p.gp_nt[WHICH];
   g.S = p.gp_s[WHICH];
   g.ngroups = g.N / (16 * g.nt);
   g.units = g.ngroups * g.S * ((p.M + 63) / 64);
-  g.nkb = g.K / KB;
+  g.nkb = g.K / KW;
   g.KR = g.K / g.S;
-  g.nkbw = g.KR / KB / NWAVES;
+  g.nkbw = g.KR / KW / NWAVES;
   return g;
 }
 
-// Weight fragments of pass pb of unit u for this lane (zeros where the pass
-// or the tile does not exist).
-template <typename T, int WHICH>
+// Weight fragments of pass pb (in weight blocks) of unit u for this lane
+// (zeros where the pass or the tile does not exist).
+template <typename T, int WHICH, int WF>
 __device__ __forceinline__ void gemm_load_weights(const GemmShape& gs, int u, int pb, int tid, WPre& out) {
-  constexpr int KB = MT<T>::KB;
+  constexpr int R = WFmt<WF>::R, KW = MT<T>::KB * R, PW = GEMM_PASS / R;
   const int lane = tid & 63, wv = tid >> 6;
   const int ng = u % gs.ngroups, s = (u / gs.ngroups) % gs.S;
   const int t0 = ng * gs.nt;
-  const int kb0 = (s * gs.KR) / KB + wv * gs.nkbw;
+  const int kb0 = (s * gs.KR) / KW + wv * gs.nkbw;
   const auto wrs = rsrc(gs.Wp);
 #pragma unroll
-  for (int i = 0; i < GEMM_PASS; ++i) {
+  for (int i = 0; i < PW; ++i) {
     const bool ok = pb + i < gs.nkbw;
     const int kb = kb0 + pb + i;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       out.w[t][i] = ld16_if(wrs, (uint32_t)((((size_t)(t0 + t) * gs.nkb + kb) * 64 + lane) * 16), ok && t < gs.nt);
   }
+  if constexpr (WF == WF_W4) {
+    const auto srs = rsrc(gs.Ws);
+    const bool ok = pb < gs.nkbw;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      out.sc[t] = ld2_if(srs, (uint32_t)((((size_t)(t0 + t) * gs.nkb + kb0 + pb) * 16 + (lane & 15)) * 2),
+                         ok && t < gs.nt);
+  }
 }
 
-template <typename T, int WHICH>
+template <typename T, int WHICH, int WF>
 __device__ __forceinline__ void gemm_prefetch(const VP& p, int layer, int wg, WPre& out) {
-  const GemmShape gs = gemm_shape<T, WHICH>(p, layer);
+  const GemmShape gs = gemm_shape<T, WHICH, WF>(p, layer);
   const int tid = tid_opaque();
-  if (wg < gs.units) gemm_load_weights<T, WHICH>(gs, wg, 0, tid, out);
+  if (wg < gs.units) gemm_load_weights<T, WHICH, WF>(gs, wg, 0, tid, out);
 }
 
-template <typename T, int WHICH>
+template <typename T, int WHICH, int WF>
 struct PrefetchHook {
   const VP& p;
   int layer, wg;
   WPre& out;
-  __device__ __forceinline__ void operator()() const { gemm_prefetch<T, WHICH>(p, layer, wg, out); }
+  __device__ __forceinline__ void operator()() const { gemm_prefetch<T, WHICH, WF>(p, layer, wg, out); }
 };
 
-template <typename T, int WHICH, bool PRE>
+// 8 bf16 activations -> 8 e4m3 codes of x * inv_scale, saturated to +-448
+// (the conversion instruction rounds to nearest even; it would give NaN
+// beyond the largest finite value, hence the clamp).
+__device__ __forceinline__ long act_to_fp8(u32x4 a, float inv) {
+  uint32_t wds[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t wd = a[2 * h + q];
+      f[2 * q] = __builtin_bit_cast(float, wd << 16) * inv;
+      f[2 * q + 1] = __builtin_bit_cast(float, wd & 0xffff0000u) * inv;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -448.0f), 448.0f);
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], v, true);
+    wds[h] = (uint32_t)v;
+  }
+  return (long)(((unsigned long long)wds[1] << 32) | wds[0]);
+}
+
+// 8 signed nibbles (element e in bits 4e..4e+3) times an fp16 scale -> 8 bf16.
+__device__ __forceinline__ u32x4 w4_to_bf16(uint32_t wd, uint32_t scale_bits) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)(((int)(wd << (28 - 4 * e))) >> 28) * s;
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+// Largest |x| of a lane's 16-byte activation fragment (calibration).
+template <typename T>
+__device__ __forceinline__ float frag_amax(u32x4 a) {
+  float m = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wd = a[q];
+      m = fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, wd << 16)), fabsf(__builtin_bit_cast(float, wd & 0xffff0000u))));
+    }
+  } else {
+    const floatx4 f = as_f4(a);
+    m = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
+  }
+  return m;
+}
+
+template <typename T, int WHICH, bool PRE, int WF = WF_NATIVE, bool CAL = false>
 __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg, const WPre& pre) {
   const int tid = tid_opaque();
-  constexpr int E = MT<T>::E, KB = MT<T>::KB;
+  constexpr int E = MT<T>::E, KM = MT<T>::KB, R = WFmt<WF>::R, KW = KM * R, PW = GEMM_PASS / R;
+  static_assert(WF == WF_NATIVE || sizeof(T) == 2, "quantised weights run with bf16 activations");
   uint8_t* sl = slab(p, step, layer);
   const T* A;
   if (WHICH == G_QKV) A = (const T*)(sl + p.off_xna);
   else if (WHICH == G_O) A = (const T*)(sl + p.off_attn);
   else if (WHICH == G_GU) A = (const T*)(sl + p.off_xnm);
   else A = (const T*)(sl + p.off_act);
-  const GemmShape gs = gemm_shape<T, WHICH>(p, layer);
+  const GemmShape gs = gemm_shape<T, WHICH, WF>(p, layer);
   const int K = gs.K, nt = gs.nt, S = gs.S, ngroups = gs.ngroups, units = gs.units, KR = gs.KR, nkbw = gs.nkbw;
   const int Mpad = ((p.M + 63) / 64) * 64;
   const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  float alpha = 1.0f, inv_act = 1.0f;
+  if constexpr (WF == WF_FP8) {
+    alpha = p.qs[(layer * 4 + WHICH) * 2];
+    inv_act = p.qs[(layer * 4 + WHICH) * 2 + 1];
+  }
+  float amax = 0.f;
   floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NWAVES][2][4][64]
   for (int u = wg; u < units; u += nwg) {
     const int ng = u % ngroups, rest = u / ngroups, s = rest % S, mt = rest / S;
     const int t0 = ng * nt, m0 = mt * 64;
-    const int kb0 = (s * KR) / KB + wv * nkbw;
+    const int kb0 = (s * KR) / KW + wv * nkbw;
     floatx4 acc[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -387,31 +471,61 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
 #pragma unroll
     for (int st = 0; st < 4; ++st) rowok[st] = m0 + st * 16 + c16 < p.M;
     const auto ars = rsrc(A);
-    for (int pb = 0; pb < nkbw; pb += GEMM_PASS) {
+    for (int pb = 0; pb < nkbw; pb += PW) {
       WPre wl;
       u32x4 ar[4][GEMM_PASS];
       if (PRE && u == wg && pb == 0) wl = pre;
-      else gemm_load_weights<T, WHICH>(gs, u, pb, tid, wl);
+      else gemm_load_weights<T, WHICH, WF>(gs, u, pb, tid, wl);
 #pragma unroll
-      for (int i = 0; i < GEMM_PASS; ++i) {
+      for (int j = 0; j < GEMM_PASS; ++j) {
+        const int i = j / R, r = j % R;
         const bool ok = pb + i < nkbw;
-        const int kb = kb0 + pb + i;
+        const int k = (kb0 + pb + i) * KW + r * KM + g * E;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const size_t row = (size_t)(m0 + st * 16 + c16);
-          const int k = kb * KB + g * E;
           // act is tile-major [K/16][Mpad][16]; the others are row-major [M][K]
           const size_t off = WHICH == G_DOWN ? ((size_t)(k / 16) * Mpad + row) * 16 + k % 16 : row * K + k;
-          ar[st][i] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
+          ar[st][j] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
         }
       }
+      if constexpr (CAL) {
 #pragma unroll
-      for (int i = 0; i < GEMM_PASS; ++i)
+        for (int j = 0; j < GEMM_PASS; ++j)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+          for (int st = 0; st < 4; ++st) amax = fmaxf(amax, frag_amax<T>(ar[st][j]));
+      }
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            if (t < nt) acc[t][st] = MT<T>::mma(wl.w[t][i], ar[st][i], acc[t][st]);
+      for (int j = 0; j < GEMM_PASS; ++j) {
+        const int i = j / R, r = j % R;
+        if constexpr (WF == WF_NATIVE) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              if (t < nt) acc[t][st] = MT<T>::mma(wl.w[t][i], ar[st][j], acc[t][st]);
+        } else if constexpr (WF == WF_FP8) {
+          long a8[4];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) a8[st] = act_to_fp8(ar[st][j], inv_act);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const i64x2 w2 = __builtin_bit_cast(i64x2, wl.w[t][i]);
+            const long w8 = (long)w2[r];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              if (t < nt) acc[t][st] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w8, a8[st], acc[t][st], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 wb = w4_to_bf16(wl.w[t][i][r], wl.sc[t]);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              if (t < nt) acc[t][st] = MT<T>::mma(wb, ar[st][j], acc[t][st]);
+          }
+        }
+      }
     }
     // sum the 8 waves' partial tiles through LDS
     __syncthreads();
@@ -427,6 +541,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
       floatx4 v = {0, 0, 0, 0};
 #pragma unroll
       for (int w2 = 0; w2 < NWAVES; ++w2) v += red[((w2 * 2 + t) * 4 + st) * 64 + lane];
+      if constexpr (WF == WF_FP8) v *= alpha;
       const int gm = m0 + st * 16 + c16;
       const int tile = t0 + t;
       if (gm < p.M) {
@@ -477,6 +592,14 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
       }
     }
   }
+  if constexpr (CAL) {
+    // calibration: the largest |activation| this workgroup loaded, per GEMM input
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (lane == 0 && amax > 0.f)
+      __hip_atomic_fetch_max(reinterpret_cast<unsigned*>(p.amax) + layer * 4 + WHICH, __builtin_bit_cast(unsigned, amax),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ============================================================ attention
@@ -490,7 +613,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
 // Scores are computed transposed, S^T = K Q^T, so a lane holds 8 keys of one
 // query and the row max / sum need only two cross-lane exchanges; the
 // probabilities then feed the PV MFMA directly from registers.
-constexpr int ATT_KEYS = 64;   // keys per split
+constexpr int ATT_KEYS = ATT_KEYS_HOST;   // keys per split
 
 template <typename T, int D, int MODE>   // MODE 0: prefix keys only, 1: chunk keys only, 2: both
 __device__ __forceinline__ void attn_load_kv(const VP& p, int tid, int b, int kvh, int s0, int s1,
@@ -715,7 +838,7 @@ __device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int
 
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
-template <typename T, int D>
+template <typename T, int D, int WF>
 __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
   const int wg = blockIdx.x, nwg = gridDim.x;
@@ -724,7 +847,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   // The next GEMM's first weight pass is loaded while the workgroup waits at
   // the barrier before it: weights do not depend on the other workgroups.
 #define VFM_BAR_PF(WHICH, LAYER) \
-  do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH>{p, LAYER, wg, pre})) return; } while (0)
+  do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
   ph_boundary<T>(p, -1, 0, wg, nwg);
   if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
@@ -735,19 +858,19 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         ph_rn<T>(p, k, l, false, wg, nwg);
         VFM_BAR_PF(G_QKV, l);
       }
-      ph_gemm<T, G_QKV, true>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR();
       ph_attn<T, D>(p, k, l, wg, nwg);
       VFM_BAR();
       ph_combine<T>(p, k, l, wg, nwg);
       VFM_BAR_PF(G_O, l);
-      ph_gemm<T, G_O, true>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_O, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR();
       ph_rn<T>(p, k, l, true, wg, nwg);
       VFM_BAR_PF(G_GU, l);
-      ph_gemm<T, G_GU, true>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_GU, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR_PF(G_DOWN, l);
-      ph_gemm<T, G_DOWN, true>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_DOWN, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR();
     }
     ph_boundary<T>(p, k, k + 1, wg, nwg);
@@ -758,113 +881,107 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
 #undef VFM_BAR
 }
 
-// One phase per launch (eager / graph modes); one kernel symbol per phase so
-// a kernel trace attributes time to phases.
-template <typename T, int D, int PH>
+// One phase per launch (eager / graph modes, and the calibration pass); one
+// kernel symbol per phase so a kernel trace attributes time to phases.
+template <typename T, int D, int PH, int WF, bool CAL>
 __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
   const int wg = blockIdx.x, nwg = gridDim.x;
   if constexpr (PH == PH_BOUNDARY) ph_boundary<T>(p, k - 1, k, wg, nwg);
   else if constexpr (PH == PH_RN_ATTN) ph_rn<T>(p, k, l, false, wg, nwg);
-  else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV, false>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_ATTN) ph_attn<T, D>(p, k, l, wg, nwg);
   else if constexpr (PH == PH_COMBINE) ph_combine<T>(p, k, l, wg, nwg);
-  else if constexpr (PH == PH_O) ph_gemm<T, G_O, false>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_O) ph_gemm<T, G_O, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_RN_MLP) ph_rn<T>(p, k, l, true, wg, nwg);
-  else if constexpr (PH == PH_GU) ph_gemm<T, G_GU, false>(p, k, l, wg, nwg, WPre{});
-  else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN, false>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_GU) ph_gemm<T, G_GU, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
 }
 
-template <typename T, int D>
+template <typename T, int D, int WF, bool CAL>
 __host__ const void* phase_kernel(int ph) {
   switch (ph) {
-    case PH_BOUNDARY: return (const void*)&k_phase<T, D, PH_BOUNDARY>;
-    case PH_RN_ATTN: return (const void*)&k_phase<T, D, PH_RN_ATTN>;
-    case PH_QKV: return (const void*)&k_phase<T, D, PH_QKV>;
-    case PH_ATTN: return (const void*)&k_phase<T, D, PH_ATTN>;
-    case PH_COMBINE: return (const void*)&k_phase<T, D, PH_COMBINE>;
-    case PH_O: return (const void*)&k_phase<T, D, PH_O>;
-    case PH_RN_MLP: return (const void*)&k_phase<T, D, PH_RN_MLP>;
-    case PH_GU: return (const void*)&k_phase<T, D, PH_GU>;
-    default: return (const void*)&k_phase<T, D, PH_DOWN>;
+    case PH_BOUNDARY: return (const void*)&k_phase<T, D, PH_BOUNDARY, WF, CAL>;
+    case PH_RN_ATTN: return (const void*)&k_phase<T, D, PH_RN_ATTN, WF, CAL>;
+    case PH_QKV: return (const void*)&k_phase<T, D, PH_QKV, WF, CAL>;
+    case PH_ATTN: return (const void*)&k_phase<T, D, PH_ATTN, WF, CAL>;
+    case PH_COMBINE: return (const void*)&k_phase<T, D, PH_COMBINE, WF, CAL>;
+    case PH_O: return (const void*)&k_phase<T, D, PH_O, WF, CAL>;
+    case PH_RN_MLP: return (const void*)&k_phase<T, D, PH_RN_MLP, WF, CAL>;
+    case PH_GU: return (const void*)&k_phase<T, D, PH_GU, WF, CAL>;
+    default: return (const void*)&k_phase<T, D, PH_DOWN, WF, CAL>;
   }
 }
 
-}  // namespace vfm
-
-// ============================================================ host-side launch table
-namespace vfm {
-
-size_t lds_bytes(const VP& p, int act_bytes) {
-  const size_t gemm = (size_t)NWAVES * 2 * 4 * 64 * 16;
-  const size_t epc = 16 / act_bytes;
-  const size_t attn = ((size_t)ATT_KEYS * (p.d + epc) + (size_t)p.d * (ATT_KEYS + epc)) * act_bytes;
-  const size_t row = ((size_t)NWAVES + p.W + 4 * NTH + MAX_A) * 4;
-  size_t m = gemm > attn ? gemm : attn;
-  return m > row ? m : row;
-}
-
-template <typename T, int D>
-static hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, size_t lds, hipStream_t st) {
-  if (mode == 0) {
-    void* args[] = {const_cast<VP*>(&p)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(NTH), args,
-                                      (unsigned)lds, st);
-  }
-  if (mode == 3) {   // same kernel, ordinary launch (grid sized by the occupancy query)
-    void* args[] = {const_cast<VP*>(&p)};
-    return hipLaunchKernel(reinterpret_cast<void*>(&k_persistent<T, D>), dim3(grid), dim3(NTH), args, lds, st);
+// ============================================================ host-side launch helpers
+// mode 0: persistent kernel, cooperative launch; 3: persistent kernel,
+// ordinary launch of the same grid; otherwise one phase. The calibration
+// variant (CAL) has phase kernels only.
+template <typename T, int D, int WF, bool CAL>
+hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, size_t lds, hipStream_t st) {
+  if (mode == 0 || mode == 3) {
+    if constexpr (CAL) {
+      return hipErrorInvalidValue;
+    } else {
+      void* args[] = {const_cast<VP*>(&p)};
+      const void* f = reinterpret_cast<const void*>(&k_persistent<T, D, WF>);
+      if (mode == 0) return hipLaunchCooperativeKernel(f, dim3(grid), dim3(NTH), args, (unsigned)lds, st);
+      return hipLaunchKernel(f, dim3(grid), dim3(NTH), args, lds, st);
+    }
   }
   void* args[] = {const_cast<VP*>(&p), &k, &l};
-  return hipLaunchKernel(phase_kernel<T, D>(phase), dim3(grid), dim3(NTH), args, lds, st);
+  return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase), dim3(grid), dim3(NTH), args, lds, st);
 }
 
-template <typename T, int D>
-static hipError_t set_lds_limit(int bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+template <typename T, int D, int WF, bool CAL>
+hipError_t set_lds_limit(int bytes) {
+  hipError_t e = hipSuccess;
+  if constexpr (!CAL)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph)
-    e = hipFuncSetAttribute(phase_kernel<T, D>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   return e;
 }
 
-hipError_t prepare_kernels(int act_bf16, int d, int lds) {
-  if (act_bf16) {
-    if (d == 64) return set_lds_limit<bf16, 64>(lds);
-    if (d == 128) return set_lds_limit<bf16, 128>(lds);
-    return set_lds_limit<bf16, 256>(lds);
+template <typename T, int D, int WF, bool CAL>
+hipError_t occupancy(size_t lds, int* per_cu) {
+  if constexpr (CAL) {
+    *per_cu = 0;
+    return hipErrorInvalidValue;
+  } else {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
+                                                        NTH, lds);
   }
-  if (d == 64) return set_lds_limit<float, 64>(lds);
-  if (d == 128) return set_lds_limit<float, 128>(lds);
-  return set_lds_limit<float, 256>(lds);
 }
 
-// mode 0 = persistent (phase ignored), 1 = one phase.
-hipError_t launch_phase(const VP& p, int act_bf16, int mode, int phase, int k, int l, int grid, size_t lds,
-                        hipStream_t st) {
-  if (act_bf16) {
-    if (p.d == 64) return launch_one<bf16, 64>(p, mode, phase, k, l, grid, lds, st);
-    if (p.d == 128) return launch_one<bf16, 128>(p, mode, phase, k, l, grid, lds, st);
-    return launch_one<bf16, 256>(p, mode, phase, k, l, grid, lds, st);
+// The entry points of one kernel set (activation type T, weight format WF,
+// calibration flag CAL) over the head dimensions Ds it is built for.
+template <typename T, int WF, bool CAL, int... Ds>
+struct KernelSet {
+  static hipError_t launch(const VP& p, int mode, int phase, int k, int l, int grid, size_t lds, hipStream_t st) {
+    hipError_t e = hipErrorInvalidValue;
+    ((p.d == Ds ? (void)(e = launch_one<T, Ds, WF, CAL>(p, mode, phase, k, l, grid, lds, st)) : (void)0), ...);
+    return e;
   }
-  if (p.d == 64) return launch_one<float, 64>(p, mode, phase, k, l, grid, lds, st);
-  if (p.d == 128) return launch_one<float, 128>(p, mode, phase, k, l, grid, lds, st);
-  return launch_one<float, 256>(p, mode, phase, k, l, grid, lds, st);
-}
+  static hipError_t prepare(int d, int lds) {
+    hipError_t e = hipErrorInvalidValue;
+    ((d == Ds ? (void)(e = set_lds_limit<T, Ds, WF, CAL>(lds)) : (void)0), ...);
+    return e;
+  }
+  static hipError_t occupancy_of(int d, size_t lds, int* per_cu) {
+    hipError_t e = hipErrorInvalidValue;
+    ((d == Ds ? (void)(e = occupancy<T, Ds, WF, CAL>(lds, per_cu)) : (void)0), ...);
+    return e;
+  }
+};
 
-hipError_t max_cooperative_grid(int act_bf16, int d, size_t lds, int* grid) {
-  const void* f;
-  if (act_bf16) f = d == 64 ? (const void*)&k_persistent<bf16, 64> : d == 128 ? (const void*)&k_persistent<bf16, 128> : (const void*)&k_persistent<bf16, 256>;
-  else f = d == 64 ? (const void*)&k_persistent<float, 64> : d == 128 ? (const void*)&k_persistent<float, 128> : (const void*)&k_persistent<float, 256>;
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, NTH, lds);
-  if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  *grid = per_cu >= 1 ? cus : 0;
-  return hipSuccess;
-}
+#define VFM_DEFINE_KERNEL_SET(NAME, ...)                                                                             \
+  hipError_t NAME##_launch(const VP& p, int mode, int phase, int k, int l, int grid, size_t lds, hipStream_t st) { \
+    return KernelSet<__VA_ARGS__>::launch(p, mode, phase, k, l, grid, lds, st);                                    \
+  }                                                                                                                \
+  hipError_t NAME##_prepare(int d, int lds) { return KernelSet<__VA_ARGS__>::prepare(d, lds); }                    \
+  hipError_t NAME##_occupancy(int d, size_t lds, int* per_cu) {                                                    \
+    return KernelSet<__VA_ARGS__>::occupancy_of(d, lds, per_cu);                                                   \
+  }
 
 }  // namespace vfm

@@ -59,6 +59,156 @@ hipError_t pack_weight(uint8_t* dst, int K, int Npk, const int* d_col_src, const
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ quantised weights
+// OCP e4m3 ("fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+// infinities, largest finite 448 (code 0x7E). Encoding rounds to nearest,
+// ties to the even code, and saturates; -0 and values that round to zero
+// encode as 0x00.
+__device__ uint8_t e4m3_encode(float x) {
+  const float a = fminf(fabsf(x), 448.0f);
+  int code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
+    code = (int)rintf(a * 512.0f);           // 0..8 (8 = 2^-6, the first normal)
+  } else {
+    int e;
+    const float m = frexpf(a, &e);           // a = m 2^e, m in [0.5, 1)
+    int q = (int)rintf((m * 2.0f - 1.0f) * 8.0f);
+    int ex = e - 1;
+    if (q == 8) { q = 0; ++ex; }
+    code = ((ex + 7) << 3) | q;
+    if (code > 0x7E) code = 0x7E;
+  }
+  if (code != 0 && x < 0.0f) code |= 0x80;
+  return (uint8_t)code;
+}
+
+__device__ float e4m3_decode(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const float v = e == 0 ? (float)m * 0.001953125f : ldexpf(1.0f + (float)m * 0.125f, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+// Largest |w| over n elements, max-reduced into *out (float bits; the values
+// are non-negative, so their bit patterns order like the values).
+template <typename TS>
+__global__ void k_amax(const TS* src, size_t n, unsigned* out) {
+  float m = 0.0f;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(to_f(src[i])));
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_max(out, __builtin_bit_cast(unsigned, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t amax_into(unsigned* out, const void* src, size_t n, int src_bf16, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  if (src_bf16) hipLaunchKernelGGL((k_amax<bf16>), dim3(blocks), dim3(256), 0, st, (const bf16*)src, n, out);
+  else hipLaunchKernelGGL((k_amax<float>), dim3(blocks), dim3(256), 0, st, (const float*)src, n, out);
+  return hipGetLastError();
+}
+
+// FP8 packing: one thread per (tile, 64-K block, lane); byte 8r + e of the
+// lane's 16 bytes is k = 64 kb + 32 r + 8 g + e, g = lane / 16. The tensor
+// scale is amax / 448 (1 if amax is 0); the code of w is e4m3(w / scale).
+template <typename TS>
+__global__ void k_pack_fp8(uint8_t* dst, int K, int Npk, const int* col_src, const int* col_idx, const TS* s0, int n0,
+                           const TS* s1, int n1, const TS* s2, int n2, const unsigned* amax_bits) {
+  const float amax = __builtin_bit_cast(float, *amax_bits);
+  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const int nkb = K / 64;
+  const size_t total = (size_t)(Npk / 16) * nkb * 64;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    const int kb = (int)((idx / 64) % nkb);
+    const int t = (int)(idx / 64 / nkb);
+    const int pc = t * 16 + (lane & 15), g = lane >> 4;
+    const int sid = col_src[pc], col = col_idx[pc];
+    const TS* src = sid == 0 ? s0 : sid == 1 ? s1 : s2;
+    const int ld = sid == 0 ? n0 : sid == 1 ? n1 : n2;
+    uint8_t out[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int k = kb * 64 + (e / 8) * 32 + 8 * g + e % 8;
+      out[e] = e4m3_encode(to_f(src[(size_t)k * ld + col]) / scale);
+    }
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = *reinterpret_cast<const u32x4*>(out);
+  }
+}
+
+// int4 packing: one thread per (tile, 128-K group, lane). The lane's column
+// gets s = fp16(amax / 7) over the group (1 if that is 0) and
+// q = clip(rint(w / s), -8, 7); nibble e (bits 4(e%8).. of word e/8) is
+// k = 128 kb + 32 (e / 8) + 8 g + e % 8. Scales follow the codes:
+// [N/16][K/128][16] fp16, written by the g = 0 lanes.
+template <typename TS>
+__global__ void k_pack_w4(uint8_t* dst, int K, int Npk, const int* col_src, const int* col_idx, const TS* s0, int n0,
+                          const TS* s1, int n1, const TS* s2, int n2) {
+  const int nkb = K / 128;
+  const size_t total = (size_t)(Npk / 16) * nkb * 64;
+  uint16_t* scales = reinterpret_cast<uint16_t*>(dst + (size_t)Npk * K / 2);
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    const int kb = (int)((idx / 64) % nkb);
+    const int t = (int)(idx / 64 / nkb);
+    const int pc = t * 16 + (lane & 15), g = lane >> 4;
+    const int sid = col_src[pc], col = col_idx[pc];
+    const TS* src = sid == 0 ? s0 : sid == 1 ? s1 : s2;
+    const int ld = sid == 0 ? n0 : sid == 1 ? n1 : n2;
+    float amax = 0.0f;
+    for (int k = kb * 128; k < kb * 128 + 128; ++k) amax = fmaxf(amax, fabsf(to_f(src[(size_t)k * ld + col])));
+    _Float16 s16 = (_Float16)(amax / 7.0f);
+    if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
+    const float s = (float)s16;
+    uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int k = kb * 128 + (e / 8) * 32 + 8 * g + e % 8;
+      const float q = fminf(fmaxf(rintf(to_f(src[(size_t)k * ld + col]) / s), -8.0f), 7.0f);
+      wd[e / 8] |= ((uint32_t)(int)q & 15u) << (4 * (e % 8));
+    }
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    if (g == 0) scales[((size_t)t * nkb + kb) * 16 + (lane & 15)] = __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
+// Calibration: the bf16 packed stream (32-K blocks) of an FP8 packed weight,
+// holding decode(code) * scale rounded to bf16.
+__global__ void k_fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax_bits) {
+  const float amax = __builtin_bit_cast(float, *amax_bits);
+  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const int nkb32 = K / 32, nkb64 = K / 64;
+  const size_t total = (size_t)(Npk / 16) * nkb32 * 64;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    const int kb = (int)((idx / 64) % nkb32);
+    const int t = (int)(idx / 64 / nkb32);
+    const uint8_t* in = src + (((size_t)t * nkb64 + kb / 2) * 64 + lane) * 16 + (kb % 2) * 8;
+    bf16 out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (bf16)(e4m3_decode(in[e]) * scale);
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = *reinterpret_cast<const u32x4*>(out);
+  }
+}
+
+hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col_src, const int* d_col_idx,
+                         const void* s0, int n0, const void* s1, int n1, const void* s2, int n2, const unsigned* amax,
+                         hipStream_t st) {
+  const int blocks = 1024;
+  if (fmt == 0)
+    hipLaunchKernelGGL((k_pack_fp8<bf16>), dim3(blocks), dim3(256), 0, st, dst, K, Npk, d_col_src, d_col_idx,
+                       (const bf16*)s0, n0, (const bf16*)s1, n1, (const bf16*)s2, n2, amax);
+  else
+    hipLaunchKernelGGL((k_pack_w4<bf16>), dim3(blocks), dim3(256), 0, st, dst, K, Npk, d_col_src, d_col_idx,
+                       (const bf16*)s0, n0, (const bf16*)s1, n1, (const bf16*)s2, n2);
+  return hipGetLastError();
+}
+
+hipError_t fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax, hipStream_t st) {
+  hipLaunchKernelGGL(k_fp8_to_bf16_packed, dim3(1024), dim3(256), 0, st, dst, src, K, Npk, amax);
+  return hipGetLastError();
+}
+
 template <typename TS>
 __global__ void k_to_f32(float* dst, const TS* src, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)

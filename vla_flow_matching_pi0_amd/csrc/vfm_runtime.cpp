@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -57,8 +58,15 @@ struct ColMap {
 
 struct vfm_expert {
   vfm_config cfg{};
-  int act_bf16 = 0;       // activations / packed weights are bf16 (else f32)
+  int act_bf16 = 0;       // activations are bf16 (else f32)
   int src_bf16 = 0;       // master weights are bf16 (else f32)
+  int wprec = VFM_W_FP32; // storage of the per-layer GEMM weights
+  int kset = vfm::KS_F32; // kernel set of the hot path
+  int KW = 16;            // K per 16-byte weight block of a lane (16 f32, 32 bf16, 64 fp8, 128 int4)
+  unsigned* wamax = nullptr;        // FP8: [L][4] largest |weight| of each fused tensor (device, float bits)
+  std::vector<float> wscale;        // FP8: [L][4] weight scales
+  std::vector<float> act_scale;     // FP8: [L][4] activation scales (empty until calibrated or set)
+  float* qs = nullptr;              // FP8: device [L][4][alpha, 1/act_scale]
   int L = 0, W = 0, Hq = 0, Hkv = 0, d = 0, F = 0, H = 0, A = 0, S = 0, E = 0, N = 0;
   int maxB = 0, maxP = 0, KSmax = 0;
   std::vector<void*> allocs;
@@ -101,6 +109,21 @@ struct vfm_expert {
 
 namespace {
 
+// Host decoders of the packed formats (export only).
+float e4m3_value(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const float v = e == 0 ? (float)m * 0.001953125f : std::ldexp(1.0f + (float)m * 0.125f, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+float half_value(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 1023;
+  float v;
+  if (e == 0) v = std::ldexp((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp(1.0f + (float)m / 1024.0f, e - 15);
+  return (h & 0x8000) ? -v : v;
+}
+
 int elem_bytes(int dt) { return dt == VFM_F32 ? 4 : dt == VFM_BF16 || dt == VFM_F16 ? 2 : 1; }
 
 vfm_status validate_config(const vfm_config* c) {
@@ -141,8 +164,15 @@ vfm_status validate_config(const vfm_config* c) {
     return fail(VFM_E_INVALID_ARG, "fp32 weights need act_dtype VFM_F32");
   if (c->weight_precision != VFM_W_FP32 && c->act_dtype != VFM_BF16)
     return fail(VFM_E_INVALID_ARG, "16-bit and quantised weights need act_dtype VFM_BF16");
-  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16)
-    return fail(VFM_E_UNSUPPORTED, "weight precision %d is not built into this library yet", c->weight_precision);
+  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16) {
+    // every wave of a GEMM workgroup takes at least one 16-byte weight block
+    const int span = (c->weight_precision == VFM_W_FP8 ? 64 : 128) * (vfm::NTHREADS / 64);
+    if (c->width % span || (c->num_q_heads * c->head_dim) % span || c->mlp_dim % span)
+      return fail(VFM_E_INVALID_ARG, "quantised weights need width, num_q_heads * head_dim and mlp_dim to be "
+                  "multiples of %d", span);
+    if (c->weight_precision == VFM_W_W4A16 && c->w4_group_size != 128)
+      return fail(VFM_E_UNSUPPORTED, "w4_group_size %d: only 128 is built", c->w4_group_size);
+  }
   return VFM_OK;
 }
 
@@ -280,9 +310,9 @@ int phase_grid(const VP& p, int phase) {
   return (int)units;
 }
 
-hipError_t enqueue_phases(vfm_expert* x, const VP& p, hipStream_t st) {
+hipError_t enqueue_phases(vfm_expert* x, const VP& p, int kset, hipStream_t st) {
   hipError_t e;
-  auto run = [&](int ph, int k, int l) { return vfm::launch_phase(p, x->act_bf16, 1, ph, k, l, phase_grid(p, ph), x->lds, st); };
+  auto run = [&](int ph, int k, int l) { return vfm::launch_phase(p, kset, 1, ph, k, l, phase_grid(p, ph), x->lds, st); };
   if ((e = run(vfm::PH_BOUNDARY, 0, 0)) != hipSuccess) return e;
   for (int k = 0; k < p.N; ++k) {
     for (int l = 0; l < p.L; ++l) {
@@ -311,6 +341,45 @@ void plan_gemm(int M, int N, int K, int KB, int nwg, bool linear, int* nt, int* 
 
 }  // namespace
 
+// The launch parameter block of one call: shapes, weights, workspace,
+// buffers and the GEMM plan for the expert's weight format.
+vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const float* state, float* actions) {
+  p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
+  p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
+  p.kps = 64;                       // keys per attention split
+  p.KS = (P + x->H + 63) / 64;
+  p.eps = x->cfg.rms_eps;
+  for (int l = 0; l < x->L; ++l) {
+    p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
+  }
+  p.in_w = x->in_w; p.in_b = x->in_b; p.st_w = x->st_w; p.st_b = x->st_b; p.out_w = x->out_w; p.out_b = x->out_b;
+  p.mod = x->mod; p.rope = x->rope;
+  p.prefix_k = x->prefix_k.ptr; p.prefix_v = x->prefix_v.ptr;
+  p.noise = noise; p.state = state; p.x = actions;
+  p.s_emb = x->s_emb; p.h = x->h; p.part_o = x->part_o; p.part_d = x->part_d; p.opart = x->opart; p.ml = x->ml;
+  p.ring = x->ring; p.slab = x->slab; p.off_xna = x->off_xna; p.off_q = x->off_q; p.off_k = x->off_k; p.off_v = x->off_v;
+  p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
+  p.trace = x->mode == 0 ? x->trace : nullptr;
+
+  {
+    int nwg = x->coop_grid;
+    if (nwg == 0) {
+      HIPCHK(vfm::max_cooperative_grid(x->kset, x->d, x->lds, &x->coop_grid));
+      if (x->coop_grid == 0) return fail(VFM_E_HIP, "persistent kernel does not fit on a compute unit");
+      nwg = x->coop_grid;
+    }
+    const int KB = x->KW;
+    const int Ks[4] = {x->W, x->Hq * x->d, x->W, x->F};
+    const int Ns[4] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W};
+    for (int i = 0; i < 4; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i == 1 || i == 3, &p.gp_nt[i], &p.gp_s[i]);
+    p.S_o = p.gp_s[1];
+    p.S_down = p.gp_s[3];
+  }
+  p.qs = x->qs;
+  p.amax = nullptr;
+  return VFM_OK;
+}
+
 extern "C" {
 
 int vfm_abi_version(void) { return VFM_ABI_VERSION; }
@@ -329,6 +398,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   tmp.cfg = *cfg;
   tmp.act_bf16 = cfg->act_dtype == VFM_BF16;
   tmp.src_bf16 = cfg->weight_precision != VFM_W_FP32;
+  tmp.wprec = cfg->weight_precision;
+  tmp.kset = tmp.wprec == VFM_W_FP32 ? vfm::KS_F32 : tmp.wprec == VFM_W_BF16 ? vfm::KS_BF16
+           : tmp.wprec == VFM_W_FP8 ? vfm::KS_FP8 : vfm::KS_W4;
+  tmp.KW = tmp.wprec == VFM_W_FP32 ? 16 : tmp.wprec == VFM_W_BF16 ? 32 : tmp.wprec == VFM_W_FP8 ? 64 : 128;
   tmp.L = cfg->num_layers; tmp.W = cfg->width; tmp.Hq = cfg->num_q_heads; tmp.Hkv = cfg->num_kv_heads;
   tmp.d = cfg->head_dim; tmp.F = cfg->mlp_dim; tmp.H = cfg->action_horizon; tmp.A = cfg->action_dim;
   tmp.S = cfg->state_dim; tmp.E = cfg->time_emb_dim; tmp.N = cfg->num_steps;
@@ -393,23 +466,76 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     fail(VFM_E_OOM, "column map upload failed");
     return bail(VFM_E_OOM);
   }
+  // packed bytes of a K x N weight (W4: codes then fp16 group scales)
+  auto wbytes = [&](size_t K, size_t N) -> size_t {
+    if (x->wprec == VFM_W_FP8) return K * N;
+    if (x->wprec == VFM_W_W4A16) return K * N / 2 + (K / 128) * N * 2;
+    return K * N * ab;
+  };
+  if (x->wprec == VFM_W_FP8) {
+    x->wamax = (unsigned*)x->dalloc((size_t)std::max(L, 1) * 4 * 4);
+    if (!x->wamax) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
+    if (hipMemsetAsync(x->wamax, 0, (size_t)std::max(L, 1) * 16, s) != hipSuccess) { fail(VFM_E_HIP, "memset"); return bail(VFM_E_HIP); }
+  }
   for (int l = 0; l < L; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
-    uint8_t* wq = (uint8_t*)x->dalloc((size_t)W * nqkv * ab);
-    uint8_t* wo = (uint8_t*)x->dalloc((size_t)Hq * d * W * ab);
-    uint8_t* wg = (uint8_t*)x->dalloc((size_t)W * 2 * F * ab);
-    uint8_t* wd = (uint8_t*)x->dalloc((size_t)F * W * ab);
+    uint8_t* wq = (uint8_t*)x->dalloc(wbytes(W, nqkv));
+    uint8_t* wo = (uint8_t*)x->dalloc(wbytes((size_t)Hq * d, W));
+    uint8_t* wg = (uint8_t*)x->dalloc(wbytes(W, 2 * (size_t)F));
+    uint8_t* wd = (uint8_t*)x->dalloc(wbytes(F, W));
     if (!wq || !wo || !wg || !wd) { fail(VFM_E_OOM, "weight allocation failed"); return bail(VFM_E_OOM); }
-    hipError_t e;
-    if ((e = vfm::pack_weight(wq, W, nqkv, qs, qi, ptr[p + "q.w"], Hq * d, ptr[p + "k.w"], Hkv * d, ptr[p + "v.w"], Hkv * d,
-                              x->src_bf16, x->act_bf16, s)) != hipSuccess ||
-        (e = vfm::pack_weight(wo, Hq * d, W, os, oi, ptr[p + "o.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
-        (e = vfm::pack_weight(wg, W, 2 * F, gs, gi, ptr[p + "gate.w"], F, ptr[p + "up.w"], F, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
-        (e = vfm::pack_weight(wd, F, W, ds, di, ptr[p + "down.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess) {
-      fail(VFM_E_HIP, "weight packing failed: %s", hipGetErrorString(e));
-      return bail(VFM_E_HIP);
+    hipError_t e = hipSuccess;
+    if (x->wprec == VFM_W_FP32 || x->wprec == VFM_W_BF16) {
+      if ((e = vfm::pack_weight(wq, W, nqkv, qs, qi, ptr[p + "q.w"], Hq * d, ptr[p + "k.w"], Hkv * d, ptr[p + "v.w"], Hkv * d,
+                                x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+          (e = vfm::pack_weight(wo, Hq * d, W, os, oi, ptr[p + "o.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+          (e = vfm::pack_weight(wg, W, 2 * F, gs, gi, ptr[p + "gate.w"], F, ptr[p + "up.w"], F, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess ||
+          (e = vfm::pack_weight(wd, F, W, ds, di, ptr[p + "down.w"], W, nullptr, 0, nullptr, 0, x->src_bf16, x->act_bf16, s)) != hipSuccess) {
+        fail(VFM_E_HIP, "weight packing failed: %s", hipGetErrorString(e));
+        return bail(VFM_E_HIP);
+      }
+    } else {
+      const int fmt = x->wprec == VFM_W_FP8 ? 0 : 1;
+      unsigned* am = x->wamax ? x->wamax + 4 * l : nullptr;
+      if (fmt == 0) {
+        // one scale per fused tensor: [q | k | v] and [gate | up] share theirs
+        const size_t qn = (size_t)W * Hq * d, kn = (size_t)W * Hkv * d;
+        if ((e = vfm::amax_into(am + 0, ptr[p + "q.w"], qn, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 0, ptr[p + "k.w"], kn, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 0, ptr[p + "v.w"], kn, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 1, ptr[p + "o.w"], (size_t)Hq * d * W, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 2, ptr[p + "gate.w"], (size_t)W * F, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 2, ptr[p + "up.w"], (size_t)W * F, 1, s)) != hipSuccess ||
+            (e = vfm::amax_into(am + 3, ptr[p + "down.w"], (size_t)F * W, 1, s)) != hipSuccess) {
+          fail(VFM_E_HIP, "weight amax failed: %s", hipGetErrorString(e));
+          return bail(VFM_E_HIP);
+        }
+      }
+      if ((e = vfm::pack_weight_q(wq, fmt, W, nqkv, qs, qi, ptr[p + "q.w"], Hq * d, ptr[p + "k.w"], Hkv * d, ptr[p + "v.w"],
+                                  Hkv * d, am ? am + 0 : nullptr, s)) != hipSuccess ||
+          (e = vfm::pack_weight_q(wo, fmt, Hq * d, W, os, oi, ptr[p + "o.w"], W, nullptr, 0, nullptr, 0, am ? am + 1 : nullptr,
+                                  s)) != hipSuccess ||
+          (e = vfm::pack_weight_q(wg, fmt, W, 2 * F, gs, gi, ptr[p + "gate.w"], F, ptr[p + "up.w"], F, nullptr, 0,
+                                  am ? am + 2 : nullptr, s)) != hipSuccess ||
+          (e = vfm::pack_weight_q(wd, fmt, F, W, ds, di, ptr[p + "down.w"], W, nullptr, 0, nullptr, 0, am ? am + 3 : nullptr,
+                                  s)) != hipSuccess) {
+        fail(VFM_E_HIP, "weight packing failed: %s", hipGetErrorString(e));
+        return bail(VFM_E_HIP);
+      }
     }
     x->w_qkv.push_back(wq); x->w_o.push_back(wo); x->w_gu.push_back(wg); x->w_down.push_back(wd);
+  }
+  if (x->wprec == VFM_W_FP8) {
+    std::vector<float> am((size_t)L * 4);
+    if (L > 0 && (hipMemcpyAsync(am.data(), x->wamax, am.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+                  hipStreamSynchronize(s) != hipSuccess)) {
+      fail(VFM_E_HIP, "weight scales readback failed");
+      return bail(VFM_E_HIP);
+    }
+    x->wscale.resize(am.size());
+    for (size_t i = 0; i < am.size(); ++i) x->wscale[i] = am[i] > 0.f ? am[i] / 448.0f : 1.0f;
+    x->qs = (float*)x->dalloc((size_t)std::max(L, 1) * 8 * 4);
+    if (!x->qs) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
   }
   // small f32 weights
   struct Cv { float** dst; const char* name; size_t n; };
@@ -478,7 +604,8 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     shape.d = d;
     shape.W = W;
     x->lds = vfm::lds_bytes(shape, ab);
-    hipError_t e = vfm::prepare_kernels(x->act_bf16, d, (int)x->lds);
+    hipError_t e = vfm::prepare_kernels(x->kset, d, (int)x->lds);
+    if (e == hipSuccess && x->wprec == VFM_W_FP8) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
   }
   if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) {
@@ -586,38 +713,10 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if ((reinterpret_cast<uintptr_t>(noise) | reinterpret_cast<uintptr_t>(actions) | reinterpret_cast<uintptr_t>(state)) % 16)
     return fail(VFM_E_INVALID_ARG, "noise / state / actions must be 16-byte aligned");
 
+  if (x->wprec == VFM_W_FP8 && x->act_scale.empty())
+    return fail(VFM_E_STATE, "FP8 expert: run vfm_calibrate or vfm_set_act_scales first");
   VP p{};
-  p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
-  p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
-  p.kps = 64;                       // keys per attention split
-  p.KS = (P + x->H + 63) / 64;
-  p.eps = x->cfg.rms_eps;
-  for (int l = 0; l < x->L; ++l) {
-    p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
-  }
-  p.in_w = x->in_w; p.in_b = x->in_b; p.st_w = x->st_w; p.st_b = x->st_b; p.out_w = x->out_w; p.out_b = x->out_b;
-  p.mod = x->mod; p.rope = x->rope;
-  p.prefix_k = x->prefix_k.ptr; p.prefix_v = x->prefix_v.ptr;
-  p.noise = noise; p.state = state; p.x = actions;
-  p.s_emb = x->s_emb; p.h = x->h; p.part_o = x->part_o; p.part_d = x->part_d; p.opart = x->opart; p.ml = x->ml;
-  p.ring = x->ring; p.slab = x->slab; p.off_xna = x->off_xna; p.off_q = x->off_q; p.off_k = x->off_k; p.off_v = x->off_v;
-  p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
-  p.trace = x->mode == 0 ? x->trace : nullptr;
-
-  {
-    int nwg = x->coop_grid;
-    if (nwg == 0) {
-      HIPCHK(vfm::max_cooperative_grid(x->act_bf16, x->d, x->lds, &x->coop_grid));
-      if (x->coop_grid == 0) return fail(VFM_E_HIP, "persistent kernel does not fit on a compute unit");
-      nwg = x->coop_grid;
-    }
-    const int KB = x->act_bf16 ? 32 : 16;
-    const int Ks[4] = {x->W, x->Hq * x->d, x->W, x->F};
-    const int Ns[4] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W};
-    for (int i = 0; i < 4; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i == 1 || i == 3, &p.gp_nt[i], &p.gp_s[i]);
-    p.S_o = p.gp_s[1];
-    p.S_down = p.gp_s[3];
-  }
+  if ((st = fill_vp(x, p, B, P, noise, state, actions)) != VFM_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (x->rope_P != P) {
     HIPCHK(vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s));
@@ -626,14 +725,14 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   }
   if (x->mode == 0) {
     HIPCHK(vfm::zero_words(x->bar, 1024, s));
-    HIPCHK(vfm::launch_phase(p, x->act_bf16, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
+    HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(x->flag_event, s));
     x->flag_pending = true;
     return VFM_OK;
   }
   if (x->mode == 2) {
-    HIPCHK(enqueue_phases(x, p, s));
+    HIPCHK(enqueue_phases(x, p, x->kset, s));
     return VFM_OK;
   }
   // graph mode
@@ -644,7 +743,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     if (!x->cap_stream) HIPCHK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
     hipGraph_t g = nullptr;
     HIPCHK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeThreadLocal));
-    hipError_t e = enqueue_phases(x, p, x->cap_stream);
+    hipError_t e = enqueue_phases(x, p, x->kset, x->cap_stream);
     hipError_t e2 = hipStreamEndCapture(x->cap_stream, &g);
     if (e != hipSuccess || e2 != hipSuccess) {
       if (g) (void)hipGraphDestroy(g);
@@ -660,18 +759,85 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
 }
 
 vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
-  (void)stream;
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  if (x->cfg.weight_precision != VFM_W_FP8) return fail(VFM_E_STATE, "calibrate applies to FP8 experts only");
-  return fail(VFM_E_UNSUPPORTED, "FP8 is not built into this library yet");
+  if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "calibrate applies to FP8 experts only");
+  vfm_status st = check_prev_flag(x, true);
+  if (st != VFM_OK) return st;
+  if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
+  const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
+  if ((st = check_buf("prefix_v", x->prefix_v, VFM_BF16, {x->L, B, P, x->Hkv, x->d})) != VFM_OK) return st;
+  if ((st = check_buf("noise", x->noise, VFM_F32, {B, x->H, x->A})) != VFM_OK) return st;
+  if ((st = check_buf("actions", x->actions, VFM_F32, {B, x->H, x->A})) != VFM_OK) return st;
+  if (x->S > 0 && (st = check_buf("state", x->state, VFM_F32, {B, x->S})) != VFM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int L = x->L, W = x->W, F = x->F, nqkv = (x->Hq + 2 * x->Hkv) * x->d, qd = x->Hq * x->d;
+  // One bf16 pass with the dequantised FP8 weights (materialised for the
+  // pass only) records the largest |input| of every GEMM over all steps.
+  std::vector<void*> tmp;
+  auto release = [&]() { for (void* q : tmp) (void)hipFree(q); tmp.clear(); };
+  auto talloc = [&](size_t bytes) -> void* {
+    void* q = nullptr;
+    if (hipMalloc(&q, bytes) != hipSuccess) return nullptr;
+    tmp.push_back(q);
+    return q;
+  };
+  float* amax = (float*)talloc((size_t)std::max(L, 1) * 16);
+  if (!amax) { release(); return fail(VFM_E_OOM, "calibration buffers"); }
+  VP p{};
+  const int kw = x->KW;
+  x->KW = 32;   // the bf16 pass plans its GEMMs for 32-K blocks
+  st = fill_vp(x, p, B, P, (const float*)x->noise.ptr, (const float*)x->state.ptr, (float*)x->actions.ptr);
+  x->KW = kw;
+  if (st != VFM_OK) { release(); return st; }
+  p.trace = nullptr;
+  p.amax = amax;
+  hipError_t e = hipMemsetAsync(amax, 0, (size_t)std::max(L, 1) * 16, s);
+  for (int l = 0; l < L && e == hipSuccess; ++l) {
+    uint8_t* bq = (uint8_t*)talloc((size_t)W * nqkv * 2);
+    uint8_t* bo = (uint8_t*)talloc((size_t)qd * W * 2);
+    uint8_t* bg = (uint8_t*)talloc((size_t)W * 2 * F * 2);
+    uint8_t* bd = (uint8_t*)talloc((size_t)F * W * 2);
+    if (!bq || !bo || !bg || !bd) { release(); return fail(VFM_E_OOM, "calibration weights"); }
+    unsigned* am = x->wamax + 4 * l;
+    if ((e = vfm::fp8_to_bf16_packed(bq, x->w_qkv[l], W, nqkv, am + 0, s)) != hipSuccess ||
+        (e = vfm::fp8_to_bf16_packed(bo, x->w_o[l], qd, W, am + 1, s)) != hipSuccess ||
+        (e = vfm::fp8_to_bf16_packed(bg, x->w_gu[l], W, 2 * F, am + 2, s)) != hipSuccess ||
+        (e = vfm::fp8_to_bf16_packed(bd, x->w_down[l], F, W, am + 3, s)) != hipSuccess)
+      break;
+    p.w_qkv[l] = bq; p.w_o[l] = bo; p.w_gu[l] = bg; p.w_down[l] = bd;
+  }
+  if (e == hipSuccess && x->rope_P != P) {
+    e = vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s);
+    if (e == hipSuccess) x->rope_P = P;
+  }
+  if (e == hipSuccess) e = enqueue_phases(x, p, vfm::KS_CAL, s);
+  std::vector<float> am((size_t)L * 4);
+  if (e == hipSuccess && L > 0) e = hipMemcpyAsync(am.data(), amax, am.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  release();
+  if (e != hipSuccess) return fail(VFM_E_HIP, "calibration pass failed: %s", hipGetErrorString(e));
+  std::vector<float> sc(am.size());
+  for (size_t i = 0; i < am.size(); ++i) sc[i] = am[i] > 0.f ? am[i] / 448.0f : 1.0f;
+  return vfm_set_act_scales(x, sc.data(), (int32_t)sc.size());
 }
 
 vfm_status vfm_set_act_scales(vfm_expert* x, const float* scales, int32_t n) {
-  (void)scales;
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  if (x->cfg.weight_precision != VFM_W_FP8) return fail(VFM_E_STATE, "activation scales apply to FP8 experts only");
+  if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "activation scales apply to FP8 experts only");
   if (n != 4 * x->L) return fail(VFM_E_SHAPE, "expected %d scales", 4 * x->L);
-  return fail(VFM_E_UNSUPPORTED, "FP8 is not built into this library yet");
+  if (n > 0 && !scales) return fail(VFM_E_INVALID_ARG, "scales is NULL");
+  for (int i = 0; i < n; ++i)
+    if (!(scales[i] > 0.f) || !std::isfinite(scales[i])) return fail(VFM_E_INVALID_ARG, "scale %d is not a positive number", i);
+  std::vector<float> q((size_t)n * 2);
+  for (int i = 0; i < n; ++i) {
+    q[2 * i] = scales[i] * x->wscale[i];      // alpha of the GEMM epilogue
+    q[2 * i + 1] = 1.0f / scales[i];          // the activation quantiser multiplies by this
+  }
+  HIPCHK(hipDeviceSynchronize());
+  if (n > 0) HIPCHK(hipMemcpy(x->qs, q.data(), q.size() * 4, hipMemcpyHostToDevice));
+  x->act_scale.assign(scales, scales + n);
+  if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
+  return VFM_OK;
 }
 
 vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) {
@@ -708,6 +874,14 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
       return VFM_OK;
     }
   }
+  if (n == "act_scales" || n == "weight_scales") {
+    if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "'%s' exists for FP8 experts only", name);
+    const std::vector<float>& v = n == "act_scales" ? x->act_scale : x->wscale;
+    if (v.empty()) return fail(VFM_E_STATE, "activation scales are not set");
+    if (bytes != v.size() * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, v.size() * 4);
+    memcpy(dst, v.data(), bytes);
+    return VFM_OK;
+  }
   if (n == "trace") {
     // microseconds since kernel start of (arrive, release) of every phase barrier of the last call
     if (!x->trace) return fail(VFM_E_STATE, "trace is off");
@@ -741,26 +915,46 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     return fail(VFM_E_INVALID_ARG, "unknown tensor '%s'", name);
   }
   if (bytes != (size_t)K * ncols * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, (size_t)K * ncols * 4);
-  const int ab = x->act_bf16 ? 2 : 4;
-  std::vector<uint8_t> host((size_t)K * Npk * ab);
+  const int gi = (w == "q" || w == "k" || w == "v") ? 0 : w == "o" ? 1 : (w == "gate" || w == "up") ? 2 : 3;
+  size_t nbytes;
+  if (x->wprec == VFM_W_FP8) nbytes = (size_t)K * Npk;
+  else if (x->wprec == VFM_W_W4A16) nbytes = (size_t)K * Npk / 2 + (size_t)(K / 128) * Npk * 2;
+  else nbytes = (size_t)K * Npk * (x->act_bf16 ? 2 : 4);
+  std::vector<uint8_t> host(nbytes);
   HIPCHK(hipDeviceSynchronize());
   HIPCHK(hipMemcpy(host.data(), packed, host.size(), hipMemcpyDeviceToHost));
-  const int E = 16 / ab, KB = 4 * E, nkb = K / KB;
   float* out = static_cast<float*>(dst);
+  const int KW = x->KW, nkb = K / KW;
   for (int pc = 0; pc < Npk; ++pc) {
     if (map->src[pc] != sid) continue;
     const int col = map->idx[pc];
     const int t = pc / 16, c16 = pc % 16;
     for (int k = 0; k < K; ++k) {
-      const int kb = k / KB, rem = k % KB, g = rem / E, e = rem % E;
-      const size_t off = (((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + (size_t)e * ab;
+      const int kb = k / KW, rem = k % KW;
       float v;
-      if (ab == 4) {
-        memcpy(&v, &host[off], 4);
+      if (x->wprec == VFM_W_FP8) {
+        // byte 8r + e of lane (g, c16) holds k = 64 kb + 32 r + 8 g + e
+        const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
+        const uint8_t c = host[(((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + r * 8 + e];
+        v = e4m3_value(c) * x->wscale[(size_t)l * 4 + gi];
+      } else if (x->wprec == VFM_W_W4A16) {
+        // nibble 8r + e of lane (g, c16) holds k = 128 kb + 32 r + 8 g + e
+        const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
+        const size_t lane_off = (((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16;
+        uint32_t wd;
+        memcpy(&wd, &host[lane_off + 4 * r], 4);
+        const int q = (int)(wd << (28 - 4 * e)) >> 28;
+        uint16_t sb;
+        memcpy(&sb, &host[(size_t)K * Npk / 2 + (((size_t)t * nkb + kb) * 16 + c16) * 2], 2);
+        v = (float)q * half_value(sb);
+      } else if (!x->act_bf16) {
+        const int g = rem / 4, e = rem % 4;
+        memcpy(&v, &host[(((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + (size_t)e * 4], 4);
       } else {
+        const int g = rem / 8, e = rem % 8;
         uint16_t hb;
-        memcpy(&hb, &host[off], 2);
-        uint32_t u = (uint32_t)hb << 16;
+        memcpy(&hb, &host[(((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + (size_t)e * 2], 2);
+        const uint32_t u = (uint32_t)hb << 16;
         memcpy(&v, &u, 4);
       }
       out[(size_t)k * ncols + col] = v;

@@ -20,7 +20,7 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_kernels.hip", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
+KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
                   "vla_flow_matching_pi0_amd/csrc/vfm_params.h"]
 
 
