@@ -62,18 +62,18 @@ typedef enum { VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3 } 
 typedef struct {
   int32_t abi_version;      /* must equal VFM_ABI_VERSION */
   int32_t num_layers;       /* L >= 0 */
-  int32_t width;            /* W, multiple of 64 */
-  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads */
+  int32_t width;            /* W, multiple of 256 in [256, 2048] (FP8: of 512, W4A16: of 1024) */
+  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads; Hq * d multiple of 256 (FP8 512, W4A16 1024) */
   int32_t num_kv_heads;     /* Hkv >= 1 */
-  int32_t head_dim;         /* d, multiple of 16, <= 256 */
-  int32_t mlp_dim;          /* F, multiple of 64 */
+  int32_t head_dim;         /* d in {64, 128, 256} (fp32 experts: 64, 128) */
+  int32_t mlp_dim;          /* F, multiple of 256 (FP8: 512, W4A16: 1024), <= 65536 */
   int32_t action_horizon;   /* H, 1..64 action tokens per sample */
-  int32_t action_dim;       /* A, 1..64 */
-  int32_t state_dim;        /* S >= 0 (0: no state input) */
-  int32_t time_emb_dim;     /* E, even, >= 4 */
-  int32_t max_prefix_len;   /* upper bound of P over all binds */
-  int32_t max_batch;        /* upper bound of B over all binds */
-  int32_t num_steps;        /* N >= 1 Euler steps, t from 1 to 0 */
+  int32_t action_dim;       /* A in {4, 8, 16, 32, 64} */
+  int32_t state_dim;        /* S in [0, 4096] (0: no state input) */
+  int32_t time_emb_dim;     /* E, even, in [4, 8192] */
+  int32_t max_prefix_len;   /* upper bound of P over all binds, 1..4000 */
+  int32_t max_batch;        /* upper bound of B over all binds, 1..1024 */
+  int32_t num_steps;        /* N in [1, 1000] Euler steps, t from 1 to 0 */
   float rope_base;          /* rotary base, > 0 */
   float rms_eps;            /* RMSNorm epsilon, > 0 */
   int32_t weight_precision; /* vfm_wprec */
@@ -154,14 +154,24 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  * Errors: VFM_E_INVALID_ARG for an unknown key or value. */
 vfm_status vfm_set_option(vfm_expert* ex, const char* key, const char* value);
 
-/* FP8 experts: measure the activation amax of every FP8 GEMM input over one
- * bf16 pass on the bound buffers and set act_scale = amax / 448 per input.
- * Synchronous on `stream`. VFM_E_STATE on a non-FP8 expert. */
+/* FP8 experts: one measurement pass, as in the FlashRT walk-through
+ * (component 6, calibration): run the whole denoise loop once on the bound
+ * buffers (prefix_k, prefix_v, noise, state; `actions` is overwritten) in
+ * bf16, with the dequantised FP8 weights materialised in bf16 for the pass
+ * only, record the largest |input| of every GEMM (4 per layer, over all
+ * steps), and set act_scale = amax / 448 (1 where amax is 0); the GEMM
+ * epilogues then use alpha = act_scale * weight_scale. An FP8 expert's
+ * denoise returns VFM_E_STATE until this or vfm_set_act_scales has run.
+ * Synchronous on `stream`; invalidates captured graphs.
+ * Errors: VFM_E_STATE (not FP8), VFM_E_UNBOUND / VFM_E_SHAPE (buffers),
+ * VFM_E_OOM, VFM_E_HIP. */
 vfm_status vfm_calibrate(vfm_expert* ex, void* stream);
 
-/* Test hook: set the n = 4 * L FP8 activation scales directly (order per
- * layer: qkv input, o input, gate/up input, down input). VFM_E_STATE on a
- * non-FP8 expert, VFM_E_SHAPE if n != 4 * L. */
+/* Set the n = 4 * L FP8 activation scales directly (host array, order per
+ * layer: qkv input, o input, gate/up input, down input; each > 0), e.g.
+ * scales cached from an earlier calibration. Synchronises the device.
+ * Errors: VFM_E_STATE (not FP8), VFM_E_SHAPE (n != 4 * L),
+ * VFM_E_INVALID_ARG (a scale not positive and finite). */
 vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
 
 /* Copy a tensor the library holds, as float32, to host memory `dst`
@@ -170,8 +180,12 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
  *      the value the kernels multiply by, i.e. dequantised for FP8 / W4A16,
  *      row-major [in][out];
  *   "mod_table": [N][2L+1][3][W], (scale, shift, gate) of every norm at
- *      every step (norm order attn_0, mlp_0, ..., final).
- * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE. */
+ *      every step (norm order attn_0, mlp_0, ..., final);
+ *   "weight_scales", "act_scales" (FP8 only): [L][4] per-GEMM scales
+ *      (qkv, o, gate/up, down); act_scales needs a calibration first;
+ *   "trace": the phase timeline of the last persistent call (option "trace").
+ * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE,
+ * VFM_E_STATE. */
 vfm_status vfm_export(vfm_expert* ex, const char* name, void* dst, size_t bytes);
 
 /* Wait for `stream` and report any device-side failure of earlier denoise
