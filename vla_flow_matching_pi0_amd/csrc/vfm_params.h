@@ -36,8 +36,9 @@ struct VP {
   float* s_emb;            // [M][W]     state embedding, per action token
   float* h;                // [M][W]     residual stream
   // write-once activation ring: one slab per (step, layer) holding, at the
-  // offsets below, xn_attn [M][W], q [B][Hq][d/16][64][16], k and v
-  // [B][Hkv][d/16][64][16], attn [M][Hq*d], xn_mlp [M][W], act [F/16][Mpad][16]
+  // offsets below, q [B][Hq][d/16][64][16], k and v [B][Hkv][d/16][64][16]
+  // and the GEMM inputs in MFMA operand order [K/KB][Mpad][KB]: xn_attn
+  // (K = W), attn (K = Hq*d), xn_mlp (K = W), act (K = F)
   uint8_t* ring;
   size_t slab;
   size_t off_xna, off_q, off_k, off_v, off_attn, off_xnm, off_act;

@@ -78,6 +78,17 @@ __device__ __forceinline__ void stf_coh(void* base, size_t idx, float v) {
 // coherence point.
 __device__ __forceinline__ uint8_t* slab(const VP& p, int k, int l) { return p.ring + ((size_t)k * p.L + l) * p.slab; }
 
+// GEMM inputs (xn_attn, attn, xn_mlp, act) are stored in MFMA operand order,
+// [K / KB][Mpad][KB] with KB = MT<T>::KB k values per block (32 bf16, 16
+// fp32): the 16 tokens x KB values one wave fetches for one MFMA block form
+// one contiguous 1 KiB run. Element offset of (token m, feature k):
+template <typename T>
+__device__ __forceinline__ size_t act_off(const VP& p, int m, int k) {
+  constexpr int KB = MT<T>::KB;
+  const int Mpad = ((p.M + 63) / 64) * 64;
+  return ((size_t)(k / KB) * Mpad + m) * KB + k % KB;
+}
+
 // q/k/v are stored tile-major, [sample][head][d/16 tiles][64 tokens][16];
 // within a q/k tile the 16 slots hold dims 8t..8t+7, then their rotary
 // partners 8t+d/2..8t+7+d/2. Element offset of (token i, canonical dim e)
@@ -130,8 +141,8 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
   const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
   if (c < W4) {
     const floatx4 y = hv * r * (1.0f + sc) + sh;
-    if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(((size_t)m * p.W + c * 4) * 4), as_u4(y));
-    else coh_st8(xn, (uint32_t)(((size_t)m * p.W + c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+    if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 4), as_u4(y));
+    else coh_st8(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
   }
 }
 
@@ -270,8 +281,8 @@ __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg,
           const float* mod = p.mod + ((size_t)kn * p.n_norms) * 3 * W;
           const floatx4 y = hv * r * (1.0f + as_f4(ro_ld16(mod + c * 4))) + as_f4(ro_ld16(mod + W + c * 4));
           uint8_t* xn = slab(p, kn, 0) + p.off_xna;
-          if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(y));
-          else coh_st8(xn, (uint32_t)(((size_t)m * W + c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+          if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 4), as_u4(y));
+          else coh_st8(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
         }
       }
     }
@@ -484,8 +495,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const size_t row = (size_t)(m0 + st * 16 + c16);
-          // act is tile-major [K/16][Mpad][16]; the others are row-major [M][K]
-          const size_t off = WHICH == G_DOWN ? ((size_t)(k / 16) * Mpad + row) * 16 + k % 16 : row * K + k;
+          const size_t off = ((size_t)(k / KM) * Mpad + row) * KM + k % KM;   // operand order, see act_off
           ar[st][j] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
         }
       }
@@ -579,7 +589,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
           // packed lane order (gate f, up f, gate f+1, up f+1), f = 8 tile + 2 g
           const int f0 = tile * 8 + 2 * g;
           const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
-          const size_t e0 = ((size_t)(f0 / 16) * Mpad + gm) * 16 + f0 % 16;   // tile-major [F/16][Mpad][16]
+          const size_t e0 = act_off<T>(p, gm, f0);
           uint8_t* dst = sl + p.off_act;
           if constexpr (sizeof(T) == 4)
             coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
@@ -829,7 +839,7 @@ __device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int
         for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
       }
       const floatx4 o = num / den;
-      const size_t e0 = (size_t)gm * p.Hq * D + jh * D + d4 * 4;
+      const size_t e0 = act_off<T>(p, gm, jh * D + d4 * 4);
       if constexpr (sizeof(T) == 4) coh_st16(attn, (uint32_t)(e0 * 4), as_u4(o));
       else coh_st8(attn, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
     }

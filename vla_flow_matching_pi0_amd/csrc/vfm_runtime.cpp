@@ -579,12 +579,12 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     auto al = [](size_t b) { return (b + 4095) / 4096 * 4096; };
     const size_t Mpad = (Mmax + 63) / 64 * 64;
     size_t off = 0;
-    x->off_xna = off; off += al(Mmax * W * ab);
+    x->off_xna = off; off += al(Mpad * W * ab);
     x->off_q = off; off += al((size_t)x->maxB * Hq * d * 64 * ab);
     x->off_k = off; off += al((size_t)x->maxB * Hkv * d * 64 * ab);
     x->off_v = off; off += al((size_t)x->maxB * Hkv * d * 64 * ab);
-    x->off_attn = off; off += al(Mmax * Hq * d * ab);
-    x->off_xnm = off; off += al(Mmax * W * ab);
+    x->off_attn = off; off += al(Mpad * Hq * d * ab);
+    x->off_xnm = off; off += al(Mpad * W * ab);
     x->off_act = off; off += al((size_t)F * Mpad * ab);
     x->slab = off;
     x->ring = (uint8_t*)x->dalloc(x->slab * (size_t)x->N * std::max(L, 1));
