@@ -155,9 +155,16 @@ struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
 
-// `hook` runs in every thread between this workgroup's arrival and its wait:
-// work that does not depend on the other workgroups (issuing loads of
-// read-only data) overlaps the wait.
+// Device-wide barrier of a persistent grid. Arrival: after its stores have
+// completed, each workgroup adds 1 to one of 8 counters (blockIdx % 8, one
+// 256-byte line each) without waiting for the old value. Wait: wave 0 reads
+// the 8 counters (one per lane) until their sum reaches epoch * gridDim.
+// The sum of values read at slightly different times never exceeds the true
+// count, so reaching the target proves every workgroup arrived. `hook` runs
+// in every thread between arrival and wait: work that does not depend on the
+// other workgroups (issuing loads of read-only data) overlaps the wait.
+// bar[1] is a sticky error word: a wait that exceeds BARRIER_SPIN_LIMIT sets
+// it, and every waiter gives up once it is set (returns false).
 template <typename HOOK = NoHook>
 __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace = nullptr,
                                              const HOOK& hook = HOOK()) {
@@ -167,28 +174,35 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
   __syncthreads();
   // optional timeline: workgroup 0 stamps (arrive, release) of every barrier
   if (trace && blockIdx.x == 0 && threadIdx.x == 0) trace[2 * epoch] = __builtin_amdgcn_s_memrealtime();
-  if (threadIdx.x == 0) {
-    const unsigned G = gridDim.x;
-    const unsigned grp = blockIdx.x % 8;
-    const unsigned gsize = (G - grp + 7) / 8;
-    const unsigned old = __hip_atomic_fetch_add(&bar[64 + 64 * grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 == epoch * gsize) __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&bar[64 + 64 * (blockIdx.x % 8)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   hook();
-  if (threadIdx.x == 0) {
-    const unsigned ngroups = gridDim.x < 8 ? gridDim.x : 8;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned target = epoch * gridDim.x;
     unsigned ok = 1;
     long spins = 0;
-    while (ld_agent(&bar[0]) < epoch * ngroups) {
-      ++spins;
-      if (((spins & 1023) == 0 && ld_agent(&bar[1]) != 0u) || spins > BARRIER_SPIN_LIMIT) {
-        __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
+    for (;;) {
+      unsigned v = lane < 8 ? ld_agent(&bar[64 + 64 * lane]) : 0u;
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v = __shfl(v, 0);
+      if (v >= target) break;
+      if ((++spins & 1023) == 0) {
+        unsigned err = lane == 0 ? ld_agent(&bar[1]) : 0u;
+        err = __shfl(err, 0);
+        if (err != 0u || spins > BARRIER_SPIN_LIMIT) {
+          if (lane == 0) __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
       }
     }
-    s_ok = ok;
-    if (trace && blockIdx.x == 0) trace[2 * epoch + 1] = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      s_ok = ok;
+      if (trace && blockIdx.x == 0) trace[2 * epoch + 1] = __builtin_amdgcn_s_memrealtime();
+    }
   }
   __syncthreads();
   return s_ok != 0;
