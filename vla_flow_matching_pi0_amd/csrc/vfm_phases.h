@@ -625,7 +625,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
 // probabilities then feed the PV MFMA directly from registers.
 constexpr int ATT_KEYS = ATT_KEYS_HOST;   // keys per split
 
-template <typename T, int D, int MODE>   // MODE 0: prefix keys only, 1: chunk keys only, 2: both
+template <typename T, int D, int MODE>   // MODE 0: prefix keys, 1: the chunk's own keys
 __device__ __forceinline__ void attn_load_kv(const VP& p, int tid, int b, int kvh, int s0, int s1,
                                              __amdgpu_buffer_rsrc_t pkr, __amdgpu_buffer_rsrc_t pvr,
                                              __amdgpu_buffer_rsrc_t kgr, __amdgpu_buffer_rsrc_t vgr,
@@ -652,18 +652,65 @@ __device__ __forceinline__ void attn_load_kv(const VP& p, int tid, int b, int kv
     if constexpr (MODE == 0) {
       kreg[j] = ld16_if(pkr, kpo, s < s1);
       vreg[j] = ld16_if(pvr, vpo, vs < s1);
-    } else if constexpr (MODE == 1) {
+    } else {
       kreg[j] = ld16_if(kgr, kco, s < s1);
       vreg[j] = ld16_if(vgr, vco, vs < s1);
-    } else {
-      kreg[j] = ld16_if(pkr, kpo, s < s1 && s < P) | ld16_if(kgr, kco, s < s1 && s >= P);
-      vreg[j] = ld16_if(pvr, vpo, vs < s1 && vs < P) | ld16_if(vgr, vco, vs < s1 && vs >= P);
     }
   }
 }
 
+// K/V fragments of a workgroup's first attention unit when its keys all lie
+// in the prefix: they depend on nothing computed in this call, so the
+// persistent kernel loads them while the workgroup waits at the barrier
+// before the attention phase.
 template <typename T, int D>
-__device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg) {
+struct APre {
+  static constexpr int LOADS = ATT_KEYS * (D / (16 / (int)sizeof(T))) / NTH;
+  u32x4 k[LOADS], v[LOADS];
+};
+
+// Key range [s0, s1) of split c: the prefix keys in splits of ATT_KEYS, then
+// the chunk's own keys in splits of their own, so that only the chunk
+// splits depend on the projection phase just before attention.
+__device__ __forceinline__ void attn_split(const VP& p, int c, int& s0, int& s1) {
+  const int KSp = (p.P + ATT_KEYS - 1) / ATT_KEYS;
+  if (c < KSp) {
+    s0 = c * ATT_KEYS;
+    s1 = min(p.P, s0 + ATT_KEYS);
+  } else {
+    s0 = p.P + (c - KSp) * ATT_KEYS;
+    s1 = min(p.P + p.H, s0 + ATT_KEYS);
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ bool attn_prefix_unit(const VP& p, int u, int& b, int& kvh, int& s0, int& s1) {
+  const int KS = p.KS;
+  const int c = u % KS, bh = u / KS, jh = bh % p.Hq;
+  b = bh / p.Hq;
+  kvh = jh / (p.Hq / p.Hkv);
+  attn_split(p, c, s0, s1);
+  return u < p.B * p.Hq * KS && s1 <= p.P;
+}
+
+template <typename T, int D>
+struct AttnPrefetchHook {
+  const VP& p;
+  int layer, wg;
+  APre<T, D>& out;
+  __device__ __forceinline__ void operator()() const {
+    int b, kvh, s0, s1;
+    if (!attn_prefix_unit<T, D>(p, wg, b, kvh, s0, s1)) return;
+    const size_t layer_elems = (size_t)p.B * p.P * p.Hkv * D;
+    const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
+    const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
+    attn_load_kv<T, D, 0>(p, tid_opaque(), b, kvh, s0, s1, pkr, pvr, pkr, pvr, out.k, out.v);
+  }
+};
+
+template <typename T, int D, bool PRE = false>
+__device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg,
+                                        const APre<T, D>& pre = APre<T, D>{}) {
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
@@ -676,7 +723,7 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
   T* Vt = Ks + ATT_KEYS * LDK;                       // [D][LDV]
   const int grp = tid >> 8, gtid = tid & 255;
   const int lane = tid & 63, wv = gtid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int H = p.H, P = p.P, S_tot = P + H, KS = p.KS;
+  const int H = p.H, P = p.P, KS = p.KS;
   const int group = p.Hq / p.Hkv;
   const int units = p.B * p.Hq * KS;
   const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
@@ -688,7 +735,8 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
   for (int u = wg; u < units; u += nwg) {
     const int c = u % KS, bh = u / KS, jh = bh % p.Hq, b = bh / p.Hq;
     const int kvh = jh / group;
-    const int s0 = c * ATT_KEYS, s1 = min(S_tot, s0 + ATT_KEYS);
+    int s0, s1;
+    attn_split(p, c, s0, s1);
     const int qrow = wv * 16 + c16;
     const bool active = wv * 16 < H;
     // query fragments (B operand of S^T): Q[qrow][kb*KB + g*E .. +E]; the
@@ -705,9 +753,11 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
       }
     }
     u32x4 kreg[LOADS], vreg[LOADS];
-    if (s1 <= P) attn_load_kv<T, D, 0>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
-    else if (s0 >= P) attn_load_kv<T, D, 1>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
-    else attn_load_kv<T, D, 2>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
+    if (PRE && u == wg && s1 <= P) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) { kreg[j] = pre.k[j]; vreg[j] = pre.v[j]; }
+    } else if (s1 <= P) attn_load_kv<T, D, 0>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
+    else attn_load_kv<T, D, 1>(p, tid, b, kvh, s0, s1, pkr, pvr, kgr, vgr, kreg, vreg);
     __syncthreads();   // the previous unit's LDS reads are done
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -869,8 +919,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         VFM_BAR_PF(G_QKV, l);
       }
       ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
-      VFM_BAR();
-      ph_attn<T, D>(p, k, l, wg, nwg);
+      {
+        APre<T, D> apre;
+        if (!grid_barrier(p.bar, epoch, p.trace, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
+        ph_attn<T, D, true>(p, k, l, wg, nwg, apre);
+      }
       VFM_BAR();
       ph_combine<T>(p, k, l, wg, nwg);
       VFM_BAR_PF(G_O, l);
