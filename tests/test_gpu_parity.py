@@ -150,3 +150,43 @@ def test_pi05_bf16_b32_sampled():
         err = gu.rel_l2(got[b:b + 1], ref)
         print(f"b32 sample {b}: rel_l2={err:.3e}")
         assert err <= 2e-2
+
+
+@pytest.mark.parametrize("shape", [
+    # the largest width, action dim and horizon the library takes, GQA with 2 KV heads of dim 128
+    dict(num_layers=1, width=2048, num_q_heads=16, num_kv_heads=2, head_dim=128, mlp_dim=8192,
+         action_horizon=64, action_dim=64, state_dim=16, time_emb_dim=512, prefix_len=300, batch=2),
+    # head dim 64, a single prefix key
+    dict(num_layers=2, width=512, num_q_heads=8, num_kv_heads=4, head_dim=64, mlp_dim=1024,
+         action_horizon=10, action_dim=4, state_dim=0, time_emb_dim=64, prefix_len=1, batch=1),
+])
+def test_bf16_other_shapes(shape):
+    gu = _gu()
+    cfg = CONFIGS["pi05_bf16_b1"].replace(**shape)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    print(f"case bf16 shape {shape}", flush=True)
+    for mode in ("persistent", "graph"):
+        got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
+        err = gu.rel_l2(got, ref)
+        print(f"{mode}: rel_l2={err:.3e}")
+        assert err <= 2e-2, mode
+
+
+def test_rebinding_a_shorter_prefix_and_smaller_batch():
+    """One expert created for the largest shapes, run at a smaller batch and
+    prefix (the rotary table and the graph key follow the bound shapes)."""
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"].replace(batch=2, prefix_len=96, state_dim=3)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ex = gu.build_expert(cfg, params, "graph", max_batch=3, max_prefix_len=200)
+    for b, P in ((2, 96), (1, 40), (2, 96)):
+        c = cfg.replace(batch=b, prefix_len=P)
+        bufs = gu.bind_inputs(ex, c, pk[:, :b, :P].copy(), pv[:, :b, :P].copy(), noise[:b].copy(), state[:b].copy())
+        ex.denoise()
+        ex.check()
+        torch.cuda.synchronize()
+        got = bufs["actions"].cpu().numpy()
+        ref = O.denoise(params, noise[:b], state[:b], pk[:, :b, :P], pv[:, :b, :P], c)
+        assert gu.rel_l2(got, ref) <= 1e-4, (b, P)
+    ex.close()

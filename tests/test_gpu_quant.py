@@ -151,3 +151,30 @@ def test_w4a16_matches_oracle(mode):
     disp = gu.rel_l2(got - ev[2], ref - ev[2])
     print(f"w4a16 {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
     assert err <= 5e-2
+
+
+@pytest.mark.parametrize("prec", ["fp8", "w4a16"])
+def test_quantised_ragged_shapes(prec):
+    """Quantised experts at batch 2 with a prefix that is not a multiple of
+    the key split, a horizon that is not a multiple of 16 and a state input."""
+    gu = _gu()
+    cfg = CONFIGS["pi05_fp8_p816" if prec == "fp8" else "pi05_w4a16"].replace(
+        num_layers=2, batch=2, prefix_len=37, action_horizon=13, state_dim=5)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    deq, _ = Q.dequantised_expert(params, cfg)
+    ref = O.denoise(deq, noise, state, pk, pv, cfg)
+    print(f"case {prec} ragged", flush=True)
+    for mode in ("persistent", "eager"):
+        ex = gu.build_expert(cfg, params, mode)
+        if prec == "fp8":
+            gu.bind_inputs(ex, cfg, *make_calibration_inputs(cfg))
+            ex.calibrate()
+        bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+        ex.denoise()
+        ex.check()
+        torch.cuda.synchronize()
+        got = bufs["actions"].cpu().numpy()
+        ex.close()
+        err = gu.rel_l2(got, ref)
+        print(f"{prec} ragged {mode}: rel_l2={err:.3e}")
+        assert err <= 5e-2, mode
