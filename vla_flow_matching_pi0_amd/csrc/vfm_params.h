@@ -42,7 +42,7 @@ struct VP {
   uint8_t* ring;
   size_t slab;
   size_t off_xna, off_q, off_k, off_v, off_attn, off_xnm, off_act;
-  float* opart;            // [B*Hq*KS*64][d]  unnormalised split outputs
+  void* opart;             // [B*Hq*KS*64][d]  unnormalised split outputs (activation type)
   float* ml;               // [B*Hq*KS*64][2]  (max, sum) per split row, log2 domain
   float* part_o;           // [S_o][M][W]  K-split partial sums of the o projection
   float* part_d;           // [S_down][M][W] ... of the down projection

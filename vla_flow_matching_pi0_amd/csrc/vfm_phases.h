@@ -844,8 +844,11 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
     if (qrow < H) {
       const size_t base = ((size_t)(b * p.Hq + jh) * KS + c) * 64 + qrow;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        coh_st16(p.opart, (uint32_t)((base * D + dbase + dt * 16 + 4 * g) * 4), as_u4(O[dt]));
+      for (int dt = 0; dt < DT; ++dt) {
+        const size_t e0 = base * D + dbase + dt * 16 + 4 * g;
+        if constexpr (sizeof(T) == 4) coh_st16(p.opart, (uint32_t)(e0 * 4), as_u4(O[dt]));
+        else coh_st8(p.opart, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(O[dt][0], O[dt][1]), pack_bf16x2(O[dt][2], O[dt][3])});
+      }
       if (g == 0 && grp == 0)
         coh_st8(p.ml, (uint32_t)(base * 8), u32x2{__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_run)});
     }
@@ -881,12 +884,25 @@ __device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int
     for (int d4 = lane; d4 < D / 4; d4 += 64) {
       floatx4 num = {0, 0, 0, 0};
       for (int c0 = 0; c0 < KS; c0 += 16) {
-        u32x4 ov[16];
+        if constexpr (sizeof(T) == 4) {
+          u32x4 ov[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          ov[j] = coh_ld16_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4), c0 + j < KS);
+          for (int j = 0; j < 16; ++j)
+            ov[j] = coh_ld16_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4), c0 + j < KS);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
+          for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
+        } else {
+          u32x2 ov[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            ov[j] = coh_ld8_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 2), c0 + j < KS);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const floatx4 f = {__builtin_bit_cast(float, ov[j][0] << 16), __builtin_bit_cast(float, ov[j][0] & 0xffff0000u),
+                               __builtin_bit_cast(float, ov[j][1] << 16), __builtin_bit_cast(float, ov[j][1] & 0xffff0000u)};
+            num += __shfl(wc, (c0 + j) & 63) * f;
+          }
+        }
       }
       const floatx4 o = num / den;
       const size_t e0 = act_off<T>(p, gm, jh * D + d4 * 4);
