@@ -481,6 +481,17 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
     bool rowok[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) rowok[st] = m0 + st * 16 + c16 < p.M;
+    // rotary (cos, sin) pairs of the epilogue item this wave finalises, fetched
+    // with the operands rather than after the products
+    floatx4 rot = {0, 0, 0, 0};
+    if constexpr (WHICH == G_QKV) {
+      const int t = wv / 4, st = wv % 4;
+      const int gm = m0 + st * 16 + c16, col0 = (t0 + t) * 16;
+      const int head = col0 / p.d, tt = (col0 % p.d) / 16;
+      const bool ok = wv < nt * 4 && gm < p.M && head < p.Hq + p.Hkv;
+      const int i = gm % p.H, j0 = tt * 8 + 2 * g;
+      rot = as_f4(ld16_if(rsrc(p.rope), (uint32_t)((((size_t)i * (p.d / 2) + j0) * 2) * 4), ok));
+    }
     const auto ars = rsrc(A);
     for (int pb = 0; pb < nkbw; pb += PW) {
       WPre wl;
@@ -563,8 +574,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
           if (head < p.Hq + p.Hkv) {
             // packed lane order (x_j, x_j+1, x_j+d/2, x_j+1+d/2), j = 8 tt + 2 g
             const int j0 = tt * 8 + 2 * g;
-            const float* rp = p.rope + ((size_t)i * hd + j0) * 2;
-            const float c0 = rp[0], s0 = rp[1], c1 = rp[2], s1 = rp[3];
+            const float c0 = rot[0], s0 = rot[1], c1 = rot[2], s1 = rot[3];
             const float y0 = v.x * c0 - v.z * s0, y0h = v.z * c0 + v.x * s0;
             const float y1 = v.y * c1 - v.w * s1, y1h = v.w * c1 + v.y * s1;
             const bool isq = head < p.Hq;
