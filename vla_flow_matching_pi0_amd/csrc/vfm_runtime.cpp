@@ -333,7 +333,11 @@ void plan_gemm(int M, int N, int K, int KB, int nwg, bool linear, int* nt, int* 
   int smax = 1;
   if (linear)
     while (smax * 2 <= vfm::MAX_KSPLIT && K % (smax * 2 * KB * waves) == 0) smax *= 2;
-  *nt = (tiles % 2 == 0 && (long)(tiles / 2) * mt * smax >= nwg) ? 2 : 1;
+  // one 16-column tile per unit unless there are at least two tiles per
+  // workgroup; then the fewest K splits that give every workgroup a unit
+  // (measured on the pi0.5 shapes: o and down run fastest as 64 tiles x 4
+  // splits, gate/up as 256 pairs of tiles)
+  *nt = (tiles % 2 == 0 && (long)tiles * mt >= 2L * nwg) ? 2 : 1;
   int s = 1;
   while (s * 2 <= smax && (long)(tiles / *nt) * mt * s < nwg) s *= 2;
   *S = s;
