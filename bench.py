@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h"]
+                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h", "vla_flow_matching_pi0_amd/csrc/vfm_launch.cpp",
+                  "vla_flow_matching_pi0_amd/csrc/vfm_runtime.cpp"]
 
 
 def kernel_source_digest() -> str:

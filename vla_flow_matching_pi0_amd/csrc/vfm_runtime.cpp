@@ -350,8 +350,9 @@ void plan_gemm(int M, int N, int K, int KB, int nwg, bool linear, int* nt, int* 
 vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const float* state, float* actions) {
   p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
   p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
-  p.kps = 64;                       // keys per attention split
-  p.KS = (P + 63) / 64 + (x->H + 63) / 64;   // prefix splits, then chunk splits
+  constexpr int AK = vfm::ATT_KEYS_HOST;   // keys per attention split
+  p.kps = AK;
+  p.KS = (P + AK - 1) / AK + (x->H + AK - 1) / AK;   // prefix splits, then chunk splits
   p.eps = x->cfg.rms_eps;
   for (int l = 0; l < x->L; ++l) {
     p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
@@ -573,7 +574,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   }
   // workspace for max_batch / max_prefix_len
   const size_t Mmax = (size_t)x->maxB * H;
-  x->KSmax = (x->maxP + 63) / 64 + (H + 63) / 64;
+  x->KSmax = (x->maxP + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST + (H + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST;
   x->rope = (float*)x->dalloc((size_t)H * d * 4);
   x->s_emb = (float*)x->dalloc(Mmax * W * 4);
   x->part_o = (float*)x->dalloc((size_t)vfm::MAX_KSPLIT * Mmax * W * 4);

@@ -21,7 +21,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h"]
+                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h", "vla_flow_matching_pi0_amd/csrc/vfm_launch.cpp",
+                  "vla_flow_matching_pi0_amd/csrc/vfm_runtime.cpp"]
 
 
 def source_digest() -> str:
