@@ -190,3 +190,51 @@ def test_rebinding_a_shorter_prefix_and_smaller_batch():
         ref = O.denoise(params, noise[:b], state[:b], pk[:, :b, :P], pv[:, :b, :P], c)
         assert gu.rel_l2(got, ref) <= 1e-4, (b, P)
     ex.close()
+
+
+def test_graph_replays_each_match_the_oracle():
+    """A captured graph replayed several times, with other device work and
+    host synchronisation between the replays: every replay must give the
+    oracle's actions (a graph that went stale after its first replay would
+    not)."""
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"].replace(state_dim=4)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    ex = gu.build_expert(cfg, params, "graph")
+    bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+    for rep in range(4):
+        bufs["actions"].fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()   # unrelated work between replays
+        ex.denoise()
+        ex.check()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        got = bufs["actions"].cpu().numpy()
+        assert gu.rel_l2(got, ref) <= 1e-4, rep
+    ex.close()
+
+
+def test_plain_persistent_launch_and_trace():
+    """The ordinary launch of the persistent kernel gives the same actions as
+    the cooperative one, and the phase timeline is ordered: every barrier is
+    released after it was reached and before the next is reached."""
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"]
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    ex = gu.build_expert(cfg, params, "persistent")
+    ex.set_option("persistent_launch", "plain")
+    ex.set_option("trace", "1")
+    bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+    ex.denoise()
+    ex.check()
+    torch.cuda.synchronize()
+    assert gu.rel_l2(bufs["actions"].cpu().numpy(), ref) <= 1e-4
+    L, N = cfg.num_layers, cfg.num_steps
+    words = 2 * (N * (8 * L + 1) + 4)
+    t = ex.export("trace", (words,)).reshape(-1, 2)
+    ex.close()
+    n_bar = 1 + N * 8 * L           # one after the first boundary, then 8 per layer (the last one at the step boundary)
+    stamps = t[1:n_bar + 1].ravel()
+    assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
