@@ -58,6 +58,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m vla_flow_matching_pi0_amd.build`")
+    # torch brings its own HIP runtime; load it first so that the library binds
+    # to the same runtime as the tensors it is handed (two runtimes in one
+    # process do not share device allocations)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
     lib.vfm_abi_version.restype = ctypes.c_int
