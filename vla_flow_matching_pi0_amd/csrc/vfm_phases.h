@@ -291,8 +291,8 @@ __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg,
 }
 
 // ============================================================ skinny GEMM on MFMA
-// C[M x N] = A[M x K] (act type T, row-major, produced by an earlier phase)
-// times a packed weight. Swap-AB: the weight supplies the 16 MFMA rows
+// C[M x N] = A[M x K] (act type T in MFMA operand order, see act_off,
+// produced by an earlier phase) times a packed weight. Swap-AB: the weight supplies the 16 MFMA rows
 // (output features) and the tokens the 16 MFMA columns, so the 50 tokens of
 // a chunk pad to 64 = 4 column tiles and a lane ends with 4 consecutive
 // output features of one token. Packed weight layout:
