@@ -134,3 +134,16 @@ def test_null_expert_calls(lib):
     assert vfm.STATUS[lib.vfm_export(None, b"mod_table", None, 0)] == "VFM_E_INVALID_ARG"
     assert vfm.STATUS[lib.vfm_check(None, None)] == "VFM_E_INVALID_ARG"
     assert lib.vfm_expert_destroy(None) == 0
+
+
+def test_create_rejects_buffers_beyond_32bit_offsets(lib):
+    """Every buffer is addressed with 32-bit byte offsets: configurations
+    whose largest buffer would exceed 2 GiB are refused up front."""
+    for kw in (dict(max_batch=1024, max_prefix_len=4000), dict(max_batch=64, max_prefix_len=4000)):
+        c = vfm.make_config(CONFIGS["pi05_bf16_b1"], **kw)
+        st, out = _create(lib, c)
+        assert vfm.STATUS[st] == "VFM_E_UNSUPPORTED", kw
+        assert "2 GiB" in lib.vfm_last_error().decode()
+        assert not out.value
+    # the batch-32 workload fits (fails later, for want of weights)
+    assert vfm.STATUS[_create(lib, vfm.make_config(CONFIGS["pi05_bf16_b32"]))[0]] == "VFM_E_INVALID_ARG"

@@ -176,6 +176,32 @@ vfm_status validate_config(const vfm_config* c) {
   return VFM_OK;
 }
 
+// The kernels address every buffer through 32-bit byte offsets from its
+// base (buffer resources of up to 2 GiB): refuse configurations whose largest
+// buffer would not fit.
+vfm_status check_extents(const vfm_config* c) {
+  const size_t ab = c->act_dtype == VFM_F32 ? 4 : 2;
+  const size_t L = c->num_layers, W = c->width, Hq = c->num_q_heads, Hkv = c->num_kv_heads, d = c->head_dim;
+  const size_t F = c->mlp_dim, H = c->action_horizon, N = c->num_steps, B = c->max_batch, P = c->max_prefix_len;
+  const size_t M = B * H, Mpad = (M + 63) / 64 * 64;
+  const size_t KS = (P + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST + (H + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST;
+  struct { const char* what; size_t bytes; } ext[] = {
+      {"modulation table", N * (2 * L + 1) * 3 * W * 4},
+      {"residual stream", M * W * 4},
+      {"K-split partial sums", (size_t)vfm::MAX_KSPLIT * M * W * 4},
+      {"one layer of the prefix K/V", B * P * Hkv * d * ab},
+      {"gate/up GEMM input or output", std::max(Mpad * W, F * Mpad) * ab},
+      {"attention output", Mpad * Hq * d * ab},
+      {"attention split outputs", B * Hq * KS * 64 * d * 4},
+      {"packed gate/up weight", W * 2 * F * 4},
+  };
+  for (const auto& e : ext)
+    if (e.bytes > 0x7FFFFFF0ull)
+      return fail(VFM_E_UNSUPPORTED, "the %s would take %zu bytes, beyond the 2 GiB one buffer offset addresses "
+                  "(reduce max_batch, max_prefix_len, num_steps or the widths)", e.what, e.bytes);
+  return VFM_OK;
+}
+
 struct WeightSpec {
   std::string name;
   std::vector<int64_t> shape;
@@ -397,6 +423,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   *out = nullptr;
   vfm_status st = validate_config(cfg);
   if (st != VFM_OK) return st;
+  if ((st = check_extents(cfg)) != VFM_OK) return st;
   if (!weights || n_weights <= 0) return fail(VFM_E_INVALID_ARG, "no weights given");
 
   vfm_expert tmp;
