@@ -99,7 +99,7 @@ def test_small_depths(layers, steps):
     assert gu.rel_l2(got, ref) <= 1e-4
 
 
-@pytest.mark.parametrize("batch,prefix,horizon", [(3, 37, 8), (2, 5, 13), (1, 130, 50)])
+@pytest.mark.parametrize("batch,prefix,horizon", [(3, 37, 8), (2, 5, 13), (1, 130, 50), (2, 3, 1)])
 def test_ragged_shapes(batch, prefix, horizon):
     """Batch > 1, prefix lengths that are not a multiple of 32, horizons that
     are not a multiple of 16 (fp32 expert with a state input)."""

@@ -90,6 +90,9 @@ __device__ __forceinline__ void coh_st8(void* base, uint32_t off, u32x2 v) {
 __device__ __forceinline__ void coh_st4(void* base, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, rsrc(base), off, 0, CPOL_SC1);
 }
+__device__ __forceinline__ void coh_st2(void* base, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, rsrc(base), off, 0, CPOL_SC1);
+}
 // read-only data (weights, prefix KV, tables): ordinary cached loads
 __device__ __forceinline__ u32x4 ro_ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 

@@ -89,6 +89,45 @@ __device__ __forceinline__ size_t act_off(const VP& p, int m, int k) {
   return ((size_t)(k / KB) * Mpad + m) * KB + k % KB;
 }
 
+// FP8 experts store their GEMM inputs as e4m3 codes, quantised once by the
+// producing phase with the input's calibrated 1/act_scale (the residual +
+// norm + quantise fusion the FlashRT walk-through lists among its
+// hand-written kernels, component 8). Layout: 64-k blocks, [K/64][Mpad][4
+// lane groups g][16 bytes]; the 16 bytes of group g are k = 8g..8g+7 and
+// 32+8g..32+8g+7 of the block, the operands of the two 16x16x32 fp8 MFMAs of
+// one weight block, fetched with one load. Byte offset of (token m, feature k):
+__device__ __forceinline__ size_t act_off8(const VP& p, int m, int k) {
+  const int Mpad = ((p.M + 63) / 64) * 64;
+  const int kk = k % 64, r = kk / 32, g = (kk % 32) / 8, e = kk % 8;
+  return (((size_t)(k / 64) * Mpad + m) * 4 + g) * 16 + r * 8 + e;
+}
+
+// e4m3 codes of x * inv, saturated to +-448 (the conversion rounds to nearest
+// even and would give NaN beyond 448), two values per call.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2(float a, float b, float inv, uint32_t old) {
+  a = fminf(fmaxf(a * inv, -448.0f), 448.0f);
+  b = fminf(fmaxf(b * inv, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// 1/act_scale of GEMM input `which` of layer l (FP8 experts)
+__device__ __forceinline__ float act_inv(const VP& p, int l, int which) { return p.qs[(l * 4 + which) * 2 + 1]; }
+
+// Four consecutive features k..k+3 (k % 4 == 0) of token m of a GEMM input,
+// in the consumer's operand layout: the activation type, or e4m3 codes.
+template <typename T, bool Q8>
+__device__ __forceinline__ void store_gemm_in4(const VP& p, void* base, int m, int k, floatx4 y, float inv) {
+  if constexpr (Q8) {
+    const uint32_t w = fp8x2<true>(y.z, y.w, inv, fp8x2<false>(y.x, y.y, inv, 0u));
+    coh_st4(base, (uint32_t)act_off8(p, m, k), w);
+  } else if constexpr (sizeof(T) == 4) {
+    coh_st16(base, (uint32_t)(act_off<T>(p, m, k) * 4), as_u4(y));
+  } else {
+    coh_st8(base, (uint32_t)(act_off<T>(p, m, k) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+  }
+}
+
 // q/k/v are stored tile-major, [sample][head][d/16 tiles][64 tokens][16];
 // within a q/k tile the 16 slots hold dims 8t..8t+7, then their rotary
 // partners 8t+d/2..8t+7+d/2. Element offset of (token i, canonical dim e)
@@ -109,9 +148,9 @@ __device__ __forceinline__ size_t v_off(int d, size_t head_block, int i, int e) 
 
 // h[m] += gate * sum_s part[s][m]; xn[m] = adaRMSNorm(h[m]) with norm `ni`
 // (ni < 0: no norm). Four columns per thread; W <= 4 * NTH.
-template <typename T>
+template <typename T, bool Q8>
 __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni,
-                                                  int ni, void* xn, float* red) {
+                                                  int ni, void* xn, float* red, float inv) {
   const int tid = tid_opaque();
   const int W4 = p.W / 4;
   const int c = tid;
@@ -141,15 +180,15 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
   const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
   if (c < W4) {
     const floatx4 y = hv * r * (1.0f + sc) + sh;
-    if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 4), as_u4(y));
-    else coh_st8(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+    store_gemm_in4<T, Q8>(p, xn, m, c * 4, y, inv);
   }
 }
 
 // Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
 // scales the partial sums, ni the norm applied.
-template <typename T>
+template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
+  constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
   const float* part = mlp ? p.part_o : p.part_d;
@@ -157,7 +196,7 @@ __device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp
   const int gate_ni = mlp ? 2 * layer : 2 * layer - 1, ni = mlp ? 2 * layer + 1 : 2 * layer;
   void* xn = slab(p, step, layer) + (mlp ? p.off_xnm : p.off_xna);
   for (int m = wg; m < p.M; m += nwg) {
-    row_residual_norm<T>(p, step, m, part, S, gate_ni, ni, xn, red);
+    row_residual_norm<T, Q8>(p, step, m, part, S, gate_ni, ni, xn, red, Q8 ? act_inv(p, layer, mlp ? 2 : 0) : 1.0f);
     __syncthreads();
   }
 }
@@ -169,8 +208,9 @@ __device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp
 // Thread c owns columns 4c..4c+3 of the row; every weight load is issued
 // before it is used.
 constexpr int MAX_A = MAX_A_HOST;
-template <typename T>
+template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
+  constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
   float* xs = red + NWAVES;                                          // [W]
@@ -281,8 +321,7 @@ __device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg,
           const float* mod = p.mod + ((size_t)kn * p.n_norms) * 3 * W;
           const floatx4 y = hv * r * (1.0f + as_f4(ro_ld16(mod + c * 4))) + as_f4(ro_ld16(mod + W + c * 4));
           uint8_t* xn = slab(p, kn, 0) + p.off_xna;
-          if constexpr (sizeof(T) == 4) coh_st16(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 4), as_u4(y));
-          else coh_st8(xn, (uint32_t)(act_off<T>(p, m, c * 4) * 2), u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
+          store_gemm_in4<T, Q8>(p, xn, m, c * 4, y, Q8 ? act_inv(p, 0, 0) : 1.0f);
         }
       }
     }
@@ -398,29 +437,6 @@ struct PrefetchHook {
   __device__ __forceinline__ void operator()() const { gemm_prefetch<T, WHICH, WF>(p, layer, wg, out); }
 };
 
-// 8 bf16 activations -> 8 e4m3 codes of x * inv_scale, saturated to +-448
-// (the conversion instruction rounds to nearest even; it would give NaN
-// beyond the largest finite value, hence the clamp).
-__device__ __forceinline__ long act_to_fp8(u32x4 a, float inv) {
-  uint32_t wds[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float f[4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t wd = a[2 * h + q];
-      f[2 * q] = __builtin_bit_cast(float, wd << 16) * inv;
-      f[2 * q + 1] = __builtin_bit_cast(float, wd & 0xffff0000u) * inv;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -448.0f), 448.0f);
-    int v = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    v = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], v, true);
-    wds[h] = (uint32_t)v;
-  }
-  return (long)(((unsigned long long)wds[1] << 32) | wds[0]);
-}
-
 // 8 signed nibbles (element e in bits 4e..4e+3) times an fp16 scale -> 8 bf16.
 __device__ __forceinline__ u32x4 w4_to_bf16(uint32_t wd, uint32_t scale_bits) {
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
@@ -462,11 +478,8 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
   const int K = gs.K, nt = gs.nt, S = gs.S, ngroups = gs.ngroups, units = gs.units, KR = gs.KR, nkbw = gs.nkbw;
   const int Mpad = ((p.M + 63) / 64) * 64;
   const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  float alpha = 1.0f, inv_act = 1.0f;
-  if constexpr (WF == WF_FP8) {
-    alpha = p.qs[(layer * 4 + WHICH) * 2];
-    inv_act = p.qs[(layer * 4 + WHICH) * 2 + 1];
-  }
+  float alpha = 1.0f;
+  if constexpr (WF == WF_FP8) alpha = p.qs[(layer * 4 + WHICH) * 2];
   float amax = 0.f;
   floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NWAVES][2][4][64]
   for (int u = wg; u < units; u += nwg) {
@@ -498,16 +511,30 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
       u32x4 ar[4][GEMM_PASS];
       if (PRE && u == wg && pb == 0) wl = pre;
       else gemm_load_weights<T, WHICH, WF>(gs, u, pb, tid, wl);
+      if constexpr (WF == WF_FP8) {
+        // e4m3 inputs (act_off8): one 16-byte fetch per weight block and token subtile
 #pragma unroll
-      for (int j = 0; j < GEMM_PASS; ++j) {
-        const int i = j / R, r = j % R;
-        const bool ok = pb + i < nkbw;
-        const int k = (kb0 + pb + i) * KW + r * KM + g * E;
+        for (int i = 0; i < PW; ++i) {
+          const bool ok = pb + i < nkbw;
+          const int kblk = kb0 + pb + i;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const size_t row = (size_t)(m0 + st * 16 + c16);
-          const size_t off = ((size_t)(k / KM) * Mpad + row) * KM + k % KM;   // operand order, see act_off
-          ar[st][j] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
+          for (int st = 0; st < 4; ++st) {
+            const size_t row = (size_t)(m0 + st * 16 + c16);
+            ar[st][i] = ld16_if(ars, (uint32_t)((((size_t)kblk * Mpad + row) * 4 + g) * 16), ok && rowok[st]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < GEMM_PASS; ++j) {
+          const int i = j / R, r = j % R;
+          const bool ok = pb + i < nkbw;
+          const int k = (kb0 + pb + i) * KW + r * KM + g * E;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const size_t row = (size_t)(m0 + st * 16 + c16);
+            const size_t off = ((size_t)(k / KM) * Mpad + row) * KM + k % KM;   // operand order, see act_off
+            ar[st][j] = ld16_if(ars, (uint32_t)(off * sizeof(T)), ok && rowok[st]);
+          }
         }
       }
       if constexpr (CAL) {
@@ -528,7 +555,7 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
         } else if constexpr (WF == WF_FP8) {
           long a8[4];
 #pragma unroll
-          for (int st = 0; st < 4; ++st) a8[st] = act_to_fp8(ar[st][j], inv_act);
+          for (int st = 0; st < 4; ++st) a8[st] = (long)__builtin_bit_cast(i64x2, ar[st][i])[r];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const i64x2 w2 = __builtin_bit_cast(i64x2, wl.w[t][i]);
@@ -599,11 +626,16 @@ __device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg
           // packed lane order (gate f, up f, gate f+1, up f+1), f = 8 tile + 2 g
           const int f0 = tile * 8 + 2 * g;
           const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
-          const size_t e0 = act_off<T>(p, gm, f0);
           uint8_t* dst = sl + p.off_act;
-          if constexpr (sizeof(T) == 4)
-            coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
-          else coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(a0, a1));
+          if constexpr (WF == WF_FP8) {
+            const uint32_t w = fp8x2<false>(a0, a1, act_inv(p, layer, G_DOWN), 0u);
+            coh_st2(dst, (uint32_t)act_off8(p, gm, f0), w & 0xffffu);
+          } else {
+            const size_t e0 = act_off<T>(p, gm, f0);
+            if constexpr (sizeof(T) == 4)
+              coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
+            else coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(a0, a1));
+          }
         } else {
           float* part = WHICH == G_O ? p.part_o : p.part_d;
           const int n0 = tile * 16 + 4 * g;
@@ -868,8 +900,9 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
 // Merge the key splits: attn[b*H+i][j*d + dd] = sum_c w_c O_c / sum_c w_c l_c,
 // w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
 // c's (max, sum), then every lane merges four head dims over all splits.
-template <typename T>
+template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
+  constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
   const int lane = tid & 63, wv = tid >> 6;
@@ -915,9 +948,7 @@ __device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int
         }
       }
       const floatx4 o = num / den;
-      const size_t e0 = act_off<T>(p, gm, jh * D + d4 * 4);
-      if constexpr (sizeof(T) == 4) coh_st16(attn, (uint32_t)(e0 * 4), as_u4(o));
-      else coh_st8(attn, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
+      store_gemm_in4<T, Q8>(p, attn, gm, jh * D + d4 * 4, o, Q8 ? act_inv(p, layer, 1) : 1.0f);
     }
   }
 }
@@ -935,13 +966,13 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
 #define VFM_BAR_PF(WHICH, LAYER) \
   do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
-  ph_boundary<T>(p, -1, 0, wg, nwg);
+  ph_boundary<T, WF>(p, -1, 0, wg, nwg);
   if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
   for (int k = 0; k < p.N; ++k) {
     for (int l = 0; l < p.L; ++l) {
       if (l > 0) {
-        ph_rn<T>(p, k, l, false, wg, nwg);
+        ph_rn<T, WF>(p, k, l, false, wg, nwg);
         VFM_BAR_PF(G_QKV, l);
       }
       ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
@@ -951,18 +982,18 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         ph_attn<T, D, true>(p, k, l, wg, nwg, apre);
       }
       VFM_BAR();
-      ph_combine<T>(p, k, l, wg, nwg);
+      ph_combine<T, WF>(p, k, l, wg, nwg);
       VFM_BAR_PF(G_O, l);
       ph_gemm<T, G_O, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR();
-      ph_rn<T>(p, k, l, true, wg, nwg);
+      ph_rn<T, WF>(p, k, l, true, wg, nwg);
       VFM_BAR_PF(G_GU, l);
       ph_gemm<T, G_GU, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR_PF(G_DOWN, l);
       ph_gemm<T, G_DOWN, true, WF>(p, k, l, wg, nwg, pre);
       VFM_BAR();
     }
-    ph_boundary<T>(p, k, k + 1, wg, nwg);
+    ph_boundary<T, WF>(p, k, k + 1, wg, nwg);
     if (p.L > 0 && k + 1 < p.N) VFM_BAR_PF(G_QKV, 0);
     else VFM_BAR();
   }
@@ -975,13 +1006,13 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
 template <typename T, int D, int PH, int WF, bool CAL>
 __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
   const int wg = blockIdx.x, nwg = gridDim.x;
-  if constexpr (PH == PH_BOUNDARY) ph_boundary<T>(p, k - 1, k, wg, nwg);
-  else if constexpr (PH == PH_RN_ATTN) ph_rn<T>(p, k, l, false, wg, nwg);
+  if constexpr (PH == PH_BOUNDARY) ph_boundary<T, WF>(p, k - 1, k, wg, nwg);
+  else if constexpr (PH == PH_RN_ATTN) ph_rn<T, WF>(p, k, l, false, wg, nwg);
   else if constexpr (PH == PH_QKV) ph_gemm<T, G_QKV, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_ATTN) ph_attn<T, D>(p, k, l, wg, nwg);
-  else if constexpr (PH == PH_COMBINE) ph_combine<T>(p, k, l, wg, nwg);
+  else if constexpr (PH == PH_COMBINE) ph_combine<T, WF>(p, k, l, wg, nwg);
   else if constexpr (PH == PH_O) ph_gemm<T, G_O, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
-  else if constexpr (PH == PH_RN_MLP) ph_rn<T>(p, k, l, true, wg, nwg);
+  else if constexpr (PH == PH_RN_MLP) ph_rn<T, WF>(p, k, l, true, wg, nwg);
   else if constexpr (PH == PH_GU) ph_gemm<T, G_GU, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
 }
