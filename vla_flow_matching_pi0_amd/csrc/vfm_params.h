@@ -10,6 +10,10 @@ namespace vfm {
 constexpr int MAX_LAYERS = 48;
 constexpr int NTHREADS = 512;      // threads per workgroup
 constexpr int MAX_KSPLIT = 16;     // K splits of the residual GEMMs
+// Grid-barrier words: [0] unused, [1] sticky error flag, then BAR_COUNTERS
+// arrival counters, each on its own 256-byte line (word 64 + 64 c).
+constexpr int BAR_COUNTERS = 64;
+constexpr int BAR_WORDS = 64 + 64 * BAR_COUNTERS;
 
 enum Phase {
   PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_COUNT

@@ -426,6 +426,7 @@ template <typename T, int WHICH, int WF>
 __device__ __forceinline__ void gemm_prefetch(const VP& p, int layer, int wg, WPre& out) {
   const GemmShape gs = gemm_shape<T, WHICH, WF>(p, layer);
   const int tid = tid_opaque();
+  out = WPre{};   // a full write, so the previous prefetch is dead from here on
   if (wg < gs.units) gemm_load_weights<T, WHICH, WF>(gs, wg, 0, tid, out);
 }
 

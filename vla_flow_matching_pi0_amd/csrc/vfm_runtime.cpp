@@ -623,7 +623,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   }
   x->opart = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * d * 4);
   x->ml = (float*)x->dalloc((size_t)x->maxB * Hq * x->KSmax * 64 * 2 * 4);
-  x->bar = (unsigned*)x->dalloc(1024 * 4);
+  x->bar = (unsigned*)x->dalloc(vfm::BAR_WORDS * 4);
   if (!x->rope || !x->s_emb || !x->part_o || !x->part_d || !x->h || !x->ring || !x->opart || !x->ml || !x->bar) {
     fail(VFM_E_OOM, "workspace allocation failed");
     return bail(VFM_E_OOM);
@@ -756,7 +756,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
   }
   if (x->mode == 0) {
-    HIPCHK(vfm::zero_words(x->bar, 1024, s));
+    HIPCHK(vfm::zero_words(x->bar, vfm::BAR_WORDS, s));
     HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(x->flag_event, s));
