@@ -50,6 +50,20 @@ __device__ __forceinline__ int tid_opaque() {
   return t;
 }
 
+// The launch parameters as a fresh reference into the kernel-argument
+// segment (every kernel here takes the VP block as its first argument). Each
+// phase starts from one, so it re-reads the fields it uses with scalar loads
+// (scalar-cache hits) instead of the compiler hoisting values derived from
+// them out of the step and layer loops and keeping them live across the whole
+// persistent kernel, which overflowed the scalar registers into vector
+// registers (hundreds of lane spills and reloads).
+typedef __attribute__((address_space(4))) const VP KVP;
+__device__ __forceinline__ const VP& vp_fresh() {
+  KVP* q = (KVP*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *(const VP*)q;
+}
+
 // Sum over the workgroup; `red` is >= NWAVES floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = warp_sum(v);
@@ -187,7 +201,8 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
 // Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
 // scales the partial sums, ni the norm applied.
 template <typename T, int WF = 0>
-__device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp, int wg, int nwg) {
+__device__ __forceinline__ void ph_rn(const VP&, int step, int layer, bool mlp, int wg, int nwg) {
+  const VP& p = vp_fresh();
   constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
@@ -209,7 +224,8 @@ __device__ __forceinline__ void ph_rn(const VP& p, int step, int layer, bool mlp
 // before it is used.
 constexpr int MAX_A = MAX_A_HOST;
 template <typename T, int WF = 0>
-__device__ __forceinline__ void ph_boundary(const VP& p, int kp, int kn, int wg, int nwg) {
+__device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, int nwg) {
+  const VP& p = vp_fresh();
   constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
@@ -423,7 +439,8 @@ __device__ __forceinline__ void gemm_load_weights(const GemmShape& gs, int u, in
 }
 
 template <typename T, int WHICH, int WF>
-__device__ __forceinline__ void gemm_prefetch(const VP& p, int layer, int wg, WPre& out) {
+__device__ __forceinline__ void gemm_prefetch(const VP&, int layer, int wg, WPre& out) {
+  const VP& p = vp_fresh();
   const GemmShape gs = gemm_shape<T, WHICH, WF>(p, layer);
   const int tid = tid_opaque();
   out = WPre{};   // a full write, so the previous prefetch is dead from here on
@@ -465,7 +482,8 @@ __device__ __forceinline__ float frag_amax(u32x4 a) {
 }
 
 template <typename T, int WHICH, bool PRE, int WF = WF_NATIVE, bool CAL = false>
-__device__ __forceinline__ void ph_gemm(const VP& p, int step, int layer, int wg, int nwg, const WPre& pre) {
+__device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, int nwg, const WPre& pre) {
+  const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KM = MT<T>::KB, R = WFmt<WF>::R, KW = KM * R, PW = GEMM_PASS / R;
   static_assert(WF == WF_NATIVE || sizeof(T) == 2, "quantised weights run with bf16 activations");
@@ -742,6 +760,7 @@ struct AttnPrefetchHook {
   int layer, wg;
   APre<T, D>& out;
   __device__ __forceinline__ void operator()() const {
+    const VP& p = vp_fresh();
     int b, kvh, s0, s1;
     if (!attn_prefix_unit<T, D>(p, wg, b, kvh, s0, s1)) return;
     const size_t layer_elems = (size_t)p.B * p.P * p.Hkv * D;
@@ -752,8 +771,9 @@ struct AttnPrefetchHook {
 };
 
 template <typename T, int D, bool PRE = false>
-__device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg, int nwg,
+__device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, int nwg,
                                         const APre<T, D>& pre = APre<T, D>{}) {
+  const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
   constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
@@ -902,7 +922,8 @@ __device__ __forceinline__ void ph_attn(const VP& p, int step, int layer, int wg
 // w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
 // c's (max, sum), then every lane merges four head dims over all splits.
 template <typename T, int WF = 0>
-__device__ __forceinline__ void ph_combine(const VP& p, int step, int layer, int wg, int nwg) {
+__device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int wg, int nwg) {
+  const VP& p = vp_fresh();
   constexpr bool Q8 = WF == 1;   // WF_FP8
   const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
