@@ -130,6 +130,10 @@ def main() -> int:
                     help="launch API of the persistent kernel (plain: for profilers that cannot follow "
                          "cooperative launches)")
     ap.add_argument("--cpu-steps", type=int, default=10, help="Euler steps of the oracle CPU sample (0: skip)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="between timed calls, stream this many MiB through the caches (cold-cache timing: "
+                         "the weights of a quantised expert otherwise stay in the 256 MB last-level cache); "
+                         "value is then the mean per-call time")
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after the timed region, run a plain streaming kernel (negation) over this many MiB "
                          "of float32, the reference for scaling HBM counters")
@@ -184,20 +188,42 @@ def main() -> int:
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    flush = None
+    if args.flush_mib > 0:
+        flush = torch.ones(args.flush_mib * (1 << 20) // 4, device="cuda")
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
         ex.denoise(stream=stream)
         ends[i].record(stream)
+        if flush is not None:
+            flush.neg_()
     t1.record(stream)
     torch.cuda.synchronize()
     ex.check(stream)
     total_ms = t0.elapsed_time(t1)
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    ms_chunk = total_ms / args.steps
     med = float(np.median(per))
     mean = float(np.mean(per))
+    ms_chunk = mean if flush is not None else total_ms / args.steps
+    del flush
+
+    # in-kernel synchronisation: one more (untimed) call with the phase timeline on; the share of the call that
+    # workgroup 0 spends between arriving at a device-wide barrier and its release
+    sync = None
+    if args.mode == "persistent":
+        L, N = cfg.num_layers, cfg.num_steps
+        ex.set_option("trace", "1")
+        ex.denoise(stream=stream)
+        ex.check(stream)
+        t = ex.export("trace", (2 * (N * (8 * L + 1) + 4),)).reshape(-1, 2).astype(np.float64)
+        ex.set_option("trace", "0")
+        nb = 1 + N * 8 * L
+        span = t[nb, 1] - t[0, 1]
+        stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
+        sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "span_us": round(float(span), 1),
+                "stall_frac": round(stall / span, 4) if span > 0 else None}
     if args.calib_mib > 0:
         n = args.calib_mib * (1 << 20) // 4
         src = torch.ones(n, device="cuda")
@@ -242,6 +268,8 @@ def main() -> int:
         "roofline_ms_per_chunk": round(bytes_launch / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "achieved_tflops": round(tflops, 2),
+        "sync": sync,
+        "flush_mib": args.flush_mib,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
