@@ -224,6 +224,23 @@ def main() -> int:
         stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
         sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "span_us": round(float(span), 1),
                 "stall_frac": round(stall / span, 4) if span > 0 else None}
+    # execution-state capsule of the bound buffers: snapshot and restore, each a set of device-to-device copies
+    cap = ex.capsule()
+    reps = 20
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        cap.save(ex, stream)
+    ev[1].record(stream)
+    for _ in range(reps):
+        cap.restore(ex, stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    save_us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    restore_us = ev[1].elapsed_time(ev[2]) * 1e3 / reps
+    capsule = {"bytes": cap.nbytes, "save_us": round(save_us, 2), "restore_us": round(restore_us, 2),
+               "restore_GBps": round(2 * cap.nbytes / (restore_us * 1e3), 1)}
+    cap.close()
     if args.calib_mib > 0:
         n = args.calib_mib * (1 << 20) // 4
         src = torch.ones(n, device="cuda")
@@ -269,6 +286,7 @@ def main() -> int:
         "algorithmic_bytes_per_launch": int(bytes_launch),
         "achieved_tflops": round(tflops, 2),
         "sync": sync,
+        "capsule": capsule,
         "flush_mib": args.flush_mib,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -196,6 +196,53 @@ vfm_status vfm_check(vfm_expert* ex, void* stream);
 /* Synchronise the expert's work and free everything it owns. NULL-safe. */
 vfm_status vfm_expert_destroy(vfm_expert* ex);
 
+/* Execution-state capsules. The FlashRT-PAI introduction (its third
+ * mechanism, execution-state capsules) and the FlashRT walk-through (serving
+ * hosts: graph-replay-native capsules with snapshot, restore, fork and time
+ * travel) describe fast snapshots of a pipeline's persistent state. Here that
+ * state is the contents of the bound buffers (prefix_k, prefix_v, noise,
+ * state, actions: whichever are bound when the capsule is created) plus, for
+ * FP8 experts, the activation scales. Taking and putting back a snapshot is
+ * a handful of stream-ordered device-to-device copies: no allocation, no
+ * host synchronisation, no graph invalidation (the bound pointers do not
+ * change). Keep several capsules for time travel; restore one into another
+ * expert of the same layout to fork a rollout. */
+typedef struct vfm_capsule vfm_capsule;   /* opaque; owned by the caller via create/destroy */
+
+/* Allocate a capsule for the expert's current bindings: one device buffer
+ * per bound buffer, of the same size. prefix_k must be bound (it fixes B and
+ * P). The capsule holds no state until vfm_capsule_save. Allocates (not for
+ * use inside a tight loop); nothing is enqueued.
+ * Errors: VFM_E_INVALID_ARG (NULL), VFM_E_UNBOUND, VFM_E_OOM. On error *out
+ * is NULL. */
+vfm_status vfm_capsule_create(vfm_expert* ex, vfm_capsule** out);
+
+/* Snapshot: enqueue on `stream` copies of every buffer in the capsule from
+ * the expert's bound buffer into the capsule (asynchronous; ordered after
+ * earlier work on `stream`, e.g. a denoise that writes `actions`), and
+ * record the FP8 activation scales. The expert must have the layout the
+ * capsule was made for: same L, Hkv, d, H, A, S and activation type, same B
+ * and P, and every buffer of the capsule bound with the same size.
+ * Errors: VFM_E_INVALID_ARG, VFM_E_UNBOUND, VFM_E_SHAPE (layout differs),
+ * VFM_E_STATE (FP8 capsule with a non-FP8 expert or the reverse), VFM_E_HIP. */
+vfm_status vfm_capsule_save(vfm_expert* ex, vfm_capsule* cap, void* stream);
+
+/* Restore / fork: enqueue on `stream` copies from the capsule into the bound
+ * buffers of `ex`, which may be the expert the capsule was saved from or
+ * another one of the same layout (a fork; its weights may differ). When
+ * both are FP8 experts, the expert's activation scales are set to the
+ * capsule's first (synchronous, only if they differ). The capsule is not
+ * changed and can be restored any number of times.
+ * Errors: VFM_E_INVALID_ARG, VFM_E_STATE (never saved), VFM_E_UNBOUND,
+ * VFM_E_SHAPE, VFM_E_HIP. */
+vfm_status vfm_capsule_restore(vfm_expert* ex, const vfm_capsule* cap, void* stream);
+
+/* Device bytes the capsule holds. Errors: VFM_E_INVALID_ARG. */
+vfm_status vfm_capsule_bytes(const vfm_capsule* cap, size_t* bytes);
+
+/* Synchronise the device and free the capsule. NULL-safe. */
+vfm_status vfm_capsule_destroy(vfm_capsule* cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,6 +136,18 @@ def test_null_expert_calls(lib):
     assert lib.vfm_expert_destroy(None) == 0
 
 
+def test_null_capsule_calls(lib):
+    out = ctypes.c_void_p(0x1234)
+    assert vfm.STATUS[lib.vfm_capsule_create(None, ctypes.byref(out))] == "VFM_E_INVALID_ARG"
+    assert not out.value                      # cleared on error
+    assert vfm.STATUS[lib.vfm_capsule_create(None, None)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_capsule_save(None, None, None)] == "VFM_E_INVALID_ARG"
+    assert vfm.STATUS[lib.vfm_capsule_restore(None, None, None)] == "VFM_E_INVALID_ARG"
+    n = ctypes.c_size_t()
+    assert vfm.STATUS[lib.vfm_capsule_bytes(None, ctypes.byref(n))] == "VFM_E_INVALID_ARG"
+    assert lib.vfm_capsule_destroy(None) == 0
+
+
 def test_create_rejects_buffers_beyond_32bit_offsets(lib):
     """Every buffer is addressed with 32-bit byte offsets: configurations
     whose largest buffer would exceed 2 GiB are refused up front."""

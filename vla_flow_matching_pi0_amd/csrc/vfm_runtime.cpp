@@ -1002,6 +1002,144 @@ vfm_status vfm_check(vfm_expert* x, void* stream) {
   return check_prev_flag(x, true);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Execution-state capsules: device copies of the bound buffers (and the FP8
+// activation scales), taken and put back with stream-ordered D2D copies.
+// ---------------------------------------------------------------------------
+
+struct vfm_capsule {
+  // layout the state belongs to
+  int L = 0, Hkv = 0, d = 0, H = 0, A = 0, S = 0, act_bf16 = 0, B = 0, P = 0;
+  struct Slot {
+    int which = 0;          // 0 prefix_k, 1 prefix_v, 2 noise, 3 state, 4 actions
+    size_t bytes = 0;
+    void* dev = nullptr;    // owned by the capsule
+  };
+  std::vector<Slot> slots;
+  bool from_fp8 = false;
+  std::vector<float> act_scale;   // FP8 source: its activation scales at save time (may be empty)
+  bool saved = false;
+};
+
+namespace {
+
+const char* const kBufNames[5] = {"prefix_k", "prefix_v", "noise", "state", "actions"};
+
+BoundBuf* buf_slot(vfm_expert* x, int which) {
+  switch (which) {
+    case 0: return &x->prefix_k;
+    case 1: return &x->prefix_v;
+    case 2: return &x->noise;
+    case 3: return &x->state;
+    default: return &x->actions;
+  }
+}
+
+size_t buf_bytes(const BoundBuf& b) {
+  size_t n = b.dtype == VFM_BF16 ? 2 : 4;
+  for (int i = 0; i < b.ndim; ++i) n *= (size_t)b.shape[i];
+  return n;
+}
+
+// The expert's bindings match the layout the capsule was made for.
+vfm_status capsule_matches(vfm_expert* x, const vfm_capsule* c) {
+  if (c->L != x->L || c->Hkv != x->Hkv || c->d != x->d || c->H != x->H || c->A != x->A || c->S != x->S ||
+      c->act_bf16 != x->act_bf16)
+    return fail(VFM_E_SHAPE, "capsule was made for a different expert layout");
+  if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
+  if (x->prefix_k.shape[1] != c->B || x->prefix_k.shape[2] != c->P)
+    return fail(VFM_E_SHAPE, "capsule holds batch %d, prefix %d; the expert has %lld, %lld bound", c->B, c->P,
+                (long long)x->prefix_k.shape[1], (long long)x->prefix_k.shape[2]);
+  for (const vfm_capsule::Slot& sl : c->slots) {
+    const BoundBuf* b = buf_slot(x, sl.which);
+    if (!b->bound) return fail(VFM_E_UNBOUND, "buffer '%s' is in the capsule but not bound", kBufNames[sl.which]);
+    if (buf_bytes(*b) != sl.bytes) return fail(VFM_E_SHAPE, "buffer '%s' has another shape than in the capsule",
+                                               kBufNames[sl.which]);
+  }
+  return VFM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vfm_status vfm_capsule_create(vfm_expert* x, vfm_capsule** out) {
+  if (!out) return fail(VFM_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
+  if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
+  vfm_capsule* c = new vfm_capsule();
+  c->L = x->L; c->Hkv = x->Hkv; c->d = x->d; c->H = x->H; c->A = x->A; c->S = x->S; c->act_bf16 = x->act_bf16;
+  c->B = (int)x->prefix_k.shape[1];
+  c->P = (int)x->prefix_k.shape[2];
+  c->from_fp8 = x->wprec == VFM_W_FP8;
+  for (int w = 0; w < 5; ++w) {
+    const BoundBuf* b = buf_slot(x, w);
+    if (!b->bound) continue;
+    vfm_capsule::Slot sl;
+    sl.which = w;
+    sl.bytes = buf_bytes(*b);
+    if (sl.bytes > 0 && hipMalloc(&sl.dev, sl.bytes) != hipSuccess) {
+      vfm_capsule_destroy(c);
+      return fail(VFM_E_OOM, "capsule buffer '%s' (%zu bytes)", kBufNames[w], sl.bytes);
+    }
+    c->slots.push_back(sl);
+  }
+  *out = c;
+  return VFM_OK;
+}
+
+vfm_status vfm_capsule_save(vfm_expert* x, vfm_capsule* c, void* stream) {
+  if (!x || !c) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  vfm_status st = capsule_matches(x, c);
+  if (st != VFM_OK) return st;
+  if (c->from_fp8 != (x->wprec == VFM_W_FP8)) return fail(VFM_E_STATE, "capsule and expert differ in FP8-ness");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (const vfm_capsule::Slot& sl : c->slots)
+    if (sl.bytes) HIPCHK(hipMemcpyAsync(sl.dev, buf_slot(x, sl.which)->ptr, sl.bytes, hipMemcpyDeviceToDevice, s));
+  c->act_scale = x->act_scale;
+  c->saved = true;
+  return VFM_OK;
+}
+
+vfm_status vfm_capsule_restore(vfm_expert* x, const vfm_capsule* c, void* stream) {
+  if (!x || !c) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  if (!c->saved) return fail(VFM_E_STATE, "capsule holds no saved state");
+  vfm_status st = capsule_matches(x, c);
+  if (st != VFM_OK) return st;
+  const bool fp8 = x->wprec == VFM_W_FP8 && c->from_fp8;
+  if (fp8 && c->act_scale != x->act_scale) {
+    if (c->act_scale.empty()) {
+      x->act_scale.clear();
+    } else if ((st = vfm_set_act_scales(x, c->act_scale.data(), (int32_t)c->act_scale.size())) != VFM_OK) {
+      return st;
+    }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (const vfm_capsule::Slot& sl : c->slots)
+    if (sl.bytes) HIPCHK(hipMemcpyAsync(buf_slot(x, sl.which)->ptr, sl.dev, sl.bytes, hipMemcpyDeviceToDevice, s));
+  return VFM_OK;
+}
+
+vfm_status vfm_capsule_bytes(const vfm_capsule* c, size_t* bytes) {
+  if (!c || !bytes) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  size_t n = 0;
+  for (const vfm_capsule::Slot& sl : c->slots) n += sl.bytes;
+  *bytes = n;
+  return VFM_OK;
+}
+
+vfm_status vfm_capsule_destroy(vfm_capsule* c) {
+  if (!c) return VFM_OK;
+  (void)hipDeviceSynchronize();
+  for (vfm_capsule::Slot& sl : c->slots)
+    if (sl.dev) (void)hipFree(sl.dev);
+  delete c;
+  return VFM_OK;
+}
+
 vfm_status vfm_expert_destroy(vfm_expert* x) {
   if (!x) return VFM_OK;
   (void)hipDeviceSynchronize();

@@ -24,7 +24,8 @@ ABI_VERSION = 1
 # Every entry point include/vfm.h declares.
 EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
-           "vfm_expert_destroy"]
+           "vfm_expert_destroy", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
+           "vfm_capsule_bytes", "vfm_capsule_destroy"]
 
 
 class VfmError(RuntimeError):
@@ -79,6 +80,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vfm_export.argtypes = [vp, ctypes.c_char_p, vp, ctypes.c_size_t]
     lib.vfm_check.argtypes = [vp, vp]
     lib.vfm_expert_destroy.argtypes = [vp]
+    lib.vfm_capsule_create.argtypes = [vp, ctypes.POINTER(vp)]
+    lib.vfm_capsule_save.argtypes = [vp, vp, vp]
+    lib.vfm_capsule_restore.argtypes = [vp, vp, vp]
+    lib.vfm_capsule_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.vfm_capsule_destroy.argtypes = [vp]
     for n in EXPORTS[2:]:
         getattr(lib, n).restype = st
     if lib.vfm_abi_version() != ABI_VERSION:
@@ -180,10 +186,48 @@ class Expert:
         _check(_lib.vfm_export(self._h, name.encode(), out.ctypes.data, out.nbytes))
         return out
 
+    def capsule(self) -> "Capsule":
+        """A capsule sized for the current bindings (holds no state until saved)."""
+        return Capsule(self)
+
     def close(self) -> None:
         if getattr(self, "_h", None):
             h, self._h = self._h, None
             _check(_lib.vfm_expert_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Capsule:
+    """Snapshot of an expert's bound buffers (and FP8 activation scales):
+    save() and restore() enqueue device-to-device copies on a stream;
+    restore() into another expert of the same layout forks the state."""
+
+    def __init__(self, expert: Expert):
+        h = ctypes.c_void_p()
+        _check(_lib.vfm_capsule_create(expert._h, ctypes.byref(h)))
+        self._h = h
+
+    def save(self, expert: Expert, stream=None) -> None:
+        _check(_lib.vfm_capsule_save(expert._h, self._h, _stream_ptr(stream)))
+
+    def restore(self, expert: Expert, stream=None) -> None:
+        _check(_lib.vfm_capsule_restore(expert._h, self._h, _stream_ptr(stream)))
+
+    @property
+    def nbytes(self) -> int:
+        n = ctypes.c_size_t()
+        _check(_lib.vfm_capsule_bytes(self._h, ctypes.byref(n)))
+        return n.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            _check(_lib.vfm_capsule_destroy(h))
 
     def __del__(self):
         try:
