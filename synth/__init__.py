@@ -21,7 +21,8 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 __all__ = ["ExpertConfig", "CONFIGS", "param_specs", "make_params", "make_inputs",
-           "make_calibration_inputs", "round_to_bf16", "workload"]
+           "make_calibration_inputs", "round_to_bf16", "workload", "PrefixConfig", "PREFIX_CONFIGS",
+           "prefix_param_specs", "make_prefix_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -176,3 +177,66 @@ def make_noise_state(cfg: ExpertConfig, seed: int):
     noise = rng.standard_normal(size=(cfg.batch, cfg.action_horizon, cfg.action_dim), dtype=np.float32)
     state = rng.standard_normal(size=(cfg.batch, cfg.state_dim), dtype=np.float32)
     return noise, state
+
+
+# ---------------------------------------------------------------------------
+# The prefix producer: a Gemma-2B-shaped decoder run once over the
+# vision + language prefix, whose per-layer keys and values are the prefix
+# K/V the action expert attends to.
+# ---------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefixConfig:
+    name: str
+    num_layers: int
+    width: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    mlp_dim: int
+    prefix_len: int
+    batch: int
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+    seed: int = 0
+    weight_std: float = 0.02
+
+    def replace(self, **kw) -> "PrefixConfig":
+        return dataclasses.replace(self, **kw)
+
+
+PREFIX_CONFIGS: Dict[str, PrefixConfig] = {
+    # small correctness case: a prefix that is not a multiple of any tile
+    "prefix_tiny": PrefixConfig(name="prefix_tiny", num_layers=2, width=256, num_q_heads=4, num_kv_heads=1,
+                                head_dim=64, mlp_dim=512, prefix_len=100, batch=1, seed=10),
+    # Gemma-2B shape (18 layers, width 2048, 8 query heads sharing one KV head of
+    # dim 256, GeGLU 16384) over 2 views x 256 image tokens + 48 text tokens
+    "prefix_gemma2b_p560": PrefixConfig(name="prefix_gemma2b_p560", num_layers=18, width=2048, num_q_heads=8,
+                                        num_kv_heads=1, head_dim=256, mlp_dim=16384, prefix_len=560, batch=1,
+                                        seed=11),
+}
+
+
+def prefix_param_specs(cfg: PrefixConfig) -> List[Tuple[str, Tuple[int, ...]]]:
+    """Names and shapes of the prefix decoder's weights, in draw order
+    (matrices [in][out]; norm weights are the w of a (1 + w) gain)."""
+    W, F = cfg.width, cfg.mlp_dim
+    qd, kd = cfg.num_q_heads * cfg.head_dim, cfg.num_kv_heads * cfg.head_dim
+    specs: List[Tuple[str, Tuple[int, ...]]] = []
+    for l in range(cfg.num_layers):
+        p = f"layers.{l}."
+        specs += [(p + "attn_norm.w", (W,)), (p + "q.w", (W, qd)), (p + "k.w", (W, kd)), (p + "v.w", (W, kd)),
+                  (p + "o.w", (qd, W)), (p + "mlp_norm.w", (W,)), (p + "gate.w", (W, F)), (p + "up.w", (W, F)),
+                  (p + "down.w", (F, W))]
+    return specs
+
+
+def make_prefix_inputs(cfg: PrefixConfig, seed: int | None = None):
+    """Return (params, embeds): bf16-grid weights N(0, std^2) in draw order,
+    then the prefix token embeddings [B][P][W] N(0, 1) on the bf16 grid (they
+    stand in for the image-encoder outputs and text-token embeddings)."""
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    params = {n: round_to_bf16(_draw(rng, s, cfg.weight_std)) for n, s in prefix_param_specs(cfg)}
+    embeds = round_to_bf16(rng.standard_normal(size=(cfg.batch, cfg.prefix_len, cfg.width), dtype=np.float32))
+    return params, embeds
