@@ -96,6 +96,65 @@ def flops_per_chunk(cfg) -> float:
     return 2.0 * (gemm + attn) * cfg.num_steps
 
 
+def prefix_flops(cfg) -> float:
+    """Multiply-adds x 2 of one prefix pass: every layer's fused QKV, o,
+    gate/up and down GEMMs and bidirectional attention over its P tokens; the
+    last layer only projects its keys and values."""
+    M = cfg.batch * cfg.prefix_len
+    W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
+    qd, kd = cfg.num_q_heads * d, cfg.num_kv_heads * d
+    layer = M * (W * (qd + 2 * kd) + qd * W + 3 * W * F) + 2 * cfg.batch * cfg.num_q_heads * cfg.prefix_len ** 2 * d
+    return 2.0 * ((L - 1) * layer + M * W * 2 * kd)
+
+
+def bench_prefix(name: str, reps: int, stream, expert=None, expert_bufs=None):
+    """Time the prefix producer on random-init weights of the workload's shape
+    (N(0, 0.02^2) bf16, drawn on the device) and N(0, 1) embeddings; with an
+    expert of matching shape, also the observation-to-actions chain (prefix
+    pass writing the expert's bound K/V buffers, then one denoise call)."""
+    import torch
+    from synth import PREFIX_CONFIGS, prefix_param_specs
+    from vla_flow_matching_pi0_amd import vfm
+    cfg = PREFIX_CONFIGS[name]
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+    w = {n: (torch.randn(s, generator=gen, device="cuda") * cfg.weight_std).to(torch.bfloat16)
+         for n, s in prefix_param_specs(cfg)}
+    pre = vfm.PrefixProducer(cfg, w)
+    del w
+    emb = torch.randn((cfg.batch, cfg.prefix_len, cfg.width), generator=gen, device="cuda").to(torch.bfloat16)
+    shape = (cfg.num_layers, cfg.batch, cfg.prefix_len, cfg.num_kv_heads, cfg.head_dim)
+    chain = expert is not None and tuple(expert_bufs["prefix_k"].shape) == shape
+    pk = expert_bufs["prefix_k"] if chain else torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    pv = expert_bufs["prefix_v"] if chain else torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        pre.run(emb, pk, pv, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        pre.run(emb, pk, pv, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    fl = prefix_flops(cfg)
+    tf = fl / (ms * 1e-3) / 1e12
+    out = {"workload": cfg.name, "ms_per_pass": round(ms, 4), "flop_per_pass": fl,
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}}
+    if chain:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            pre.run(emb, pk, pv, stream)
+            expert.denoise(stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        expert.check(stream)
+        out["chain_ms"] = round(ev[0].elapsed_time(ev[1]) / reps, 4)
+    pre.close()
+    return out
+
+
 def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: float = 10.0):
     """The oracle, untuned, timed on the host cores on a bounded sample:
     `steps` Euler steps of the same chunk, repeated until `min_seconds` have
@@ -134,6 +193,9 @@ def main() -> int:
                     help="between timed calls, stream this many MiB through the caches (cold-cache timing: "
                          "the weights of a quantised expert otherwise stay in the 256 MB last-level cache); "
                          "value is then the mean per-call time")
+    ap.add_argument("--prefix", default="prefix_gemma2b_p560",
+                    help="prefix-producer workload timed after the expert ('none': skip)")
+    ap.add_argument("--prefix-reps", type=int, default=20)
     ap.add_argument("--calib-mib", type=int, default=0,
                     help="after the timed region, run a plain streaming kernel (negation) over this many MiB "
                          "of float32, the reference for scaling HBM counters")
@@ -241,6 +303,10 @@ def main() -> int:
     capsule = {"bytes": cap.nbytes, "save_us": round(save_us, 2), "restore_us": round(restore_us, 2),
                "restore_GBps": round(2 * cap.nbytes / (restore_us * 1e3), 1)}
     cap.close()
+    prefix = None
+    if args.prefix != "none":
+        print(f"[bench] prefix producer {args.prefix}", file=sys.stderr, flush=True)
+        prefix = bench_prefix(args.prefix, args.prefix_reps, stream, ex, bufs)
     if args.calib_mib > 0:
         n = args.calib_mib * (1 << 20) // 4
         src = torch.ones(n, device="cuda")
@@ -287,6 +353,7 @@ def main() -> int:
         "achieved_tflops": round(tflops, 2),
         "sync": sync,
         "capsule": capsule,
+        "prefix_producer": prefix,
         "flush_mib": args.flush_mib,
         "roofline": roofline,
         "cpu_baseline": cpu,

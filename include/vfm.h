@@ -243,6 +243,64 @@ vfm_status vfm_capsule_bytes(const vfm_capsule* cap, size_t* bytes);
 /* Synchronise the device and free the capsule. NULL-safe. */
 vfm_status vfm_capsule_destroy(vfm_capsule* cap);
 
+/* ------------------------------------------------------------------------
+ * Prefix producer. The pages treat the vision + language prefix as the part
+ * of pi0 / pi0.5 that runs once per observation before the action expert,
+ * which reads it only through the cached per-layer keys and values (PhyAI
+ * summary, profiling paragraph: the expert's share of batch-1 latency is what
+ * remains after this pass; the FlashRT forum post lists Pi0 / Pi0.5 as its
+ * flagship VLA integrations). This is that pass for a Gemma-shaped decoder:
+ * per layer, x -> RMSNorm with a (1 + w) gain -> fused Q/K/V projection with
+ * rotary encoding (half-split pairs, positions 0..P-1) -> bidirectional
+ * grouped-query attention over the sample's P tokens -> o projection ->
+ * residual -> RMSNorm (1 + w) -> GeGLU (tanh GELU) MLP -> residual. Its
+ * outputs are every layer's rotary-encoded keys and values, written straight
+ * into the buffers the expert binds as "prefix_k" / "prefix_v". The last
+ * layer's attention output and MLP reach no output and are not computed.
+ * ------------------------------------------------------------------------ */
+typedef struct vfm_prefix vfm_prefix;   /* opaque; owned by the library */
+
+typedef struct {
+  int32_t abi_version;      /* must equal VFM_ABI_VERSION */
+  int32_t num_layers;       /* L in [1, 256]; the expert that reads the K/V has the same L */
+  int32_t width;            /* W, multiple of 128 in [128, 4096] */
+  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads, <= 64; Hq * d multiple of 128 */
+  int32_t num_kv_heads;     /* Hkv >= 1 */
+  int32_t head_dim;         /* d in {64, 128, 256} */
+  int32_t mlp_dim;          /* F, multiple of 64 in [64, 65536] */
+  int32_t max_prefix_len;   /* upper bound of P over all runs, 1..8192 */
+  int32_t max_batch;        /* upper bound of B over all runs, 1..256 */
+  float rope_base;          /* rotary base, > 0 */
+  float rms_eps;            /* RMSNorm epsilon, > 0 */
+} vfm_prefix_config;
+
+/* Create a prefix producer from bf16 weights (row-major [in][out]):
+ * layers.{l}.attn_norm.w [W], layers.{l}.{q,k,v}.w [W][H*d] (head-major
+ * columns), layers.{l}.o.w [Hq*d][W], layers.{l}.mlp_norm.w [W],
+ * layers.{l}.{gate,up}.w [W][F], layers.{l}.down.w [F][W]; norm weights are
+ * the w of the (1 + w) gain. Every name is required (also the last layer's,
+ * though only its attn_norm, k and v are used). Synchronous on `stream`:
+ * repacks the weights into MFMA operand order and allocates all workspace for
+ * max_batch x max_prefix_len tokens; run never allocates. The caller may free
+ * its weight tensors afterwards.
+ * Errors: VFM_E_INVALID_ARG (config, missing / unknown / NULL weight),
+ * VFM_E_SHAPE, VFM_E_DTYPE (weights not bf16), VFM_E_UNSUPPORTED (a buffer
+ * beyond 2 GiB), VFM_E_OOM, VFM_E_HIP. On error *out is NULL. */
+vfm_status vfm_prefix_create(const vfm_prefix_config* cfg, const vfm_tensor* weights, int32_t n_weights,
+                             void* stream, vfm_prefix** out);
+
+/* Run the pass on `stream` (asynchronous): embeds [B][P][W] bf16 token
+ * embeddings (device), prefix_k / prefix_v [L][B][P][Hkv][d] bf16 outputs
+ * (device; the expert's "prefix_k" / "prefix_v" layout). Pointers 16-byte
+ * aligned; the outputs must not alias the input. Errors: VFM_E_INVALID_ARG
+ * (NULL or misaligned pointer), VFM_E_SHAPE (B or P outside [1, max]),
+ * VFM_E_HIP (launch failure). */
+vfm_status vfm_prefix_run(vfm_prefix* pre, const void* embeds, int32_t batch, int32_t prefix_len,
+                          void* prefix_k, void* prefix_v, void* stream);
+
+/* Synchronise the device and free everything the producer owns. NULL-safe. */
+vfm_status vfm_prefix_destroy(vfm_prefix* pre);
+
 #ifdef __cplusplus
 }
 #endif

@@ -136,6 +136,48 @@ def test_null_expert_calls(lib):
     assert lib.vfm_expert_destroy(None) == 0
 
 
+def test_prefix_producer_rejects_bad_configs_and_weights(lib):
+    from synth import PREFIX_CONFIGS, prefix_param_specs
+    cfg = PREFIX_CONFIGS["prefix_tiny"]
+    out = ctypes.c_void_p(0x1234)
+    assert vfm.STATUS[lib.vfm_prefix_create(None, None, 0, None, ctypes.byref(out))] == "VFM_E_INVALID_ARG"
+    assert not out.value
+    for field, value in [("abi_version", 3), ("width", 200), ("head_dim", 32), ("num_q_heads", 3), ("mlp_dim", 100),
+                         ("max_batch", 0), ("max_prefix_len", 0), ("num_layers", 0)]:
+        c = vfm.make_prefix_config(cfg)
+        setattr(c, field, value)
+        st = lib.vfm_prefix_create(ctypes.byref(c), None, 0, None, ctypes.byref(out))
+        assert vfm.STATUS[st] == "VFM_E_INVALID_ARG", field
+        assert not out.value
+    c = vfm.make_prefix_config(cfg.replace(mlp_dim=65536, width=4096), max_batch=256, max_prefix_len=8192)
+    assert vfm.STATUS[lib.vfm_prefix_create(ctypes.byref(c), None, 0, None, ctypes.byref(out))] == "VFM_E_UNSUPPORTED"
+    c = vfm.make_prefix_config(cfg)
+    specs = prefix_param_specs(cfg)
+
+    def arr(drop=None, dtype=vfm.VFM_BF16, grow=None):
+        ts, keep = [], []
+        for name, shape in specs:
+            if name == drop:
+                continue
+            t = vfm.VfmTensor()
+            keep.append(name.encode())
+            t.name, t.dev_ptr, t.dtype, t.ndim = keep[-1], 0x1000, dtype, len(shape)
+            for i, sz in enumerate(shape):
+                t.shape[i] = sz + (1 if name == grow and i == 0 else 0)
+            ts.append(t)
+        return (vfm.VfmTensor * len(ts))(*ts), len(ts), keep
+
+    a, n, keep = arr(drop="layers.1.down.w")
+    assert vfm.STATUS[lib.vfm_prefix_create(ctypes.byref(c), a, n, None, ctypes.byref(out))] == "VFM_E_INVALID_ARG"
+    assert "layers.1.down.w" in lib.vfm_last_error().decode()
+    a, n, keep = arr(dtype=vfm.VFM_F32)
+    assert vfm.STATUS[lib.vfm_prefix_create(ctypes.byref(c), a, n, None, ctypes.byref(out))] == "VFM_E_DTYPE"
+    a, n, keep = arr(grow="layers.0.attn_norm.w")
+    assert vfm.STATUS[lib.vfm_prefix_create(ctypes.byref(c), a, n, None, ctypes.byref(out))] == "VFM_E_SHAPE"
+    assert vfm.STATUS[lib.vfm_prefix_run(None, None, 1, 1, None, None, None)] == "VFM_E_INVALID_ARG"
+    assert lib.vfm_prefix_destroy(None) == 0
+
+
 def test_null_capsule_calls(lib):
     out = ctypes.c_void_p(0x1234)
     assert vfm.STATUS[lib.vfm_capsule_create(None, ctypes.byref(out))] == "VFM_E_INVALID_ARG"

@@ -371,6 +371,18 @@ void plan_gemm(int M, int N, int K, int KB, int nwg, bool linear, int* nt, int* 
 
 }  // namespace
 
+namespace vfm {
+vfm_status report(vfm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+}  // namespace vfm
+
 // The launch parameter block of one call: shapes, weights, workspace,
 // buffers and the GEMM plan for the expert's weight format.
 vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const float* state, float* actions) {

@@ -25,7 +25,8 @@ ABI_VERSION = 1
 EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
            "vfm_expert_destroy", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
-           "vfm_capsule_bytes", "vfm_capsule_destroy"]
+           "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
+           "vfm_prefix_destroy"]
 
 
 class VfmError(RuntimeError):
@@ -42,6 +43,12 @@ class VfmConfig(ctypes.Structure):
         "num_steps")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
                          ("weight_precision", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                          ("w4_group_size", ctypes.c_int32)]
+
+
+class VfmPrefixConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim",
+        "max_prefix_len", "max_batch")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)]
 
 
 class VfmTensor(ctypes.Structure):
@@ -85,6 +92,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vfm_capsule_restore.argtypes = [vp, vp, vp]
     lib.vfm_capsule_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.vfm_capsule_destroy.argtypes = [vp]
+    lib.vfm_prefix_create.argtypes = [ctypes.POINTER(VfmPrefixConfig), ctypes.POINTER(VfmTensor), i32, vp,
+                                      ctypes.POINTER(vp)]
+    lib.vfm_prefix_run.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.vfm_prefix_destroy.argtypes = [vp]
     for n in EXPORTS[2:]:
         getattr(lib, n).restype = st
     if lib.vfm_abi_version() != ABI_VERSION:
@@ -228,6 +239,65 @@ class Capsule:
         if getattr(self, "_h", None):
             h, self._h = self._h, None
             _check(_lib.vfm_capsule_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_prefix_config(cfg, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None) -> VfmPrefixConfig:
+    """C config of the prefix producer from any object with its fields."""
+    c = VfmPrefixConfig()
+    c.abi_version = ABI_VERSION
+    for n in ("num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim"):
+        setattr(c, n, int(getattr(cfg, n)))
+    c.max_prefix_len = int(max_prefix_len or cfg.prefix_len)
+    c.max_batch = int(max_batch or cfg.batch)
+    c.rope_base = float(cfg.rope_base)
+    c.rms_eps = float(cfg.rms_eps)
+    return c
+
+
+def _tensor_array(weights):
+    names = list(weights.keys())
+    arr = (VfmTensor * len(names))()
+    keep = [n.encode() for n in names]
+    for i, n in enumerate(names):
+        t = weights[n]
+        arr[i].name = keep[i]
+        arr[i].dev_ptr = t.data_ptr()
+        arr[i].dtype = _dtype_code(t)
+        arr[i].ndim = t.dim()
+        for j, sz in enumerate(t.shape):
+            arr[i].shape[j] = int(sz)
+    return arr, keep
+
+
+class PrefixProducer:
+    """The vision + language prefix pass that writes the per-layer prefix K/V
+    an Expert binds. weights: name -> bf16 device tensor."""
+
+    def __init__(self, cfg, weights: Mapping[str, "object"], stream=None, max_batch: Optional[int] = None,
+                 max_prefix_len: Optional[int] = None):
+        lib = load_library()
+        self._ccfg = make_prefix_config(cfg, max_batch, max_prefix_len)
+        arr, keep = _tensor_array(weights)
+        h = ctypes.c_void_p()
+        _check(lib.vfm_prefix_create(ctypes.byref(self._ccfg), arr, len(keep), _stream_ptr(stream), ctypes.byref(h)))
+        self._h = h
+
+    def run(self, embeds, prefix_k, prefix_v, stream=None) -> None:
+        """embeds [B][P][W] bf16 -> prefix_k, prefix_v [L][B][P][Hkv][d] bf16 (all device tensors)."""
+        B, P = int(embeds.shape[0]), int(embeds.shape[1])
+        _check(_lib.vfm_prefix_run(self._h, embeds.data_ptr(), B, P, prefix_k.data_ptr(), prefix_v.data_ptr(),
+                                   _stream_ptr(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            _check(_lib.vfm_prefix_destroy(h))
 
     def __del__(self):
         try:
