@@ -1,9 +1,11 @@
-"""CPU oracle of the weight quantisers (FP8 e4m3 per-tensor, int4 group-wise).
+"""CPU oracle of the weight quantisers (FP8 e4m3 per-tensor, int4 group-wise,
+int8 per output channel).
 
 TEST INFRASTRUCTURE ONLY: imported by the tests and never by the product path.
 
 The PhyAI summary ("Real-Time Physical AI at the Edge, Scalable Rollouts in the
-Cloud", optimisation paragraph) lists offline W4A16 and W8A8 quantisation; the
+Cloud", optimisation paragraph) lists offline W4A16, W8A16, W8A8 and W4A8
+quantisation; the
 FlashRT walk-through (component 6, calibration) describes FP8 GEMMs whose
 alpha is the product of an activation scale and a weight scale. The pages fix
 no rounding rule or format details, so this module takes the plainest reading:
@@ -16,13 +18,17 @@ no rounding rule or format details, so this module takes the plainest reading:
 * int4 is symmetric, per output column and per group of 128 consecutive K
   rows: s = float16(amax / 7) (1 if that is 0), q = clip(rint(w / s), -8, 7)
   with the division in float32; the dequantised weight is q * s.
+* W8A16 weights are symmetric int8 per output column over the whole K:
+  s = float32(amax / 127) (1 if amax is 0), q = clip(rint(w / s), -127, 127)
+  with the division in float32 (rint: ties to even); the dequantised weight
+  is q * s and the activations stay bf16.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = ["e4m3_decode", "e4m3_encode", "e4m3_all_values", "quantise_fp8_tensor",
-           "quantise_w4", "dequantised_expert", "E4M3_MAX"]
+           "quantise_w4", "quantise_w8", "dequantised_expert", "E4M3_MAX"]
 
 E4M3_MAX = 448.0
 
@@ -96,14 +102,26 @@ def quantise_w4(w: np.ndarray, group: int = 128):
     return q.reshape(K, N), s16, deq.reshape(K, N)
 
 
+def quantise_w8(w: np.ndarray):
+    """Symmetric int8 per output column. w is [K][N]. Returns (q int8 [K][N],
+    scales float32 [N], dequantised float64 = q * s)."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=0)                                   # [N], exact
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    q = np.clip(np.rint((w32 / s[None, :]).astype(np.float32)), -127, 127).astype(np.int8)
+    deq = q.astype(np.float64) * s[None, :].astype(np.float64)
+    return q, s, deq
+
+
 def dequantised_expert(params, cfg):
     """The expert's parameters with every per-layer GEMM weight replaced by
     the float64 value its quantised form stands for (what the oracle is fed
     for the FP8 and W4A16 experts). FP8 quantises each fused GEMM tensor as a
     whole, [q | k | v] and [gate | up] along the output columns, so the
     fused parts share one scale; int4 scales are per column, so fusion does
-    not matter there. Also returns the FP8 weight scales [L][4] (qkv, o,
-    gate/up, down), or None for W4A16."""
+    not matter there (nor for the per-column int8 of W8A16). Also returns the
+    FP8 weight scales [L][4] (qkv, o, gate/up, down), or None otherwise."""
     out = dict(params)
     L = cfg.num_layers
     if cfg.weight_precision == "fp8":
@@ -120,11 +138,14 @@ def dequantised_expert(params, cfg):
                     out[pre + n + ".w"] = deq[:, c0:c0 + m.shape[1]]
                     c0 += m.shape[1]
         return out, scales
-    if cfg.weight_precision == "w4a16":
+    if cfg.weight_precision in ("w4a16", "w8a16"):
         for l in range(L):
             pre = f"layers.{l}."
             for n in ("q", "k", "v", "o", "gate", "up", "down"):
-                _, _, deq = quantise_w4(params[pre + n + ".w"], cfg.w4_group)
+                if cfg.weight_precision == "w4a16":
+                    _, _, deq = quantise_w4(params[pre + n + ".w"], cfg.w4_group)
+                else:
+                    _, _, deq = quantise_w8(params[pre + n + ".w"])
                 out[pre + n + ".w"] = deq
         return out, None
     raise ValueError(f"{cfg.weight_precision} weights are not quantised")

@@ -120,3 +120,52 @@ def test_dequantised_expert_w4_is_per_matrix():
         _, _, d1 = Q.quantise_w4(params[f"layers.0.{n}.w"], 128)
         assert np.array_equal(deq[f"layers.0.{n}.w"], d1), n
     assert deq["in_proj.w"] is params["in_proj.w"]
+
+
+def test_w8_quantiser():
+    """Per-column int8: the scale is exactly amax / 127 in float32, codes in
+    [-127, 127] with every column's largest magnitude at +-127, error at most
+    half a step, ties to even, grid values round-trip, zero columns get
+    scale 1; cross-checked against torch's own float32 division and
+    round-half-even."""
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((192, 24)) * 0.02).astype(np.float32)
+    w[:, 5] = 0.0
+    q, s, deq = Q.quantise_w8(w)
+    assert q.dtype == np.int8 and q.min() >= -127 and q.max() <= 127
+    amax = np.max(np.abs(w), axis=0)
+    for n in range(24):
+        want = np.float32(1.0) if amax[n] == 0 else np.float32(amax[n] / np.float32(127.0))
+        assert s[n] == want
+    live = amax > 0
+    assert np.all(np.max(np.abs(q[:, live].astype(np.int64)), axis=0) == 127)
+    assert s[5] == 1.0 and np.all(q[:, 5] == 0)
+    assert np.all(np.abs(deq - w.astype(np.float64)) <= s.astype(np.float64)[None, :] / 2 * (1 + 1e-6))
+    tq = torch.clamp(torch.round(torch.from_numpy(w) / torch.from_numpy(s)[None, :]), -127, 127).to(torch.int8)
+    assert np.array_equal(tq.numpy(), q)
+    # exact half steps round to the even code
+    s1 = np.float32(0.5)
+    ww = np.array([[127 * 0.5], [0.75], [1.25], [-0.75], [0.25]], dtype=np.float32)   # quotients 127, 1.5, 2.5, -1.5, 0.5
+    qq, ss, _ = Q.quantise_w8(ww)
+    assert ss[0] == s1
+    assert qq[:, 0].tolist() == [127, 2, 2, -2, 0]
+    # values on the grid keep their codes (the rescale is exact up to float32 rounding of 127 s)
+    grid = (q.astype(np.float32) * s[None, :]).astype(np.float32)
+    q2, s2, d2 = Q.quantise_w8(grid)
+    assert np.array_equal(q2, q)
+    assert np.all(np.abs(s2 / s - 1.0) <= 2.0 ** -22)
+
+
+def test_dequantised_expert_w8_is_per_column():
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["tiny_fp32"].replace(weight_precision="w8a16", num_layers=1)
+    params, *_ = make_inputs(cfg)
+    deq, scales = Q.dequantised_expert(params, cfg)
+    assert scales is None
+    for n in ("q", "k", "v", "o", "gate", "up", "down"):
+        _, _, d1 = Q.quantise_w8(params[f"layers.0.{n}.w"])
+        assert np.array_equal(deq[f"layers.0.{n}.w"], d1), n
+        # slicing columns quantises identically (per-column scales ignore fusion)
+        m = params[f"layers.0.{n}.w"]
+        _, _, d2 = Q.quantise_w8(m[:, : m.shape[1] // 2])
+        assert np.array_equal(d2, d1[:, : m.shape[1] // 2])
