@@ -81,6 +81,9 @@ def algorithmic_bytes_per_step(cfg) -> int:
         gemm = L * per_layer                                  # one byte per weight
     elif cfg.weight_precision == "w4a16":
         gemm = L * per_layer // 2 + L * per_layer // cfg.w4_group * 2   # nibbles + fp16 group scales
+    elif cfg.weight_precision == "w8a16":
+        cols = (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d + W + 2 * F + W
+        gemm = L * per_layer + L * cols * 4                            # int8 codes + fp32 column scales
     else:
         gemm = L * per_layer * act_b
     return gemm + small * act_b + prefix * act_b
@@ -337,7 +340,8 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8e4m3", "w4a16": "int4/bf16"}[cfg.weight_precision],
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8e4m3", "w4a16": "int4/bf16",
+                  "w8a16": "int8/bf16"}[cfg.weight_precision],
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,

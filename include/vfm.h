@@ -56,17 +56,21 @@ typedef enum {
 
 typedef enum { VFM_F32 = 0, VFM_BF16 = 1, VFM_F16 = 2, VFM_FP8_E4M3 = 3, VFM_I4X2 = 4 } vfm_dtype;
 
-/* Storage precision of the per-layer GEMM weights (q/k/v/o/gate/up/down). */
-typedef enum { VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3 } vfm_wprec;
+/* Storage precision of the per-layer GEMM weights (q/k/v/o/gate/up/down):
+ * fp32; bf16; FP8 e4m3 per tensor with FP8 activations (W8A8); int4 with fp16
+ * scales per (column, 128-K group) and bf16 activations (W4A16); int8 with
+ * fp32 scales per output column and bf16 activations (W8A16). The PhyAI
+ * summary's optimisation paragraph lists these offline quantisation modes. */
+typedef enum { VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3, VFM_W_W8A16 = 4 } vfm_wprec;
 
 typedef struct {
   int32_t abi_version;      /* must equal VFM_ABI_VERSION */
   int32_t num_layers;       /* L >= 0 */
-  int32_t width;            /* W, multiple of 256 in [256, 2048] (FP8: of 512, W4A16: of 1024) */
-  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads; Hq * d multiple of 256 (FP8 512, W4A16 1024) */
+  int32_t width;            /* W, multiple of 256 in [256, 2048] (FP8, W8A16: of 512, W4A16: of 1024) */
+  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads; Hq * d multiple of 256 (FP8/W8A16 512, W4A16 1024) */
   int32_t num_kv_heads;     /* Hkv >= 1 */
   int32_t head_dim;         /* d in {64, 128, 256} (fp32 experts: 64, 128) */
-  int32_t mlp_dim;          /* F, multiple of 256 (FP8: 512, W4A16: 1024), <= 65536 */
+  int32_t mlp_dim;          /* F, multiple of 256 (FP8/W8A16: 512, W4A16: 1024), <= 65536 */
   int32_t action_horizon;   /* H, 1..64 action tokens per sample */
   int32_t action_dim;       /* A in {4, 8, 16, 32, 64} */
   int32_t state_dim;        /* S in [0, 4096] (0: no state input) */
@@ -177,7 +181,7 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
 /* Copy a tensor the library holds, as float32, to host memory `dst`
  * (`bytes` must equal 4 * element count):
  *   a per-layer GEMM weight by its create-time name (e.g. "layers.3.q.w"):
- *      the value the kernels multiply by, i.e. dequantised for FP8 / W4A16,
+ *      the value the kernels multiply by, i.e. dequantised for FP8 / W4A16 / W8A16,
  *      row-major [in][out];
  *   "mod_table": [N][2L+1][3][W], (scale, shift, gate) of every norm at
  *      every step (norm order attn_0, mlp_0, ..., final);

@@ -1,7 +1,10 @@
 """GPU parity of the quantised experts (FP8 e4m3 weights with calibrated
-activation scales; int4 weights with fp16 group scales) against the CPU
-oracle fed the same dequantised weights. Tolerance: relative L2 5e-2 on the
-final actions."""
+activation scales; int4 weights with fp16 group scales; int8 weights with
+fp32 column scales) against the CPU oracle fed the same dequantised weights.
+Tolerance: relative L2 5e-2 on the final actions for FP8 and W4A16, whose
+kernels also quantise activations or round the dequantised weights to bf16;
+2e-2 (the bf16 bar) for W8A16, whose int8 codes turn into bf16 exactly and
+whose column scale multiplies the fp32 sum."""
 import numpy as np
 import pytest
 
@@ -44,7 +47,7 @@ def fp8_case():
     return _CACHE["fp8"]
 
 
-@pytest.mark.parametrize("cfgname", ["pi05_fp8_p816", "pi05_w4a16"])
+@pytest.mark.parametrize("cfgname", ["pi05_fp8_p816", "pi05_w4a16", "pi05_w8a16"])
 def test_quantised_export_matches_oracle_quantiser(cfgname):
     """The library's own quantiser (create time, on the GPU) gives exactly
     the oracle's codes and scales: the exported dequantised weights equal
@@ -136,29 +139,30 @@ def test_fp8_set_act_scales_from_oracle():
     assert gu.rel_l2(got, ref) <= 5e-2
 
 
-@pytest.mark.parametrize("mode", ["persistent", "eager"])
-def test_w4a16_matches_oracle(mode):
+@pytest.mark.parametrize("prec,mode", [("w4a16", "persistent"), ("w4a16", "eager"), ("w8a16", "persistent"),
+                                       ("w8a16", "graph")])
+def test_weight_only_quantised_matches_oracle(prec, mode):
     gu = _gu()
-    if "w4" not in _CACHE:
-        cfg = CONFIGS["pi05_w4a16"]
+    if prec not in _CACHE:
+        cfg = CONFIGS["pi05_" + prec]
         params, pk, pv, noise, state = make_inputs(cfg)
         deq, _ = Q.dequantised_expert(params, cfg)
-        _CACHE["w4"] = (cfg, params, (pk, pv, noise, state), O.denoise(deq, noise, state, pk, pv, cfg))
-    cfg, params, ev, ref = _CACHE["w4"]
-    print(f"case w4a16 mode={mode}", flush=True)
+        _CACHE[prec] = (cfg, params, (pk, pv, noise, state), O.denoise(deq, noise, state, pk, pv, cfg))
+    cfg, params, ev, ref = _CACHE[prec]
+    print(f"case {prec} mode={mode}", flush=True)
     got = gu.run_gpu(cfg, params, *ev, mode, repeats=2)
     err = gu.rel_l2(got, ref)
     disp = gu.rel_l2(got - ev[2], ref - ev[2])
-    print(f"w4a16 {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
-    assert err <= 5e-2
+    print(f"{prec} {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
+    assert err <= (5e-2 if prec == "w4a16" else 2e-2)
 
 
-@pytest.mark.parametrize("prec", ["fp8", "w4a16"])
+@pytest.mark.parametrize("prec", ["fp8", "w4a16", "w8a16"])
 def test_quantised_ragged_shapes(prec):
     """Quantised experts at batch 2 with a prefix that is not a multiple of
     the key split, a horizon that is not a multiple of 16 and a state input."""
     gu = _gu()
-    cfg = CONFIGS["pi05_fp8_p816" if prec == "fp8" else "pi05_w4a16"].replace(
+    cfg = CONFIGS["pi05_fp8_p816" if prec == "fp8" else "pi05_" + prec].replace(
         num_layers=2, batch=2, prefix_len=37, action_horizon=13, state_dim=5)
     params, pk, pv, noise, state = make_inputs(cfg)
     deq, _ = Q.dequantised_expert(params, cfg)
@@ -177,4 +181,4 @@ def test_quantised_ragged_shapes(prec):
         ex.close()
         err = gu.rel_l2(got, ref)
         print(f"{prec} ragged {mode}: rel_l2={err:.3e}")
-        assert err <= 5e-2, mode
+        assert err <= (2e-2 if prec == "w8a16" else 5e-2), mode

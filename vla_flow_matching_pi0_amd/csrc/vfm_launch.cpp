@@ -13,6 +13,7 @@ VFM_DECLARE_KERNEL_SET(ks_bf16)
 VFM_DECLARE_KERNEL_SET(ks_cal)
 VFM_DECLARE_KERNEL_SET(ks_fp8)
 VFM_DECLARE_KERNEL_SET(ks_w4)
+VFM_DECLARE_KERNEL_SET(ks_i8)
 
 size_t lds_bytes(const VP& p, int act_bytes) {
   const size_t nwaves = NTHREADS / 64;
@@ -31,6 +32,7 @@ hipError_t prepare_kernels(int kset, int d, int lds) {
     case KS_CAL: return ks_cal_prepare(d, lds);
     case KS_FP8: return ks_fp8_prepare(d, lds);
     case KS_W4: return ks_w4_prepare(d, lds);
+    case KS_I8: return ks_i8_prepare(d, lds);
     default: return hipErrorInvalidValue;
   }
 }
@@ -43,6 +45,7 @@ hipError_t launch_phase(const VP& p, int kset, int mode, int phase, int k, int l
     case KS_CAL: return ks_cal_launch(p, mode, phase, k, l, grid, lds, st);
     case KS_FP8: return ks_fp8_launch(p, mode, phase, k, l, grid, lds, st);
     case KS_W4: return ks_w4_launch(p, mode, phase, k, l, grid, lds, st);
+    case KS_I8: return ks_i8_launch(p, mode, phase, k, l, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -55,6 +58,7 @@ hipError_t max_cooperative_grid(int kset, int d, size_t lds, int* grid) {
     case KS_BF16: e = ks_bf16_occupancy(d, lds, &per_cu); break;
     case KS_FP8: e = ks_fp8_occupancy(d, lds, &per_cu); break;
     case KS_W4: e = ks_w4_occupancy(d, lds, &per_cu); break;
+    case KS_I8: e = ks_i8_occupancy(d, lds, &per_cu); break;
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

@@ -57,7 +57,7 @@ struct VP {
 };
 
 // Kernel sets: activation type x weight format (x calibration).
-enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4 };
+enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4, KS_I8 = 5 };
 constexpr int ATT_KEYS_HOST = 64;   // keys per attention split (the kernels' ATT_KEYS)
 constexpr int MAX_A_HOST = 64;      // largest action dim (the kernels' MAX_A)
 
@@ -75,7 +75,8 @@ hipError_t pack_weight(uint8_t* dst, int K, int Npk, const int* d_col_src, const
                        int src_bf16, int dst_bf16, hipStream_t st);
 hipError_t to_f32(float* dst, const void* src, size_t n, int src_bf16, hipStream_t st);
 // quantised packing (bf16 masters): fmt 0 = FP8 e4m3 per tensor (scale from
-// *amax), 1 = int4 with fp16 scales per (column, 128-K group)
+// *amax), 1 = int4 with fp16 scales per (column, 128-K group), 2 = int8 with
+// fp32 scales per output column
 hipError_t amax_into(unsigned* out, const void* src, size_t n, int src_bf16, hipStream_t st);
 hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col_src, const int* d_col_idx,
                          const void* s0, int n0, const void* s1, int n1, const void* s2, int n2, const unsigned* amax,

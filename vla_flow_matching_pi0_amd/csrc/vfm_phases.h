@@ -373,9 +373,13 @@ constexpr int GEMM_PASS = 4;     // MFMA k blocks per wave per pass
 //   WF_W4      symmetric int4 with an fp16 scale per (column, 128-K group),
 //              R = 4: word r holds the 8 nibbles of block r, dequantised to
 //              bf16 in registers before the MFMA (the W4A16 variant of the
-//              PhyAI optimisation paragraph).
-enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2 };
-template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : WF == WF_FP8 ? 2 : 4; };
+//              PhyAI optimisation paragraph);
+//   WF_I8      symmetric int8 with an fp32 scale per output column (W8A16),
+//              R = 2: bytes 8r..8r+7 are the codes of block r, turned into
+//              bf16 in registers (exact: |q| <= 127) before the MFMA; the
+//              column scale multiplies the accumulated sum in the epilogue.
+enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2, WF_I8 = 3 };
+template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : WF == WF_W4 ? 4 : 2; };
 
 // Weight fragments of one pass of one unit, held in registers. The
 // persistent kernel loads a workgroup's first pass of the next GEMM while it
@@ -387,7 +391,7 @@ struct WPre {
 
 struct GemmShape {
   const uint8_t* Wp;
-  const uint8_t* Ws;       // WF_W4: scales [N/16][K/128][16] fp16, after the codes
+  const uint8_t* Ws;       // after the codes: WF_W4 scales [N/16][K/128][16] fp16, WF_I8 scales [N] fp32
   int K, N, nt, S, ngroups, units, nkb, KR, nkbw;
 };
 
@@ -399,7 +403,7 @@ __device__ __forceinline__ GemmShape gemm_shape(const VP& p, int layer) {
   else if (WHICH == G_O) { g.K = p.Hq * p.d; g.N = p.W; g.Wp = p.w_o[layer]; }
   else if (WHICH == G_GU) { g.K = p.W; g.N = 2 * p.F; g.Wp = p.w_gu[layer]; }
   else { g.K = p.F; g.N = p.W; g.Wp = p.w_down[layer]; }
-  g.Ws = g.Wp + (size_t)g.N * g.K / 2;
+  g.Ws = g.Wp + (WF == WF_I8 ? (size_t)g.N * g.K : (size_t)g.N * g.K / 2);
   g.nt = p.gp_nt[WHICH];
   g.S = p.gp_s[WHICH];
   g.ngroups = g.N / (16 * g.nt);
@@ -464,6 +468,21 @@ __device__ __forceinline__ u32x4 w4_to_bf16(uint32_t wd, uint32_t scale_bits) {
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
+// 8 int8 codes (byte e of the pair of words is element e) -> 8 bf16, exact
+// since |q| <= 127 needs 7 significand bits: the upper half of the float32.
+__device__ __forceinline__ u32x4 i8_to_bf16(uint32_t lo, uint32_t hi) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t wd = q < 2 ? lo : hi;
+    const int b = 2 * (q & 1);
+    const float f0 = (float)((int)(wd << (24 - 8 * b)) >> 24);
+    const float f1 = (float)((int)(wd << (16 - 8 * b)) >> 24);
+    o[q] = (__builtin_bit_cast(uint32_t, f0) >> 16) | (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u);
+  }
+  return o;
+}
+
 // Largest |x| of a lane's 16-byte activation fragment (calibration).
 template <typename T>
 __device__ __forceinline__ float frag_amax(u32x4 a) {
@@ -524,6 +543,9 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       const int i = gm % p.H, j0 = tt * 8 + 2 * g;
       rot = as_f4(ld16_if(rsrc(p.rope), (uint32_t)((((size_t)i * (p.d / 2) + j0) * 2) * 4), ok));
     }
+    // W8A16: the column scales of that epilogue item, fetched up front too
+    floatx4 csc = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (WF == WF_I8) csc = as_f4(ld16_if(rsrc(gs.Ws), (uint32_t)(((t0 + wv / 4) * 16 + 4 * g) * 4), wv < nt * 4));
     const auto ars = rsrc(A);
     for (int pb = 0; pb < nkbw; pb += PW) {
       WPre wl;
@@ -583,6 +605,14 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
             for (int st = 0; st < 4; ++st)
               if (t < nt) acc[t][st] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w8, a8[st], acc[t][st], 0, 0, 0);
           }
+        } else if constexpr (WF == WF_I8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 wb = i8_to_bf16(wl.w[t][i][2 * r], wl.w[t][i][2 * r + 1]);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              if (t < nt) acc[t][st] = MT<T>::mma(wb, ar[st][j], acc[t][st]);
+          }
         } else {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -611,6 +641,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       if constexpr (WF == WF_FP8) v *= alpha;
       const int gm = m0 + st * 16 + c16;
       const int tile = t0 + t;
+      if constexpr (WF == WF_I8) v *= csc;
       if (gm < p.M) {
         if (WHICH == G_QKV) {
           const int d = p.d, hd = d / 2;

@@ -172,6 +172,49 @@ __global__ void k_pack_w4(uint8_t* dst, int K, int Npk, const int* col_src, cons
   }
 }
 
+// int8 (W8A16) column scales: one thread per packed column, s = amax / 127
+// over the whole K (1 if amax is 0), stored fp32 after the codes.
+template <typename TS>
+__global__ void k_scale_i8(float* scales, int K, int Npk, const int* col_src, const int* col_idx, const TS* s0, int n0,
+                           const TS* s1, int n1, const TS* s2, int n2) {
+  for (int pc = blockIdx.x * blockDim.x + threadIdx.x; pc < Npk; pc += gridDim.x * blockDim.x) {
+    const int sid = col_src[pc], col = col_idx[pc];
+    const TS* src = sid == 0 ? s0 : sid == 1 ? s1 : s2;
+    const int ld = sid == 0 ? n0 : sid == 1 ? n1 : n2;
+    float amax = 0.0f;
+    for (int k = 0; k < K; ++k) amax = fmaxf(amax, fabsf(to_f(src[(size_t)k * ld + col])));
+    scales[pc] = amax > 0.0f ? amax / 127.0f : 1.0f;
+  }
+}
+
+// int8 packing: one thread per (tile, 64-K block, lane), the FP8 byte order
+// (byte 8r + e is k = 64 kb + 32 r + 8 g + e); q = clip(rint(w / s), -127, 127).
+template <typename TS>
+__global__ void k_pack_i8(uint8_t* dst, int K, int Npk, const int* col_src, const int* col_idx, const TS* s0, int n0,
+                          const TS* s1, int n1, const TS* s2, int n2) {
+  const int nkb = K / 64;
+  const size_t total = (size_t)(Npk / 16) * nkb * 64;
+  const float* scales = reinterpret_cast<const float*>(dst + (size_t)Npk * K);
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    const int kb = (int)((idx / 64) % nkb);
+    const int t = (int)(idx / 64 / nkb);
+    const int pc = t * 16 + (lane & 15), g = lane >> 4;
+    const int sid = col_src[pc], col = col_idx[pc];
+    const TS* src = sid == 0 ? s0 : sid == 1 ? s1 : s2;
+    const int ld = sid == 0 ? n0 : sid == 1 ? n1 : n2;
+    const float s = scales[pc];
+    uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int k = kb * 64 + (e / 8) * 32 + 8 * g + e % 8;
+      const float q = fminf(fmaxf(rintf(to_f(src[(size_t)k * ld + col]) / s), -127.0f), 127.0f);
+      wd[e / 4] |= ((uint32_t)(int)q & 255u) << (8 * (e % 4));
+    }
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+  }
+}
+
 // Calibration: the bf16 packed stream (32-K blocks) of an FP8 packed weight,
 // holding decode(code) * scale rounded to bf16.
 __global__ void k_fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax_bits) {
@@ -198,9 +241,16 @@ hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col
   if (fmt == 0)
     hipLaunchKernelGGL((k_pack_fp8<bf16>), dim3(blocks), dim3(256), 0, st, dst, K, Npk, d_col_src, d_col_idx,
                        (const bf16*)s0, n0, (const bf16*)s1, n1, (const bf16*)s2, n2, amax);
-  else
+  else if (fmt == 1)
     hipLaunchKernelGGL((k_pack_w4<bf16>), dim3(blocks), dim3(256), 0, st, dst, K, Npk, d_col_src, d_col_idx,
                        (const bf16*)s0, n0, (const bf16*)s1, n1, (const bf16*)s2, n2);
+  else {
+    hipLaunchKernelGGL((k_scale_i8<bf16>), dim3((Npk + 255) / 256), dim3(256), 0, st,
+                       reinterpret_cast<float*>(dst + (size_t)Npk * K), K, Npk, d_col_src, d_col_idx, (const bf16*)s0,
+                       n0, (const bf16*)s1, n1, (const bf16*)s2, n2);
+    hipLaunchKernelGGL((k_pack_i8<bf16>), dim3(blocks), dim3(256), 0, st, dst, K, Npk, d_col_src, d_col_idx,
+                       (const bf16*)s0, n0, (const bf16*)s1, n1, (const bf16*)s2, n2);
+  }
   return hipGetLastError();
 }
 

@@ -158,15 +158,15 @@ vfm_status validate_config(const vfm_config* c) {
   if (c->num_steps < 1 || c->num_steps > 1000) return fail(VFM_E_INVALID_ARG, "num_steps %d outside [1, 1000]", c->num_steps);
   if (!(c->rope_base > 0.f)) return fail(VFM_E_INVALID_ARG, "rope_base must be > 0");
   if (!(c->rms_eps > 0.f)) return fail(VFM_E_INVALID_ARG, "rms_eps must be > 0");
-  if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W4A16)
+  if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W8A16)
     return fail(VFM_E_INVALID_ARG, "weight_precision %d unknown", c->weight_precision);
   if (c->weight_precision == VFM_W_FP32 && c->act_dtype != VFM_F32)
     return fail(VFM_E_INVALID_ARG, "fp32 weights need act_dtype VFM_F32");
   if (c->weight_precision != VFM_W_FP32 && c->act_dtype != VFM_BF16)
     return fail(VFM_E_INVALID_ARG, "16-bit and quantised weights need act_dtype VFM_BF16");
-  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16) {
+  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16 || c->weight_precision == VFM_W_W8A16) {
     // every wave of a GEMM workgroup takes at least one 16-byte weight block
-    const int span = (c->weight_precision == VFM_W_FP8 ? 64 : 128) * (vfm::NTHREADS / 64);
+    const int span = (c->weight_precision == VFM_W_W4A16 ? 128 : 64) * (vfm::NTHREADS / 64);
     if (c->width % span || (c->num_q_heads * c->head_dim) % span || c->mlp_dim % span)
       return fail(VFM_E_INVALID_ARG, "quantised weights need width, num_q_heads * head_dim and mlp_dim to be "
                   "multiples of %d", span);
@@ -444,8 +444,8 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   tmp.src_bf16 = cfg->weight_precision != VFM_W_FP32;
   tmp.wprec = cfg->weight_precision;
   tmp.kset = tmp.wprec == VFM_W_FP32 ? vfm::KS_F32 : tmp.wprec == VFM_W_BF16 ? vfm::KS_BF16
-           : tmp.wprec == VFM_W_FP8 ? vfm::KS_FP8 : vfm::KS_W4;
-  tmp.KW = tmp.wprec == VFM_W_FP32 ? 16 : tmp.wprec == VFM_W_BF16 ? 32 : tmp.wprec == VFM_W_FP8 ? 64 : 128;
+           : tmp.wprec == VFM_W_FP8 ? vfm::KS_FP8 : tmp.wprec == VFM_W_W8A16 ? vfm::KS_I8 : vfm::KS_W4;
+  tmp.KW = tmp.wprec == VFM_W_FP32 ? 16 : tmp.wprec == VFM_W_BF16 ? 32 : tmp.wprec == VFM_W_W4A16 ? 128 : 64;
   tmp.L = cfg->num_layers; tmp.W = cfg->width; tmp.Hq = cfg->num_q_heads; tmp.Hkv = cfg->num_kv_heads;
   tmp.d = cfg->head_dim; tmp.F = cfg->mlp_dim; tmp.H = cfg->action_horizon; tmp.A = cfg->action_dim;
   tmp.S = cfg->state_dim; tmp.E = cfg->time_emb_dim; tmp.N = cfg->num_steps;
@@ -510,9 +510,11 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     fail(VFM_E_OOM, "column map upload failed");
     return bail(VFM_E_OOM);
   }
-  // packed bytes of a K x N weight (W4: codes then fp16 group scales)
+  // packed bytes of a K x N weight (W4: codes then fp16 group scales; W8A16:
+  // codes then fp32 column scales)
   auto wbytes = [&](size_t K, size_t N) -> size_t {
     if (x->wprec == VFM_W_FP8) return K * N;
+    if (x->wprec == VFM_W_W8A16) return K * N + N * 4;
     if (x->wprec == VFM_W_W4A16) return K * N / 2 + (K / 128) * N * 2;
     return K * N * ab;
   };
@@ -539,7 +541,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
         return bail(VFM_E_HIP);
       }
     } else {
-      const int fmt = x->wprec == VFM_W_FP8 ? 0 : 1;
+      const int fmt = x->wprec == VFM_W_FP8 ? 0 : x->wprec == VFM_W_W4A16 ? 1 : 2;
       unsigned* am = x->wamax ? x->wamax + 4 * l : nullptr;
       if (fmt == 0) {
         // one scale per fused tensor: [q | k | v] and [gate | up] share theirs
@@ -962,6 +964,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   const int gi = (w == "q" || w == "k" || w == "v") ? 0 : w == "o" ? 1 : (w == "gate" || w == "up") ? 2 : 3;
   size_t nbytes;
   if (x->wprec == VFM_W_FP8) nbytes = (size_t)K * Npk;
+  else if (x->wprec == VFM_W_W8A16) nbytes = (size_t)K * Npk + (size_t)Npk * 4;
   else if (x->wprec == VFM_W_W4A16) nbytes = (size_t)K * Npk / 2 + (size_t)(K / 128) * Npk * 2;
   else nbytes = (size_t)K * Npk * (x->act_bf16 ? 2 : 4);
   std::vector<uint8_t> host(nbytes);
@@ -981,6 +984,13 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
         const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
         const uint8_t c = host[(((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + r * 8 + e];
         v = e4m3_value(c) * x->wscale[(size_t)l * 4 + gi];
+      } else if (x->wprec == VFM_W_W8A16) {
+        // byte 8r + e of lane (g, c16) holds k = 64 kb + 32 r + 8 g + e; column scales after the codes
+        const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
+        const int8_t q = (int8_t)host[(((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16 + r * 8 + e];
+        float sc;
+        memcpy(&sc, &host[(size_t)K * Npk + (size_t)pc * 4], 4);
+        v = (float)q * sc;
       } else if (x->wprec == VFM_W_W4A16) {
         // nibble 8r + e of lane (g, c16) holds k = 128 kb + 32 r + 8 g + e
         const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
