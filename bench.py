@@ -79,7 +79,7 @@ def algorithmic_bytes_per_step(cfg) -> int:
     act_b = 4 if cfg.weight_precision == "fp32" else 2
     if cfg.weight_precision == "fp8":
         gemm = L * per_layer                                  # one byte per weight
-    elif cfg.weight_precision == "w4a16":
+    elif cfg.weight_precision in ("w4a16", "w4a8"):
         gemm = L * per_layer // 2 + L * per_layer // cfg.w4_group * 2   # nibbles + fp16 group scales
     elif cfg.weight_precision == "w8a16":
         cols = (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d + W + 2 * F + W
@@ -229,7 +229,7 @@ def main() -> int:
     if cfg.state_dim:
         bufs["state"] = torch.from_numpy(state).to("cuda")
     stream = torch.cuda.current_stream()
-    if cfg.weight_precision == "fp8":
+    if cfg.weight_precision in ("fp8", "w4a8"):
         # activation scales from one calibration pass over a separate draw
         cpk, cpv, cnoise, cstate = make_calibration_inputs(cfg)
         cal = {"prefix_k": torch.from_numpy(cpk).to("cuda").to(wdt), "prefix_v": torch.from_numpy(cpv).to("cuda").to(wdt),
@@ -341,7 +341,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8e4m3", "w4a16": "int4/bf16",
-                  "w8a16": "int8/bf16"}[cfg.weight_precision],
+                  "w8a16": "int8/bf16", "w4a8": "int4/fp8e4m3"}[cfg.weight_precision],
         "data": "synthetic",
         "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,

@@ -59,18 +59,23 @@ typedef enum { VFM_F32 = 0, VFM_BF16 = 1, VFM_F16 = 2, VFM_FP8_E4M3 = 3, VFM_I4X
 /* Storage precision of the per-layer GEMM weights (q/k/v/o/gate/up/down):
  * fp32; bf16; FP8 e4m3 per tensor with FP8 activations (W8A8); int4 with fp16
  * scales per (column, 128-K group) and bf16 activations (W4A16); int8 with
- * fp32 scales per output column and bf16 activations (W8A16). The PhyAI
- * summary's optimisation paragraph lists these offline quantisation modes. */
-typedef enum { VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3, VFM_W_W8A16 = 4 } vfm_wprec;
+ * fp32 scales per output column and bf16 activations (W8A16); the int4
+ * weights of W4A16 with the FP8 activations of W8A8 (W4A8). The PhyAI
+ * summary's optimisation paragraph lists these offline quantisation modes.
+ * FP8 and W4A8 experts need activation scales (vfm_calibrate or
+ * vfm_set_act_scales) before they can denoise. */
+typedef enum {
+  VFM_W_FP32 = 0, VFM_W_BF16 = 1, VFM_W_FP8 = 2, VFM_W_W4A16 = 3, VFM_W_W8A16 = 4, VFM_W_W4A8 = 5
+} vfm_wprec;
 
 typedef struct {
   int32_t abi_version;      /* must equal VFM_ABI_VERSION */
   int32_t num_layers;       /* L >= 0 */
-  int32_t width;            /* W, multiple of 256 in [256, 2048] (FP8, W8A16: of 512, W4A16: of 1024) */
-  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads; Hq * d multiple of 256 (FP8/W8A16 512, W4A16 1024) */
+  int32_t width;            /* W, multiple of 256 in [256, 2048] (FP8, W8A16: of 512, W4A16, W4A8: of 1024) */
+  int32_t num_q_heads;      /* Hq, multiple of num_kv_heads; Hq * d multiple of 256 (FP8/W8A16 512, W4A16/W4A8 1024) */
   int32_t num_kv_heads;     /* Hkv >= 1 */
   int32_t head_dim;         /* d in {64, 128, 256} (fp32 experts: 64, 128) */
-  int32_t mlp_dim;          /* F, multiple of 256 (FP8/W8A16: 512, W4A16: 1024), <= 65536 */
+  int32_t mlp_dim;          /* F, multiple of 256 (FP8/W8A16: 512, W4A16/W4A8: 1024), <= 65536 */
   int32_t action_horizon;   /* H, 1..64 action tokens per sample */
   int32_t action_dim;       /* A in {4, 8, 16, 32, 64} */
   int32_t state_dim;        /* S in [0, 4096] (0: no state input) */
@@ -82,7 +87,7 @@ typedef struct {
   float rms_eps;            /* RMSNorm epsilon, > 0 */
   int32_t weight_precision; /* vfm_wprec */
   int32_t act_dtype;        /* VFM_F32 (with VFM_W_FP32) or VFM_BF16 (all others) */
-  int32_t w4_group_size;    /* 128 for VFM_W_W4A16, ignored otherwise */
+  int32_t w4_group_size;    /* 128 for VFM_W_W4A16 and VFM_W_W4A8, ignored otherwise */
 } vfm_config;
 
 /* A named weight handed to vfm_expert_create. Matrices are row-major
@@ -158,34 +163,35 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  * Errors: VFM_E_INVALID_ARG for an unknown key or value. */
 vfm_status vfm_set_option(vfm_expert* ex, const char* key, const char* value);
 
-/* FP8 experts: one measurement pass, as in the FlashRT walk-through
+/* FP8 and W4A8 experts: one measurement pass, as in the FlashRT walk-through
  * (component 6, calibration): run the whole denoise loop once on the bound
  * buffers (prefix_k, prefix_v, noise, state; `actions` is overwritten) in
- * bf16, with the dequantised FP8 weights materialised in bf16 for the pass
+ * bf16, with the dequantised weights materialised in bf16 for the pass
  * only, record the largest |input| of every GEMM (4 per layer, over all
  * steps), and set act_scale = amax / 448 (1 where amax is 0); the GEMM
- * epilogues then use alpha = act_scale * weight_scale. An FP8 expert's
- * denoise returns VFM_E_STATE until this or vfm_set_act_scales has run.
+ * epilogues then use alpha = act_scale * weight_scale (W4A8: act_scale, the
+ * group scales being applied inside the GEMM). Such an expert's denoise
+ * returns VFM_E_STATE until this or vfm_set_act_scales has run.
  * Synchronous on `stream`; invalidates captured graphs.
- * Errors: VFM_E_STATE (not FP8), VFM_E_UNBOUND / VFM_E_SHAPE (buffers),
- * VFM_E_OOM, VFM_E_HIP. */
+ * Errors: VFM_E_STATE (not FP8 / W4A8), VFM_E_UNBOUND / VFM_E_SHAPE
+ * (buffers), VFM_E_OOM, VFM_E_HIP. */
 vfm_status vfm_calibrate(vfm_expert* ex, void* stream);
 
 /* Set the n = 4 * L FP8 activation scales directly (host array, order per
  * layer: qkv input, o input, gate/up input, down input; each > 0), e.g.
  * scales cached from an earlier calibration. Synchronises the device.
- * Errors: VFM_E_STATE (not FP8), VFM_E_SHAPE (n != 4 * L),
+ * Errors: VFM_E_STATE (not FP8 / W4A8), VFM_E_SHAPE (n != 4 * L),
  * VFM_E_INVALID_ARG (a scale not positive and finite). */
 vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
 
 /* Copy a tensor the library holds, as float32, to host memory `dst`
  * (`bytes` must equal 4 * element count):
  *   a per-layer GEMM weight by its create-time name (e.g. "layers.3.q.w"):
- *      the value the kernels multiply by, i.e. dequantised for FP8 / W4A16 / W8A16,
+ *      the value the kernels multiply by, i.e. dequantised for the quantised formats,
  *      row-major [in][out];
  *   "mod_table": [N][2L+1][3][W], (scale, shift, gate) of every norm at
  *      every step (norm order attn_0, mlp_0, ..., final);
- *   "weight_scales", "act_scales" (FP8 only): [L][4] per-GEMM scales
+ *   "weight_scales" (FP8), "act_scales" (FP8, W4A8): [L][4] per-GEMM scales
  *      (qkv, o, gate/up, down); act_scales needs a calibration first;
  *   "trace": the phase timeline of the last persistent call (option "trace").
  * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE,

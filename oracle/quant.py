@@ -117,7 +117,7 @@ def quantise_w8(w: np.ndarray):
 def dequantised_expert(params, cfg):
     """The expert's parameters with every per-layer GEMM weight replaced by
     the float64 value its quantised form stands for (what the oracle is fed
-    for the FP8 and W4A16 experts). FP8 quantises each fused GEMM tensor as a
+    for the quantised experts). FP8 quantises each fused GEMM tensor as a
     whole, [q | k | v] and [gate | up] along the output columns, so the
     fused parts share one scale; int4 scales are per column, so fusion does
     not matter there (nor for the per-column int8 of W8A16). Also returns the
@@ -138,11 +138,13 @@ def dequantised_expert(params, cfg):
                     out[pre + n + ".w"] = deq[:, c0:c0 + m.shape[1]]
                     c0 += m.shape[1]
         return out, scales
-    if cfg.weight_precision in ("w4a16", "w8a16"):
+    if cfg.weight_precision in ("w4a16", "w8a16", "w4a8"):
+        # W4A8 stores the weights of W4A16 (its e4m3 activations are the
+        # kernels' rounding of the GEMM inputs, like FP8's)
         for l in range(L):
             pre = f"layers.{l}."
             for n in ("q", "k", "v", "o", "gate", "up", "down"):
-                if cfg.weight_precision == "w4a16":
+                if cfg.weight_precision in ("w4a16", "w4a8"):
                     _, _, deq = quantise_w4(params[pre + n + ".w"], cfg.w4_group)
                 else:
                     _, _, deq = quantise_w8(params[pre + n + ".w"])

@@ -43,7 +43,7 @@ class ExpertConfig:
     num_steps: int = 10
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
-    weight_precision: str = "fp32"     # fp32 | bf16 | fp8 | w4a16 | w8a16
+    weight_precision: str = "fp32"     # fp32 | bf16 | fp8 | w4a16 | w8a16 | w4a8
     w4_group: int = 128
     seed: int = 0
     weight_std: float = 0.02
@@ -82,6 +82,7 @@ CONFIGS: Dict[str, ExpertConfig] = {
     "pi05_w4a16": _pi05("pi05_w4a16", weight_precision="w4a16", seed=3),
     "pi05_bf16_b32": _pi05("pi05_bf16_b32", batch=32, seed=4),
     "pi05_w8a16": _pi05("pi05_w8a16", weight_precision="w8a16", seed=5),
+    "pi05_w4a8": _pi05("pi05_w4a8", weight_precision="w4a8", seed=6),
 }
 
 

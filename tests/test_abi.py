@@ -69,7 +69,7 @@ def test_create_rejects_bad_configs(lib):
 def test_create_rejects_quantised_shapes_it_cannot_split(lib):
     """FP8 and int4 weights need every K to hold at least one 16-byte weight
     block per wave (512 and 1024 K values); W4A16 is built for group 128."""
-    for prec, width in [("fp8", 256), ("w4a16", 512), ("w8a16", 256)]:
+    for prec, width in [("fp8", 256), ("w4a16", 512), ("w8a16", 256), ("w4a8", 512)]:
         c = vfm.make_config(CONFIGS["pi05_bf16_b1"].replace(weight_precision=prec, width=width))
         st, out = _create(lib, c)
         assert vfm.STATUS[st] == "VFM_E_INVALID_ARG", prec
@@ -77,7 +77,7 @@ def test_create_rejects_quantised_shapes_it_cannot_split(lib):
     c = vfm.make_config(CONFIGS["pi05_w4a16"])
     c.w4_group_size = 64
     assert vfm.STATUS[_create(lib, c)[0]] == "VFM_E_UNSUPPORTED"
-    for name in ("pi05_fp8_p816", "pi05_w4a16", "pi05_w8a16"):   # valid: fails later, for want of weights
+    for name in ("pi05_fp8_p816", "pi05_w4a16", "pi05_w8a16", "pi05_w4a8"):   # valid: fails later, for want of weights
         assert vfm.STATUS[_create(lib, vfm.make_config(CONFIGS[name]))[0]] == "VFM_E_INVALID_ARG"
 
 

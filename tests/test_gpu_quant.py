@@ -1,10 +1,11 @@
 """GPU parity of the quantised experts (FP8 e4m3 weights with calibrated
 activation scales; int4 weights with fp16 group scales; int8 weights with
-fp32 column scales) against the CPU oracle fed the same dequantised weights.
-Tolerance: relative L2 5e-2 on the final actions for FP8 and W4A16, whose
-kernels also quantise activations or round the dequantised weights to bf16;
-2e-2 (the bf16 bar) for W8A16, whose int8 codes turn into bf16 exactly and
-whose column scale multiplies the fp32 sum."""
+fp32 column scales; int4 weights with calibrated e4m3 activations) against
+the CPU oracle fed the same dequantised weights. Tolerance: relative L2 5e-2
+on the final actions for FP8, W4A16 and W4A8, whose kernels also quantise
+activations or round the dequantised weights to bf16; 2e-2 (the bf16 bar)
+for W8A16, whose int8 codes turn into bf16 exactly and whose column scale
+multiplies the fp32 sum."""
 import numpy as np
 import pytest
 
@@ -47,7 +48,7 @@ def fp8_case():
     return _CACHE["fp8"]
 
 
-@pytest.mark.parametrize("cfgname", ["pi05_fp8_p816", "pi05_w4a16", "pi05_w8a16"])
+@pytest.mark.parametrize("cfgname", ["pi05_fp8_p816", "pi05_w4a16", "pi05_w8a16", "pi05_w4a8"])
 def test_quantised_export_matches_oracle_quantiser(cfgname):
     """The library's own quantiser (create time, on the GPU) gives exactly
     the oracle's codes and scales: the exported dequantised weights equal
@@ -157,7 +158,7 @@ def test_weight_only_quantised_matches_oracle(prec, mode):
     assert err <= (5e-2 if prec == "w4a16" else 2e-2)
 
 
-@pytest.mark.parametrize("prec", ["fp8", "w4a16", "w8a16"])
+@pytest.mark.parametrize("prec", ["fp8", "w4a16", "w8a16", "w4a8"])
 def test_quantised_ragged_shapes(prec):
     """Quantised experts at batch 2 with a prefix that is not a multiple of
     the key split, a horizon that is not a multiple of 16 and a state input."""
@@ -170,7 +171,7 @@ def test_quantised_ragged_shapes(prec):
     print(f"case {prec} ragged", flush=True)
     for mode in ("persistent", "eager"):
         ex = gu.build_expert(cfg, params, mode)
-        if prec == "fp8":
+        if prec in ("fp8", "w4a8"):
             gu.bind_inputs(ex, cfg, *make_calibration_inputs(cfg))
             ex.calibrate()
         bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
@@ -182,3 +183,39 @@ def test_quantised_ragged_shapes(prec):
         err = gu.rel_l2(got, ref)
         print(f"{prec} ragged {mode}: rel_l2={err:.3e}")
         assert err <= (2e-2 if prec == "w8a16" else 5e-2), mode
+
+
+@pytest.mark.parametrize("mode", ["persistent", "eager"])
+def test_w4a8_matches_oracle(mode):
+    """W4A8: int4 weights, e4m3 activations with scales from one calibration
+    pass on a separate draw; the calibration's amax is also checked against
+    the oracle's on that draw."""
+    gu = _gu()
+    if "w4a8" not in _CACHE:
+        cfg = CONFIGS["pi05_w4a8"]
+        params, pk, pv, noise, state = make_inputs(cfg)
+        cal = make_calibration_inputs(cfg)
+        deq, _ = Q.dequantised_expert(params, cfg)
+        ref = O.denoise(deq, noise, state, pk, pv, cfg)
+        amax = O.gemm_input_amax(deq, cal[2], cal[3], cal[0], cal[1], cfg)
+        _CACHE["w4a8"] = (cfg, params, (pk, pv, noise, state), cal, ref, amax)
+    cfg, params, ev, cal, ref, amax = _CACHE["w4a8"]
+    print(f"case w4a8 mode={mode}", flush=True)
+    ex = gu.build_expert(cfg, params, mode)
+    gu.bind_inputs(ex, cfg, *cal)
+    ex.calibrate()
+    got_amax = ex.export("act_scales", (cfg.num_layers, 4)) * 448.0
+    bufs = gu.bind_inputs(ex, cfg, *ev)
+    ex.denoise()
+    ex.denoise()
+    ex.check()
+    torch.cuda.synchronize()
+    got = bufs["actions"].cpu().numpy()
+    ex.close()
+    rel = np.abs(got_amax - amax) / amax
+    err = gu.rel_l2(got, ref)
+    disp = gu.rel_l2(got - ev[2], ref - ev[2])
+    print(f"w4a8 {mode}: calibration amax max rel diff {rel.max():.3e}; rel_l2={err:.3e} "
+          f"displacement rel_l2={disp:.3e} (diagnostic)")
+    assert rel.max() <= 5e-2
+    assert err <= 5e-2

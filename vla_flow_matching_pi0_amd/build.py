@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvfm.so")
-SOURCES = ["vfm_k_bf16.hip", "vfm_k_fp8.hip", "vfm_k_w4.hip", "vfm_k_i8.hip", "vfm_k_cal.hip", "vfm_k_f32.hip", "vfm_prep.hip",
+SOURCES = ["vfm_k_bf16.hip", "vfm_k_fp8.hip", "vfm_k_w4.hip", "vfm_k_i8.hip", "vfm_k_w4a8.hip", "vfm_k_cal.hip", "vfm_k_f32.hip", "vfm_prep.hip",
            "vfm_prefix.hip", "vfm_launch.cpp", "vfm_runtime.cpp", "vfm_prefix_rt.cpp"]
 
 HIPCC_FLAGS = [

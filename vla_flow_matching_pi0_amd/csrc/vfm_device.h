@@ -112,6 +112,9 @@ __device__ __forceinline__ u32x4 coh_ld16_if(__amdgpu_buffer_rsrc_t r, uint32_t 
 __device__ __forceinline__ u32x2 coh_ld8_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, ok ? off : OOB, 0, CPOL_SC1);
 }
+__device__ __forceinline__ u32x2 ld8_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, ok ? off : OOB, 0, 0);
+}
 __device__ __forceinline__ uint32_t ld2_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, ok ? off : OOB, 0, 0);
 }

@@ -14,6 +14,7 @@ VFM_DECLARE_KERNEL_SET(ks_cal)
 VFM_DECLARE_KERNEL_SET(ks_fp8)
 VFM_DECLARE_KERNEL_SET(ks_w4)
 VFM_DECLARE_KERNEL_SET(ks_i8)
+VFM_DECLARE_KERNEL_SET(ks_w4a8)
 
 size_t lds_bytes(const VP& p, int act_bytes) {
   const size_t nwaves = NTHREADS / 64;
@@ -33,6 +34,7 @@ hipError_t prepare_kernels(int kset, int d, int lds) {
     case KS_FP8: return ks_fp8_prepare(d, lds);
     case KS_W4: return ks_w4_prepare(d, lds);
     case KS_I8: return ks_i8_prepare(d, lds);
+    case KS_W4A8: return ks_w4a8_prepare(d, lds);
     default: return hipErrorInvalidValue;
   }
 }
@@ -46,6 +48,7 @@ hipError_t launch_phase(const VP& p, int kset, int mode, int phase, int k, int l
     case KS_FP8: return ks_fp8_launch(p, mode, phase, k, l, grid, lds, st);
     case KS_W4: return ks_w4_launch(p, mode, phase, k, l, grid, lds, st);
     case KS_I8: return ks_i8_launch(p, mode, phase, k, l, grid, lds, st);
+    case KS_W4A8: return ks_w4a8_launch(p, mode, phase, k, l, grid, lds, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -59,6 +62,7 @@ hipError_t max_cooperative_grid(int kset, int d, size_t lds, int* grid) {
     case KS_FP8: e = ks_fp8_occupancy(d, lds, &per_cu); break;
     case KS_W4: e = ks_w4_occupancy(d, lds, &per_cu); break;
     case KS_I8: e = ks_i8_occupancy(d, lds, &per_cu); break;
+    case KS_W4A8: e = ks_w4a8_occupancy(d, lds, &per_cu); break;
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

@@ -57,7 +57,7 @@ struct VP {
 };
 
 // Kernel sets: activation type x weight format (x calibration).
-enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4, KS_I8 = 5 };
+enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4, KS_I8 = 5, KS_W4A8 = 6 };
 constexpr int ATT_KEYS_HOST = 64;   // keys per attention split (the kernels' ATT_KEYS)
 constexpr int MAX_A_HOST = 64;      // largest action dim (the kernels' MAX_A)
 
@@ -82,6 +82,7 @@ hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col
                          const void* s0, int n0, const void* s1, int n1, const void* s2, int n2, const unsigned* amax,
                          hipStream_t st);
 hipError_t fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax, hipStream_t st);
+hipError_t w4_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, hipStream_t st);
 hipError_t build_mod_table(float* tab, const void* const* mod_w, const void* const* mod_b, int n_norms,
                            const void* t1w, const void* t1b, const void* t2w, const void* t2b,
                            int N, int E, int W, int src_bf16, double* scratch, hipStream_t st);

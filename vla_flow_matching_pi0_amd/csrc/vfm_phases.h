@@ -198,12 +198,38 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
   }
 }
 
+// Storage format of the per-layer GEMM weights. A lane's 16-byte weight load
+// ("weight block") feeds R MFMA k blocks of K = MT<T>::KB each:
+//   WF_NATIVE  weights in the activation type (fp32 or bf16), R = 1;
+//   WF_FP8     OCP e4m3 codes with a per-tensor scale, R = 2: bytes 8r..8r+7
+//              are the fp8 operand of block r, the activations are quantised
+//              to e4m3 with the calibrated activation scale as they are
+//              loaded, and alpha = act_scale * weight_scale scales the
+//              accumulator (FlashRT walk-through, component 6, calibration);
+//   WF_W4      symmetric int4 with an fp16 scale per (column, 128-K group),
+//              R = 4: word r holds the 8 nibbles of block r, dequantised to
+//              bf16 in registers before the MFMA (the W4A16 variant of the
+//              PhyAI optimisation paragraph);
+//   WF_I8      symmetric int8 with an fp32 scale per output column (W8A16),
+//              R = 2: bytes 8r..8r+7 are the codes of block r, turned into
+//              bf16 in registers (exact: |q| <= 127) before the MFMA; the
+//              column scale multiplies the accumulated sum in the epilogue;
+//   WF_W4A8    the int4 codes and group scales of WF_W4 with the e4m3
+//              activations of WF_FP8 (W4A8): the codes become e4m3 in
+//              registers (exact: |q| <= 8), one group's four fp8 MFMAs
+//              accumulate apart and are added to the sum times the group
+//              scales of the output columns; alpha = act_scale.
+enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2, WF_I8 = 3, WF_W4A8 = 4 };
+template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : (WF == WF_W4 || WF == WF_W4A8) ? 4 : 2; };
+// GEMM inputs stored as e4m3 with the calibrated activation scale.
+template <int WF> constexpr bool act_fp8() { return WF == WF_FP8 || WF == WF_W4A8; }
+
 // Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
 // scales the partial sums, ni the norm applied.
 template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_rn(const VP&, int step, int layer, bool mlp, int wg, int nwg) {
   const VP& p = vp_fresh();
-  constexpr bool Q8 = WF == 1;   // WF_FP8
+  constexpr bool Q8 = act_fp8<WF>();
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
   const float* part = mlp ? p.part_o : p.part_d;
@@ -226,7 +252,7 @@ constexpr int MAX_A = MAX_A_HOST;
 template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, int nwg) {
   const VP& p = vp_fresh();
-  constexpr bool Q8 = WF == 1;   // WF_FP8
+  constexpr bool Q8 = act_fp8<WF>();
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);                       // [NWAVES]
   float* xs = red + NWAVES;                                          // [W]
@@ -362,24 +388,7 @@ __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, i
 enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3 };
 constexpr int GEMM_PASS = 4;     // MFMA k blocks per wave per pass
 
-// Storage format of the per-layer GEMM weights. A lane's 16-byte weight load
-// ("weight block") feeds R MFMA k blocks of K = MT<T>::KB each:
-//   WF_NATIVE  weights in the activation type (fp32 or bf16), R = 1;
-//   WF_FP8     OCP e4m3 codes with a per-tensor scale, R = 2: bytes 8r..8r+7
-//              are the fp8 operand of block r, the activations are quantised
-//              to e4m3 with the calibrated activation scale as they are
-//              loaded, and alpha = act_scale * weight_scale scales the
-//              accumulator (FlashRT walk-through, component 6, calibration);
-//   WF_W4      symmetric int4 with an fp16 scale per (column, 128-K group),
-//              R = 4: word r holds the 8 nibbles of block r, dequantised to
-//              bf16 in registers before the MFMA (the W4A16 variant of the
-//              PhyAI optimisation paragraph);
-//   WF_I8      symmetric int8 with an fp32 scale per output column (W8A16),
-//              R = 2: bytes 8r..8r+7 are the codes of block r, turned into
-//              bf16 in registers (exact: |q| <= 127) before the MFMA; the
-//              column scale multiplies the accumulated sum in the epilogue.
-enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2, WF_I8 = 3 };
-template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : WF == WF_W4 ? 4 : 2; };
+
 
 // Weight fragments of one pass of one unit, held in registers. The
 // persistent kernel loads a workgroup's first pass of the next GEMM while it
@@ -387,11 +396,12 @@ template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : W
 struct WPre {
   u32x4 w[2][GEMM_PASS];
   uint32_t sc[2];          // WF_W4: the fp16 group scale of each tile's column
+  u32x2 sc4[2];            // WF_W4A8: the group scales of the 4 output columns a lane accumulates
 };
 
 struct GemmShape {
   const uint8_t* Wp;
-  const uint8_t* Ws;       // after the codes: WF_W4 scales [N/16][K/128][16] fp16, WF_I8 scales [N] fp32
+  const uint8_t* Ws;       // after the codes: WF_W4(A8) scales [N/16][K/128][16] fp16, WF_I8 scales [N] fp32
   int K, N, nt, S, ngroups, units, nkb, KR, nkbw;
 };
 
@@ -440,6 +450,15 @@ __device__ __forceinline__ void gemm_load_weights(const GemmShape& gs, int u, in
       out.sc[t] = ld2_if(srs, (uint32_t)((((size_t)(t0 + t) * gs.nkb + kb0 + pb) * 16 + (lane & 15)) * 2),
                          ok && t < gs.nt);
   }
+  if constexpr (WF == WF_W4A8) {
+    // the lane's output rows are columns 4 g .. 4 g + 3 of the tile: their 4 fp16 scales are adjacent
+    const auto srs = rsrc(gs.Ws);
+    const bool ok = pb < gs.nkbw;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      out.sc4[t] = ld8_if(srs, (uint32_t)((((size_t)(t0 + t) * gs.nkb + kb0 + pb) * 16 + 4 * (lane >> 4)) * 2),
+                          ok && t < gs.nt);
+  }
 }
 
 template <typename T, int WHICH, int WF>
@@ -466,6 +485,28 @@ __device__ __forceinline__ u32x4 w4_to_bf16(uint32_t wd, uint32_t scale_bits) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = (float)(((int)(wd << (28 - 4 * e))) >> 28) * s;
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
+// 8 signed nibbles (element e in bits 4e..4e+3) -> 8 e4m3 codes (byte e),
+// exact: every integer in [-8, 7] is an e4m3 value.
+__device__ __forceinline__ long w4_to_fp8(uint32_t wd) {
+  uint32_t o[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = (float)(((int)(wd << (28 - 4 * (4 * h + e)))) >> 28);
+    o[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false), true);
+  }
+  return (long)(((unsigned long long)o[1] << 32) | o[0]);
+}
+
+// 4 fp16 values (2 words) -> floatx4.
+__device__ __forceinline__ floatx4 half4_to_f4(u32x2 h) {
+  return floatx4{(float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] & 0xffffu)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(h[0] >> 16)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] & 0xffffu)),
+                 (float)__builtin_bit_cast(_Float16, (uint16_t)(h[1] >> 16))};
 }
 
 // 8 int8 codes (byte e of the pair of words is element e) -> 8 bf16, exact
@@ -517,7 +558,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
   const int Mpad = ((p.M + 63) / 64) * 64;
   const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
   float alpha = 1.0f;
-  if constexpr (WF == WF_FP8) alpha = p.qs[(layer * 4 + WHICH) * 2];
+  if constexpr (act_fp8<WF>()) alpha = p.qs[(layer * 4 + WHICH) * 2];
   float amax = 0.f;
   floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NWAVES][2][4][64]
   for (int u = wg; u < units; u += nwg) {
@@ -529,6 +570,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int st = 0; st < 4; ++st) acc[t][st] = floatx4{0, 0, 0, 0};
+    floatx4 tmp[2][4];   // WF_W4A8: one group's sum before its scales
     bool rowok[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) rowok[st] = m0 + st * 16 + c16 < p.M;
@@ -552,7 +594,19 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       u32x4 ar[4][GEMM_PASS];
       if (PRE && u == wg && pb == 0) wl = pre;
       else gemm_load_weights<T, WHICH, WF>(gs, u, pb, tid, wl);
-      if constexpr (WF == WF_FP8) {
+      if constexpr (WF == WF_W4A8) {
+        // e4m3 inputs (act_off8): a 128-K weight block spans two 64-K activation blocks
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = pb < nkbw;
+          const int kblk = (kb0 + pb) * 2 + h;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const size_t row = (size_t)(m0 + st * 16 + c16);
+            ar[st][h] = ld16_if(ars, (uint32_t)((((size_t)kblk * Mpad + row) * 4 + g) * 16), ok && rowok[st]);
+          }
+        }
+      } else if constexpr (WF == WF_FP8) {
         // e4m3 inputs (act_off8): one 16-byte fetch per weight block and token subtile
 #pragma unroll
         for (int i = 0; i < PW; ++i) {
@@ -605,6 +659,32 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
             for (int st = 0; st < 4; ++st)
               if (t < nt) acc[t][st] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w8, a8[st], acc[t][st], 0, 0, 0);
           }
+        } else if constexpr (WF == WF_W4A8) {
+          // one weight block = one 128-K group: its four MFMAs go to tmp, then acc += tmp x group scales
+          if (r == 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int st = 0; st < 4; ++st) tmp[t][st] = floatx4{0, 0, 0, 0};
+          }
+          long a8[4];
+#pragma unroll
+          for (int st = 0; st < 4; ++st) a8[st] = (long)__builtin_bit_cast(i64x2, ar[st][r / 2])[r % 2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const long w8 = w4_to_fp8(wl.w[t][i][r]);
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              if (t < nt) tmp[t][st] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(w8, a8[st], tmp[t][st], 0, 0, 0);
+          }
+          if (r == R - 1) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const floatx4 gsc = half4_to_f4(wl.sc4[t]);
+#pragma unroll
+              for (int st = 0; st < 4; ++st) acc[t][st] += tmp[t][st] * gsc;
+            }
+          }
         } else if constexpr (WF == WF_I8) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -638,7 +718,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       floatx4 v = {0, 0, 0, 0};
 #pragma unroll
       for (int w2 = 0; w2 < NWAVES; ++w2) v += red[((w2 * 2 + t) * 4 + st) * 64 + lane];
-      if constexpr (WF == WF_FP8) v *= alpha;
+      if constexpr (act_fp8<WF>()) v *= alpha;
       const int gm = m0 + st * 16 + c16;
       const int tile = t0 + t;
       if constexpr (WF == WF_I8) v *= csc;
@@ -677,7 +757,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
           const int f0 = tile * 8 + 2 * g;
           const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
           uint8_t* dst = sl + p.off_act;
-          if constexpr (WF == WF_FP8) {
+          if constexpr (act_fp8<WF>()) {
             const uint32_t w = fp8x2<false>(a0, a1, act_inv(p, layer, G_DOWN), 0u);
             coh_st2(dst, (uint32_t)act_off8(p, gm, f0), w & 0xffffu);
           } else {
@@ -955,7 +1035,7 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
 template <typename T, int WF = 0>
 __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int wg, int nwg) {
   const VP& p = vp_fresh();
-  constexpr bool Q8 = WF == 1;   // WF_FP8
+  constexpr bool Q8 = act_fp8<WF>();
   const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
   const int lane = tid & 63, wv = tid >> 6;

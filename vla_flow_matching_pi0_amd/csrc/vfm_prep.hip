@@ -254,6 +254,31 @@ hipError_t pack_weight_q(uint8_t* dst, int fmt, int K, int Npk, const int* d_col
   return hipGetLastError();
 }
 
+// Calibration of a W4A8 expert: the bf16 packed stream (32-K blocks) of an
+// int4 packed weight, holding q x s rounded to bf16. Lane (g, c) of 32-K
+// block kb reads word kb % 4 of its lane in 128-K block kb / 4.
+__global__ void k_w4_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk) {
+  const int nkb32 = K / 32, nkb128 = K / 128;
+  const size_t total = (size_t)(Npk / 16) * nkb32 * 64;
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(src + (size_t)Npk * K / 2);
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total; idx += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx % 64);
+    const int kb = (int)((idx / 64) % nkb32);
+    const int t = (int)(idx / 64 / nkb32);
+    const uint32_t wd = *reinterpret_cast<const uint32_t*>(src + (((size_t)t * nkb128 + kb / 4) * 64 + lane) * 16 + (kb % 4) * 4);
+    const float s = (float)__builtin_bit_cast(_Float16, scales[((size_t)t * nkb128 + kb / 4) * 16 + (lane & 15)]);
+    bf16 out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (bf16)((float)(((int)(wd << (28 - 4 * e))) >> 28) * s);
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = *reinterpret_cast<const u32x4*>(out);
+  }
+}
+
+hipError_t w4_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, hipStream_t st) {
+  hipLaunchKernelGGL(k_w4_to_bf16_packed, dim3(1024), dim3(256), 0, st, dst, src, K, Npk);
+  return hipGetLastError();
+}
+
 hipError_t fp8_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, const unsigned* amax, hipStream_t st) {
   hipLaunchKernelGGL(k_fp8_to_bf16_packed, dim3(1024), dim3(256), 0, st, dst, src, K, Npk, amax);
   return hipGetLastError();

@@ -109,6 +109,9 @@ struct vfm_expert {
 
 namespace {
 
+// GEMM inputs are e4m3 with calibrated activation scales (FP8 and W4A8).
+bool fp8_act(const vfm_expert* x) { return x->wprec == VFM_W_FP8 || x->wprec == VFM_W_W4A8; }
+
 // Host decoders of the packed formats (export only).
 float e4m3_value(uint8_t c) {
   const int e = (c >> 3) & 15, m = c & 7;
@@ -158,19 +161,20 @@ vfm_status validate_config(const vfm_config* c) {
   if (c->num_steps < 1 || c->num_steps > 1000) return fail(VFM_E_INVALID_ARG, "num_steps %d outside [1, 1000]", c->num_steps);
   if (!(c->rope_base > 0.f)) return fail(VFM_E_INVALID_ARG, "rope_base must be > 0");
   if (!(c->rms_eps > 0.f)) return fail(VFM_E_INVALID_ARG, "rms_eps must be > 0");
-  if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W8A16)
+  if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W4A8)
     return fail(VFM_E_INVALID_ARG, "weight_precision %d unknown", c->weight_precision);
   if (c->weight_precision == VFM_W_FP32 && c->act_dtype != VFM_F32)
     return fail(VFM_E_INVALID_ARG, "fp32 weights need act_dtype VFM_F32");
   if (c->weight_precision != VFM_W_FP32 && c->act_dtype != VFM_BF16)
     return fail(VFM_E_INVALID_ARG, "16-bit and quantised weights need act_dtype VFM_BF16");
-  if (c->weight_precision == VFM_W_FP8 || c->weight_precision == VFM_W_W4A16 || c->weight_precision == VFM_W_W8A16) {
+  if (c->weight_precision >= VFM_W_FP8) {
     // every wave of a GEMM workgroup takes at least one 16-byte weight block
-    const int span = (c->weight_precision == VFM_W_W4A16 ? 128 : 64) * (vfm::NTHREADS / 64);
+    const bool w4 = c->weight_precision == VFM_W_W4A16 || c->weight_precision == VFM_W_W4A8;
+    const int span = (w4 ? 128 : 64) * (vfm::NTHREADS / 64);
     if (c->width % span || (c->num_q_heads * c->head_dim) % span || c->mlp_dim % span)
       return fail(VFM_E_INVALID_ARG, "quantised weights need width, num_q_heads * head_dim and mlp_dim to be "
                   "multiples of %d", span);
-    if (c->weight_precision == VFM_W_W4A16 && c->w4_group_size != 128)
+    if (w4 && c->w4_group_size != 128)
       return fail(VFM_E_UNSUPPORTED, "w4_group_size %d: only 128 is built", c->w4_group_size);
   }
   return VFM_OK;
@@ -444,8 +448,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   tmp.src_bf16 = cfg->weight_precision != VFM_W_FP32;
   tmp.wprec = cfg->weight_precision;
   tmp.kset = tmp.wprec == VFM_W_FP32 ? vfm::KS_F32 : tmp.wprec == VFM_W_BF16 ? vfm::KS_BF16
-           : tmp.wprec == VFM_W_FP8 ? vfm::KS_FP8 : tmp.wprec == VFM_W_W8A16 ? vfm::KS_I8 : vfm::KS_W4;
-  tmp.KW = tmp.wprec == VFM_W_FP32 ? 16 : tmp.wprec == VFM_W_BF16 ? 32 : tmp.wprec == VFM_W_W4A16 ? 128 : 64;
+           : tmp.wprec == VFM_W_FP8 ? vfm::KS_FP8 : tmp.wprec == VFM_W_W8A16 ? vfm::KS_I8
+           : tmp.wprec == VFM_W_W4A8 ? vfm::KS_W4A8 : vfm::KS_W4;
+  tmp.KW = tmp.wprec == VFM_W_FP32 ? 16 : tmp.wprec == VFM_W_BF16 ? 32
+         : (tmp.wprec == VFM_W_W4A16 || tmp.wprec == VFM_W_W4A8) ? 128 : 64;
   tmp.L = cfg->num_layers; tmp.W = cfg->width; tmp.Hq = cfg->num_q_heads; tmp.Hkv = cfg->num_kv_heads;
   tmp.d = cfg->head_dim; tmp.F = cfg->mlp_dim; tmp.H = cfg->action_horizon; tmp.A = cfg->action_dim;
   tmp.S = cfg->state_dim; tmp.E = cfg->time_emb_dim; tmp.N = cfg->num_steps;
@@ -515,7 +521,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   auto wbytes = [&](size_t K, size_t N) -> size_t {
     if (x->wprec == VFM_W_FP8) return K * N;
     if (x->wprec == VFM_W_W8A16) return K * N + N * 4;
-    if (x->wprec == VFM_W_W4A16) return K * N / 2 + (K / 128) * N * 2;
+    if (x->wprec == VFM_W_W4A16 || x->wprec == VFM_W_W4A8) return K * N / 2 + (K / 128) * N * 2;
     return K * N * ab;
   };
   if (x->wprec == VFM_W_FP8) {
@@ -541,7 +547,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
         return bail(VFM_E_HIP);
       }
     } else {
-      const int fmt = x->wprec == VFM_W_FP8 ? 0 : x->wprec == VFM_W_W4A16 ? 1 : 2;
+      const int fmt = x->wprec == VFM_W_FP8 ? 0 : x->wprec == VFM_W_W8A16 ? 2 : 1;
       unsigned* am = x->wamax ? x->wamax + 4 * l : nullptr;
       if (fmt == 0) {
         // one scale per fused tensor: [q | k | v] and [gate | up] share theirs
@@ -580,6 +586,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     }
     x->wscale.resize(am.size());
     for (size_t i = 0; i < am.size(); ++i) x->wscale[i] = am[i] > 0.f ? am[i] / 448.0f : 1.0f;
+  }
+  if (fp8_act(x)) {
+    // W4A8: the group scales are inside the GEMM, so alpha is the activation scale alone
+    if (x->wprec == VFM_W_W4A8) x->wscale.assign((size_t)L * 4, 1.0f);
     x->qs = (float*)x->dalloc((size_t)std::max(L, 1) * 8 * 4);
     if (!x->qs) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
   }
@@ -651,7 +661,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     shape.W = W;
     x->lds = vfm::lds_bytes(shape, ab);
     hipError_t e = vfm::prepare_kernels(x->kset, d, (int)x->lds);
-    if (e == hipSuccess && x->wprec == VFM_W_FP8) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
+    if (e == hipSuccess && fp8_act(x)) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
   }
   if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) {
@@ -759,8 +769,8 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if ((reinterpret_cast<uintptr_t>(noise) | reinterpret_cast<uintptr_t>(actions) | reinterpret_cast<uintptr_t>(state)) % 16)
     return fail(VFM_E_INVALID_ARG, "noise / state / actions must be 16-byte aligned");
 
-  if (x->wprec == VFM_W_FP8 && x->act_scale.empty())
-    return fail(VFM_E_STATE, "FP8 expert: run vfm_calibrate or vfm_set_act_scales first");
+  if (fp8_act(x) && x->act_scale.empty())
+    return fail(VFM_E_STATE, "FP8-activation expert: run vfm_calibrate or vfm_set_act_scales first");
   VP p{};
   if ((st = fill_vp(x, p, B, P, noise, state, actions)) != VFM_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -806,7 +816,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
 
 vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "calibrate applies to FP8 experts only");
+  if (!fp8_act(x)) return fail(VFM_E_STATE, "calibrate applies to FP8 and W4A8 experts only");
   vfm_status st = check_prev_flag(x, true);
   if (st != VFM_OK) return st;
   if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
@@ -844,12 +854,19 @@ vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
     uint8_t* bg = (uint8_t*)talloc((size_t)W * 2 * F * 2);
     uint8_t* bd = (uint8_t*)talloc((size_t)F * W * 2);
     if (!bq || !bo || !bg || !bd) { release(); return fail(VFM_E_OOM, "calibration weights"); }
-    unsigned* am = x->wamax + 4 * l;
-    if ((e = vfm::fp8_to_bf16_packed(bq, x->w_qkv[l], W, nqkv, am + 0, s)) != hipSuccess ||
-        (e = vfm::fp8_to_bf16_packed(bo, x->w_o[l], qd, W, am + 1, s)) != hipSuccess ||
-        (e = vfm::fp8_to_bf16_packed(bg, x->w_gu[l], W, 2 * F, am + 2, s)) != hipSuccess ||
-        (e = vfm::fp8_to_bf16_packed(bd, x->w_down[l], F, W, am + 3, s)) != hipSuccess)
+    if (x->wprec == VFM_W_FP8) {
+      unsigned* am = x->wamax + 4 * l;
+      if ((e = vfm::fp8_to_bf16_packed(bq, x->w_qkv[l], W, nqkv, am + 0, s)) != hipSuccess ||
+          (e = vfm::fp8_to_bf16_packed(bo, x->w_o[l], qd, W, am + 1, s)) != hipSuccess ||
+          (e = vfm::fp8_to_bf16_packed(bg, x->w_gu[l], W, 2 * F, am + 2, s)) != hipSuccess ||
+          (e = vfm::fp8_to_bf16_packed(bd, x->w_down[l], F, W, am + 3, s)) != hipSuccess)
+        break;
+    } else if ((e = vfm::w4_to_bf16_packed(bq, x->w_qkv[l], W, nqkv, s)) != hipSuccess ||
+               (e = vfm::w4_to_bf16_packed(bo, x->w_o[l], qd, W, s)) != hipSuccess ||
+               (e = vfm::w4_to_bf16_packed(bg, x->w_gu[l], W, 2 * F, s)) != hipSuccess ||
+               (e = vfm::w4_to_bf16_packed(bd, x->w_down[l], F, W, s)) != hipSuccess) {
       break;
+    }
     p.w_qkv[l] = bq; p.w_o[l] = bo; p.w_gu[l] = bg; p.w_down[l] = bd;
   }
   if (e == hipSuccess && x->rope_P != P) {
@@ -869,7 +886,7 @@ vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
 
 vfm_status vfm_set_act_scales(vfm_expert* x, const float* scales, int32_t n) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "activation scales apply to FP8 experts only");
+  if (!fp8_act(x)) return fail(VFM_E_STATE, "activation scales apply to FP8 and W4A8 experts only");
   if (n != 4 * x->L) return fail(VFM_E_SHAPE, "expected %d scales", 4 * x->L);
   if (n > 0 && !scales) return fail(VFM_E_INVALID_ARG, "scales is NULL");
   for (int i = 0; i < n; ++i)
@@ -921,7 +938,8 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     }
   }
   if (n == "act_scales" || n == "weight_scales") {
-    if (x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "'%s' exists for FP8 experts only", name);
+    if (n == "weight_scales" && x->wprec != VFM_W_FP8) return fail(VFM_E_STATE, "'%s' exists for FP8 experts only", name);
+    if (!fp8_act(x)) return fail(VFM_E_STATE, "'%s' exists for FP8 and W4A8 experts only", name);
     const std::vector<float>& v = n == "act_scales" ? x->act_scale : x->wscale;
     if (v.empty()) return fail(VFM_E_STATE, "activation scales are not set");
     if (bytes != v.size() * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, v.size() * 4);
@@ -965,7 +983,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   size_t nbytes;
   if (x->wprec == VFM_W_FP8) nbytes = (size_t)K * Npk;
   else if (x->wprec == VFM_W_W8A16) nbytes = (size_t)K * Npk + (size_t)Npk * 4;
-  else if (x->wprec == VFM_W_W4A16) nbytes = (size_t)K * Npk / 2 + (size_t)(K / 128) * Npk * 2;
+  else if (x->wprec == VFM_W_W4A16 || x->wprec == VFM_W_W4A8) nbytes = (size_t)K * Npk / 2 + (size_t)(K / 128) * Npk * 2;
   else nbytes = (size_t)K * Npk * (x->act_bf16 ? 2 : 4);
   std::vector<uint8_t> host(nbytes);
   HIPCHK(hipDeviceSynchronize());
@@ -991,7 +1009,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
         float sc;
         memcpy(&sc, &host[(size_t)K * Npk + (size_t)pc * 4], 4);
         v = (float)q * sc;
-      } else if (x->wprec == VFM_W_W4A16) {
+      } else if (x->wprec == VFM_W_W4A16 || x->wprec == VFM_W_W4A8) {
         // nibble 8r + e of lane (g, c16) holds k = 128 kb + 32 r + 8 g + e
         const int r = rem / 32, g = (rem % 32) / 8, e = rem % 8;
         const size_t lane_off = (((size_t)t * nkb + kb) * 64 + g * 16 + c16) * 16;
@@ -1096,7 +1114,7 @@ vfm_status vfm_capsule_create(vfm_expert* x, vfm_capsule** out) {
   c->L = x->L; c->Hkv = x->Hkv; c->d = x->d; c->H = x->H; c->A = x->A; c->S = x->S; c->act_bf16 = x->act_bf16;
   c->B = (int)x->prefix_k.shape[1];
   c->P = (int)x->prefix_k.shape[2];
-  c->from_fp8 = x->wprec == VFM_W_FP8;
+  c->from_fp8 = fp8_act(x);
   for (int w = 0; w < 5; ++w) {
     const BoundBuf* b = buf_slot(x, w);
     if (!b->bound) continue;
@@ -1117,7 +1135,7 @@ vfm_status vfm_capsule_save(vfm_expert* x, vfm_capsule* c, void* stream) {
   if (!x || !c) return fail(VFM_E_INVALID_ARG, "NULL argument");
   vfm_status st = capsule_matches(x, c);
   if (st != VFM_OK) return st;
-  if (c->from_fp8 != (x->wprec == VFM_W_FP8)) return fail(VFM_E_STATE, "capsule and expert differ in FP8-ness");
+  if (c->from_fp8 != fp8_act(x)) return fail(VFM_E_STATE, "capsule and expert differ in FP8 activations");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   for (const vfm_capsule::Slot& sl : c->slots)
     if (sl.bytes) HIPCHK(hipMemcpyAsync(sl.dev, buf_slot(x, sl.which)->ptr, sl.bytes, hipMemcpyDeviceToDevice, s));
@@ -1131,7 +1149,7 @@ vfm_status vfm_capsule_restore(vfm_expert* x, const vfm_capsule* c, void* stream
   if (!c->saved) return fail(VFM_E_STATE, "capsule holds no saved state");
   vfm_status st = capsule_matches(x, c);
   if (st != VFM_OK) return st;
-  const bool fp8 = x->wprec == VFM_W_FP8 && c->from_fp8;
+  const bool fp8 = fp8_act(x) && c->from_fp8;
   if (fp8 && c->act_scale != x->act_scale) {
     if (c->act_scale.empty()) {
       x->act_scale.clear();

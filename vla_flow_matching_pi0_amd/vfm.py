@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvfm.so")
 
 VFM_F32, VFM_BF16, VFM_F16, VFM_FP8_E4M3, VFM_I4X2 = 0, 1, 2, 3, 4
-WPREC = {"fp32": 0, "bf16": 1, "fp8": 2, "w4a16": 3, "w8a16": 4}
+WPREC = {"fp32": 0, "bf16": 1, "fp8": 2, "w4a16": 3, "w8a16": 4, "w4a8": 5}
 STATUS = {0: "VFM_OK", 1: "VFM_E_INVALID_ARG", 2: "VFM_E_SHAPE", 3: "VFM_E_DTYPE", 4: "VFM_E_UNBOUND",
           5: "VFM_E_STATE", 6: "VFM_E_UNSUPPORTED", 7: "VFM_E_OOM", 8: "VFM_E_HIP"}
 ABI_VERSION = 1
