@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output into the short text summaries kept with the
 library (kernel time statistics, HBM traffic of one kernel).
 
-  python -m vla_flow_matching_pi0_amd.profsum stats <kernel_stats.csv> <out.md> --cmd "<command>"
+  python -m vla_flow_matching_pi0_amd.profsum stats <kernel_stats.csv> <out.md> --cmd "<command>" [--match <name part>]
   python -m vla_flow_matching_pi0_amd.profsum traffic <fetch counter_collection.csv> <write counter_collection.csv>
          <out.md> --kernel k_persistent --calib-mib 1024 --cmd-fetch "<command>" --cmd-write "<command>"
 
@@ -40,10 +40,11 @@ def short_name(name: str) -> str:
     return name.split("(")[0][:110]
 
 
-def stats(path: str, out: str, cmd: str, top: int = 20) -> None:
-    rows = list(csv.DictReader(open(path)))
+def stats(path: str, out: str, cmd: str, top: int = 20, match: str = "") -> None:
+    rows = [r for r in csv.DictReader(open(path)) if match in r["Name"]]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
+    title = "# rocprofv3 kernel statistics" + (f" (kernels matching `{match}`)" if match else "")
+    lines = [title, "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows[:top]:
         lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
@@ -107,6 +108,7 @@ def main(argv=None) -> int:
     a.add_argument("csv")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--match", default="", help="keep only kernels whose name contains this")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -118,7 +120,7 @@ def main(argv=None) -> int:
     b.add_argument("--cmd-write", required=True)
     args = ap.parse_args(argv)
     if args.mode == "stats":
-        stats(args.csv, args.out, args.cmd)
+        stats(args.csv, args.out, args.cmd, match=args.match)
     else:
         traffic(args.fetch_csv, args.write_csv, args.out, args.kernel, args.calib_mib, args.cmd_fetch,
                 args.cmd_write, args.workload)
