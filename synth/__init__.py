@@ -47,6 +47,7 @@ class ExpertConfig:
     w4_group: int = 128
     seed: int = 0
     weight_std: float = 0.02
+    variant: str = "pi05"              # pi05: adaptive norms; pi0: state token + action-time MLP
 
     @property
     def act_dtype(self) -> str:
@@ -83,6 +84,13 @@ CONFIGS: Dict[str, ExpertConfig] = {
     "pi05_bf16_b32": _pi05("pi05_bf16_b32", batch=32, seed=4),
     "pi05_w8a16": _pi05("pi05_w8a16", weight_precision="w8a16", seed=5),
     "pi05_w4a8": _pi05("pi05_w4a8", weight_precision="w4a8", seed=6),
+    # pi0: a state token before the action tokens, the time folded into the
+    # action tokens by an MLP, plain norms
+    "pi0_tiny_fp32": ExpertConfig(name="pi0_tiny_fp32", num_layers=2, width=256, num_q_heads=4, num_kv_heads=1,
+                                  head_dim=64, mlp_dim=1024, action_horizon=8, action_dim=8, state_dim=8,
+                                  time_emb_dim=256, prefix_len=64, batch=1, weight_precision="fp32", seed=20,
+                                  variant="pi0"),
+    "pi0_bf16_b1": _pi05("pi0_bf16_b1", seed=21, variant="pi0"),
 }
 
 
@@ -90,9 +98,31 @@ def workload(name: str) -> ExpertConfig:
     return CONFIGS[name]
 
 
+def _pi0_specs(cfg: ExpertConfig) -> List[Tuple[str, Tuple[int, ...]]]:
+    W, A, S, F = cfg.width, cfg.action_dim, cfg.state_dim, cfg.mlp_dim
+    qd, kd = cfg.num_q_heads * cfg.head_dim, cfg.num_kv_heads * cfg.head_dim
+    specs: List[Tuple[str, Tuple[int, ...]]] = [
+        ("time_mlp_in.w", (2 * W, W)), ("time_mlp_in.b", (W,)),
+        ("time_mlp_out.w", (W, W)), ("time_mlp_out.b", (W,)),
+        ("in_proj.w", (A, W)), ("in_proj.b", (W,)),
+        ("state_proj.w", (S, W)), ("state_proj.b", (W,)),
+    ]
+    for l in range(cfg.num_layers):
+        p = f"layers.{l}."
+        specs += [(p + "attn_norm.w", (W,)), (p + "q.w", (W, qd)), (p + "k.w", (W, kd)), (p + "v.w", (W, kd)),
+                  (p + "o.w", (qd, W)), (p + "mlp_norm.w", (W,)), (p + "gate.w", (W, F)), (p + "up.w", (W, F)),
+                  (p + "down.w", (F, W))]
+    specs += [("final_norm.w", (W,)), ("out_proj.w", (W, A)), ("out_proj.b", (A,))]
+    return specs
+
+
 def param_specs(cfg: ExpertConfig) -> List[Tuple[str, Tuple[int, ...]]]:
     """Canonical parameter names and shapes, in draw order. All matrices are
-    stored [in][out] (y = x @ W)."""
+    stored [in][out] (y = x @ W). The pi0 variant has an action-time MLP
+    ([action ; time] 2W -> W -> W), a state projection and plain (1 + w)
+    norm weights instead of the modulation layers."""
+    if cfg.variant == "pi0":
+        return _pi0_specs(cfg)
     W, E, A, S = cfg.width, cfg.time_emb_dim, cfg.action_dim, cfg.state_dim
     qd = cfg.num_q_heads * cfg.head_dim
     kd = cfg.num_kv_heads * cfg.head_dim
