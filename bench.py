@@ -75,6 +75,8 @@ def algorithmic_bytes_per_step(cfg) -> int:
     o = cfg.num_q_heads * d * W
     per_layer = qkv + o + 2 * W * F + F * W
     small = cfg.action_dim * W + W * cfg.action_dim + cfg.state_dim * W
+    if getattr(cfg, "variant", "pi05") == "pi0":
+        small += W * W              # pi0: the time-MLP output GEMM of every step
     prefix = 2 * L * cfg.batch * cfg.prefix_len * cfg.num_kv_heads * d
     act_b = 4 if cfg.weight_precision == "fp32" else 2
     if cfg.weight_precision == "fp8":
@@ -90,12 +92,15 @@ def algorithmic_bytes_per_step(cfg) -> int:
 
 
 def flops_per_chunk(cfg) -> float:
-    """Multiply-adds x 2 of the GEMMs and attention of one chunk."""
-    M = cfg.batch * cfg.action_horizon
+    """Multiply-adds x 2 of the GEMMs and attention of one chunk (pi0: one
+    state token more per sample, plus the time-MLP output GEMM)."""
+    pi0 = getattr(cfg, "variant", "pi05") == "pi0"
+    T = cfg.action_horizon + (1 if pi0 else 0)
+    M = cfg.batch * T
     W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
     qkv = W * (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d
-    gemm = M * (L * (qkv + cfg.num_q_heads * d * W + 3 * W * F) + 2 * cfg.action_dim * W)
-    attn = L * cfg.batch * cfg.num_q_heads * cfg.action_horizon * (cfg.prefix_len + cfg.action_horizon) * d * 2
+    gemm = M * (L * (qkv + cfg.num_q_heads * d * W + 3 * W * F) + 2 * cfg.action_dim * W + (W * W if pi0 else 0))
+    attn = L * cfg.batch * cfg.num_q_heads * T * (cfg.prefix_len + T) * d * 2
     return 2.0 * (gemm + attn) * cfg.num_steps
 
 
@@ -163,6 +168,8 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: flo
     `steps` Euler steps of the same chunk, repeated until `min_seconds` have
     passed, scaled to the full chunk."""
     from oracle import denoise as O
+    from oracle import pi0 as P0
+    run = P0.denoise_pi0 if getattr(cfg, "variant", "pi05") == "pi0" else O.denoise
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -172,7 +179,7 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: flo
     reps, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
-        O.denoise(p64, noise, state, pk, pv, cfg, num_steps=steps)
+        run(p64, noise, state, pk, pv, cfg, num_steps=steps)
         dt += time.perf_counter() - t0
         reps += 1
     per_chunk_ms = dt * 1e3 * cfg.num_steps / (steps * reps)
@@ -282,9 +289,10 @@ def main() -> int:
         ex.set_option("trace", "1")
         ex.denoise(stream=stream)
         ex.check(stream)
-        t = ex.export("trace", (2 * (N * (8 * L + 1) + 4),)).reshape(-1, 2).astype(np.float64)
+        pi0 = 1 if cfg.variant == "pi0" else 0   # pi0: the time-MLP GEMM and layer 0's norm add 2 per step
+        t = ex.export("trace", (2 * (N * (8 * L + 1 + 2 * pi0) + 4),)).reshape(-1, 2).astype(np.float64)
         ex.set_option("trace", "0")
-        nb = 1 + N * 8 * L
+        nb = 1 + N * (8 * L + 2 * pi0)
         span = t[nb, 1] - t[0, 1]
         stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
         sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "span_us": round(float(span), 1),

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define VFM_ABI_VERSION 1
+#define VFM_ABI_VERSION 2
 
 typedef struct vfm_expert vfm_expert;   /* opaque; owned by the library */
 
@@ -55,6 +55,18 @@ typedef enum {
 } vfm_status;
 
 typedef enum { VFM_F32 = 0, VFM_BF16 = 1, VFM_F16 = 2, VFM_FP8_E4M3 = 3, VFM_I4X2 = 4 } vfm_dtype;
+
+/* Expert variant. VFM_VARIANT_PI05: the time enters every norm (adaptive
+ * RMSNorm with gated residuals) and the state embedding is added to every
+ * action token. VFM_VARIANT_PI0: one state token (state W_s + b_s) precedes
+ * the action tokens and sees only the prefix and itself; the time enters an
+ * action-time MLP on [x W_in + b_in ; sincos(t)] (2W -> W -> W, SiLU); the
+ * norms are plain RMSNorm with a (1 + w) gain and the residuals ungated. The
+ * pages list pi0 and pi0.5 side by side (PhyAI summary, FlashRT forum post)
+ * without their equations; both readings are stated with the oracle. pi0 is
+ * built for fp32 / bf16 weights, state_dim >= 1, time_emb_dim == width,
+ * action_horizon <= 63 and num_layers >= 1. */
+typedef enum { VFM_VARIANT_PI05 = 0, VFM_VARIANT_PI0 = 1 } vfm_variant;
 
 /* Storage precision of the per-layer GEMM weights (q/k/v/o/gate/up/down):
  * fp32; bf16; FP8 e4m3 per tensor with FP8 activations (W8A8); int4 with fp16
@@ -88,6 +100,7 @@ typedef struct {
   int32_t weight_precision; /* vfm_wprec */
   int32_t act_dtype;        /* VFM_F32 (with VFM_W_FP32) or VFM_BF16 (all others) */
   int32_t w4_group_size;    /* 128 for VFM_W_W4A16 and VFM_W_W4A8, ignored otherwise */
+  int32_t variant;          /* vfm_variant */
 } vfm_config;
 
 /* A named weight handed to vfm_expert_create. Matrices are row-major
@@ -108,12 +121,17 @@ int vfm_abi_version(void);
 const char* vfm_last_error(void);
 
 /* Create an expert from a config and its named weights.
- * Names: time_mlp_in.{w,b} [E][W],[W]; time_mlp_out.{w,b} [W][W],[W];
+ * pi0.5 names: time_mlp_in.{w,b} [E][W],[W]; time_mlp_out.{w,b} [W][W],[W];
  * in_proj.{w,b} [A][W],[W]; state_proj.{w,b} [S][W],[W] (S > 0 only);
  * layers.{l}.attn_norm.mod.{w,b} and layers.{l}.mlp_norm.mod.{w,b} [W][3W],[3W]
  * (columns [scale | shift | gate]); layers.{l}.{q,k,v}.w [W][H*d] (head-major
  * columns); layers.{l}.o.w [Hq*d][W]; layers.{l}.{gate,up}.w [W][F];
  * layers.{l}.down.w [F][W]; final_norm.mod.{w,b}; out_proj.{w,b} [W][A],[A].
+ * pi0 names: time_mlp_in.{w,b} [2W][W],[W] (rows 0..W-1 take the action
+ * embedding, rows W..2W-1 the time embedding); time_mlp_out.{w,b};
+ * in_proj.{w,b}; state_proj.{w,b}; layers.{l}.attn_norm.w and
+ * layers.{l}.mlp_norm.w [W] (the w of a (1 + w) gain); the same q/k/v/o/
+ * gate/up/down; final_norm.w [W]; out_proj.{w,b}.
  * Synchronous on `stream`: copies, repacks and (for FP8 / W4A16) quantises the
  * weights on the device and precomputes the time-conditioning table for the
  * N fixed times t_k = (N-k)/N. All workspace for max_batch / max_prefix_len

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vfm_abi_version() == vfm.ABI_VERSION == 1
+    assert lib.vfm_abi_version() == vfm.ABI_VERSION == 2
 
 
 def _create(lib, cfg, weights=None):
@@ -64,6 +64,33 @@ def test_create_rejects_bad_configs(lib):
     c.rope_base = -1.0
     assert vfm.STATUS[_create(lib, c)[0]] == "VFM_E_INVALID_ARG"
     assert vfm.STATUS[_create(lib, good)[0]] == "VFM_E_INVALID_ARG"      # no weights
+
+
+def test_pi0_config_limits(lib):
+    base = CONFIGS["pi0_tiny_fp32"]
+    for kw, want in [(dict(), "VFM_E_INVALID_ARG"),                         # valid: fails for want of weights
+                     (dict(state_dim=0), "VFM_E_INVALID_ARG"),
+                     (dict(time_emb_dim=128), "VFM_E_INVALID_ARG"),
+                     (dict(action_horizon=64), "VFM_E_INVALID_ARG"),
+                     (dict(num_layers=0), "VFM_E_INVALID_ARG"),
+                     (dict(weight_precision="w8a16", width=512, mlp_dim=1024, time_emb_dim=512, num_q_heads=8),
+                      "VFM_E_UNSUPPORTED")]:
+        c = vfm.make_config(base.replace(**kw))
+        st, out = _create(lib, c)
+        assert vfm.STATUS[st] == want, (kw, lib.vfm_last_error().decode())
+        assert not out.value
+    c = vfm.make_config(base)
+    c.variant = 2
+    assert vfm.STATUS[_create(lib, c)[0]] == "VFM_E_INVALID_ARG"
+    assert "variant" in lib.vfm_last_error().decode()
+    # a pi0.5 weight set is refused for a pi0 config (its time MLP input is E wide, not 2W)
+    ws, keep = _fake_weights(CONFIGS["tiny_fp32"].replace(state_dim=8))
+    st, _ = _create(lib, vfm.make_config(base), ws)
+    assert vfm.STATUS[st] == "VFM_E_SHAPE" and "time_mlp_in.w" in lib.vfm_last_error().decode()
+    # and the pi0 set passes every name, dtype and shape check (it fails only on the fake pointers' first use)
+    ws, keep = _fake_weights(base, drop="final_norm.w")
+    st, _ = _create(lib, vfm.make_config(base), ws)
+    assert vfm.STATUS[st] == "VFM_E_INVALID_ARG" and "final_norm.w" in lib.vfm_last_error().decode()
 
 
 def test_create_rejects_quantised_shapes_it_cannot_split(lib):

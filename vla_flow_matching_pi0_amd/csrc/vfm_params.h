@@ -16,20 +16,26 @@ constexpr int BAR_COUNTERS = 64;
 constexpr int BAR_WORDS = 64 + 64 * BAR_COUNTERS;
 
 enum Phase {
-  PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_COUNT
+  PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_TMLP, PH_COUNT
 };
 
 // Everything a phase needs; passed by value as the kernel argument.
 struct VP {
+  // H: suffix tokens per sample (the action horizon; pi0: one state token
+  // more, token 0); M = B H rows
   int L, W, Hq, Hkv, d, F, H, A, S, N, B, P, M, n_norms, KS, kps;
-  int gp_nt[4], gp_s[4];   // GEMM plan (qkv, o, gateup, down): tiles per unit, K splits
+  int pi0;                 // variant: 0 pi0.5 (adaptive norms), 1 pi0 (state token, action-time MLP)
+  int gp_nt[5], gp_s[5];   // GEMM plan (qkv, o, gateup, down, time MLP out): tiles per unit, K splits
   int S_o, S_down;         // = gp_s[1], gp_s[3]
   float eps;
   const uint8_t* w_qkv[MAX_LAYERS];   // packed [N/16][K/KB][64][16 B]
   const uint8_t* w_o[MAX_LAYERS];
   const uint8_t* w_gu[MAX_LAYERS];
   const uint8_t* w_down[MAX_LAYERS];
-  const float *in_w, *in_b, *st_w, *st_b, *out_w, *out_b;   // f32 copies
+  const float *in_w, *in_b, *st_w, *st_b, *out_w, *out_b;   // f32 copies (pi0: in_w = W_in W_mi[:W], in_b unused)
+  const uint8_t* w_tmlp;   // pi0: packed time-MLP output weight [W][W]
+  const float* tbias;      // pi0: [N][W] b_in W_mi[:W] + sincos(t_k) W_mi[W:] + b_mi
+  const float* tmlp_b;     // pi0: [W] time-MLP output bias
   const float* mod;        // [N][2L+1][3][W]  (scale, shift, gate) per step and norm
   const float* rope;       // [H][d/2][2]      (cos, sin) at positions P..P+H-1
   const void* prefix_k;    // [L][B][P][Hkv][d] act type
@@ -45,7 +51,7 @@ struct VP {
   // (K = W), attn (K = Hq*d), xn_mlp (K = W), act (K = F)
   uint8_t* ring;
   size_t slab;
-  size_t off_xna, off_q, off_k, off_v, off_attn, off_xnm, off_act;
+  size_t off_xna, off_q, off_k, off_v, off_attn, off_xnm, off_act, off_u;   // off_u: pi0 time-MLP hidden (slab of layer 0)
   void* opart;             // [B*Hq*KS*64][d]  unnormalised split outputs (activation type)
   float* ml;               // [B*Hq*KS*64][2]  (max, sum) per split row, log2 domain
   float* part_o;           // [S_o][M][W]  K-split partial sums of the o projection
@@ -86,6 +92,11 @@ hipError_t w4_to_bf16_packed(uint8_t* dst, const uint8_t* src, int K, int Npk, h
 hipError_t build_mod_table(float* tab, const void* const* mod_w, const void* const* mod_b, int n_norms,
                            const void* t1w, const void* t1b, const void* t2w, const void* t2b,
                            int N, int E, int W, int src_bf16, double* scratch, hipStream_t st);
+// pi0: plain-norm modulation rows (w, 0, 1), the folded action projection
+// fold = W_in W_mi[:W] ([A][W]) and the per-step bias tbias ([N][W]); scratch >= N W doubles
+hipError_t build_pi0_tables(float* mod, const void* const* norm_w, int n_norms, float* fold, float* tbias,
+                            const void* in_w, const void* in_b, const void* wmi, const void* bmi, int A, int W, int N,
+                            int src_bf16, double* scratch, hipStream_t st);
 hipError_t build_rope(float* rope, int H, int d, int P, float base, hipStream_t st);
 hipError_t zero_words(unsigned* p, int n, hipStream_t st);
 

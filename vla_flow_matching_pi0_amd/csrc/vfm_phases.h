@@ -180,8 +180,9 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
 #pragma unroll
     for (int s = 0; s < MAX_KSPLIT; ++s)
       pv[s] = coh_ld16_if(pr, (uint32_t)((((size_t)s * p.M + m) * p.W + c * 4) * 4), act && s < S);
-    const floatx4 gate =
-        as_f4(ld16_if(mr, (uint32_t)(((((size_t)step * p.n_norms + gate_ni) * 3 + 2) * p.W + c * 4) * 4), act));
+    // gate_ni < 0: the partial sums of pi0's time-MLP output, ungated
+    const floatx4 gate = gate_ni < 0 ? floatx4{1.f, 1.f, 1.f, 1.f}
+        : as_f4(ld16_if(mr, (uint32_t)(((((size_t)step * p.n_norms + gate_ni) * 3 + 2) * p.W + c * 4) * 4), act));
     floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < MAX_KSPLIT; ++s) acc += as_f4(pv[s]);
@@ -233,7 +234,7 @@ __device__ __forceinline__ void ph_rn(const VP&, int step, int layer, bool mlp, 
   const int tid = tid_opaque();
   float* red = reinterpret_cast<float*>(smem);
   const float* part = mlp ? p.part_o : p.part_d;
-  const int S = mlp ? p.S_o : p.S_down;
+  const int S = mlp ? p.S_o : layer == 0 ? p.gp_s[4] : p.S_down;   // layer 0 (pi0 only): the time-MLP output
   const int gate_ni = mlp ? 2 * layer : 2 * layer - 1, ni = mlp ? 2 * layer + 1 : 2 * layer;
   void* xn = slab(p, step, layer) + (mlp ? p.off_xnm : p.off_xna);
   for (int m = wg; m < p.M; m += nwg) {
@@ -262,14 +263,16 @@ __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, i
   const float dt = -1.0f / (float)p.N;
   const auto wout = rsrc(p.out_w), win = rsrc(p.in_w), wst = rsrc(p.st_w);
   for (int m = wg; m < p.M; m += nwg) {
-    const int b = m / p.H;
+    const int b = m / p.H, i = m - b * p.H;
+    const bool srow = p.pi0 && i == 0;                     // pi0's state token: no action of its own
+    const int xm = p.pi0 ? b * (p.H - 1) + i - 1 : m;     // row of x / noise
     if (kp < 0) {
-      if (c < A) {
-        const float v = p.noise[(size_t)m * A + c];
+      if (c < A && !srow) {
+        const float v = p.noise[(size_t)xm * A + c];
         xrow[c] = v;
-        if (p.noise != p.x) stf_coh(p.x, (size_t)m * A + c, v);
+        if (p.noise != p.x) stf_coh(p.x, (size_t)xm * A + c, v);
       }
-    } else {
+    } else if (!srow) {
       // h += gate * sum_s partial_s of the last layer, then the final adaRMSNorm into LDS
       floatx4 hv = {0, 0, 0, 0};
       if (c < W4) {
@@ -316,14 +319,54 @@ __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, i
       if (c < nq) {
         floatx4 v = as_f4(ro_ld16(p.out_b + 4 * c));
         for (int j = 0; j < nsub; ++j) v += part[c + j * nq];
-        const uint32_t off = (uint32_t)(((size_t)m * A + 4 * c) * 4);
+        const uint32_t off = (uint32_t)(((size_t)xm * A + 4 * c) * 4);
         const floatx4 x = as_f4(coh_ld16(p.x, off)) + dt * v;
         coh_st16(p.x, off, as_u4(x));
         *reinterpret_cast<floatx4*>(xrow + 4 * c) = x;
       }
     }
     __syncthreads();
-    if (kn < p.N) {
+    if (kn < p.N && p.pi0) {
+      // pi0: the state token starts from s = state W_s + b_s; an action token
+      // from the time-MLP output bias, its hidden u = SiLU(x (W_in W_mi) +
+      // tbias[t]) going to the time-MLP output GEMM (the state row's u is 0)
+      floatx4 hv = {0, 0, 0, 0}, u = {0, 0, 0, 0};
+      if (c < W4) {
+        if (srow) {
+          if (kp < 0) {
+            floatx4 sv = as_f4(ro_ld16(p.st_b + c * 4));
+            for (int j0 = 0; j0 < p.S; j0 += 16) {
+              u32x4 wv[16];
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                wv[j] = ld16_if(wst, (uint32_t)(((size_t)(j0 + j) * W + c * 4) * 4), j0 + j < p.S);
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (j0 + j < p.S) sv += p.state[(size_t)b * p.S + j0 + j] * as_f4(wv[j]);
+            }
+            coh_st16(p.s_emb, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(sv));
+            hv = sv;
+          } else {
+            hv = as_f4(coh_ld16(p.s_emb, (uint32_t)(((size_t)m * W + c * 4) * 4)));
+          }
+        } else {
+          floatx4 pre = as_f4(ro_ld16(p.tbias + (size_t)kn * W + c * 4));
+          for (int a0 = 0; a0 < A; a0 += 16) {
+            u32x4 wv[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              wv[j] = ld16_if(win, (uint32_t)(((size_t)(a0 + j) * W + c * 4) * 4), a0 + j < A);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pre += (a0 + j < A ? xrow[a0 + j] : 0.f) * as_f4(wv[j]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) u[q] = pre[q] / (1.0f + expf(-pre[q]));
+          hv = as_f4(ro_ld16(p.tmlp_b + c * 4));
+        }
+        coh_st16(p.h, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(hv));
+        store_gemm_in4<T, false>(p, slab(p, kn, 0) + p.off_u, m, c * 4, u, 1.0f);
+      }
+    } else if (kn < p.N) {
       // h = x W_in + b_in + s, four columns per thread
       floatx4 hv = {0, 0, 0, 0};
       if (c < W4) {
@@ -385,7 +428,7 @@ __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, i
 // are summed through LDS. Nonlinear epilogues (RoPE, GeGLU) need S = 1; the
 // linear residual GEMMs (o, down) write S partial sums that the next row
 // phase adds.
-enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3 };
+enum { G_QKV = 0, G_O = 1, G_GU = 2, G_DOWN = 3, G_TMLP = 4 };
 constexpr int GEMM_PASS = 4;     // MFMA k blocks per wave per pass
 
 
@@ -412,7 +455,8 @@ __device__ __forceinline__ GemmShape gemm_shape(const VP& p, int layer) {
   if (WHICH == G_QKV) { g.K = p.W; g.N = (p.Hq + 2 * p.Hkv) * p.d; g.Wp = p.w_qkv[layer]; }
   else if (WHICH == G_O) { g.K = p.Hq * p.d; g.N = p.W; g.Wp = p.w_o[layer]; }
   else if (WHICH == G_GU) { g.K = p.W; g.N = 2 * p.F; g.Wp = p.w_gu[layer]; }
-  else { g.K = p.F; g.N = p.W; g.Wp = p.w_down[layer]; }
+  else if (WHICH == G_DOWN) { g.K = p.F; g.N = p.W; g.Wp = p.w_down[layer]; }
+  else { g.K = p.W; g.N = p.W; g.Wp = p.w_tmlp; }
   g.Ws = g.Wp + (WF == WF_I8 ? (size_t)g.N * g.K : (size_t)g.N * g.K / 2);
   g.nt = p.gp_nt[WHICH];
   g.S = p.gp_s[WHICH];
@@ -552,7 +596,8 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
   if (WHICH == G_QKV) A = (const T*)(sl + p.off_xna);
   else if (WHICH == G_O) A = (const T*)(sl + p.off_attn);
   else if (WHICH == G_GU) A = (const T*)(sl + p.off_xnm);
-  else A = (const T*)(sl + p.off_act);
+  else if (WHICH == G_DOWN) A = (const T*)(sl + p.off_act);
+  else A = (const T*)(sl + p.off_u);
   const GemmShape gs = gemm_shape<T, WHICH, WF>(p, layer);
   const int K = gs.K, nt = gs.nt, S = gs.S, ngroups = gs.ngroups, units = gs.units, KR = gs.KR, nkbw = gs.nkbw;
   const int Mpad = ((p.M + 63) / 64) * 64;
@@ -970,10 +1015,12 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
         }
       }
       float pr[8];
+      // pi0: the state token (query row 0) sees the prefix and its own key only
+      const int lim = (p.pi0 && qrow == 0) ? min(s1, P + 1) : s1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pr[r] = (sc + 4 * g + r < s1) ? slo[r] * scale : -INFINITY;
-        pr[4 + r] = (sc + 16 + 4 * g + r < s1) ? shi[r] * scale : -INFINITY;
+        pr[r] = (sc + 4 * g + r < lim) ? slo[r] * scale : -INFINITY;
+        pr[4 + r] = (sc + 16 + 4 * g + r < lim) ? shi[r] * scale : -INFINITY;
       }
       float cmax = pr[0];
 #pragma unroll
@@ -1100,9 +1147,17 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
   ph_boundary<T, WF>(p, -1, 0, wg, nwg);
-  if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
+  if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
+  else if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
   for (int k = 0; k < p.N; ++k) {
+    if (p.pi0) {
+      // the action tokens' time-MLP output, then layer 0's norm
+      ph_gemm<T, G_TMLP, true, WF>(p, k, 0, wg, nwg, pre);
+      VFM_BAR();
+      ph_rn<T, WF>(p, k, 0, false, wg, nwg);
+      VFM_BAR_PF(G_QKV, 0);
+    }
     for (int l = 0; l < p.L; ++l) {
       if (l > 0) {
         ph_rn<T, WF>(p, k, l, false, wg, nwg);
@@ -1127,7 +1182,8 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       VFM_BAR();
     }
     ph_boundary<T, WF>(p, k, k + 1, wg, nwg);
-    if (p.L > 0 && k + 1 < p.N) VFM_BAR_PF(G_QKV, 0);
+    if (p.pi0 && k + 1 < p.N) VFM_BAR_PF(G_TMLP, 0);
+    else if (p.L > 0 && k + 1 < p.N) VFM_BAR_PF(G_QKV, 0);
     else VFM_BAR();
   }
 #undef VFM_BAR_PF
@@ -1148,6 +1204,7 @@ __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
   else if constexpr (PH == PH_RN_MLP) ph_rn<T, WF>(p, k, l, true, wg, nwg);
   else if constexpr (PH == PH_GU) ph_gemm<T, G_GU, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
   else if constexpr (PH == PH_DOWN) ph_gemm<T, G_DOWN, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
+  else if constexpr (PH == PH_TMLP) ph_gemm<T, G_TMLP, false, WF, CAL>(p, k, l, wg, nwg, WPre{});
 }
 
 template <typename T, int D, int WF, bool CAL>
@@ -1161,7 +1218,8 @@ __host__ const void* phase_kernel(int ph) {
     case PH_O: return (const void*)&k_phase<T, D, PH_O, WF, CAL>;
     case PH_RN_MLP: return (const void*)&k_phase<T, D, PH_RN_MLP, WF, CAL>;
     case PH_GU: return (const void*)&k_phase<T, D, PH_GU, WF, CAL>;
-    default: return (const void*)&k_phase<T, D, PH_DOWN, WF, CAL>;
+    case PH_DOWN: return (const void*)&k_phase<T, D, PH_DOWN, WF, CAL>;
+    default: return (const void*)&k_phase<T, D, PH_TMLP, WF, CAL>;
   }
 }
 

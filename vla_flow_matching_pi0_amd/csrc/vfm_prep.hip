@@ -358,6 +358,69 @@ hipError_t build_mod_table(float* tab, const void* const* mod_w, const void* con
   return build_mod_table_t<float>(tab, mod_w, mod_b, n_norms, t1w, t1b, t2w, t2b, N, E, W, scratch, st);
 }
 
+// ---------------------------------------------------------------- pi0 tables
+// Plain (1 + w) norms as modulation rows: (scale, shift, gate) = (w, 0, 1) at every step.
+template <typename TS>
+__global__ void k_plain_mod(float* tab, const TS* w, int N, int n_norms, int ni, int W) {
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < N * W; idx += gridDim.x * blockDim.x) {
+    const int k = idx / W, c = idx % W;
+    float* row = tab + ((size_t)k * n_norms + ni) * 3 * W;
+    row[c] = to_f(w[c]);
+    row[W + c] = 0.0f;
+    row[2 * W + c] = 1.0f;
+  }
+}
+
+// fold[a][o] = sum_i in_w[a][i] W_mi[i][o] (the action half of the time MLP's
+// first layer folded into the action projection), fp64 sums.
+template <typename TS>
+__global__ void k_fold(float* fold, const TS* in_w, const TS* wmi, int A, int W) {
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < A * W; idx += gridDim.x * blockDim.x) {
+    const int a = idx / W, o = idx % W;
+    double acc = 0.0;
+    for (int i = 0; i < W; ++i) acc += (double)to_f(in_w[(size_t)a * W + i]) * (double)to_f(wmi[(size_t)i * W + o]);
+    fold[idx] = (float)acc;
+  }
+}
+
+// tbias[k][o] = b_in W_mi[:W] + sincos(t_k) W_mi[W:] + b_mi, fp64 sums; e [N][W].
+template <typename TS>
+__global__ void k_tbias(float* tbias, const double* e, const TS* in_b, const TS* wmi, const TS* bmi, int N, int W) {
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < N * W; idx += gridDim.x * blockDim.x) {
+    const int k = idx / W, o = idx % W;
+    double acc = (double)to_f(bmi[o]);
+    for (int i = 0; i < W; ++i) {
+      acc += (double)to_f(in_b[i]) * (double)to_f(wmi[(size_t)i * W + o]);
+      acc += e[(size_t)k * W + i] * (double)to_f(wmi[(size_t)(W + i) * W + o]);
+    }
+    tbias[idx] = (float)acc;
+  }
+}
+
+template <typename TS>
+static hipError_t build_pi0_tables_t(float* mod, const void* const* norm_w, int n_norms, float* fold, float* tbias,
+                                     const void* in_w, const void* in_b, const void* wmi, const void* bmi, int A, int W,
+                                     int N, double* scratch, hipStream_t st) {
+  const int tb = 256;
+  for (int ni = 0; ni < n_norms; ++ni)
+    hipLaunchKernelGGL((k_plain_mod<TS>), dim3((N * W + tb - 1) / tb), dim3(tb), 0, st, mod, (const TS*)norm_w[ni], N,
+                       n_norms, ni, W);
+  hipLaunchKernelGGL((k_fold<TS>), dim3((A * W + tb - 1) / tb), dim3(tb), 0, st, fold, (const TS*)in_w, (const TS*)wmi,
+                     A, W);
+  hipLaunchKernelGGL(k_time_embed, dim3((N * W / 2 + tb - 1) / tb), dim3(tb), 0, st, scratch, N, W);
+  hipLaunchKernelGGL((k_tbias<TS>), dim3((N * W + tb - 1) / tb), dim3(tb), 0, st, tbias, scratch, (const TS*)in_b,
+                     (const TS*)wmi, (const TS*)bmi, N, W);
+  return hipGetLastError();
+}
+
+hipError_t build_pi0_tables(float* mod, const void* const* norm_w, int n_norms, float* fold, float* tbias,
+                            const void* in_w, const void* in_b, const void* wmi, const void* bmi, int A, int W, int N,
+                            int src_bf16, double* scratch, hipStream_t st) {
+  if (src_bf16)
+    return build_pi0_tables_t<bf16>(mod, norm_w, n_norms, fold, tbias, in_w, in_b, wmi, bmi, A, W, N, scratch, st);
+  return build_pi0_tables_t<float>(mod, norm_w, n_norms, fold, tbias, in_w, in_b, wmi, bmi, A, W, N, scratch, st);
+}
+
 // rope[i][j] = (cos, sin)((P + i) * base^(-2j/d)), angles in fp64.
 __global__ void k_rope(float* rope, int H, int d, int P, double base) {
   const int hd = d / 2, total = H * hd;

@@ -68,6 +68,10 @@ struct vfm_expert {
   std::vector<float> act_scale;     // FP8: [L][4] activation scales (empty until calibrated or set)
   float* qs = nullptr;              // FP8: device [L][4][alpha, 1/act_scale]
   int L = 0, W = 0, Hq = 0, Hkv = 0, d = 0, F = 0, H = 0, A = 0, S = 0, E = 0, N = 0;
+  int pi0 = 0;            // variant pi0: a state token before the action tokens
+  int T = 0;              // suffix tokens per sample: H (+1 for pi0)
+  uint8_t* w_tmlp = nullptr;   // pi0: packed time-MLP output weight
+  float *tbias = nullptr, *tmlp_b = nullptr;
   int maxB = 0, maxP = 0, KSmax = 0;
   std::vector<void*> allocs;
   std::vector<uint8_t*> w_qkv, w_o, w_gu, w_down;
@@ -80,7 +84,7 @@ struct vfm_expert {
   float* h = nullptr;
   float *part_o = nullptr, *part_d = nullptr;
   uint8_t* ring = nullptr;     // write-once activation slabs, one per (step, layer)
-  size_t slab = 0, off_xna = 0, off_q = 0, off_k = 0, off_v = 0, off_attn = 0, off_xnm = 0, off_act = 0;
+  size_t slab = 0, off_xna = 0, off_q = 0, off_k = 0, off_v = 0, off_attn = 0, off_xnm = 0, off_act = 0, off_u = 0;
   float *opart = nullptr, *ml = nullptr;
   unsigned* bar = nullptr;
   unsigned long long* trace = nullptr;   // phase timeline (option "trace")
@@ -163,6 +167,16 @@ vfm_status validate_config(const vfm_config* c) {
   if (!(c->rms_eps > 0.f)) return fail(VFM_E_INVALID_ARG, "rms_eps must be > 0");
   if (c->weight_precision < VFM_W_FP32 || c->weight_precision > VFM_W_W4A8)
     return fail(VFM_E_INVALID_ARG, "weight_precision %d unknown", c->weight_precision);
+  if (c->variant != VFM_VARIANT_PI05 && c->variant != VFM_VARIANT_PI0)
+    return fail(VFM_E_INVALID_ARG, "variant %d unknown", c->variant);
+  if (c->variant == VFM_VARIANT_PI0) {
+    if (c->weight_precision != VFM_W_FP32 && c->weight_precision != VFM_W_BF16)
+      return fail(VFM_E_UNSUPPORTED, "the pi0 variant is built for fp32 and bf16 weights");
+    if (c->state_dim < 1) return fail(VFM_E_INVALID_ARG, "the pi0 variant needs a state input (state_dim >= 1)");
+    if (c->time_emb_dim != c->width) return fail(VFM_E_INVALID_ARG, "the pi0 variant needs time_emb_dim == width");
+    if (c->action_horizon > 63) return fail(VFM_E_INVALID_ARG, "the pi0 variant takes at most 63 action tokens");
+    if (c->num_layers < 1) return fail(VFM_E_INVALID_ARG, "the pi0 variant needs at least one layer");
+  }
   if (c->weight_precision == VFM_W_FP32 && c->act_dtype != VFM_F32)
     return fail(VFM_E_INVALID_ARG, "fp32 weights need act_dtype VFM_F32");
   if (c->weight_precision != VFM_W_FP32 && c->act_dtype != VFM_BF16)
@@ -186,7 +200,8 @@ vfm_status validate_config(const vfm_config* c) {
 vfm_status check_extents(const vfm_config* c) {
   const size_t ab = c->act_dtype == VFM_F32 ? 4 : 2;
   const size_t L = c->num_layers, W = c->width, Hq = c->num_q_heads, Hkv = c->num_kv_heads, d = c->head_dim;
-  const size_t F = c->mlp_dim, H = c->action_horizon, N = c->num_steps, B = c->max_batch, P = c->max_prefix_len;
+  const size_t F = c->mlp_dim, H = c->action_horizon + (c->variant == VFM_VARIANT_PI0), N = c->num_steps;
+  const size_t B = c->max_batch, P = c->max_prefix_len;
   const size_t M = B * H, Mpad = (M + 63) / 64 * 64;
   const size_t KS = (P + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST + (H + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST;
   struct { const char* what; size_t bytes; } ext[] = {
@@ -214,6 +229,33 @@ struct WeightSpec {
 std::vector<WeightSpec> weight_specs(const vfm_expert& x) {
   std::vector<WeightSpec> v;
   const int64_t W = x.W, E = x.E, A = x.A, S = x.S, F = x.F, qd = (int64_t)x.Hq * x.d, kd = (int64_t)x.Hkv * x.d;
+  if (x.pi0) {
+    // action-time MLP on [action ; time] (2W -> W -> W), state token, plain (1 + w) norms
+    v.push_back({"time_mlp_in.w", {2 * W, W}});
+    v.push_back({"time_mlp_in.b", {W}});
+    v.push_back({"time_mlp_out.w", {W, W}});
+    v.push_back({"time_mlp_out.b", {W}});
+    v.push_back({"in_proj.w", {A, W}});
+    v.push_back({"in_proj.b", {W}});
+    v.push_back({"state_proj.w", {S, W}});
+    v.push_back({"state_proj.b", {W}});
+    for (int l = 0; l < x.L; ++l) {
+      const std::string p = "layers." + std::to_string(l) + ".";
+      v.push_back({p + "attn_norm.w", {W}});
+      v.push_back({p + "q.w", {W, qd}});
+      v.push_back({p + "k.w", {W, kd}});
+      v.push_back({p + "v.w", {W, kd}});
+      v.push_back({p + "o.w", {qd, W}});
+      v.push_back({p + "mlp_norm.w", {W}});
+      v.push_back({p + "gate.w", {W, F}});
+      v.push_back({p + "up.w", {W, F}});
+      v.push_back({p + "down.w", {F, W}});
+    }
+    v.push_back({"final_norm.w", {W}});
+    v.push_back({"out_proj.w", {W, A}});
+    v.push_back({"out_proj.b", {A}});
+    return v;
+  }
   v.push_back({"time_mlp_in.w", {E, W}});
   v.push_back({"time_mlp_in.b", {W}});
   v.push_back({"time_mlp_out.w", {W, W}});
@@ -332,6 +374,7 @@ int phase_grid(const VP& p, int phase) {
     case vfm::PH_O: units = (long)p.W / (16 * p.gp_nt[1]) * p.gp_s[1] * mt; break;
     case vfm::PH_GU: units = (long)2 * p.F / (16 * p.gp_nt[2]) * p.gp_s[2] * mt; break;
     case vfm::PH_DOWN: units = (long)p.W / (16 * p.gp_nt[3]) * p.gp_s[3] * mt; break;
+    case vfm::PH_TMLP: units = (long)p.W / (16 * p.gp_nt[4]) * p.gp_s[4] * mt; break;
     case vfm::PH_ATTN: units = (long)p.B * p.Hq * p.KS; break;
     case vfm::PH_COMBINE: units = cdiv((long)p.M * p.Hq, vfm::NTHREADS / 64); break;
   }
@@ -345,6 +388,7 @@ hipError_t enqueue_phases(vfm_expert* x, const VP& p, int kset, hipStream_t st) 
   auto run = [&](int ph, int k, int l) { return vfm::launch_phase(p, kset, 1, ph, k, l, phase_grid(p, ph), x->lds, st); };
   if ((e = run(vfm::PH_BOUNDARY, 0, 0)) != hipSuccess) return e;
   for (int k = 0; k < p.N; ++k) {
+    if (p.pi0 && ((e = run(vfm::PH_TMLP, k, 0)) != hipSuccess || (e = run(vfm::PH_RN_ATTN, k, 0)) != hipSuccess)) return e;
     for (int l = 0; l < p.L; ++l) {
       if (l > 0 && (e = run(vfm::PH_RN_ATTN, k, l)) != hipSuccess) return e;
       const int seq[] = {vfm::PH_QKV, vfm::PH_ATTN, vfm::PH_COMBINE, vfm::PH_O, vfm::PH_RN_MLP, vfm::PH_GU, vfm::PH_DOWN};
@@ -390,11 +434,13 @@ vfm_status report(vfm_status s, const char* fmt, ...) {
 // The launch parameter block of one call: shapes, weights, workspace,
 // buffers and the GEMM plan for the expert's weight format.
 vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const float* state, float* actions) {
-  p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->H; p.A = x->A;
-  p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->H; p.n_norms = 2 * x->L + 1;
+  p.L = x->L; p.W = x->W; p.Hq = x->Hq; p.Hkv = x->Hkv; p.d = x->d; p.F = x->F; p.H = x->T; p.A = x->A;
+  p.S = x->S; p.N = x->N; p.B = B; p.P = P; p.M = B * x->T; p.n_norms = 2 * x->L + 1;
+  p.pi0 = x->pi0;
+  p.w_tmlp = x->w_tmlp; p.tbias = x->tbias; p.tmlp_b = x->tmlp_b; p.off_u = x->off_u;
   constexpr int AK = vfm::ATT_KEYS_HOST;   // keys per attention split
   p.kps = AK;
-  p.KS = (P + AK - 1) / AK + (x->H + AK - 1) / AK;   // prefix splits, then chunk splits
+  p.KS = (P + AK - 1) / AK + (x->T + AK - 1) / AK;   // prefix splits, then chunk splits
   p.eps = x->cfg.rms_eps;
   for (int l = 0; l < x->L; ++l) {
     p.w_qkv[l] = x->w_qkv[l]; p.w_o[l] = x->w_o[l]; p.w_gu[l] = x->w_gu[l]; p.w_down[l] = x->w_down[l];
@@ -416,9 +462,9 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
       nwg = x->coop_grid;
     }
     const int KB = x->KW;
-    const int Ks[4] = {x->W, x->Hq * x->d, x->W, x->F};
-    const int Ns[4] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W};
-    for (int i = 0; i < 4; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i == 1 || i == 3, &p.gp_nt[i], &p.gp_s[i]);
+    const int Ks[5] = {x->W, x->Hq * x->d, x->W, x->F, x->W};
+    const int Ns[5] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W, x->W};
+    for (int i = 0; i < 5; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i != 0 && i != 2, &p.gp_nt[i], &p.gp_s[i]);
     p.S_o = p.gp_s[1];
     p.S_down = p.gp_s[3];
   }
@@ -456,6 +502,8 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   tmp.d = cfg->head_dim; tmp.F = cfg->mlp_dim; tmp.H = cfg->action_horizon; tmp.A = cfg->action_dim;
   tmp.S = cfg->state_dim; tmp.E = cfg->time_emb_dim; tmp.N = cfg->num_steps;
   tmp.maxB = cfg->max_batch; tmp.maxP = cfg->max_prefix_len;
+  tmp.pi0 = cfg->variant == VFM_VARIANT_PI0;
+  tmp.T = tmp.H + tmp.pi0;
 
   // ---- weights: every expected name exactly once, right dtype and shape, nothing else
   const int master_dt = tmp.src_bf16 ? VFM_BF16 : VFM_F32;
@@ -577,6 +625,13 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     }
     x->w_qkv.push_back(wq); x->w_o.push_back(wo); x->w_gu.push_back(wg); x->w_down.push_back(wd);
   }
+  if (x->pi0) {
+    x->w_tmlp = (uint8_t*)x->dalloc(wbytes(W, W));
+    if (!x->w_tmlp) { fail(VFM_E_OOM, "weight allocation failed"); return bail(VFM_E_OOM); }
+    hipError_t e = vfm::pack_weight(x->w_tmlp, W, W, os, oi, ptr["time_mlp_out.w"], W, nullptr, 0, nullptr, 0,
+                                    x->src_bf16, x->act_bf16, s);
+    if (e != hipSuccess) { fail(VFM_E_HIP, "weight packing failed: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
   if (x->wprec == VFM_W_FP8) {
     std::vector<float> am((size_t)L * 4);
     if (L > 0 && (hipMemcpyAsync(am.data(), x->wamax, am.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -595,8 +650,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   }
   // small f32 weights
   struct Cv { float** dst; const char* name; size_t n; };
-  std::vector<Cv> cvs = {{&x->in_w, "in_proj.w", (size_t)A * W}, {&x->in_b, "in_proj.b", (size_t)W},
-                         {&x->out_w, "out_proj.w", (size_t)W * A}, {&x->out_b, "out_proj.b", (size_t)A}};
+  std::vector<Cv> cvs = {{&x->in_b, "in_proj.b", (size_t)W}, {&x->out_w, "out_proj.w", (size_t)W * A},
+                         {&x->out_b, "out_proj.b", (size_t)A}};
+  if (x->pi0) cvs.push_back({&x->tmlp_b, "time_mlp_out.b", (size_t)W});
+  else cvs.push_back({&x->in_w, "in_proj.w", (size_t)A * W});
   if (S > 0) {
     cvs.push_back({&x->st_w, "state_proj.w", (size_t)S * W});
     cvs.push_back({&x->st_b, "state_proj.b", (size_t)W});
@@ -611,7 +668,23 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
   x->mod = (float*)x->dalloc((size_t)x->N * n_norms * 3 * W * 4);
   double* scratch = (double*)x->dalloc(((size_t)x->N * x->E + 2 * (size_t)x->N * W) * 8);
   if (!x->mod || !scratch) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
-  {
+  if (x->pi0) {
+    // plain norms as constant modulation rows; the action half of the time MLP's
+    // first layer folded into the action projection; its time half per step
+    x->in_w = (float*)x->dalloc((size_t)A * W * 4);
+    x->tbias = (float*)x->dalloc((size_t)x->N * W * 4);
+    if (!x->in_w || !x->tbias) { fail(VFM_E_OOM, "allocation failed"); return bail(VFM_E_OOM); }
+    std::vector<const void*> nw;
+    for (int l = 0; l < L; ++l) {
+      const std::string p = "layers." + std::to_string(l) + ".";
+      nw.push_back(ptr[p + "attn_norm.w"]);
+      nw.push_back(ptr[p + "mlp_norm.w"]);
+    }
+    nw.push_back(ptr["final_norm.w"]);
+    hipError_t e = vfm::build_pi0_tables(x->mod, nw.data(), n_norms, x->in_w, x->tbias, ptr["in_proj.w"], ptr["in_proj.b"],
+                                         ptr["time_mlp_in.w"], ptr["time_mlp_in.b"], A, W, x->N, x->src_bf16, scratch, s);
+    if (e != hipSuccess) { fail(VFM_E_HIP, "pi0 tables: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  } else {
     std::vector<const void*> mw, mb;
     for (int l = 0; l < L; ++l) {
       const std::string p = "layers." + std::to_string(l) + ".";
@@ -623,10 +696,11 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
                                         ptr["time_mlp_out.w"], ptr["time_mlp_out.b"], x->N, x->E, W, x->src_bf16, scratch, s);
     if (e != hipSuccess) { fail(VFM_E_HIP, "modulation table: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
   }
-  // workspace for max_batch / max_prefix_len
-  const size_t Mmax = (size_t)x->maxB * H;
-  x->KSmax = (x->maxP + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST + (H + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST;
-  x->rope = (float*)x->dalloc((size_t)H * d * 4);
+  // workspace for max_batch / max_prefix_len (T suffix tokens per sample)
+  const int T = x->T;
+  const size_t Mmax = (size_t)x->maxB * T;
+  x->KSmax = (x->maxP + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST + (T + vfm::ATT_KEYS_HOST - 1) / vfm::ATT_KEYS_HOST;
+  x->rope = (float*)x->dalloc((size_t)T * d * 4);
   x->s_emb = (float*)x->dalloc(Mmax * W * 4);
   x->part_o = (float*)x->dalloc((size_t)vfm::MAX_KSPLIT * Mmax * W * 4);
   x->part_d = (float*)x->dalloc((size_t)vfm::MAX_KSPLIT * Mmax * W * 4);
@@ -642,6 +716,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->off_attn = off; off += al(Mpad * Hq * d * ab);
     x->off_xnm = off; off += al(Mpad * W * ab);
     x->off_act = off; off += al((size_t)F * Mpad * ab);
+    if (x->pi0) { x->off_u = off; off += al(Mpad * W * ab); }
     x->slab = off;
     x->ring = (uint8_t*)x->dalloc(x->slab * (size_t)x->N * std::max(L, 1));
   }
@@ -720,7 +795,7 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
   const std::string k = key, v = value;
   if (k == "trace") {
     if (v == "1" && !x->trace) {
-      x->trace_words = 2 * (size_t)(x->N * (8 * (size_t)x->L + 1) + 4);
+      x->trace_words = 2 * (size_t)(x->N * (8 * (size_t)x->L + 1 + 2 * x->pi0) + 4);
       x->trace = (unsigned long long*)x->dalloc(x->trace_words * 8);
       if (!x->trace) return fail(VFM_E_OOM, "trace buffer");
     } else if (v == "0") {
@@ -775,7 +850,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if ((st = fill_vp(x, p, B, P, noise, state, actions)) != VFM_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (x->rope_P != P) {
-    HIPCHK(vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s));
+    HIPCHK(vfm::build_rope(x->rope, x->T, x->d, P, x->cfg.rope_base, s));
     x->rope_P = P;
     if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
   }
@@ -870,7 +945,7 @@ vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
     p.w_qkv[l] = bq; p.w_o[l] = bo; p.w_gu[l] = bg; p.w_down[l] = bd;
   }
   if (e == hipSuccess && x->rope_P != P) {
-    e = vfm::build_rope(x->rope, x->H, x->d, P, x->cfg.rope_base, s);
+    e = vfm::build_rope(x->rope, x->T, x->d, P, x->cfg.rope_base, s);
     if (e == hipSuccess) x->rope_P = P;
   }
   if (e == hipSuccess) e = enqueue_phases(x, p, vfm::KS_CAL, s);
@@ -916,7 +991,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   // workspace tensors as left by the last denoise call (diagnostics)
   {
     const int B = x->prefix_k.bound ? (int)x->prefix_k.shape[1] : x->maxB;
-    const size_t M = (size_t)B * x->H;
+    const size_t M = (size_t)B * x->T;
     struct Ws { const char* name; const void* ptr; size_t count; bool act; };
     const Ws ws[] = {{"ws.h", x->h, M * x->W, false}};
     for (const Ws& w : ws) {

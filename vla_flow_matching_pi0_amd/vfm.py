@@ -17,9 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libvfm.so")
 
 VFM_F32, VFM_BF16, VFM_F16, VFM_FP8_E4M3, VFM_I4X2 = 0, 1, 2, 3, 4
 WPREC = {"fp32": 0, "bf16": 1, "fp8": 2, "w4a16": 3, "w8a16": 4, "w4a8": 5}
+VARIANT = {"pi05": 0, "pi0": 1}
 STATUS = {0: "VFM_OK", 1: "VFM_E_INVALID_ARG", 2: "VFM_E_SHAPE", 3: "VFM_E_DTYPE", 4: "VFM_E_UNBOUND",
           5: "VFM_E_STATE", 6: "VFM_E_UNSUPPORTED", 7: "VFM_E_OOM", 8: "VFM_E_HIP"}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every entry point include/vfm.h declares.
 EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
@@ -42,7 +43,7 @@ class VfmConfig(ctypes.Structure):
         "action_horizon", "action_dim", "state_dim", "time_emb_dim", "max_prefix_len", "max_batch",
         "num_steps")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
                          ("weight_precision", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                         ("w4_group_size", ctypes.c_int32)]
+                         ("w4_group_size", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class VfmPrefixConfig(ctypes.Structure):
@@ -112,7 +113,7 @@ def _check(status: int) -> None:
 
 def make_config(cfg, max_batch: Optional[int] = None, max_prefix_len: Optional[int] = None) -> VfmConfig:
     """Build the C config from any object with the expert's fields
-    (num_layers, width, ..., weight_precision in {'fp32','bf16','fp8','w4a16'})."""
+    (num_layers, width, ..., weight_precision in WPREC, variant 'pi05' or 'pi0')."""
     c = VfmConfig()
     c.abi_version = ABI_VERSION
     for n in ("num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim", "action_horizon",
@@ -125,6 +126,7 @@ def make_config(cfg, max_batch: Optional[int] = None, max_prefix_len: Optional[i
     c.weight_precision = WPREC[cfg.weight_precision]
     c.act_dtype = VFM_F32 if cfg.weight_precision == "fp32" else VFM_BF16
     c.w4_group_size = int(getattr(cfg, "w4_group", 128))
+    c.variant = VARIANT[getattr(cfg, "variant", "pi05")]
     return c
 
 
