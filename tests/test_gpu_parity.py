@@ -136,14 +136,16 @@ def test_packed_weights_round_trip(cfgname):
     ex.close()
 
 
-def test_pi05_bf16_b32_sampled():
-    """Batch 32, one prefix per sample; checked on three samples (samples
-    never interact, so the oracle runs them alone)."""
+@pytest.mark.parametrize("mode", ["persistent", "graph"])
+def test_pi05_bf16_b32_sampled(mode):
+    """Batch 32, one prefix per sample; checked on two samples (samples
+    never interact, so the oracle runs them alone). In graph mode the 1600
+    rows take the large-M GEMM kernels."""
     gu = _gu()
     cfg = CONFIGS["pi05_bf16_b32"]
     params, pk, pv, noise, state = make_inputs(cfg)
-    print("case pi05_bf16_b32", flush=True)
-    got = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+    print(f"case pi05_bf16_b32 {mode}", flush=True)
+    got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
     c1 = cfg.replace(batch=1)
     for b in (0, 31):
         ref = O.denoise(params, noise[b:b + 1], state[b:b + 1], pk[:, b:b + 1], pv[:, b:b + 1], c1)
@@ -238,3 +240,25 @@ def test_plain_persistent_launch_and_trace():
     n_bar = 1 + N * 8 * L           # one after the first boundary, then 8 per layer (the last one at the step boundary)
     stamps = t[1:n_bar + 1].ravel()
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
+
+
+@pytest.mark.parametrize("variant,batch,horizon", [("pi05", 8, 50), ("pi05", 20, 13), ("pi0", 6, 50)])
+def test_large_m_gemm_matches_oracle(variant, batch, horizon):
+    """Graph and eager launch of a bf16 expert with M = B x T >= 256 rows run
+    the large-M GEMM kernels (128 x 128 tiles; rows not a multiple of 128;
+    pi0's time-MLP GEMM too); persistent launch runs the skinny GEMM. All
+    against the oracle on the whole batch."""
+    gu = _gu()
+    from oracle import pi0 as P0
+    base = CONFIGS["pi0_tiny_fp32" if variant == "pi0" else "tiny_fp32"]
+    cfg = base.replace(weight_precision="bf16", batch=batch, action_horizon=horizon, prefix_len=70,
+                       state_dim=base.state_dim or 6, seed=60 + batch)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    run = P0.denoise_pi0 if variant == "pi0" else O.denoise
+    ref = run(params, noise, state, pk, pv, cfg)
+    print(f"case large-M {variant} B={batch} H={horizon}", flush=True)
+    for mode in ("graph", "eager", "persistent"):
+        got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
+        err = gu.rel_l2(got, ref)
+        print(f"{mode}: rel_l2={err:.3e}")
+        assert err <= 2e-2, mode

@@ -1133,6 +1133,145 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
   }
 }
 
+// ============================================================ large-M GEMM
+// For many tokens (a batch of samples) the skinny GEMM above re-reads every
+// weight slice once per 64-token tile. In the graph and eager launch modes a
+// bf16 expert with M >= 256 rows runs its GEMM phases with this kernel
+// instead: 128 output columns x 128 tokens per workgroup (4 waves of 64 x 64,
+// 16x16x32 bf16 MFMA), both operand tiles staged through LDS in the packed
+// lane order, double-buffered with the next stage's global loads in flight,
+// and the same epilogues (RoPE into the q/k/v tiles, GeGLU into the
+// activation operand, K-split partial sums) as the skinny GEMM. The
+// activation tile comes from the operand order [K/32][Mpad][32], whose
+// 16-token x 32-K block is 1 KiB with lane (c, g) at c * 64 + g * 16 bytes;
+// the LDS store moves it to lane order (g * 16 + c) so that every LDS read
+// is one contiguous 1 KiB.
+constexpr int GM_THREADS = 256;
+constexpr int GM_LDS = 2 * 32768;   // two stages of (A tile + B tile)
+
+template <typename T, int WHICH>
+__global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int layer) {
+  static_assert(sizeof(T) == 2, "the large-M GEMM runs bf16 operands");
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  const GemmShape gs = gemm_shape<T, WHICH, WF_NATIVE>(p, layer);
+  const int K = gs.K, N = gs.N, S = gs.S;
+  const int Mpad = ((p.M + 63) / 64) * 64;
+  const int MTL = (p.M + 127) / 128, NTL = N / 128, total = MTL * NTL * S;
+  const int per = (total + 7) >> 3;
+  const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (v >= total) return;
+  const int mt = v % MTL, nt = (v / MTL) % NTL, s = v / (MTL * NTL);
+  const int KB32 = K >> 5, Ks = K / S, nk = Ks / 64, kb0 = (s * Ks) >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wn = w >> 1, wm = w & 1;
+  uint8_t* sl = slab(p, step, layer);
+  const uint8_t* act;
+  if (WHICH == G_QKV) act = sl + p.off_xna;
+  else if (WHICH == G_O) act = sl + p.off_attn;
+  else if (WHICH == G_GU) act = sl + p.off_xnm;
+  else if (WHICH == G_DOWN) act = sl + p.off_act;
+  else act = sl + p.off_u;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(gs.Wp), rb = rsrc(act);
+  uint32_t aoff[4], boff[4];
+  int bdst[4];
+  bool bok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, blk = c >> 7, rest = c & 127;
+    aoff[i] = (uint32_t)(((nt * 8 + blk) * KB32 + kb0) * 1024 + rest * 16);
+    const int kk = rest >> 6, u = rest & 63;
+    const int m = mt * 128 + blk * 16 + (u >> 2);
+    bok[i] = m < Mpad;
+    boff[i] = (uint32_t)((((kb0 + kk) * Mpad + m) * 32 + (u & 3) * 8) * 2);
+    bdst[i] = (blk * 2 + kk) * 64 + (u & 3) * 16 + (u >> 2);
+  }
+  const uint32_t bstep = (uint32_t)(2 * Mpad * 64);   // two 32-K blocks of activations
+  u32x4 ga[4], gb[4];
+  auto gload = [&](int it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + (uint32_t)it * 2048u, 0, 0);
+      gb[i] = ld16_if(rb, boff[i] + (uint32_t)it * bstep, bok[i]);
+    }
+  };
+  auto lstore = [&](int buf) {
+    u32x4* A = reinterpret_cast<u32x4*>(lds + buf * (GM_LDS / 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A[tid + 256 * i] = ga[i];
+      A[1024 + bdst[i]] = gb[i];
+    }
+  };
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    if (it + 1 < nk) gload(it + 1);
+    const u32x4* A = reinterpret_cast<const u32x4*>(lds + (it & 1) * (GM_LDS / 2));
+    const u32x4* B = A + 1024;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = A[(wn * 4 + i) * 128 + kb * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = B[(wm * 4 + j) * 128 + kb * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = MT<T>::mma(a[i], b[j], acc[i][j]);
+    }
+    if (it + 1 < nk) lstore((it + 1) & 1);
+    __syncthreads();
+  }
+  // epilogue: lane holds rows 4g..4g+3 of 16-column tile `tile` for token gm
+  const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tile = nt * 8 + wn * 4 + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gm = mt * 128 + wm * 64 + j * 16 + c16;
+      if (gm >= p.M) continue;
+      const floatx4 vv = acc[i][j];
+      if (WHICH == G_QKV) {
+        const int d = p.d;
+        const int col0 = tile * 16;
+        const int head = col0 / d, tt = (col0 % d) / 16;
+        const int b = gm / p.H, ti = gm % p.H;
+        if (head < p.Hq + p.Hkv) {
+          const int j0 = tt * 8 + 2 * g;
+          const floatx4 rot = as_f4(ro_ld16(p.rope + ((size_t)ti * (d / 2) + j0) * 2));
+          const float y0 = vv.x * rot[0] - vv.z * rot[1], y0h = vv.z * rot[0] + vv.x * rot[1];
+          const float y1 = vv.y * rot[2] - vv.w * rot[3], y1h = vv.w * rot[2] + vv.y * rot[3];
+          const bool isq = head < p.Hq;
+          uint8_t* dst = sl + (isq ? p.off_q : p.off_k);
+          const size_t hb = isq ? (size_t)b * p.Hq + head : (size_t)b * p.Hkv + (head - p.Hq);
+          const size_t e0 = ((hb * (d / 16) + tt) * 64 + ti) * 16 + 2 * g;
+          coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(y0, y1));
+          coh_st4(dst, (uint32_t)((e0 + 8) * 2), pack_bf16x2(y0h, y1h));
+        } else {
+          const int kvh = head - p.Hq - p.Hkv;
+          const size_t e0 = ((((size_t)b * p.Hkv + kvh) * (d / 16) + tt) * 64 + ti) * 16 + 4 * g;
+          coh_st8(sl + p.off_v, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(vv.x, vv.y), pack_bf16x2(vv.z, vv.w)});
+        }
+      } else if (WHICH == G_GU) {
+        const int f0 = tile * 8 + 2 * g;
+        const float a0 = gelu_tanh(vv.x) * vv.y, a1 = gelu_tanh(vv.z) * vv.w;
+        coh_st4(sl + p.off_act, (uint32_t)(act_off<T>(p, gm, f0) * 2), pack_bf16x2(a0, a1));
+      } else {
+        float* part = WHICH == G_O ? p.part_o : p.part_d;
+        const int n0 = tile * 16 + 4 * g;
+        coh_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(vv));
+      }
+    }
+  }
+}
+
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
 template <typename T, int D, int WF>
@@ -1208,7 +1347,19 @@ __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
 }
 
 template <typename T, int D, int WF, bool CAL>
-__host__ const void* phase_kernel(int ph) {
+__host__ const void* phase_kernel(int ph, bool bigm = false) {
+  if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
+    if (bigm) {
+      switch (ph) {
+        case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV>;
+        case PH_O: return (const void*)&k_gemm_m<T, G_O>;
+        case PH_GU: return (const void*)&k_gemm_m<T, G_GU>;
+        case PH_DOWN: return (const void*)&k_gemm_m<T, G_DOWN>;
+        case PH_TMLP: return (const void*)&k_gemm_m<T, G_TMLP>;
+        default: break;
+      }
+    }
+  }
   switch (ph) {
     case PH_BOUNDARY: return (const void*)&k_phase<T, D, PH_BOUNDARY, WF, CAL>;
     case PH_RN_ATTN: return (const void*)&k_phase<T, D, PH_RN_ATTN, WF, CAL>;
@@ -1240,7 +1391,10 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
     }
   }
   void* args[] = {const_cast<VP*>(&p), &k, &l};
-  return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase), dim3(grid), dim3(NTH), args, lds, st);
+  const bool gemm = phase == PH_QKV || phase == PH_O || phase == PH_GU || phase == PH_DOWN || phase == PH_TMLP;
+  const bool bigm = p.bigm && gemm;
+  return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, bigm), dim3(grid), dim3(bigm ? GM_THREADS : NTH), args,
+                         lds, st);
 }
 
 template <typename T, int D, int WF, bool CAL>
@@ -1249,8 +1403,12 @@ hipError_t set_lds_limit(int bytes) {
   if constexpr (!CAL)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph)
+  for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph) {
     e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    const void* big = phase_kernel<T, D, WF, CAL>(ph, true);
+    if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph))
+      e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > GM_LDS ? bytes : GM_LDS);
+  }
   return e;
 }
 

@@ -366,6 +366,20 @@ int phase_grid(const VP& p, int phase) {
   auto cdiv = [](long a, long b) { return (int)((a + b - 1) / b); };
   const int mt = cdiv(p.M, 64);
   long units = 1;
+  if (p.bigm) {
+    // large-M GEMM kernels: one workgroup per 128 x 128 tile and K split, rounded up to whole XCD rounds
+    const int mt128 = cdiv(p.M, 128);
+    long tiles = -1;
+    switch (phase) {
+      case vfm::PH_QKV: tiles = (long)(p.Hq + 2 * p.Hkv) * p.d / 128 * mt128 * p.gp_s[0]; break;
+      case vfm::PH_O: tiles = (long)p.W / 128 * mt128 * p.gp_s[1]; break;
+      case vfm::PH_GU: tiles = (long)2 * p.F / 128 * mt128 * p.gp_s[2]; break;
+      case vfm::PH_DOWN: tiles = (long)p.W / 128 * mt128 * p.gp_s[3]; break;
+      case vfm::PH_TMLP: tiles = (long)p.W / 128 * mt128 * p.gp_s[4]; break;
+      default: break;
+    }
+    if (tiles > 0) return (int)((tiles + 7) / 8 * 8);
+  }
   switch (phase) {
     case vfm::PH_BOUNDARY:
     case vfm::PH_RN_ATTN:
@@ -465,6 +479,19 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
     const int Ks[5] = {x->W, x->Hq * x->d, x->W, x->F, x->W};
     const int Ns[5] = {(x->Hq + 2 * x->Hkv) * x->d, x->W, 2 * x->F, x->W, x->W};
     for (int i = 0; i < 5; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i != 0 && i != 2, &p.gp_nt[i], &p.gp_s[i]);
+    // many rows in the per-phase launch modes: 128 x 128 tiles of the large-M GEMM kernel, and K splits of
+    // the linear GEMMs until there are 256 tiles, each split a whole number of 64-K stages
+    p.bigm = x->mode != 0 && x->kset == vfm::KS_BF16 && p.M >= 256;
+    if (p.bigm) {
+      const int mt = (p.M + 127) / 128;
+      for (int i = 0; i < 5; ++i) {
+        int sp = 1;
+        if (i != 0 && i != 2)
+          while (sp < vfm::MAX_KSPLIT && (long)(Ns[i] / 128) * mt * sp < 256 && Ks[i] % (sp * 2 * 64) == 0) sp *= 2;
+        p.gp_nt[i] = 8;
+        p.gp_s[i] = sp;
+      }
+    }
     p.S_o = p.gp_s[1];
     p.S_down = p.gp_s[3];
   }
