@@ -178,6 +178,12 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       launches (kernel profilers).
  *   "trace": "1" / "0": record a timeline of the persistent kernel's phase
  *       barriers (workgroup 0), read with vfm_export("trace").
+ *   "graph_cache": "1" .. "64" (default 8): graph mode keeps one captured
+ *       graph per key (B, P and the noise / state / actions / prefix
+ *       pointers), at most this many, dropping the least recently used (the
+ *       FlashRT walk-through's Graph object: an exact-key variant table with
+ *       LRU). Alternating between a few buffer sets then replays without
+ *       capturing again.
  * Errors: VFM_E_INVALID_ARG for an unknown key or value. */
 vfm_status vfm_set_option(vfm_expert* ex, const char* key, const char* value);
 
@@ -328,6 +334,96 @@ vfm_status vfm_prefix_run(vfm_prefix* pre, const void* embeds, int32_t batch, in
 
 /* Synchronise the device and free everything the producer owns. NULL-safe. */
 vfm_status vfm_prefix_destroy(vfm_prefix* pre);
+
+/* ------------------------------------------------------------------------
+ * Plan. The FlashRT walk-through (its exec/ C ABI: Buffer, Graph, Plan)
+ * describes a Plan as a DAG of graphs across streams that carries data
+ * dependencies only, with no priorities or preemption, and the FlashRT-PAI
+ * introduction's execution contract adds per-stage update rates, reuse of
+ * state across decisions and selective refresh. Here a plan is a list of
+ * stages, each the prefix pass of a producer, the denoise call of an expert
+ * or an adopted graph, each with an update rate: stage i runs at tick t when
+ * t >= offset_i and (t - offset_i) is a multiple of every_i, so a prefix stage
+ * with every = 5 refreshes the prefix K/V on every fifth control tick and the
+ * expert stages in between reuse it. Dependencies are derived, not declared:
+ * every stage has the device byte ranges it reads and writes (the producer's
+ * embeddings and K/V outputs; the expert's bound prefix_k / prefix_v / noise /
+ * state / actions, or the pointers given at add time; an adopted graph's
+ * declared ranges) and the private workspace of its producer or expert. Within
+ * a tick, a due stage waits for every earlier due stage (in add order) whose
+ * writes overlap its reads or writes, or whose reads overlap its writes, or that
+ * uses the same producer or expert, or that vfm_plan_add_edge names; other
+ * stages run concurrently on their own streams. An expert in persistent
+ * launch mode holds every compute unit with device-wide barriers, so it also
+ * waits for every earlier due stage, and every later one waits for it. Each
+ * tick is ordered after earlier work on the caller's stream and before later
+ * work on it (the tick forks from and joins back into that stream), so ticks
+ * do not overlap one another.
+ * Thread safety: a plan, and the producers and experts in it, must not be used
+ * from two threads at once.
+ * ------------------------------------------------------------------------ */
+typedef struct vfm_plan vfm_plan;   /* opaque; owned by the caller via create/destroy */
+
+typedef struct {
+  const void* ptr;   /* device address */
+  size_t bytes;
+} vfm_range;
+
+/* Create an empty plan. Host only (streams and events are made at the first
+ * run). Errors: VFM_E_INVALID_ARG (out is NULL). */
+vfm_status vfm_plan_create(vfm_plan** out);
+
+/* Add a stage that runs vfm_prefix_run(pre, embeds, batch, prefix_len,
+ * prefix_k, prefix_v) at its ticks. Reads embeds ([B][P][W] bf16), writes
+ * prefix_k and prefix_v ([L][B][P][Hkv][d] bf16 each). every >= 1,
+ * 0 <= offset < every. *stage receives the stage index (0, 1, ... in add
+ * order). The producer must outlive the plan.
+ * Errors: VFM_E_INVALID_ARG (NULL, misaligned pointer, bad rate),
+ * VFM_E_SHAPE (batch or prefix_len outside the producer's limits). */
+vfm_status vfm_plan_add_prefix(vfm_plan* pl, vfm_prefix* pre, const void* embeds, int32_t batch, int32_t prefix_len,
+                               void* prefix_k, void* prefix_v, int32_t every, int32_t offset, int32_t* stage);
+
+/* Add a stage that runs vfm_denoise(ex, noise, state, actions) at its ticks.
+ * NULL pointers mean the expert's bound buffers as bound when the tick runs
+ * (rebinding between ticks is seen). Reads prefix_k, prefix_v, noise and
+ * state; writes actions. The expert must outlive the plan.
+ * Errors: VFM_E_INVALID_ARG (NULL expert, misaligned pointer, bad rate). */
+vfm_status vfm_plan_add_denoise(vfm_plan* pl, vfm_expert* ex, const float* noise, const float* state, float* actions,
+                                int32_t every, int32_t offset, int32_t* stage);
+
+/* Adopt a graph captured elsewhere (a hipGraphExec_t instantiated on this
+ * device, e.g. a camera pre-processing step or a torch-captured graph): the
+ * stage launches it with hipGraphLaunch at its ticks. reads / writes list
+ * the device ranges the graph reads and writes (n may be 0). The graph
+ * stays owned by the caller and must outlive the plan.
+ * Errors: VFM_E_INVALID_ARG (NULL graph, NULL range list with n > 0, a range
+ * with a NULL pointer or 0 bytes, bad rate). */
+vfm_status vfm_plan_add_graph(vfm_plan* pl, void* graph_exec, const vfm_range* reads, int32_t n_reads,
+                              const vfm_range* writes, int32_t n_writes, int32_t every, int32_t offset,
+                              int32_t* stage);
+
+/* Declare that stage `to` depends on stage `from` through memory the plan
+ * cannot see (from < to). Applies at ticks where both run.
+ * Errors: VFM_E_INVALID_ARG (index out of range, from >= to). */
+vfm_status vfm_plan_add_edge(vfm_plan* pl, int32_t from, int32_t to);
+
+/* Host-only query: the stages that stage `stage` waits for at tick `tick`
+ * (ascending), written to deps[0 .. min(*n, cap) - 1]; *n = their count, and
+ * -1 if the stage does not run at that tick. Errors: VFM_E_INVALID_ARG,
+ * VFM_E_UNBOUND (an expert stage whose buffers are not bound). */
+vfm_status vfm_plan_deps(vfm_plan* pl, int64_t tick, int32_t stage, int32_t* deps, int32_t cap, int32_t* n);
+
+/* Run tick `tick` (>= 0): enqueue every due stage, in add order, each on its
+ * own stream after the stages it depends on; `stream` then waits for all of
+ * them. Asynchronous; no allocation after the first run (graph-mode experts
+ * capture their graph on first use of a shape and pointer set). If a stage
+ * fails to enqueue, the stages already enqueued are still joined into
+ * `stream` and the stage's error is returned. Errors: VFM_E_INVALID_ARG,
+ * any error of the stages' own calls. */
+vfm_status vfm_plan_run(vfm_plan* pl, int64_t tick, void* stream);
+
+/* Synchronise the plan's streams and free them. NULL-safe. */
+vfm_status vfm_plan_destroy(vfm_plan* pl);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvfm.so")
 SOURCES = ["vfm_k_bf16.hip", "vfm_k_fp8.hip", "vfm_k_w4.hip", "vfm_k_i8.hip", "vfm_k_w4a8.hip", "vfm_k_cal.hip", "vfm_k_f32.hip", "vfm_prep.hip",
-           "vfm_prefix.hip", "vfm_launch.cpp", "vfm_runtime.cpp", "vfm_prefix_rt.cpp"]
+           "vfm_prefix.hip", "vfm_launch.cpp", "vfm_runtime.cpp", "vfm_prefix_rt.cpp", "vfm_plan.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

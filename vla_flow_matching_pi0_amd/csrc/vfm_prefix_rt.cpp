@@ -13,6 +13,7 @@
 #include "vfm.h"
 #include "vfm_params.h"
 #include "vfm_prefix.h"
+#include "vfm_stage_io.h"
 
 using namespace vfm;
 
@@ -130,6 +131,23 @@ int plan_split(int tiles, int K) {
 }
 
 }  // namespace
+
+namespace vfm {
+
+vfm_status prefix_stage_io(const vfm_prefix* p, const void* embeds, int B, int P, const void* prefix_k,
+                           const void* prefix_v, StageIO* io) {
+  if (!p || !io) return report(VFM_E_INVALID_ARG, "NULL argument");
+  if (B < 1 || B > p->maxB) return report(VFM_E_SHAPE, "batch %d outside [1, %d]", B, p->maxB);
+  if (P < 1 || P > p->maxP) return report(VFM_E_SHAPE, "prefix length %d outside [1, %d]", P, p->maxP);
+  const size_t kv = (size_t)p->L * B * P * p->Hkv * p->d * 2;
+  io->reads = {{embeds, (size_t)B * P * p->W * 2}};
+  io->writes = {{prefix_k, kv}, {prefix_v, kv}};
+  io->owner = p;
+  io->device_wide = false;
+  return VFM_OK;
+}
+
+}  // namespace vfm
 
 extern "C" {
 

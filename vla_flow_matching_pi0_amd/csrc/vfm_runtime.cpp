@@ -7,12 +7,14 @@
 // and Graph objects; component 7, graph capture with pointer-only inputs).
 #include "vfm.h"
 #include "vfm_params.h"
+#include "vfm_stage_io.h"
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <algorithm>
 #include <cstring>
 #include <map>
@@ -97,10 +99,19 @@ struct vfm_expert {
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
-  // graph cache (one entry): key = shape + pointers
-  hipGraphExec_t gexec = nullptr;
-  std::vector<uintptr_t> gkey;
+  // graph variants, most recently used first: key = shape + pointers
+  struct GraphEntry {
+    std::vector<uintptr_t> key;
+    hipGraphExec_t exec;
+  };
+  std::vector<GraphEntry> graphs;
+  int graph_cap = 8;
   hipStream_t cap_stream = nullptr;
+
+  void drop_graphs() {
+    for (GraphEntry& g : graphs) (void)hipGraphExecDestroy(g.exec);
+    graphs.clear();
+  }
 
   void* dalloc(size_t bytes) {
     void* p = nullptr;
@@ -326,7 +337,7 @@ ColMap ident_map(int N) {
 }
 
 void free_all(vfm_expert* x) {
-  if (x->gexec) (void)hipGraphExecDestroy(x->gexec);
+  x->drop_graphs();
   if (x->cap_stream) (void)hipStreamDestroy(x->cap_stream);
   if (x->flag_event) (void)hipEventDestroy(x->flag_event);
   if (x->host_flag) (void)hipHostFree(x->host_flag);
@@ -442,6 +453,24 @@ vfm_status report(vfm_status s, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return s;
+}
+
+vfm_status expert_stage_io(const vfm_expert* x, const float* noise, const float* state, const float* actions,
+                           StageIO* io) {
+  if (!x || !io) return report(VFM_E_INVALID_ARG, "NULL argument");
+  if (!x->prefix_k.bound || !x->prefix_v.bound) return report(VFM_E_UNBOUND, "prefix_k / prefix_v are not bound");
+  const size_t B = (size_t)x->prefix_k.shape[1], P = (size_t)x->prefix_k.shape[2];
+  const size_t kv = (size_t)x->L * B * P * x->Hkv * x->d * (x->act_bf16 ? 2 : 4);
+  const size_t xa = B * x->H * x->A * 4;
+  if (!noise && !x->noise.bound) return report(VFM_E_UNBOUND, "buffer 'noise' is not bound");
+  if (!actions && !x->actions.bound) return report(VFM_E_UNBOUND, "buffer 'actions' is not bound");
+  if (x->S > 0 && !state && !x->state.bound) return report(VFM_E_UNBOUND, "buffer 'state' is not bound");
+  io->reads = {{x->prefix_k.ptr, kv}, {x->prefix_v.ptr, kv}, {noise ? noise : x->noise.ptr, xa}};
+  if (x->S > 0) io->reads.push_back({state ? state : x->state.ptr, B * x->S * 4});
+  io->writes = {{actions ? actions : x->actions.ptr, xa}};
+  io->owner = x;
+  io->device_wide = x->mode == 0;
+  return VFM_OK;
 }
 }  // namespace vfm
 
@@ -838,6 +867,17 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     else return fail(VFM_E_INVALID_ARG, "persistent_launch must be 'cooperative' or 'plain'");
     return VFM_OK;
   }
+  if (k == "graph_cache") {
+    char* end = nullptr;
+    const long n = std::strtol(value, &end, 10);
+    if (end == value || *end || n < 1 || n > 64) return fail(VFM_E_INVALID_ARG, "graph_cache must be an integer in [1, 64]");
+    x->graph_cap = (int)n;
+    while ((int)x->graphs.size() > x->graph_cap) {
+      (void)hipGraphExecDestroy(x->graphs.back().exec);
+      x->graphs.pop_back();
+    }
+    return VFM_OK;
+  }
   if (k == "launch_mode") {
     if (v == "persistent") x->mode = 0;
     else if (v == "graph") x->mode = 1;
@@ -877,9 +917,10 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if ((st = fill_vp(x, p, B, P, noise, state, actions)) != VFM_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (x->rope_P != P) {
+    // The table (positions P .. P + T - 1) is rebuilt in place; graphs of
+    // other P read it at the same address and see it rebuilt before replay.
     HIPCHK(vfm::build_rope(x->rope, x->T, x->d, P, x->cfg.rope_base, s));
     x->rope_P = P;
-    if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
   }
   if (x->mode == 0) {
     HIPCHK(vfm::zero_words(x->bar, vfm::BAR_WORDS, s));
@@ -896,8 +937,14 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   // graph mode
   std::vector<uintptr_t> key = {(uintptr_t)B, (uintptr_t)P, (uintptr_t)noise, (uintptr_t)state, (uintptr_t)actions,
                                 (uintptr_t)p.prefix_k, (uintptr_t)p.prefix_v};
-  if (!x->gexec || key != x->gkey) {
-    if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
+  auto hit = std::find_if(x->graphs.begin(), x->graphs.end(), [&](const vfm_expert::GraphEntry& g) { return g.key == key; });
+  if (hit != x->graphs.end()) {
+    std::rotate(x->graphs.begin(), hit, hit + 1);
+  } else {
+    while ((int)x->graphs.size() >= x->graph_cap) {
+      (void)hipGraphExecDestroy(x->graphs.back().exec);
+      x->graphs.pop_back();
+    }
     if (!x->cap_stream) HIPCHK(hipStreamCreateWithFlags(&x->cap_stream, hipStreamNonBlocking));
     hipGraph_t g = nullptr;
     HIPCHK(hipStreamBeginCapture(x->cap_stream, hipStreamCaptureModeThreadLocal));
@@ -907,12 +954,13 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
       if (g) (void)hipGraphDestroy(g);
       return fail(VFM_E_HIP, "graph capture failed: %s", hipGetErrorString(e != hipSuccess ? e : e2));
     }
-    e = hipGraphInstantiate(&x->gexec, g, nullptr, nullptr, 0);
+    hipGraphExec_t ge = nullptr;
+    e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
     (void)hipGraphDestroy(g);
-    if (e != hipSuccess) { x->gexec = nullptr; return fail(VFM_E_HIP, "graph instantiate: %s", hipGetErrorString(e)); }
-    x->gkey = key;
+    if (e != hipSuccess) return fail(VFM_E_HIP, "graph instantiate: %s", hipGetErrorString(e));
+    x->graphs.insert(x->graphs.begin(), vfm_expert::GraphEntry{key, ge});
   }
-  HIPCHK(hipGraphLaunch(x->gexec, s));
+  HIPCHK(hipGraphLaunch(x->graphs.front().exec, s));
   return VFM_OK;
 }
 
@@ -1001,7 +1049,7 @@ vfm_status vfm_set_act_scales(vfm_expert* x, const float* scales, int32_t n) {
   HIPCHK(hipDeviceSynchronize());
   if (n > 0) HIPCHK(hipMemcpy(x->qs, q.data(), q.size() * 4, hipMemcpyHostToDevice));
   x->act_scale.assign(scales, scales + n);
-  if (x->gexec) { (void)hipGraphExecDestroy(x->gexec); x->gexec = nullptr; }
+  x->drop_graphs();
   return VFM_OK;
 }
 

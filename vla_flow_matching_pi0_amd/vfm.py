@@ -27,7 +27,8 @@ EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
            "vfm_expert_destroy", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
            "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
-           "vfm_prefix_destroy"]
+           "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
+           "vfm_plan_add_graph", "vfm_plan_add_edge", "vfm_plan_deps", "vfm_plan_run", "vfm_plan_destroy"]
 
 
 class VfmError(RuntimeError):
@@ -50,6 +51,10 @@ class VfmPrefixConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "num_layers", "width", "num_q_heads", "num_kv_heads", "head_dim", "mlp_dim",
         "max_prefix_len", "max_batch")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class VfmRange(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("bytes", ctypes.c_size_t)]
 
 
 class VfmTensor(ctypes.Structure):
@@ -97,6 +102,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(vp)]
     lib.vfm_prefix_run.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.vfm_prefix_destroy.argtypes = [vp]
+    lib.vfm_plan_create.argtypes = [ctypes.POINTER(vp)]
+    lib.vfm_plan_add_prefix.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, ctypes.POINTER(i32)]
+    lib.vfm_plan_add_denoise.argtypes = [vp, vp, vp, vp, vp, i32, i32, ctypes.POINTER(i32)]
+    lib.vfm_plan_add_graph.argtypes = [vp, vp, ctypes.POINTER(VfmRange), i32, ctypes.POINTER(VfmRange), i32, i32, i32,
+                                       ctypes.POINTER(i32)]
+    lib.vfm_plan_add_edge.argtypes = [vp, i32, i32]
+    lib.vfm_plan_deps.argtypes = [vp, ctypes.c_int64, i32, ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+    lib.vfm_plan_run.argtypes = [vp, ctypes.c_int64, vp]
+    lib.vfm_plan_destroy.argtypes = [vp]
     for n in EXPORTS[2:]:
         getattr(lib, n).restype = st
     if lib.vfm_abi_version() != ABI_VERSION:
@@ -300,6 +314,92 @@ class PrefixProducer:
         if getattr(self, "_h", None):
             h, self._h = self._h, None
             _check(_lib.vfm_prefix_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor, an int address, or None (NULL)."""
+    if t is None:
+        return None
+    return t if isinstance(t, int) else t.data_ptr()
+
+
+def _ranges(items):
+    """(tensor | (address, bytes)) list -> C array of vfm_range."""
+    arr = (VfmRange * max(1, len(items)))()
+    for i, it in enumerate(items):
+        if isinstance(it, tuple):
+            arr[i].ptr, arr[i].bytes = int(it[0]), int(it[1])
+        else:
+            arr[i].ptr, arr[i].bytes = it.data_ptr(), it.numel() * it.element_size()
+    return arr
+
+
+class Plan:
+    """Stages (prefix passes, denoise calls, adopted graphs) with update
+    rates; dependencies are derived from the buffers each stage reads and
+    writes. run(tick) enqueues the due stages on their own streams, forked
+    from and joined into the caller's stream. Keeps references to everything
+    its stages point at."""
+
+    def __init__(self):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.vfm_plan_create(ctypes.byref(h)))
+        self._h = h
+        self._keep = []
+
+    def add_prefix(self, producer: PrefixProducer, embeds, prefix_k, prefix_v, every: int = 1,
+                   offset: int = 0) -> int:
+        sid = ctypes.c_int32()
+        _check(_lib.vfm_plan_add_prefix(self._h, producer._h, embeds.data_ptr(), int(embeds.shape[0]),
+                                        int(embeds.shape[1]), prefix_k.data_ptr(), prefix_v.data_ptr(), every, offset,
+                                        ctypes.byref(sid)))
+        self._keep += [producer, embeds, prefix_k, prefix_v]
+        return sid.value
+
+    def add_denoise(self, expert: Expert, noise=None, state=None, actions=None, every: int = 1,
+                    offset: int = 0) -> int:
+        sid = ctypes.c_int32()
+        _check(_lib.vfm_plan_add_denoise(self._h, expert._h, _ptr(noise), _ptr(state), _ptr(actions), every, offset,
+                                         ctypes.byref(sid)))
+        self._keep += [expert, noise, state, actions]
+        return sid.value
+
+    def add_graph(self, graph_exec, reads=(), writes=(), every: int = 1, offset: int = 0) -> int:
+        """graph_exec: an int hipGraphExec_t, or a torch.cuda.CUDAGraph
+        (its executable graph is adopted; the CUDAGraph must stay alive)."""
+        h = graph_exec if isinstance(graph_exec, int) else graph_exec.raw_cuda_graph_exec()
+        r, w = list(reads), list(writes)
+        sid = ctypes.c_int32()
+        _check(_lib.vfm_plan_add_graph(self._h, h, _ranges(r), len(r), _ranges(w), len(w), every, offset,
+                                       ctypes.byref(sid)))
+        self._keep += [graph_exec, *r, *w]
+        return sid.value
+
+    def add_edge(self, src: int, dst: int) -> None:
+        _check(_lib.vfm_plan_add_edge(self._h, src, dst))
+
+    def deps(self, tick: int, stage: int):
+        """Stages that `stage` waits for at `tick`, or None if it does not run then."""
+        buf = (ctypes.c_int32 * 256)()
+        n = ctypes.c_int32()
+        _check(_lib.vfm_plan_deps(self._h, tick, stage, buf, 256, ctypes.byref(n)))
+        return None if n.value < 0 else [buf[i] for i in range(n.value)]
+
+    def run(self, tick: int, stream=None) -> None:
+        _check(_lib.vfm_plan_run(self._h, tick, _stream_ptr(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            _check(_lib.vfm_plan_destroy(h))
+            self._keep = []
 
     def __del__(self):
         try:
