@@ -159,8 +159,40 @@ def bench_prefix(name: str, reps: int, stream, expert=None, expert_bufs=None):
         torch.cuda.synchronize()
         expert.check(stream)
         out["chain_ms"] = round(ev[0].elapsed_time(ev[1]) / reps, 4)
+        out["plan"] = bench_plan(pre, emb, pk, pv, expert, stream, ticks=max(5, reps // 5 * 5))
     pre.close()
     return out
+
+
+def bench_plan(pre, emb, pk, pv, expert, stream, ticks: int, every: int = 5):
+    """A control loop as a plan: the prefix stage refreshes the K/V every
+    `every` ticks, the expert denoises on every tick (selective refresh).
+    Mean ms per tick over `ticks` ticks, against the same sequence of calls
+    issued directly on one stream."""
+    import torch
+    from vla_flow_matching_pi0_amd import vfm
+    plan = vfm.Plan()
+    plan.add_prefix(pre, emb, pk, pv, every=every)
+    plan.add_denoise(expert)
+    for t in range(every):
+        plan.run(t, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    for t in range(ticks):
+        plan.run(t, stream)
+    ev[1].record(stream)
+    ev[2].record(stream)
+    for t in range(ticks):
+        if t % every == 0:
+            pre.run(emb, pk, pv, stream)
+        expert.denoise(stream=stream)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    expert.check(stream)
+    plan.close()
+    return {"prefix_every": every, "ticks": ticks, "ms_per_tick": round(ev[0].elapsed_time(ev[1]) / ticks, 4),
+            "direct_ms_per_tick": round(ev[2].elapsed_time(ev[3]) / ticks, 4)}
 
 
 def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: float = 10.0):
