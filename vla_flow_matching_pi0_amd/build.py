@@ -13,8 +13,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvfm.so")
-SOURCES = ["vfm_k_bf16.hip", "vfm_k_fp8.hip", "vfm_k_w4.hip", "vfm_k_i8.hip", "vfm_k_w4a8.hip", "vfm_k_cal.hip", "vfm_k_f32.hip", "vfm_prep.hip",
+SOURCES = ["vfm_k_bf16.hip", "vfm_k_attn.hip", "vfm_k_fp8.hip", "vfm_k_w4.hip", "vfm_k_i8.hip", "vfm_k_w4a8.hip", "vfm_k_cal.hip", "vfm_k_f32.hip", "vfm_prep.hip",
            "vfm_prefix.hip", "vfm_launch.cpp", "vfm_runtime.cpp", "vfm_prefix_rt.cpp", "vfm_plan.cpp"]
+
+# per-file additions: the large-batch attention keeps its MFMA accumulators
+# in VGPRs (it rescales them with vector ALU operations between MFMAs)
+EXTRA_FLAGS = {"vfm_k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -41,7 +45,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [hipcc(), *HIPCC_FLAGS, *inc, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *inc, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

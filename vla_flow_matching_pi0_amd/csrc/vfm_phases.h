@@ -30,6 +30,8 @@
 // partial sums the following row-parallel norm phase reduces, is ours: it
 // lets every GEMM phase use all compute units without atomics.
 #pragma once
+#include <type_traits>
+
 #include "vfm_device.h"
 #include "vfm_params.h"
 
@@ -1272,6 +1274,277 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
   }
 }
 
+// ============================================================ large-batch attention
+// With the large-M GEMMs (graph / eager launch, bf16, M >= 256 rows), the
+// attention of a batch runs in one pass instead of key splits plus a combine
+// phase: one workgroup per (sample, query head) takes the head's H queries
+// (wave w: rows 16w .. 16w + 15) over all P + H keys with an online softmax
+// (the flash-attention recurrence, R8's result) and writes the o
+// projection's input itself. The chunk's own H keys and values are staged
+// into LDS once; the prefix streams through two LDS stages of 32 keys, the
+// next tile's global loads in flight during the current tile's MFMAs. K is
+// kept in natural dim order, [key][D]; V as [key / 4][D][4 keys], so that a
+// lane's operand of the P.V product (4 keys of one dim, twice) is two 8-byte
+// LDS reads. The workgroups of one sample share an XCD (blockIdx % 8), so
+// its keys and values come from HBM once and from that XCD's L2 for the
+// other heads.
+constexpr int AM_KEYS = 32;
+constexpr int AM_THREADS = 256;
+constexpr int AM_CHUNK = 64;   // chunk keys staged once (H <= 64)
+
+template <int D>
+struct AttnMLds {
+  static constexpr int K_LD = D + 8;                  // elements per K row (16-byte pad)
+  static constexpr int V_LD = D * 8 + 128;            // bytes per 4-key group: [D][4] bf16, shifts, pad
+  static constexpr int K_TILE = AM_KEYS * K_LD * 2;
+  static constexpr int STAGE = K_TILE + (AM_KEYS / 4) * V_LD;
+  static constexpr int CK = 2 * STAGE;                // chunk K: [AM_CHUNK][K_LD]
+  static constexpr int CV = CK + AM_CHUNK * K_LD * 2; // chunk V: [AM_CHUNK / 4][V_LD]
+  static constexpr int TOTAL = CV + (AM_CHUNK / 4) * V_LD;
+  static_assert((D - 1) * 8 + ((D - 1) / 32) * 8 + 8 <= V_LD, "V key group row too short for its shifts");
+};
+
+// Byte offset of dim e in a V key group ([D][4 keys] bf16): every 32 dims
+// shift by 8 bytes, so that the 32 lanes storing dims 8c .. 8c + 7 of one
+// group (c = 0 .. 31) hit distinct bank pairs instead of four.
+__device__ __forceinline__ int am_v_off(int e) { return e * 8 + (e >> 5) * 8; }
+
+// Transpose 4 keys x 8 dims (rows of natural-order bf16) into LDS as
+// [key group][dim][4 keys]: dims 8c .. 8c + 7 of one key group.
+__device__ __forceinline__ void am_store_v(uint8_t* grp, int c, const u32x4 (&row)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t w0 = row[0][m], w1 = row[1][m], w2 = row[2][m], w3 = row[3][m];
+    const u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+    const u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+    uint8_t* dst = grp + am_v_off(8 * c + 2 * m);   // dims 8c + 2m and 8c + 2m + 1 share the shift
+    *reinterpret_cast<u32x2*>(dst) = lo;
+    *reinterpret_cast<u32x2*>(dst + 8) = hi;
+  }
+}
+
+// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave: the two
+// lane-swap instructions of gfx950 pair rows 0/1 and 2/3 of 16 lanes, then
+// halves 0/1 of 32 lanes, without a round trip through LDS.
+__device__ __forceinline__ float am_max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int layer) {
+  static_assert(sizeof(T) == 2, "the large-batch attention runs bf16 operands");
+  using L = AttnMLds<D>;
+  constexpr int KCH = D / 8;                          // 16-byte chunks per key row
+  constexpr int KL = AM_KEYS * KCH / AM_THREADS;      // prefix K chunks per thread per tile
+  constexpr int VI = (D + AM_THREADS - 1) / AM_THREADS;   // (4 keys x 8 dims) V items per thread per tile
+  static_assert(KL >= 1 && AM_KEYS * KCH % AM_THREADS == 0, "K tile must split evenly over the threads");
+  uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+  // sample b on XCD b % 8: blockIdx = 8 * (Hq * (b / 8) + head) + b % 8
+  const int xcd = (int)(blockIdx.x & 7), loc = (int)(blockIdx.x >> 3);
+  const int jh = loc % p.Hq, b = (loc / p.Hq) * 8 + xcd;
+  if (b >= p.B) return;
+  const int H = p.H, P = p.P;
+  const int kvh = jh / (p.Hq / p.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const size_t layer_elems = (size_t)p.B * P * p.Hkv * D;
+  const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
+  const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
+  uint8_t* sl = slab(p, step, layer);
+  const auto qrs = rsrc(sl + p.off_q), kgr = rsrc(sl + p.off_k), vgr = rsrc(sl + p.off_v);
+  const size_t kvb = (size_t)b * p.Hkv + kvh;
+  const int qrow = w * 16 + c16;
+  const bool active = w * 16 < H;
+
+  // -- prologue: query fragments, the chunk's keys and values into LDS
+  u32x4 qf[D / 32];
+  {
+    const size_t hb = (size_t)b * p.Hq + jh;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      qf[kb] = ld16_if(qrs, (uint32_t)(qk_off(D, hb, qrow < H ? qrow : 0, kb * 32 + 8 * g) * 2), qrow < H);
+    // rows i fastest, so a wave reads whole 32-byte rows of the tiles
+    constexpr int CKL = AM_CHUNK * KCH / AM_THREADS;
+#pragma unroll
+    for (int j = 0; j < CKL; ++j) {
+      const int idx = tid + j * AM_THREADS, i = idx % AM_CHUNK, c = idx / AM_CHUNK;
+      const u32x4 v = ld16_if(kgr, (uint32_t)(qk_off(D, kvb, i < H ? i : 0, 8 * c) * 2), i < H);
+      *reinterpret_cast<u32x4*>(lds + L::CK + (i * L::K_LD + 8 * c) * 2) = v;
+    }
+    constexpr int CVI = (AM_CHUNK / 4) * KCH / AM_THREADS;
+#pragma unroll
+    for (int j = 0; j < (CVI > 0 ? CVI : 1); ++j) {
+      const int idx = tid + j * AM_THREADS, kq = idx % (AM_CHUNK / 4), c = idx / (AM_CHUNK / 4);
+      if (idx >= (AM_CHUNK / 4) * KCH) break;
+      u32x4 row[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * kq + r;
+        row[r] = ld16_if(vgr, (uint32_t)(v_off(D, kvb, i < H ? i : 0, 8 * c) * 2), i < H);
+      }
+      am_store_v(lds + L::CV + kq * L::V_LD, c, row);
+    }
+    // complete every prologue load here: left in flight into the loop, the
+    // in-order load counter would make each tile's MFMAs wait for the next
+    // tile's loads as well
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // -- prefix tiles: per-thread byte offsets of tile 0, plus t * tile stride
+  const uint32_t tstride = (uint32_t)(AM_KEYS * p.Hkv * D * 2);
+  uint32_t kofs[KL], vofs[VI][4];
+  int kkey[KL], vkey[VI];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    const int idx = tid + j * AM_THREADS;
+    kkey[j] = idx / KCH;
+    kofs[j] = (uint32_t)(((((size_t)b * P + kkey[j]) * p.Hkv + kvh) * D + 8 * (idx % KCH)) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int idx = tid + j * AM_THREADS, kq = idx / KCH, c = idx % KCH;
+    vkey[j] = idx < D ? 4 * kq : 1 << 30;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vofs[j][r] = (uint32_t)(((((size_t)b * P + 4 * kq + r) * p.Hkv + kvh) * D + 8 * c) * 2);
+  }
+  // tile t + 1's loads are in flight during tile t's MFMAs
+  u32x4 kr[KL], vr[VI][4];
+  auto gload = [&](int t) {
+    const int s0 = t * AM_KEYS;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) kr[j] = ld16_if(pkr, kofs[j] + (uint32_t)t * tstride, s0 + kkey[j] < P);
+#pragma unroll
+    for (int j = 0; j < VI; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vr[j][r] = ld16_if(pvr, vofs[j][r] + (uint32_t)t * tstride, s0 + vkey[j] + r < P);
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* kb = lds + buf * L::STAGE;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+      const int idx = tid + j * AM_THREADS;
+      *reinterpret_cast<u32x4*>(kb + ((idx / KCH) * L::K_LD + (idx % KCH) * 8) * 2) = kr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int idx = tid + j * AM_THREADS;
+      if (idx < D) am_store_v(kb + L::K_TILE + (idx / KCH) * L::V_LD, idx % KCH, vr[j]);
+    }
+  };
+
+  floatx4 O[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) O[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
+  // One 32-key tile: keys s0 + kk (kk = 0..31) valid while below `limit`.
+  auto tile = [&](const T* Ks, const uint8_t* Vq, int s0, int limit) {
+    floatx4 slo = {0.f, 0.f, 0.f, 0.f}, shi = {0.f, 0.f, 0.f, 0.f};
+    constexpr int KH = D / 32 < 4 ? D / 32 : 4;   // K fragments read ahead per batch
+#pragma unroll
+    for (int k0 = 0; k0 < D / 32; k0 += KH) {
+      u32x4 alo[KH], ahi[KH];
+#pragma unroll
+      for (int kb = 0; kb < KH; ++kb) {
+        alo[kb] = *reinterpret_cast<const u32x4*>(Ks + c16 * L::K_LD + (k0 + kb) * 32 + 8 * g);
+        ahi[kb] = *reinterpret_cast<const u32x4*>(Ks + (16 + c16) * L::K_LD + (k0 + kb) * 32 + 8 * g);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KH; ++kb) {
+        slo = MT<T>::mma(alo[kb], qf[k0 + kb], slo);
+        shi = MT<T>::mma(ahi[kb], qf[k0 + kb], shi);
+      }
+    }
+    // lane (c16, g): keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of query c16
+    float pr[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = (s0 + 4 * g + r < limit) ? slo[r] * scale : -INFINITY;
+      pr[4 + r] = (s0 + 16 + 4 * g + r < limit) ? shi[r] * scale : -INFINITY;
+    }
+    float cmax = pr[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
+    cmax = am_max4(cmax);
+    // Lazy rescaling: the reference point m_run of the exponentials moves
+    // only when a row's maximum exceeds it by more than 8 (log2 units), so
+    // every weight stays <= 2^8 and the running sums are rescaled on few
+    // tiles; O / l is the same for any reference point.
+    const bool grow = cmax > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_set = grow ? cmax : m_run;
+      // 0 on the first tile (m_run = -inf), 1 for rows that did not grow
+      const float alpha = m_set == m_run ? 1.f : fast_exp2(m_run - m_set);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) O[dt] *= alpha;
+      m_run = m_set;
+    }
+    // (before any valid key m_run is -inf and every weight is 0)
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // l_run is this lane's share (its 8 keys per tile); the four lanes of a
+    // row are summed once, after the last tile
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_use); l_run += pr[e]; }
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = (bf16)pr[e];
+    const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(Vq + g * L::V_LD + am_v_off(dt * 16 + c16));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(Vq + (4 + g) * L::V_LD + am_v_off(dt * 16 + c16));
+      O[dt] = MT<T>::mma(u32x4{lo.x, lo.y, hi.x, hi.y}, pbu, O[dt]);
+    }
+  };
+
+  const int ptiles = (P + AM_KEYS - 1) / AM_KEYS;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int t = 0; t < ptiles; ++t) {
+    gload(t + 1);   // past the last tile: predicated off, fetches nothing
+    if (active) {
+      const uint8_t* st = lds + (t & 1) * L::STAGE;
+      tile(reinterpret_cast<const T*>(st), st + L::K_TILE, t * AM_KEYS, P);
+    }
+    if (t + 1 < ptiles) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+  if (active) {
+    // the chunk's keys: P + i for i < H (pi0: the state token, query row 0,
+    // sees only the first of them, its own)
+    const int lim = (p.pi0 && qrow == 0) ? P + 1 : P + H;
+    for (int j0 = 0; j0 < H; j0 += AM_KEYS)
+      tile(reinterpret_cast<const T*>(lds + L::CK) + j0 * L::K_LD, lds + L::CV + (j0 / 4) * L::V_LD, P + j0, lim);
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (qrow < H) {
+      const float inv = 1.f / l;
+      uint8_t* attn = sl + p.off_attn;
+      const int gm = b * H + qrow;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        store_gemm_in4<T, false>(p, attn, gm, jh * D + dt * 16 + 4 * g, O[dt] * inv, 1.0f);
+    }
+  }
+}
+
+// Instantiated in vfm_k_attn.hip only (built with MFMA accumulators in
+// VGPRs, which keeps the running output out of AGPR copies around its
+// rescaling); other translation units refer to those instantiations.
+#ifndef VFM_ATTN_M_INSTANTIATE
+extern template __global__ void k_attn_m<bf16, 64>(VP, int, int);
+extern template __global__ void k_attn_m<bf16, 128>(VP, int, int);
+extern template __global__ void k_attn_m<bf16, 256>(VP, int, int);
+#endif
+
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
 template <typename T, int D, int WF>
@@ -1351,6 +1624,7 @@ __host__ const void* phase_kernel(int ph, bool bigm = false) {
   if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
     if (bigm) {
       switch (ph) {
+        case PH_ATTN: return (const void*)&k_attn_m<T, D>;
         case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV>;
         case PH_O: return (const void*)&k_gemm_m<T, G_O>;
         case PH_GU: return (const void*)&k_gemm_m<T, G_GU>;
@@ -1392,7 +1666,18 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
   }
   void* args[] = {const_cast<VP*>(&p), &k, &l};
   const bool gemm = phase == PH_QKV || phase == PH_O || phase == PH_GU || phase == PH_DOWN || phase == PH_TMLP;
-  const bool bigm = p.bigm && gemm;
+  const bool bigm = p.bigm && (gemm || phase == PH_ATTN);
+  if (bigm && phase == PH_ATTN) {
+    if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
+      // the single-pass attention keeps every query row of a head in one
+      // workgroup (H <= 64) and needs its two LDS stages
+      if (p.H > AM_CHUNK || D % 32) return hipErrorInvalidValue;
+      return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, true), dim3(grid), dim3(AM_THREADS), args,
+                             (size_t)AttnMLds<D>::TOTAL, st);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, bigm), dim3(grid), dim3(bigm ? GM_THREADS : NTH), args,
                          lds, st);
 }
@@ -1406,8 +1691,10 @@ hipError_t set_lds_limit(int bytes) {
   for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph) {
     e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     const void* big = phase_kernel<T, D, WF, CAL>(ph, true);
-    if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph))
-      e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > GM_LDS ? bytes : GM_LDS);
+    if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph)) {
+      const int need = ph == PH_ATTN ? AttnMLds<D>::TOTAL : GM_LDS;
+      e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > need ? bytes : need);
+    }
   }
   return e;
 }

@@ -387,6 +387,8 @@ int phase_grid(const VP& p, int phase) {
       case vfm::PH_GU: tiles = (long)2 * p.F / 128 * mt128 * p.gp_s[2]; break;
       case vfm::PH_DOWN: tiles = (long)p.W / 128 * mt128 * p.gp_s[3]; break;
       case vfm::PH_TMLP: tiles = (long)p.W / 128 * mt128 * p.gp_s[4]; break;
+      // single-pass attention: one workgroup per (sample, head), samples in groups of 8 (one per XCD)
+      case vfm::PH_ATTN: tiles = (long)cdiv(p.B, 8) * 8 * p.Hq; break;
       default: break;
     }
     if (tiles > 0) return (int)((tiles + 7) / 8 * 8);
@@ -417,8 +419,10 @@ hipError_t enqueue_phases(vfm_expert* x, const VP& p, int kset, hipStream_t st) 
     for (int l = 0; l < p.L; ++l) {
       if (l > 0 && (e = run(vfm::PH_RN_ATTN, k, l)) != hipSuccess) return e;
       const int seq[] = {vfm::PH_QKV, vfm::PH_ATTN, vfm::PH_COMBINE, vfm::PH_O, vfm::PH_RN_MLP, vfm::PH_GU, vfm::PH_DOWN};
-      for (int ph : seq)
+      for (int ph : seq) {
+        if (ph == vfm::PH_COMBINE && p.bigm) continue;   // the single-pass attention writes the o input itself
         if ((e = run(ph, k, l)) != hipSuccess) return e;
+      }
     }
     if ((e = run(vfm::PH_BOUNDARY, k + 1, 0)) != hipSuccess) return e;
   }
