@@ -902,6 +902,18 @@ __device__ __forceinline__ void attn_split(const VP& p, int c, int& s0, int& s1)
   }
 }
 
+// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave: the two
+// lane-swap instructions of gfx950 pair rows 0/1 and 2/3 of 16 lanes, then
+// halves 0/1 of 32 lanes, without a round trip through LDS.
+__device__ __forceinline__ float am_max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
+
 template <typename T, int D>
 __device__ __forceinline__ bool attn_prefix_unit(const VP& p, int u, int& b, int& kvh, int& s0, int& s1) {
   const int KS = p.KS;
@@ -1027,16 +1039,13 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
       float cmax = pr[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) cmax = fmaxf(cmax, pr[e]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = am_max4(cmax);
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
+      // l_run: this lane's share of the row sum, reduced after the last chunk
+      l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); psum += pr[e]; }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
+      for (int e = 0; e < 8; ++e) { pr[e] = fast_exp2(pr[e] - m_new); l_run += pr[e]; }
       m_run = m_new;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
@@ -1064,6 +1073,8 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
         }
       }
     }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
     if (qrow < H) {
       const size_t base = ((size_t)(b * p.Hq + jh) * KS + c) * 64 + qrow;
 #pragma unroll
@@ -1321,18 +1332,6 @@ __device__ __forceinline__ void am_store_v(uint8_t* grp, int c, const u32x4 (&ro
     *reinterpret_cast<u32x2*>(dst) = lo;
     *reinterpret_cast<u32x2*>(dst + 8) = hi;
   }
-}
-
-// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave: the two
-// lane-swap instructions of gfx950 pair rows 0/1 and 2/3 of 16 lanes, then
-// halves 0/1 of 32 lanes, without a round trip through LDS.
-__device__ __forceinline__ float am_max4(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
 }
 
 template <typename T, int D>
