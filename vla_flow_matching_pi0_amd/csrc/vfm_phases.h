@@ -902,18 +902,6 @@ __device__ __forceinline__ void attn_split(const VP& p, int c, int& s0, int& s1)
   }
 }
 
-// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave: the two
-// lane-swap instructions of gfx950 pair rows 0/1 and 2/3 of 16 lanes, then
-// halves 0/1 of 32 lanes, without a round trip through LDS.
-__device__ __forceinline__ float am_max4(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
-}
-
 template <typename T, int D>
 __device__ __forceinline__ bool attn_prefix_unit(const VP& p, int u, int& b, int& kvh, int& s0, int& s1) {
   const int KS = p.KS;

@@ -17,7 +17,7 @@ namespace pfx {
 constexpr int TM = 128;   // tokens per GEMM tile
 constexpr int TN = 128;   // output columns per GEMM tile
 constexpr int TK = 64;    // K per pipeline stage
-constexpr int AQ = 64;    // queries per attention workgroup (4 waves x 16)
+constexpr int AQ = 32;    // queries per attention workgroup (2 waves x 16)
 constexpr int AK = 32;    // keys per attention tile
 constexpr int MAX_SPLIT = 8;
 

@@ -150,10 +150,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
 // where the 32 keys of the MFMA's k index are ordered (4g..4g+3, 16+4g..16+4g+3)
 // on both operands, so P^T comes straight from the S^T registers.
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a) {
+__global__ __launch_bounds__(AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
+  constexpr int NT = AQ / 16 * 64;     // one wave per 16 queries
   constexpr int KROW = 2 * D + 16;     // bytes per K row in LDS
   constexpr int VROW = 2 * AK + 16;    // bytes per V^T row in LDS
-  constexpr int CPT = D / 64;          // 16-byte chunks per thread per operand tile
+  constexpr int CPT = AK * D / 8 / NT; // 16-byte chunks per thread per operand tile
+  static_assert(AK * D / 8 == D * AK / 8 && AK * D / 8 % NT == 0, "tiles must split evenly over the threads");
   __shared__ __align__(16) uint8_t sk[AK * KROW];
   __shared__ __align__(16) uint8_t sv[D * VROW];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a) {
   auto fetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int key = c / (D / 8), part = c % (D / 8);
       const int kk = kt * AK + key;
       pkk[i] = ld16_if(rk, (uint32_t)((((size_t)b * P + kk) * a.Hkv + kvh) * D + part * 8) * 2, kk < P);
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       *reinterpret_cast<u32x4*>(sk + (c / (D / 8)) * KROW + (c % (D / 8)) * 16) = pkk[i];
       *reinterpret_cast<u32x4*>(sv + (c >> 2) * VROW + (c & 3) * 16) = pvv[i];
     }
@@ -219,23 +221,29 @@ __global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a) {
         s[h16][r] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    float sum = 0.f;
+    mx = am_max4(mx);
+    // Lazy rescaling: the reference point m moves only when a row's maximum
+    // exceeds it by more than 8 (log2 units), so every weight stays <= 2^8
+    // and the output is rescaled on few tiles (O / l does not depend on m).
+    // l is this lane's share of the row sum, reduced after the last tile.
+    const bool grow = mx > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mset = grow ? mx : m;
+      const float alpha = mset == m ? 1.f : fast_exp2(m - mset);   // 0 on the first tile (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
+      m = mset;
+    }
+    const float muse = m == -INFINITY ? 0.f : m;
 #pragma unroll
     for (int h16 = 0; h16 < 2; ++h16)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(s[h16][r] - mn);
+        const float p = fast_exp2(s[h16][r] - muse);
         s[h16][r] = p;
-        sum += p;
+        l += p;
       }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    l = l * alpha + sum;
-    m = mn;
     u32x4 pb;
     pb[0] = bf16_bits(s[0][0]) | (bf16_bits(s[0][1]) << 16);
     pb[1] = bf16_bits(s[0][2]) | (bf16_bits(s[0][3]) << 16);
@@ -248,9 +256,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(const AttnArgs a) {
       const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 32 + 8 * g);
       u32x4 vf;
       vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = hi[0]; vf[3] = hi[1];
-      o[db] = MT<bf16>::mma(vf, pb, o[db] * alpha);
+      o[db] = MT<bf16>::mma(vf, pb, o[db]);
     }
   }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
   if (!qok) return;
   const float inv = 1.0f / l;
   const int token = b * P + qi, K = a.Hq * D;
@@ -354,9 +364,9 @@ hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st) {
 hipError_t attention(int d, const AttnArgs& a, int B, hipStream_t st) {
   const dim3 grid((a.P + AQ - 1) / AQ, a.Hq, B);
   switch (d) {
-    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(k_attn<256>, grid, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(k_attn<256>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
