@@ -164,10 +164,14 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
                        void* stream);
 
 /* Options (string key/value), host-only:
- *   "launch_mode": "persistent" (default: one cooperative launch per
- *       denoise with device-wide phase barriers), "graph" (one kernel per
- *       phase, captured once into a hipGraph and replayed) or "eager" (one
- *       kernel per phase, launched directly).
+ *   "launch_mode": "auto" (default), "persistent", "graph" or "eager".
+ *       "persistent": one cooperative launch per denoise with device-wide
+ *       phase barriers; "graph": one kernel per phase, captured into a
+ *       hipGraph per shape and pointer set and replayed; "eager": the same
+ *       kernels launched directly. With bf16 weights and B x T >= 256 rows
+ *       the graph and eager modes run large-batch kernels (128 x 128 GEMM
+ *       tiles, single-pass attention). "auto" chooses, per call, graph launch
+ *       where those apply and the persistent kernel otherwise.
  *   "persistent_launch": "cooperative" (default) or "plain": how the
  *       persistent kernel is launched. "plain" is an ordinary launch of the
  *       same grid (one workgroup per compute unit, from the occupancy query);

@@ -257,8 +257,24 @@ def test_large_m_gemm_matches_oracle(variant, batch, horizon):
     run = P0.denoise_pi0 if variant == "pi0" else O.denoise
     ref = run(params, noise, state, pk, pv, cfg)
     print(f"case large-M {variant} B={batch} H={horizon}", flush=True)
-    for mode in ("graph", "eager", "persistent"):
-        got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
+    outs = {}
+    for mode in ("graph", "eager", "persistent", "auto"):
+        got = outs[mode] = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
         err = gu.rel_l2(got, ref)
         print(f"{mode}: rel_l2={err:.3e}")
         assert err <= 2e-2, mode
+    # the default launch mode takes the large-batch kernels here
+    np.testing.assert_array_equal(outs["auto"], outs["graph"])
+
+
+def test_auto_launch_mode_keeps_the_persistent_kernel_for_few_rows():
+    """Below 256 rows (and for fp32 weights at any size) the default launch
+    mode is the persistent kernel: bitwise the same actions."""
+    gu = _gu()
+    for name, batch in (("tiny_fp32", 2), ("tiny_fp32", 40)):
+        cfg = CONFIGS[name].replace(weight_precision="bf16" if batch == 2 else "fp32", batch=batch, seed=70 + batch)
+        params, pk, pv, noise, state = make_inputs(cfg)
+        print(f"case auto launch {name} B={batch} {cfg.weight_precision}", flush=True)
+        a = gu.run_gpu(cfg, params, pk, pv, noise, state, "auto")
+        b = gu.run_gpu(cfg, params, pk, pv, noise, state, "persistent")
+        np.testing.assert_array_equal(a, b)

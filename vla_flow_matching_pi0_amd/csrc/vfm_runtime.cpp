@@ -95,7 +95,7 @@ struct vfm_expert {
   hipEvent_t flag_event = nullptr;
   bool flag_pending = false;
   BoundBuf prefix_k, prefix_v, noise, state, actions;
-  int mode = 0;                    // 0 persistent, 1 graph, 2 eager
+  int mode = 3;                    // 0 persistent, 1 graph, 2 eager, 3 auto (see launch_mode_of)
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
@@ -126,6 +126,15 @@ namespace {
 
 // GEMM inputs are e4m3 with calibrated activation scales (FP8 and W4A8).
 bool fp8_act(const vfm_expert* x) { return x->wprec == VFM_W_FP8 || x->wprec == VFM_W_W4A8; }
+
+// Launch mode of a call with M = B x T rows. "auto" takes graph launch where
+// the large-batch kernels apply (bf16 weights, M >= 256 rows: large-M GEMM
+// tiles and single-pass attention), else the persistent kernel, which is the
+// faster one while the GEMMs are skinny.
+int launch_mode_of(const vfm_expert* x, int M) {
+  if (x->mode != 3) return x->mode;
+  return (x->kset == vfm::KS_BF16 && M >= 256) ? 1 : 0;
+}
 
 // Host decoders of the packed formats (export only).
 float e4m3_value(uint8_t c) {
@@ -473,7 +482,7 @@ vfm_status expert_stage_io(const vfm_expert* x, const float* noise, const float*
   if (x->S > 0) io->reads.push_back({state ? state : x->state.ptr, B * x->S * 4});
   io->writes = {{actions ? actions : x->actions.ptr, xa}};
   io->owner = x;
-  io->device_wide = x->mode == 0;
+  io->device_wide = launch_mode_of(x, (int)B * x->T) == 0;
   return VFM_OK;
 }
 }  // namespace vfm
@@ -499,7 +508,8 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   p.s_emb = x->s_emb; p.h = x->h; p.part_o = x->part_o; p.part_d = x->part_d; p.opart = x->opart; p.ml = x->ml;
   p.ring = x->ring; p.slab = x->slab; p.off_xna = x->off_xna; p.off_q = x->off_q; p.off_k = x->off_k; p.off_v = x->off_v;
   p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
-  p.trace = x->mode == 0 ? x->trace : nullptr;
+  const int mode = launch_mode_of(x, B * x->T);
+  p.trace = mode == 0 ? x->trace : nullptr;
 
   {
     int nwg = x->coop_grid;
@@ -514,7 +524,7 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
     for (int i = 0; i < 5; ++i) plan_gemm(p.M, Ns[i], Ks[i], KB, nwg, i != 0 && i != 2, &p.gp_nt[i], &p.gp_s[i]);
     // many rows in the per-phase launch modes: 128 x 128 tiles of the large-M GEMM kernel, and K splits of
     // the linear GEMMs until there are 256 tiles, each split a whole number of 64-K stages
-    p.bigm = x->mode != 0 && x->kset == vfm::KS_BF16 && p.M >= 256;
+    p.bigm = mode != 0 && x->kset == vfm::KS_BF16 && p.M >= 256;
     if (p.bigm) {
       const int mt = (p.M + 127) / 128;
       for (int i = 0; i < 5; ++i) {
@@ -886,6 +896,7 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     if (v == "persistent") x->mode = 0;
     else if (v == "graph") x->mode = 1;
     else if (v == "eager") x->mode = 2;
+    else if (v == "auto") x->mode = 3;
     else return fail(VFM_E_INVALID_ARG, "launch_mode '%s' unknown", value);
     return VFM_OK;
   }
@@ -926,7 +937,8 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     HIPCHK(vfm::build_rope(x->rope, x->T, x->d, P, x->cfg.rope_base, s));
     x->rope_P = P;
   }
-  if (x->mode == 0) {
+  const int mode = launch_mode_of(x, B * x->T);
+  if (mode == 0) {
     HIPCHK(vfm::zero_words(x->bar, vfm::BAR_WORDS, s));
     HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
@@ -934,7 +946,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     x->flag_pending = true;
     return VFM_OK;
   }
-  if (x->mode == 2) {
+  if (mode == 2) {
     HIPCHK(enqueue_phases(x, p, x->kset, s));
     return VFM_OK;
   }
