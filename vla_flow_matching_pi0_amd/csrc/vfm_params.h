@@ -26,6 +26,7 @@ struct VP {
   int L, W, Hq, Hkv, d, F, H, A, S, N, B, P, M, n_norms, KS, kps;
   int pi0;                 // variant: 0 pi0.5 (adaptive norms), 1 pi0 (state token, action-time MLP)
   int bigm;                // graph / eager launch of a bf16 expert with many rows: large-tile GEMM kernels
+  int gp_bm[5];            // large-M GEMMs: tokens per tile (128 or 64), same order as gp_nt
   int gp_nt[5], gp_s[5];   // GEMM plan (qkv, o, gateup, down, time MLP out): tiles per unit, K splits
   int S_o, S_down;         // = gp_s[1], gp_s[3]
   float eps;

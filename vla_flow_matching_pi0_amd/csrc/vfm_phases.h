@@ -1150,14 +1150,19 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
 constexpr int GM_THREADS = 256;
 constexpr int GM_LDS = 2 * 32768;   // two stages of (A tile + B tile)
 
-template <typename T, int WHICH>
+// BM: tokens per tile, 128 or 64 (a 64-token tile where 128-token tiles
+// would leave a few compute units with a second tile: waves then take 64
+// columns x 32 tokens).
+template <typename T, int WHICH, int BM>
 __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int layer) {
   static_assert(sizeof(T) == 2, "the large-M GEMM runs bf16 operands");
+  static_assert(BM == 128 || BM == 64, "token tile of 128 or 64");
+  constexpr int NJ = BM / 32;   // 16-token blocks per wave; also B chunks per thread
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
   const GemmShape gs = gemm_shape<T, WHICH, WF_NATIVE>(p, layer);
   const int K = gs.K, N = gs.N, S = gs.S;
   const int Mpad = ((p.M + 63) / 64) * 64;
-  const int MTL = (p.M + 127) / 128, NTL = N / 128, total = MTL * NTL * S;
+  const int MTL = (p.M + BM - 1) / BM, NTL = N / 128, total = MTL * NTL * S;
   const int per = (total + 7) >> 3;
   const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (v >= total) return;
@@ -1180,8 +1185,8 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
     const int c = tid + 256 * i, blk = c >> 7, rest = c & 127;
     aoff[i] = (uint32_t)(((nt * 8 + blk) * KB32 + kb0) * 1024 + rest * 16);
     const int kk = rest >> 6, u = rest & 63;
-    const int m = mt * 128 + blk * 16 + (u >> 2);
-    bok[i] = m < Mpad;
+    const int m = mt * BM + blk * 16 + (u >> 2);
+    bok[i] = m < Mpad && i < NJ;
     boff[i] = (uint32_t)((((kb0 + kk) * Mpad + m) * 32 + (u & 3) * 8) * 2);
     bdst[i] = (blk * 2 + kk) * 64 + (u & 3) * 16 + (u >> 2);
   }
@@ -1191,7 +1196,7 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + (uint32_t)it * 2048u, 0, 0);
-      gb[i] = ld16_if(rb, boff[i] + (uint32_t)it * bstep, bok[i]);
+      if (i < NJ) gb[i] = ld16_if(rb, boff[i] + (uint32_t)it * bstep, bok[i]);
     }
   };
   auto lstore = [&](int buf) {
@@ -1199,14 +1204,14 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       A[tid + 256 * i] = ga[i];
-      A[1024 + bdst[i]] = gb[i];
+      if (i < NJ) A[1024 + bdst[i]] = gb[i];
     }
   };
-  floatx4 acc[4][4];
+  floatx4 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   gload(0);
   lstore(0);
   __syncthreads();
@@ -1216,15 +1221,15 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
     const u32x4* B = A + 1024;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x4 a[4], b[4];
+      u32x4 a[4], b[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = A[(wn * 4 + i) * 128 + kb * 64 + lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = B[(wm * 4 + j) * 128 + kb * 64 + lane];
+      for (int j = 0; j < NJ; ++j) b[j] = B[(wm * NJ + j) * 128 + kb * 64 + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = MT<T>::mma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = MT<T>::mma(a[i], b[j], acc[i][j]);
     }
     if (it + 1 < nk) lstore((it + 1) & 1);
     __syncthreads();
@@ -1235,8 +1240,8 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
   for (int i = 0; i < 4; ++i) {
     const int tile = nt * 8 + wn * 4 + i;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gm = mt * 128 + wm * 64 + j * 16 + c16;
+    for (int j = 0; j < NJ; ++j) {
+      const int gm = mt * BM + wm * (BM / 2) + j * 16 + c16;
       if (gm >= p.M) continue;
       const floatx4 vv = acc[i][j];
       if (WHICH == G_QKV) {
@@ -1607,16 +1612,26 @@ __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
 }
 
 template <typename T, int D, int WF, bool CAL>
-__host__ const void* phase_kernel(int ph, bool bigm = false) {
+__host__ const void* phase_kernel(int ph, bool bigm = false, int bm = 128) {
   if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
+    if (bigm && bm == 64) {
+      switch (ph) {
+        case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV, 64>;
+        case PH_O: return (const void*)&k_gemm_m<T, G_O, 64>;
+        case PH_GU: return (const void*)&k_gemm_m<T, G_GU, 64>;
+        case PH_DOWN: return (const void*)&k_gemm_m<T, G_DOWN, 64>;
+        case PH_TMLP: return (const void*)&k_gemm_m<T, G_TMLP, 64>;
+        default: break;
+      }
+    }
     if (bigm) {
       switch (ph) {
         case PH_ATTN: return (const void*)&k_attn_m<T, D>;
-        case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV>;
-        case PH_O: return (const void*)&k_gemm_m<T, G_O>;
-        case PH_GU: return (const void*)&k_gemm_m<T, G_GU>;
-        case PH_DOWN: return (const void*)&k_gemm_m<T, G_DOWN>;
-        case PH_TMLP: return (const void*)&k_gemm_m<T, G_TMLP>;
+        case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV, 128>;
+        case PH_O: return (const void*)&k_gemm_m<T, G_O, 128>;
+        case PH_GU: return (const void*)&k_gemm_m<T, G_GU, 128>;
+        case PH_DOWN: return (const void*)&k_gemm_m<T, G_DOWN, 128>;
+        case PH_TMLP: return (const void*)&k_gemm_m<T, G_TMLP, 128>;
         default: break;
       }
     }
@@ -1665,8 +1680,13 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
       return hipErrorInvalidValue;
     }
   }
-  return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, bigm), dim3(grid), dim3(bigm ? GM_THREADS : NTH), args,
-                         lds, st);
+  int bm = 128;
+  if (bigm) {
+    const int gi = phase == PH_QKV ? 0 : phase == PH_O ? 1 : phase == PH_GU ? 2 : phase == PH_DOWN ? 3 : 4;
+    bm = p.gp_bm[gi];
+  }
+  return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, bigm, bm), dim3(grid), dim3(bigm ? GM_THREADS : NTH),
+                         args, lds, st);
 }
 
 template <typename T, int D, int WF, bool CAL>
@@ -1677,10 +1697,12 @@ hipError_t set_lds_limit(int bytes) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph) {
     e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    const void* big = phase_kernel<T, D, WF, CAL>(ph, true);
-    if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph)) {
-      const int need = ph == PH_ATTN ? AttnMLds<D>::TOTAL : GM_LDS;
-      e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > need ? bytes : need);
+    for (int bm : {128, 64}) {
+      const void* big = phase_kernel<T, D, WF, CAL>(ph, true, bm);
+      if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph)) {
+        const int need = ph == PH_ATTN ? AttnMLds<D>::TOTAL : GM_LDS;
+        e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > need ? bytes : need);
+      }
     }
   }
   return e;

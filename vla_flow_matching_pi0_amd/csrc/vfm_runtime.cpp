@@ -388,14 +388,14 @@ int phase_grid(const VP& p, int phase) {
   long units = 1;
   if (p.bigm) {
     // large-M GEMM kernels: one workgroup per 128 x 128 tile and K split, rounded up to whole XCD rounds
-    const int mt128 = cdiv(p.M, 128);
+    auto mtl = [&](int i) { return cdiv(p.M, p.gp_bm[i]); };
     long tiles = -1;
     switch (phase) {
-      case vfm::PH_QKV: tiles = (long)(p.Hq + 2 * p.Hkv) * p.d / 128 * mt128 * p.gp_s[0]; break;
-      case vfm::PH_O: tiles = (long)p.W / 128 * mt128 * p.gp_s[1]; break;
-      case vfm::PH_GU: tiles = (long)2 * p.F / 128 * mt128 * p.gp_s[2]; break;
-      case vfm::PH_DOWN: tiles = (long)p.W / 128 * mt128 * p.gp_s[3]; break;
-      case vfm::PH_TMLP: tiles = (long)p.W / 128 * mt128 * p.gp_s[4]; break;
+      case vfm::PH_QKV: tiles = (long)(p.Hq + 2 * p.Hkv) * p.d / 128 * mtl(0) * p.gp_s[0]; break;
+      case vfm::PH_O: tiles = (long)p.W / 128 * mtl(1) * p.gp_s[1]; break;
+      case vfm::PH_GU: tiles = (long)2 * p.F / 128 * mtl(2) * p.gp_s[2]; break;
+      case vfm::PH_DOWN: tiles = (long)p.W / 128 * mtl(3) * p.gp_s[3]; break;
+      case vfm::PH_TMLP: tiles = (long)p.W / 128 * mtl(4) * p.gp_s[4]; break;
       // single-pass attention: one workgroup per (sample, head), samples in groups of 8 (one per XCD)
       case vfm::PH_ATTN: tiles = (long)cdiv(p.B, 8) * 8 * p.Hq; break;
       default: break;
@@ -533,6 +533,10 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
           while (sp < vfm::MAX_KSPLIT && (long)(Ns[i] / 128) * mt * sp < 256 && Ks[i] % (sp * 2 * 64) == 0) sp *= 2;
         p.gp_nt[i] = 8;
         p.gp_s[i] = sp;
+        // 128-token tiles just past one per compute unit (256 < tiles <= 384) would run a second round on a
+        // few units: 64-token tiles spread the same work about two per unit, both resident at once
+        const long t128 = (long)(Ns[i] / 128) * mt * sp;
+        p.gp_bm[i] = (t128 > 256 && t128 <= 384) ? 64 : 128;
       }
     }
     p.S_o = p.gp_s[1];
