@@ -255,3 +255,42 @@ def test_graph_variants_alternate_shapes_and_buffers(chain, cache):
             assert err <= TOL, (rnd, P)
     ex.check()
     ex.close()
+
+
+def test_unbound_stage_is_refused_before_anything_runs(chain):
+    """A tick whose denoise stage lacks its prefix binding fails on the host
+    with VFM_E_UNBOUND before any stage is enqueued: the prefix stage ahead of
+    it leaves its outputs untouched. Binding the buffers makes the same tick
+    run."""
+    from vla_flow_matching_pi0_amd import vfm
+    c = chain
+    print("case plan unbound stage", flush=True)
+    emb = dev(c["emb"]["a"], torch.bfloat16)
+    pk, pv = kv_buffers(c)
+    pk.fill_(7.0)
+    pv.fill_(7.0)
+    pre = make_producer(c)
+    ex = vfm.Expert(c["ecfg"], {k: dev(v, torch.bfloat16) for k, v in c["eparams"].items()})
+    shape = (c["ecfg"].batch, c["ecfg"].action_horizon, c["ecfg"].action_dim)
+    noise = dev(noise_for(0, shape, salt=30))
+    actions = torch.zeros_like(noise)
+    plan = vfm.Plan()
+    plan.add_prefix(pre, emb, pk, pv)
+    se = plan.add_denoise(ex, noise=noise, state=dev(c["state"]), actions=actions)
+    with pytest.raises(vfm.VfmError) as e:
+        plan.run(0)
+    assert e.value.name == "VFM_E_UNBOUND"
+    with pytest.raises(vfm.VfmError):
+        plan.deps(0, se)
+    torch.cuda.synchronize()
+    assert bool((pk.float() == 7.0).all()) and bool((actions == 0).all())
+    ex.bind("prefix_k", pk)
+    ex.bind("prefix_v", pv)
+    ex.bind("state", dev(c["state"]))
+    plan.run(0)
+    err = rel_l2(actions.cpu().numpy(), expect(c, "a", noise.cpu().numpy()))
+    print(f"after binding: rel_l2 {err:.3e}")
+    assert err <= TOL
+    plan.close()
+    ex.close()
+    pre.close()
