@@ -16,12 +16,17 @@ VFM_DECLARE_KERNEL_SET(ks_w4)
 VFM_DECLARE_KERNEL_SET(ks_i8)
 VFM_DECLARE_KERNEL_SET(ks_w4a8)
 
+// LDS of the row phases (norms, step boundary): the boundary's reduction
+// slots, row, per-thread partials and action row, which covers the norms'
+// reduction slots too.
+static size_t row_lds_bytes(const VP& p) { return (NTHREADS / 64 + p.W + 4 * NTHREADS + MAX_A_HOST) * 4; }
+
 size_t lds_bytes(const VP& p, int act_bytes) {
   const size_t nwaves = NTHREADS / 64;
   const size_t gemm = nwaves * 2 * 4 * 64 * 16;
   const size_t epc = 16 / act_bytes;
   const size_t attn = ((size_t)ATT_KEYS_HOST * (p.d + epc) + (size_t)p.d * (ATT_KEYS_HOST + epc)) * act_bytes;
-  const size_t row = (nwaves + p.W + 4 * NTHREADS + MAX_A_HOST) * 4;
+  const size_t row = row_lds_bytes(p);
   size_t m = gemm > attn ? gemm : attn;
   return m > row ? m : row;
 }
@@ -41,6 +46,14 @@ hipError_t prepare_kernels(int kset, int d, int lds) {
 
 hipError_t launch_phase(const VP& p, int kset, int mode, int phase, int k, int l, int grid, size_t lds,
                         hipStream_t st) {
+  // A phase launched on its own takes only the LDS its own kernel uses: the
+  // row phases then fit several workgroups per compute unit (one row each)
+  // instead of the two that the GEMM phases' allocation would allow.
+  if (mode != 0 && mode != 3 &&
+      (phase == PH_RN_ATTN || phase == PH_RN_MLP || phase == PH_BOUNDARY || phase == PH_COMBINE)) {
+    const size_t row = row_lds_bytes(p);
+    if (row < lds) lds = row;
+  }
   switch (kset) {
     case KS_F32: return ks_f32_launch(p, mode, phase, k, l, grid, lds, st);
     case KS_BF16: return ks_bf16_launch(p, mode, phase, k, l, grid, lds, st);
