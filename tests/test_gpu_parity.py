@@ -250,10 +250,10 @@ def test_plain_persistent_launch_and_trace():
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
 
 
-@pytest.mark.parametrize("variant,batch,horizon", [("pi05", 8, 50), ("pi05", 20, 13), ("pi0", 6, 50)])
+@pytest.mark.parametrize("variant,batch,horizon", [("pi05", 8, 50), ("pi05", 21, 13), ("pi0", 6, 50)])
 def test_large_m_gemm_matches_oracle(variant, batch, horizon):
     """Graph and eager launch of a bf16 expert with M = B x T >= 256 rows run
-    the large-M GEMM kernels (128 x 128 tiles; rows not a multiple of 128;
+    the large-M GEMM kernels (128 x 128 tiles; rows not a multiple of 128, an odd row count;
     pi0's time-MLP GEMM too); persistent launch runs the skinny GEMM. All
     against the oracle on the whole batch."""
     gu = _gu()

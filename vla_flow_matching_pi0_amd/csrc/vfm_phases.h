@@ -162,15 +162,33 @@ __device__ __forceinline__ size_t v_off(int d, size_t head_block, int i, int e) 
 // Row m of the residual stream is always handled by workgroup m % nwg, in
 // every row phase, so a row of h and x is only ever touched by one workgroup.
 
+// Sum over the waves of one half of the workgroup (threads [0, NTH/2) or
+// [NTH/2, NTH)); every thread of the workgroup must call it.
+__device__ __forceinline__ float half_block_sum(float v, float* red, int half) {
+  v = warp_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES / 2; ++i) s += red[half * (NWAVES / 2) + i];
+  return s;
+}
+
 // h[m] += gate * sum_s part[s][m]; xn[m] = adaRMSNorm(h[m]) with norm `ni`
-// (ni < 0: no norm). Four columns per thread; W <= 4 * NTH.
-template <typename T, bool Q8>
+// (ni < 0: no norm). Four columns per thread. RPP rows per pass: 1 (W <=
+// 4 * NTH), or 2 (W <= 2 * NTH; threads [0, NTH/2) take row m of the pair,
+// the others row m + 1, each half with its own reduction; a row m >= M is
+// a no-op for its half).
+template <typename T, bool Q8, int RPP = 1>
 __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, const float* part, int S, int gate_ni,
                                                   int ni, void* xn, float* red, float inv) {
   const int tid = tid_opaque();
   const int W4 = p.W / 4;
-  const int c = tid;
-  const bool act = c < W4;
+  const int half = RPP == 2 ? tid / (NTH / 2) : 0;
+  const int c = RPP == 2 ? tid - half * (NTH / 2) : tid;
+  if (RPP == 2) m += half;
+  const bool act = c < W4 && m < p.M;
   const auto mr = rsrc(p.mod);
   const size_t mrow = ((size_t)step * p.n_norms + (ni >= 0 ? ni : 0)) * 3 * p.W + c * 4;
   const floatx4 sc = as_f4(ld16_if(mr, (uint32_t)(mrow * 4), act && ni >= 0));
@@ -193,9 +211,9 @@ __device__ __forceinline__ void row_residual_norm(const VP& p, int step, int m, 
   }
   if (ni < 0) return;
   float ss = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
-  ss = block_sum(ss, red);
+  ss = RPP == 2 ? half_block_sum(ss, red, half) : block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)p.W + p.eps);
-  if (c < W4) {
+  if (act) {
     const floatx4 y = hv * r * (1.0f + sc) + sh;
     store_gemm_in4<T, Q8>(p, xn, m, c * 4, y, inv);
   }
@@ -239,8 +257,17 @@ __device__ __forceinline__ void ph_rn(const VP&, int step, int layer, bool mlp, 
   const int S = mlp ? p.S_o : layer == 0 ? p.gp_s[4] : p.S_down;   // layer 0 (pi0 only): the time-MLP output
   const int gate_ni = mlp ? 2 * layer : 2 * layer - 1, ni = mlp ? 2 * layer + 1 : 2 * layer;
   void* xn = slab(p, step, layer) + (mlp ? p.off_xnm : p.off_xna);
+  const float inv = Q8 ? act_inv(p, layer, mlp ? 2 : 0) : 1.0f;
+  if (p.bigm && p.W <= 2 * NTH) {
+    // per-phase launch with many rows: two rows per workgroup pass (at W = 1024 one row occupies half the threads)
+    for (int m = 2 * wg; m < p.M; m += 2 * nwg) {
+      row_residual_norm<T, Q8, 2>(p, step, m, part, S, gate_ni, ni, xn, red, inv);
+      __syncthreads();
+    }
+    return;
+  }
   for (int m = wg; m < p.M; m += nwg) {
-    row_residual_norm<T, Q8>(p, step, m, part, S, gate_ni, ni, xn, red, Q8 ? act_inv(p, layer, mlp ? 2 : 0) : 1.0f);
+    row_residual_norm<T, Q8>(p, step, m, part, S, gate_ni, ni, xn, red, inv);
     __syncthreads();
   }
 }

@@ -403,9 +403,9 @@ int phase_grid(const VP& p, int phase) {
     if (tiles > 0) return (int)((tiles + 7) / 8 * 8);
   }
   switch (phase) {
-    case vfm::PH_BOUNDARY:
+    case vfm::PH_BOUNDARY: units = p.M; break;
     case vfm::PH_RN_ATTN:
-    case vfm::PH_RN_MLP: units = p.M; break;
+    case vfm::PH_RN_MLP: units = p.bigm && p.W <= 2 * vfm::NTHREADS ? cdiv(p.M, 2) : p.M; break;
     case vfm::PH_QKV: units = (long)(p.Hq + 2 * p.Hkv) * p.d / (16 * p.gp_nt[0]) * p.gp_s[0] * mt; break;
     case vfm::PH_O: units = (long)p.W / (16 * p.gp_nt[1]) * p.gp_s[1] * mt; break;
     case vfm::PH_GU: units = (long)2 * p.F / (16 * p.gp_nt[2]) * p.gp_s[2] * mt; break;
