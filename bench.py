@@ -70,13 +70,14 @@ def measured_traffic(workload: str, mode: str):
 
 def algorithmic_bytes_per_step(cfg) -> int:
     """Bytes the method must read from HBM per Euler step: the per-step GEMM
-    weights (q/k/v/o/gate/up/down of every layer, in/out/state projections)
-    plus every layer's prefix K and V."""
+    weights (q/k/v/o/gate/up/down of every layer, in/out projections) plus
+    every layer's prefix K and V. The state projection is applied once per
+    call (algorithmic_bytes_per_launch)."""
     W, F, d, L = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.num_layers
     qkv = W * (cfg.num_q_heads + 2 * cfg.num_kv_heads) * d
     o = cfg.num_q_heads * d * W
     per_layer = qkv + o + 2 * W * F + F * W
-    small = cfg.action_dim * W + W * cfg.action_dim + cfg.state_dim * W
+    small = cfg.action_dim * W + W * cfg.action_dim
     if getattr(cfg, "variant", "pi05") == "pi0":
         small += W * W              # pi0: the time-MLP output GEMM of every step
     prefix = 2 * L * cfg.batch * cfg.prefix_len * cfg.num_kv_heads * d
@@ -91,6 +92,20 @@ def algorithmic_bytes_per_step(cfg) -> int:
     else:
         gemm = L * per_layer * act_b
     return gemm + small * act_b + prefix * act_b
+
+
+def algorithmic_bytes_per_launch(cfg) -> int:
+    """One call: num_steps Euler steps plus the state projection, read once."""
+    act_b = 4 if cfg.weight_precision == "fp32" else 2
+    return algorithmic_bytes_per_step(cfg) * cfg.num_steps + cfg.state_dim * cfg.width * act_b
+
+
+def roofline_bound(cfg) -> str:
+    """'hbm' or 'mfma': whichever of the weight stream and the arithmetic
+    (dense MFMA peak of the type the GEMMs multiply in) takes longer at peak."""
+    t_hbm = algorithmic_bytes_per_launch(cfg) / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_per_chunk(cfg) / (MFMA_PEAK_TFLOPS[cfg.weight_precision] * 1e12)
+    return "mfma" if t_mfma > t_hbm else "hbm"
 
 
 def flops_per_chunk(cfg) -> float:
@@ -361,16 +376,13 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    bytes_step = algorithmic_bytes_per_step(cfg)
-    bytes_launch = bytes_step * cfg.num_steps
+    bytes_launch = algorithmic_bytes_per_launch(cfg)
     achieved = bytes_launch / (mean * 1e-3) / 1e9
     tflops = flops_per_chunk(cfg) / (mean * 1e-3) / 1e12
-    # the bound is whichever of the weight stream (HBM) and the arithmetic
-    # (dense MFMA peak of the type the GEMMs multiply in) takes longer at peak
     mfma_peak = MFMA_PEAK_TFLOPS[cfg.weight_precision]
     t_hbm = bytes_launch / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops_per_chunk(cfg) / (mfma_peak * 1e12)
-    if t_mfma > t_hbm:
+    if roofline_bound(cfg) == "mfma":
         roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                     "frac": round(tflops / mfma_peak, 4), "traffic": None}
     else:
