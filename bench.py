@@ -100,6 +100,15 @@ def algorithmic_bytes_per_launch(cfg) -> int:
     return algorithmic_bytes_per_step(cfg) * cfg.num_steps + cfg.state_dim * cfg.width * act_b
 
 
+def resolved_mode(cfg, mode: str) -> str:
+    """The launch the library takes for `mode` (its 'auto' rule: graph launch
+    for bf16 weights and at least 256 rows, else the persistent kernel)."""
+    if mode != "auto":
+        return mode
+    T = cfg.action_horizon + (1 if getattr(cfg, "variant", "pi05") == "pi0" else 0)
+    return "graph" if cfg.weight_precision == "bf16" and cfg.batch * T >= 256 else "persistent"
+
+
 def roofline_bound(cfg) -> str:
     """'hbm' or 'mfma': whichever of the weight stream and the arithmetic
     (dense MFMA peak of the type the GEMMs multiply in) takes longer at peak."""
@@ -243,7 +252,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200, help="timed denoise calls (chunks)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi05_bf16_b1")
-    ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager"])
+    ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager", "auto"],
+                    help="launch mode; 'auto' is the library default (graph launch of the large-batch kernels for "
+                         "bf16 experts with at least 256 rows, else the persistent kernel)")
     ap.add_argument("--persistent-launch", default="cooperative", choices=["cooperative", "plain"],
                     help="launch API of the persistent kernel (plain: for profilers that cannot follow "
                          "cooperative launches)")
@@ -409,7 +420,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "layers": cfg.num_layers, "width": cfg.width, "heads": f"{cfg.num_q_heads}q/{cfg.num_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp": cfg.mlp_dim, "horizon": cfg.action_horizon,
                    "action_dim": cfg.action_dim, "state_dim": cfg.state_dim, "prefix": cfg.prefix_len,
-                   "batch": cfg.batch, "euler_steps": cfg.num_steps, "launch_mode": args.mode,
+                   "batch": cfg.batch, "euler_steps": cfg.num_steps, "launch_mode": resolved_mode(cfg, args.mode),
                    "persistent_launch": args.persistent_launch},
         "chunks_per_s": round(cfg.batch * 1e3 / ms_chunk, 2),
         "ms_per_launch_mean": round(mean, 4),

@@ -60,3 +60,10 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_auto_mode_resolution_matches_the_library_rule():
+    assert bench.resolved_mode(CONFIGS["pi05_bf16_b1"], "auto") == "persistent"
+    assert bench.resolved_mode(CONFIGS["pi05_bf16_b32"], "auto") == "graph"
+    assert bench.resolved_mode(CONFIGS["pi05_fp8_p816"], "auto") == "persistent"
+    assert bench.resolved_mode(CONFIGS["pi05_bf16_b32"], "eager") == "eager"
