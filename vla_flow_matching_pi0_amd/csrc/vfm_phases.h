@@ -1320,7 +1320,8 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
 // its keys and values come from HBM once and from that XCD's L2 for the
 // other heads.
 constexpr int AM_KEYS = 32;
-constexpr int AM_THREADS = 256;
+constexpr int AM_GT = 256;              // threads of one tile group (4 waves, 16 query rows each)
+constexpr int AM_THREADS = 2 * AM_GT;   // two groups take alternate prefix tiles
 constexpr int AM_CHUNK = 64;   // chunk keys staged once (H <= 64)
 
 template <int D>
@@ -1359,9 +1360,10 @@ __global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int la
   static_assert(sizeof(T) == 2, "the large-batch attention runs bf16 operands");
   using L = AttnMLds<D>;
   constexpr int KCH = D / 8;                          // 16-byte chunks per key row
-  constexpr int KL = AM_KEYS * KCH / AM_THREADS;      // prefix K chunks per thread per tile
-  constexpr int VI = (D + AM_THREADS - 1) / AM_THREADS;   // (4 keys x 8 dims) V items per thread per tile
-  static_assert(KL >= 1 && AM_KEYS * KCH % AM_THREADS == 0, "K tile must split evenly over the threads");
+  constexpr int KL = AM_KEYS * KCH / AM_GT;           // prefix K chunks per group thread per tile
+  constexpr int VI = (D + AM_GT - 1) / AM_GT;         // (4 keys x 8 dims) V items per group thread per tile
+  static_assert(KL >= 1 && AM_KEYS * KCH % AM_GT == 0, "K tile must split evenly over a group's threads");
+  static_assert(AttnMLds<D>::CK >= (4 * (D / 16) * 64 * 16 + 4 * 64 * 8), "the merge reuses the two stages");
   uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
   // sample b on XCD b % 8: blockIdx = 8 * (Hq * (b / 8) + head) + b % 8
   const int xcd = (int)(blockIdx.x & 7), loc = (int)(blockIdx.x >> 3);
@@ -1369,7 +1371,8 @@ __global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int la
   if (b >= p.B) return;
   const int H = p.H, P = p.P;
   const int kvh = jh / (p.Hq / p.Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, grp = tid / AM_GT, gtid = tid % AM_GT;
+  const int lane = tid & 63, w = gtid >> 6, g = lane >> 4, c16 = lane & 15;
   const size_t layer_elems = (size_t)p.B * P * p.Hkv * D;
   const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
   const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
@@ -1419,19 +1422,19 @@ __global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int la
   int kkey[KL], vkey[VI];
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
-    const int idx = tid + j * AM_THREADS;
+    const int idx = gtid + j * AM_GT;
     kkey[j] = idx / KCH;
     kofs[j] = (uint32_t)(((((size_t)b * P + kkey[j]) * p.Hkv + kvh) * D + 8 * (idx % KCH)) * 2);
   }
 #pragma unroll
   for (int j = 0; j < VI; ++j) {
-    const int idx = tid + j * AM_THREADS, kq = idx / KCH, c = idx % KCH;
+    const int idx = gtid + j * AM_GT, kq = idx / KCH, c = idx % KCH;
     vkey[j] = idx < D ? 4 * kq : 1 << 30;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       vofs[j][r] = (uint32_t)(((((size_t)b * P + 4 * kq + r) * p.Hkv + kvh) * D + 8 * c) * 2);
   }
-  // tile t + 1's loads are in flight during tile t's MFMAs
+  // a group's next tile (t + 2) is loaded during its tile t's MFMAs
   u32x4 kr[KL], vr[VI][4];
   auto gload = [&](int t) {
     const int s0 = t * AM_KEYS;
@@ -1446,12 +1449,12 @@ __global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int la
     uint8_t* kb = lds + buf * L::STAGE;
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
-      const int idx = tid + j * AM_THREADS;
+      const int idx = gtid + j * AM_GT;
       *reinterpret_cast<u32x4*>(kb + ((idx / KCH) * L::K_LD + (idx % KCH) * 8) * 2) = kr[j];
     }
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
-      const int idx = tid + j * AM_THREADS;
+      const int idx = gtid + j * AM_GT;
       if (idx < D) am_store_v(kb + L::K_TILE + (idx / KCH) * L::V_LD, idx % KCH, vr[j]);
     }
   };
@@ -1522,26 +1525,47 @@ __global__ __launch_bounds__(AM_THREADS, 1) void k_attn_m(VP p, int step, int la
     }
   };
 
+  // Group grp takes prefix tiles grp, grp + 2, ... through its own LDS
+  // stage (one wave of each group per SIMD, so one group's latency chain
+  // overlaps the other's work), then chunk keys 32 grp .. 32 grp + 31.
   const int ptiles = (P + AM_KEYS - 1) / AM_KEYS;
-  gload(0);
-  lstore(0);
+  const uint8_t* st = lds + grp * L::STAGE;
+  gload(grp);   // past the last tile: predicated off, fetches nothing
+  lstore(grp);
   __syncthreads();
-  for (int t = 0; t < ptiles; ++t) {
-    gload(t + 1);   // past the last tile: predicated off, fetches nothing
-    if (active) {
-      const uint8_t* st = lds + (t & 1) * L::STAGE;
-      tile(reinterpret_cast<const T*>(st), st + L::K_TILE, t * AM_KEYS, P);
-    }
-    if (t + 1 < ptiles) lstore((t + 1) & 1);
+  for (int t = grp; t - grp < ptiles; t += 2) {
+    gload(t + 2);
+    if (active && t < ptiles) tile(reinterpret_cast<const T*>(st), st + L::K_TILE, t * AM_KEYS, P);
+    __syncthreads();   // both groups' LDS reads of this pass are done
+    if (t + 2 < ptiles) lstore(grp);
     __syncthreads();
   }
-  if (active) {
-    // the chunk's keys: P + i for i < H (pi0: the state token, query row 0,
-    // sees only the first of them, its own)
-    const int lim = (p.pi0 && qrow == 0) ? P + 1 : P + H;
-    for (int j0 = 0; j0 < H; j0 += AM_KEYS)
-      tile(reinterpret_cast<const T*>(lds + L::CK) + j0 * L::K_LD, lds + L::CV + (j0 / 4) * L::V_LD, P + j0, lim);
-    float l = l_run;
+  // the chunk's keys: P + i for i < H (pi0: the state token, query row 0,
+  // sees only the first of them, its own)
+  const int lim = (p.pi0 && qrow == 0) ? P + 1 : P + H;
+  const int j0 = grp * AM_KEYS;
+  if (active && j0 < H)
+    tile(reinterpret_cast<const T*>(lds + L::CK) + j0 * L::K_LD, lds + L::CV + (j0 / 4) * L::V_LD, P + j0, lim);
+  // merge: group 1 leaves its running output, reference maximum and sum
+  // shares in the (now free) stages; group 0 combines them with its own
+  floatx4* mo = reinterpret_cast<floatx4*>(lds);                       // [4 waves][D / 16][64]
+  float* mm = reinterpret_cast<float*>(lds + 4 * (D / 16) * 64 * 16);  // [4 waves][64][2]
+  if (grp == 1 && active) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) mo[(w * (D / 16) + dt) * 64 + lane] = O[dt];
+    mm[(w * 64 + lane) * 2] = m_run;
+    mm[(w * 64 + lane) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  if (grp == 0 && active) {
+    const float m1 = mm[(w * 64 + lane) * 2], l1 = mm[(w * 64 + lane) * 2 + 1];
+    const float mx = fmaxf(m_run, m1);
+    // (a group that saw no key keeps m = -inf, O = 0, l = 0: weight 0)
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mx);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mx);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) O[dt] = O[dt] * a0 + mo[(w * (D / 16) + dt) * 64 + lane] * a1;
+    float l = l_run * a0 + l1 * a1;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (qrow < H) {
