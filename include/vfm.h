@@ -234,6 +234,20 @@ vfm_status vfm_check(vfm_expert* ex, void* stream);
 /* Synchronise the expert's work and free everything it owns. NULL-safe. */
 vfm_status vfm_expert_destroy(vfm_expert* ex);
 
+/* Diagnostics of the streaming batch-1 kernel (launch_mode "stream"): copy
+ * the raw bytes of one of its internal buffers to host memory `dst`
+ * (synchronous; `bytes` must equal the buffer size). Names: "slab" (the
+ * intermediates of step k, layer l at index = k L + l: y_attn, norm sums of
+ * squares, q, k, transposed v, attention output, y_mlp, sums, MLP
+ * activation), "h" (residual stream, [64][W] f32), "s_emb", "vt" (prefix
+ * values transposed), "apart" / "aml" (attention split outputs and their
+ * (max, sum)), "shw_q" / "shw_g" (create-time shift x W tables);
+ * "slab_layout" writes 10 uint64: the byte offsets of the nine slab
+ * sections in that order, then the slab size. For tests; not a hot-path call.
+ * Errors: VFM_E_INVALID_ARG, VFM_E_STATE (no streaming state), VFM_E_SHAPE,
+ * VFM_E_HIP. */
+vfm_status vfm_stream_debug(vfm_expert* ex, const char* name, int32_t index, void* dst, size_t bytes);
+
 /* Execution-state capsules. The FlashRT-PAI introduction (its third
  * mechanism, execution-state capsules) and the FlashRT walk-through (serving
  * hosts: graph-replay-native capsules with snapshot, restore, fork and time

@@ -119,16 +119,15 @@ __device__ __forceinline__ uint32_t ld2_if(__amdgpu_buffer_rsrc_t r, uint32_t of
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, ok ? off : OOB, 0, 0);
 }
 
-// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave: the two
-// lane-swap instructions of gfx950 pair rows 0/1 and 2/3 of 16 lanes, then
-// halves 0/1 of 32 lanes, without a round trip through LDS.
+// Maximum over the four lanes c16 + 16 g (g = 0 .. 3) of a wave, in every
+// one of them: two butterfly steps across the 16-lane rows. (The gfx950
+// lane-swap instructions would do this without the LDS crossbar, but with
+// both inputs the same value the compiler keeps one half of the swapped pair
+// and drops the max between them, which returns lane group 0's value instead
+// of the maximum.)
 __device__ __forceinline__ float am_max4(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t v = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
 }
 
 __device__ __forceinline__ floatx4 as_f4(u32x4 v) { return __builtin_bit_cast(floatx4, v); }

@@ -8,6 +8,7 @@
 #include "vfm.h"
 #include "vfm_params.h"
 #include "vfm_stage_io.h"
+#include "vfm_stream_rt.h"
 
 #include <hip/hip_runtime.h>
 
@@ -95,7 +96,12 @@ struct vfm_expert {
   hipEvent_t flag_event = nullptr;
   bool flag_pending = false;
   BoundBuf prefix_k, prefix_v, noise, state, actions;
-  int mode = 3;                    // 0 persistent, 1 graph, 2 eager, 3 auto (see launch_mode_of)
+  int mode = 3;                    // 0 persistent, 1 graph, 2 eager, 3 auto, 4 stream (see launch_mode_of)
+  vfm::sk::StreamState* ss = nullptr;   // streaming batch-1 kernel (bf16 pi0.5 experts whose shapes fit it)
+  std::string ss_why;                    // why there is none
+  int ss_P = -1;                         // prefix length of the last stream-eligibility check
+  bool ss_P_ok = false;
+  int ss_stop = 0;                       // diagnostics: streaming kernel leaves after this barrier
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
@@ -131,9 +137,20 @@ bool fp8_act(const vfm_expert* x) { return x->wprec == VFM_W_FP8 || x->wprec == 
 // the large-batch kernels apply (bf16 weights, M >= 256 rows: large-M GEMM
 // tiles and single-pass attention), else the persistent kernel, which is the
 // faster one while the GEMMs are skinny.
-int launch_mode_of(const vfm_expert* x, int M) {
+bool stream_fits(const vfm_expert* x, int B, int P) {
+  if (!x->ss || B != 1) return false;
+  vfm_expert* m = const_cast<vfm_expert*>(x);
+  if (P != m->ss_P) {
+    std::string why;
+    m->ss_P_ok = vfm::sk::stream_accepts(x->ss, P, &why);
+    m->ss_P = P;
+  }
+  return m->ss_P_ok;
+}
+
+int launch_mode_of(const vfm_expert* x, int B, int P) {
   if (x->mode != 3) return x->mode;
-  return (x->kset == vfm::KS_BF16 && M >= 256) ? 1 : 0;
+  return (x->kset == vfm::KS_BF16 && B * x->T >= 256) ? 1 : 0;
 }
 
 // Host decoders of the packed formats (export only).
@@ -347,6 +364,8 @@ ColMap ident_map(int N) {
 
 void free_all(vfm_expert* x) {
   x->drop_graphs();
+  vfm::sk::stream_destroy(x->ss);
+  x->ss = nullptr;
   if (x->cap_stream) (void)hipStreamDestroy(x->cap_stream);
   if (x->flag_event) (void)hipEventDestroy(x->flag_event);
   if (x->host_flag) (void)hipHostFree(x->host_flag);
@@ -363,10 +382,22 @@ vfm_status check_prev_flag(vfm_expert* x, bool wait) {
   }
   x->flag_pending = false;
   if (*x->host_flag != 0u) {
+    // the device word is sticky (never cleared by a launch): clear it now that it is reported
     *x->host_flag = 0u;
+    (void)vfm::zero_words(x->bar + 1, 1, nullptr);
+    (void)hipDeviceSynchronize();
     return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
   }
   return VFM_OK;
+}
+
+// A streaming launch that failed (a barrier that timed out) raised the
+// host-mapped error word; report it once and clear every counter it may have
+// left behind.
+vfm_status check_stream_flag(vfm_expert* x, hipStream_t s) {
+  if (!x->ss || !vfm::sk::stream_failed(x->ss)) return VFM_OK;
+  (void)vfm::sk::stream_reset(x->ss, s);
+  return fail(VFM_E_HIP, "a device-wide barrier of the streaming kernel timed out in an earlier denoise call");
 }
 
 vfm_status check_buf(const char* name, const BoundBuf& b, int dtype, std::initializer_list<int64_t> shape) {
@@ -482,7 +513,8 @@ vfm_status expert_stage_io(const vfm_expert* x, const float* noise, const float*
   if (x->S > 0) io->reads.push_back({state ? state : x->state.ptr, B * x->S * 4});
   io->writes = {{actions ? actions : x->actions.ptr, xa}};
   io->owner = x;
-  io->device_wide = launch_mode_of(x, (int)B * x->T) == 0;
+  const int lm = launch_mode_of(x, (int)B, (int)P);
+  io->device_wide = lm == 0 || lm == 4;
   return VFM_OK;
 }
 }  // namespace vfm
@@ -508,7 +540,7 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   p.s_emb = x->s_emb; p.h = x->h; p.part_o = x->part_o; p.part_d = x->part_d; p.opart = x->opart; p.ml = x->ml;
   p.ring = x->ring; p.slab = x->slab; p.off_xna = x->off_xna; p.off_q = x->off_q; p.off_k = x->off_k; p.off_v = x->off_v;
   p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
-  const int mode = launch_mode_of(x, B * x->T);
+  const int mode = launch_mode_of(x, B, P);
   p.trace = mode == 0 ? x->trace : nullptr;
 
   {
@@ -801,6 +833,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     fail(VFM_E_OOM, "workspace allocation failed");
     return bail(VFM_E_OOM);
   }
+  if (vfm::zero_words(x->bar, vfm::BAR_WORDS, s) != hipSuccess) { fail(VFM_E_HIP, "barrier clear"); return bail(VFM_E_HIP); }
   if (hipHostMalloc((void**)&x->host_flag, 4) != hipSuccess) { fail(VFM_E_OOM, "pinned allocation failed"); return bail(VFM_E_OOM); }
   *x->host_flag = 0u;
   if (hipEventCreateWithFlags(&x->flag_event, hipEventDisableTiming) != hipSuccess) { fail(VFM_E_HIP, "event"); return bail(VFM_E_HIP); }
@@ -812,6 +845,15 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     hipError_t e = vfm::prepare_kernels(x->kset, d, (int)x->lds);
     if (e == hipSuccess && fp8_act(x)) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
+  // the streaming batch-1 kernel: bf16 pi0.5 experts whose shapes fit it
+  if (x->kset == vfm::KS_BF16 && !x->pi0) {
+    const vfm::sk::StreamShape sh{L, W, Hq, Hkv, d, F, H, A, S, x->N, x->maxP, cfg->rms_eps};
+    const vfm_status sst = vfm::sk::stream_create(sh, x->w_qkv.data(), x->w_o.data(), x->w_gu.data(), x->w_down.data(),
+                                                  x->mod, s, &x->ss, &x->ss_why);
+    if (sst != VFM_OK) return bail(sst);
+  } else {
+    x->ss_why = "the streaming kernel is built for bf16 pi0.5 experts";
   }
   if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) {
     fail(VFM_E_HIP, "create-time device work failed");
@@ -870,6 +912,7 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
   if (k == "trace") {
     if (v == "1" && !x->trace) {
       x->trace_words = 2 * (size_t)(x->N * (8 * (size_t)x->L + 1 + 2 * x->pi0) + 4);
+      if (x->ss) x->trace_words = std::max(x->trace_words, 3 * (size_t)(vfm::sk::stream_barriers(x->ss) + 2));
       x->trace = (unsigned long long*)x->dalloc(x->trace_words * 8);
       if (!x->trace) return fail(VFM_E_OOM, "trace buffer");
     } else if (v == "0") {
@@ -877,6 +920,13 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     } else if (v != "1") {
       return fail(VFM_E_INVALID_ARG, "trace must be 0 or 1");
     }
+    return VFM_OK;
+  }
+  if (k == "stream_stop_after") {
+    char* end = nullptr;
+    const long n = std::strtol(value, &end, 10);
+    if (end == value || *end || n < 0) return fail(VFM_E_INVALID_ARG, "stream_stop_after must be a barrier count >= 0");
+    x->ss_stop = (int)n;
     return VFM_OK;
   }
   if (k == "persistent_launch") {
@@ -901,6 +951,10 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     else if (v == "graph") x->mode = 1;
     else if (v == "eager") x->mode = 2;
     else if (v == "auto") x->mode = 3;
+    else if (v == "stream") {
+      if (!x->ss) return fail(VFM_E_UNSUPPORTED, "launch_mode 'stream' unavailable: %s", x->ss_why.c_str());
+      x->mode = 4;
+    }
     else return fail(VFM_E_INVALID_ARG, "launch_mode '%s' unknown", value);
     return VFM_OK;
   }
@@ -941,9 +995,18 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     HIPCHK(vfm::build_rope(x->rope, x->T, x->d, P, x->cfg.rope_base, s));
     x->rope_P = P;
   }
-  const int mode = launch_mode_of(x, B * x->T);
+  const int mode = launch_mode_of(x, B, P);
+  if (mode == 4) {
+    if (!stream_fits(x, B, P))
+      return fail(VFM_E_UNSUPPORTED, "launch_mode 'stream' runs batch 1 with a prefix the attention plan fits (B = %d, P = %d)", B, P);
+    if ((st = check_stream_flag(x, s)) != VFM_OK) return st;
+    return vfm::sk::stream_run(x->ss, P, x->prefix_k.ptr, x->prefix_v.ptr, noise, state, actions, x->in_w, x->in_b,
+                               x->st_w, x->st_b, x->out_w, x->out_b, x->rope, x->coop_launch, x->trace,
+                               x->ss_stop, s);
+  }
   if (mode == 0) {
-    HIPCHK(vfm::zero_words(x->bar, vfm::BAR_WORDS, s));
+    // the arrival counters only: bar[1], the error word, stays set until reported
+    HIPCHK(vfm::zero_words(x->bar + 64, vfm::BAR_WORDS - 64, s));
     HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
     HIPCHK(hipEventRecord(x->flag_event, s));
@@ -1205,10 +1268,28 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   return VFM_OK;
 }
 
+vfm_status vfm_stream_debug(vfm_expert* x, const char* name, int32_t index, void* dst, size_t bytes) {
+  if (!x || !name || !dst) return fail(VFM_E_INVALID_ARG, "NULL argument");
+  if (!x->ss) return fail(VFM_E_STATE, "no streaming kernel state: %s", x->ss_why.c_str());
+  if (std::string(name) == "slab_layout") {
+    if (bytes != 10 * sizeof(uint64_t)) return fail(VFM_E_SHAPE, "'slab_layout' needs 10 uint64");
+    size_t offs[9];
+    const size_t slab = vfm::sk::stream_slab_layout(x->ss, offs);
+    uint64_t* o = static_cast<uint64_t*>(dst);
+    for (int i = 0; i < 9; ++i) o[i] = offs[i];
+    o[9] = slab;
+    return VFM_OK;
+  }
+  return vfm::sk::stream_debug_copy(x->ss, name, index, dst, bytes);
+}
+
 vfm_status vfm_check(vfm_expert* x, void* stream) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIPCHK(hipStreamSynchronize(s));
   HIPCHK(hipGetLastError());
+  vfm_status st = check_stream_flag(x, s);
+  if (st != VFM_OK) return st;
   return check_prev_flag(x, true);
 }
 

@@ -25,7 +25,7 @@ ABI_VERSION = 2
 # Every entry point include/vfm.h declares.
 EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
-           "vfm_expert_destroy", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
+           "vfm_expert_destroy", "vfm_stream_debug", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
            "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
            "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
            "vfm_plan_add_graph", "vfm_plan_add_edge", "vfm_plan_deps", "vfm_plan_run", "vfm_plan_destroy"]
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(vp)]
     lib.vfm_bind.argtypes = [vp, ctypes.c_char_p, vp, i32, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.vfm_denoise.argtypes = [vp, vp, vp, vp, vp]
+    lib.vfm_stream_debug.argtypes = [vp, ctypes.c_char_p, i32, vp, ctypes.c_size_t]
     lib.vfm_set_option.argtypes = [vp, ctypes.c_char_p, ctypes.c_char_p]
     lib.vfm_calibrate.argtypes = [vp, vp]
     lib.vfm_set_act_scales.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32]
@@ -211,6 +212,15 @@ class Expert:
     def export(self, name: str, shape) -> np.ndarray:
         out = np.empty(shape, dtype=np.float32)
         _check(_lib.vfm_export(self._h, name.encode(), out.ctypes.data, out.nbytes))
+        return out
+
+    def stream_debug(self, name: str, index: int = 0, nbytes: int = 0) -> np.ndarray:
+        """Raw bytes of an internal buffer of the streaming kernel (diagnostics; see vfm_stream_debug)."""
+        if name == "slab_layout":
+            out = np.empty(10, dtype=np.uint64)
+        else:
+            out = np.empty(nbytes, dtype=np.uint8)
+        _check(_lib.vfm_stream_debug(self._h, name.encode(), index, out.ctypes.data, out.nbytes))
         return out
 
     def capsule(self) -> "Capsule":
