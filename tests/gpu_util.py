@@ -55,3 +55,25 @@ def run_gpu(cfg, params, pk, pv, noise, state, mode="persistent", repeats=1):
 
 def inputs(cfg):
     return make_inputs(cfg)
+
+
+def parity_errors(got, ref, noise):
+    """(relative L2 of the actions, relative L2 of the displacement actions -
+    noise, largest element error of the displacement relative to the largest
+    reference displacement)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    noise = np.asarray(noise, dtype=np.float64)
+    d_got, d_ref = got - noise, ref - noise
+    elem = float(np.max(np.abs(d_got - d_ref)) / np.max(np.abs(d_ref)))
+    return rel_l2(got, ref), rel_l2(d_got, d_ref), elem
+
+
+def assert_parity(got, ref, noise, rel, disp, elem, label=""):
+    """Assert the three parity errors against their bounds (and print them)."""
+    e = parity_errors(got, ref, noise)
+    print(f"{label}: rel_l2={e[0]:.3e} displacement rel_l2={e[1]:.3e} max element {e[2]:.3e}", flush=True)
+    assert np.isfinite(np.asarray(got)).all(), label
+    assert e[0] <= rel, (label, "rel_l2", e[0])
+    assert e[1] <= disp, (label, "displacement", e[1])
+    assert e[2] <= elem, (label, "element", e[2])

@@ -1,6 +1,12 @@
 """GPU parity: the HIP path through the C ABI against the CPU fp64 oracle on
 the same seeded inputs. Tolerances are relative L2 on the final actions:
-1e-4 for the fp32 expert, 2e-2 for bf16."""
+1e-4 for the fp32 expert, 2e-2 for bf16 where only the actions are checked.
+The pi0.5 batch-1 bf16 workload also bounds the displacement (actions -
+noise, what the network adds) and every element of it: relative L2 2e-3,
+displacement 5e-3, elements within 1e-2 of the largest reference
+displacement. One bf16 rounding is 2^-9 = 2e-3 relative and the measured
+errors are 2.2e-4, 3.7e-4 and 4.1e-4: an order of magnitude of margin, while a
+dropped term or a wrong index (errors of order one) fails every bound."""
 import numpy as np
 import pytest
 
@@ -61,10 +67,7 @@ def test_pi05_bf16_b1_matches_oracle(mode):
     cfg, params, pk, pv, noise, state, ref = pi05_case()
     print(f"case pi05_bf16_b1 mode={mode}", flush=True)
     got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode, repeats=2)
-    err = gu.rel_l2(got, ref)
-    disp = gu.rel_l2(got - noise, ref - noise)
-    print(f"pi05 rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
-    assert err <= 2e-2
+    gu.assert_parity(got, ref, noise, 2e-3, 5e-3, 1e-2, f"pi05 {mode}")
 
 
 @pytest.mark.parametrize("cfgname", ["tiny_fp32", "pi05_bf16_b1"])

@@ -64,10 +64,10 @@ def test_pi0_bf16_b1_matches_oracle(mode):
     print(f"case pi0 bf16 mode={mode}", flush=True)
     got = gu.run_gpu(cfg, params, pk, pv, noise, state, mode)
     ref = P0.denoise_pi0(params, noise, state, pk, pv, cfg)
-    err = gu.rel_l2(got, ref)
-    disp = gu.rel_l2(got - noise, ref - noise)
-    print(f"pi0 bf16 {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
-    assert err <= 2e-2
+    # measured 2.6e-3 / 1.5e-2: the displacement error is forty times the
+    # pi0.5 expert's at the same precision (an open item); bounds at about
+    # three times the measurement
+    gu.assert_parity(got, ref, noise, 1e-2, 5e-2, 1e-1, f"pi0 bf16 {mode}")
 
 
 def test_pi0_state_changes_the_actions_and_the_trace_has_two_more_barriers_per_step():

@@ -5,7 +5,14 @@ the CPU oracle fed the same dequantised weights. Tolerance: relative L2 5e-2
 on the final actions for FP8, W4A16 and W4A8, whose kernels also quantise
 activations or round the dequantised weights to bf16; 2e-2 (the bf16 bar)
 for W8A16, whose int8 codes turn into bf16 exactly and whose column scale
-multiplies the fp32 sum."""
+multiplies the fp32 sum.
+
+The full-size cases also bound the displacement (actions - noise) and every
+element of it. FP8 and W4A8 round every GEMM input to e4m3 (rounding unit
+2^-4): relative L2 2e-2, displacement 3e-2, elements within 1e-1 of the
+largest reference displacement (measured 3.5e-3 / 7.9e-3 for FP8, 3.9e-3 /
+8.6e-3 for W4A8). W4A16 and W8A16 keep bf16 activations (unit 2^-9): 2e-3,
+5e-3 and 1e-2 (measured 3.5e-4 / 7.0e-4 and 2.5e-4 / 5.3e-4)."""
 import numpy as np
 import pytest
 
@@ -118,10 +125,7 @@ def test_fp8_p816_matches_oracle(mode):
     torch.cuda.synchronize()
     got = bufs["actions"].cpu().numpy()
     ex.close()
-    err = gu.rel_l2(got, ref)
-    disp = gu.rel_l2(got - ev[2], ref - ev[2])
-    print(f"fp8 {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
-    assert err <= 5e-2
+    gu.assert_parity(got, ref, ev[2], 2e-2, 3e-2, 1e-1, f"fp8 {mode}")
 
 
 def test_fp8_set_act_scales_from_oracle():
@@ -152,10 +156,7 @@ def test_weight_only_quantised_matches_oracle(prec, mode):
     cfg, params, ev, ref = _CACHE[prec]
     print(f"case {prec} mode={mode}", flush=True)
     got = gu.run_gpu(cfg, params, *ev, mode, repeats=2)
-    err = gu.rel_l2(got, ref)
-    disp = gu.rel_l2(got - ev[2], ref - ev[2])
-    print(f"{prec} {mode}: rel_l2={err:.3e} displacement rel_l2={disp:.3e} (diagnostic)")
-    assert err <= (5e-2 if prec == "w4a16" else 2e-2)
+    gu.assert_parity(got, ref, ev[2], 2e-3, 5e-3, 1e-2, f"{prec} {mode}")
 
 
 @pytest.mark.parametrize("prec", ["fp8", "w4a16", "w8a16", "w4a8"])
@@ -213,9 +214,6 @@ def test_w4a8_matches_oracle(mode):
     got = bufs["actions"].cpu().numpy()
     ex.close()
     rel = np.abs(got_amax - amax) / amax
-    err = gu.rel_l2(got, ref)
-    disp = gu.rel_l2(got - ev[2], ref - ev[2])
-    print(f"w4a8 {mode}: calibration amax max rel diff {rel.max():.3e}; rel_l2={err:.3e} "
-          f"displacement rel_l2={disp:.3e} (diagnostic)")
+    print(f"w4a8 {mode}: calibration amax max rel diff {rel.max():.3e}")
     assert rel.max() <= 5e-2
-    assert err <= 5e-2
+    gu.assert_parity(got, ref, ev[2], 2e-2, 3e-2, 1e-1, f"w4a8 {mode}")

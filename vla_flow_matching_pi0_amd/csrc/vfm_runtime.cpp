@@ -101,7 +101,7 @@ struct vfm_expert {
   std::string ss_why;                    // why there is none
   int ss_P = -1;                         // prefix length of the last stream-eligibility check
   bool ss_P_ok = false;
-  int ss_stop = 0;                       // diagnostics: streaming kernel leaves after this barrier
+  vfm::sk::StreamTune ss_tune;          // streaming kernel launch settings (diagnostics, loader depth)
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
@@ -926,7 +926,14 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     char* end = nullptr;
     const long n = std::strtol(value, &end, 10);
     if (end == value || *end || n < 0) return fail(VFM_E_INVALID_ARG, "stream_stop_after must be a barrier count >= 0");
-    x->ss_stop = (int)n;
+    x->ss_tune.stop_after = (int)n;
+    return VFM_OK;
+  }
+  if (k == "stream_dma_cap") {
+    char* end = nullptr;
+    const long n = std::strtol(value, &end, 10);
+    if (end == value || *end || n < 1 || n > 63) return fail(VFM_E_INVALID_ARG, "stream_dma_cap must be an integer in [1, 63]");
+    x->ss_tune.dma_cap = (int)n;
     return VFM_OK;
   }
   if (k == "persistent_launch") {
@@ -1002,7 +1009,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
     if ((st = check_stream_flag(x, s)) != VFM_OK) return st;
     return vfm::sk::stream_run(x->ss, P, x->prefix_k.ptr, x->prefix_v.ptr, noise, state, actions, x->in_w, x->in_b,
                                x->st_w, x->st_b, x->out_w, x->out_b, x->rope, x->coop_launch, x->trace,
-                               x->ss_stop, s);
+                               x->ss_tune, s);
   }
   if (mode == 0) {
     // the arrival counters only: bar[1], the error word, stays set until reported

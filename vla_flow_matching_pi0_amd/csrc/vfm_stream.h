@@ -42,6 +42,15 @@ namespace sk {
 
 extern __shared__ __align__(16) char lds[];
 
+// Loads of activations written earlier in the launch (by other XCDs) skip the
+// compute unit's L1 and read L2 (the workgroup-scope policy sc0): a cold
+// broadcast of 100 KB to every compute unit measured 2.0 us this way against
+// 3.5 us with plain loads, while device-scope (sc1) loads lost L2 sharing.
+constexpr int CPOL_SC0 = 1;
+__device__ __forceinline__ u32x4 act_ld16_if(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : OOB, 0, CPOL_SC0);
+}
+
 __device__ __forceinline__ void wg_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // wait for this wave's outstanding vector-memory operations (stores acknowledged)
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -107,8 +116,8 @@ __device__ __forceinline__ void cw_sync(KSP& p) {
 // ------------------------------------------------------------------ grid barrier
 // Flat 64-counter barrier (the fastest of the variants measured on MI355X:
 // 1.7 us for 256 workgroups; a two-level tree and a per-XCD tree measured
-// 1.8 and 1.9 us), run by the compute waves. Wave 0 publishes the GEMM phases
-// completed (`done`: their LDS regions may be refilled) and polls the
+// 1.8 and 1.9 us), run by the compute waves. Wave 0 publishes the phase
+// slots completed (`done`: the LDS regions they used may be refilled) and polls the
 // counters; meanwhile wave 1 waits until the loader reports fill `need`
 // (the next phase's weights) landed.
 __device__ __forceinline__ bool gbar(KSP& p, unsigned& epoch, int done, int need) {
@@ -170,8 +179,9 @@ __device__ __forceinline__ bool gbar(KSP& p, unsigned& epoch, int done, int need
 // instance lambda = k L + l, GEMM gi), f = 4 lambda + gi; fill f copies the
 // workgroup's tiles of that GEMM (1 KiB blocks, one direct-to-LDS load of 16
 // bytes per lane each) into the GEMM's LDS region. Fill f may start once
-// GEMM phase f - 4 (the previous user of the region) has completed, so every
-// region is refilled a whole layer ahead of its next use. The loader wave
+// the previous users of the region (the same GEMM one layer earlier, and for
+// the qkv region the attention phase that follows it) have completed, so every
+// region is refilled about a layer ahead of its next use. The loader wave
 // runs this sequence on its own, issuing as far ahead as the regions allow
 // and publishing in LDS how many fills have landed.
 struct Loader {
@@ -188,27 +198,6 @@ struct Loader {
   __device__ __forceinline__ int end(int f) const { return (f >> 2) * nbl + pre(f & 3) + nb(f & 3); }
 };
 
-__device__ __forceinline__ int units_of(KSG& g, int w) {
-  int n = 0;
-  for (int i = 0; i < g.U; ++i) n += g.units[w * g.U + i] != 0xFFFFFFFFu;
-  return n;
-}
-
-__device__ __forceinline__ void loader_init(KSP& p, int w, Loader& ld) {
-  if (lane_id() < 4 * UMAX) {
-    const int gi = lane_id() / UMAX, i = lane_id() % UMAX;
-    KSG& g = p.g[gi];
-    ctl3(p)[C_UNITS + lane_id()] = i < g.U ? g.units[w * g.U + i] : 0xFFFFFFFFu;
-  }
-  ld.nb0 = units_of(p.g[0], w) * p.g[0].nkbs;
-  ld.nb1 = units_of(p.g[1], w) * p.g[1].nkbs;
-  ld.nb2 = units_of(p.g[2], w) * p.g[2].nkbs;
-  ld.nb3 = units_of(p.g[3], w) * p.g[3].nkbs;
-  ld.nbl = ld.nb0 + ld.nb1 + ld.nb2 + ld.nb3;
-  ld.issued = ld.landed = ld.pub = 0;
-  ld.total = p.N * p.L * 4;
-}
-
 // The loader's own LDS control accesses are written as inline asm: the
 // compiler treats any LDS access after a direct-to-LDS load as possibly
 // aliasing its destination and would wait for every copy in flight first
@@ -223,6 +212,23 @@ __device__ __forceinline__ unsigned loader_ld(lds_u32* a) {
   return (unsigned)__builtin_amdgcn_readfirstlane((int)v);
 }
 
+// units of GEMM gi this workgroup holds (entries copied to LDS at start)
+__device__ __forceinline__ int units_of(KSP& p, int gi) {
+  int n = 0;
+  for (int i = 0; i < UMAX; ++i) n += loader_ld(ctl3(p) + C_UNITS + gi * UMAX + i) != 0xFFFFFFFFu;
+  return n;
+}
+
+__device__ __forceinline__ void loader_init(KSP& p, Loader& ld) {
+  ld.nb0 = units_of(p, 0) * p.g[0].nkbs;
+  ld.nb1 = units_of(p, 1) * p.g[1].nkbs;
+  ld.nb2 = units_of(p, 2) * p.g[2].nkbs;
+  ld.nb3 = units_of(p, 3) * p.g[3].nkbs;
+  ld.nbl = ld.nb0 + ld.nb1 + ld.nb2 + ld.nb3;
+  ld.issued = ld.landed = ld.pub = 0;
+  ld.total = p.N * p.L * 4;
+}
+
 // publish every fill whose loads are known complete (fills without blocks
 // count as landed once the fills before them have)
 __device__ __forceinline__ void loader_publish(KSP& p, Loader& ld) {
@@ -231,20 +237,39 @@ __device__ __forceinline__ void loader_publish(KSP& p, Loader& ld) {
   if (ld.pub != old) loader_st(ctl3(p) + C_LAND, (unsigned)ld.pub);
 }
 
-__device__ void loader_run(KSP& p, int w) {
+__device__ void loader_run(KSP& p) {
   Loader ld;
-  loader_init(p, w, ld);
+  loader_init(p, ld);
   lds_u32* ct = ctl3(p);
+  // everything the copy loop needs, read once: per GEMM the 32-K blocks
+  // (all, per split), the LDS region and the unit entries; the loop itself
+  // then issues copies with no scalar or LDS loads in between
+  int nkb[4], nkbs[4], region[4];
+  uint32_t ue[4][UMAX];
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    nkb[gi] = p.g[gi].nkb;
+    nkbs[gi] = p.g[gi].nkbs;
+    region[gi] = p.g[gi].region;
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) ue[gi][i] = loader_ld(ct + C_UNITS + gi * UMAX + i);
+  }
+  const int cap = p.dma_cap;
+  const uint32_t lane16 = (uint32_t)lane_id() * 16u;
   for (int f = 0; f < ld.total; ++f) {
-    const int gi = f & 3, nbf = ld.nb(gi);
+    const int gi = f & 3, nbf = __builtin_amdgcn_readfirstlane(ld.nb(gi));
     if (nbf == 0) continue;
-    // the region's previous user, GEMM phase f - 4, must have completed
-    if (f >= 4 && loader_ld(ct + C_FREE) < (unsigned)(f - 3)) {
+    // the region's previous users must have completed: the same GEMM one
+    // layer earlier, and for the qkv region the attention after it (which
+    // stages its keys and values there); phase slots count 5 per layer
+    // (qkv, attention, o, gate/up, down)
+    const unsigned free_at = (unsigned)(5 * ((f >> 2) - 1) + 2 + gi);
+    if (f >= 4 && loader_ld(ct + C_FREE) < free_at) {
       vmwait(0);
       ld.landed = ld.issued;
       loader_publish(p, ld);
       long spins = 0;
-      while (loader_ld(ct + C_FREE) < (unsigned)(f - 3)) {
+      while (loader_ld(ct + C_FREE) < free_at) {
         if (loader_ld(ct + C_ABORT) != 0u) return;   // nothing in flight: the wait above drained it
         __builtin_amdgcn_s_sleep(2);
         if (++spins > SPIN_LIMIT) {
@@ -253,24 +278,44 @@ __device__ void loader_run(KSP& p, int w) {
         }
       }
     }
-    KSG& g = p.g[gi];
-    const uint8_t* wsrc = p.w[gi][(f >> 2) % p.L];
-    for (int b = 0; b < nbf; ++b) {
-      const int i = b / g.nkbs, j = b - i * g.nkbs;
-      // the workgroup's unit entries sit in LDS (copied at start): the
-      // loader's only vector-memory operations are its copies, so vmcnt
-      // counts exactly them
-      const uint32_t ue = loader_ld(ct + C_UNITS + gi * UMAX + i);
-      const int tile = (int)(ue >> 8), split = (int)(ue & 0xFF);
-      const uint8_t* src = wsrc + ((((size_t)tile * g.nkb + split * g.nkbs + j) * 64 + lane_id()) * 16);
-      auto* dst = (__attribute__((address_space(3))) void*)(lds + g.region + (i * g.nkbs + j) * 1024);
-      if (ld.issued - ld.landed >= DMA_CAP) {
-        vmwait(DMA_CAP - 1);
-        ld.landed = ld.issued - (DMA_CAP - 1);
-        loader_publish(p, ld);
+    // select this GEMM's constants (uniform, unrolled selects keep them in registers)
+    int kb_all = 0, kbs = 0, reg = 0;
+    uint32_t u[UMAX];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q == gi) {
+        kb_all = nkb[q];
+        kbs = nkbs[q];
+        reg = region[q];
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i) u[i] = ue[q][i];
       }
-      __builtin_amdgcn_global_load_lds((const void*)src, dst, 16, 0, 0);
-      ++ld.issued;
+    }
+    kb_all = __builtin_amdgcn_readfirstlane(kb_all);
+    kbs = __builtin_amdgcn_readfirstlane(kbs);
+    reg = __builtin_amdgcn_readfirstlane(reg);
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) u[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)u[i]);
+    const uint8_t* wsrc = p.w[gi][(f >> 2) % p.L];
+    // the workgroup's units of one GEMM are its first nbf / kbs entries
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) {
+      if (i * kbs >= nbf) break;
+      const int tile = (int)(u[i] >> 8), split = (int)(u[i] & 0xFF);
+      const uint8_t* src = wsrc + (((size_t)tile * kb_all + (size_t)split * kbs) << 10) + lane16;
+      const uint32_t dst0 = (uint32_t)(reg + i * kbs * 1024);
+      for (int j = 0; j < kbs; ++j) {
+        // the loader's only vector-memory operations are its copies, so
+        // vmcnt counts exactly them
+        if (ld.issued - ld.landed >= cap) {
+          vmwait(cap - 1);
+          ld.landed = ld.issued - (cap - 1);
+          loader_publish(p, ld);
+        }
+        auto* dst = (__attribute__((address_space(3))) void*)(lds + dst0 + j * 1024);
+        __builtin_amdgcn_global_load_lds((const void*)(src + ((size_t)j << 10)), dst, 16, 0, 0);
+        ++ld.issued;
+      }
     }
   }
   vmwait(0);
@@ -316,8 +361,8 @@ __device__ void ph_in(KSP& p, int k, int w) {
   const bool act = m < p.H;
   const float* xin = k == 0 ? p.noise : p.x;
   uint8_t* sl = slab(p, k, 0);
-  for (int i = 0; i < p.IU; ++i) {
-    const uint32_t ue = p.in_units[w * p.IU + i];
+  for (int i = 0; i < IUMAX; ++i) {
+    const uint32_t ue = (uint32_t)__builtin_amdgcn_readfirstlane((int)ctl3(p)[C_IUNITS + i]);
     if (ue == 0xFFFFFFFFu) break;
     const int t = (int)(ue >> 8);   // table entries are (tile << 8) | split, split 0 here
     const int c = t * 16 + 4 * c4;
@@ -426,13 +471,13 @@ __device__ __forceinline__ float row_rms_inv(KSP& p, const uint8_t* ss, int m) {
 }
 
 template <int GI>
-__device__ void ph_gemm(KSP& p, int k, int l, int w) {
+__device__ __forceinline__ void ph_gemm(KSP& p, int k, int l, int w) {
   KSG& g = p.g[GI];
   int nu = 0;
   uint32_t ue[UMAX];
 #pragma unroll
   for (int i = 0; i < UMAX; ++i) {
-    ue[i] = i < g.U ? g.units[w * g.U + i] : 0xFFFFFFFFu;
+    ue[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ctl3(p)[C_UNITS + GI * UMAX + i]);
     nu += ue[i] != 0xFFFFFFFFu;
   }
   if (nu == 0) return;
@@ -451,21 +496,27 @@ __device__ void ph_gemm(KSP& p, int k, int l, int w) {
   if (cw) {
     const auto ars = rsrc(gemm_input<GI>(p, sl));
     const int nj = g.nkbs >> 1;
+    // the workgroups of an XCD all read the same activation; each starts at
+    // a different k block (rotation by its slot) so that they do not queue
+    // on the same L2 lines at the same time
+    const int rot = (w % p.per_xcd) % nj;
     u32x4 a[MAXJ];
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
-      const int kb = kb0 + kp + 2 * j;
-      a[j] = ld16_if(ars, (uint32_t)((((kb * 64 + m) << 5) + 8 * gq) * 2), mok && j < nj);
+      const int jr = j + rot < nj ? j + rot : j + rot - nj;
+      const int kb = kb0 + kp + 2 * jr;
+      a[j] = act_ld16_if(ars, (uint32_t)((((kb * 64 + m) << 5) + 8 * gq) * 2), mok && j < nj);
     }
     if constexpr (GI == GQ || GI == GG) r = row_rms_inv(p, sl + (GI == GQ ? p.o_ssa : p.o_ssm), m);
     const uint8_t* wr = reinterpret_cast<const uint8_t*>(lds) + g.region + lane * 16;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       if (j < nj) {
+        const int jr = j + rot < nj ? j + rot : j + rot - nj;
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
           if (i < nu) {
-            const u32x4 wf = *reinterpret_cast<const u32x4*>(wr + (i * g.nkbs + kp + 2 * j) * 1024);
+            const u32x4 wf = *reinterpret_cast<const u32x4*>(wr + (i * g.nkbs + kp + 2 * jr) * 1024);
             acc[i] = MT<bf16>::mma(wf, a[j], acc[i]);
           }
         }
@@ -575,13 +626,16 @@ __device__ void ph_gemm(KSP& p, int k, int l, int w) {
         if (i >= nu || ctl3(p)[C_LAST + i] == 0u) continue;
         const int tile = (int)(ue[i] >> 8);
         const int c = tile * 16 + 4 * gq;
-        floatx4 sum = acc[i];
         u32x4 pv[SMAX];
 #pragma unroll
         for (int s = 0; s < SMAX; ++s)
           pv[s] = coh_ld16_if(pr, (uint32_t)((((s * g.T + tile) * 64 + m) * 16 + 4 * gq) * 4), mok && s < S && s != split);
+        // splits added in their fixed order 0 .. S-1 whichever one arrived
+        // last, so the result does not depend on the arrival order
+        floatx4 sum = {0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s) sum += as_f4(pv[s]);
+        for (int s = 0; s < SMAX; ++s)
+          if (s < S) sum += s == split ? acc[i] : as_f4(pv[s]);
         const floatx4 hn = hv[i] + gate[i] * sum;
         float ss = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
         ss += __shfl_xor(ss, 16);
@@ -605,19 +659,23 @@ __device__ void ph_gemm(KSP& p, int k, int l, int w) {
 // the chunk's own keys. Wave (qs, dh): query subtile qs (16 action tokens),
 // half dh of the head dims for P V. Scores are computed transposed,
 // S^T = K Q^T, so a lane holds 8 keys of one query (keys 4g..4g+3 and
-// 16+4g..16+4g+3), the row max needs the two lane-swap instructions and the
-// probabilities feed the P V MFMA from registers (the transposed values are
-// stored with the same key order). All operands come straight from global
-// memory: q and the chunk's k in the tile-major layout of the qkv epilogue,
-// prefix keys in the caller's layout (8 consecutive dims are contiguous in
-// both), values from the transposed copies. After every split of a head is
-// stored, the head's units (all on one XCD) meet at a counter and each
-// merges a share of the query rows.
+// 16+4g..16+4g+3) and the probabilities feed the P V MFMA from registers (the
+// transposed values are stored with the same key order). The unit's keys and
+// values are fetched once per workgroup, one 1 KiB operand fragment per load
+// spread over the eight waves, into LDS (the qkv weight region: its refill
+// for the next layer waits for this phase); each wave then reads the
+// fragments it needs from there, and only q comes from global memory per
+// wave. After every split of a head is stored, the head's units (all on one
+// XCD) meet at a counter and each merges a share of the query rows, loading
+// the (max, sum) pairs and the partial outputs of all splits at once.
+constexpr int MERGE_MAX = 32;   // splits merged per pass (more take further passes)
+
 template <int D>
-__device__ bool ph_attn(KSP& p, int k, int l, int w) {
+__device__ __forceinline__ bool ph_attn(KSP& p, int k, int l, int w) {
   constexpr int KB = D / 32, DT = D / 32;   // k-blocks of the scores, dim tiles per half
+  constexpr int NKF = 2 * KB, NVF = 2 * DT; // 1 KiB fragments: keys (ks, kb), values (dh, dt)
+  constexpr int PERW = (NKF + NVF + NCW - 1) / NCW;
   const int wv = wave_id(), lane = lane_id(), c16 = lane & 15, gq = lane >> 4;
-  const bool cw = wv < NCW;
   const int qs = wv & 3, dh = (wv >> 2) & 1;
   const uint8_t* sl = slab(p, k, l);
   const int group = p.Hq / p.Hkv;
@@ -626,11 +684,12 @@ __device__ bool ph_attn(KSP& p, int k, int l, int w) {
   int na = 0;
 #pragma unroll
   for (int i = 0; i < AUMAX; ++i) {
-    au[i] = i < p.AU ? p.attn_units[w * p.AU + i] : 0xFFFFFFFFu;
+    au[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)ctl3(p)[C_AUNITS + i]);
     na += au[i] != 0xFFFFFFFFu;
   }
   if (na == 0) return true;
   const int qrow = 16 * qs + c16;
+  u32x4* stg = reinterpret_cast<u32x4*>(lds + p.g[GQ].region);
 #pragma unroll
   for (int i = 0; i < AUMAX; ++i) {
     if (i >= na) continue;
@@ -638,85 +697,86 @@ __device__ bool ph_attn(KSP& p, int k, int l, int w) {
     const bool pre = c < p.KSp;
     const int s0 = pre ? 32 * c : p.P + 32 * (c - p.KSp);
     const int s1 = pre ? min(p.P, s0 + 32) : min(p.P + p.H, s0 + 32);
-    if (cw && 16 * qs < p.H) {
-      const auto qr = rsrc(sl + p.o_q);
-      u32x4 qf[KB];
+    // this wave's queries (all dims) and its share of the unit's key / value fragments
+    const auto qr = rsrc(sl + p.o_q);
+    u32x4 qf[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int tt = 2 * kb + (gq >> 1);
-        qf[kb] = ld16_if(qr, (uint32_t)((((j * (D / 16) + tt) * 64 + qrow) * 16 + (gq & 1) * 8) * 2), qrow < p.H);
-      }
-      floatx4 sacc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    for (int kb = 0; kb < KB; ++kb) {
+      const int tt = 2 * kb + (gq >> 1);
+      qf[kb] = act_ld16_if(qr, (uint32_t)((((j * (D / 16) + tt) * 64 + qrow) * 16 + (gq & 1) * 8) * 2), qrow < p.H);
+    }
+    u32x4 sf[PERW];
+    {
       const auto kpr = rsrc(p.pk + (size_t)l * p.P * p.Hkv * D);
       const auto kcr = rsrc(sl + p.o_k);
+      const uint8_t* vbase = pre ? reinterpret_cast<const uint8_t*>(p.vt + (size_t)(l * p.Hkv + kvh) * D * p.Ppad)
+                                 : sl + p.o_vt + (size_t)kvh * D * 64 * 2;
+      const int ld_keys = pre ? p.Ppad : 64;
+      const int kofs = pre ? 32 * c : 32 * (c - p.KSp);
+      const auto vr = rsrc(vbase);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int key = s0 + 16 * ks + c16;
-        const bool kok = key < s1;
-        u32x4 kf[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int tt = 2 * kb + (gq >> 1);
-          if (pre)
-            kf[kb] = ld16_if(kpr, (uint32_t)(((key * p.Hkv + kvh) * D + 8 * tt + (gq & 1) * (D / 2)) * 2), kok);
-          else
-            kf[kb] = ld16_if(kcr, (uint32_t)((((kvh * (D / 16) + tt) * 64 + (key - p.P)) * 16 + (gq & 1) * 8) * 2), kok);
-        }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sacc[ks] = MT<bf16>::mma(kf[kb], qf[kb], sacc[ks]);
-      }
-      // values for this wave's half of the dims (issued before the softmax)
-      u32x4 vf[DT];
-      {
-        const uint8_t* vbase = pre ? reinterpret_cast<const uint8_t*>(p.vt + (size_t)(l * p.Hkv + kvh) * D * p.Ppad)
-                                   : sl + p.o_vt + (size_t)kvh * D * 64 * 2;
-        const int ld_keys = pre ? p.Ppad : 64;
-        const int kofs = pre ? 32 * c : 32 * (c - p.KSp);
-        const auto vr = rsrc(vbase);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int dim = dh * (D / 2) + 16 * dt + c16;
-          vf[dt] = ld16_if(vr, (uint32_t)(((size_t)dim * ld_keys + kofs + 8 * gq) * 2), true);
+      for (int r = 0; r < PERW; ++r) {
+        const int fa = wv + NCW * r;
+        if (fa < NKF) {
+          const int ks = fa / KB, kb = fa % KB;
+          const int key = s0 + 16 * ks + c16, tt = 2 * kb + (gq >> 1);
+          const bool kok = key < s1;
+          sf[r] = pre ? ld16_if(kpr, (uint32_t)(((key * p.Hkv + kvh) * D + 8 * tt + (gq & 1) * (D / 2)) * 2), kok)
+                      : act_ld16_if(kcr, (uint32_t)((((kvh * (D / 16) + tt) * 64 + (key - p.P)) * 16 + (gq & 1) * 8) * 2), kok);
+        } else if (fa < NKF + NVF) {
+          const int dv = (fa - NKF) / DT, dt = (fa - NKF) % DT;
+          const int dim = dv * (D / 2) + 16 * dt + c16;
+          sf[r] = act_ld16_if(vr, (uint32_t)(((size_t)dim * ld_keys + kofs + 8 * gq) * 2), true);
         }
       }
-      float pr[8];
+    }
+    if (i > 0) cw_sync(p);   // the previous unit's readers are done with the staging area
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pr[e] = s0 + 4 * gq + e < s1 ? sacc[0][e] * scale : -INFINITY;
-        pr[4 + e] = s0 + 16 + 4 * gq + e < s1 ? sacc[1][e] * scale : -INFINITY;
-      }
-      float mx = pr[0];
+    for (int r = 0; r < PERW; ++r)
+      if (wv + NCW * r < NKF + NVF) stg[(wv + NCW * r) * 64 + lane] = sf[r];
+    cw_sync(p);
+    floatx4 sacc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, pr[e]);
-      mx = am_max4(mx);
-      float lsum = 0.f;
-      bf16x8 pb;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = fast_exp2(pr[e] - mx);
-        lsum += pe;
-        pb[e] = (bf16)pe;
-      }
-      lsum += __shfl_xor(lsum, 16);
-      lsum += __shfl_xor(lsum, 32);
-      const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
-      // the MFMAs run with every lane active (an MFMA reads its operands from
-      // the whole wave); only the stores of rows beyond H are masked
-      floatx4 o[DT];
+      for (int kb = 0; kb < KB; ++kb) sacc[ks] = MT<bf16>::mma(stg[(ks * KB + kb) * 64 + lane], qf[kb], sacc[ks]);
+    float pr[8];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = MT<bf16>::mma(vf[dt], pbu, floatx4{0, 0, 0, 0});
-      if (qrow < p.H) {
-        const size_t row = ((size_t)j * p.KS + c) * 64 + qrow;
+    for (int e = 0; e < 4; ++e) {
+      pr[e] = s0 + 4 * gq + e < s1 ? sacc[0][e] * scale : -INFINITY;
+      pr[4 + e] = s0 + 16 + 4 * gq + e < s1 ? sacc[1][e] * scale : -INFINITY;
+    }
+    float mx = pr[0];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          coh_st16(p.apart, (uint32_t)((row * D + dh * (D / 2) + 16 * dt + 4 * gq) * 4), as_u4(o[dt]));
-        if (dh == 0 && gq == 0)
-          coh_st8(p.aml, (uint32_t)(row * 8), u32x2{__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)});
-      }
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, pr[e]);
+    mx = am_max4(mx);
+    float lsum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(pr[e] - mx);
+      lsum += pe;
+      pb[e] = (bf16)pe;
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    const u32x4 pbu = __builtin_bit_cast(u32x4, pb);
+    // the MFMAs run with every lane active (an MFMA reads its operands from
+    // the whole wave); only the stores of rows beyond H are masked
+    floatx4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = MT<bf16>::mma(stg[(NKF + dh * DT + dt) * 64 + lane], pbu, floatx4{0, 0, 0, 0});
+    if (qrow < p.H) {
+      const size_t row = ((size_t)j * p.KS + c) * 64 + qrow;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        coh_st16(p.apart, (uint32_t)((row * D + dh * (D / 2) + 16 * dt + 4 * gq) * 4), as_u4(o[dt]));
+      if (dh == 0 && gq == 0)
+        coh_st8(p.aml, (uint32_t)(row * 8), u32x2{__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, lsum)});
     }
   }
   // the head's units meet: every split output of the head is stored
-  if (cw) vm_drain();
+  vm_drain();
   cw_sync(p);
   const unsigned inst = (unsigned)(k * p.L + l);
   if (threadIdx.x == 0) {
@@ -743,42 +803,45 @@ __device__ bool ph_attn(KSP& p, int k, int l, int w) {
   cw_sync(p);
   if (lds_ld(ctl3(p) + C_OK) == 0u) return false;
   // merge: unit (j, c) takes query rows c, c + KS, ...; one wave per row
-  if (cw) {
-    uint8_t* at = slab(p, k, l) + p.o_at;
+  uint8_t* at = slab(p, k, l) + p.o_at;
+  const auto apr = rsrc(p.apart);
+  const auto amr = rsrc(p.aml);
 #pragma unroll
-    for (int i = 0; i < AUMAX; ++i) {
-      if (i >= na) continue;
-      const int j = (int)(au[i] >> 8), c = (int)(au[i] & 0xFF);
-      for (int m = c + wv * p.KS; m < p.H; m += NCW * p.KS) {
-        const size_t base = (size_t)j * p.KS * 64 + m;   // row m of split 0; split s at + s * 64
-        float mi = -INFINITY, li = 0.f;
-        if (lane < p.KS) {
-          // whole-vector bit cast: casting single components of a loaded
-          // vector reads component 0 for every one of them
-          const floatx2 ml = __builtin_bit_cast(floatx2, coh_ld8(p.aml, (uint32_t)((base + (size_t)lane * 64) * 8)));
-          mi = ml[0];
-          li = ml[1];
-        }
+  for (int i = 0; i < AUMAX; ++i) {
+    if (i >= na) continue;
+    const int j = (int)(au[i] >> 8), c = (int)(au[i] & 0xFF);
+    for (int m = c + wv * p.KS; m < p.H; m += NCW * p.KS) {
+      const size_t base = (size_t)j * p.KS * 64 + m;   // row m of split 0; split s at + s * 64
+      floatx4 num = {0, 0, 0, 0};
+      float den = 0.f, mrun = -INFINITY;
+      for (int s0 = 0; s0 < p.KS; s0 += MERGE_MAX) {
+        // (max, sum) of split s0 + lane and the partial rows of every split of this pass, issued together
+        const u32x2 mlv = coh_ld8_if(amr, (uint32_t)((base + (size_t)(s0 + lane) * 64) * 8), lane < MERGE_MAX && s0 + lane < p.KS);
+        u32x4 ov[MERGE_MAX];
+#pragma unroll
+        for (int e = 0; e < MERGE_MAX; ++e)
+          ov[e] = coh_ld16_if(apr, (uint32_t)(((base + (size_t)(s0 + e) * 64) * D + 4 * lane) * 4), 4 * lane < D && s0 + e < p.KS);
+        // whole-vector bit cast: casting single components of a loaded
+        // vector reads component 0 for every one of them
+        const floatx2 ml = __builtin_bit_cast(floatx2, mlv);
+        const bool live = lane < MERGE_MAX && s0 + lane < p.KS;
+        const float mi = live ? ml[0] : -INFINITY;
         float mx = mi;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        const float wc = lane < p.KS ? fast_exp2(mi - mx) : 0.f;
-        const float den = warp_sum(wc * li);
-        if (4 * lane < D) {
-          const auto apr = rsrc(p.apart);
-          floatx4 num = {0, 0, 0, 0};
-          for (int s0 = 0; s0 < p.KS; s0 += 8) {
-            u32x4 ov[8];
+        const float mnew = fmaxf(mrun, mx);
+        const float resc = fast_exp2(mrun - mnew);   // 0 on the first pass
+        const float wc = live ? fast_exp2(mi - mnew) : 0.f;
+        den = den * resc + warp_sum(wc * (live ? ml[1] : 0.f));
+        num *= resc;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              ov[e] = coh_ld16_if(apr, (uint32_t)(((base + (size_t)(s0 + e) * 64) * D + 4 * lane) * 4), s0 + e < p.KS);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) num += __shfl(wc, (s0 + e) & 63) * as_f4(ov[e]);
-          }
-          const floatx4 o = num / den;
-          const int col = j * D + 4 * lane;
-          coh_st8(at, opo(m, col) * 2, u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
-        }
+        for (int e = 0; e < MERGE_MAX; ++e) num += __shfl(wc, e) * as_f4(ov[e]);
+        mrun = mnew;
+      }
+      if (4 * lane < D) {
+        const floatx4 o = num / den;
+        const int col = j * D + 4 * lane;
+        coh_st8(at, opo(m, col) * 2, u32x2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)});
       }
     }
   }
@@ -807,11 +870,27 @@ __global__ __launch_bounds__(NT) void k_stream(SP) {
     ct[C_CWB] = ct[C_FREE] = ct[C_LAND] = ct[C_ABORT] = ct[C_LFAIL] = 0u;
     if (p.trace && blockIdx.x == 0) p.trace[0] = p.trace[1] = p.trace[2] = __builtin_amdgcn_s_memrealtime();
   }
-  wg_sync();   // the last s_barrier: from here on the loader runs on its own
-  const int w = (int)ct[C_WID];
+  wg_sync();
+  const int w = __builtin_amdgcn_readfirstlane((int)ct[C_WID]);
   if (w < 0) return;
+  // the workgroup's unit entries of every phase, read from LDS from here on
+  {
+    const int t = threadIdx.x;
+    if (t < 4 * UMAX) {
+      KSG& g = p.g[t / UMAX];
+      const int i = t % UMAX;
+      ct[C_UNITS + t] = i < g.U ? g.units[w * g.U + i] : 0xFFFFFFFFu;
+    } else if (t < 4 * UMAX + AUMAX) {
+      const int i = t - 4 * UMAX;
+      ct[C_AUNITS + i] = i < p.AU ? p.attn_units[w * p.AU + i] : 0xFFFFFFFFu;
+    } else if (t < 4 * UMAX + AUMAX + IUMAX) {
+      const int i = t - 4 * UMAX - AUMAX;
+      ct[C_IUNITS + i] = i < p.IU ? p.in_units[w * p.IU + i] : 0xFFFFFFFFu;
+    }
+  }
+  wg_sync();   // the last s_barrier: from here on the loader runs on its own
   if (wv == LOADER) {
-    loader_run(p, w);
+    loader_run(p);
     return;
   }
   unsigned epoch = 0;
@@ -826,19 +905,20 @@ __global__ __launch_bounds__(NT) void k_stream(SP) {
   ph_in(p, 0, w);
   for (int k = 0; k < p.N; ++k) {
     for (int l = 0; l < p.L; ++l) {
-      const int q = 4 * (k * p.L + l);   // GEMM phase index of this layer's qkv
-      VFM_GBAR(q, q);
+      const int q = 4 * (k * p.L + l);   // fill (GEMM phase) index of this layer's qkv
+      const int z = 5 * (k * p.L + l);   // phase slots completed before this layer
+      VFM_GBAR(z, q);
       ph_gemm<GQ>(p, k, l, w);
-      VFM_GBAR(q + 1, -1);
+      VFM_GBAR(z + 1, -1);
       if (!ph_attn<D>(p, k, l, w)) return;
-      VFM_GBAR(q + 1, q + 1);
+      VFM_GBAR(z + 2, q + 1);
       ph_gemm<GO>(p, k, l, w);
-      VFM_GBAR(q + 2, q + 2);
+      VFM_GBAR(z + 3, q + 2);
       ph_gemm<GG>(p, k, l, w);
-      VFM_GBAR(q + 3, q + 3);
+      VFM_GBAR(z + 4, q + 3);
       ph_gemm<GD>(p, k, l, w);
     }
-    const int done = 4 * (k + 1) * p.L;
+    const int done = 5 * (k + 1) * p.L;
     VFM_GBAR(done, -1);
     ph_out(p, k, w);
     if (k + 1 < p.N) {

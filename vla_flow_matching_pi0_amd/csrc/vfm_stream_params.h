@@ -19,8 +19,8 @@ constexpr int MAXJ = 16;               // act fragments per wave per GEMM (K sli
 constexpr int UMAX = 4;                // GEMM units per workgroup
 constexpr int AUMAX = 2;               // attention units per workgroup
 constexpr int SMAX = 8;                // K splits of the o and down projections
-constexpr int CTL = 256;               // control words
-constexpr int DMA_CAP = 56;            // loader: most direct-to-LDS loads in flight
+constexpr int CTL = 256;               // bytes of LDS control words (64 words)
+constexpr int DMA_CAP = 56;            // loader: default of the most direct-to-LDS loads in flight
 constexpr long SPIN_LIMIT = 1L << 21;
 
 enum { GQ = 0, GO = 1, GG = 2, GD = 3 };
@@ -30,8 +30,13 @@ constexpr int BAR_WORDS_S = BW_CTR + 64 * N_CTR;
 // control words in LDS: workgroup id, barrier outcome, last-arriver flags
 // (UMAX), compute-wave barrier counter, GEMM phases completed (regions the
 // loader may refill), fills landed, stop request to the loader, failed
-// weight wait, loader unit entries (4 x UMAX)
-enum { C_WID = 0, C_OK = 1, C_LAST = 4, C_CWB = 8, C_FREE = 9, C_LAND = 10, C_ABORT = 11, C_LFAIL = 12, C_UNITS = 16 };
+// weight wait, the workgroup's unit entries: GEMMs (4 x UMAX), attention
+// (AUMAX), in projection (IUMAX)
+constexpr int IUMAX = 4;
+enum { C_WID = 0, C_OK = 1, C_LAST = 4, C_CWB = 8, C_FREE = 9, C_LAND = 10, C_ABORT = 11, C_LFAIL = 12, C_UNITS = 16,
+       C_AUNITS = 32, C_IUNITS = 36 };
+static_assert(C_IUNITS + IUMAX <= CTL / 4, "control words exceed their LDS block");
+static_assert(C_UNITS + 4 * UMAX <= C_AUNITS && C_AUNITS + AUMAX <= C_IUNITS, "control word overlap");
 
 struct SGemm {
   int T, S, nkb, nkbs, U;    // 16-column tiles, K splits, 32-K blocks (all, per split), units per workgroup
@@ -74,6 +79,7 @@ struct SP {
   unsigned* herr;               // host-mapped copy of the error word (may be null)
   unsigned long long* trace;    // optional timeline of workgroup 0's barriers
   int stop_after;               // diagnostics: leave after this barrier (0: run the whole loop)
+  int dma_cap;                  // loader: most direct-to-LDS loads in flight (1 .. 63)
 };
 
 hipError_t stream_launch(const SP& p, size_t lds, hipStream_t st, bool cooperative);

@@ -74,11 +74,14 @@ bool stream_plan(const StreamShape& s, int G, const int splits[4], StreamPlan* o
     if (!plan_gemm(T[gi], K[gi], splits[gi], G, P.per_xcd, umax[gi], P.g[gi], why, names[gi])) return false;
     if ((gi == GQ || gi == GG) && splits[gi] != 1) { *why = "qkv and gate/up run unsplit"; return false; }
   }
-  if (!plan_gemm(s.W / 16, 0, 1, G, P.per_xcd, 4, P.in, why, "in")) return false;
+  if (!plan_gemm(s.W / 16, 0, 1, G, P.per_xcd, IUMAX, P.in, why, "in")) return false;
   int off = 0, umx = 1;
   for (int gi = 0; gi < 4; ++gi) {
     P.regions[gi] = off;
-    off += P.g[gi].U * P.g[gi].nkbs * 1024;
+    int bytes = P.g[gi].U * P.g[gi].nkbs * 1024;
+    // attention stages one unit's keys and values (4 d / 32 fragments of 1 KiB) in the qkv region
+    if (gi == GQ) bytes = std::max(bytes, 4 * (s.d / 32) * 1024);
+    off += bytes;
     umx = std::max(umx, P.g[gi].U);
   }
   P.scratch = off;
@@ -306,7 +309,7 @@ const StreamPlan& stream_plan_of(const StreamState* s) { return s->plan; }
 vfm_status stream_run(StreamState* s, int P, const void* pk, const void* pv, const float* noise, const float* state,
                       float* x, const float* in_w, const float* in_b, const float* st_w, const float* st_b,
                       const float* out_w, const float* out_b, const float* rope, bool cooperative,
-                      unsigned long long* trace, int stop_after, hipStream_t st) {
+                      unsigned long long* trace, const StreamTune& tune, hipStream_t st) {
   const StreamShape& sh = s->s;
   const StreamPlan& pl = s->plan;
   if (P != s->cur_P) {
@@ -354,7 +357,8 @@ vfm_status stream_run(StreamState* s, int P, const void* pk, const void* pv, con
   p.apart = s->apart; p.aml = s->aml;
   p.bar = s->bar; p.err = s->err; p.herr = s->herr_dev;
   p.trace = trace;
-  p.stop_after = stop_after;
+  p.stop_after = tune.stop_after;
+  p.dma_cap = tune.dma_cap;
   const hipError_t e = stream_launch(p, (size_t)pl.lds, st, cooperative);
   if (e != hipSuccess) return report(VFM_E_HIP, "streaming kernel launch: %s", hipGetErrorString(e));
   return VFM_OK;

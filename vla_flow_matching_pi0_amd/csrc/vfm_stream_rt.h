@@ -41,6 +41,12 @@ bool stream_attn_plan(const StreamShape& s, int G, int per_xcd, int P, std::vect
 
 struct StreamState;
 
+// Launch settings that do not change results.
+struct StreamTune {
+  int stop_after = 0;        // diagnostics: leave after this barrier (0: the whole loop)
+  int dma_cap = DMA_CAP;     // loader: most direct-to-LDS loads in flight, 1 .. 63
+};
+
 vfm_status stream_create(const StreamShape& shape, const uint8_t* const* wq, const uint8_t* const* wo,
                          const uint8_t* const* wg, const uint8_t* const* wd, const float* mod, hipStream_t st,
                          StreamState** out, std::string* why);
@@ -50,7 +56,7 @@ bool stream_accepts(const StreamState* s, int P, std::string* why);
 vfm_status stream_run(StreamState* s, int P, const void* pk, const void* pv, const float* noise, const float* state,
                       float* x, const float* in_w, const float* in_b, const float* st_w, const float* st_b,
                       const float* out_w, const float* out_b, const float* rope, bool cooperative,
-                      unsigned long long* trace, int stop_after, hipStream_t st);
+                      unsigned long long* trace, const StreamTune& tune, hipStream_t st);
 // Device-side failure flagged by an earlier launch (host-mapped word; no synchronisation).
 bool stream_failed(const StreamState* s);
 // Clear the failure and every counter a failed launch may have left behind (enqueued on st).
