@@ -164,7 +164,7 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // [1] error flag, [64 + 64 * g] arrival count of group g (g = block % 8).
 // Counts are monotonic within one launch (zeroed before it). Spins are
 // bounded; on timeout the error flag is raised and every block returns.
-constexpr long BARRIER_SPIN_LIMIT = 1L << 22;
+constexpr long BARRIER_SPIN_LIMIT = BARRIER_SPIN_LIMIT_HOST;
 
 __device__ __forceinline__ unsigned ld_agent(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -186,11 +186,13 @@ struct NoHook {
 // count, so reaching the target proves every workgroup arrived. `hook` runs
 // in every thread between arrival and wait: work that does not depend on the
 // other workgroups (issuing loads of read-only data) overlaps the wait.
-// bar[1] is a sticky error word: a wait that exceeds BARRIER_SPIN_LIMIT sets
-// it, and every waiter gives up once it is set (returns false).
+// bar[1] is a sticky error word: a wait that exceeds `spin_limit` polls sets
+// it, and every waiter gives up once it is set (returns false). Barrier
+// `fail_epoch` (diagnostics, 0: none) waits for one arrival more than the grid
+// holds, so its bounded wait gives up and every workgroup exits normally.
 template <typename HOOK = NoHook>
-__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace = nullptr,
-                                             const HOOK& hook = HOOK()) {
+__device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace, long spin_limit,
+                                             int fail_epoch, const HOOK& hook = HOOK()) {
   __shared__ unsigned s_ok;
   ++epoch;
   __builtin_amdgcn_s_waitcnt(0);   // this wave's stores (and loads) have completed
@@ -203,7 +205,7 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
   hook();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const unsigned target = epoch * gridDim.x;
+    const unsigned target = epoch * gridDim.x + ((int)epoch == fail_epoch ? 1u : 0u);
     unsigned ok = 1;
     long spins = 0;
     for (;;) {
@@ -218,7 +220,7 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
       if ((++spins & 1023) == 0) {
         unsigned err = lane == 0 ? ld_agent(&bar[1]) : 0u;
         err = __shfl(err, 0);
-        if (err != 0u || spins > BARRIER_SPIN_LIMIT) {
+        if (err != 0u || spins > spin_limit) {
           if (lane == 0) __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;

@@ -14,6 +14,7 @@ constexpr int MAX_KSPLIT = 16;     // K splits of the residual GEMMs
 // arrival counters, each on its own 256-byte line (word 64 + 64 c).
 constexpr int BAR_COUNTERS = 64;
 constexpr int BAR_WORDS = 64 + 64 * BAR_COUNTERS;
+constexpr long BARRIER_SPIN_LIMIT_HOST = 1L << 22;   // default polls before a device-wide wait gives up
 
 enum Phase {
   PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_TMLP, PH_COUNT
@@ -62,6 +63,8 @@ struct VP {
   float* amax;             // calibration: [L][4 GEMMs] largest |input| (null: off)
   unsigned* bar;           // grid-barrier words
   unsigned long long* trace;  // optional phase timeline of the persistent kernel (null: off)
+  long spin_limit;         // polls before a barrier wait gives up
+  int fail_epoch;          // diagnostics: barrier whose target is never reached (0: none)
 };
 
 // Kernel sets: activation type x weight format (x calibration).

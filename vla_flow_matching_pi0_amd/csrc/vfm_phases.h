@@ -1595,11 +1595,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
   const int wg = blockIdx.x, nwg = gridDim.x;
   if (p.trace && wg == 0 && threadIdx.x == 0) p.trace[0] = p.trace[1] = __builtin_amdgcn_s_memrealtime();
-#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace)) return; } while (0)
+#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch)) return; } while (0)
   // The next GEMM's first weight pass is loaded while the workgroup waits at
   // the barrier before it: weights do not depend on the other workgroups.
 #define VFM_BAR_PF(WHICH, LAYER) \
-  do { if (!grid_barrier(p.bar, epoch, p.trace, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
+  do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
   ph_boundary<T, WF>(p, -1, 0, wg, nwg);
   if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
@@ -1621,7 +1621,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
       {
         APre<T, D> apre;
-        if (!grid_barrier(p.bar, epoch, p.trace, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
+        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
         ph_attn<T, D, true>(p, k, l, wg, nwg, apre);
       }
       VFM_BAR();

@@ -102,6 +102,8 @@ struct vfm_expert {
   int ss_P = -1;                         // prefix length of the last stream-eligibility check
   bool ss_P_ok = false;
   vfm::sk::StreamTune ss_tune;          // streaming kernel launch settings (diagnostics, loader depth)
+  long spin_limit = vfm::BARRIER_SPIN_LIMIT_HOST;   // polls before a device-wide wait gives up
+  int fail_barrier = 0;                  // diagnostics: barrier made unreachable (0: none)
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
@@ -542,6 +544,8 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   p.off_attn = x->off_attn; p.off_xnm = x->off_xnm; p.off_act = x->off_act; p.bar = x->bar;
   const int mode = launch_mode_of(x, B, P);
   p.trace = mode == 0 ? x->trace : nullptr;
+  p.spin_limit = x->spin_limit;
+  p.fail_epoch = mode == 0 ? x->fail_barrier : 0;
 
   {
     int nwg = x->coop_grid;
@@ -929,6 +933,23 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     x->ss_tune.stop_after = (int)n;
     return VFM_OK;
   }
+  if (k == "barrier_spin_limit") {
+    char* end = nullptr;
+    const long long n = std::strtoll(value, &end, 10);
+    if (end == value || *end || n < 1024 || n > (1LL << 40))
+      return fail(VFM_E_INVALID_ARG, "barrier_spin_limit must be an integer in [1024, 2^40]");
+    x->spin_limit = (long)n;
+    x->ss_tune.spin_limit = (long)n;
+    return VFM_OK;
+  }
+  if (k == "fail_barrier") {
+    char* end = nullptr;
+    const long n = std::strtol(value, &end, 10);
+    if (end == value || *end || n < 0) return fail(VFM_E_INVALID_ARG, "fail_barrier must be a barrier index >= 0");
+    x->fail_barrier = (int)n;
+    x->ss_tune.fail_epoch = (int)n;
+    return VFM_OK;
+  }
   if (k == "stream_dma_cap") {
     char* end = nullptr;
     const long n = std::strtol(value, &end, 10);
@@ -1086,6 +1107,8 @@ vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
   x->KW = kw;
   if (st != VFM_OK) { release(); return st; }
   p.trace = nullptr;
+  p.spin_limit = x->spin_limit;
+  p.fail_epoch = 0;
   p.amax = amax;
   hipError_t e = hipMemsetAsync(amax, 0, (size_t)std::max(L, 1) * 16, s);
   for (int l = 0; l < L && e == hipSuccess; ++l) {

@@ -132,7 +132,8 @@ __device__ __forceinline__ bool gbar(KSP& p, unsigned& epoch, int done, int need
       __hip_atomic_fetch_add(&p.bar[BW_CTR + 64 * (blockIdx.x % N_CTR)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       lds_st(ct + C_FREE, (unsigned)done);
     }
-    const unsigned target = epoch * (unsigned)p.G;
+    // barrier fail_epoch (diagnostics) waits for one arrival more than the grid holds
+    const unsigned target = epoch * (unsigned)p.G + ((int)epoch == p.fail_epoch ? 1u : 0u);
     unsigned ok = 1;
     long spins = 0;
     for (;;) {
@@ -143,7 +144,7 @@ __device__ __forceinline__ bool gbar(KSP& p, unsigned& epoch, int done, int need
       if ((++spins & 255) == 0) {
         unsigned e = lane == 0 ? ld_dev(p.err) : 0u;
         e = __shfl(e, 0);
-        if (e != 0u || spins > SPIN_LIMIT) {
+        if (e != 0u || spins > p.spin_limit) {
           if (lane == 0) raise_err(p, 1u);
           ok = 0;
           break;
@@ -482,55 +483,103 @@ __device__ __forceinline__ void ph_gemm(KSP& p, int k, int l, int w) {
   }
   if (nu == 0) return;
   const int wv = wave_id(), lane = lane_id(), c16 = lane & 15, gq = lane >> 4;
-  const bool cw = wv < NCW;
   const int st = wv & 3, kp = (wv >> 2) & 1;
+  const bool ep = kp == 0;   // waves 0..3 finish the tiles
   const int split = (int)(ue[0] & 0xFF);
   const int kb0 = split * g.nkbs;
   uint8_t* sl = slab(p, k, l);
   const int m = 16 * st + c16;
   const bool mok = m < p.H;
-  floatx4 acc[UMAX];
+  const int W = p.W;
+  int tile[UMAX];
 #pragma unroll
-  for (int i = 0; i < UMAX; ++i) acc[i] = floatx4{0, 0, 0, 0};
-  float r = 1.0f;
-  if (cw) {
-    const auto ars = rsrc(gemm_input<GI>(p, sl));
-    const int nj = g.nkbs >> 1;
-    // the workgroups of an XCD all read the same activation; each starts at
-    // a different k block (rotation by its slot) so that they do not queue
-    // on the same L2 lines at the same time
-    const int rot = (w % p.per_xcd) % nj;
-    u32x4 a[MAXJ];
+  for (int i = 0; i < UMAX; ++i) tile[i] = (int)(ue[i < nu ? i : 0] >> 8);
+  // activation fragments of this wave's token subtile and k-block parity
+  const auto ars = rsrc(gemm_input<GI>(p, sl));
+  const int nj = g.nkbs >> 1;
+  // the workgroups of an XCD all read the same activation; each starts at
+  // a different k block (rotation by its slot)
+  const int rot = (w % p.per_xcd) % nj;
+  u32x4 a[MAXJ];
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int jr = j + rot < nj ? j + rot : j + rot - nj;
-      const int kb = kb0 + kp + 2 * jr;
-      a[j] = act_ld16_if(ars, (uint32_t)((((kb * 64 + m) << 5) + 8 * gq) * 2), mok && j < nj);
-    }
-    if constexpr (GI == GQ || GI == GG) r = row_rms_inv(p, sl + (GI == GQ ? p.o_ssa : p.o_ssm), m);
-    const uint8_t* wr = reinterpret_cast<const uint8_t*>(lds) + g.region + lane * 16;
+  for (int j = 0; j < MAXJ; ++j) {
+    const int jr = j + rot < nj ? j + rot : j + rot - nj;
+    const int kb = kb0 + kp + 2 * jr;
+    a[j] = act_ld16_if(ars, (uint32_t)((((kb * 64 + m) << 5) + 8 * gq) * 2), mok && j < nj);
+  }
+  // everything the epilogue reads, issued now so that it lands during the
+  // contraction: the shift tables (qkv, gate/up), the rotary table (qkv),
+  // the residual, its gate and the next norm's scale (o, down)
+  floatx4 e0[UMAX], e1[UMAX], e2[UMAX];
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      if (j < nj) {
-        const int jr = j + rot < nj ? j + rot : j + rot - nj;
+  for (int i = 0; i < UMAX; ++i) e0[i] = e1[i] = e2[i] = floatx4{0, 0, 0, 0};
+  const int nrm_g = GI == GO ? 2 * l : 2 * l + 1;                 // norm whose gate scales this residual
+  const bool next = GI == GO || l + 1 < p.L;                       // y of a following norm to write
+  const int nrm_n = GI == GO ? 2 * l + 1 : 2 * l + 2;              // that norm
+  if (ep && mok) {
 #pragma unroll
-        for (int i = 0; i < UMAX; ++i) {
-          if (i < nu) {
-            const u32x4 wf = *reinterpret_cast<const u32x4*>(wr + (i * g.nkbs + kp + 2 * jr) * 1024);
-            acc[i] = MT<bf16>::mma(wf, a[j], acc[i]);
-          }
+    for (int i = 0; i < UMAX; ++i) {
+      if (i >= nu) continue;
+      const int col0 = tile[i] * 16;
+      if constexpr (GI == GQ) {
+        const int d = p.d, Nq = (p.Hq + 2 * p.Hkv) * d;
+        e0[i] = as_f4(ro_ld16(p.shw_q + ((size_t)k * p.L + l) * Nq + col0 + 4 * gq));
+        if (col0 / d < p.Hq + p.Hkv) {
+          const int j0 = ((col0 % d) / 16) * 8 + 2 * gq;
+          e1[i] = as_f4(ro_ld16(p.rope + ((size_t)m * (d / 2) + j0) * 2));
         }
+      } else if constexpr (GI == GG) {
+        e0[i] = as_f4(ro_ld16(p.shw_g + ((size_t)k * p.L + l) * 2 * p.F + col0 + 4 * gq));
+      } else {
+        const float* modk = p.mod + (size_t)k * (2 * p.L + 1) * 3 * W;
+        const int c = col0 + 4 * gq;
+        e0[i] = as_f4(coh_ld16(p.h, (uint32_t)((m * W + c) * 4)));
+        e1[i] = as_f4(ro_ld16(modk + ((size_t)nrm_g * 3 + 2) * W + c));
+        if (next) e2[i] = as_f4(ro_ld16(modk + (size_t)nrm_n * 3 * W + c));
       }
     }
   }
+  float r = 1.0f;
+  if constexpr (GI == GQ || GI == GG) r = row_rms_inv(p, sl + (GI == GQ ? p.o_ssa : p.o_ssm), m);
+  // contraction: the weight fragments of step j + PF are read from LDS while
+  // step j multiplies; the reads are unconditional (clamped to the unit's
+  // last block), only the MFMAs depend on the slice length
+  constexpr int PF = 2;
+  const uint8_t* wr = reinterpret_cast<const uint8_t*>(lds) + g.region + lane * 16;
+  const int njm1 = nj - 1;
+  auto wblk = [&](int j, int i) -> u32x4 {
+    const int jj = j < njm1 ? j : njm1;
+    const int jr = jj + rot < nj ? jj + rot : jj + rot - nj;
+    const int ii = i < nu ? i : nu - 1;
+    return *reinterpret_cast<const u32x4*>(wr + (ii * g.nkbs + kp + 2 * jr) * 1024);
+  };
+  floatx4 acc[UMAX];
+#pragma unroll
+  for (int i = 0; i < UMAX; ++i) acc[i] = floatx4{0, 0, 0, 0};
+  u32x4 wq[PF + 1][UMAX];
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) wq[j][i] = wblk(j, i);
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    if (j + PF < MAXJ) {
+#pragma unroll
+      for (int i = 0; i < UMAX; ++i) wq[(j + PF) % (PF + 1)][i] = wblk(j + PF, i);
+    }
+    if (j < nj) {
+#pragma unroll
+      for (int i = 0; i < UMAX; ++i)
+        if (i < nu) acc[i] = MT<bf16>::mma(wq[j % (PF + 1)][i], a[j], acc[i]);
+    }
+  }
   floatx4* scr = reinterpret_cast<floatx4*>(lds + p.scratch);
-  if (cw && kp == 1) {
+  if (kp == 1) {
 #pragma unroll
     for (int i = 0; i < UMAX; ++i)
       if (i < nu) scr[(i * 4 + st) * 64 + lane] = acc[i];
   }
   cw_sync(p);
-  const bool ep = cw && kp == 0;   // waves 0..3 finish the tiles
   if (ep) {
 #pragma unroll
     for (int i = 0; i < UMAX; ++i)
@@ -538,28 +587,25 @@ __device__ __forceinline__ void ph_gemm(KSP& p, int k, int l, int w) {
   }
   if constexpr (GI == GQ) {
     if (ep) {
-      const int d = p.d, hd = d / 2, Nq = (p.Hq + 2 * p.Hkv) * d;
-      const float* shw = p.shw_q + ((size_t)k * p.L + l) * Nq;
+      const int d = p.d;
 #pragma unroll
       for (int i = 0; i < UMAX; ++i) {
         if (i >= nu) continue;
-        const int tile = (int)(ue[i] >> 8);
-        const int col0 = tile * 16;
-        const floatx4 v = r * acc[i] + as_f4(ro_ld16(shw + col0 + 4 * gq));
+        const int col0 = tile[i] * 16;
+        const floatx4 v = r * acc[i] + e0[i];
         const int head = col0 / d, tt = (col0 % d) / 16;
         if (head < p.Hq + p.Hkv) {
           if (!mok) continue;
           // packed lane order (x_j, x_j+1, x_j+d/2, x_j+1+d/2), j = 8 tt + 2 g
-          const int j0 = tt * 8 + 2 * gq;
-          const floatx4 rot = as_f4(ro_ld16(p.rope + ((size_t)m * hd + j0) * 2));
-          const float y0 = v.x * rot[0] - v.z * rot[1], y0h = v.z * rot[0] + v.x * rot[1];
-          const float y1 = v.y * rot[2] - v.w * rot[3], y1h = v.w * rot[2] + v.y * rot[3];
+          const floatx4 rt = e1[i];
+          const float y0 = v.x * rt[0] - v.z * rt[1], y0h = v.z * rt[0] + v.x * rt[1];
+          const float y1 = v.y * rt[2] - v.w * rt[3], y1h = v.w * rt[2] + v.y * rt[3];
           const bool isq = head < p.Hq;
           uint8_t* dst = sl + (isq ? p.o_q : p.o_k);
           const int hb = isq ? head : head - p.Hq;
-          const uint32_t e0 = (uint32_t)(((hb * (d / 16) + tt) * 64 + m) * 16 + 2 * gq);
-          coh_st4(dst, e0 * 2, pack_bf16x2(y0, y1));
-          coh_st4(dst, (e0 + 8) * 2, pack_bf16x2(y0h, y1h));
+          const uint32_t o0 = (uint32_t)(((hb * (d / 16) + tt) * 64 + m) * 16 + 2 * gq);
+          coh_st4(dst, o0 * 2, pack_bf16x2(y0, y1));
+          coh_st4(dst, (o0 + 8) * 2, pack_bf16x2(y0h, y1h));
         } else {
           // values transposed: vt[kvh][dim][key'] with the key permutation of the PV operand
           const int kvh = head - p.Hq - p.Hkv;
@@ -576,45 +622,29 @@ __device__ __forceinline__ void ph_gemm(KSP& p, int k, int l, int w) {
     }
   } else if constexpr (GI == GG) {
     if (ep && mok) {
-      const float* shw = p.shw_g + ((size_t)k * p.L + l) * 2 * p.F;
 #pragma unroll
       for (int i = 0; i < UMAX; ++i) {
         if (i >= nu) continue;
-        const int tile = (int)(ue[i] >> 8);
-        const floatx4 v = r * acc[i] + as_f4(ro_ld16(shw + tile * 16 + 4 * gq));
+        const floatx4 v = r * acc[i] + e0[i];
         // packed lane order (gate f, up f, gate f+1, up f+1), f = 8 tile + 2 g
-        const int f0 = tile * 8 + 2 * gq;
+        const int f0 = tile[i] * 8 + 2 * gq;
         const float a0 = gelu_tanh(v.x) * v.y, a1 = gelu_tanh(v.z) * v.w;
         coh_st4(sl + p.o_act, opo(m, f0) * 2, pack_bf16x2(a0, a1));
       }
     }
   } else {
     // split GEMM: partial sums, then the last unit of each tile finishes it
-    const int W = p.W, S = g.S;
-    const int nrm_g = GI == GO ? 2 * l : 2 * l + 1;                 // norm whose gate scales this residual
-    const bool next = GI == GO || l + 1 < p.L;                       // y of a following norm to write
-    const int nrm_n = GI == GO ? 2 * l + 1 : 2 * l + 2;              // that norm
-    const float* modk = p.mod + (size_t)k * (2 * p.L + 1) * 3 * W;
-    floatx4 hv[UMAX], gate[UMAX], scn[UMAX];
-#pragma unroll
-    for (int i = 0; i < UMAX; ++i) hv[i] = gate[i] = scn[i] = floatx4{0, 0, 0, 0};
+    const int S = g.S;
     if (ep && mok) {
 #pragma unroll
-      for (int i = 0; i < UMAX; ++i) {
-        if (i >= nu) continue;
-        const int tile = (int)(ue[i] >> 8);
-        const int c = tile * 16 + 4 * gq;
-        coh_st16(g.part, (uint32_t)((((split * g.T + tile) * 64 + m) * 16 + 4 * gq) * 4), as_u4(acc[i]));
-        hv[i] = as_f4(coh_ld16(p.h, (uint32_t)((m * W + c) * 4)));
-        gate[i] = as_f4(ro_ld16(modk + ((size_t)nrm_g * 3 + 2) * W + c));
-        scn[i] = next ? as_f4(ro_ld16(modk + (size_t)nrm_n * 3 * W + c)) : floatx4{0, 0, 0, 0};
-      }
+      for (int i = 0; i < UMAX; ++i)
+        if (i < nu)
+          coh_st16(g.part, (uint32_t)((((split * g.T + tile[i]) * 64 + m) * 16 + 4 * gq) * 4), as_u4(acc[i]));
     }
-    if (cw) vm_drain();
+    vm_drain();
     cw_sync(p);
     if ((int)threadIdx.x < nu) {
-      const int tile = (int)(ue[threadIdx.x] >> 8);
-      const unsigned old = __hip_atomic_fetch_add(&g.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned old = __hip_atomic_fetch_add(&g.cnt[tile[threadIdx.x]], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ctl3(p)[C_LAST + threadIdx.x] = (old + 1u) % (unsigned)S == 0u ? 1u : 0u;
     }
     cw_sync(p);
@@ -624,29 +654,28 @@ __device__ __forceinline__ void ph_gemm(KSP& p, int k, int l, int w) {
 #pragma unroll
       for (int i = 0; i < UMAX; ++i) {
         if (i >= nu || ctl3(p)[C_LAST + i] == 0u) continue;
-        const int tile = (int)(ue[i] >> 8);
-        const int c = tile * 16 + 4 * gq;
+        const int c = tile[i] * 16 + 4 * gq;
         u32x4 pv[SMAX];
 #pragma unroll
         for (int s = 0; s < SMAX; ++s)
-          pv[s] = coh_ld16_if(pr, (uint32_t)((((s * g.T + tile) * 64 + m) * 16 + 4 * gq) * 4), mok && s < S && s != split);
+          pv[s] = coh_ld16_if(pr, (uint32_t)((((s * g.T + tile[i]) * 64 + m) * 16 + 4 * gq) * 4), mok && s < S && s != split);
         // splits added in their fixed order 0 .. S-1 whichever one arrived
         // last, so the result does not depend on the arrival order
         floatx4 sum = {0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < SMAX; ++s)
           if (s < S) sum += s == split ? acc[i] : as_f4(pv[s]);
-        const floatx4 hn = hv[i] + gate[i] * sum;
+        const floatx4 hn = e0[i] + e1[i] * sum;
         float ss = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
         if (mok) {
           coh_st16(p.h, (uint32_t)((m * W + c) * 4), as_u4(hn));
           if (next) {
-            const floatx4 y = hn * (1.0f + scn[i]);
+            const floatx4 y = hn * (1.0f + e2[i]);
             coh_st8(sln + (GI == GO ? p.o_ym : p.o_ya), opo(m, c) * 2, u32x2{pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)});
             if (gq == 0)
-              coh_st4(sln + (GI == GO ? p.o_ssm : p.o_ssa), (uint32_t)((m * (W / 16) + tile) * 4), __builtin_bit_cast(uint32_t, ss));
+              coh_st4(sln + (GI == GO ? p.o_ssm : p.o_ssa), (uint32_t)((m * (W / 16) + tile[i]) * 4), __builtin_bit_cast(uint32_t, ss));
           }
         }
       }
@@ -790,7 +819,7 @@ __device__ __forceinline__ bool ph_attn(KSP& p, int k, int l, int w) {
       const unsigned target = (inst + 1u) * (unsigned)p.KS;
       long spins = 0;
       while (ld_dev(&p.hcnt[au[i] >> 8]) < target) {
-        if ((++spins & 255) == 0 && (ld_dev(p.err) != 0u || spins > SPIN_LIMIT)) {
+        if ((++spins & 255) == 0 && (ld_dev(p.err) != 0u || spins > p.spin_limit)) {
           raise_err(p, 2u);
           ok = 0;
           break;

@@ -16,7 +16,7 @@ constexpr int NT = (NCW + 1) * 64;     // + the loader wave
 constexpr int LOADER = NCW;
 constexpr int NXCD = 8;
 constexpr int MAXJ = 16;               // act fragments per wave per GEMM (K slice <= 1024)
-constexpr int UMAX = 4;                // GEMM units per workgroup
+constexpr int UMAX = 2;                // GEMM units per workgroup
 constexpr int AUMAX = 2;               // attention units per workgroup
 constexpr int SMAX = 8;                // K splits of the o and down projections
 constexpr int CTL = 256;               // bytes of LDS control words (64 words)
@@ -80,6 +80,8 @@ struct SP {
   unsigned long long* trace;    // optional timeline of workgroup 0's barriers
   int stop_after;               // diagnostics: leave after this barrier (0: run the whole loop)
   int dma_cap;                  // loader: most direct-to-LDS loads in flight (1 .. 63)
+  int fail_epoch;               // diagnostics: barrier whose target is never reached (0: none)
+  long spin_limit;              // polls before a device-wide or head wait gives up
 };
 
 hipError_t stream_launch(const SP& p, size_t lds, hipStream_t st, bool cooperative);

@@ -66,7 +66,7 @@ bool stream_plan(const StreamShape& s, int G, const int splits[4], StreamPlan* o
   if (s.L < 1 || s.L > MAX_LAYERS) { *why = "layer count"; return false; }
   if (s.Hq % s.Hkv) { *why = "query heads not a multiple of KV heads"; return false; }
   const int Nq = (s.Hq + 2 * s.Hkv) * s.d;
-  const int umax[4] = {2, 2, UMAX, 2};
+  const int umax[4] = {UMAX, UMAX, UMAX, UMAX};
   const int T[4] = {Nq / 16, s.W / 16, 2 * s.F / 16, s.W / 16};
   const int K[4] = {s.W, s.Hq * s.d, s.W, s.F};
   const char* names[4] = {"qkv", "o", "gate/up", "down"};
@@ -359,6 +359,8 @@ vfm_status stream_run(StreamState* s, int P, const void* pk, const void* pv, con
   p.trace = trace;
   p.stop_after = tune.stop_after;
   p.dma_cap = tune.dma_cap;
+  p.fail_epoch = tune.fail_epoch;
+  p.spin_limit = tune.spin_limit;
   const hipError_t e = stream_launch(p, (size_t)pl.lds, st, cooperative);
   if (e != hipSuccess) return report(VFM_E_HIP, "streaming kernel launch: %s", hipGetErrorString(e));
   return VFM_OK;

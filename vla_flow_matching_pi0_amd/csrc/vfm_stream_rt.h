@@ -45,6 +45,8 @@ struct StreamState;
 struct StreamTune {
   int stop_after = 0;        // diagnostics: leave after this barrier (0: the whole loop)
   int dma_cap = DMA_CAP;     // loader: most direct-to-LDS loads in flight, 1 .. 63
+  int fail_epoch = 0;        // diagnostics: barrier made unreachable (0: none)
+  long spin_limit = SPIN_LIMIT;   // polls before a device-wide or head wait gives up
 };
 
 vfm_status stream_create(const StreamShape& shape, const uint8_t* const* wq, const uint8_t* const* wo,
