@@ -350,6 +350,25 @@ vfm_status vfm_prefix_create(const vfm_prefix_config* cfg, const vfm_tensor* wei
 vfm_status vfm_prefix_run(vfm_prefix* pre, const void* embeds, int32_t batch, int32_t prefix_len,
                           void* prefix_k, void* prefix_v, void* stream);
 
+/* vfm_prefix_run for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same pass with the same arguments and results, but its workspace
+ * (residual stream, K-split partial sums, normalised and attention operands,
+ * activations, queries, transposed values, rotary table) lives in one static
+ * 64 MiB device array per GPU instead of the producer's buffers. It calls no
+ * hipMalloc, hipFree or allocating library routine; the array's address is
+ * looked up once per device on the first call there. Workspace needed:
+ * round_up(B P, 128) x (W (6 + 4 S) + 4 Hq d + 2 F) bytes (S the K splits,
+ * at most 8) + B Hkv d round_up(P, 32) x 2 + P d x 4 bytes, each piece
+ * rounded up to 256; more than 64 MiB fails with VFM_E_UNSUPPORTED before
+ * any launch. Every call on a GPU shares that GPU's array and clears what
+ * must start at zero itself; calls that overlap on one GPU (different
+ * streams, different producers) race and must be ordered by the caller.
+ * Errors: those of vfm_prefix_run, VFM_E_UNSUPPORTED, VFM_E_HIP (symbol
+ * lookup or launch failure). */
+vfm_status vfm_prefix_run_noalloc(vfm_prefix* pre, const void* embeds, int32_t batch, int32_t prefix_len,
+                                  void* prefix_k, void* prefix_v, void* stream);
+
 /* Synchronise the device and free everything the producer owns. NULL-safe. */
 vfm_status vfm_prefix_destroy(vfm_prefix* pre);
 

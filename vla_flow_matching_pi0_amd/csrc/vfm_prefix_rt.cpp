@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -16,6 +17,13 @@
 #include "vfm_stage_io.h"
 
 using namespace vfm;
+
+// Static workspace of vfm_prefix_run_noalloc: one array per device (each GPU
+// the library runs on holds it until the process ends), its device address
+// taken once per device with hipGetSymbolAddress; host code never passes the
+// array's name to a kernel.
+constexpr size_t NOALLOC_BYTES = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
 
 struct vfm_prefix {
   vfm_prefix_config cfg{};
@@ -128,6 +136,38 @@ int plan_split(int tiles, int K) {
   int s = 1;
   while (s < pfx::MAX_SPLIT && tiles * s < 256 && (K / (2 * s)) % pfx::TK == 0 && K % (2 * s) == 0) s *= 2;
   return s;
+}
+
+// The buffers one pass reads and writes besides its inputs and outputs.
+struct PrefixWork {
+  float* x;        // [Mpad][W] residual stream
+  float* part;     // [S][Mpad][W] K-split partial sums
+  uint8_t* xn;     // normalised stream, operand order
+  uint8_t* attn;   // attention output, operand order
+  uint8_t* act;    // GeGLU activations, operand order
+  uint16_t* q;     // rotated queries
+  uint16_t* vt;    // transposed values [B][Hkv][d][Ppad]
+  float* rope;     // [P][d/2][2]
+};
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;
+
+hipError_t scratch_of_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -254,33 +294,35 @@ vfm_status vfm_prefix_create(const vfm_prefix_config* cfg, const vfm_tensor* wei
   return VFM_OK;
 }
 
-vfm_status vfm_prefix_run(vfm_prefix* x, const void* embeds, int32_t B, int32_t P, void* prefix_k, void* prefix_v,
-                          void* stream) {
+namespace {
+
+vfm_status check_run_args(vfm_prefix* x, const void* embeds, int32_t B, int32_t P, void* prefix_k, void* prefix_v) {
   if (!x) return report(VFM_E_INVALID_ARG, "producer is NULL");
   if (B < 1 || B > x->maxB) return report(VFM_E_SHAPE, "batch %d outside [1, %d]", B, x->maxB);
   if (P < 1 || P > x->maxP) return report(VFM_E_SHAPE, "prefix length %d outside [1, %d]", P, x->maxP);
   if (!embeds || !prefix_k || !prefix_v) return report(VFM_E_INVALID_ARG, "NULL buffer");
   if ((reinterpret_cast<uintptr_t>(embeds) | reinterpret_cast<uintptr_t>(prefix_k) | reinterpret_cast<uintptr_t>(prefix_v)) % 16)
     return report(VFM_E_INVALID_ARG, "buffers must be 16-byte aligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return VFM_OK;
+}
+
+// The layer sequence over workspace `ws` (rope already holds positions 0 .. P-1).
+vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int32_t B, int32_t P, void* prefix_k,
+                    void* prefix_v, hipStream_t s) {
   const int L = x->L, W = x->W, Hq = x->Hq, Hkv = x->Hkv, d = x->d, F = x->F;
   const int M = B * P, Mpad = (int)round_up(M, pfx::TM), Ppad = (int)round_up(P, pfx::AK);
   const size_t kv_layer = (size_t)B * P * Hkv * d;
-  if (x->rope_P != P) {
-    PCHK(build_rope(x->rope, P, d, 0, x->cfg.rope_base, s));
-    x->rope_P = P;
-  }
   const int MT = Mpad / pfx::TM;
   const int S_o = plan_split(MT * (W / pfx::TN), Hq * d), S_d = plan_split(MT * (W / pfx::TN), F);
 
   pfx::NormArgs na{};
   na.embeds = static_cast<const uint16_t*>(embeds);
-  na.x = x->x; na.part = x->part; na.xn = x->xn; na.M = M; na.Mpad = Mpad; na.W = W; na.eps = x->cfg.rms_eps;
+  na.x = ws.x; na.part = ws.part; na.xn = ws.xn; na.M = M; na.Mpad = Mpad; na.W = W; na.eps = x->cfg.rms_eps;
   pfx::GemmArgs ga{};
   ga.M = M; ga.Mpad = Mpad; ga.P = P; ga.Ppad = Ppad; ga.Hq = Hq; ga.Hkv = Hkv; ga.d = d;
-  ga.part = x->part; ga.act = x->act; ga.q = x->q; ga.vt = x->vt; ga.rope = x->rope;
+  ga.part = ws.part; ga.act = ws.act; ga.q = ws.q; ga.vt = ws.vt; ga.rope = ws.rope;
   pfx::AttnArgs aa{};
-  aa.q = x->q; aa.vt = x->vt; aa.out = x->attn; aa.P = P; aa.Ppad = Ppad; aa.Hq = Hq; aa.Hkv = Hkv;
+  aa.q = ws.q; aa.vt = ws.vt; aa.out = ws.attn; aa.P = P; aa.Ppad = Ppad; aa.Hq = Hq; aa.Hkv = Hkv;
   aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
 
   for (int l = 0; l < L; ++l) {
@@ -290,23 +332,75 @@ vfm_status vfm_prefix_run(vfm_prefix* x, const void* embeds, int32_t B, int32_t 
     na.gain = x->g_attn[l];
     na.S = l == 0 ? 0 : S_d;
     PCHK(pfx::norm(l == 0, na, s));
-    ga.A = x->w_qkv[l]; ga.B = x->xn; ga.K = W; ga.S = 1;
+    ga.A = x->w_qkv[l]; ga.B = ws.xn; ga.K = W; ga.S = 1;
     ga.N = last ? 2 * Hkv * d : (Hq + 2 * Hkv) * d;   // the last layer needs its keys and values only
     ga.k_out = kl; ga.v_out = vl;
     PCHK(pfx::gemm(pfx::EPI_QKV, ga, s));
     if (last) break;
     aa.k = kl;
     PCHK(pfx::attention(d, aa, B, s));
-    ga.A = x->w_o[l]; ga.B = x->attn; ga.N = W; ga.K = Hq * d; ga.S = S_o;
+    ga.A = x->w_o[l]; ga.B = ws.attn; ga.N = W; ga.K = Hq * d; ga.S = S_o;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
     na.gain = x->g_mlp[l]; na.S = S_o;
     PCHK(pfx::norm(false, na, s));
-    ga.A = x->w_gu[l]; ga.B = x->xn; ga.N = 2 * F; ga.K = W; ga.S = 1;
+    ga.A = x->w_gu[l]; ga.B = ws.xn; ga.N = 2 * F; ga.K = W; ga.S = 1;
     PCHK(pfx::gemm(pfx::EPI_GU, ga, s));
-    ga.A = x->w_down[l]; ga.B = x->act; ga.N = W; ga.K = F; ga.S = S_d;
+    ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
   }
   return VFM_OK;
+}
+
+}  // namespace
+
+vfm_status vfm_prefix_run(vfm_prefix* x, const void* embeds, int32_t B, int32_t P, void* prefix_k, void* prefix_v,
+                          void* stream) {
+  vfm_status st = check_run_args(x, embeds, B, P, prefix_k, prefix_v);
+  if (st != VFM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (x->rope_P != P) {
+    PCHK(build_rope(x->rope, P, x->d, 0, x->cfg.rope_base, s));
+    x->rope_P = P;
+  }
+  const PrefixWork ws{x->x, x->part, x->xn, x->attn, x->act, x->q, x->vt, x->rope};
+  return run_pass(x, ws, embeds, B, P, prefix_k, prefix_v, s);
+}
+
+vfm_status vfm_prefix_run_noalloc(vfm_prefix* x, const void* embeds, int32_t B, int32_t P, void* prefix_k,
+                                  void* prefix_v, void* stream) {
+  vfm_status st = check_run_args(x, embeds, B, P, prefix_k, prefix_v);
+  if (st != VFM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t W = x->W, F = x->F, qd = (size_t)x->Hq * x->d;
+  const size_t Mpad = round_up((size_t)B * P, pfx::TM), Ppad = round_up(P, pfx::AK);
+  const int MT = (int)(Mpad / pfx::TM);
+  const size_t S = (size_t)std::max(plan_split(MT * ((int)W / pfx::TN), (int)qd), plan_split(MT * ((int)W / pfx::TN), (int)F));
+  // this call's workspace, carved from the static array (256-byte aligned pieces)
+  const size_t sz[8] = {Mpad * W * 4, S * Mpad * W * 4, Mpad * W * 2, Mpad * qd * 2, Mpad * F * 2, Mpad * qd * 2,
+                        (size_t)B * x->Hkv * x->d * Ppad * 2, (size_t)P * x->d * 4};
+  size_t off[8], total = 0;
+  for (int i = 0; i < 8; ++i) {
+    off[i] = total;
+    total += round_up(sz[i], 256);
+  }
+  if (total > NOALLOC_BYTES)
+    return report(VFM_E_UNSUPPORTED, "batch %d x prefix %d needs %zu bytes of workspace; the static workspace holds %zu",
+                  B, P, total, NOALLOC_BYTES);
+  void* base = nullptr;
+  PCHK(scratch_of_device(&base));
+  unsigned char* b = static_cast<unsigned char*>(base);
+  const PrefixWork ws{reinterpret_cast<float*>(b + off[0]), reinterpret_cast<float*>(b + off[1]),
+                      b + off[2], b + off[3], b + off[4], reinterpret_cast<uint16_t*>(b + off[5]),
+                      reinterpret_cast<uint16_t*>(b + off[6]), reinterpret_cast<float*>(b + off[7])};
+  // the array keeps the last call's contents: the buffers whose padding is
+  // read (padded token rows, padded key columns) start at zero again, and the
+  // rotary table is rebuilt (with fill and table kernels, no memset nodes)
+  PCHK(zero_words(reinterpret_cast<unsigned*>(ws.xn), (int)(sz[2] / 4), s));
+  PCHK(zero_words(reinterpret_cast<unsigned*>(ws.attn), (int)(sz[3] / 4), s));
+  PCHK(zero_words(reinterpret_cast<unsigned*>(ws.act), (int)(sz[4] / 4), s));
+  PCHK(zero_words(reinterpret_cast<unsigned*>(ws.vt), (int)(sz[6] / 4), s));
+  PCHK(build_rope(ws.rope, P, x->d, 0, x->cfg.rope_base, s));
+  return run_pass(x, ws, embeds, B, P, prefix_k, prefix_v, s);
 }
 
 vfm_status vfm_prefix_destroy(vfm_prefix* x) {

@@ -27,7 +27,7 @@ EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
            "vfm_expert_destroy", "vfm_stream_debug", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
            "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
-           "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
+           "vfm_prefix_run_noalloc", "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
            "vfm_plan_add_graph", "vfm_plan_add_edge", "vfm_plan_deps", "vfm_plan_run", "vfm_plan_destroy"]
 
 
@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vfm_prefix_create.argtypes = [ctypes.POINTER(VfmPrefixConfig), ctypes.POINTER(VfmTensor), i32, vp,
                                       ctypes.POINTER(vp)]
     lib.vfm_prefix_run.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.vfm_prefix_run_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.vfm_prefix_destroy.argtypes = [vp]
     lib.vfm_plan_create.argtypes = [ctypes.POINTER(vp)]
     lib.vfm_plan_add_prefix.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, ctypes.POINTER(i32)]
@@ -319,6 +320,12 @@ class PrefixProducer:
         B, P = int(embeds.shape[0]), int(embeds.shape[1])
         _check(_lib.vfm_prefix_run(self._h, embeds.data_ptr(), B, P, prefix_k.data_ptr(), prefix_v.data_ptr(),
                                    _stream_ptr(stream)))
+
+    def run_noalloc(self, embeds, prefix_k, prefix_v, stream=None) -> None:
+        """run() with the workspace in the library's static per-device array (no allocation)."""
+        B, P = int(embeds.shape[0]), int(embeds.shape[1])
+        _check(_lib.vfm_prefix_run_noalloc(self._h, embeds.data_ptr(), B, P, prefix_k.data_ptr(),
+                                           prefix_v.data_ptr(), _stream_ptr(stream)))
 
     def close(self) -> None:
         if getattr(self, "_h", None):
