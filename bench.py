@@ -30,28 +30,17 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 # dense MFMA peaks (TFLOP/s) of the type each weight format's GEMMs multiply in
 MFMA_PEAK_TFLOPS = {"fp32": 157.3, "bf16": 2500.0, "fp8": 5000.0, "w4a16": 2500.0, "w8a16": 2500.0, "w4a8": 5000.0}
-KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h", "vla_flow_matching_pi0_amd/csrc/vfm_launch.cpp",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_runtime.cpp"]
-
-
-def kernel_source_digest() -> str:
-    """sha256 over the sources of the timed kernel: a traffic figure taken
-    from counters is only reported while it still describes this code."""
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+from vla_flow_matching_pi0_amd.profsum import source_digest as kernel_source_digest  # noqa: E402
 
 
 def measured_traffic(workload: str, mode: str):
     """HBM bytes per launch of the timed kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain streaming kernel of
     known size), or None when there is none for this code and workload."""
-    if mode != "persistent":
+    kernel = {"persistent": "k_persistent", "stream": "k_stream"}.get(mode)
+    if kernel is None:
         return None
-    path = os.path.join(ROOT, "profiles", f"k_persistent_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -60,7 +49,7 @@ def measured_traffic(workload: str, mode: str):
             if ":" in line and line.startswith("- `"):
                 k, v = line[3:].split("`", 1)[0], line.split(":", 1)[1].strip().strip("`")
                 vals[k] = v
-    if vals.get("kernel_source_sha256") != kernel_source_digest():
+    if vals.get("kernel_source_sha256") != kernel_source_digest(kernel):
         return None
     try:
         return int(vals["hbm_bytes_per_launch"])
@@ -228,22 +217,30 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: flo
     from oracle import denoise as O
     from oracle import pi0 as P0
     run = P0.denoise_pi0 if getattr(cfg, "variant", "pi05") == "pi0" else O.denoise
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    affinity = len(os.sched_getaffinity(0))
     p64 = O.to_f64(params)
-    reps, dt = 0, 0.0
-    while dt < min_seconds:
-        t0 = time.perf_counter()
-        run(p64, noise, state, pk, pv, cfg, num_steps=steps)
-        dt += time.perf_counter() - t0
-        reps += 1
-    per_chunk_ms = dt * 1e3 * cfg.num_steps / (steps * reps)
-    return {"value": round(per_chunk_ms, 1), "unit": "ms/chunk", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} x {steps} of {cfg.num_steps} Euler steps of the {cfg.name} chunk (float64 numpy), "
-                      f"scaled to {cfg.num_steps} steps; {dt:.1f} s measured"}
+
+    def leg(seconds: float):
+        reps, dt = 0, 0.0
+        while dt < seconds:
+            t0 = time.perf_counter()
+            run(p64, noise, state, pk, pv, cfg, num_steps=steps)
+            dt += time.perf_counter() - t0
+            reps += 1
+        return dt * 1e3 * cfg.num_steps / (steps * reps), reps, dt
+
+    per_chunk_ms, reps, dt = leg(min_seconds)
+    with threadpool_limits(limits=1):
+        one_ms, one_reps, one_dt = leg(min_seconds)
+    return {"value": round(per_chunk_ms, 1), "unit": "ms/chunk", "cores": int(blas), "kind": "oracle",
+            "sample": f"{reps} x {steps} of {cfg.num_steps} Euler steps of the {cfg.name} chunk (float64 numpy, "
+                      f"BLAS on {blas} threads), scaled to {cfg.num_steps} steps; {dt:.1f} s measured",
+            "affinity_cores": affinity, "blas_threads": int(blas),
+            "single_thread": {"value": round(one_ms, 1), "unit": "ms/chunk", "cores": 1,
+                              "sample": f"{one_reps} x {steps} Euler steps with BLAS limited to one thread, "
+                                        f"{one_dt:.1f} s measured"}}
 
 
 def main() -> int:
@@ -252,9 +249,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200, help="timed denoise calls (chunks)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi05_bf16_b1")
-    ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager", "auto"],
+    ap.add_argument("--mode", default="persistent", choices=["persistent", "graph", "eager", "auto", "stream"],
                     help="launch mode; 'auto' is the library default (graph launch of the large-batch kernels for "
-                         "bf16 experts with at least 256 rows, else the persistent kernel)")
+                         "bf16 experts with at least 256 rows, else the persistent kernel); 'stream' is the "
+                         "batch-1 kernel whose weights stream into LDS ahead of use (bf16 pi0.5 shapes)")
     ap.add_argument("--persistent-launch", default="cooperative", choices=["cooperative", "plain"],
                     help="launch API of the persistent kernel (plain: for profilers that cannot follow "
                          "cooperative launches)")
@@ -357,6 +355,22 @@ def main() -> int:
         stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
         sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "span_us": round(float(span), 1),
                 "stall_frac": round(stall / span, 4) if span > 0 else None}
+    elif args.mode == "stream":
+        # (arrive, counters complete, workgroup ready) per barrier: the stall is
+        # arrival to ready (the device-wide wait plus any wait for weights)
+        L, N = cfg.num_layers, cfg.num_steps
+        nb = N * (5 * L + 2) - 1
+        words = max(2 * (N * (8 * L + 1) + 4), 3 * (nb + 2))
+        ex.set_option("trace", "1")
+        ex.denoise(stream=stream)
+        ex.check(stream)
+        t = ex.export("trace", (words,))[: 3 * (nb + 1)].reshape(-1, 3).astype(np.float64)
+        ex.set_option("trace", "0")
+        span = t[nb, 2] - t[0, 2]
+        stall = float(np.sum(t[1:, 2] - t[1:, 0]))
+        weight_wait = float(np.sum(t[1:, 2] - t[1:, 1]))
+        sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "weight_wait_us": round(weight_wait, 1),
+                "span_us": round(float(span), 1), "stall_frac": round(stall / span, 4) if span > 0 else None}
     # execution-state capsule of the bound buffers: snapshot and restore, each a set of device-to-device copies
     cap = ex.capsule()
     reps = 20
@@ -384,6 +398,11 @@ def main() -> int:
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
+        # the same bytes copied with plain and with device-scope (sc1) loads,
+        # to check the counter scale on the load policy the kernels also use
+        for policy in (0, 16):
+            for _ in range(3):
+                vfm.copy_probe(src, dst, policy, stream)
         torch.cuda.synchronize()
         del src, dst
 

@@ -226,6 +226,14 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
  * VFM_E_STATE. */
 vfm_status vfm_export(vfm_expert* ex, const char* name, void* dst, size_t bytes);
 
+/* Measurement helper (not part of the denoise path): copy `bytes` (a multiple
+ * of 16 below 2 GiB) from `src` to `dst` (device, 16-byte aligned, not
+ * overlapping) with loads of cache policy `policy`: 0 plain, 1 sc0
+ * (workgroup scope), 16 sc1 (device scope); stores plain. A kernel of known
+ * traffic against which HBM counters are scaled for each load policy the
+ * kernels use. Asynchronous on `stream`. Errors: VFM_E_INVALID_ARG, VFM_E_HIP. */
+vfm_status vfm_copy_probe(const void* src, void* dst, size_t bytes, int32_t policy, void* stream);
+
 /* Wait for `stream` and report any device-side failure of earlier denoise
  * calls (a launch error, or a phase barrier that timed out and stopped the
  * persistent kernel early): VFM_E_HIP with a message. */

@@ -187,12 +187,13 @@ struct NoHook {
 // in every thread between arrival and wait: work that does not depend on the
 // other workgroups (issuing loads of read-only data) overlaps the wait.
 // bar[1] is a sticky error word: a wait that exceeds `spin_limit` polls sets
-// it, and every waiter gives up once it is set (returns false). Barrier
+// it (and the host-mapped word `herr`), and every waiter gives up once it is
+// set (returns false). Barrier
 // `fail_epoch` (diagnostics, 0: none) waits for one arrival more than the grid
 // holds, so its bounded wait gives up and every workgroup exits normally.
 template <typename HOOK = NoHook>
 __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, unsigned long long* trace, long spin_limit,
-                                             int fail_epoch, const HOOK& hook = HOOK()) {
+                                             int fail_epoch, unsigned* herr, const HOOK& hook = HOOK()) {
   __shared__ unsigned s_ok;
   ++epoch;
   __builtin_amdgcn_s_waitcnt(0);   // this wave's stores (and loads) have completed
@@ -221,7 +222,10 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
         unsigned err = lane == 0 ? ld_agent(&bar[1]) : 0u;
         err = __shfl(err, 0);
         if (err != 0u || spins > spin_limit) {
-          if (lane == 0) __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) {
+            __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (herr) __hip_atomic_store(herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
           ok = 0;
           break;
         }

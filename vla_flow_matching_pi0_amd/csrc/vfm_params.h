@@ -10,7 +10,7 @@ namespace vfm {
 constexpr int MAX_LAYERS = 48;
 constexpr int NTHREADS = 512;      // threads per workgroup
 constexpr int MAX_KSPLIT = 16;     // K splits of the residual GEMMs
-// Grid-barrier words: [0] unused, [1] sticky error flag, then BAR_COUNTERS
+// Grid-barrier words: [0] exit count, [1] sticky error flag, then BAR_COUNTERS
 // arrival counters, each on its own 256-byte line (word 64 + 64 c).
 constexpr int BAR_COUNTERS = 64;
 constexpr int BAR_WORDS = 64 + 64 * BAR_COUNTERS;
@@ -64,6 +64,7 @@ struct VP {
   unsigned* bar;           // grid-barrier words
   unsigned long long* trace;  // optional phase timeline of the persistent kernel (null: off)
   long spin_limit;         // polls before a barrier wait gives up
+  unsigned* herr;          // host-mapped error word (set with a system-scope store when a wait gives up)
   int fail_epoch;          // diagnostics: barrier whose target is never reached (0: none)
 };
 
@@ -104,5 +105,6 @@ hipError_t build_pi0_tables(float* mod, const void* const* norm_w, int n_norms, 
                             int src_bf16, double* scratch, hipStream_t st);
 hipError_t build_rope(float* rope, int H, int d, int P, float base, hipStream_t st);
 hipError_t zero_words(unsigned* p, int n, hipStream_t st);
+hipError_t copy_probe(const void* src, void* dst, size_t bytes, int policy, hipStream_t st);
 
 }  // namespace vfm

@@ -1595,11 +1595,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
   const int wg = blockIdx.x, nwg = gridDim.x;
   if (p.trace && wg == 0 && threadIdx.x == 0) p.trace[0] = p.trace[1] = __builtin_amdgcn_s_memrealtime();
-#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch)) return; } while (0)
+#define VFM_BAR() do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr)) return; } while (0)
   // The next GEMM's first weight pass is loaded while the workgroup waits at
   // the barrier before it: weights do not depend on the other workgroups.
 #define VFM_BAR_PF(WHICH, LAYER) \
-  do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
+  do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
   ph_boundary<T, WF>(p, -1, 0, wg, nwg);
   if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
@@ -1621,7 +1621,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
       {
         APre<T, D> apre;
-        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
+        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
         ph_attn<T, D, true>(p, k, l, wg, nwg, apre);
       }
       VFM_BAR();
@@ -1643,6 +1643,18 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   }
 #undef VFM_BAR_PF
 #undef VFM_BAR
+  // Every workgroup has passed the last barrier; the last one to leave (an
+  // exit count) clears the arrival counters for the next launch, so no
+  // workgroup can still be polling them. A launch that gave up leaves them
+  // behind and the host clears them when it reports the failure.
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(&p.bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == gridDim.x) {
+      for (int c = 0; c < BAR_COUNTERS; ++c)
+        __hip_atomic_store(&p.bar[64 + 64 * c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // One phase per launch (eager / graph modes, and the calibration pass); one

@@ -447,4 +447,26 @@ hipError_t zero_words(unsigned* p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Streaming copy whose loads carry cache policy CP (0 plain, 1 sc0, 16 sc1);
+// stores are plain. 16 bytes per lane, grid-stride.
+template <int CP>
+__global__ void k_copy_probe(const uint8_t* src, uint8_t* dst, uint32_t n16) {
+  const auto rs = rsrc(src);
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += gridDim.x * blockDim.x) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16u, 0, CP);
+    *reinterpret_cast<u32x4*>(dst + (size_t)i * 16) = v;
+  }
+}
+
+hipError_t copy_probe(const void* src, void* dst, size_t bytes, int policy, hipStream_t st) {
+  const uint32_t n16 = (uint32_t)(bytes / 16);
+  const dim3 grid(2048), block(256);
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  if (policy == 0) hipLaunchKernelGGL(k_copy_probe<0>, grid, block, 0, st, s, d, n16);
+  else if (policy == 1) hipLaunchKernelGGL(k_copy_probe<1>, grid, block, 0, st, s, d, n16);
+  else hipLaunchKernelGGL(k_copy_probe<16>, grid, block, 0, st, s, d, n16);
+  return hipGetLastError();
+}
+
 }  // namespace vfm

@@ -92,9 +92,8 @@ struct vfm_expert {
   unsigned* bar = nullptr;
   unsigned long long* trace = nullptr;   // phase timeline (option "trace")
   size_t trace_words = 0;
-  unsigned* host_flag = nullptr;   // pinned copy of the barrier error word
-  hipEvent_t flag_event = nullptr;
-  bool flag_pending = false;
+  unsigned* herr = nullptr;        // pinned, host-mapped: set by a persistent launch whose barrier wait gave up
+  unsigned* herr_dev = nullptr;    // its device address
   BoundBuf prefix_k, prefix_v, noise, state, actions;
   int mode = 3;                    // 0 persistent, 1 graph, 2 eager, 3 auto, 4 stream (see launch_mode_of)
   vfm::sk::StreamState* ss = nullptr;   // streaming batch-1 kernel (bf16 pi0.5 experts whose shapes fit it)
@@ -369,28 +368,22 @@ void free_all(vfm_expert* x) {
   vfm::sk::stream_destroy(x->ss);
   x->ss = nullptr;
   if (x->cap_stream) (void)hipStreamDestroy(x->cap_stream);
-  if (x->flag_event) (void)hipEventDestroy(x->flag_event);
-  if (x->host_flag) (void)hipHostFree(x->host_flag);
+  if (x->herr) (void)hipHostFree(x->herr);
   for (void* p : x->allocs) (void)hipFree(p);
   x->allocs.clear();
 }
 
-vfm_status check_prev_flag(vfm_expert* x, bool wait) {
-  if (!x->flag_pending) return VFM_OK;
-  if (wait) {
-    HIPCHK(hipEventSynchronize(x->flag_event));
-  } else if (hipEventQuery(x->flag_event) != hipSuccess) {
-    return VFM_OK;
-  }
-  x->flag_pending = false;
-  if (*x->host_flag != 0u) {
-    // the device word is sticky (never cleared by a launch): clear it now that it is reported
-    *x->host_flag = 0u;
-    (void)vfm::zero_words(x->bar + 1, 1, nullptr);
-    (void)hipDeviceSynchronize();
-    return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
-  }
-  return VFM_OK;
+// A persistent launch whose barrier wait gave up raised the host-mapped
+// error word (and the sticky device word bar[1]); report it once, and clear
+// both and the arrival counters that launch left behind (ordered on `s`).
+// No synchronisation: a failure not yet visible is reported by a later call
+// or by vfm_check, which synchronises first.
+vfm_status check_host_err(vfm_expert* x, hipStream_t s) {
+  if (!x->herr || __atomic_load_n(x->herr, __ATOMIC_ACQUIRE) == 0u) return VFM_OK;
+  *x->herr = 0u;
+  (void)vfm::zero_words(x->bar, vfm::BAR_WORDS, s);
+  (void)hipStreamSynchronize(s);
+  return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
 }
 
 // A streaming launch that failed (a barrier that timed out) raised the
@@ -546,6 +539,7 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   p.trace = mode == 0 ? x->trace : nullptr;
   p.spin_limit = x->spin_limit;
   p.fail_epoch = mode == 0 ? x->fail_barrier : 0;
+  p.herr = mode == 0 ? x->herr_dev : nullptr;
 
   {
     int nwg = x->coop_grid;
@@ -838,9 +832,9 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     return bail(VFM_E_OOM);
   }
   if (vfm::zero_words(x->bar, vfm::BAR_WORDS, s) != hipSuccess) { fail(VFM_E_HIP, "barrier clear"); return bail(VFM_E_HIP); }
-  if (hipHostMalloc((void**)&x->host_flag, 4) != hipSuccess) { fail(VFM_E_OOM, "pinned allocation failed"); return bail(VFM_E_OOM); }
-  *x->host_flag = 0u;
-  if (hipEventCreateWithFlags(&x->flag_event, hipEventDisableTiming) != hipSuccess) { fail(VFM_E_HIP, "event"); return bail(VFM_E_HIP); }
+  if (hipHostMalloc((void**)&x->herr, 4, hipHostMallocMapped) != hipSuccess) { fail(VFM_E_OOM, "pinned allocation failed"); return bail(VFM_E_OOM); }
+  *x->herr = 0u;
+  if (hipHostGetDevicePointer((void**)&x->herr_dev, x->herr, 0) != hipSuccess) { fail(VFM_E_HIP, "mapped error word"); return bail(VFM_E_HIP); }
   {
     VP shape{};
     shape.d = d;
@@ -991,7 +985,7 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
 
 vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, float* actions, void* stream) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
-  vfm_status st = check_prev_flag(x, false);
+  vfm_status st = check_host_err(x, reinterpret_cast<hipStream_t>(stream));
   if (st != VFM_OK) return st;
   if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
   const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
@@ -1033,12 +1027,9 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
                                x->ss_tune, s);
   }
   if (mode == 0) {
-    // the arrival counters only: bar[1], the error word, stays set until reported
-    HIPCHK(vfm::zero_words(x->bar + 64, vfm::BAR_WORDS - 64, s));
+    // one launch per call: the kernel's last workgroup clears the arrival
+    // counters, and a failure raises the host-mapped word read by the checks
     HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
-    HIPCHK(hipMemcpyAsync(x->host_flag, x->bar + 1, 4, hipMemcpyDeviceToHost, s));
-    HIPCHK(hipEventRecord(x->flag_event, s));
-    x->flag_pending = true;
     return VFM_OK;
   }
   if (mode == 2) {
@@ -1078,7 +1069,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
 vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
   if (!fp8_act(x)) return fail(VFM_E_STATE, "calibrate applies to FP8 and W4A8 experts only");
-  vfm_status st = check_prev_flag(x, true);
+  vfm_status st = check_host_err(x, reinterpret_cast<hipStream_t>(stream));
   if (st != VFM_OK) return st;
   if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
   const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
@@ -1109,6 +1100,7 @@ vfm_status vfm_calibrate(vfm_expert* x, void* stream) {
   p.trace = nullptr;
   p.spin_limit = x->spin_limit;
   p.fail_epoch = 0;
+  p.herr = nullptr;
   p.amax = amax;
   hipError_t e = hipMemsetAsync(amax, 0, (size_t)std::max(L, 1) * 16, s);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
@@ -1313,6 +1305,15 @@ vfm_status vfm_stream_debug(vfm_expert* x, const char* name, int32_t index, void
   return vfm::sk::stream_debug_copy(x->ss, name, index, dst, bytes);
 }
 
+vfm_status vfm_copy_probe(const void* src, void* dst, size_t bytes, int32_t policy, void* stream) {
+  if (!src || !dst) return fail(VFM_E_INVALID_ARG, "NULL buffer");
+  if (bytes == 0 || bytes % 16 || bytes >= (1ull << 31)) return fail(VFM_E_INVALID_ARG, "bytes must be a positive multiple of 16 below 2 GiB");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16) return fail(VFM_E_INVALID_ARG, "buffers must be 16-byte aligned");
+  if (policy != 0 && policy != 1 && policy != 16) return fail(VFM_E_INVALID_ARG, "policy must be 0 (plain), 1 (sc0) or 16 (sc1)");
+  HIPCHK(vfm::copy_probe(src, dst, bytes, policy, reinterpret_cast<hipStream_t>(stream)));
+  return VFM_OK;
+}
+
 vfm_status vfm_check(vfm_expert* x, void* stream) {
   if (!x) return fail(VFM_E_INVALID_ARG, "expert is NULL");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1320,7 +1321,7 @@ vfm_status vfm_check(vfm_expert* x, void* stream) {
   HIPCHK(hipGetLastError());
   vfm_status st = check_stream_flag(x, s);
   if (st != VFM_OK) return st;
-  return check_prev_flag(x, true);
+  return check_host_err(x, s);
 }
 
 }  // extern "C"
@@ -1464,7 +1465,7 @@ vfm_status vfm_capsule_destroy(vfm_capsule* c) {
 vfm_status vfm_expert_destroy(vfm_expert* x) {
   if (!x) return VFM_OK;
   (void)hipDeviceSynchronize();
-  vfm_status st = check_prev_flag(x, true);
+  vfm_status st = check_host_err(x, nullptr);
   free_all(x);
   delete x;
   return st;

@@ -4,6 +4,7 @@ library (kernel time statistics, HBM traffic of one kernel).
   python -m vla_flow_matching_pi0_amd.profsum stats <kernel_stats.csv> <out.md> --cmd "<command>" [--match <name part>]
   python -m vla_flow_matching_pi0_amd.profsum traffic <fetch counter_collection.csv> <write counter_collection.csv>
          <out.md> --kernel k_persistent --calib-mib 1024 --cmd-fetch "<command>" --cmd-write "<command>"
+  python -m vla_flow_matching_pi0_amd.profsum gaps <kernel_trace.csv> <out.md> --match <name part> --cmd "<command>"
 
 The traffic summary scales the FETCH_SIZE / WRITE_SIZE counters (KiB per
 dispatch) of the kernel by the ratio of known bytes to counted bytes of a
@@ -20,14 +21,20 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ["vla_flow_matching_pi0_amd/csrc/vfm_phases.h", "vla_flow_matching_pi0_amd/csrc/vfm_device.h",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_params.h", "vla_flow_matching_pi0_amd/csrc/vfm_launch.cpp",
-                  "vla_flow_matching_pi0_amd/csrc/vfm_runtime.cpp"]
+_C = "vla_flow_matching_pi0_amd/csrc/"
+# the sources each timed kernel is built from: a traffic figure taken from
+# counters is only reported while it still describes this code
+KERNEL_SOURCES = {
+    "k_persistent": [_C + "vfm_phases.h", _C + "vfm_device.h", _C + "vfm_params.h", _C + "vfm_launch.cpp",
+                     _C + "vfm_runtime.cpp"],
+    "k_stream": [_C + "vfm_stream.h", _C + "vfm_stream_params.h", _C + "vfm_k_stream.hip", _C + "vfm_stream_rt.cpp",
+                 _C + "vfm_device.h", _C + "vfm_params.h"],
+}
 
 
-def source_digest() -> str:
+def source_digest(kernel: str = "k_persistent") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -76,12 +83,20 @@ def _kernel_and_calib(path: str, counter: str, kernel: str, calib_bytes: int):
     return sum(kv) / len(kv) * 1024, sum(cv) / len(cv) * 1024, len(kv), len(cv)
 
 
+def _probe_scale(path: str, counter: str, policy: int, calib_bytes: int):
+    """known bytes / counted bytes of the copy probe with load policy `policy` (None if absent)."""
+    disp = _per_dispatch(path, counter)
+    v = [x for n, x in disp.values() if f"k_copy_probe<{policy}>" in n and x * 1024 > 0.5 * calib_bytes]
+    return calib_bytes / (sum(v) / len(v) * 1024) if v else None
+
+
 def traffic(fetch_csv: str, write_csv: str, out: str, kernel: str, calib_mib: int, cmd_fetch: str,
             cmd_write: str, workload: str) -> None:
     cb = calib_mib << 20
     kf, cf, nkf, ncf = _kernel_and_calib(fetch_csv, "FETCH_SIZE", kernel, cb)
     kw, cw, nkw, ncw = _kernel_and_calib(write_csv, "WRITE_SIZE", kernel, cb)
     sf, sw = cb / cf, cb / cw
+    probe = {pol: _probe_scale(fetch_csv, "FETCH_SIZE", pol, cb) for pol in (0, 16)}
     fetch, write = kf * sf, kw * sw
     lines = [f"# HBM traffic of `{kernel}` ({workload})", "",
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs, each scaled by the "
@@ -93,10 +108,42 @@ def traffic(fetch_csv: str, write_csv: str, out: str, kernel: str, calib_mib: in
              f"- `write_counter_bytes_per_launch`: {int(kw)}",
              f"- `calib_fetch_counter_bytes`: {int(cf)} (known {cb}; scale {sf:.4f})",
              f"- `calib_write_counter_bytes`: {int(cw)} (known {cb}; scale {sw:.4f})",
+             f"- `fetch_scale_copy_plain_loads`: {probe[0]:.4f}" if probe[0] else "- `fetch_scale_copy_plain_loads`: n/a",
+             f"- `fetch_scale_copy_sc1_loads`: {probe[16]:.4f}" if probe[16] else "- `fetch_scale_copy_sc1_loads`: n/a",
              f"- `fetch_bytes_per_launch`: {int(fetch)}",
              f"- `write_bytes_per_launch`: {int(write)}",
              f"- `hbm_bytes_per_launch`: {int(fetch + write)}",
-             f"- `kernel_source_sha256`: {source_digest()}", ""]
+             f"- `kernel_source_sha256`: {source_digest(kernel)}", ""]
+    open(out, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def gaps(path: str, out: str, cmd: str, match: str, skip_frac: float) -> None:
+    """Launch-gap share of a kernel-trace timeline: over the dispatches whose
+    name contains `match` (the first `skip_frac` of them dropped as warmup),
+    the share of the wall span from the first start to the last end during
+    which none of them runs."""
+    rows = [r for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows)
+    iv = iv[int(len(iv) * skip_frac):]
+    if not iv:
+        raise SystemExit(f"{path}: no dispatch matching {match!r}")
+    busy, cur_s, cur_e = 0, iv[0][0], iv[0][1]
+    for s0, e0 in iv[1:]:
+        if s0 > cur_e:
+            busy += cur_e - cur_s
+            cur_s, cur_e = s0, e0
+        else:
+            cur_e = max(cur_e, e0)
+    busy += cur_e - cur_s
+    span = max(e for _, e in iv) - iv[0][0]
+    frac = 1.0 - busy / span
+    lines = [f"# Launch gaps of the kernels matching `{match}`", "", "Command:", "", "```", cmd, "```", "",
+             f"Dispatches after dropping the first {skip_frac:.0%} as warmup: {len(iv)}.", "",
+             f"- `span_us`: {span / 1e3:.1f}",
+             f"- `busy_us`: {busy / 1e3:.1f}",
+             f"- `gap_us`: {(span - busy) / 1e3:.1f}",
+             f"- `launch_gap_frac`: {frac:.4f}", ""]
     open(out, "w").write("\n".join(lines))
     print("\n".join(lines))
 
@@ -118,7 +165,16 @@ def main(argv=None) -> int:
     b.add_argument("--calib-mib", type=int, required=True)
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("gaps")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--match", required=True)
+    c.add_argument("--skip-frac", type=float, default=0.2)
     args = ap.parse_args(argv)
+    if args.mode == "gaps":
+        gaps(args.csv, args.out, args.cmd, args.match, args.skip_frac)
+        return 0
     if args.mode == "stats":
         stats(args.csv, args.out, args.cmd, match=args.match)
     else:

@@ -24,7 +24,7 @@ ABI_VERSION = 2
 
 # Every entry point include/vfm.h declares.
 EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind", "vfm_denoise",
-           "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_check",
+           "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_copy_probe", "vfm_check",
            "vfm_expert_destroy", "vfm_stream_debug", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
            "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
            "vfm_prefix_run_noalloc", "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vfm_set_act_scales.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32]
     lib.vfm_export.argtypes = [vp, ctypes.c_char_p, vp, ctypes.c_size_t]
     lib.vfm_check.argtypes = [vp, vp]
+    lib.vfm_copy_probe.argtypes = [vp, vp, ctypes.c_size_t, i32, vp]
     lib.vfm_expert_destroy.argtypes = [vp]
     lib.vfm_capsule_create.argtypes = [vp, ctypes.POINTER(vp)]
     lib.vfm_capsule_save.argtypes = [vp, vp, vp]
@@ -423,3 +424,11 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def copy_probe(src, dst, policy: int, stream=None) -> None:
+    """Measurement helper: copy src -> dst (device tensors of equal byte size)
+    with loads of cache policy 0 (plain), 1 (sc0) or 16 (sc1)."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    _check(lib.vfm_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, policy, _stream_ptr(stream)))
