@@ -135,9 +135,16 @@ const char* vfm_last_error(void);
  * Synchronous on `stream`: copies, repacks and (for FP8 / W4A16) quantises the
  * weights on the device and precomputes the time-conditioning table for the
  * N fixed times t_k = (N-k)/N. All workspace for max_batch / max_prefix_len
- * is allocated here; denoise never allocates.
+ * is allocated here; denoise never allocates. The workspace is dominated by
+ * a write-once activation ring of N L slabs, each slab (4 KiB-aligned parts)
+ * Mp W (2 a) + B Hq d 64 a + 2 B Hkv d 64 a + Mp Hq d a + Mp F a bytes (plus
+ * Mp W a for pi0), with Mp = round_up(max_batch T, 64), T the suffix tokens
+ * per sample, a the activation bytes (2 bf16, 4 f32); about 225 MB for the
+ * pi0.5 expert at batch 1. A configuration whose workspace would exceed
+ * 64 GiB fails with VFM_E_UNSUPPORTED before anything is allocated.
  * Errors: VFM_E_INVALID_ARG (config field out of range, missing or unknown
- * name), VFM_E_SHAPE, VFM_E_DTYPE, VFM_E_OOM, VFM_E_HIP. On error *out is NULL. */
+ * name), VFM_E_SHAPE, VFM_E_DTYPE, VFM_E_UNSUPPORTED (a buffer beyond 2 GiB,
+ * or the workspace beyond 64 GiB), VFM_E_OOM, VFM_E_HIP. On error *out is NULL. */
 vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, int32_t n_weights,
                              void* stream, vfm_expert** out);
 

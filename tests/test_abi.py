@@ -228,3 +228,19 @@ def test_create_rejects_buffers_beyond_32bit_offsets(lib):
         assert not out.value
     # the batch-32 workload fits (fails later, for want of weights)
     assert vfm.STATUS[_create(lib, vfm.make_config(CONFIGS["pi05_bf16_b32"]))[0]] == "VFM_E_INVALID_ARG"
+
+
+def test_create_rejects_a_workspace_beyond_the_limit(lib):
+    """The write-once activation ring grows as slab x steps x layers: the
+    pi0.5 expert at max_batch 64 with 1000 Euler steps would need about
+    1.3 TB, refused with VFM_E_UNSUPPORTED before anything is allocated (every
+    single buffer stays below 2 GiB, so only the total check can catch it)."""
+    c = vfm.make_config(CONFIGS["pi05_bf16_b1"].replace(batch=64, num_steps=1000))
+    st, out = _create(lib, c)
+    assert vfm.STATUS[st] == "VFM_E_UNSUPPORTED"
+    msg = lib.vfm_last_error().decode()
+    assert "workspace" in msg and "activation ring" in msg
+    assert not out.value
+    # the benchmarked shape stays well inside
+    c = vfm.make_config(CONFIGS["pi05_bf16_b1"])
+    assert vfm.STATUS[_create(lib, c)[0]] == "VFM_E_INVALID_ARG"     # valid config; fails for want of weights

@@ -153,20 +153,14 @@ def test_producer_feeds_the_expert():
     ex.close()
 
 
-def test_full_depth_sampled_layers():
+def test_full_depth_every_layer():
     """The full 18-layer Gemma-2B-shaped pass at 560 tokens (what the benchmark
-    times): every output finite, layers 0 and 1 against the oracle (a
-    two-layer oracle pass computes exactly those), and every layer's key and
-    value scale within 2 % of the oracle's layer-1 scale band."""
+    times): every layer's keys and values against the fp64 oracle element-wise
+    (the whole-depth oracle pass, about a minute on the host)."""
     cfg = PREFIX_CONFIGS["prefix_gemma2b_p560"]
     params, emb = make_prefix_inputs(cfg)
     print("case prefix gemma2b full depth", flush=True)
     pre, k, v = run_producer(cfg, params, emb)
     pre.close()
-    two = cfg.replace(num_layers=2)
-    sub = {n: a for n, a in params.items() if int(n.split(".")[1]) < 2}
-    rk, rv = PO.prefix_kv(sub, emb, two)
-    check_layers(k, v, rk, rv, layers=(0, 1))
-    rms = [float(np.sqrt(np.mean(k[l].astype(np.float64) ** 2))) for l in range(cfg.num_layers)]
-    print("k rms per layer:", " ".join(f"{r:.3f}" for r in rms))
-    assert all(0.5 < r < 2.0 for r in rms)
+    rk, rv = PO.prefix_kv(params, emb, cfg)
+    check_layers(k, v, rk, rv)

@@ -169,3 +169,39 @@ def test_dequantised_expert_w8_is_per_column():
         m = params[f"layers.0.{n}.w"]
         _, _, d2 = Q.quantise_w8(m[:, : m.shape[1] // 2])
         assert np.array_equal(d2, d1[:, : m.shape[1] // 2])
+
+
+def test_dequantised_expert_w4a8_is_the_int4_group_grid():
+    """The W4A8 branch (int4 weights, e4m3 activations): every GEMM weight is
+    an integer code in [-8, 7] times the fp16 scale of its (128-row group,
+    column), the scale being the group's largest magnitude over 7 rounded to
+    fp16; each value lies within half a step of the bf16 master, each group's
+    largest magnitude takes code +-7, and the weights outside the GEMMs pass
+    through untouched. Checked from the definition, group by group, without
+    the oracle's quantiser."""
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["tiny_fp32"].replace(weight_precision="w4a8", num_layers=2)
+    params, *_ = make_inputs(cfg)
+    deq, scales = Q.dequantised_expert(params, cfg)
+    assert scales is None
+    G = cfg.w4_group
+    for l in range(cfg.num_layers):
+        for n in ("q", "k", "v", "o", "gate", "up", "down"):
+            w = params[f"layers.{l}.{n}.w"].astype(np.float64)
+            d = np.asarray(deq[f"layers.{l}.{n}.w"], dtype=np.float64)
+            K, N = w.shape
+            assert d.shape == (K, N)
+            for g0 in range(0, K, G):
+                for c in range(N):
+                    col = w[g0:g0 + G, c]
+                    amax = float(np.max(np.abs(col)))
+                    s = float(np.float16(np.float32(amax) / np.float32(7.0))) if amax > 0 else 1.0
+                    codes = d[g0:g0 + G, c] / s
+                    assert np.all(codes == np.round(codes)), (l, n, g0, c)
+                    assert codes.min() >= -8 and codes.max() <= 7
+                    assert np.all(np.abs(d[g0:g0 + G, c] - col) <= s / 2 * (1 + 1e-6) + 1e-300)
+                    if amax > 0:
+                        assert np.max(np.abs(codes)) == 7.0
+    for name in ("in_proj.w", "out_proj.w", "time_mlp_in.w"):
+        if name in params:
+            assert deq[name] is params[name]

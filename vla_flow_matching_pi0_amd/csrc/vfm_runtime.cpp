@@ -235,6 +235,8 @@ vfm_status validate_config(const vfm_config* c) {
 // The kernels address every buffer through 32-bit byte offsets from its
 // base (buffer resources of up to 2 GiB): refuse configurations whose largest
 // buffer would not fit.
+constexpr size_t WORKSPACE_MAX = 64ull << 30;   // largest workspace an expert may allocate
+
 vfm_status check_extents(const vfm_config* c) {
   const size_t ab = c->act_dtype == VFM_F32 ? 4 : 2;
   const size_t L = c->num_layers, W = c->width, Hq = c->num_q_heads, Hkv = c->num_kv_heads, d = c->head_dim;
@@ -256,6 +258,18 @@ vfm_status check_extents(const vfm_config* c) {
     if (e.bytes > 0x7FFFFFF0ull)
       return fail(VFM_E_UNSUPPORTED, "the %s would take %zu bytes, beyond the 2 GiB one buffer offset addresses "
                   "(reduce max_batch, max_prefix_len, num_steps or the widths)", e.what, e.bytes);
+  // total workspace: the write-once activation ring (one slab per step and
+  // layer, the slab of create's layout) plus the per-call buffers
+  auto al = [](size_t b) { return (b + 4095) / 4096 * 4096; };
+  const size_t slab = al(Mpad * W * ab) + al(B * Hq * d * 64 * ab) + 2 * al(B * Hkv * d * 64 * ab) +
+                      al(Mpad * Hq * d * ab) + al(Mpad * W * ab) + al(F * Mpad * ab) +
+                      (c->variant == VFM_VARIANT_PI0 ? al(Mpad * W * ab) : 0);
+  const size_t ring = slab * N * std::max<size_t>(L, 1);
+  const size_t other = M * W * 4 * (2 + 2 * (size_t)vfm::MAX_KSPLIT) + B * Hq * KS * 64 * (d + 2) * 4;
+  if (ring + other > WORKSPACE_MAX)
+    return fail(VFM_E_UNSUPPORTED, "the workspace would take %zu bytes (activation ring %zu = slab %zu x %zu steps x "
+                "%zu layers), beyond the %zu the library accepts (reduce max_batch or num_steps)",
+                ring + other, ring, slab, N, std::max<size_t>(L, 1), WORKSPACE_MAX);
   return VFM_OK;
 }
 
