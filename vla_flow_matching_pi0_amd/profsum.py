@@ -148,6 +148,37 @@ def gaps(path: str, out: str, cmd: str, match: str, skip_frac: float) -> None:
     print("\n".join(lines))
 
 
+def mfma(path: str, out: str, cmd: str, match: str = "", top: int = 12) -> None:
+    """MFMA activity per kernel from SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+    (both summed over the device: the busy counter over its 1024 SIMDs, the
+    active counter over its 8 XCDs): busy fraction = MFMA busy cycles /
+    (1024 x active cycles per XCD), aggregated over each kernel's dispatches."""
+    busy = _per_dispatch(path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    act = _per_dispatch(path, "GRBM_GUI_ACTIVE")
+    agg = collections.defaultdict(lambda: [0, 0.0, 0.0])
+    keep = [m for m in match.split(",") if m]
+    for d, (name, b) in busy.items():
+        if d not in act or (keep and not any(m in name for m in keep)):
+            continue
+        a = agg[short_name(name)]
+        a[0] += 1
+        a[1] += b
+        a[2] += act[d][1] / 8.0
+    rows = sorted(agg.items(), key=lambda kv: -kv[1][2])
+    tb = sum(v[1] for v in agg.values())
+    ta = sum(v[2] for v in agg.values())
+    lines = ["# MFMA activity per kernel", "", "Command:", "", "```", cmd, "```", "",
+             "Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), summed over "
+             "the kernel's dispatches; time share = its active cycles over all kernels counted"
+             + (f" (names containing any of: {', '.join(keep)})" if keep else "") + ".", "",
+             "| kernel | dispatches | active Mcycles per XCD | time share | MFMA busy |", "|---|---:|---:|---:|---:|"]
+    for n, (c, b, a) in rows[:top]:
+        lines.append(f"| `{n}` | {c} | {a / 1e6:.2f} | {a / ta:.3f} | {b / (1024 * a):.4f} |")
+    lines += ["", f"- `mfma_busy_fraction_counted_kernels`: {tb / (1024 * ta):.4f}", ""]
+    open(out, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -171,7 +202,15 @@ def main(argv=None) -> int:
     c.add_argument("--cmd", required=True)
     c.add_argument("--match", required=True)
     c.add_argument("--skip-frac", type=float, default=0.2)
+    dm = sub.add_parser("mfma")
+    dm.add_argument("csv")
+    dm.add_argument("out")
+    dm.add_argument("--cmd", required=True)
+    dm.add_argument("--match", default="", help="comma-separated name parts; count only kernels matching one")
     args = ap.parse_args(argv)
+    if args.mode == "mfma":
+        mfma(args.csv, args.out, args.cmd, args.match)
+        return 0
     if args.mode == "gaps":
         gaps(args.csv, args.out, args.cmd, args.match, args.skip_frac)
         return 0
