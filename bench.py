@@ -253,6 +253,8 @@ def main() -> int:
                     help="launch mode; 'auto' is the library default (graph launch of the large-batch kernels for "
                          "bf16 experts with at least 256 rows, else the persistent kernel); 'stream' is the "
                          "batch-1 kernel whose weights stream into LDS ahead of use (bf16 pi0.5 shapes)")
+    ap.add_argument("--large-m-tiles", default="auto", choices=["auto", "narrow", "wide"],
+                    help="graph / eager launch with many rows: the large-M GEMM tile plan")
     ap.add_argument("--persistent-launch", default="cooperative", choices=["cooperative", "plain"],
                     help="launch API of the persistent kernel (plain: for profilers that cannot follow "
                          "cooperative launches)")
@@ -289,6 +291,7 @@ def main() -> int:
     del dev
     ex.set_option("launch_mode", args.mode)
     ex.set_option("persistent_launch", args.persistent_launch)
+    ex.set_option("large_m_tiles", args.large_m_tiles)
     bufs = {"prefix_k": torch.from_numpy(pk).to("cuda").to(wdt), "prefix_v": torch.from_numpy(pv).to("cuda").to(wdt),
             "noise": torch.from_numpy(noise).to("cuda"), "actions": torch.empty(noise.shape, device="cuda")}
     if cfg.state_dim:

@@ -278,6 +278,52 @@ def test_large_m_gemm_matches_oracle(variant, batch, horizon):
     np.testing.assert_array_equal(outs["auto"], outs["graph"])
 
 
+def _run_tiles(cfg, params, pk, pv, noise, state, mode, tiles):
+    gu = _gu()
+    ex = gu.build_expert(cfg, params, mode)
+    try:
+        ex.set_option("large_m_tiles", tiles)
+        bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+        ex.denoise()
+        ex.check()
+        torch.cuda.synchronize()
+        return bufs["actions"].cpu().numpy()
+    finally:
+        ex.close()
+
+
+@pytest.mark.parametrize("variant,batch,horizon,width", [
+    ("pi05", 8, 50, 256),     # 400 rows: two 224-token tiles, the second ragged
+    ("pi05", 21, 13, 256),    # 273 rows: tiles past the padded row count
+    ("pi0", 6, 50, 256),      # pi0's time-MLP GEMM on the 256-column tiles too
+    ("pi05", 12, 50, 1024),   # pi0.5 widths (qkv 2560 columns, K splits of o and down), 600 rows
+])
+def test_large_m_wide_tiles_match_oracle(variant, batch, horizon, width):
+    """The large-M GEMM tile plans in graph and eager launch, each against
+    the oracle on the whole batch: 256-column tiles (direct-to-LDS ring, one
+    workgroup per compute unit) forced for every GEMM whose shape takes them,
+    128-column tiles only, and the default plan (256-column tiles for
+    gate/up). Bounds as for the batch-1 bf16 expert: relative L2 2e-3, of the
+    displacement 5e-3, largest element 1e-2 (measured at most 2.8e-4,
+    1.6e-3, 2.2e-3: the pi0 case, whose displacement is smallest)."""
+    gu = _gu()
+    from oracle import pi0 as P0
+    base = CONFIGS["pi0_tiny_fp32" if variant == "pi0" else "tiny_fp32"]
+    extra = {}
+    if width == 1024:
+        extra = dict(width=1024, num_q_heads=8, num_kv_heads=1, head_dim=256, mlp_dim=4096, time_emb_dim=1024)
+    cfg = base.replace(weight_precision="bf16", batch=batch, action_horizon=horizon, prefix_len=70,
+                       state_dim=base.state_dim or 6, seed=80 + batch, **extra)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    run = P0.denoise_pi0 if variant == "pi0" else O.denoise
+    ref = run(params, noise, state, pk, pv, cfg)
+    for mode in ("graph", "eager"):
+        for tiles in ("wide", "narrow", "auto"):
+            print(f"case large-M tiles {variant} B={batch} H={horizon} W={width} {mode} {tiles}", flush=True)
+            got = _run_tiles(cfg, params, pk, pv, noise, state, mode, tiles)
+            gu.assert_parity(got, ref, noise, 2e-3, 5e-3, 1e-2, label=f"{mode} {tiles}")
+
+
 def test_auto_launch_mode_keeps_the_persistent_kernel_for_few_rows():
     """Below 256 rows (and for fp32 weights at any size) the default launch
     mode is the persistent kernel: bitwise the same actions."""

@@ -95,6 +95,18 @@ __device__ __forceinline__ void coh_st4(void* base, uint32_t off, uint32_t v) {
 __device__ __forceinline__ void coh_st2(void* base, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, rsrc(base), off, 0, CPOL_SC1);
 }
+// Ordinary write-back stores, for results read only by later launches (the
+// kernel boundary makes them visible): partial lines merge in L2 instead of
+// going through to memory one piece at a time as device-coherent stores do.
+__device__ __forceinline__ void wb_st16(void* base, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), off, 0, 0);
+}
+__device__ __forceinline__ void wb_st8(void* base, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, rsrc(base), off, 0, 0);
+}
+__device__ __forceinline__ void wb_st4(void* base, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, rsrc(base), off, 0, 0);
+}
 // read-only data (weights, prefix KV, tables): ordinary cached loads
 __device__ __forceinline__ u32x4 ro_ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -136,13 +148,14 @@ __device__ __forceinline__ u32x4 as_u4(floatx4 v) { return __builtin_bit_cast(u3
 // ------------------------------------------------------------------ math
 // exp2 via the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-// GELU, tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3);
-// tanh(z) = 1 - 2 / (exp(2z) + 1), with exp(2z) = exp2(2 z log2(e)).
+// GELU, tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3).
+// With e = exp(2z): 0.5 (1 + tanh z) = e / (e + 1), so the value is
+// u - u / (e + 1), one exp2 and one hardware reciprocal (e = inf gives u,
+// e = 0 gives 0); exp(2z) = exp2(2 log2(e) sqrt(2/pi) (u + 0.044715 u^3)).
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
-  const float e = fast_exp2(2.8853900817779268f * z);
-  const float th = 1.0f - 2.0f / (e + 1.0f);
-  return 0.5f * u * (1.0f + th);
+  const float t = __builtin_fmaf(0.044715f * u * u, u, u);
+  const float e = fast_exp2(2.3022082f * t);
+  return __builtin_fmaf(-u, __builtin_amdgcn_rcpf(e + 1.0f), u);
 }
 
 __device__ __forceinline__ float warp_sum(float v) {

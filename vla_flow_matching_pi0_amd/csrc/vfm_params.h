@@ -15,6 +15,10 @@ constexpr int MAX_KSPLIT = 16;     // K splits of the residual GEMMs
 constexpr int BAR_COUNTERS = 64;
 constexpr int BAR_WORDS = 64 + 64 * BAR_COUNTERS;
 constexpr long BARRIER_SPIN_LIMIT_HOST = 1L << 22;   // default polls before a device-wide wait gives up
+// large-M GEMM, 256-column tiles of 224 / 256 tokens: stages of 32 K in the
+// LDS ring (a pass takes an even stage count of at least the ring less one)
+constexpr int GW_RING_224 = 5;
+constexpr int GW_RING_256 = 4;
 
 enum Phase {
   PH_BOUNDARY = 0, PH_RN_ATTN, PH_QKV, PH_ATTN, PH_COMBINE, PH_O, PH_RN_MLP, PH_GU, PH_DOWN, PH_TMLP, PH_COUNT
@@ -27,7 +31,7 @@ struct VP {
   int L, W, Hq, Hkv, d, F, H, A, S, N, B, P, M, n_norms, KS, kps;
   int pi0;                 // variant: 0 pi0.5 (adaptive norms), 1 pi0 (state token, action-time MLP)
   int bigm;                // graph / eager launch of a bf16 expert with many rows: large-tile GEMM kernels
-  int gp_bm[5];            // large-M GEMMs: tokens per tile (128 or 64), same order as gp_nt
+  int gp_bm[5];            // large-M GEMMs: tokens per tile (128 or 64; 224 or 256: 256-column tiles), same order as gp_nt
   int gp_nt[5], gp_s[5];   // GEMM plan (qkv, o, gateup, down, time MLP out): tiles per unit, K splits
   int S_o, S_down;         // = gp_s[1], gp_s[3]
   float eps;

@@ -1177,6 +1177,45 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
 constexpr int GM_THREADS = 256;
 constexpr int GM_LDS = 2 * 32768;   // two stages of (A tile + B tile)
 
+// One 16 x 16 accumulator tile of a large-M GEMM: this lane's four columns
+// 16 tile + 4g .. +3 of token gm (the MFMA output layout), through the
+// GEMM's epilogue: RoPE into the q / k tiles (v as is), GeGLU into the
+// down projection's operand, or the K split's partial sums. These GEMMs
+// run as launches of their own, so their results take write-back stores.
+template <typename T, int WHICH>
+__device__ __forceinline__ void gemm_m_store(const VP& p, uint8_t* sl, int tile, int gm, int s, int g, floatx4 vv) {
+  if (WHICH == G_QKV) {
+    const int d = p.d;
+    const int col0 = tile * 16;
+    const int head = col0 / d, tt = (col0 % d) / 16;
+    const int b = gm / p.H, ti = gm % p.H;
+    if (head < p.Hq + p.Hkv) {
+      const int j0 = tt * 8 + 2 * g;
+      const floatx4 rot = as_f4(ro_ld16(p.rope + ((size_t)ti * (d / 2) + j0) * 2));
+      const float y0 = vv.x * rot[0] - vv.z * rot[1], y0h = vv.z * rot[0] + vv.x * rot[1];
+      const float y1 = vv.y * rot[2] - vv.w * rot[3], y1h = vv.w * rot[2] + vv.y * rot[3];
+      const bool isq = head < p.Hq;
+      uint8_t* dst = sl + (isq ? p.off_q : p.off_k);
+      const size_t hb = isq ? (size_t)b * p.Hq + head : (size_t)b * p.Hkv + (head - p.Hq);
+      const size_t e0 = ((hb * (d / 16) + tt) * 64 + ti) * 16 + 2 * g;
+      wb_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(y0, y1));
+      wb_st4(dst, (uint32_t)((e0 + 8) * 2), pack_bf16x2(y0h, y1h));
+    } else {
+      const int kvh = head - p.Hq - p.Hkv;
+      const size_t e0 = ((((size_t)b * p.Hkv + kvh) * (d / 16) + tt) * 64 + ti) * 16 + 4 * g;
+      wb_st8(sl + p.off_v, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(vv.x, vv.y), pack_bf16x2(vv.z, vv.w)});
+    }
+  } else if (WHICH == G_GU) {
+    const int f0 = tile * 8 + 2 * g;
+    const float a0 = gelu_tanh(vv.x) * vv.y, a1 = gelu_tanh(vv.z) * vv.w;
+    wb_st4(sl + p.off_act, (uint32_t)(act_off<T>(p, gm, f0) * 2), pack_bf16x2(a0, a1));
+  } else {
+    float* part = WHICH == G_O ? p.part_o : p.part_d;
+    const int n0 = tile * 16 + 4 * g;
+    wb_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(vv));
+  }
+}
+
 // BM: tokens per tile, 128 or 64 (a 64-token tile where 128-token tiles
 // would leave a few compute units with a second tile: waves then take 64
 // columns x 32 tokens).
@@ -1269,37 +1308,243 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int gm = mt * BM + wm * (BM / 2) + j * 16 + c16;
-      if (gm >= p.M) continue;
-      const floatx4 vv = acc[i][j];
-      if (WHICH == G_QKV) {
-        const int d = p.d;
-        const int col0 = tile * 16;
-        const int head = col0 / d, tt = (col0 % d) / 16;
-        const int b = gm / p.H, ti = gm % p.H;
-        if (head < p.Hq + p.Hkv) {
-          const int j0 = tt * 8 + 2 * g;
-          const floatx4 rot = as_f4(ro_ld16(p.rope + ((size_t)ti * (d / 2) + j0) * 2));
-          const float y0 = vv.x * rot[0] - vv.z * rot[1], y0h = vv.z * rot[0] + vv.x * rot[1];
-          const float y1 = vv.y * rot[2] - vv.w * rot[3], y1h = vv.w * rot[2] + vv.y * rot[3];
-          const bool isq = head < p.Hq;
-          uint8_t* dst = sl + (isq ? p.off_q : p.off_k);
-          const size_t hb = isq ? (size_t)b * p.Hq + head : (size_t)b * p.Hkv + (head - p.Hq);
-          const size_t e0 = ((hb * (d / 16) + tt) * 64 + ti) * 16 + 2 * g;
-          coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(y0, y1));
-          coh_st4(dst, (uint32_t)((e0 + 8) * 2), pack_bf16x2(y0h, y1h));
-        } else {
-          const int kvh = head - p.Hq - p.Hkv;
-          const size_t e0 = ((((size_t)b * p.Hkv + kvh) * (d / 16) + tt) * 64 + ti) * 16 + 4 * g;
-          coh_st8(sl + p.off_v, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(vv.x, vv.y), pack_bf16x2(vv.z, vv.w)});
+      if (gm < p.M) gemm_m_store<T, WHICH>(p, sl, tile, gm, s, g, acc[i][j]);
+    }
+  }
+}
+
+// ============================================================ wide large-M GEMM
+// The tiles above stage 32 KB of operands through registers into LDS per
+// 64-K step and read 16 KB of it back per wave for 32 MFMAs, so the vector
+// memory, LDS and MFMA pipes each need about the same cycles and the single
+// stage in flight leaves the load latency exposed. This kernel takes 256
+// output columns x 32 MB tokens per workgroup (one per compute unit, four
+// waves of 128 columns x 16 MB tokens): a 32-K step reads 8 + MB fragments
+// per wave for 8 MB MFMAs, and the accumulators (32 MB registers) sit in the
+// accumulation half of the unified register file. Both operand tiles go
+// from global memory straight into an LDS ring of NS stages of 32 K
+// (direct-to-LDS loads of 16 bytes per lane, no registers), issued NS - 1
+// stages ahead of their use. The copies are inline asm: the compiler would
+// otherwise treat each later LDS read as possibly aliasing a copy in flight
+// and wait for all of them; each wave waits for its own copies by count
+// instead. One barrier per stage: after it the stage has landed everywhere
+// and every wave is done with the previous stage, whose slot the copies
+// issued during this stage refill. Within the stage the weight fragments
+// are read two MFMA groups ahead of their use and the copies are spread
+// over the groups, so that the MFMAs cover both.
+constexpr int GW_THREADS = 256;
+constexpr int GW_LDS_MAX = 160 * 1024;
+
+template <int MB>
+struct GW {
+  static constexpr int NB = 16 + 2 * MB;   // 1 KiB blocks per 32-K stage: 16 of weights, 2 MB of tokens
+  static constexpr int SLOT = NB * 1024;
+  // copies per wave and stage, the same for every wave (so that every wait
+  // is one immediate): blocks w, w + 4, ...; a wave with a slot left over
+  // copies its first block once more into a spare KiB past the ring
+  static constexpr int CW = (NB + 3) / 4;
+  static constexpr int SPARE = (4 * CW - NB) * 1024;
+  static constexpr int NS = (GW_LDS_MAX - 4096) / SLOT >= 5 ? 5 : (GW_LDS_MAX - 4096) / SLOT;
+  static constexpr int LDS = NS * SLOT + SPARE;
+  static constexpr int BMT = 32 * MB;                          // tokens per tile
+  static_assert(NS >= 4, "the ring needs four stages");
+  static_assert((NS - 2) * CW <= 63, "vmcnt range");
+  static_assert(16 * MB * 1024 <= NS * SLOT, "the epilogue's staging fits in the ring");
+};
+
+static_assert(GW<7>::NS == GW_RING_224 && GW<8>::NS == GW_RING_256, "ring depths known to the planner");
+
+template <int N>
+__device__ __forceinline__ void gw_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void gw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// one direct-to-LDS copy of 16 bytes per lane: global base + voff -> LDS m0 + 16 lane
+__device__ __forceinline__ void gw_copy(const void* base, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+// One wave per SIMD (the LDS ring takes the compute unit): the scheduler is
+// told so, or it trades latency hiding for registers it cannot use.
+template <typename T, int WHICH, int MB>
+__global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_w(VP p, int step,
+                                                                                                     int layer) {
+  static_assert(sizeof(T) == 2, "the wide large-M GEMM runs bf16 operands");
+  using C = GW<MB>;
+  const GemmShape gs = gemm_shape<T, WHICH, WF_NATIVE>(p, layer);
+  const int K = gs.K, N = gs.N, S = gs.S;
+  const int Mpad = ((p.M + 63) / 64) * 64;
+  const int MTL = (p.M + C::BMT - 1) / C::BMT, NTL = N / 256, total = MTL * NTL * S;
+  const int per = (total + 7) >> 3;
+  const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (v >= total) return;
+  const int mt = v % MTL, nt = (v / MTL) % NTL, s = v / (MTL * NTL);
+  const int KB32 = K >> 5, nst = (K / S) >> 5, kb0 = s * nst;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wn = w & 1, wm = w >> 1;
+  uint8_t* sl = slab(p, step, layer);
+  const uint8_t* act;
+  if (WHICH == G_QKV) act = sl + p.off_xna;
+  else if (WHICH == G_O) act = sl + p.off_attn;
+  else if (WHICH == G_GU) act = sl + p.off_xnm;
+  else if (WHICH == G_DOWN) act = sl + p.off_act;
+  else act = sl + p.off_u;
+  const uint8_t* wsrc = gs.Wp;
+  // this wave's copies per stage: blocks w + 4i; i < 4 are weight column tiles
+  // nt * 16 + w + 4i, the rest token blocks j = w + 4 (i - 4) (16 tokens, rows
+  // past the padded count read its last row; their outputs are dropped). The
+  // LDS block of copy i is w + 4i either way. A token block goes to LDS in
+  // lane order: lane (c, g) (c = lane & 15) takes token c's K-group g.
+  uint32_t voff[C::CW];
+#pragma unroll
+  for (int i = 0; i < C::CW; ++i) {
+    if (i < 4) {
+      voff[i] = (uint32_t)(((nt * 16 + w + 4 * i) * KB32 + kb0) * 1024 + lane * 16);
+    } else {
+      const int j = w + 4 * (i - 4);
+      int m = mt * C::BMT + j * 16 + (lane & 15);
+      m = m < Mpad ? m : Mpad - 1;
+      voff[i] = (uint32_t)((((size_t)kb0 * Mpad + m) * 32 + (lane >> 4) * 8) * 2);
+    }
+  }
+  const uint32_t astep = (uint32_t)(Mpad * 64);   // one 32-K block of tokens
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+  const u32x4* L = reinterpret_cast<const u32x4*>(smem);
+  auto frag_a = [&](int st, int i) { return L[(st % C::NS) * (C::SLOT / 16) + (wn * 8 + i) * 64 + lane]; };
+  auto frag_b = [&](int st, int j) { return L[(st % C::NS) * (C::SLOT / 16) + (16 + wm * MB + j) * 64 + lane]; };
+
+  floatx4 acc[8][MB];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // The pipeline. Every stage issues the same copies (CW per wave: the
+  // stages past the last one copy the last one again, into the slot that is
+  // free anyway), so every wait is the same immediate and the loop body is
+  // one basic block: the scheduler may then hide the copies' and reads'
+  // issue behind the MFMAs, and the register allocator keeps the
+  // accumulators in place.
+  constexpr int CW = C::CW;
+  const int nreal = (C::NB - w + 3) / 4;   // this wave's real copies; the rest repeat copy 0 into a spare KiB
+  const uint32_t spare = lds0 + (uint32_t)(C::NS * C::SLOT + (w & 1) * 1024);
+  // copy i of stage cst into slot `slot`
+  auto copy = [&](int i, int cst, int slot) {
+    const uint32_t dst = lds0 + (uint32_t)(slot * C::SLOT + w * 1024 + 4096 * i);
+    if (i < 4) {
+      gw_copy(wsrc, voff[i] + (uint32_t)cst * 1024u, dst);
+    } else {
+      const bool real = i < nreal;
+      gw_copy(real ? act : wsrc, real ? voff[i] + (uint32_t)cst * astep : voff[0] + (uint32_t)cst * 1024u,
+              real ? dst : spare);
+    }
+  };
+  // prologue: stages 0 .. NS - 2 in flight (nst >= NS - 1)
+#pragma unroll
+  for (int st = 0; st < C::NS - 1; ++st)
+#pragma unroll
+    for (int i = 0; i < CW; ++i) copy(i, st, st);
+  for (int st = 0; st < nst; ++st) {
+    // this wave's copies of stage st have landed (the NS - 2 stages after it
+    // may still be in flight), then the barrier: every wave's copies of stage
+    // st have landed and every wave is done with stage st - 1, whose slot
+    // this stage's copies refill (with stage st + NS - 1, or the last again)
+    // (the last NS - 2 stages wait for every copy: the same for the stages
+    // that count, and the branch keeps the register allocator from turning
+    // the accumulation into copy-and-accumulate pairs, as it does when the
+    // whole loop body is one basic block)
+    if (st + C::NS - 2 < nst) gw_vmcnt<(C::NS - 2) * CW>();
+    else gw_vmcnt<0>();
+    gw_barrier();
+    const int cst = st + C::NS - 1 < nst ? st + C::NS - 1 : nst - 1;
+    const int cslot = (st + C::NS - 1) % C::NS;
+    u32x4 fa[8], fb[MB];
+    fa[0] = frag_a(st, 0);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) fb[j] = frag_b(st, j);
+    fa[1] = frag_a(st, 1);
+    // Program order is kept (scheduling barriers): weight fragment i + 2 is
+    // requested during MFMA group i, and copy i issued in its middle, so
+    // that the MFMAs cover both the reads' latency and the copies' issue.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        acc[i][j] = MT<T>::mma(fa[i], fb[j], acc[i][j]);
+        if (j == 0 && i + 2 < 8) fa[i + 2] = frag_a(st, i + 2);
+        if (j == 2 && i < CW) copy(i, cst, cslot);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  gw_vmcnt<0>();   // the repeated copies of the last stages land before the ring is reused or released
+
+  const int g = lane >> 4, c16 = lane & 15;
+  if constexpr (WHICH == G_GU || WHICH == G_QKV) {
+    // Epilogues that compute on the sums (GeGLU, RoPE) take them back from
+    // LDS, half a wave tile at a time: computing on them in place leads the
+    // register allocator to keep the accumulators in ordinary registers (the
+    // loop's operands then spill), and GeGLU reads them back transposed for
+    // whole-row stores. The ring is free once every wave is past this
+    // barrier (all copies have landed: each wave waited for its own).
+    gw_barrier();
+    floatx4* E = reinterpret_cast<floatx4*>(smem + w * (4 * MB * 1024));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) E[(i * MB + j) * 64 + lane] = acc[4 * h + i][j];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (WHICH == G_GU) {
+        // Read back transposed: lane (token c, tile il of the four) takes
+        // all 16 sums of its token in that tile (the four 16-byte pieces of
+        // lanes (c, 0..3)), i.e. gate and up of 8 consecutive features, and
+        // stores their 8 GeGLU values as one 16-byte piece; the four tiles
+        // of a token are one 64-byte row of the down projection's operand,
+        // so each store writes 16 whole rows.
+        // Rows past the batch get an offset beyond the buffer range, which
+        // drops the store: the code stays one block, so the reads are all
+        // issued before the first GeGLU.
+        const int c = lane & 15, il = lane >> 4;
+        const int f0 = (nt * 16 + wn * 8 + 4 * h + il) * 8;
+        floatx4 q[MB][4];
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) q[j][gg] = E[(il * MB + j) * 64 + gg * 16 + c];
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          u32x4 y;
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            y[gg] = pack_bf16x2(gelu_tanh(q[j][gg].x) * q[j][gg].y, gelu_tanh(q[j][gg].z) * q[j][gg].w);
+          const int gm = mt * C::BMT + (wm * MB + j) * 16 + c;
+          const uint32_t off = gm < p.M ? (uint32_t)(act_off<T>(p, gm, f0) * 2) : 0x80000000u;
+          wb_st16(sl + p.off_act, off, y);
         }
-      } else if (WHICH == G_GU) {
-        const int f0 = tile * 8 + 2 * g;
-        const float a0 = gelu_tanh(vv.x) * vv.y, a1 = gelu_tanh(vv.z) * vv.w;
-        coh_st4(sl + p.off_act, (uint32_t)(act_off<T>(p, gm, f0) * 2), pack_bf16x2(a0, a1));
       } else {
-        float* part = WHICH == G_O ? p.part_o : p.part_d;
-        const int n0 = tile * 16 + 4 * g;
-        coh_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(vv));
+        floatx4 vq[4 * MB];
+#pragma unroll
+        for (int q = 0; q < 4 * MB; ++q) vq[q] = E[q * 64 + lane];
+#pragma unroll
+        for (int q = 0; q < 4 * MB; ++q) {
+          const int i = q / MB, j = q % MB;
+          const int tile = nt * 16 + wn * 8 + 4 * h + i;
+          const int gm = mt * C::BMT + (wm * MB + j) * 16 + c16;
+          if (gm < p.M) gemm_m_store<T, WHICH>(p, sl, tile, gm, s, g, vq[q]);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tile = nt * 16 + wn * 8 + i;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int gm = mt * C::BMT + (wm * MB + j) * 16 + c16;
+        if (gm < p.M) gemm_m_store<T, WHICH>(p, sl, tile, gm, s, g, acc[i][j]);
       }
     }
   }
@@ -1677,6 +1922,28 @@ __global__ __launch_bounds__(NTH) void k_phase(VP p, int k, int l) {
 template <typename T, int D, int WF, bool CAL>
 __host__ const void* phase_kernel(int ph, bool bigm = false, int bm = 128) {
   if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
+    if (bigm && (bm == 224 || bm == 256)) {
+      // the wide tiles: 256 columns x bm tokens
+      if (bm == 224) {
+        switch (ph) {
+          case PH_QKV: return (const void*)&k_gemm_w<T, G_QKV, 7>;
+          case PH_O: return (const void*)&k_gemm_w<T, G_O, 7>;
+          case PH_GU: return (const void*)&k_gemm_w<T, G_GU, 7>;
+          case PH_DOWN: return (const void*)&k_gemm_w<T, G_DOWN, 7>;
+          case PH_TMLP: return (const void*)&k_gemm_w<T, G_TMLP, 7>;
+          default: break;
+        }
+      } else {
+        switch (ph) {
+          case PH_QKV: return (const void*)&k_gemm_w<T, G_QKV, 8>;
+          case PH_O: return (const void*)&k_gemm_w<T, G_O, 8>;
+          case PH_GU: return (const void*)&k_gemm_w<T, G_GU, 8>;
+          case PH_DOWN: return (const void*)&k_gemm_w<T, G_DOWN, 8>;
+          case PH_TMLP: return (const void*)&k_gemm_w<T, G_TMLP, 8>;
+          default: break;
+        }
+      }
+    }
     if (bigm && bm == 64) {
       switch (ph) {
         case PH_QKV: return (const void*)&k_gemm_m<T, G_QKV, 64>;
@@ -1747,6 +2014,11 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
   if (bigm) {
     const int gi = phase == PH_QKV ? 0 : phase == PH_O ? 1 : phase == PH_GU ? 2 : phase == PH_DOWN ? 3 : 4;
     bm = p.gp_bm[gi];
+    if constexpr (sizeof(T) == 2 && WF == WF_NATIVE && !CAL) {
+      if (bm == 224 || bm == 256)   // the wide tiles' LDS ring
+        return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, true, bm), dim3(grid), dim3(GW_THREADS), args,
+                               (size_t)(bm == 224 ? GW<7>::LDS : GW<8>::LDS), st);
+    }
   }
   return hipLaunchKernel(phase_kernel<T, D, WF, CAL>(phase, bigm, bm), dim3(grid), dim3(bigm ? GM_THREADS : NTH),
                          args, lds, st);
@@ -1760,10 +2032,10 @@ hipError_t set_lds_limit(int bytes) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph) {
     e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    for (int bm : {128, 64}) {
+    for (int bm : {128, 64, 224, 256}) {
       const void* big = phase_kernel<T, D, WF, CAL>(ph, true, bm);
       if (e == hipSuccess && big != phase_kernel<T, D, WF, CAL>(ph)) {
-        const int need = ph == PH_ATTN ? AttnMLds<D>::TOTAL : GM_LDS;
+        const int need = ph == PH_ATTN ? AttnMLds<D>::TOTAL : bm == 224 ? GW<7>::LDS : bm == 256 ? GW<8>::LDS : GM_LDS;
         e = hipFuncSetAttribute(big, hipFuncAttributeMaxDynamicSharedMemorySize, bytes > need ? bytes : need);
       }
     }

@@ -106,6 +106,7 @@ struct vfm_expert {
   size_t lds = 0;
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
+  int gemm_tiles = 0;        // large-M GEMMs: 0 auto, 1 128-column tiles only, 2 256-column tiles where they apply
   // graph variants, most recently used first: key = shape + pointers
   struct GraphEntry {
     std::vector<uintptr_t> key;
@@ -428,14 +429,16 @@ int phase_grid(const VP& p, int phase) {
   long units = 1;
   if (p.bigm) {
     // large-M GEMM kernels: one workgroup per 128 x 128 tile and K split, rounded up to whole XCD rounds
+    // (wide tiles, 224 or 256 tokens: 256 columns)
     auto mtl = [&](int i) { return cdiv(p.M, p.gp_bm[i]); };
+    auto ncol = [&](int i) { return p.gp_bm[i] > 128 ? 256 : 128; };
     long tiles = -1;
     switch (phase) {
-      case vfm::PH_QKV: tiles = (long)(p.Hq + 2 * p.Hkv) * p.d / 128 * mtl(0) * p.gp_s[0]; break;
-      case vfm::PH_O: tiles = (long)p.W / 128 * mtl(1) * p.gp_s[1]; break;
-      case vfm::PH_GU: tiles = (long)2 * p.F / 128 * mtl(2) * p.gp_s[2]; break;
-      case vfm::PH_DOWN: tiles = (long)p.W / 128 * mtl(3) * p.gp_s[3]; break;
-      case vfm::PH_TMLP: tiles = (long)p.W / 128 * mtl(4) * p.gp_s[4]; break;
+      case vfm::PH_QKV: tiles = (long)(p.Hq + 2 * p.Hkv) * p.d / ncol(0) * mtl(0) * p.gp_s[0]; break;
+      case vfm::PH_O: tiles = (long)p.W / ncol(1) * mtl(1) * p.gp_s[1]; break;
+      case vfm::PH_GU: tiles = (long)2 * p.F / ncol(2) * mtl(2) * p.gp_s[2]; break;
+      case vfm::PH_DOWN: tiles = (long)p.W / ncol(3) * mtl(3) * p.gp_s[3]; break;
+      case vfm::PH_TMLP: tiles = (long)p.W / ncol(4) * mtl(4) * p.gp_s[4]; break;
       // single-pass attention: one workgroup per (sample, head), samples in groups of 8 (one per XCD)
       case vfm::PH_ATTN: tiles = (long)cdiv(p.B, 8) * 8 * p.Hq; break;
       default: break;
@@ -528,6 +531,16 @@ vfm_status expert_stage_io(const vfm_expert* x, const float* noise, const float*
 }
 }  // namespace vfm
 
+// Whether large-M GEMM i (qkv, o, gate/up, down, time MLP) of N columns runs
+// the 256-column tiles: gate/up by default, any GEMM when asked for. At batch
+// 32 (pi0.5 widths) the others measured no faster: qkv's 2560 columns make
+// too few tiles, and o and down need twice the K splits, whose partial sums
+// the next row phase then reads.
+static bool wide_tiles(const vfm_expert* x, int i, int N) {
+  if (N % 256 != 0 || x->gemm_tiles == 1) return false;
+  return x->gemm_tiles == 2 || i == 2;
+}
+
 // The launch parameter block of one call: shapes, weights, workspace,
 // buffers and the GEMM plan for the expert's weight format.
 vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const float* state, float* actions) {
@@ -581,6 +594,30 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
         // few units: 64-token tiles spread the same work about two per unit, both resident at once
         const long t128 = (long)(Ns[i] / 128) * mt * sp;
         p.gp_bm[i] = (t128 > 256 && t128 <= 384) ? 64 : 128;
+        if (wide_tiles(x, i, Ns[i])) {
+          // 256 columns x 224 or 256 tokens, one tile per compute unit: the token count with the fewer
+          // tokens per unit over the whole grid, and for the linear GEMMs K splits (whole 32-K stages)
+          // until the tiles fill the 256 units
+          int best_bm = 224, best_sp = 1;
+          long best_cost = -1;
+          for (int bmw : {224, 256}) {
+            const long mtw = (p.M + bmw - 1) / bmw;
+            int spw = 1;
+            if (i != 0 && i != 2)
+              while (spw < vfm::MAX_KSPLIT && (long)(Ns[i] / 256) * mtw * spw < 256 && Ks[i] % (spw * 2 * 32) == 0)
+                spw *= 2;
+            // the kernel's pipeline takes an even number of 32-K stages, at least its ring depth less one
+            const int nst = Ks[i] / spw / 32, ring = bmw == 224 ? vfm::GW_RING_224 : vfm::GW_RING_256;
+            if (Ks[i] % (spw * 32) != 0 || nst % 2 != 0 || nst < ring - 1) continue;
+            const long tiles = (long)(Ns[i] / 256) * mtw * spw;
+            const long cost = (tiles + 255) / 256 * bmw * (Ks[i] / spw);
+            if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bm = bmw, best_sp = spw;
+          }
+          if (best_cost >= 0) {
+            p.gp_bm[i] = best_bm;
+            p.gp_s[i] = best_sp;
+          }
+        }
       }
     }
     p.S_o = p.gp_s[1];
@@ -963,6 +1000,15 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     const long n = std::strtol(value, &end, 10);
     if (end == value || *end || n < 1 || n > 63) return fail(VFM_E_INVALID_ARG, "stream_dma_cap must be an integer in [1, 63]");
     x->ss_tune.dma_cap = (int)n;
+    return VFM_OK;
+  }
+  if (k == "large_m_tiles") {
+    // diagnostics: the large-M GEMM tiles of the per-phase launch modes
+    if (v == "auto") x->gemm_tiles = 0;
+    else if (v == "narrow") x->gemm_tiles = 1;
+    else if (v == "wide") x->gemm_tiles = 2;
+    else return fail(VFM_E_INVALID_ARG, "large_m_tiles must be 'auto', 'narrow' or 'wide'");
+    x->drop_graphs();
     return VFM_OK;
   }
   if (k == "persistent_launch") {
