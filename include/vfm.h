@@ -176,9 +176,16 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       phase barriers; "graph": one kernel per phase, captured into a
  *       hipGraph per shape and pointer set and replayed; "eager": the same
  *       kernels launched directly. With bf16 weights and B x T >= 256 rows
- *       the graph and eager modes run large-batch kernels (128 x 128 GEMM
- *       tiles, single-pass attention). "auto" chooses, per call, graph launch
- *       where those apply and the persistent kernel otherwise.
+ *       the graph and eager modes run large-batch kernels (128-column GEMM
+ *       tiles, 256-column tiles for gate/up, single-pass attention). "auto"
+ *       chooses, per call, graph launch where those apply and the persistent
+ *       kernel otherwise.
+ *   "large_m_tiles": "auto" (default), "narrow" or "wide": the large-batch
+ *       GEMM tiles of the graph and eager modes: 256 columns x 224 or 256
+ *       tokens (one workgroup per compute unit, a direct-to-LDS operand
+ *       ring) for gate/up only, for no GEMM, or for every GEMM whose column
+ *       count is a multiple of 256. Results agree to rounding (K splits
+ *       differ). Invalidates captured graphs.
  *   "persistent_launch": "cooperative" (default) or "plain": how the
  *       persistent kernel is launched. "plain" is an ordinary launch of the
  *       same grid (one workgroup per compute unit, from the occupancy query);
@@ -383,6 +390,14 @@ vfm_status vfm_prefix_run(vfm_prefix* pre, const void* embeds, int32_t batch, in
  * lookup or launch failure). */
 vfm_status vfm_prefix_run_noalloc(vfm_prefix* pre, const void* embeds, int32_t batch, int32_t prefix_len,
                                   void* prefix_k, void* prefix_v, void* stream);
+
+/* Options (string key/value), host-only:
+ *   "gate_up_tiles": "wide" (default) or "narrow": the gate/up GEMM on
+ *       256-column tiles (one workgroup per compute unit, a direct-to-LDS
+ *       operand ring; used where N is a multiple of 256 and K of 64) or on
+ *       the 128 x 128 tiles of the other GEMMs. Results agree to rounding.
+ * Errors: VFM_E_INVALID_ARG for a NULL argument or an unknown key or value. */
+vfm_status vfm_prefix_set_option(vfm_prefix* pre, const char* key, const char* value);
 
 /* Synchronise the device and free everything the producer owns. NULL-safe. */
 vfm_status vfm_prefix_destroy(vfm_prefix* pre);

@@ -105,6 +105,53 @@ def test_rerun_with_other_shapes_on_one_producer():
     pre.close()
 
 
+@pytest.mark.parametrize("which", ["tiny_ragged", "gemma_two_layers"])
+def test_gate_up_tiles_agree(which):
+    """The gate/up GEMM on the 256-column tiles (the default where the shape
+    takes them) and on the 128 x 128 tiles: both against the oracle per
+    layer, and against each other: the same bf16 products summed in the
+    same order and the same epilogue arithmetic, so the keys and values are
+    bitwise equal (measured so on both shapes; asserted to 1e-3)."""
+    from vla_flow_matching_pi0_amd import vfm
+    if which == "tiny_ragged":   # 390 tokens: the last token tile ragged, tiles past the padded count
+        cfg = PREFIX_CONFIGS["prefix_tiny"].replace(batch=3, prefix_len=130, seed=71)
+    else:
+        cfg = PREFIX_CONFIGS["prefix_gemma2b_p560"].replace(num_layers=2, seed=72)
+    params, emb = make_prefix_inputs(cfg)
+    rk, rv = PO.prefix_kv(params, emb, cfg)
+    got = {}
+    for tiles in ("narrow", "wide"):
+        print(f"case prefix gate/up tiles {which} {tiles}", flush=True)
+        dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
+        pre = vfm.PrefixProducer(cfg, dev)
+        del dev
+        pre.set_option("gate_up_tiles", tiles)
+        pre, k, v = run_producer(cfg, params, emb, producer=pre)
+        pre.close()
+        check_layers(k, v, rk, rv)
+        got[tiles] = (k, v)
+    for l in range(cfg.num_layers):
+        ek = rel_l2(got["wide"][0][l], got["narrow"][0][l])
+        ev = rel_l2(got["wide"][1][l], got["narrow"][1][l])
+        print(f"layer {l}: wide vs narrow k {ek:.3e} v {ev:.3e}")
+        assert ek <= 1e-3 and ev <= 1e-3, l
+
+
+def test_prefix_option_is_validated():
+    from vla_flow_matching_pi0_amd import vfm
+    cfg = PREFIX_CONFIGS["prefix_tiny"]
+    params, _ = make_prefix_inputs(cfg)
+    dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
+    pre = vfm.PrefixProducer(cfg, dev)
+    try:
+        for key, val in (("gate_up_tiles", "huge"), ("no_such_option", "1")):
+            with pytest.raises(vfm.VfmError) as e:
+                pre.set_option(key, val)
+            assert e.value.name == "VFM_E_INVALID_ARG"
+    finally:
+        pre.close()
+
+
 def test_gemma_shape_three_layers():
     """Every kernel at the Gemma-2B per-layer shape (width 2048, 8 query heads
     sharing one KV head of dim 256, GeGLU 16384, 560 prefix tokens: the

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "vfm_device.h"
+#include "vfm_gemm_wide.h"
 #include "vfm_params.h"
 
 namespace vfm {
@@ -1317,51 +1318,12 @@ __global__ __launch_bounds__(GM_THREADS, 2) void k_gemm_m(VP p, int step, int la
 // The tiles above stage 32 KB of operands through registers into LDS per
 // 64-K step and read 16 KB of it back per wave for 32 MFMAs, so the vector
 // memory, LDS and MFMA pipes each need about the same cycles and the single
-// stage in flight leaves the load latency exposed. This kernel takes 256
-// output columns x 32 MB tokens per workgroup (one per compute unit, four
-// waves of 128 columns x 16 MB tokens): a 32-K step reads 8 + MB fragments
-// per wave for 8 MB MFMAs, and the accumulators (32 MB registers) sit in the
-// accumulation half of the unified register file. Both operand tiles go
-// from global memory straight into an LDS ring of NS stages of 32 K
-// (direct-to-LDS loads of 16 bytes per lane, no registers), issued NS - 1
-// stages ahead of their use. The copies are inline asm: the compiler would
-// otherwise treat each later LDS read as possibly aliasing a copy in flight
-// and wait for all of them; each wave waits for its own copies by count
-// instead. One barrier per stage: after it the stage has landed everywhere
-// and every wave is done with the previous stage, whose slot the copies
-// issued during this stage refill. Within the stage the weight fragments
-// are read two MFMA groups ahead of their use and the copies are spread
-// over the groups, so that the MFMAs cover both.
-constexpr int GW_THREADS = 256;
-constexpr int GW_LDS_MAX = 160 * 1024;
-
-template <int MB>
-struct GW {
-  static constexpr int NB = 16 + 2 * MB;   // 1 KiB blocks per 32-K stage: 16 of weights, 2 MB of tokens
-  static constexpr int SLOT = NB * 1024;
-  // copies per wave and stage, the same for every wave (so that every wait
-  // is one immediate): blocks w, w + 4, ...; a wave with a slot left over
-  // copies its first block once more into a spare KiB past the ring
-  static constexpr int CW = (NB + 3) / 4;
-  static constexpr int SPARE = (4 * CW - NB) * 1024;
-  static constexpr int NS = (GW_LDS_MAX - 4096) / SLOT >= 5 ? 5 : (GW_LDS_MAX - 4096) / SLOT;
-  static constexpr int LDS = NS * SLOT + SPARE;
-  static constexpr int BMT = 32 * MB;                          // tokens per tile
-  static_assert(NS >= 4, "the ring needs four stages");
-  static_assert((NS - 2) * CW <= 63, "vmcnt range");
-  static_assert(16 * MB * 1024 <= NS * SLOT, "the epilogue's staging fits in the ring");
-};
-
+// stage in flight leaves the load latency exposed. The 256-column tiles of
+// vfm_gemm_wide.h (one workgroup per compute unit, a 5-stage direct-to-LDS
+// ring) run gate/up by default; the activation operand's token blocks come
+// from [K/32][Mpad][32] and are permuted to the MFMA lane order by the
+// copies' per-lane addresses.
 static_assert(GW<7>::NS == GW_RING_224 && GW<8>::NS == GW_RING_256, "ring depths known to the planner");
-
-template <int N>
-__device__ __forceinline__ void gw_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-__device__ __forceinline__ void gw_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// one direct-to-LDS copy of 16 bytes per lane: global base + voff -> LDS m0 + 16 lane
-__device__ __forceinline__ void gw_copy(const void* base, uint32_t voff, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_dst), "v"(voff), "s"(base)
-               : "memory", "m0");
-}
 
 // One wave per SIMD (the LDS ring takes the compute unit): the scheduler is
 // told so, or it trades latency hiding for registers it cannot use.
@@ -1388,7 +1350,6 @@ __global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
   else if (WHICH == G_GU) act = sl + p.off_xnm;
   else if (WHICH == G_DOWN) act = sl + p.off_act;
   else act = sl + p.off_u;
-  const uint8_t* wsrc = gs.Wp;
   // this wave's copies per stage: blocks w + 4i; i < 4 are weight column tiles
   // nt * 16 + w + 4i, the rest token blocks j = w + 4 (i - 4) (16 tokens, rows
   // past the padded count read its last row; their outputs are dropped). The
@@ -1406,78 +1367,12 @@ __global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
       voff[i] = (uint32_t)((((size_t)kb0 * Mpad + m) * 32 + (lane >> 4) * 8) * 2);
     }
   }
-  const uint32_t astep = (uint32_t)(Mpad * 64);   // one 32-K block of tokens
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-  const u32x4* L = reinterpret_cast<const u32x4*>(smem);
-  auto frag_a = [&](int st, int i) { return L[(st % C::NS) * (C::SLOT / 16) + (wn * 8 + i) * 64 + lane]; };
-  auto frag_b = [&](int st, int j) { return L[(st % C::NS) * (C::SLOT / 16) + (16 + wm * MB + j) * 64 + lane]; };
-
   floatx4 acc[8][MB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // The pipeline. Every stage issues the same copies (CW per wave: the
-  // stages past the last one copy the last one again, into the slot that is
-  // free anyway), so every wait is the same immediate and the loop body is
-  // one basic block: the scheduler may then hide the copies' and reads'
-  // issue behind the MFMAs, and the register allocator keeps the
-  // accumulators in place.
-  constexpr int CW = C::CW;
-  const int nreal = (C::NB - w + 3) / 4;   // this wave's real copies; the rest repeat copy 0 into a spare KiB
-  const uint32_t spare = lds0 + (uint32_t)(C::NS * C::SLOT + (w & 1) * 1024);
-  // copy i of stage cst into slot `slot`
-  auto copy = [&](int i, int cst, int slot) {
-    const uint32_t dst = lds0 + (uint32_t)(slot * C::SLOT + w * 1024 + 4096 * i);
-    if (i < 4) {
-      gw_copy(wsrc, voff[i] + (uint32_t)cst * 1024u, dst);
-    } else {
-      const bool real = i < nreal;
-      gw_copy(real ? act : wsrc, real ? voff[i] + (uint32_t)cst * astep : voff[0] + (uint32_t)cst * 1024u,
-              real ? dst : spare);
-    }
-  };
-  // prologue: stages 0 .. NS - 2 in flight (nst >= NS - 1)
-#pragma unroll
-  for (int st = 0; st < C::NS - 1; ++st)
-#pragma unroll
-    for (int i = 0; i < CW; ++i) copy(i, st, st);
-  for (int st = 0; st < nst; ++st) {
-    // this wave's copies of stage st have landed (the NS - 2 stages after it
-    // may still be in flight), then the barrier: every wave's copies of stage
-    // st have landed and every wave is done with stage st - 1, whose slot
-    // this stage's copies refill (with stage st + NS - 1, or the last again)
-    // (the last NS - 2 stages wait for every copy: the same for the stages
-    // that count, and the branch keeps the register allocator from turning
-    // the accumulation into copy-and-accumulate pairs, as it does when the
-    // whole loop body is one basic block)
-    if (st + C::NS - 2 < nst) gw_vmcnt<(C::NS - 2) * CW>();
-    else gw_vmcnt<0>();
-    gw_barrier();
-    const int cst = st + C::NS - 1 < nst ? st + C::NS - 1 : nst - 1;
-    const int cslot = (st + C::NS - 1) % C::NS;
-    u32x4 fa[8], fb[MB];
-    fa[0] = frag_a(st, 0);
-#pragma unroll
-    for (int j = 0; j < MB; ++j) fb[j] = frag_b(st, j);
-    fa[1] = frag_a(st, 1);
-    // Program order is kept (scheduling barriers): weight fragment i + 2 is
-    // requested during MFMA group i, and copy i issued in its middle, so
-    // that the MFMAs cover both the reads' latency and the copies' issue.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        acc[i][j] = MT<T>::mma(fa[i], fb[j], acc[i][j]);
-        if (j == 0 && i + 2 < 8) fa[i + 2] = frag_a(st, i + 2);
-        if (j == 2 && i < CW) copy(i, cst, cslot);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  gw_vmcnt<0>();   // the repeated copies of the last stages land before the ring is reused or released
+  gw_mainloop<MB>(acc, reinterpret_cast<uint8_t*>(smem), gs.Wp, act, voff, (uint32_t)(Mpad * 64), nst, w, lane);
 
   const int g = lane >> 4, c16 = lane & 15;
   if constexpr (WHICH == G_GU || WHICH == G_QKV) {

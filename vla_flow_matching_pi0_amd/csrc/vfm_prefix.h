@@ -66,7 +66,8 @@ struct NormArgs {
 };
 
 hipError_t prepare();
-hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st);
+// wide_gu: the gate/up GEMM (epi EPI_GU) on the 256-column tiles where the shape takes them
+hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu = true);
 hipError_t attention(int d, const AttnArgs& a, int B, hipStream_t st);
 hipError_t norm(bool first, const NormArgs& n, hipStream_t st);
 

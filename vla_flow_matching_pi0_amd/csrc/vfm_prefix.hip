@@ -9,6 +9,7 @@
 // contractions: they run on bf16 MFMA (16x16x32) with 128 x 128 tiles staged
 // through LDS, two workgroups per compute unit.
 #include "vfm_device.h"
+#include "vfm_gemm_wide.h"
 #include "vfm_prefix.h"
 
 namespace vfm {
@@ -140,6 +141,96 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ wide gate/up GEMM
+// The gate/up GEMM (the largest of the pass) on the 256-column tiles of
+// vfm_gemm_wide.h: one workgroup per compute unit, four waves of 128
+// columns x 16 MB tokens, both operands through a 5-stage direct-to-LDS
+// ring. The token blocks are stored in the MFMA lane order already, so the
+// copies are linear. Epilogue: the sums go through LDS half a wave tile at a
+// time and come back transposed, lane (token c, tile il) taking the 16 sums
+// of its token in one 16-column tile (gate and up of 8 features): their 8
+// GeGLU values are one 16-byte piece of the packed operand, and the 64
+// lanes of a store fill whole 1 KiB blocks.
+template <int MB>
+__global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_gu_w(const GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  using C = GW<MB>;
+  const int MTL = (g.M + C::BMT - 1) / C::BMT, NTL = g.N / 256, total = MTL * NTL;
+  const int per = (total + 7) >> 3;
+  const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (v >= total) return;
+  const int mt = v % MTL, nt = v / MTL;
+  const int KB32 = g.K >> 5, nblk = g.Mpad >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wn = w & 1, wm = w >> 1;
+  // copy i: weight tile nt * 16 + w + 4i (i < 4), else token block
+  // 2 MB mt + w + 4 (i - 4) (clamped to the last padded block; its outputs
+  // are not stored)
+  uint32_t voff[C::CW];
+#pragma unroll
+  for (int i = 0; i < C::CW; ++i) {
+    int blk;
+    if (i < 4) {
+      blk = nt * 16 + w + 4 * i;
+    } else {
+      blk = 2 * MB * mt + w + 4 * (i - 4);
+      blk = blk < nblk ? blk : nblk - 1;
+    }
+    voff[i] = (uint32_t)(blk * KB32) * 1024u + (uint32_t)lane * 16u;
+  }
+  floatx4 acc[8][MB];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  gw_mainloop<MB>(acc, lds, g.A, g.B, voff, 1024u, KB32, w, lane);
+
+  gw_barrier();   // every wave is done with the ring (and every copy has landed)
+  floatx4* E = reinterpret_cast<floatx4*>(lds + w * (4 * MB * 1024));
+  const int c = lane & 15, il = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < MB; ++j) E[(i * MB + j) * 64 + lane] = acc[4 * h + i][j];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    floatx4 q[MB][4];
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) q[j][gg] = E[(il * MB + j) * 64 + gg * 16 + c];
+    const int f0 = (nt * 16 + wn * 8 + 4 * h + il) * 8;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      u32x4 y;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        y[gg] = bf16_bits(gelu_tanh(q[j][gg].x) * q[j][gg].y) | (bf16_bits(gelu_tanh(q[j][gg].z) * q[j][gg].w) << 16);
+      // tokens past the padded count: an offset beyond the buffer range drops the store
+      const int token = mt * C::BMT + (wm * MB + j) * 16 + c;
+      const uint32_t off = token < g.Mpad ? pk_off(token, f0, g.N >> 1) : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b128(y, rsrc(g.act), off, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+// Tokens per tile of the wide gate/up GEMM for M tokens (0: the shape does
+// not fit it): the choice with the least work per compute unit, counting a
+// second round of tiles and a fixed cost per 32-K stage.
+int gu_wide_tokens(const GemmArgs& g) {
+  if (g.N % 256 != 0 || g.S != 1 || g.K % 64 != 0 || g.K / 32 < GW<5>::NS - 1) return 0;
+  int best = 0;
+  long best_cost = -1;
+  for (int mb : {5, 6, 7}) {
+    const long tiles = (long)(g.N / 256) * ((g.M + 32 * mb - 1) / (32 * mb));
+    const long cost = (tiles + 255) / 256 * (mb * 8 * 17 + 350);
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best = 32 * mb;
+  }
+  return best;
 }
 
 // ------------------------------------------------------------------ attention
@@ -347,10 +438,26 @@ hipError_t prepare() {
     return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm<EPI_GU>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE)) != hipSuccess)
     return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<5>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<5>::LDS)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<6>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<6>::LDS)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<7>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<7>::LDS)) != hipSuccess)
+    return e;
   return hipFuncSetAttribute((const void*)k_gemm<EPI_QKV>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
 }
 
-hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st) {
+hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
+  if (epi == EPI_GU && wide_gu) {
+    const int bm = gu_wide_tokens(g);
+    if (bm > 0) {
+      const int tiles = (g.N / 256) * ((g.M + bm - 1) / bm), grid = (tiles + 7) / 8 * 8;
+      if (bm == 160) hipLaunchKernelGGL(k_gemm_gu_w<5>, dim3(grid), dim3(GW_THREADS), GW<5>::LDS, st, g);
+      else if (bm == 192) hipLaunchKernelGGL(k_gemm_gu_w<6>, dim3(grid), dim3(GW_THREADS), GW<6>::LDS, st, g);
+      else hipLaunchKernelGGL(k_gemm_gu_w<7>, dim3(grid), dim3(GW_THREADS), GW<7>::LDS, st, g);
+      return hipGetLastError();
+    }
+  }
   const int total = (g.Mpad / TM) * (g.N / TN) * g.S;
   const int grid = (total + 7) / 8 * 8;
   switch (epi) {

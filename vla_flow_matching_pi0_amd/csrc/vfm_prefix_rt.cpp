@@ -40,6 +40,7 @@ struct vfm_prefix {
   uint16_t* vt = nullptr;    // [maxB][Hkv][d][Ppad max]
   float* rope = nullptr;     // [maxP][d/2][2]
   int rope_P = -1;
+  bool wide_gu = true;       // option "gate_up_tiles"
 
   void* dalloc(size_t bytes) {
     void* p = nullptr;
@@ -344,7 +345,7 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
     na.gain = x->g_mlp[l]; na.S = S_o;
     PCHK(pfx::norm(false, na, s));
     ga.A = x->w_gu[l]; ga.B = ws.xn; ga.N = 2 * F; ga.K = W; ga.S = 1;
-    PCHK(pfx::gemm(pfx::EPI_GU, ga, s));
+    PCHK(pfx::gemm(pfx::EPI_GU, ga, s, x->wide_gu));
     ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
   }
@@ -401,6 +402,18 @@ vfm_status vfm_prefix_run_noalloc(vfm_prefix* x, const void* embeds, int32_t B, 
   PCHK(zero_words(reinterpret_cast<unsigned*>(ws.vt), (int)(sz[6] / 4), s));
   PCHK(build_rope(ws.rope, P, x->d, 0, x->cfg.rope_base, s));
   return run_pass(x, ws, embeds, B, P, prefix_k, prefix_v, s);
+}
+
+vfm_status vfm_prefix_set_option(vfm_prefix* x, const char* key, const char* value) {
+  if (!x || !key || !value) return report(VFM_E_INVALID_ARG, "NULL argument");
+  const std::string k = key, v = value;
+  if (k == "gate_up_tiles") {
+    if (v == "wide") x->wide_gu = true;
+    else if (v == "narrow") x->wide_gu = false;
+    else return report(VFM_E_INVALID_ARG, "gate_up_tiles must be 'wide' or 'narrow'");
+    return VFM_OK;
+  }
+  return report(VFM_E_INVALID_ARG, "unknown option '%s'", key);
 }
 
 vfm_status vfm_prefix_destroy(vfm_prefix* x) {

@@ -27,7 +27,7 @@ EXPORTS = ["vfm_abi_version", "vfm_last_error", "vfm_expert_create", "vfm_bind",
            "vfm_set_option", "vfm_calibrate", "vfm_set_act_scales", "vfm_export", "vfm_copy_probe", "vfm_check",
            "vfm_expert_destroy", "vfm_stream_debug", "vfm_capsule_create", "vfm_capsule_save", "vfm_capsule_restore",
            "vfm_capsule_bytes", "vfm_capsule_destroy", "vfm_prefix_create", "vfm_prefix_run",
-           "vfm_prefix_run_noalloc", "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
+           "vfm_prefix_run_noalloc", "vfm_prefix_set_option", "vfm_prefix_destroy", "vfm_plan_create", "vfm_plan_add_prefix", "vfm_plan_add_denoise",
            "vfm_plan_add_graph", "vfm_plan_add_edge", "vfm_plan_deps", "vfm_plan_run", "vfm_plan_destroy"]
 
 
@@ -104,6 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.POINTER(vp)]
     lib.vfm_prefix_run.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.vfm_prefix_run_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.vfm_prefix_set_option.argtypes = [vp, ctypes.c_char_p, ctypes.c_char_p]
     lib.vfm_prefix_destroy.argtypes = [vp]
     lib.vfm_plan_create.argtypes = [ctypes.POINTER(vp)]
     lib.vfm_plan_add_prefix.argtypes = [vp, vp, vp, i32, i32, vp, vp, i32, i32, ctypes.POINTER(i32)]
@@ -327,6 +328,9 @@ class PrefixProducer:
         B, P = int(embeds.shape[0]), int(embeds.shape[1])
         _check(_lib.vfm_prefix_run_noalloc(self._h, embeds.data_ptr(), B, P, prefix_k.data_ptr(),
                                            prefix_v.data_ptr(), _stream_ptr(stream)))
+
+    def set_option(self, key: str, value: str) -> None:
+        _check(_lib.vfm_prefix_set_option(self._h, key.encode(), value.encode()))
 
     def close(self) -> None:
         if getattr(self, "_h", None):
