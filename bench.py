@@ -316,27 +316,44 @@ def main() -> int:
     ex.check(stream)
     torch.cuda.synchronize()
 
-    # timed region: per-call HIP events on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: HIP events on the launch stream around the whole run of
+    # back-to-back calls (a timing event recorded between two calls costs
+    # about 5 us of idle device time itself); with --flush-mib every call is
+    # bracketed instead, so that the flush kernel between calls stays out
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     flush = None
     if args.flush_mib > 0:
         flush = torch.ones(args.flush_mib * (1 << 20) // 4, device="cuda")
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        ex.denoise(stream=stream)
-        ends[i].record(stream)
-        if flush is not None:
-            flush.neg_()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ex.check(stream)
-    total_ms = t0.elapsed_time(t1)
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+    def bracketed(n):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            starts[i].record(stream)
+            ex.denoise(stream=stream)
+            ends[i].record(stream)
+            if flush is not None:
+                flush.neg_()
+        torch.cuda.synchronize()
+        ex.check(stream)
+        return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+    if flush is not None:
+        per = bracketed(args.steps)
+        total_ms = float(np.sum(per))
+    else:
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            ex.denoise(stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ex.check(stream)
+        total_ms = t0.elapsed_time(t1)
+        # the per-call distribution from a separate, shorter bracketed run
+        per = bracketed(min(args.steps, 50))
     med = float(np.median(per))
     mean = float(np.mean(per))
     ms_chunk = mean if flush is not None else total_ms / args.steps
