@@ -194,6 +194,17 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       up after a bounded spin and the next vfm_check / vfm_denoise
  *       reports VFM_E_HIP. Used where a tool cannot follow cooperative
  *       launches (kernel profilers).
+ *   "fused_norms": "1" (default where it applies) or "0": the persistent
+ *       kernel of a bf16 pi0.5 expert (width a multiple of 256, at most 1024)
+ *       folds the adaptive RMSNorms into the GEMMs next to them (the
+ *       residual + norm fusion of the FlashRT walk-through, component 8):
+ *       the o and down projections finish the gated residual in the
+ *       epilogue of the last K split of each column group to arrive and
+ *       write y = h (1 + scale) of the next norm with per-16-column sums of
+ *       squares; qkv and gate/up apply r = 1 / sqrt(mean(h^2) + eps) and a
+ *       create-time shift W table: six device-wide barriers per layer
+ *       instead of eight. Results agree with "0" to bf16 rounding of the
+ *       GEMM inputs. VFM_E_UNSUPPORTED for "1" on other experts.
  *   "trace": "1" / "0": record a timeline of the persistent kernel's phase
  *       barriers (workgroup 0), read with vfm_export("trace").
  *   "graph_cache": "1" .. "64" (default 8): graph mode keeps one captured
@@ -235,7 +246,12 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
  *      every step (norm order attn_0, mlp_0, ..., final);
  *   "weight_scales" (FP8), "act_scales" (FP8, W4A8): [L][4] per-GEMM scales
  *      (qkv, o, gate/up, down); act_scales needs a calibration first;
- *   "trace": the phase timeline of the last persistent call (option "trace").
+ *   "trace": the phase timeline of the last persistent call (option "trace");
+ *   "persistent_plan": 4 int32 (not float32): whether the persistent kernel
+ *      runs with folded norms (0 / 1), its device-wide barriers per call,
+ *      and the K splits of the o and down projections, at the bound batch
+ *      and prefix; VFM_E_UNBOUND without prefix_k, VFM_E_STATE when the
+ *      expert would not run the persistent kernel there.
  * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE,
  * VFM_E_STATE. */
 vfm_status vfm_export(vfm_expert* ex, const char* name, void* dst, size_t bytes);

@@ -70,7 +70,19 @@ struct VP {
   long spin_limit;         // polls before a barrier wait gives up
   unsigned* herr;          // host-mapped error word (set with a system-scope store when a wait gives up)
   int fail_epoch;          // diagnostics: barrier whose target is never reached (0: none)
+  // Norms folded into the GEMMs (persistent kernel, bf16 pi0.5 experts). The
+  // o and down projections finish the residual in the epilogue of the last
+  // K split of a tile to arrive and write y = h (1 + scale) of the next norm
+  // plus per-16-column sums of squares of h; qkv and gate/up compute
+  // r (y W) + shift W, r = 1 / sqrt(mean(h^2) + eps).
+  int fuse;                // 1: the fused kernel runs
+  const float* shw_q;      // [N][L][Nqkv] shift W of each attention norm (packed column order)
+  const float* shw_g;      // [N][L][2F]   ... of each MLP norm
+  size_t off_ssa;          // slab offset of [Mpad][W/16] f32: sums of squares of h over each 16 columns, before qkv
+  size_t off_ssm;          // ... before gate/up
+  unsigned* fcnt;          // arrival counters: [2 (o, down)][FCNT_MAX]; zero between launches
 };
+constexpr int FCNT_MAX = 4096;   // counters per split GEMM: 16-column tile groups x 64-row tiles
 
 // Kernel sets: activation type x weight format (x calibration).
 enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4, KS_I8 = 5, KS_W4A8 = 6 };

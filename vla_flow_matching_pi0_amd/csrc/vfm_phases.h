@@ -280,7 +280,7 @@ __device__ __forceinline__ void ph_rn(const VP&, int step, int layer, bool mlp, 
 // Thread c owns columns 4c..4c+3 of the row; every weight load is issued
 // before it is used.
 constexpr int MAX_A = MAX_A_HOST;
-template <typename T, int WF = 0>
+template <typename T, int WF = 0, bool FUSE = false>
 __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, int nwg) {
   const VP& p = vp_fresh();
   constexpr bool Q8 = act_fp8<WF>();
@@ -429,7 +429,21 @@ __device__ __forceinline__ void ph_boundary(const VP&, int kp, int kn, int wg, i
         }
         coh_st16(p.h, (uint32_t)(((size_t)m * W + c * 4) * 4), as_u4(hv));
       }
-      if (p.L > 0) {
+      if (FUSE && p.L > 0) {
+        // norms folded into the GEMMs: layer 0's qkv applies r and the shift;
+        // here y = h (1 + scale) and the sums of squares of h per 16 columns
+        // (threads 4t .. 4t + 3 of a wave hold tile t)
+        float ss = hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w;
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if (c < W4) {
+          const float* mod = p.mod + ((size_t)kn * p.n_norms) * 3 * W;
+          const floatx4 y = hv * (1.0f + as_f4(ro_ld16(mod + c * 4)));
+          store_gemm_in4<T, false>(p, slab(p, kn, 0) + p.off_xna, m, c * 4, y, 1.0f);
+          if ((c & 3) == 0)
+            coh_st4(slab(p, kn, 0) + p.off_ssa, (uint32_t)(((size_t)m * (W / 16) + c / 4) * 4), __builtin_bit_cast(uint32_t, ss));
+        }
+      } else if (p.L > 0) {
         const float ss = block_sum(hv.x * hv.x + hv.y * hv.y + hv.z * hv.z + hv.w * hv.w, red);
         const float r = 1.0f / sqrtf(ss / (float)W + p.eps);
         if (c < W4) {
@@ -615,12 +629,26 @@ __device__ __forceinline__ float frag_amax(u32x4 a) {
   return m;
 }
 
-template <typename T, int WHICH, bool PRE, int WF = WF_NATIVE, bool CAL = false>
+// FUSE (bf16 weights and activations): the norms next to the GEMM are folded
+// into it. qkv and gate/up read y = h (1 + scale) and finish
+// xn W = r (y W) + shift W with r = 1 / sqrt(mean(h^2) + eps) from the per-16-
+// column sums of squares and shift W from the step's table. o and down (not
+// the last layer's down, which the step boundary finishes) store their K-split
+// partial sums; the last unit of a column group to arrive (an arrival counter
+// per group and 64-row tile) adds the splits in the fixed order 0 .. S-1,
+// applies the gated residual h += gate * sum, and writes h, the next norm's
+// y = h (1 + scale) and the group's sums of squares.
+template <typename T, int WHICH, bool PRE, int WF = WF_NATIVE, bool CAL = false, bool FUSE = false>
 __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, int nwg, const WPre& pre) {
   const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KM = MT<T>::KB, R = WFmt<WF>::R, KW = KM * R, PW = GEMM_PASS / R;
   static_assert(WF == WF_NATIVE || sizeof(T) == 2, "quantised weights run with bf16 activations");
+  static_assert(!FUSE || (WF == WF_NATIVE && sizeof(T) == 2 && !CAL), "folded norms: bf16 weights and activations");
+  constexpr bool FIN = FUSE && (WHICH == G_QKV || WHICH == G_GU);    // applies r and the shift
+  constexpr bool FOUT = FUSE && (WHICH == G_O || WHICH == G_DOWN);   // finishes the residual
+  const bool fout = FOUT && (WHICH == G_O || layer + 1 < p.L);
+  __shared__ unsigned s_last;
   uint8_t* sl = slab(p, step, layer);
   const T* A;
   if (WHICH == G_QKV) A = (const T*)(sl + p.off_xna);
@@ -659,6 +687,23 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       const bool ok = wv < nt * 4 && gm < p.M && head < p.Hq + p.Hkv;
       const int i = gm % p.H, j0 = tt * 8 + 2 * g;
       rot = as_f4(ld16_if(rsrc(p.rope), (uint32_t)((((size_t)i * (p.d / 2) + j0) * 2) * 4), ok));
+    }
+    // folded norm: shift W of the item's columns and this lane's quarter of the
+    // row's per-tile sums of squares (W <= 1024: at most 4 loads; write-once
+    // slab data, read through L2), fetched up front too
+    floatx4 shv = {0, 0, 0, 0};
+    u32x4 ssv[4];
+    if constexpr (FIN) {
+      const int t = wv / 4, st = wv % 4;
+      const int gm = m0 + st * 16 + c16;
+      const bool ok = wv < nt * 4 && gm < p.M;
+      const float* shw = (WHICH == G_QKV ? p.shw_q : p.shw_g) + ((size_t)step * p.L + layer) * gs.N;
+      shv = as_f4(ld16_if(rsrc(shw), (uint32_t)(((t0 + t) * 16 + 4 * g) * 4), ok));
+      const int per = p.W / 64;
+      const auto sr = rsrc(sl + (WHICH == G_QKV ? p.off_ssa : p.off_ssm));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ssv[j] = ld16_if(sr, (uint32_t)(((size_t)gm * (p.W / 16) + g * per + 4 * j) * 4), ok && 4 * j < per);
     }
     // W8A16: the column scales of that epilogue item, fetched up front too
     floatx4 csc = {1.f, 1.f, 1.f, 1.f};
@@ -788,15 +833,26 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
         if (t < nt) red[((wv * 2 + t) * 4 + st) * 64 + lane] = acc[t][st];
     __syncthreads();
     // epilogue: wave w finalises item w = (tile t, token subtile st)
+    floatx4 v = {0, 0, 0, 0};
     if (wv < nt * 4) {
       const int t = wv / 4, st = wv % 4;
-      floatx4 v = {0, 0, 0, 0};
 #pragma unroll
       for (int w2 = 0; w2 < NWAVES; ++w2) v += red[((w2 * 2 + t) * 4 + st) * 64 + lane];
       if constexpr (act_fp8<WF>()) v *= alpha;
       const int gm = m0 + st * 16 + c16;
       const int tile = t0 + t;
       if constexpr (WF == WF_I8) v *= csc;
+      if constexpr (FIN) {
+        float sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 q = as_f4(ssv[j]);
+          sq += (q.x + q.y) + (q.z + q.w);
+        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        v = (1.0f / sqrtf(sq / (float)p.W + p.eps)) * v + shv;
+      }
       if (gm < p.M) {
         if (WHICH == G_QKV) {
           const int d = p.d, hd = d / 2;
@@ -841,10 +897,62 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
               coh_st8(dst, (uint32_t)(e0 * 4), u32x2{__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1)});
             else coh_st4(dst, (uint32_t)(e0 * 2), pack_bf16x2(a0, a1));
           }
-        } else {
+        } else if (!fout || S > 1) {
           float* part = WHICH == G_O ? p.part_o : p.part_d;
           const int n0 = tile * 16 + 4 * g;
           coh_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(v));
+        }
+      }
+    }
+    if (FOUT && fout) {
+      const int t = wv / 4, st = wv % 4;
+      const int gm = m0 + st * 16 + c16, c = (t0 + t) * 16 + 4 * g, W = p.W;
+      const bool mine = wv < nt * 4 && gm < p.M;
+      const int gate_ni = WHICH == G_O ? 2 * layer : 2 * layer + 1, next_ni = gate_ni + 1;
+      const auto mr = rsrc(p.mod);
+      // the residual, its gate and the next norm's scale, issued before the
+      // wait for the partial sums' stores
+      const floatx4 h0 = as_f4(coh_ld16_if(rsrc(p.h), (uint32_t)(((size_t)gm * W + c) * 4), mine));
+      const floatx4 gt = as_f4(ld16_if(mr, (uint32_t)(((((size_t)step * p.n_norms + gate_ni) * 3 + 2) * W + c) * 4), mine));
+      const floatx4 sc = as_f4(ld16_if(mr, (uint32_t)(((((size_t)step * p.n_norms + next_ni) * 3) * W + c) * 4), mine));
+      bool last = true;
+      if (S > 1) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's partial sums are stored
+        __syncthreads();
+        if (tid == 0) {
+          const unsigned old = __hip_atomic_fetch_add(&p.fcnt[(WHICH == G_O ? 0 : FCNT_MAX) + mt * ngroups + ng], 1u,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = (old + 1u) % (unsigned)S == 0u ? 1u : 0u;
+        }
+        __syncthreads();
+        last = s_last != 0u;
+      }
+      if (last && wv < nt * 4) {
+        const float* part = WHICH == G_O ? p.part_o : p.part_d;
+        const auto pr = rsrc(part);
+        floatx4 sum = {0, 0, 0, 0};
+        for (int s0 = 0; s0 < S; s0 += 8) {
+          u32x4 pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pv[j] = coh_ld16_if(pr, (uint32_t)((((size_t)(s0 + j) * p.M + gm) * W + c) * 4),
+                                mine && s0 + j < S && s0 + j != s);
+          // splits added in their fixed order whichever arrived last
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (s0 + j < S) sum += s0 + j == s ? v : as_f4(pv[j]);
+        }
+        const floatx4 hn = h0 + gt * sum;
+        float sq = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (mine) {
+          coh_st16(p.h, (uint32_t)(((size_t)gm * W + c) * 4), as_u4(hn));
+          uint8_t* dsl = WHICH == G_O ? sl : slab(p, step, layer + 1);
+          store_gemm_in4<T, false>(p, dsl + (WHICH == G_O ? p.off_xnm : p.off_xna), gm, c, hn * (1.0f + sc), 1.0f);
+          if (g == 0)
+            coh_st4(dsl + (WHICH == G_O ? p.off_ssm : p.off_ssa), (uint32_t)(((size_t)gm * (W / 16) + c / 16) * 4),
+                    __builtin_bit_cast(uint32_t, sq));
         }
       }
     }
@@ -1730,7 +1838,10 @@ extern template __global__ void k_attn_m<bf16, 256>(VP, int, int);
 
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
-template <typename T, int D, int WF>
+// FUSE: the norms are folded into the GEMMs (ph_gemm), so a layer runs
+// qkv | attention | combine | o | gate/up | down with six device-wide
+// barriers instead of eight (bf16 pi0.5 experts).
+template <typename T, int D, int WF, bool FUSE = false>
 __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
   const int wg = blockIdx.x, nwg = gridDim.x;
@@ -1741,7 +1852,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
 #define VFM_BAR_PF(WHICH, LAYER) \
   do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
-  ph_boundary<T, WF>(p, -1, 0, wg, nwg);
+  ph_boundary<T, WF, FUSE>(p, -1, 0, wg, nwg);
   if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
   else if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
@@ -1754,11 +1865,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       VFM_BAR_PF(G_QKV, 0);
     }
     for (int l = 0; l < p.L; ++l) {
-      if (l > 0) {
+      if (!FUSE && l > 0) {
         ph_rn<T, WF>(p, k, l, false, wg, nwg);
         VFM_BAR_PF(G_QKV, l);
       }
-      ph_gemm<T, G_QKV, true, WF>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_QKV, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
       {
         APre<T, D> apre;
         if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
@@ -1767,16 +1878,19 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       VFM_BAR();
       ph_combine<T, WF>(p, k, l, wg, nwg);
       VFM_BAR_PF(G_O, l);
-      ph_gemm<T, G_O, true, WF>(p, k, l, wg, nwg, pre);
-      VFM_BAR();
-      ph_rn<T, WF>(p, k, l, true, wg, nwg);
+      ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
+      if (!FUSE) {
+        VFM_BAR();
+        ph_rn<T, WF>(p, k, l, true, wg, nwg);
+      }
       VFM_BAR_PF(G_GU, l);
-      ph_gemm<T, G_GU, true, WF>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_GU, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
       VFM_BAR_PF(G_DOWN, l);
-      ph_gemm<T, G_DOWN, true, WF>(p, k, l, wg, nwg, pre);
-      VFM_BAR();
+      ph_gemm<T, G_DOWN, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
+      if (FUSE && l + 1 < p.L) VFM_BAR_PF(G_QKV, l + 1);
+      else VFM_BAR();
     }
-    ph_boundary<T, WF>(p, k, k + 1, wg, nwg);
+    ph_boundary<T, WF, FUSE>(p, k, k + 1, wg, nwg);
     if (p.pi0 && k + 1 < p.N) VFM_BAR_PF(G_TMLP, 0);
     else if (p.L > 0 && k + 1 < p.N) VFM_BAR_PF(G_QKV, 0);
     else VFM_BAR();
@@ -1792,6 +1906,14 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
     if (old + 1u == gridDim.x) {
       for (int c = 0; c < BAR_COUNTERS; ++c)
         __hip_atomic_store(&p.bar[64 + 64 * c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (FUSE) {
+        // the split GEMMs' arrival counters (multiples of their split counts
+        // here), so that the next launch may split differently
+        const int mt = (p.M + 63) / 64;
+        const int no = p.W / (16 * p.gp_nt[1]) * mt, nd = p.W / (16 * p.gp_nt[3]) * mt;
+        for (int c = 0; c < no; ++c) __hip_atomic_store(&p.fcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < nd; ++c) __hip_atomic_store(&p.fcnt[FCNT_MAX + c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __hip_atomic_store(&p.bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -1887,6 +2009,10 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
     } else {
       void* args[] = {const_cast<VP*>(&p)};
       const void* f = reinterpret_cast<const void*>(&k_persistent<T, D, WF>);
+      if (p.fuse) {
+        if constexpr (sizeof(T) == 2 && WF == WF_NATIVE) f = reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>);
+        else return hipErrorInvalidValue;
+      }
       if (mode == 0) return hipLaunchCooperativeKernel(f, dim3(grid), dim3(NTH), args, (unsigned)lds, st);
       return hipLaunchKernel(f, dim3(grid), dim3(NTH), args, lds, st);
     }
@@ -1925,6 +2051,10 @@ hipError_t set_lds_limit(int bytes) {
   if constexpr (!CAL)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if constexpr (!CAL && sizeof(T) == 2 && WF == WF_NATIVE)
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   for (int ph = 0; ph < PH_COUNT && e == hipSuccess; ++ph) {
     e = hipFuncSetAttribute(phase_kernel<T, D, WF, CAL>(ph), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     for (int bm : {128, 64, 224, 256}) {
@@ -1944,8 +2074,17 @@ hipError_t occupancy(size_t lds, int* per_cu) {
     *per_cu = 0;
     return hipErrorInvalidValue;
   } else {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
-                                                        NTH, lds);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        per_cu, reinterpret_cast<const void*>(&k_persistent<T, D, WF>), NTH, lds);
+    if constexpr (sizeof(T) == 2 && WF == WF_NATIVE) {
+      // the grid must fit with either kernel resident
+      int fused = 0;
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &fused, reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>), NTH, lds);
+      if (e == hipSuccess && fused < *per_cu) *per_cu = fused;
+    }
+    return e;
   }
 }
 

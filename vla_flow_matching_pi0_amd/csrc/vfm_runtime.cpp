@@ -107,6 +107,12 @@ struct vfm_expert {
   int coop_grid = 0;
   bool coop_launch = true;   // persistent kernel: cooperative launch (else an ordinary one of the same grid)
   int gemm_tiles = 0;        // large-M GEMMs: 0 auto, 1 128-column tiles only, 2 256-column tiles where they apply
+  // norms folded into the persistent kernel's GEMMs (bf16 pi0.5 experts, W a multiple of 256 up to 1024)
+  bool can_fuse = false;
+  bool fuse_norms = true;    // option "fused_norms"
+  float *shw_q = nullptr, *shw_g = nullptr;   // [N][L][columns] shift W per step, layer and norm
+  size_t off_ssa = 0, off_ssm = 0;            // slab offsets of the per-tile sums of squares [Mpad][W/16]
+  unsigned* fcnt = nullptr;                   // [2][FCNT_MAX] split arrival counters
   // graph variants, most recently used first: key = shape + pointers
   struct GraphEntry {
     std::vector<uintptr_t> key;
@@ -233,6 +239,14 @@ vfm_status validate_config(const vfm_config* c) {
   return VFM_OK;
 }
 
+// Whether the persistent kernel can fold the norms into its GEMMs: bf16
+// pi0.5 experts whose width is a multiple of 256 up to 1024 (a GEMM lane
+// reads at most 16 per-tile sums of squares of a row).
+bool can_fold_norms(const vfm_config* c) {
+  return c->weight_precision == VFM_W_BF16 && c->variant != VFM_VARIANT_PI0 && c->num_layers > 0 &&
+         c->width % 256 == 0 && c->width <= 1024;
+}
+
 // The kernels address every buffer through 32-bit byte offsets from its
 // base (buffer resources of up to 2 GiB): refuse configurations whose largest
 // buffer would not fit.
@@ -264,7 +278,8 @@ vfm_status check_extents(const vfm_config* c) {
   auto al = [](size_t b) { return (b + 4095) / 4096 * 4096; };
   const size_t slab = al(Mpad * W * ab) + al(B * Hq * d * 64 * ab) + 2 * al(B * Hkv * d * 64 * ab) +
                       al(Mpad * Hq * d * ab) + al(Mpad * W * ab) + al(F * Mpad * ab) +
-                      (c->variant == VFM_VARIANT_PI0 ? al(Mpad * W * ab) : 0);
+                      (c->variant == VFM_VARIANT_PI0 ? al(Mpad * W * ab) : 0) +
+                      (can_fold_norms(c) ? 2 * al(Mpad * (W / 16) * 4) : 0);
   const size_t ring = slab * N * std::max<size_t>(L, 1);
   const size_t other = M * W * 4 * (2 + 2 * (size_t)vfm::MAX_KSPLIT) + B * Hq * KS * 64 * (d + 2) * 4;
   if (ring + other > WORKSPACE_MAX)
@@ -397,6 +412,7 @@ vfm_status check_host_err(vfm_expert* x, hipStream_t s) {
   if (!x->herr || __atomic_load_n(x->herr, __ATOMIC_ACQUIRE) == 0u) return VFM_OK;
   *x->herr = 0u;
   (void)vfm::zero_words(x->bar, vfm::BAR_WORDS, s);
+  if (x->fcnt) (void)vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s);
   (void)hipStreamSynchronize(s);
   return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
 }
@@ -622,6 +638,15 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
     }
     p.S_o = p.gp_s[1];
     p.S_down = p.gp_s[3];
+  }
+  p.fuse = 0;
+  if (mode == 0 && x->can_fuse && x->fuse_norms) {
+    const long mt = (p.M + 63) / 64;
+    const long go = (long)p.W / (16 * p.gp_nt[1]) * mt, gd = (long)p.W / (16 * p.gp_nt[3]) * mt;
+    if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX) {
+      p.fuse = 1;
+      p.shw_q = x->shw_q; p.shw_g = x->shw_g; p.off_ssa = x->off_ssa; p.off_ssm = x->off_ssm; p.fcnt = x->fcnt;
+    }
   }
   p.qs = x->qs;
   p.amax = nullptr;
@@ -872,6 +897,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->off_xnm = off; off += al(Mpad * W * ab);
     x->off_act = off; off += al((size_t)F * Mpad * ab);
     if (x->pi0) { x->off_u = off; off += al(Mpad * W * ab); }
+    if (can_fold_norms(cfg)) {
+      x->off_ssa = off; off += al(Mpad * (W / 16) * 4);
+      x->off_ssm = off; off += al(Mpad * (W / 16) * 4);
+    }
     x->slab = off;
     x->ring = (uint8_t*)x->dalloc(x->slab * (size_t)x->N * std::max(L, 1));
   }
@@ -894,6 +923,22 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     hipError_t e = vfm::prepare_kernels(x->kset, d, (int)x->lds);
     if (e == hipSuccess && fp8_act(x)) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
+  }
+  // norms folded into the persistent kernel's GEMMs: shift W tables (fp64
+  // sums over the packed bf16 weights), sums-of-squares rows, split counters
+  if (can_fold_norms(cfg)) {
+    const int Nq = (Hq + 2 * Hkv) * d, n_norms = 2 * L + 1;
+    x->shw_q = (float*)x->dalloc((size_t)x->N * L * Nq * 4);
+    x->shw_g = (float*)x->dalloc((size_t)x->N * L * 2 * F * 4);
+    x->fcnt = (unsigned*)x->dalloc((size_t)2 * vfm::FCNT_MAX * 4);
+    if (!x->shw_q || !x->shw_g || !x->fcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
+    if (vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s) != hipSuccess ||
+        vfm::sk::shift_proj(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, s) != hipSuccess ||
+        vfm::sk::shift_proj(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, s) != hipSuccess) {
+      fail(VFM_E_HIP, "shift projection tables");
+      return bail(VFM_E_HIP);
+    }
+    x->can_fuse = true;
   }
   // the streaming batch-1 kernel: bf16 pi0.5 experts whose shapes fit it
   if (x->kset == vfm::KS_BF16 && !x->pi0) {
@@ -1009,6 +1054,20 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     else if (v == "wide") x->gemm_tiles = 2;
     else return fail(VFM_E_INVALID_ARG, "large_m_tiles must be 'auto', 'narrow' or 'wide'");
     x->drop_graphs();
+    return VFM_OK;
+  }
+  if (k == "fused_norms") {
+    // the persistent kernel with the norms folded into its GEMMs (1, the
+    // default where it applies) or with separate norm phases (0)
+    if (v == "1") {
+      if (!x->can_fuse)
+        return fail(VFM_E_UNSUPPORTED, "fused_norms applies to bf16 pi0.5 experts with a width that is a multiple of 256 up to 1024");
+      x->fuse_norms = true;
+    } else if (v == "0") {
+      x->fuse_norms = false;
+    } else {
+      return fail(VFM_E_INVALID_ARG, "fused_norms must be 0 or 1");
+    }
     return VFM_OK;
   }
   if (k == "persistent_launch") {
@@ -1259,6 +1318,23 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     if (v.empty()) return fail(VFM_E_STATE, "activation scales are not set");
     if (bytes != v.size() * 4) return fail(VFM_E_SHAPE, "'%s' needs %zu bytes", name, v.size() * 4);
     memcpy(dst, v.data(), bytes);
+    return VFM_OK;
+  }
+  if (n == "persistent_plan") {
+    // int32 [fused norms (0 / 1), device-wide barriers per call, o splits,
+    // down splits] of the persistent kernel at the bound batch and prefix
+    if (bytes != 4 * 4) return fail(VFM_E_SHAPE, "'persistent_plan' needs 16 bytes");
+    if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
+    const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
+    if (launch_mode_of(x, B, P) != 0) return fail(VFM_E_STATE, "the expert does not run the persistent kernel");
+    VP p{};
+    const vfm_status st = fill_vp(x, p, B, P, nullptr, nullptr, nullptr);
+    if (st != VFM_OK) return st;
+    int32_t* o = static_cast<int32_t*>(dst);
+    o[0] = p.fuse;
+    o[1] = p.fuse ? 1 + x->N * (6 * x->L + 1) : 1 + x->N * (8 * x->L + 2 * x->pi0);
+    o[2] = p.S_o;
+    o[3] = p.S_down;
     return VFM_OK;
   }
   if (n == "trace") {

@@ -217,6 +217,12 @@ class Expert:
         _check(_lib.vfm_export(self._h, name.encode(), out.ctypes.data, out.nbytes))
         return out
 
+    def persistent_plan(self) -> dict:
+        """The persistent kernel's plan at the bound batch and prefix (vfm_export "persistent_plan")."""
+        out = np.empty(4, dtype=np.int32)
+        _check(_lib.vfm_export(self._h, b"persistent_plan", out.ctypes.data, out.nbytes))
+        return {"fused_norms": bool(out[0]), "barriers": int(out[1]), "o_splits": int(out[2]), "down_splits": int(out[3])}
+
     def stream_debug(self, name: str, index: int = 0, nbytes: int = 0) -> np.ndarray:
         """Raw bytes of an internal buffer of the streaming kernel (diagnostics; see vfm_stream_debug)."""
         if name == "slab_layout":
