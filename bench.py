@@ -243,6 +243,32 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: flo
                                         f"{one_dt:.1f} s measured"}}
 
 
+def phase_breakdown(t, nb, N, L, fused, pi0):
+    """Mean (work, wait) in microseconds of each phase of a middle layer, from
+    workgroup 0's (arrive, release) stamps: work runs from the previous
+    release to this arrival, wait from arrival to release."""
+    if pi0 or L < 3:
+        return None
+    names = (["qkv", "attn", "combine", "o", "gu", "down"] if fused
+             else ["rn_attn", "qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"])
+    per_step = 6 * L + 1 if fused else 8 * L
+    # barrier index i ends the phase that ran before it; the first layer-l
+    # phase of step k (k >= 0) follows barrier 1 + k * per_step + (l * len(names) - (0 if fused else 1))
+    out = {n: [0.0, 0.0] for n in names}
+    cnt = 0
+    for k in range(N):
+        for l in range(1, L - 1):
+            base = 1 + k * per_step + l * len(names) - (0 if fused else 1)
+            for j, n in enumerate(names):
+                i = base + j + (0 if fused else 0)
+                if i + 1 > nb:
+                    continue
+                out[n][0] += t[i + 1, 0] - t[i, 1]
+                out[n][1] += t[i + 1, 1] - t[i + 1, 0]
+            cnt += 1
+    return {n: [round(a / cnt, 2), round(b / cnt, 2)] for n, (a, b) in out.items()} if cnt else None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,17 +390,19 @@ def main() -> int:
     sync = None
     if args.mode == "persistent":
         L, N = cfg.num_layers, cfg.num_steps
+        plan = ex.persistent_plan()
         ex.set_option("trace", "1")
         ex.denoise(stream=stream)
         ex.check(stream)
         pi0 = 1 if cfg.variant == "pi0" else 0   # pi0: the time-MLP GEMM and layer 0's norm add 2 per step
         t = ex.export("trace", (2 * (N * (8 * L + 1 + 2 * pi0) + 4),)).reshape(-1, 2).astype(np.float64)
         ex.set_option("trace", "0")
-        nb = 1 + N * (8 * L + 2 * pi0)
+        nb = plan["barriers"]
         span = t[nb, 1] - t[0, 1]
         stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
-        sync = {"barriers_per_call": nb, "stall_us": round(stall, 1), "span_us": round(float(span), 1),
-                "stall_frac": round(stall / span, 4) if span > 0 else None}
+        sync = {"barriers_per_call": nb, "fused_norms": plan["fused_norms"], "stall_us": round(stall, 1),
+                "span_us": round(float(span), 1), "stall_frac": round(stall / span, 4) if span > 0 else None,
+                "per_layer_us": phase_breakdown(t, nb, N, L, plan["fused_norms"], pi0)}
     elif args.mode == "stream":
         # (arrive, counters complete, workgroup ready) per barrier: the stall is
         # arrival to ready (the device-wide wait plus any wait for weights)
