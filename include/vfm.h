@@ -205,6 +205,12 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       create-time shift W table: six device-wide barriers per layer
  *       instead of eight. Results agree with "0" to bf16 rounding of the
  *       GEMM inputs. VFM_E_UNSUPPORTED for "1" on other experts.
+ *   "xcd_local": "1" (default) or "0": with folded norms, the K-split
+ *       units of one o / down column group all run on one XCD (unit index
+ *       mod 8, checked at kernel start from the hardware XCD id; a launch
+ *       whose workgroups are placed otherwise uses the device-wide path),
+ *       and exchange their partial sums through that XCD's L2 instead of
+ *       the device coherence point. Results are bitwise the same as "0".
  *   "trace": "1" / "0": record a timeline of the persistent kernel's phase
  *       barriers (workgroup 0), read with vfm_export("trace").
  *   "graph_cache": "1" .. "64" (default 8): graph mode keeps one captured
@@ -247,11 +253,12 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
  *   "weight_scales" (FP8), "act_scales" (FP8, W4A8): [L][4] per-GEMM scales
  *      (qkv, o, gate/up, down); act_scales needs a calibration first;
  *   "trace": the phase timeline of the last persistent call (option "trace");
- *   "persistent_plan": 4 int32 (not float32): whether the persistent kernel
+ *   "persistent_plan": 5 int32 (not float32): whether the persistent kernel
  *      runs with folded norms (0 / 1), its device-wide barriers per call,
- *      and the K splits of the o and down projections, at the bound batch
- *      and prefix; VFM_E_UNBOUND without prefix_k, VFM_E_STATE when the
- *      expert would not run the persistent kernel there.
+ *      the K splits of the o and down projections, and whether their split
+ *      sums are exchanged through one XCD's L2 (0 / 1; option "xcd_local"),
+ *      at the bound batch and prefix; VFM_E_UNBOUND without prefix_k,
+ *      VFM_E_STATE when the expert would not run the persistent kernel there.
  * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE,
  * VFM_E_STATE. */
 vfm_status vfm_export(vfm_expert* ex, const char* name, void* dst, size_t bytes);

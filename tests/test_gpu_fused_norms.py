@@ -35,10 +35,11 @@ def _gu():
     return gpu_util
 
 
-def _run(cfg, params, pk, pv, noise, state, fused, repeats=1, plain=False):
+def _run(cfg, params, pk, pv, noise, state, fused, repeats=1, plain=False, xcd_local=True):
     gu = _gu()
     ex = gu.build_expert(cfg, params, "persistent")
     ex.set_option("fused_norms", "1" if fused else "0")
+    ex.set_option("xcd_local", "1" if xcd_local else "0")
     if plain:
         ex.set_option("persistent_launch", "plain")
     bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
@@ -168,4 +169,37 @@ def test_fused_norms_option_is_validated():
     with pytest.raises(vfm.VfmError) as e:
         ex.set_option("fused_norms", "yes")
     assert e.value.name == "VFM_E_INVALID_ARG"
+    ex.close()
+
+
+def test_xcd_local_split_sums_bitwise_equal_device_path():
+    """The o / down split sums exchanged through one XCD's L2 (the default)
+    against the device-coherence-point exchange: the same products summed in
+    the same split order, so the actions agree bit for bit, over several
+    calls (the XCD-local counters carry over between launches); both match
+    the oracle."""
+    gu = _gu()
+    cfg = CONFIGS["pi05_bf16_b1"].replace(num_layers=4, num_steps=4)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ref = O.denoise(params, noise, state, pk, pv, cfg)
+    print("case pi05 b1 (4 layers, 4 steps) xcd_local 1 / 0", flush=True)
+    loc, pl = _run(cfg, params, pk, pv, noise, state, True, repeats=3)
+    dev, pd = _run(cfg, params, pk, pv, noise, state, True, repeats=3, xcd_local=False)
+    print(f"plans {pl} {pd}")
+    assert pl["xcd_local"] and not pd["xcd_local"]
+    assert pl["o_splits"] > 1 and pl["down_splits"] > 1
+    assert np.array_equal(loc, dev)
+    gu.assert_parity(loc, ref, noise, 2e-3, 5e-3, 1e-2, "xcd-local")
+
+
+def test_xcd_local_option_is_validated():
+    from vla_flow_matching_pi0_amd import vfm
+    gu = _gu()
+    cfg = CONFIGS["tiny_fp32"]
+    params, *_ = make_inputs(cfg)
+    ex = gu.build_expert(cfg, params, "persistent")
+    with pytest.raises(vfm.VfmError) as e:
+        ex.set_option("xcd_local", "2")
+    assert e.value.name == "VFM_E_INVALID_ARG"
+    ex.set_option("xcd_local", "0")
     ex.close()

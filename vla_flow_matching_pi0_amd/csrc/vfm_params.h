@@ -81,8 +81,13 @@ struct VP {
   size_t off_ssa;          // slab offset of [Mpad][W/16] f32: sums of squares of h over each 16 columns, before qkv
   size_t off_ssm;          // ... before gate/up
   unsigned* fcnt;          // arrival counters: [2 (o, down)][FCNT_MAX]; zero between launches
+  int xl;                  // 1: the o / down split units of a column group share an XCD (see ph_gemm)
+  unsigned* xcnt;          // their XCD-local arrival counters, [2][FCNT_MAX] at XCNT_STRIDE words
 };
 constexpr int FCNT_MAX = 4096;   // counters per split GEMM: 16-column tile groups x 64-row tiles
+constexpr int XCNT_STRIDE = 32;  // one 128-byte line per XCD-local counter
+constexpr int XCNT_WORDS = 2 * FCNT_MAX * XCNT_STRIDE;
+constexpr int BAR_XL_BAD = 32;   // grid-barrier word: set when a workgroup runs off its XCD (blockIdx % 8)
 
 // Kernel sets: activation type x weight format (x calibration).
 enum KernelSetId { KS_F32 = 0, KS_BF16 = 1, KS_FP8 = 2, KS_W4 = 3, KS_CAL = 4, KS_I8 = 5, KS_W4A8 = 6 };

@@ -638,8 +638,19 @@ __device__ __forceinline__ float frag_amax(u32x4 a) {
 // per group and 64-row tile) adds the splits in the fixed order 0 .. S-1,
 // applies the gated residual h += gate * sum, and writes h, the next norm's
 // y = h (1 + scale) and the group's sums of squares.
+//
+// xl (set by the persistent kernel once every workgroup is known to run on
+// XCD blockIdx % 8): the S split units of a column group are units
+// ng + ngroups (s + S mt) with ngroups and the grid multiples of 8, so they
+// all run on XCD ng % 8 and exchange their partial sums through that XCD's
+// L2 alone: write-back stores, an arrival atomic performed in the L2 (a
+// counter per 128-byte line, never cleared by the kernel: S is a power of
+// two, every complete launch adds a multiple of S, and the host clears them
+// when the split plan changes or a launch fails), and, in the last unit, an
+// L1 invalidation before ordinary loads that the L2 serves.
 template <typename T, int WHICH, bool PRE, int WF = WF_NATIVE, bool CAL = false, bool FUSE = false>
-__device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, int nwg, const WPre& pre) {
+__device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, int nwg, const WPre& pre,
+                                        bool xl = false) {
   const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KM = MT<T>::KB, R = WFmt<WF>::R, KW = KM * R, PW = GEMM_PASS / R;
@@ -900,7 +911,9 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
         } else if (!fout || S > 1) {
           float* part = WHICH == G_O ? p.part_o : p.part_d;
           const int n0 = tile * 16 + 4 * g;
-          coh_st16(part, (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4), as_u4(v));
+          const uint32_t off = (uint32_t)((((size_t)s * p.M + gm) * p.W + n0) * 4);
+          if (FOUT && fout && xl) wb_st16(part, off, as_u4(v));
+          else coh_st16(part, off, as_u4(v));
         }
       }
     }
@@ -920,8 +933,10 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
         __builtin_amdgcn_s_waitcnt(0);   // this wave's partial sums are stored
         __syncthreads();
         if (tid == 0) {
-          const unsigned old = __hip_atomic_fetch_add(&p.fcnt[(WHICH == G_O ? 0 : FCNT_MAX) + mt * ngroups + ng], 1u,
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int ci = (WHICH == G_O ? 0 : FCNT_MAX) + mt * ngroups + ng;
+          const unsigned old =
+              xl ? __hip_atomic_fetch_add(&p.xcnt[ci * XCNT_STRIDE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                 : __hip_atomic_fetch_add(&p.fcnt[ci], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           s_last = (old + 1u) % (unsigned)S == 0u ? 1u : 0u;
         }
         __syncthreads();
@@ -930,13 +945,18 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
       if (last && wv < nt * 4) {
         const float* part = WHICH == G_O ? p.part_o : p.part_d;
         const auto pr = rsrc(part);
+        // the other splits' sums sit in this XCD's L2; lines this compute
+        // unit's L1 kept from earlier reads of the buffer are dropped first
+        if (xl && S > 1) asm volatile("buffer_inv sc0" ::: "memory");
         floatx4 sum = {0, 0, 0, 0};
         for (int s0 = 0; s0 < S; s0 += 8) {
           u32x4 pv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            pv[j] = coh_ld16_if(pr, (uint32_t)((((size_t)(s0 + j) * p.M + gm) * W + c) * 4),
-                                mine && s0 + j < S && s0 + j != s);
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t off = (uint32_t)((((size_t)(s0 + j) * p.M + gm) * W + c) * 4);
+            const bool ok = mine && s0 + j < S && s0 + j != s;
+            pv[j] = xl ? ld16_if(pr, off, ok) : coh_ld16_if(pr, off, ok);
+          }
           // splits added in their fixed order whichever arrived last
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -1852,10 +1872,20 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
 #define VFM_BAR_PF(WHICH, LAYER) \
   do { if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, PrefetchHook<T, WHICH, WF>{p, LAYER, wg, pre})) return; } while (0)
   WPre pre;
+  // XCD-local split sums (ph_gemm): only while every workgroup runs on XCD
+  // blockIdx % 8; one that does not raises a word that every workgroup reads
+  // after the first barrier, and the launch takes the device-scope path
+  if (FUSE && p.xl && threadIdx.x == 0) {
+    unsigned xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if ((xcc & 15u) != (blockIdx.x & 7u))
+      __hip_atomic_fetch_or(&p.bar[BAR_XL_BAD], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   ph_boundary<T, WF, FUSE>(p, -1, 0, wg, nwg);
   if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
   else if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
+  const bool xl = FUSE && p.xl && ld_agent(&p.bar[BAR_XL_BAD]) == 0u;
   for (int k = 0; k < p.N; ++k) {
     if (p.pi0) {
       // the action tokens' time-MLP output, then layer 0's norm
@@ -1878,7 +1908,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       VFM_BAR();
       ph_combine<T, WF>(p, k, l, wg, nwg);
       VFM_BAR_PF(G_O, l);
-      ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre, xl);
       if (!FUSE) {
         VFM_BAR();
         ph_rn<T, WF>(p, k, l, true, wg, nwg);
@@ -1886,7 +1916,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       VFM_BAR_PF(G_GU, l);
       ph_gemm<T, G_GU, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
       VFM_BAR_PF(G_DOWN, l);
-      ph_gemm<T, G_DOWN, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
+      ph_gemm<T, G_DOWN, true, WF, false, FUSE>(p, k, l, wg, nwg, pre, xl);
       if (FUSE && l + 1 < p.L) VFM_BAR_PF(G_QKV, l + 1);
       else VFM_BAR();
     }
@@ -1914,6 +1944,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         for (int c = 0; c < no; ++c) __hip_atomic_store(&p.fcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int c = 0; c < nd; ++c) __hip_atomic_store(&p.fcnt[FCNT_MAX + c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      if constexpr (FUSE) __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&p.bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

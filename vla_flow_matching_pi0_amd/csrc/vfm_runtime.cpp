@@ -113,6 +113,13 @@ struct vfm_expert {
   float *shw_q = nullptr, *shw_g = nullptr;   // [N][L][columns] shift W per step, layer and norm
   size_t off_ssa = 0, off_ssm = 0;            // slab offsets of the per-tile sums of squares [Mpad][W/16]
   unsigned* fcnt = nullptr;                   // [2][FCNT_MAX] split arrival counters
+  // XCD-local split exchange of the fused kernel (option "xcd_local"): its
+  // counters are never cleared by the kernel, so the host clears them when
+  // the split plan changes (xl_plan: S and column groups of o and down) or a
+  // launch failed
+  bool xcd_local = true;
+  unsigned* xcnt = nullptr;                   // [2][FCNT_MAX] counters, XCNT_STRIDE words apart
+  long long xl_plan = -1;
   // graph variants, most recently used first: key = shape + pointers
   struct GraphEntry {
     std::vector<uintptr_t> key;
@@ -413,6 +420,8 @@ vfm_status check_host_err(vfm_expert* x, hipStream_t s) {
   *x->herr = 0u;
   (void)vfm::zero_words(x->bar, vfm::BAR_WORDS, s);
   if (x->fcnt) (void)vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s);
+  if (x->xcnt) (void)vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s);
+  x->xl_plan = -1;
   (void)hipStreamSynchronize(s);
   return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
 }
@@ -646,6 +655,15 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
     if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX) {
       p.fuse = 1;
       p.shw_q = x->shw_q; p.shw_g = x->shw_g; p.off_ssa = x->off_ssa; p.off_ssm = x->off_ssm; p.fcnt = x->fcnt;
+      // XCD-local split sums: every unit of a column group on one XCD (the
+      // column-group count and the grid multiples of 8) and a power-of-two
+      // split count (the never-cleared counters stay multiples of S, also
+      // across a 32-bit wrap)
+      const long ngo = (long)p.W / (16 * p.gp_nt[1]), ngd = (long)p.W / (16 * p.gp_nt[3]);
+      auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
+      p.xl = x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) &&
+             pow2(p.gp_s[3]) ? 1 : 0;
+      p.xcnt = x->xcnt;
     }
   }
   p.qs = x->qs;
@@ -931,8 +949,10 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->shw_q = (float*)x->dalloc((size_t)x->N * L * Nq * 4);
     x->shw_g = (float*)x->dalloc((size_t)x->N * L * 2 * F * 4);
     x->fcnt = (unsigned*)x->dalloc((size_t)2 * vfm::FCNT_MAX * 4);
-    if (!x->shw_q || !x->shw_g || !x->fcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
+    x->xcnt = (unsigned*)x->dalloc((size_t)vfm::XCNT_WORDS * 4);
+    if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
     if (vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s) != hipSuccess ||
+        vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s) != hipSuccess ||
         vfm::sk::shift_proj(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, s) != hipSuccess ||
         vfm::sk::shift_proj(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, s) != hipSuccess) {
       fail(VFM_E_HIP, "shift projection tables");
@@ -1070,6 +1090,14 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     }
     return VFM_OK;
   }
+  if (k == "xcd_local") {
+    // the fused kernel's o / down split sums through one XCD's L2 (1, the
+    // default where the plan allows it) or through the device coherence point (0)
+    if (v == "1") x->xcd_local = true;
+    else if (v == "0") x->xcd_local = false;
+    else return fail(VFM_E_INVALID_ARG, "xcd_local must be 0 or 1");
+    return VFM_OK;
+  }
   if (k == "persistent_launch") {
     if (v == "cooperative") x->coop_launch = true;
     else if (v == "plain") x->coop_launch = false;
@@ -1148,6 +1176,15 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if (mode == 0) {
     // one launch per call: the kernel's last workgroup clears the arrival
     // counters, and a failure raises the host-mapped word read by the checks
+    if (p.xl) {
+      const int mt = (p.M + 63) / 64;
+      const long long plan = (((long long)p.gp_s[1] * 64 + p.gp_s[3]) * 4096 + (long long)(p.W / (16 * p.gp_nt[1])) * mt) *
+                                 4096 + (long long)(p.W / (16 * p.gp_nt[3])) * mt;
+      if (plan != x->xl_plan) {
+        HIPCHK(vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s));
+        x->xl_plan = plan;
+      }
+    }
     HIPCHK(vfm::launch_phase(p, x->kset, x->coop_launch ? 0 : 3, 0, 0, 0, x->coop_grid, x->lds, s));
     return VFM_OK;
   }
@@ -1322,8 +1359,9 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   }
   if (n == "persistent_plan") {
     // int32 [fused norms (0 / 1), device-wide barriers per call, o splits,
-    // down splits] of the persistent kernel at the bound batch and prefix
-    if (bytes != 4 * 4) return fail(VFM_E_SHAPE, "'persistent_plan' needs 16 bytes");
+    // down splits, XCD-local split sums (0 / 1)] of the persistent kernel at
+    // the bound batch and prefix
+    if (bytes != 5 * 4) return fail(VFM_E_SHAPE, "'persistent_plan' needs 20 bytes");
     if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
     const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
     if (launch_mode_of(x, B, P) != 0) return fail(VFM_E_STATE, "the expert does not run the persistent kernel");
@@ -1335,6 +1373,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     o[1] = p.fuse ? 1 + x->N * (6 * x->L + 1) : 1 + x->N * (8 * x->L + 2 * x->pi0);
     o[2] = p.S_o;
     o[3] = p.S_down;
+    o[4] = p.fuse ? p.xl : 0;
     return VFM_OK;
   }
   if (n == "trace") {
