@@ -210,7 +210,10 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       mod 8, checked at kernel start from the hardware XCD id; a launch
  *       whose workgroups are placed otherwise uses the device-wide path),
  *       and exchange their partial sums through that XCD's L2 instead of
- *       the device coherence point. Results are bitwise the same as "0".
+ *       the device coherence point; likewise the key splits of attention
+ *       head j and the merge of its rows run on XCD j mod 8. "splits"
+ *       (diagnostics) keeps only the o / down part. Results are bitwise
+ *       the same for every value.
  *   "trace": "1" / "0": record a timeline of the persistent kernel's phase
  *       barriers (workgroup 0), read with vfm_export("trace").
  *   "graph_cache": "1" .. "64" (default 8): graph mode keeps one captured

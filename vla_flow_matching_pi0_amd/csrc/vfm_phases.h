@@ -1058,14 +1058,37 @@ __device__ __forceinline__ void attn_split(const VP& p, int c, int& s0, int& s1)
   }
 }
 
+// Attention unit of grid slot v: (sample x head bh, split c); false past
+// the last unit. Plain order v = bh KS + c. XCD order (xl: the grid a
+// multiple of 8, workgroup w on XCD w % 8): head bh's splits run on XCD
+// bh % 8, v = bh % 8 + 8 ((bh / 8) KS + c), so that the merge of its splits
+// (ph_combine, same placement) reads them from that XCD's L2.
+__device__ __forceinline__ bool attn_unit(const VP& p, int v, bool xl, int& bh, int& c) {
+  const int KS = p.KS, nbh = p.B * p.Hq;
+  if (!xl) {
+    bh = v / KS;
+    c = v % KS;
+    return bh < nbh;
+  }
+  const int r = v >> 3;
+  bh = (r / KS) * 8 + (v & 7);
+  c = r % KS;
+  return bh < nbh;
+}
+__device__ __forceinline__ int attn_slots(const VP& p, bool xl) {
+  const int nbh = p.B * p.Hq;
+  return (xl ? (nbh + 7) / 8 * 8 : nbh) * p.KS;
+}
+
 template <typename T, int D>
-__device__ __forceinline__ bool attn_prefix_unit(const VP& p, int u, int& b, int& kvh, int& s0, int& s1) {
-  const int KS = p.KS;
-  const int c = u % KS, bh = u / KS, jh = bh % p.Hq;
+__device__ __forceinline__ bool attn_prefix_unit(const VP& p, int v, bool xl, int& b, int& kvh, int& s0, int& s1) {
+  int bh, c;
+  if (v >= attn_slots(p, xl) || !attn_unit(p, v, xl, bh, c)) return false;
+  const int jh = bh % p.Hq;
   b = bh / p.Hq;
   kvh = jh / (p.Hq / p.Hkv);
   attn_split(p, c, s0, s1);
-  return u < p.B * p.Hq * KS && s1 <= p.P;
+  return s1 <= p.P;
 }
 
 template <typename T, int D>
@@ -1073,10 +1096,11 @@ struct AttnPrefetchHook {
   const VP& p;
   int layer, wg;
   APre<T, D>& out;
+  bool xl;
   __device__ __forceinline__ void operator()() const {
     const VP& p = vp_fresh();
     int b, kvh, s0, s1;
-    if (!attn_prefix_unit<T, D>(p, wg, b, kvh, s0, s1)) return;
+    if (!attn_prefix_unit<T, D>(p, wg, xl, b, kvh, s0, s1)) return;
     const size_t layer_elems = (size_t)p.B * p.P * p.Hkv * D;
     const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
     const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
@@ -1084,9 +1108,11 @@ struct AttnPrefetchHook {
   }
 };
 
+// xl: XCD-ordered units (attn_unit) whose split outputs stay in the XCD's
+// L2 (write-back stores) for the XCD-local merge.
 template <typename T, int D, bool PRE = false>
 __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, int nwg,
-                                        const APre<T, D>& pre = APre<T, D>{}) {
+                                        const APre<T, D>& pre = APre<T, D>{}, bool xl = false) {
   const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
@@ -1102,15 +1128,17 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
   const int lane = tid & 63, wv = gtid >> 6, g = lane >> 4, c16 = lane & 15;
   const int H = p.H, P = p.P, KS = p.KS;
   const int group = p.Hq / p.Hkv;
-  const int units = p.B * p.Hq * KS;
+  const int slots = attn_slots(p, xl);
   const float scale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
   const size_t layer_elems = (size_t)p.B * P * p.Hkv * D;
   const auto pkr = rsrc(reinterpret_cast<const T*>(p.prefix_k) + (size_t)layer * layer_elems);
   const auto pvr = rsrc(reinterpret_cast<const T*>(p.prefix_v) + (size_t)layer * layer_elems);
   const uint8_t* sl = slab(p, step, layer);
   const auto qrs = rsrc(sl + p.off_q), kgr = rsrc(sl + p.off_k), vgr = rsrc(sl + p.off_v);
-  for (int u = wg; u < units; u += nwg) {
-    const int c = u % KS, bh = u / KS, jh = bh % p.Hq, b = bh / p.Hq;
+  for (int u = wg; u < slots; u += nwg) {
+    int bh, c;
+    if (!attn_unit(p, u, xl, bh, c)) continue;   // the same for the whole workgroup
+    const int jh = bh % p.Hq, b = bh / p.Hq;
     const int kvh = jh / group;
     int s0, s1;
     attn_split(p, c, s0, s1);
@@ -1224,11 +1252,20 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const size_t e0 = base * D + dbase + dt * 16 + 4 * g;
-        if constexpr (sizeof(T) == 4) coh_st16(p.opart, (uint32_t)(e0 * 4), as_u4(O[dt]));
-        else coh_st8(p.opart, (uint32_t)(e0 * 2), u32x2{pack_bf16x2(O[dt][0], O[dt][1]), pack_bf16x2(O[dt][2], O[dt][3])});
+        if constexpr (sizeof(T) == 4) {
+          if (xl) wb_st16(p.opart, (uint32_t)(e0 * 4), as_u4(O[dt]));
+          else coh_st16(p.opart, (uint32_t)(e0 * 4), as_u4(O[dt]));
+        } else {
+          const u32x2 ov = {pack_bf16x2(O[dt][0], O[dt][1]), pack_bf16x2(O[dt][2], O[dt][3])};
+          if (xl) wb_st8(p.opart, (uint32_t)(e0 * 2), ov);
+          else coh_st8(p.opart, (uint32_t)(e0 * 2), ov);
+        }
       }
-      if (g == 0 && grp == 0)
-        coh_st8(p.ml, (uint32_t)(base * 8), u32x2{__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_run)});
+      if (g == 0 && grp == 0) {
+        const u32x2 mlv = {__builtin_bit_cast(uint32_t, m_run), __builtin_bit_cast(uint32_t, l_run)};
+        if (xl) wb_st8(p.ml, (uint32_t)(base * 8), mlv);
+        else coh_st8(p.ml, (uint32_t)(base * 8), mlv);
+      }
     }
   }
 }
@@ -1236,22 +1273,42 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
 // Merge the key splits: attn[b*H+i][j*d + dd] = sum_c w_c O_c / sum_c w_c l_c,
 // w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
 // c's (max, sum), then every lane merges four head dims over all splits.
+// xl: the rows of head bh are merged on XCD bh % 8, where attn_unit placed
+// its splits: their outputs are read from that XCD's L2 (ordinary loads
+// after this compute unit's L1 is invalidated) instead of from memory.
 template <typename T, int WF = 0>
-__device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int wg, int nwg) {
+__device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int wg, int nwg, bool xl = false) {
   const VP& p = vp_fresh();
   constexpr bool Q8 = act_fp8<WF>();
   const int tid = tid_opaque();
   const int D = p.d, KS = p.KS;
   const int lane = tid & 63, wv = tid >> 6;
-  const int items = p.M * p.Hq;
+  // item order: plain (row gm, head jh) = it / Hq, it % Hq over every wave of
+  // the grid; XCD-local: the waves of XCD x take (head 8 q + x, row i) = it / H, it % H
+  const int nbh = p.B * p.Hq, x = wg & 7;
+  const int items = xl ? (nbh > x ? (nbh - x + 7) / 8 : 0) * p.H : p.M * p.Hq;
+  const int it0 = xl ? (wg >> 3) * NWAVES + wv : wg * NWAVES + wv;
+  const int its = xl ? (nwg >> 3) * NWAVES : nwg * NWAVES;
+  if (xl) asm volatile("buffer_inv sc0" ::: "memory");
   uint8_t* attn = slab(p, step, layer) + p.off_attn;
-  for (int it = wg * NWAVES + wv; it < items; it += nwg * NWAVES) {
-    const int jh = it % p.Hq, gm = it / p.Hq;
-    const int b = gm / p.H, i = gm % p.H;
+  for (int it = it0; it < items; it += its) {
+    int jh, b, i;
+    if (xl) {
+      const int bh = (it / p.H) * 8 + x;
+      jh = bh % p.Hq;
+      b = bh / p.Hq;
+      i = it % p.H;
+    } else {
+      jh = it % p.Hq;
+      b = (it / p.Hq) / p.H;
+      i = (it / p.Hq) % p.H;
+    }
+    const int gm = b * p.H + i;
     const size_t base0 = ((size_t)(b * p.Hq + jh) * KS) * 64 + i;
     float mc = -INFINITY, lc = 0.f;
     if (lane < KS) {
-      const floatx2 ml = __builtin_bit_cast(floatx2, coh_ld8(p.ml, (uint32_t)((base0 + (size_t)lane * 64) * 8)));
+      const uint32_t mo = (uint32_t)((base0 + (size_t)lane * 64) * 8);
+      const floatx2 ml = __builtin_bit_cast(floatx2, xl ? ld8_if(rsrc(p.ml), mo, true) : coh_ld8(p.ml, mo));
       mc = ml[0];
       lc = ml[1];
     }
@@ -1267,15 +1324,19 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
         if constexpr (sizeof(T) == 4) {
           u32x4 ov[16];
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            ov[j] = coh_ld16_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4), c0 + j < KS);
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4);
+            ov[j] = xl ? ld16_if(opr, oo, c0 + j < KS) : coh_ld16_if(opr, oo, c0 + j < KS);
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
         } else {
           u32x2 ov[16];
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            ov[j] = coh_ld8_if(opr, (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 2), c0 + j < KS);
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 2);
+            ov[j] = xl ? ld8_if(opr, oo, c0 + j < KS) : coh_ld8_if(opr, oo, c0 + j < KS);
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const floatx4 f = {__builtin_bit_cast(float, ov[j][0] << 16), __builtin_bit_cast(float, ov[j][0] & 0xffff0000u),
@@ -1886,6 +1947,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   else if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
   const bool xl = FUSE && p.xl && ld_agent(&p.bar[BAR_XL_BAD]) == 0u;
+  const bool xla = xl && (p.xl & 2);
   for (int k = 0; k < p.N; ++k) {
     if (p.pi0) {
       // the action tokens' time-MLP output, then layer 0's norm
@@ -1902,11 +1964,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       ph_gemm<T, G_QKV, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
       {
         APre<T, D> apre;
-        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre})) return;
-        ph_attn<T, D, true>(p, k, l, wg, nwg, apre);
+        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre, xla})) return;
+        ph_attn<T, D, true>(p, k, l, wg, nwg, apre, xla);
       }
       VFM_BAR();
-      ph_combine<T, WF>(p, k, l, wg, nwg);
+      ph_combine<T, WF>(p, k, l, wg, nwg, xla);
       VFM_BAR_PF(G_O, l);
       ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre, xl);
       if (!FUSE) {

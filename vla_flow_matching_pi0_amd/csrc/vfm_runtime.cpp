@@ -118,6 +118,7 @@ struct vfm_expert {
   // the split plan changes (xl_plan: S and column groups of o and down) or a
   // launch failed
   bool xcd_local = true;
+  bool xcd_attn = true;                       // ... and the attention splits with their merge
   unsigned* xcnt = nullptr;                   // [2][FCNT_MAX] counters, XCNT_STRIDE words apart
   long long xl_plan = -1;
   // graph variants, most recently used first: key = shape + pointers
@@ -662,7 +663,7 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
       const long ngo = (long)p.W / (16 * p.gp_nt[1]), ngd = (long)p.W / (16 * p.gp_nt[3]);
       auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
       p.xl = x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) &&
-             pow2(p.gp_s[3]) ? 1 : 0;
+             pow2(p.gp_s[3]) ? (x->xcd_attn ? 3 : 1) : 0;
       p.xcnt = x->xcnt;
     }
   }
@@ -1093,9 +1094,10 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
   if (k == "xcd_local") {
     // the fused kernel's o / down split sums through one XCD's L2 (1, the
     // default where the plan allows it) or through the device coherence point (0)
-    if (v == "1") x->xcd_local = true;
+    if (v == "1") x->xcd_local = true, x->xcd_attn = true;
     else if (v == "0") x->xcd_local = false;
-    else return fail(VFM_E_INVALID_ARG, "xcd_local must be 0 or 1");
+    else if (v == "splits") x->xcd_local = true, x->xcd_attn = false;   // diagnostics: o / down sums only
+    else return fail(VFM_E_INVALID_ARG, "xcd_local must be 0, 1 or 'splits'");
     return VFM_OK;
   }
   if (k == "persistent_launch") {
