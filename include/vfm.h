@@ -422,6 +422,12 @@ vfm_status vfm_prefix_run_noalloc(vfm_prefix* pre, const void* embeds, int32_t b
  *       256-column tiles (one workgroup per compute unit, a direct-to-LDS
  *       operand ring; used where N is a multiple of 256 and K of 64) or on
  *       the 128 x 128 tiles of the other GEMMs. Results agree to rounding.
+ *   "down_tiles": "wide" (default) or "narrow": the down projection on the
+ *       same 256-column tiles with K splits (up to 8, partial sums added by
+ *       the next norm) where one round of tiles fills at least 192 compute
+ *       units, every split has at least 1024 K and the tiles cover the
+ *       padded token rows, or on the 128 x 128 tiles. Results agree to
+ *       rounding (a different summation order).
  * Errors: VFM_E_INVALID_ARG for a NULL argument or an unknown key or value. */
 vfm_status vfm_prefix_set_option(vfm_prefix* pre, const char* key, const char* value);
 

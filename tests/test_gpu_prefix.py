@@ -137,6 +137,35 @@ def test_gate_up_tiles_agree(which):
         assert ek <= 1e-3 and ev <= 1e-3, l
 
 
+def test_down_tiles_agree():
+    """The down projection on the 256-column tiles with 8 K splits (the
+    default at the Gemma-2B shape, P = 560: 4 x 8 tiles x 8 splits) and on
+    the 128 x 128 tiles with 4: both against the oracle per layer, and
+    against each other to 1e-3 (the same products, partial sums added in
+    another grouping). Layer 1's keys and values see layer 0's down
+    projection through the residual stream."""
+    from vla_flow_matching_pi0_amd import vfm
+    cfg = PREFIX_CONFIGS["prefix_gemma2b_p560"].replace(num_layers=2, seed=73)
+    params, emb = make_prefix_inputs(cfg)
+    rk, rv = PO.prefix_kv(params, emb, cfg)
+    got = {}
+    for tiles in ("narrow", "wide"):
+        print(f"case prefix down tiles {tiles}", flush=True)
+        dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
+        pre = vfm.PrefixProducer(cfg, dev)
+        del dev
+        pre.set_option("down_tiles", tiles)
+        pre, k, v = run_producer(cfg, params, emb, producer=pre)
+        pre.close()
+        check_layers(k, v, rk, rv)
+        got[tiles] = (k, v)
+    for l in range(cfg.num_layers):
+        ek = rel_l2(got["wide"][0][l], got["narrow"][0][l])
+        ev = rel_l2(got["wide"][1][l], got["narrow"][1][l])
+        print(f"layer {l}: wide vs narrow k {ek:.3e} v {ev:.3e}")
+        assert ek <= 1e-3 and ev <= 1e-3, l
+
+
 def test_prefix_option_is_validated():
     from vla_flow_matching_pi0_amd import vfm
     cfg = PREFIX_CONFIGS["prefix_tiny"]
@@ -144,7 +173,7 @@ def test_prefix_option_is_validated():
     dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
     pre = vfm.PrefixProducer(cfg, dev)
     try:
-        for key, val in (("gate_up_tiles", "huge"), ("no_such_option", "1")):
+        for key, val in (("gate_up_tiles", "huge"), ("down_tiles", "1"), ("no_such_option", "1")):
             with pytest.raises(vfm.VfmError) as e:
                 pre.set_option(key, val)
             assert e.value.name == "VFM_E_INVALID_ARG"

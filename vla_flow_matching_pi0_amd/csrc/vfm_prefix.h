@@ -31,6 +31,7 @@ struct GemmArgs {
   const uint8_t* A;
   const uint8_t* B;
   int N, K, M, Mpad, S;     // S: K splits (EPI_PART only)
+  int bm;                   // EPI_PART: tokens per 256-column tile (part_plan), 0: 128 x 128 tiles
   // EPI_PART: part[s][Mpad][N] fp32
   float* part;
   // EPI_GU: act packed [Mpad/16][N/2/32][64][16 B] (gate/up interleaved columns)
@@ -64,6 +65,15 @@ struct NormArgs {
   int M, Mpad, W;
   float eps;
 };
+
+// Tile plan of a K-split GEMM (EPI_PART): bm tokens per 256-column tile
+// with S splits when that fills one round of at least 192 compute units with
+// at least 1024 K per split and the tiles cover all Mpad rows; else bm = 0
+// (128 x 128 tiles) with narrow_split splits.
+struct PartPlan {
+  int bm, S;
+};
+PartPlan part_plan(int M, int Mpad, int N, int K, int narrow_split, bool wide);
 
 hipError_t prepare();
 // wide_gu: the gate/up GEMM (epi EPI_GU) on the 256-column tiles where the shape takes them

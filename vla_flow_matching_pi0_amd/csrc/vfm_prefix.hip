@@ -143,26 +143,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
   }
 }
 
-// ------------------------------------------------------------------ wide gate/up GEMM
-// The gate/up GEMM (the largest of the pass) on the 256-column tiles of
-// vfm_gemm_wide.h: one workgroup per compute unit, four waves of 128
-// columns x 16 MB tokens, both operands through a 5-stage direct-to-LDS
-// ring. The token blocks are stored in the MFMA lane order already, so the
-// copies are linear. Epilogue: the sums go through LDS half a wave tile at a
-// time and come back transposed, lane (token c, tile il) taking the 16 sums
-// of its token in one 16-column tile (gate and up of 8 features): their 8
-// GeGLU values are one 16-byte piece of the packed operand, and the 64
-// lanes of a store fill whole 1 KiB blocks.
-template <int MB>
-__global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_gu_w(const GemmArgs g) {
+// ------------------------------------------------------------------ wide GEMMs
+// The gate/up GEMM (the largest of the pass) and the down projection on the
+// 256-column tiles of vfm_gemm_wide.h: one workgroup per compute unit, four
+// waves of 128 columns x 16 MB tokens, both operands through a 5-stage
+// direct-to-LDS ring. The token blocks are stored in the MFMA lane order
+// already, so the copies are linear.
+// EPI_GU: the sums go through LDS half a wave tile at a time and come back
+// transposed, lane (token c, tile il) taking the 16 sums of its token in one
+// 16-column tile (gate and up of 8 features): their 8 GeGLU values are one
+// 16-byte piece of the packed operand, and the 64 lanes of a store fill whole
+// 1 KiB blocks.
+// EPI_PART: split s of g.S takes K range [s K / S, (s + 1) K / S) and stores
+// its sums straight from the accumulators into part[s] (the next norm adds
+// the splits); the tiles cover every padded token row (part_plan).
+template <int MB, int EPI>
+__global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_w(const GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
   using C = GW<MB>;
-  const int MTL = (g.M + C::BMT - 1) / C::BMT, NTL = g.N / 256, total = MTL * NTL;
+  const int S = EPI == EPI_PART ? g.S : 1;
+  const int MTL = (g.M + C::BMT - 1) / C::BMT, NTL = g.N / 256, total = MTL * NTL * S;
   const int per = (total + 7) >> 3;
   const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (v >= total) return;
-  const int mt = v % MTL, nt = v / MTL;
-  const int KB32 = g.K >> 5, nblk = g.Mpad >> 4;
+  const int mt = v % MTL, nt = (v / MTL) % NTL, s = v / (MTL * NTL);
+  const int KB32 = g.K >> 5, nblk = g.Mpad >> 4, nst = KB32 / S, kb0 = s * nst;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wn = w & 1, wm = w >> 1;
   // copy i: weight tile nt * 16 + w + 4i (i < 4), else token block
@@ -178,15 +183,29 @@ __global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
       blk = 2 * MB * mt + w + 4 * (i - 4);
       blk = blk < nblk ? blk : nblk - 1;
     }
-    voff[i] = (uint32_t)(blk * KB32) * 1024u + (uint32_t)lane * 16u;
+    voff[i] = (uint32_t)(blk * KB32 + kb0) * 1024u + (uint32_t)lane * 16u;
   }
   floatx4 acc[8][MB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  gw_mainloop<MB>(acc, lds, g.A, g.B, voff, 1024u, KB32, w, lane);
+  gw_mainloop<MB>(acc, lds, g.A, g.B, voff, 1024u, nst, w, lane);
 
+  if constexpr (EPI == EPI_PART) {
+    // lane (c, g) of block (i, j): columns n0 .. n0 + 3 of token c
+    const int g4 = 4 * (lane >> 4), c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n0 = nt * 256 + (wn * 8 + i) * 16 + g4;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int token = mt * C::BMT + (wm * MB + j) * 16 + c;
+        if (token < g.Mpad) *reinterpret_cast<floatx4*>(g.part + ((size_t)s * g.Mpad + token) * g.N + n0) = acc[i][j];
+      }
+    }
+    return;
+  }
   gw_barrier();   // every wave is done with the ring (and every copy has landed)
   floatx4* E = reinterpret_cast<floatx4*>(lds + w * (4 * MB * 1024));
   const int c = lane & 15, il = lane >> 4;
@@ -221,7 +240,7 @@ __global__ __launch_bounds__(GW_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
 // Tokens per tile of the wide gate/up GEMM for M tokens (0: the shape does
 // not fit it): the choice with the least work per compute unit, counting a
 // second round of tiles and a fixed cost per 32-K stage.
-int gu_wide_tokens(const GemmArgs& g) {
+static int gu_wide_tokens(const GemmArgs& g) {
   if (g.N % 256 != 0 || g.S != 1 || g.K % 64 != 0 || g.K / 32 < GW<5>::NS - 1) return 0;
   int best = 0;
   long best_cost = -1;
@@ -438,13 +457,32 @@ hipError_t prepare() {
     return e;
   if ((e = hipFuncSetAttribute((const void*)k_gemm<EPI_GU>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE)) != hipSuccess)
     return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<5>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<5>::LDS)) != hipSuccess)
-    return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<6>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<6>::LDS)) != hipSuccess)
-    return e;
-  if ((e = hipFuncSetAttribute((const void*)k_gemm_gu_w<7>, hipFuncAttributeMaxDynamicSharedMemorySize, GW<7>::LDS)) != hipSuccess)
-    return e;
+  const void* wide[6] = {(const void*)k_gemm_w<5, EPI_GU>, (const void*)k_gemm_w<6, EPI_GU>, (const void*)k_gemm_w<7, EPI_GU>,
+                         (const void*)k_gemm_w<5, EPI_PART>, (const void*)k_gemm_w<6, EPI_PART>,
+                         (const void*)k_gemm_w<7, EPI_PART>};
+  const int wlds[3] = {GW<5>::LDS, GW<6>::LDS, GW<7>::LDS};
+  for (int i = 0; i < 6; ++i)
+    if ((e = hipFuncSetAttribute(wide[i], hipFuncAttributeMaxDynamicSharedMemorySize, wlds[i % 3])) != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)k_gemm<EPI_QKV>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
+}
+
+PartPlan part_plan(int M, int Mpad, int N, int K, int narrow_split, bool wide) {
+  PartPlan best{0, narrow_split};
+  if (!wide || N % 256 != 0 || K % 64 != 0) return best;
+  long best_fill = 0;
+  for (int mb : {5, 6, 7}) {
+    const int bmt = 32 * mb, mtl = (M + bmt - 1) / bmt;
+    if ((long)mtl * bmt < Mpad) continue;   // every padded row gets its partial sums
+    const int ring = mb == 5 ? GW<5>::NS : mb == 6 ? GW<6>::NS : GW<7>::NS;
+    const long tiles = (long)mtl * (N / 256);
+    for (int sp = 1; sp <= MAX_SPLIT; sp *= 2) {
+      const int nst = K / 32 / sp;
+      if (K % (64 * sp) != 0 || nst < ring - 1 || nst * 32 < 1024 || tiles * sp > 256) continue;
+      if (tiles * sp > best_fill) best_fill = tiles * sp, best = PartPlan{bmt, sp};
+    }
+  }
+  // one round of tiles on at least three quarters of the compute units
+  return best_fill >= 192 ? best : PartPlan{0, narrow_split};
 }
 
 hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
@@ -452,11 +490,19 @@ hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
     const int bm = gu_wide_tokens(g);
     if (bm > 0) {
       const int tiles = (g.N / 256) * ((g.M + bm - 1) / bm), grid = (tiles + 7) / 8 * 8;
-      if (bm == 160) hipLaunchKernelGGL(k_gemm_gu_w<5>, dim3(grid), dim3(GW_THREADS), GW<5>::LDS, st, g);
-      else if (bm == 192) hipLaunchKernelGGL(k_gemm_gu_w<6>, dim3(grid), dim3(GW_THREADS), GW<6>::LDS, st, g);
-      else hipLaunchKernelGGL(k_gemm_gu_w<7>, dim3(grid), dim3(GW_THREADS), GW<7>::LDS, st, g);
+      if (bm == 160) hipLaunchKernelGGL((k_gemm_w<5, EPI_GU>), dim3(grid), dim3(GW_THREADS), GW<5>::LDS, st, g);
+      else if (bm == 192) hipLaunchKernelGGL((k_gemm_w<6, EPI_GU>), dim3(grid), dim3(GW_THREADS), GW<6>::LDS, st, g);
+      else hipLaunchKernelGGL((k_gemm_w<7, EPI_GU>), dim3(grid), dim3(GW_THREADS), GW<7>::LDS, st, g);
       return hipGetLastError();
     }
+  }
+  if (epi == EPI_PART && g.bm > 0) {
+    const int tiles = (g.N / 256) * ((g.M + g.bm - 1) / g.bm) * g.S, grid = (tiles + 7) / 8 * 8;
+    if (g.bm == 160) hipLaunchKernelGGL((k_gemm_w<5, EPI_PART>), dim3(grid), dim3(GW_THREADS), GW<5>::LDS, st, g);
+    else if (g.bm == 192) hipLaunchKernelGGL((k_gemm_w<6, EPI_PART>), dim3(grid), dim3(GW_THREADS), GW<6>::LDS, st, g);
+    else if (g.bm == 224) hipLaunchKernelGGL((k_gemm_w<7, EPI_PART>), dim3(grid), dim3(GW_THREADS), GW<7>::LDS, st, g);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
   }
   const int total = (g.Mpad / TM) * (g.N / TN) * g.S;
   const int grid = (total + 7) / 8 * 8;

@@ -41,6 +41,7 @@ struct vfm_prefix {
   float* rope = nullptr;     // [maxP][d/2][2]
   int rope_P = -1;
   bool wide_gu = true;       // option "gate_up_tiles"
+  bool wide_down = true;     // option "down_tiles"
 
   void* dalloc(size_t bytes) {
     void* p = nullptr;
@@ -314,7 +315,9 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
   const int M = B * P, Mpad = (int)round_up(M, pfx::TM), Ppad = (int)round_up(P, pfx::AK);
   const size_t kv_layer = (size_t)B * P * Hkv * d;
   const int MT = Mpad / pfx::TM;
-  const int S_o = plan_split(MT * (W / pfx::TN), Hq * d), S_d = plan_split(MT * (W / pfx::TN), F);
+  const int S_o = plan_split(MT * (W / pfx::TN), Hq * d);
+  const pfx::PartPlan pd = pfx::part_plan(M, Mpad, W, F, plan_split(MT * (W / pfx::TN), F), x->wide_down);
+  const int S_d = pd.S;
 
   pfx::NormArgs na{};
   na.embeds = static_cast<const uint16_t*>(embeds);
@@ -340,13 +343,13 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
     if (last) break;
     aa.k = kl;
     PCHK(pfx::attention(d, aa, B, s));
-    ga.A = x->w_o[l]; ga.B = ws.attn; ga.N = W; ga.K = Hq * d; ga.S = S_o;
+    ga.A = x->w_o[l]; ga.B = ws.attn; ga.N = W; ga.K = Hq * d; ga.S = S_o; ga.bm = 0;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
     na.gain = x->g_mlp[l]; na.S = S_o;
     PCHK(pfx::norm(false, na, s));
     ga.A = x->w_gu[l]; ga.B = ws.xn; ga.N = 2 * F; ga.K = W; ga.S = 1;
     PCHK(pfx::gemm(pfx::EPI_GU, ga, s, x->wide_gu));
-    ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d;
+    ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d; ga.bm = pd.bm;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
   }
   return VFM_OK;
@@ -375,7 +378,9 @@ vfm_status vfm_prefix_run_noalloc(vfm_prefix* x, const void* embeds, int32_t B, 
   const size_t W = x->W, F = x->F, qd = (size_t)x->Hq * x->d;
   const size_t Mpad = round_up((size_t)B * P, pfx::TM), Ppad = round_up(P, pfx::AK);
   const int MT = (int)(Mpad / pfx::TM);
-  const size_t S = (size_t)std::max(plan_split(MT * ((int)W / pfx::TN), (int)qd), plan_split(MT * ((int)W / pfx::TN), (int)F));
+  const pfx::PartPlan pd = pfx::part_plan(B * P, (int)Mpad, (int)W, (int)F, plan_split(MT * ((int)W / pfx::TN), (int)F),
+                                          x->wide_down);
+  const size_t S = (size_t)std::max(plan_split(MT * ((int)W / pfx::TN), (int)qd), pd.S);
   // this call's workspace, carved from the static array (256-byte aligned pieces)
   const size_t sz[8] = {Mpad * W * 4, S * Mpad * W * 4, Mpad * W * 2, Mpad * qd * 2, Mpad * F * 2, Mpad * qd * 2,
                         (size_t)B * x->Hkv * x->d * Ppad * 2, (size_t)P * x->d * 4};
@@ -411,6 +416,12 @@ vfm_status vfm_prefix_set_option(vfm_prefix* x, const char* key, const char* val
     if (v == "wide") x->wide_gu = true;
     else if (v == "narrow") x->wide_gu = false;
     else return report(VFM_E_INVALID_ARG, "gate_up_tiles must be 'wide' or 'narrow'");
+    return VFM_OK;
+  }
+  if (k == "down_tiles") {
+    if (v == "wide") x->wide_down = true;
+    else if (v == "narrow") x->wide_down = false;
+    else return report(VFM_E_INVALID_ARG, "down_tiles must be 'wide' or 'narrow'");
     return VFM_OK;
   }
   return report(VFM_E_INVALID_ARG, "unknown option '%s'", key);
