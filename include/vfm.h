@@ -428,6 +428,10 @@ vfm_status vfm_prefix_run_noalloc(vfm_prefix* pre, const void* embeds, int32_t b
  *       units, every split has at least 1024 K and the tiles cover the
  *       padded token rows, or on the 128 x 128 tiles. Results agree to
  *       rounding (a different summation order).
+ *   "qkv_tiles": "auto" (default) or "full": the fused QKV projection on
+ *       128-token x 64-column tiles where 128 x 128 tiles would number at
+ *       most 128 (half the compute units), or always on 128 x 128 tiles.
+ *       Results are the same (each output's sum is formed the same way).
  * Errors: VFM_E_INVALID_ARG for a NULL argument or an unknown key or value. */
 vfm_status vfm_prefix_set_option(vfm_prefix* pre, const char* key, const char* value);
 

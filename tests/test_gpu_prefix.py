@@ -166,6 +166,30 @@ def test_down_tiles_agree():
         assert ek <= 1e-3 and ev <= 1e-3, l
 
 
+def test_qkv_tiles_bitwise_equal():
+    """The fused QKV projection on 128 x 64 tiles (the default at the
+    Gemma-2B shape: 100 tiles of 128 x 128 would leave most compute units
+    idle) and on 128 x 128 tiles: every output is the same sum of the same
+    bf16 products in the same k order, so the keys and values agree bit for
+    bit; both match the oracle."""
+    from vla_flow_matching_pi0_amd import vfm
+    cfg = PREFIX_CONFIGS["prefix_gemma2b_p560"].replace(num_layers=2, seed=74)
+    params, emb = make_prefix_inputs(cfg)
+    rk, rv = PO.prefix_kv(params, emb, cfg)
+    got = {}
+    for tiles in ("full", "auto"):
+        print(f"case prefix qkv tiles {tiles}", flush=True)
+        dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
+        pre = vfm.PrefixProducer(cfg, dev)
+        del dev
+        pre.set_option("qkv_tiles", tiles)
+        pre, k, v = run_producer(cfg, params, emb, producer=pre)
+        pre.close()
+        check_layers(k, v, rk, rv)
+        got[tiles] = (k, v)
+    assert np.array_equal(got["full"][0], got["auto"][0]) and np.array_equal(got["full"][1], got["auto"][1])
+
+
 def test_prefix_option_is_validated():
     from vla_flow_matching_pi0_amd import vfm
     cfg = PREFIX_CONFIGS["prefix_tiny"]
@@ -173,7 +197,7 @@ def test_prefix_option_is_validated():
     dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
     pre = vfm.PrefixProducer(cfg, dev)
     try:
-        for key, val in (("gate_up_tiles", "huge"), ("down_tiles", "1"), ("no_such_option", "1")):
+        for key, val in (("gate_up_tiles", "huge"), ("down_tiles", "1"), ("qkv_tiles", "half"), ("no_such_option", "1")):
             with pytest.raises(vfm.VfmError) as e:
                 pre.set_option(key, val)
             assert e.value.name == "VFM_E_INVALID_ARG"

@@ -32,12 +32,17 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) { return (uint32_t)__buil
 // next stage's global loads are in flight while the current one computes.
 // Block b runs on XCD b % 8; each XCD takes a contiguous range of tiles,
 // tokens fastest, so the token tiles that share a weight tile share an L2.
+// TNC = 64 (half-width tiles, twice as many: a GEMM with few 128 x 128
+// tiles, such as the fused QKV projection) keeps the stage layout, the A
+// half of the stage half filled, and gives each wave 32 x 64.
 constexpr int STAGE = 2 * 16384;   // A tile + B tile bytes
 
-template <int EPI>
+template <int EPI, int TNC = TN>
 __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int MTL = g.Mpad / TM, NTL = g.N / TN, total = MTL * NTL * g.S;
+  constexpr int NB = TNC / 32;          // 16-column blocks per wave
+  constexpr int AL = TNC / 32;          // A chunks per thread and stage (16 bytes each)
+  const int MTL = g.Mpad / TM, NTL = g.N / TNC, total = MTL * NTL * g.S;
   const int per = (total + 7) >> 3;
   const int v = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (v >= total) return;
@@ -49,14 +54,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i, blk = c >> 7, rest = c & 127;
-    aoff[i] = (uint32_t)(((nt * 8 + blk) * KB32 + (s * Ks >> 5)) * 1024 + rest * 16);
+    aoff[i] = (uint32_t)(((nt * (TNC / 16) + blk) * KB32 + (s * Ks >> 5)) * 1024 + rest * 16);
     boff[i] = (uint32_t)(((mt * 8 + blk) * KB32 + (s * Ks >> 5)) * 1024 + rest * 16);
   }
   u32x4 ga[4], gb[4];
   auto gload = [&](int it) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + (uint32_t)it * 2048u, 0, 0);
+      if (i < AL) ga[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] + (uint32_t)it * 2048u, 0, 0);
       gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[i] + (uint32_t)it * 2048u, 0, 0);
     }
   };
@@ -64,13 +69,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
     u32x4* A = reinterpret_cast<u32x4*>(lds + buf * STAGE);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      A[tid + 256 * i] = ga[i];
+      if (i < AL) A[tid + 256 * i] = ga[i];
       A[1024 + tid + 256 * i] = gb[i];
     }
   };
-  floatx4 acc[4][4];
+  floatx4 acc[NB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -83,13 +88,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
     const u32x4* B = A + 1024;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x4 a[4], b[4];
+      u32x4 a[NB], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = A[(wn * 4 + i) * 128 + kb * 64 + lane];
+      for (int i = 0; i < NB; ++i) a[i] = A[(wn * NB + i) * 128 + kb * 64 + lane];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = B[(wm * 4 + j) * 128 + kb * 64 + lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = MT<bf16>::mma(a[i], b[j], acc[i][j]);
     }
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const GemmArgs g) {
   // epilogue: lane holds D[n0 + r][token], r = 0..3
   const int g4 = 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n0 = nt * TN + wn * 64 + i * 16 + g4;
+  for (int i = 0; i < NB; ++i) {
+    const int n0 = nt * TNC + wn * (TNC / 2) + i * 16 + g4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int token = mt * TM + wm * 64 + j * 16 + (lane & 15);
@@ -463,6 +468,9 @@ hipError_t prepare() {
   const int wlds[3] = {GW<5>::LDS, GW<6>::LDS, GW<7>::LDS};
   for (int i = 0; i < 6; ++i)
     if ((e = hipFuncSetAttribute(wide[i], hipFuncAttributeMaxDynamicSharedMemorySize, wlds[i % 3])) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm<EPI_QKV, 64>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE)) !=
+      hipSuccess)
+    return e;
   return hipFuncSetAttribute((const void*)k_gemm<EPI_QKV>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
 }
 
@@ -506,6 +514,12 @@ hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
   }
   const int total = (g.Mpad / TM) * (g.N / TN) * g.S;
   const int grid = (total + 7) / 8 * 8;
+  if (epi == EPI_QKV && g.qkv_half && total <= 128 && g.N % 64 == 0) {
+    // fewer 128 x 128 tiles than half the compute units: 128 x 64 tiles
+    const int grid64 = (2 * total + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_gemm<EPI_QKV, 64>), dim3(grid64), dim3(256), 2 * STAGE, st, g);
+    return hipGetLastError();
+  }
   switch (epi) {
     case EPI_PART: hipLaunchKernelGGL(k_gemm<EPI_PART>, dim3(grid), dim3(256), 2 * STAGE, st, g); break;
     case EPI_GU: hipLaunchKernelGGL(k_gemm<EPI_GU>, dim3(grid), dim3(256), 2 * STAGE, st, g); break;

@@ -42,6 +42,7 @@ struct vfm_prefix {
   int rope_P = -1;
   bool wide_gu = true;       // option "gate_up_tiles"
   bool wide_down = true;     // option "down_tiles"
+  bool half_qkv = true;      // option "qkv_tiles"
 
   void* dalloc(size_t bytes) {
     void* p = nullptr;
@@ -325,6 +326,7 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
   pfx::GemmArgs ga{};
   ga.M = M; ga.Mpad = Mpad; ga.P = P; ga.Ppad = Ppad; ga.Hq = Hq; ga.Hkv = Hkv; ga.d = d;
   ga.part = ws.part; ga.act = ws.act; ga.q = ws.q; ga.vt = ws.vt; ga.rope = ws.rope;
+  ga.qkv_half = x->half_qkv ? 1 : 0;
   pfx::AttnArgs aa{};
   aa.q = ws.q; aa.vt = ws.vt; aa.out = ws.attn; aa.P = P; aa.Ppad = Ppad; aa.Hq = Hq; aa.Hkv = Hkv;
   aa.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
@@ -416,6 +418,12 @@ vfm_status vfm_prefix_set_option(vfm_prefix* x, const char* key, const char* val
     if (v == "wide") x->wide_gu = true;
     else if (v == "narrow") x->wide_gu = false;
     else return report(VFM_E_INVALID_ARG, "gate_up_tiles must be 'wide' or 'narrow'");
+    return VFM_OK;
+  }
+  if (k == "qkv_tiles") {
+    if (v == "auto") x->half_qkv = true;
+    else if (v == "full") x->half_qkv = false;
+    else return report(VFM_E_INVALID_ARG, "qkv_tiles must be 'auto' or 'full'");
     return VFM_OK;
   }
   if (k == "down_tiles") {
