@@ -258,25 +258,33 @@ static int gu_wide_tokens(const GemmArgs& g) {
 }
 
 // ------------------------------------------------------------------ attention
-// Workgroup (query block of 64, head h, sample b); wave w owns 16 queries.
+// Workgroup (query block of AQ = 32, head h, sample b), two groups of two
+// waves: group q takes the key tiles kt = q, q + 2, ..., each through its own
+// LDS stage, and wave w of a group owns queries 16 (w % 2) .. + 15; the two
+// groups' running outputs are merged through LDS at the end (one wave per
+// SIMD: one group's LDS -> MFMA -> softmax chain overlaps the other's).
 // Per 32-key tile: K [32][d] and V^T [d][32] staged in LDS (padded rows);
 // S^T = K Q^T on MFMA (lane: keys 4g..4g+3 of each 16-key half, query l % 16),
 // online softmax in the log2 domain per query column, then O^T += V^T P^T
 // where the 32 keys of the MFMA's k index are ordered (4g..4g+3, 16+4g..16+4g+3)
 // on both operands, so P^T comes straight from the S^T registers.
 template <int D>
-__global__ __launch_bounds__(AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
-  constexpr int NT = AQ / 16 * 64;     // one wave per 16 queries
+__global__ __launch_bounds__(2 * AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
+  constexpr int GT = AQ / 16 * 64;     // threads of one group (one wave per 16 queries)
   constexpr int KROW = 2 * D + 16;     // bytes per K row in LDS
   constexpr int VROW = 2 * AK + 16;    // bytes per V^T row in LDS
-  constexpr int CPT = AK * D / 8 / NT; // 16-byte chunks per thread per operand tile
-  static_assert(AK * D / 8 == D * AK / 8 && AK * D / 8 % NT == 0, "tiles must split evenly over the threads");
-  __shared__ __align__(16) uint8_t sk[AK * KROW];
-  __shared__ __align__(16) uint8_t sv[D * VROW];
+  constexpr int CPT = AK * D / 8 / GT; // 16-byte chunks per thread per operand tile
+  constexpr int GLDS = AK * KROW + D * VROW;   // one group's stage
+  static_assert(AK * D / 8 % GT == 0, "tiles must split evenly over a group's threads");
+  static_assert((D / 16) * 4 * 4 * GT + 2 * 4 * GT <= GLDS, "the merge fits in one group's stage");
+  __shared__ __align__(16) uint8_t lds[2 * GLDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int grp = tid / GT, gtid = tid % GT, wq = w % (AQ / 16);
+  uint8_t* sk = lds + grp * GLDS;
+  uint8_t* sv = sk + AK * KROW;
   const int h = blockIdx.y, b = blockIdx.z, kvh = h / (a.Hq / a.Hkv);
   const int P = a.P;
-  const int qi = blockIdx.x * AQ + w * 16 + c16;
+  const int qi = blockIdx.x * AQ + wq * 16 + c16;
   const bool qok = qi < P;
   const __amdgpu_buffer_rsrc_t rq = rsrc(a.q), rk = rsrc(a.k), rv = rsrc(a.vt);
 
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
   auto fetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
+      const int c = gtid + GT * i;
       const int key = c / (D / 8), part = c % (D / 8);
       const int kk = kt * AK + key;
       pkk[i] = ld16_if(rk, (uint32_t)((((size_t)b * P + kk) * a.Hkv + kvh) * D + part * 8) * 2, kk < P);
@@ -304,17 +312,24 @@ __global__ __launch_bounds__(AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
           rv, (uint32_t)((((size_t)b * a.Hkv + kvh) * D + dim) * a.Ppad + kt * AK + vp * 8) * 2, 0, 0);
     }
   };
-  fetch(0);
-  for (int kt = 0; kt < ntile; ++kt) {
+  if (grp < ntile) fetch(grp);
+  // both groups take the same number of steps (barriers are workgroup-wide);
+  // a group past the last tile idles through its final step
+  for (int it = 0; it < (ntile + 1) / 2; ++it) {
+    const int kt = 2 * it + grp;
+    const bool live = kt < ntile;
     __syncthreads();
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
-      *reinterpret_cast<u32x4*>(sk + (c / (D / 8)) * KROW + (c % (D / 8)) * 16) = pkk[i];
-      *reinterpret_cast<u32x4*>(sv + (c >> 2) * VROW + (c & 3) * 16) = pvv[i];
+      for (int i = 0; i < CPT; ++i) {
+        const int c = gtid + GT * i;
+        *reinterpret_cast<u32x4*>(sk + (c / (D / 8)) * KROW + (c % (D / 8)) * 16) = pkk[i];
+        *reinterpret_cast<u32x4*>(sv + (c >> 2) * VROW + (c & 3) * 16) = pvv[i];
+      }
     }
     __syncthreads();
-    if (kt + 1 < ntile) fetch(kt + 1);
+    if (kt + 2 < ntile) fetch(kt + 2);
+    if (!live) continue;
 
     floatx4 s[2];
 #pragma unroll
@@ -373,6 +388,27 @@ __global__ __launch_bounds__(AQ / 16 * 64, 2) void k_attn(const AttnArgs a) {
       vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = hi[0]; vf[3] = hi[1];
       o[db] = MT<bf16>::mma(vf, pb, o[db]);
     }
+  }
+  // merge: group 1 leaves (m, l, o) in its stage; group 0 rescales both to
+  // the larger reference point (a group that saw no key has m = -inf and
+  // weight 0) and stores
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(lds + GLDS);
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *reinterpret_cast<floatx4*>(xo + (db * GT + gtid) * 4) = o[db];
+    xo[(D / 16) * GT * 4 + gtid] = m;
+    xo[(D / 16) * GT * 4 + GT + gtid] = l;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = xo[(D / 16) * GT * 4 + gtid], l1 = xo[(D / 16) * GT * 4 + GT + gtid];
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : fast_exp2(m - mm), a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = o[db] * a0 + *reinterpret_cast<const floatx4*>(xo + (db * GT + gtid) * 4) * a1;
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -531,9 +567,9 @@ hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
 hipError_t attention(int d, const AttnArgs& a, int B, hipStream_t st) {
   const dim3 grid((a.P + AQ - 1) / AQ, a.Hq, B);
   switch (d) {
-    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
-    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
-    case 256: hipLaunchKernelGGL(k_attn<256>, grid, dim3(AQ / 16 * 64), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_attn<64>, grid, dim3(2 * AQ / 16 * 64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_attn<128>, grid, dim3(2 * AQ / 16 * 64), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(k_attn<256>, grid, dim3(2 * AQ / 16 * 64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
