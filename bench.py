@@ -249,9 +249,9 @@ def phase_breakdown(t, nb, N, L, fused, pi0):
     release to this arrival, wait from arrival to release."""
     if pi0 or L < 3:
         return None
-    names = (["qkv", "attn", "combine", "o", "gu", "down"] if fused
+    names = (["qkv", "attn", "o", "gu", "down"] if fused
              else ["rn_attn", "qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"])
-    per_step = 6 * L + 1 if fused else 8 * L
+    per_step = len(names) * L + 1 if fused else 8 * L
     # barrier index i ends the phase that ran before it; the first layer-l
     # phase of step k (k >= 0) follows barrier 1 + k * per_step + (l * len(names) - (0 if fused else 1))
     out = {n: [0.0, 0.0] for n in names}

@@ -253,4 +253,28 @@ __device__ __forceinline__ bool grid_barrier(unsigned* bar, unsigned& epoch, uns
   return s_ok != 0;
 }
 
+// Wait until the arrival counter *cnt reaches `target` (thread 0 polls, the
+// workgroup then proceeds together), with grid_barrier's bounded spin and
+// sticky error word: returns false, in every thread, when the wait gave up or
+// another wait already had. Every thread of the workgroup must call it.
+__device__ __forceinline__ bool counter_wait(const unsigned* cnt, unsigned target, unsigned* bar, long spin_limit,
+                                             unsigned* herr) {
+  __shared__ unsigned s_cok;
+  if (threadIdx.x == 0) {
+    unsigned ok = 1;
+    long spins = 0;
+    while (ld_agent(cnt) < target) {
+      if ((++spins & 1023) == 0 && (ld_agent(&bar[1]) != 0u || spins > spin_limit)) {
+        __hip_atomic_fetch_or(&bar[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (herr) __hip_atomic_store(herr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        ok = 0;
+        break;
+      }
+    }
+    s_cok = ok;
+  }
+  __syncthreads();
+  return s_cok != 0;
+}
+
 }  // namespace vfm

@@ -83,7 +83,10 @@ struct VP {
   unsigned* fcnt;          // arrival counters: [2 (o, down)][FCNT_MAX]; zero between launches
   int xl;                  // 1: the o / down split units of a column group share an XCD (see ph_gemm)
   unsigned* xcnt;          // their XCD-local arrival counters, [2][FCNT_MAX] at XCNT_STRIDE words
+  unsigned* hcnt;          // attention heads' arrival counters, [HCNT_MAX] at HCNT_STRIDE words; zero between launches
 };
+constexpr int HCNT_MAX = 1024;   // samples x query heads the folded attention merge takes
+constexpr int HCNT_STRIDE = 32;
 constexpr int FCNT_MAX = 4096;   // counters per split GEMM: 16-column tile groups x 64-row tiles
 constexpr int XCNT_STRIDE = 32;  // one 128-byte line per XCD-local counter
 constexpr int XCNT_WORDS = 2 * FCNT_MAX * XCNT_STRIDE;

@@ -1108,10 +1108,23 @@ struct AttnPrefetchHook {
   }
 };
 
+template <typename T, bool Q8>
+__device__ __forceinline__ void combine_row(const VP& p, int layer, uint8_t* attn, int b, int jh, int i, int lane,
+                                            bool xl);
+
 // xl: XCD-ordered units (attn_unit) whose split outputs stay in the XCD's
 // L2 (write-back stores) for the XCD-local merge.
-template <typename T, int D, bool PRE = false>
-__device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, int nwg,
+// MERGE (the folded-norm persistent kernel): the key splits of a head are
+// merged in this phase instead of a combine phase behind a device-wide
+// barrier. Each unit, once its split output is stored, adds 1 to its head's
+// arrival counter (one 128-byte line per head, so that a head's arrivals and
+// polls do not queue behind other heads'); after its last unit, a workgroup
+// waits for each of its units' heads to have all KS splits and merges that
+// unit's share of the head's query rows (rows c, c + KS, ...). Every arrival
+// comes before any wait, so the waits cannot form a cycle. Returns false when
+// a wait gave up.
+template <typename T, int D, bool PRE = false, bool MERGE = false>
+__device__ __forceinline__ bool ph_attn(const VP&, int step, int layer, int wg, int nwg,
                                         const APre<T, D>& pre = APre<T, D>{}, bool xl = false) {
   const VP& p = vp_fresh();
   const int tid = tid_opaque();
@@ -1174,7 +1187,7 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
       for (int e = 0; e < EPC; ++e) Vt[(e0 + e) * LDV + kk] = ve[e];
     }
     __syncthreads();
-    if (!active) continue;
+    if (active) {
     float m_run = -INFINITY, l_run = 0.f;
     floatx4 O[DT];
 #pragma unroll
@@ -1267,12 +1280,90 @@ __device__ __forceinline__ void ph_attn(const VP&, int step, int layer, int wg, 
         else coh_st8(p.ml, (uint32_t)(base * 8), mlv);
       }
     }
+    }   // active
+    if constexpr (MERGE) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's split output is stored
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(&p.hcnt[bh * HCNT_STRIDE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if constexpr (MERGE) {
+    // the counters count every arrival of the launch: this layer's target is
+    // KS times the number of (step, layer) instances so far
+    const unsigned target = (unsigned)((step * p.L + layer + 1) * KS);
+    uint8_t* attn = slab(p, step, layer) + p.off_attn;
+    const int wv8 = tid >> 6;
+    for (int u = wg; u < slots; u += nwg) {
+      int bh, c;
+      if (!attn_unit(p, u, xl, bh, c)) continue;
+      if (!counter_wait(&p.hcnt[bh * HCNT_STRIDE], target, p.bar, p.spin_limit, p.herr)) return false;
+      if (xl) asm volatile("buffer_inv sc0" ::: "memory");
+      for (int i = c + wv8 * KS; i < H; i += NWAVES * KS)
+        combine_row<T, false>(p, layer, attn, bh / p.Hq, bh % p.Hq, i, lane, xl);
+    }
+  }
+  return true;
+}
+
+// Merge the key splits of query row i of head jh (sample b), one wave:
+// attn[b*H+i][jh*d + dd] = sum_c w_c O_c / sum_c w_c l_c, w_c = 2^(m_c - max m).
+// Lane c first fetches split c's (max, sum), then every lane merges four
+// head dims over all splits. xl: the splits were stored on this XCD and are
+// read from its L2 with ordinary loads (the caller has invalidated its L1);
+// else from the coherence point.
+template <typename T, bool Q8>
+__device__ __forceinline__ void combine_row(const VP& p, int layer, uint8_t* attn, int b, int jh, int i, int lane,
+                                            bool xl) {
+  const int D = p.d, KS = p.KS;
+  const int gm = b * p.H + i;
+  const size_t base0 = ((size_t)(b * p.Hq + jh) * KS) * 64 + i;
+  float mc = -INFINITY, lc = 0.f;
+  if (lane < KS) {
+    const uint32_t mo = (uint32_t)((base0 + (size_t)lane * 64) * 8);
+    const floatx2 ml = __builtin_bit_cast(floatx2, xl ? ld8_if(rsrc(p.ml), mo, true) : coh_ld8(p.ml, mo));
+    mc = ml[0];
+    lc = ml[1];
+  }
+  float mx = mc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float wc = lane < KS ? fast_exp2(mc - mx) : 0.f;
+  const float den = warp_sum(wc * lc);
+  const auto opr = rsrc(p.opart);
+  for (int d4 = lane; d4 < D / 4; d4 += 64) {
+    floatx4 num = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < KS; c0 += 16) {
+      if constexpr (sizeof(T) == 4) {
+        u32x4 ov[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4);
+          ov[j] = xl ? ld16_if(opr, oo, c0 + j < KS) : coh_ld16_if(opr, oo, c0 + j < KS);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
+      } else {
+        u32x2 ov[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 2);
+          ov[j] = xl ? ld8_if(opr, oo, c0 + j < KS) : coh_ld8_if(opr, oo, c0 + j < KS);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const floatx4 f = {__builtin_bit_cast(float, ov[j][0] << 16), __builtin_bit_cast(float, ov[j][0] & 0xffff0000u),
+                             __builtin_bit_cast(float, ov[j][1] << 16), __builtin_bit_cast(float, ov[j][1] & 0xffff0000u)};
+          num += __shfl(wc, (c0 + j) & 63) * f;
+        }
+      }
+    }
+    const floatx4 o = num / den;
+    store_gemm_in4<T, Q8>(p, attn, gm, jh * D + d4 * 4, o, Q8 ? act_inv(p, layer, 1) : 1.0f);
   }
 }
 
-// Merge the key splits: attn[b*H+i][j*d + dd] = sum_c w_c O_c / sum_c w_c l_c,
-// w_c = 2^(m_c - max m). One wave per (row, head): lane c first fetches split
-// c's (max, sum), then every lane merges four head dims over all splits.
+// Merge phase: one wave per (row, head) item.
 // xl: the rows of head bh are merged on XCD bh % 8, where attn_unit placed
 // its splits: their outputs are read from that XCD's L2 (ordinary loads
 // after this compute unit's L1 is invalidated) instead of from memory.
@@ -1281,7 +1372,6 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
   const VP& p = vp_fresh();
   constexpr bool Q8 = act_fp8<WF>();
   const int tid = tid_opaque();
-  const int D = p.d, KS = p.KS;
   const int lane = tid & 63, wv = tid >> 6;
   // item order: plain (row gm, head jh) = it / Hq, it % Hq over every wave of
   // the grid; XCD-local: the waves of XCD x take (head 8 q + x, row i) = it / H, it % H
@@ -1303,51 +1393,7 @@ __device__ __forceinline__ void ph_combine(const VP&, int step, int layer, int w
       b = (it / p.Hq) / p.H;
       i = (it / p.Hq) % p.H;
     }
-    const int gm = b * p.H + i;
-    const size_t base0 = ((size_t)(b * p.Hq + jh) * KS) * 64 + i;
-    float mc = -INFINITY, lc = 0.f;
-    if (lane < KS) {
-      const uint32_t mo = (uint32_t)((base0 + (size_t)lane * 64) * 8);
-      const floatx2 ml = __builtin_bit_cast(floatx2, xl ? ld8_if(rsrc(p.ml), mo, true) : coh_ld8(p.ml, mo));
-      mc = ml[0];
-      lc = ml[1];
-    }
-    float mx = mc;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float wc = lane < KS ? fast_exp2(mc - mx) : 0.f;
-    const float den = warp_sum(wc * lc);
-    const auto opr = rsrc(p.opart);
-    for (int d4 = lane; d4 < D / 4; d4 += 64) {
-      floatx4 num = {0, 0, 0, 0};
-      for (int c0 = 0; c0 < KS; c0 += 16) {
-        if constexpr (sizeof(T) == 4) {
-          u32x4 ov[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 4);
-            ov[j] = xl ? ld16_if(opr, oo, c0 + j < KS) : coh_ld16_if(opr, oo, c0 + j < KS);
-          }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) num += __shfl(wc, (c0 + j) & 63) * as_f4(ov[j]);
-        } else {
-          u32x2 ov[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const uint32_t oo = (uint32_t)(((base0 + (size_t)(c0 + j) * 64) * D + d4 * 4) * 2);
-            ov[j] = xl ? ld8_if(opr, oo, c0 + j < KS) : coh_ld8_if(opr, oo, c0 + j < KS);
-          }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const floatx4 f = {__builtin_bit_cast(float, ov[j][0] << 16), __builtin_bit_cast(float, ov[j][0] & 0xffff0000u),
-                               __builtin_bit_cast(float, ov[j][1] << 16), __builtin_bit_cast(float, ov[j][1] & 0xffff0000u)};
-            num += __shfl(wc, (c0 + j) & 63) * f;
-          }
-        }
-      }
-      const floatx4 o = num / den;
-      store_gemm_in4<T, Q8>(p, attn, gm, jh * D + d4 * 4, o, Q8 ? act_inv(p, layer, 1) : 1.0f);
-    }
+    combine_row<T, Q8>(p, layer, attn, b, jh, i, lane, xl);
   }
 }
 
@@ -1919,9 +1965,10 @@ extern template __global__ void k_attn_m<bf16, 256>(VP, int, int);
 
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
-// FUSE: the norms are folded into the GEMMs (ph_gemm), so a layer runs
-// qkv | attention | combine | o | gate/up | down with six device-wide
-// barriers instead of eight (bf16 pi0.5 experts).
+// FUSE: the norms are folded into the GEMMs (ph_gemm) and the key-split
+// merge into the attention phase (ph_attn), so a layer runs
+// qkv | attention | o | gate/up | down with five device-wide barriers
+// instead of eight (bf16 pi0.5 experts).
 template <typename T, int D, int WF, bool FUSE = false>
 __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
@@ -1965,10 +2012,12 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       {
         APre<T, D> apre;
         if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre, xla})) return;
-        ph_attn<T, D, true>(p, k, l, wg, nwg, apre, xla);
+        if (!ph_attn<T, D, true, FUSE>(p, k, l, wg, nwg, apre, xla)) return;
       }
-      VFM_BAR();
-      ph_combine<T, WF>(p, k, l, wg, nwg, xla);
+      if (!FUSE) {
+        VFM_BAR();
+        ph_combine<T, WF>(p, k, l, wg, nwg, xla);
+      }
       VFM_BAR_PF(G_O, l);
       ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre, xl);
       if (!FUSE) {
@@ -2006,7 +2055,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         for (int c = 0; c < no; ++c) __hip_atomic_store(&p.fcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int c = 0; c < nd; ++c) __hip_atomic_store(&p.fcnt[FCNT_MAX + c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if constexpr (FUSE) __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (FUSE) {
+        __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < p.B * p.Hq; ++c)
+          __hip_atomic_store(&p.hcnt[c * HCNT_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __hip_atomic_store(&p.bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
