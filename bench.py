@@ -249,7 +249,7 @@ def phase_breakdown(t, nb, N, L, fused, pi0):
     release to this arrival, wait from arrival to release."""
     if pi0 or L < 3:
         return None
-    names = (["qkv", "attn", "o", "gu", "down"] if fused
+    names = (["qkv_attn", "o", "gu", "down"] if fused
              else ["rn_attn", "qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"])
     per_step = len(names) * L + 1 if fused else 8 * L
     # barrier index i ends the phase that ran before it; the first layer-l

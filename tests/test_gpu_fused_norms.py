@@ -64,7 +64,7 @@ def test_pi05_b1_fused_matches_oracle_and_unfused():
     plain, pp = _run(cfg, params, pk, pv, noise, state, False)
     L, N = cfg.num_layers, cfg.num_steps
     assert pf["fused_norms"] and not pp["fused_norms"]
-    assert pf["barriers"] == 1 + N * (5 * L + 1) and pp["barriers"] == 1 + N * 8 * L
+    assert pf["barriers"] == 1 + N * (4 * L + 1) and pp["barriers"] == 1 + N * 8 * L
     assert pf["o_splits"] > 1 and pf["down_splits"] > 1   # the last-arriver epilogue runs
     gu.assert_parity(fused, ref, noise, 2e-3, 5e-3, 1e-2, "fused")
     gu.assert_parity(plain, ref, noise, 2e-3, 5e-3, 1e-2, "unfused")
@@ -151,7 +151,7 @@ def test_fused_plain_launch_and_trace():
     t = ex.export("trace", (words,))[: 2 * (N * (8 * L + 1) + 4)].reshape(-1, 2)
     ex.close()
     nb = plan["barriers"]
-    assert nb == 1 + N * (5 * L + 1)
+    assert nb == 1 + N * (4 * L + 1)
     stamps = t[1:nb + 1].ravel()
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
 

@@ -84,9 +84,11 @@ struct VP {
   int xl;                  // 1: the o / down split units of a column group share an XCD (see ph_gemm)
   unsigned* xcnt;          // their XCD-local arrival counters, [2][FCNT_MAX] at XCNT_STRIDE words
   unsigned* hcnt;          // attention heads' arrival counters, [HCNT_MAX] at HCNT_STRIDE words; zero between launches
+  unsigned* qcnt;          // qkv tiles stored per query head [QCNT_KV] and per key / value head [QCNT_KV], same stride
 };
 constexpr int HCNT_MAX = 1024;   // samples x query heads the folded attention merge takes
 constexpr int HCNT_STRIDE = 32;
+constexpr int QCNT_KV = 64;      // query heads the folded kernel takes (the kv counters follow)
 constexpr int FCNT_MAX = 4096;   // counters per split GEMM: 16-column tile groups x 64-row tiles
 constexpr int XCNT_STRIDE = 32;  // one 128-byte line per XCD-local counter
 constexpr int XCNT_WORDS = 2 * FCNT_MAX * XCNT_STRIDE;

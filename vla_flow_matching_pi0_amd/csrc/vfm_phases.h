@@ -976,6 +976,18 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
         }
       }
     }
+    if constexpr (FUSE && WHICH == G_QKV) {
+      // the folded-norm kernel has no barrier between qkv and attention:
+      // once its outputs are stored, the unit adds its tiles to the counter
+      // of their head (q), or of their key / value head (k and v share one)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const int head = (t0 * 16) / p.d;   // the nt tiles of a unit lie in one head
+        const int ci = head < p.Hq ? head : QCNT_KV + (head - p.Hq) % p.Hkv;
+        __hip_atomic_fetch_add(&p.qcnt[ci * HCNT_STRIDE], (unsigned)nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
   if constexpr (CAL) {
     // calibration: the largest |activation| this workgroup loaded, per GEMM input
@@ -1155,6 +1167,17 @@ __device__ __forceinline__ bool ph_attn(const VP&, int step, int layer, int wg, 
     const int kvh = jh / group;
     int s0, s1;
     attn_split(p, c, s0, s1);
+    if constexpr (MERGE) {
+      // no barrier after qkv: wait for this head's query tiles (every
+      // 64-row tile), and for a split of the chunk's own keys also for its
+      // key / value head's tiles
+      const unsigned inst = (unsigned)(step * p.L + layer + 1), mtl = (unsigned)((p.M + 63) / 64);
+      if (!counter_wait(&p.qcnt[jh * HCNT_STRIDE], inst * (unsigned)(D / 16) * mtl, p.bar, p.spin_limit, p.herr))
+        return false;
+      if (s1 > P && !counter_wait(&p.qcnt[(QCNT_KV + kvh) * HCNT_STRIDE], inst * (unsigned)(2 * D / 16) * mtl, p.bar,
+                                  p.spin_limit, p.herr))
+        return false;
+    }
     const int qrow = wv * 16 + c16;
     const bool active = wv * 16 < H;
     // query fragments (B operand of S^T): Q[qrow][kb*KB + g*E .. +E]; the
@@ -1965,10 +1988,11 @@ extern template __global__ void k_attn_m<bf16, 256>(VP, int, int);
 
 // ============================================================ kernels
 // Persistent: the whole loop in one cooperative launch.
-// FUSE: the norms are folded into the GEMMs (ph_gemm) and the key-split
-// merge into the attention phase (ph_attn), so a layer runs
-// qkv | attention | o | gate/up | down with five device-wide barriers
-// instead of eight (bf16 pi0.5 experts).
+// FUSE: the norms are folded into the GEMMs (ph_gemm), the key-split merge
+// into the attention phase (ph_attn), and attention waits for its heads'
+// qkv tiles through counters, so a layer runs qkv + attention | o |
+// gate/up | down with four device-wide barriers instead of eight (bf16
+// pi0.5 experts).
 template <typename T, int D, int WF, bool FUSE = false>
 __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   unsigned epoch = 0;
@@ -2011,7 +2035,12 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       ph_gemm<T, G_QKV, true, WF, false, FUSE>(p, k, l, wg, nwg, pre);
       {
         APre<T, D> apre;
-        if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre, xla})) return;
+        if constexpr (FUSE) {
+          // dependency-scoped: attention units wait for their heads' qkv tiles
+          AttnPrefetchHook<T, D>{p, l, wg, apre, xla}();
+        } else {
+          if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre, xla})) return;
+        }
         if (!ph_attn<T, D, true, FUSE>(p, k, l, wg, nwg, apre, xla)) return;
       }
       if (!FUSE) {
@@ -2059,6 +2088,8 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int c = 0; c < p.B * p.Hq; ++c)
           __hip_atomic_store(&p.hcnt[c * HCNT_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < 2 * QCNT_KV; ++c)
+          __hip_atomic_store(&p.qcnt[c * HCNT_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __hip_atomic_store(&p.bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

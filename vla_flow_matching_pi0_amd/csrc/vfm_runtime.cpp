@@ -423,7 +423,7 @@ vfm_status check_host_err(vfm_expert* x, hipStream_t s) {
   (void)vfm::zero_words(x->bar, vfm::BAR_WORDS, s);
   if (x->fcnt) (void)vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s);
   if (x->xcnt) (void)vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s);
-  if (x->hcnt) (void)vfm::zero_words(x->hcnt, vfm::HCNT_MAX * vfm::HCNT_STRIDE, s);
+  if (x->hcnt) (void)vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s);
   x->xl_plan = -1;
   (void)hipStreamSynchronize(s);
   return fail(VFM_E_HIP, "a device-wide phase barrier timed out in an earlier denoise call");
@@ -655,7 +655,8 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   if (mode == 0 && x->can_fuse && x->fuse_norms) {
     const long mt = (p.M + 63) / 64;
     const long go = (long)p.W / (16 * p.gp_nt[1]) * mt, gd = (long)p.W / (16 * p.gp_nt[3]) * mt;
-    if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX && (long)B * p.Hq <= vfm::HCNT_MAX) {
+    if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX && (long)B * p.Hq <= vfm::HCNT_MAX && p.Hq <= vfm::QCNT_KV &&
+        p.Hkv <= vfm::QCNT_KV && p.d % (16 * p.gp_nt[0]) == 0) {
       p.fuse = 1;
       p.shw_q = x->shw_q; p.shw_g = x->shw_g; p.off_ssa = x->off_ssa; p.off_ssm = x->off_ssm; p.fcnt = x->fcnt;
       // XCD-local split sums: every unit of a column group on one XCD (the
@@ -668,6 +669,7 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
              pow2(p.gp_s[3]) ? (x->xcd_attn ? 3 : 1) : 0;
       p.xcnt = x->xcnt;
       p.hcnt = x->hcnt;
+      p.qcnt = x->hcnt + (size_t)vfm::HCNT_MAX * vfm::HCNT_STRIDE;
     }
   }
   p.qs = x->qs;
@@ -954,14 +956,14 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->shw_g = (float*)x->dalloc((size_t)x->N * L * 2 * F * 4);
     x->fcnt = (unsigned*)x->dalloc((size_t)2 * vfm::FCNT_MAX * 4);
     x->xcnt = (unsigned*)x->dalloc((size_t)vfm::XCNT_WORDS * 4);
-    x->hcnt = (unsigned*)x->dalloc((size_t)vfm::HCNT_MAX * vfm::HCNT_STRIDE * 4);
+    x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
     if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt || !x->hcnt) {
       fail(VFM_E_OOM, "workspace allocation failed");
       return bail(VFM_E_OOM);
     }
     if (vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s) != hipSuccess ||
         vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s) != hipSuccess ||
-        vfm::zero_words(x->hcnt, vfm::HCNT_MAX * vfm::HCNT_STRIDE, s) != hipSuccess ||
+        vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess ||
         vfm::sk::shift_proj(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, s) != hipSuccess ||
         vfm::sk::shift_proj(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, s) != hipSuccess) {
       fail(VFM_E_HIP, "shift projection tables");
@@ -1380,7 +1382,7 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     if (st != VFM_OK) return st;
     int32_t* o = static_cast<int32_t*>(dst);
     o[0] = p.fuse;
-    o[1] = p.fuse ? 1 + x->N * (5 * x->L + 1) : 1 + x->N * (8 * x->L + 2 * x->pi0);
+    o[1] = p.fuse ? 1 + x->N * (4 * x->L + 1) : 1 + x->N * (8 * x->L + 2 * x->pi0);
     o[2] = p.S_o;
     o[3] = p.S_down;
     o[4] = p.fuse ? p.xl : 0;
