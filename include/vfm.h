@@ -195,7 +195,9 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       reports VFM_E_HIP. Used where a tool cannot follow cooperative
  *       launches (kernel profilers).
  *   "fused_norms": "1" (default where it applies) or "0": the persistent
- *       kernel of a bf16 pi0.5 expert (width a multiple of 256, at most 1024)
+ *       kernel of a pi0.5 expert with bf16, W4A16 or W8A16 weights (width a
+ *       multiple of 256, at most 1024; the shift W table is built from the
+ *       weights the GEMMs multiply by)
  *       folds the adaptive RMSNorms into the GEMMs next to them (the
  *       residual + norm fusion of the FlashRT walk-through, component 8):
  *       the o and down projections finish the gated residual in the

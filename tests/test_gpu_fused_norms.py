@@ -203,3 +203,24 @@ def test_xcd_local_option_is_validated():
     assert e.value.name == "VFM_E_INVALID_ARG"
     ex.set_option("xcd_local", "0")
     ex.close()
+
+
+@pytest.mark.parametrize("prec", ["w4a16", "w8a16"])
+def test_weight_only_quantised_fused_matches_oracle_and_unfused(prec):
+    """Weight-only quantised experts (bf16 activations) take the folded-norm
+    kernel too, with shift W tables built from the weights the GEMMs
+    multiply by (bf16 (q s) for int4, codes times column scales for int8):
+    against the oracle on the dequantised expert and against the same
+    expert with separate norm phases."""
+    from oracle import quant as Q
+    gu = _gu()
+    cfg = CONFIGS["pi05_" + prec].replace(num_layers=4)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    deq, _ = Q.dequantised_expert(params, cfg)
+    ref = O.denoise(deq, noise, state, pk, pv, cfg)
+    print(f"case {prec} (4 layers) fused / unfused", flush=True)
+    fused, pf = _run(cfg, params, pk, pv, noise, state, True, repeats=2)
+    plain, pp = _run(cfg, params, pk, pv, noise, state, False)
+    assert pf["fused_norms"] and not pp["fused_norms"]
+    gu.assert_parity(fused, ref, noise, 2e-3, 5e-3, 1e-2, f"{prec} fused")
+    gu.assert_parity(fused, plain, noise, 2e-3, 5e-3, 1e-2, f"{prec} fused vs unfused")

@@ -245,6 +245,11 @@ enum { WF_NATIVE = 0, WF_FP8 = 1, WF_W4 = 2, WF_I8 = 3, WF_W4A8 = 4 };
 template <int WF> struct WFmt { static constexpr int R = WF == WF_NATIVE ? 1 : (WF == WF_W4 || WF == WF_W4A8) ? 4 : 2; };
 // GEMM inputs stored as e4m3 with the calibrated activation scale.
 template <int WF> constexpr bool act_fp8() { return WF == WF_FP8 || WF == WF_W4A8; }
+// Kernel sets with a folded-norm persistent kernel: bf16 activations, and
+// bf16, int4-with-group-scales or int8-with-column-scales weights.
+template <typename T, int WF> constexpr bool fusable() {
+  return sizeof(T) == 2 && (WF == WF_NATIVE || WF == WF_W4 || WF == WF_I8);
+}
 
 // Residual + adaRMSNorm between sublayers: gate_ni is the norm whose gate
 // scales the partial sums, ni the norm applied.
@@ -655,7 +660,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KM = MT<T>::KB, R = WFmt<WF>::R, KW = KM * R, PW = GEMM_PASS / R;
   static_assert(WF == WF_NATIVE || sizeof(T) == 2, "quantised weights run with bf16 activations");
-  static_assert(!FUSE || (WF == WF_NATIVE && sizeof(T) == 2 && !CAL), "folded norms: bf16 weights and activations");
+  static_assert(!FUSE || (fusable<T, WF>() && !CAL), "folded norms: bf16 activations, bf16 / W4 / W8 weights");
   constexpr bool FIN = FUSE && (WHICH == G_QKV || WHICH == G_GU);    // applies r and the shift
   constexpr bool FOUT = FUSE && (WHICH == G_O || WHICH == G_DOWN);   // finishes the residual
   const bool fout = FOUT && (WHICH == G_O || layer + 1 < p.L);
@@ -2187,7 +2192,7 @@ hipError_t launch_one(const VP& p, int mode, int phase, int k, int l, int grid, 
       void* args[] = {const_cast<VP*>(&p)};
       const void* f = reinterpret_cast<const void*>(&k_persistent<T, D, WF>);
       if (p.fuse) {
-        if constexpr (sizeof(T) == 2 && WF == WF_NATIVE) f = reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>);
+        if constexpr (fusable<T, WF>()) f = reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>);
         else return hipErrorInvalidValue;
       }
       if (mode == 0) return hipLaunchCooperativeKernel(f, dim3(grid), dim3(NTH), args, (unsigned)lds, st);
@@ -2228,7 +2233,7 @@ hipError_t set_lds_limit(int bytes) {
   if constexpr (!CAL)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if constexpr (!CAL && sizeof(T) == 2 && WF == WF_NATIVE)
+  if constexpr (!CAL && fusable<T, WF>())
     if (e == hipSuccess)
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_persistent<T, D, WF, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -2253,7 +2258,7 @@ hipError_t occupancy(size_t lds, int* per_cu) {
   } else {
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         per_cu, reinterpret_cast<const void*>(&k_persistent<T, D, WF>), NTH, lds);
-    if constexpr (sizeof(T) == 2 && WF == WF_NATIVE) {
+    if constexpr (fusable<T, WF>()) {
       // the grid must fit with either kernel resident
       int fused = 0;
       if (e == hipSuccess)

@@ -251,9 +251,24 @@ vfm_status validate_config(const vfm_config* c) {
 // Whether the persistent kernel can fold the norms into its GEMMs: bf16
 // pi0.5 experts whose width is a multiple of 256 up to 1024 (a GEMM lane
 // reads at most 16 per-tile sums of squares of a row).
+// The folded norms' shift W tables over the weights the GEMMs multiply by
+// (bf16, dequantised int4, or int8 codes times their column scales).
+hipError_t shift_tables(vfm_expert* x, int L, int W, int Nq, int F, int n_norms, hipStream_t s) {
+  if (x->kset == vfm::KS_BF16) {
+    hipError_t e = vfm::sk::shift_proj(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, s);
+    if (e == hipSuccess) e = vfm::sk::shift_proj(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, s);
+    return e;
+  }
+  const int fmt = x->kset == vfm::KS_W4 ? 1 : 2;
+  hipError_t e = vfm::sk::shift_proj_q(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, fmt, s);
+  if (e == hipSuccess) e = vfm::sk::shift_proj_q(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, fmt, s);
+  return e;
+}
+
 bool can_fold_norms(const vfm_config* c) {
-  return c->weight_precision == VFM_W_BF16 && c->variant != VFM_VARIANT_PI0 && c->num_layers > 0 &&
-         c->width % 256 == 0 && c->width <= 1024;
+  const int w = c->weight_precision;
+  return (w == VFM_W_BF16 || w == VFM_W_W4A16 || w == VFM_W_W8A16) && c->variant != VFM_VARIANT_PI0 &&
+         c->num_layers > 0 && c->width % 256 == 0 && c->width <= 1024;
 }
 
 // The kernels address every buffer through 32-bit byte offsets from its
@@ -964,8 +979,7 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     if (vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s) != hipSuccess ||
         vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s) != hipSuccess ||
         vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess ||
-        vfm::sk::shift_proj(x->shw_q, x->w_qkv.data(), L, W, Nq, x->mod, n_norms, 0, W, x->N, s) != hipSuccess ||
-        vfm::sk::shift_proj(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, s) != hipSuccess) {
+        shift_tables(x, L, W, Nq, F, n_norms, s) != hipSuccess) {
       fail(VFM_E_HIP, "shift projection tables");
       return bail(VFM_E_HIP);
     }
@@ -1092,7 +1106,7 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     // default where it applies) or with separate norm phases (0)
     if (v == "1") {
       if (!x->can_fuse)
-        return fail(VFM_E_UNSUPPORTED, "fused_norms applies to bf16 pi0.5 experts with a width that is a multiple of 256 up to 1024");
+        return fail(VFM_E_UNSUPPORTED, "fused_norms applies to pi0.5 experts with bf16, W4A16 or W8A16 weights and a width that is a multiple of 256 up to 1024");
       x->fuse_norms = true;
     } else if (v == "0") {
       x->fuse_norms = false;

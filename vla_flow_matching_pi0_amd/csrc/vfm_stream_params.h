@@ -91,6 +91,9 @@ hipError_t stream_occupancy(int d, size_t lds, int* per_cu);
 // weight W_l (K x Npk), for every step k; norm = 2 l + which (0: attention, 1: MLP)
 hipError_t shift_proj(float* out, const uint8_t* const* packed, int L, int K, int Npk, const float* mod, int n_norms,
                       int which, int W, int N, hipStream_t st);
+// ... over quantised weights: fmt 1 W4A16, 2 W8A16 (vfm_k_stream.hip)
+hipError_t shift_proj_q(float* out, const uint8_t* const* packed, int L, int K, int Npk, const float* mod, int n_norms,
+                        int which, int W, int N, int fmt, hipStream_t st);
 
 }  // namespace sk
 }  // namespace vfm
