@@ -204,7 +204,10 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       epilogue of the last K split of each column group to arrive and
  *       write y = h (1 + scale) of the next norm with per-16-column sums of
  *       squares; qkv and gate/up apply r = 1 / sqrt(mean(h^2) + eps) and a
- *       create-time shift W table: six device-wide barriers per layer
+ *       create-time shift W table. The same kernel merges the attention key
+ *       splits inside the attention phase (per-head arrival counters) and
+ *       starts each attention unit once its head's qkv tiles are stored
+ *       (per-head tile counters): four device-wide barriers per layer
  *       instead of eight. Results agree with "0" to bf16 rounding of the
  *       GEMM inputs. VFM_E_UNSUPPORTED for "1" on other experts.
  *   "xcd_local": "1" (default) or "0": with folded norms, the K-split
