@@ -1346,6 +1346,38 @@ __device__ __forceinline__ void combine_row(const VP& p, int layer, uint8_t* att
   const int D = p.d, KS = p.KS;
   const int gm = b * p.H + i;
   const size_t base0 = ((size_t)(b * p.Hq + jh) * KS) * 64 + i;
+  if constexpr (sizeof(T) == 2) {
+    if (D <= 256 && KS <= 16) {
+      // one round trip: each lane's four dims of every split are requested
+      // together with the splits' (max, sum) pairs
+      const auto opr = rsrc(p.opart);
+      const int d4 = lane;
+      u32x2 ov[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t oo = (uint32_t)(((base0 + (size_t)j * 64) * D + d4 * 4) * 2);
+        const bool ok = j < KS && d4 < D / 4;
+        ov[j] = xl ? ld8_if(opr, oo, ok) : coh_ld8_if(opr, oo, ok);
+      }
+      const uint32_t mo = (uint32_t)((base0 + (size_t)lane * 64) * 8);
+      const floatx2 ml = __builtin_bit_cast(floatx2, xl ? ld8_if(rsrc(p.ml), mo, lane < KS) : coh_ld8_if(rsrc(p.ml), mo, lane < KS));
+      const float mc = lane < KS ? ml[0] : -INFINITY, lc = lane < KS ? ml[1] : 0.f;
+      float mx = mc;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float wc = lane < KS ? fast_exp2(mc - mx) : 0.f;
+      const float den = warp_sum(wc * lc);
+      floatx4 num = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const floatx4 f = {__builtin_bit_cast(float, ov[j][0] << 16), __builtin_bit_cast(float, ov[j][0] & 0xffff0000u),
+                           __builtin_bit_cast(float, ov[j][1] << 16), __builtin_bit_cast(float, ov[j][1] & 0xffff0000u)};
+        num += __shfl(wc, j) * f;
+      }
+      if (d4 < D / 4) store_gemm_in4<T, Q8>(p, attn, gm, jh * D + d4 * 4, num / den, Q8 ? act_inv(p, layer, 1) : 1.0f);
+      return;
+    }
+  }
   float mc = -INFINITY, lc = 0.f;
   if (lane < KS) {
     const uint32_t mo = (uint32_t)((base0 + (size_t)lane * 64) * 8);
