@@ -243,15 +243,16 @@ def cpu_baseline(cfg, params, pk, pv, noise, state, steps: int, min_seconds: flo
                                         f"{one_dt:.1f} s measured"}}
 
 
-def phase_breakdown(t, nb, N, L, fused, pi0):
+def phase_breakdown(t, nb, N, L, fused, pi0, merged=True):
     """Mean (work, wait) in microseconds of each phase of a middle layer, from
     workgroup 0's (arrive, release) stamps: work runs from the previous
     release to this arrival, wait from arrival to release."""
     if pi0 or L < 3:
         return None
     names = (["qkv_attn", "o", "gu", "down"] if fused
+             else ["rn_attn", "qkv_attn", "o", "rn_mlp", "gu", "down"] if merged
              else ["rn_attn", "qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"])
-    per_step = len(names) * L + 1 if fused else 8 * L
+    per_step = len(names) * L + 1 if fused else len(names) * L
     # barrier index i ends the phase that ran before it; the first layer-l
     # phase of step k (k >= 0) follows barrier 1 + k * per_step + (l * len(names) - (0 if fused else 1))
     out = {n: [0.0, 0.0] for n in names}
@@ -402,7 +403,7 @@ def main() -> int:
         stall = float(np.sum(t[1:nb + 1, 1] - t[1:nb + 1, 0]))
         sync = {"barriers_per_call": nb, "fused_norms": plan["fused_norms"], "stall_us": round(stall, 1),
                 "span_us": round(float(span), 1), "stall_frac": round(stall / span, 4) if span > 0 else None,
-                "per_layer_us": phase_breakdown(t, nb, N, L, plan["fused_norms"], pi0)}
+                "per_layer_us": phase_breakdown(t, nb, N, L, plan["fused_norms"], pi0, plan["attn_merge"])}
     elif args.mode == "stream":
         # (arrive, counters complete, workgroup ready) per barrier: the stall is
         # arrival to ready (the device-wide wait plus any wait for weights)

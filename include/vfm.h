@@ -210,6 +210,14 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       (per-head tile counters): four device-wide barriers per layer
  *       instead of eight. Results agree with "0" to bf16 rounding of the
  *       GEMM inputs. VFM_E_UNSUPPORTED for "1" on other experts.
+ *   "attn_merge": "1" (default) or "0": every persistent kernel merges
+ *       the attention key splits inside the attention phase (per-head
+ *       arrival counters, one 128-byte line each) and starts each attention
+ *       unit once its head's qkv tiles are stored (per-head tile counters),
+ *       so the barriers after qkv and after attention go; "0" runs a combine
+ *       phase between device-wide barriers instead (and, since the
+ *       folded-norm kernel needs the in-place merge, separate norm phases).
+ *       Results are bitwise the same with separate norm phases.
  *   "xcd_local": "1" (default) or "0": with folded norms, the K-split
  *       units of one o / down column group all run on one XCD (unit index
  *       mod 8, checked at kernel start from the hardware XCD id; a launch
@@ -261,10 +269,12 @@ vfm_status vfm_set_act_scales(vfm_expert* ex, const float* scales, int32_t n);
  *   "weight_scales" (FP8), "act_scales" (FP8, W4A8): [L][4] per-GEMM scales
  *      (qkv, o, gate/up, down); act_scales needs a calibration first;
  *   "trace": the phase timeline of the last persistent call (option "trace");
- *   "persistent_plan": 5 int32 (not float32): whether the persistent kernel
+ *   "persistent_plan": 6 int32 (not float32): whether the persistent kernel
  *      runs with folded norms (0 / 1), its device-wide barriers per call,
- *      the K splits of the o and down projections, and whether their split
+ *      the K splits of the o and down projections, whether their split
  *      sums are exchanged through one XCD's L2 (0 / 1; option "xcd_local"),
+ *      and whether the attention splits are merged in place (0 / 1; option
+ *      "attn_merge"),
  *      at the bound batch and prefix; VFM_E_UNBOUND without prefix_k,
  *      VFM_E_STATE when the expert would not run the persistent kernel there.
  * Synchronous. Errors: VFM_E_INVALID_ARG (unknown name), VFM_E_SHAPE,

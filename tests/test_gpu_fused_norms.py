@@ -64,7 +64,7 @@ def test_pi05_b1_fused_matches_oracle_and_unfused():
     plain, pp = _run(cfg, params, pk, pv, noise, state, False)
     L, N = cfg.num_layers, cfg.num_steps
     assert pf["fused_norms"] and not pp["fused_norms"]
-    assert pf["barriers"] == 1 + N * (4 * L + 1) and pp["barriers"] == 1 + N * 8 * L
+    assert pf["barriers"] == 1 + N * (4 * L + 1) and pp["barriers"] == 1 + N * 6 * L
     assert pf["o_splits"] > 1 and pf["down_splits"] > 1   # the last-arriver epilogue runs
     gu.assert_parity(fused, ref, noise, 2e-3, 5e-3, 1e-2, "fused")
     gu.assert_parity(plain, ref, noise, 2e-3, 5e-3, 1e-2, "unfused")
@@ -224,3 +224,41 @@ def test_weight_only_quantised_fused_matches_oracle_and_unfused(prec):
     assert pf["fused_norms"] and not pp["fused_norms"]
     gu.assert_parity(fused, ref, noise, 2e-3, 5e-3, 1e-2, f"{prec} fused")
     gu.assert_parity(fused, plain, noise, 2e-3, 5e-3, 1e-2, f"{prec} fused vs unfused")
+
+
+@pytest.mark.parametrize("cfgname", ["pi05_bf16_b1", "pi0_tiny_fp32"])
+def test_attn_merge_option_matches_combine_phase(cfgname):
+    """The persistent kernel's in-place attention merge (default) against the
+    combine phase between device-wide barriers (option attn_merge 0, which
+    also selects separate norm phases): the same split outputs merged in the
+    same order, so the actions agree to the folded-norm bound (bitwise where
+    the norms are separate in both)."""
+    gu = _gu()
+    cfg = CONFIGS[cfgname]
+    if cfgname == "pi05_bf16_b1":
+        cfg = cfg.replace(num_layers=3, num_steps=3)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    outs, plans = {}, {}
+    for merge in ("1", "0"):
+        for fused in ("1", "0"):
+            if fused == "1" and (merge == "0" or cfgname != "pi05_bf16_b1"):
+                continue
+            print(f"case {cfgname} attn_merge={merge} fused_norms={fused}", flush=True)
+            ex = gu.build_expert(cfg, params, "persistent")
+            if cfgname == "pi05_bf16_b1":
+                ex.set_option("fused_norms", fused)
+            ex.set_option("attn_merge", merge)
+            bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+            plans[(merge, fused)] = ex.persistent_plan()
+            for _ in range(2):
+                ex.denoise()
+            ex.check()
+            torch.cuda.synchronize()
+            outs[(merge, fused)] = bufs["actions"].cpu().numpy()
+            ex.close()
+    assert plans[("1", "0")]["attn_merge"] and not plans[("0", "0")]["attn_merge"]
+    assert not plans[("0", "0")]["fused_norms"]
+    assert np.array_equal(outs[("1", "0")], outs[("0", "0")])
+    if ("1", "1") in outs:
+        assert plans[("1", "1")]["fused_norms"]
+        gu.assert_parity(outs[("1", "1")], outs[("0", "0")], noise, 2e-3, 5e-3, 1e-2, "merged fused vs combine")

@@ -240,6 +240,7 @@ def test_plain_persistent_launch_and_trace():
     ex.set_option("persistent_launch", "plain")
     ex.set_option("trace", "1")
     bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+    plan = ex.persistent_plan()
     ex.denoise()
     ex.check()
     torch.cuda.synchronize()
@@ -248,7 +249,11 @@ def test_plain_persistent_launch_and_trace():
     words = 2 * (N * (8 * L + 1) + 4)
     t = ex.export("trace", (words,)).reshape(-1, 2)
     ex.close()
-    n_bar = 1 + N * 8 * L           # one after the first boundary, then 8 per layer (the last one at the step boundary)
+    # one after the first boundary, then 6 per layer with the in-place attention
+    # merge (8 with a combine phase; the last one at the step boundary)
+    assert plan["attn_merge"]
+    n_bar = plan["barriers"]
+    assert n_bar == 1 + N * 6 * L
     stamps = t[1:n_bar + 1].ravel()
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
 

@@ -73,19 +73,21 @@ def test_pi0_bf16_b1_matches_oracle(mode):
 def test_pi0_state_changes_the_actions_and_the_trace_has_two_more_barriers_per_step():
     """The state reaches the actions only through the state token (so a
     different state gives other actions, matching the oracle), and the
-    persistent kernel runs 8 barriers per layer plus 3 per step."""
+    persistent kernel runs 6 barriers per layer (the attention merge in place) plus 3 per step."""
     gu = _gu()
     cfg = CONFIGS["pi0_tiny_fp32"].replace(num_steps=3)
     params, pk, pv, noise, state = make_inputs(cfg)
     ex = gu.build_expert(cfg, params, "persistent")
     ex.set_option("trace", "1")
     bufs = gu.bind_inputs(ex, cfg, pk, pv, noise, state)
+    plan = ex.persistent_plan()
     ex.denoise()
     ex.check()
     a1 = bufs["actions"].cpu().numpy()
     L, N = cfg.num_layers, cfg.num_steps
     t = ex.export("trace", (2 * (N * (8 * L + 3) + 4),)).reshape(-1, 2)
-    n_bar = 1 + N * (8 * L + 2)
+    n_bar = plan["barriers"]
+    assert plan["attn_merge"] and n_bar == 1 + N * (6 * L + 2)
     stamps = t[1:n_bar + 1].ravel()
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
     state2 = state + 1.0

@@ -81,7 +81,9 @@ struct VP {
   size_t off_ssa;          // slab offset of [Mpad][W/16] f32: sums of squares of h over each 16 columns, before qkv
   size_t off_ssm;          // ... before gate/up
   unsigned* fcnt;          // arrival counters: [2 (o, down)][FCNT_MAX]; zero between launches
-  int xl;                  // 1: the o / down split units of a column group share an XCD (see ph_gemm)
+  int xl;                  // bit 0: the o / down split units of a column group share an XCD (see ph_gemm);
+                           // bit 1: the attention splits of a head share one (attn_unit)
+  int merge;               // the persistent kernel merges the attention splits in place (see ph_attn)
   unsigned* xcnt;          // their XCD-local arrival counters, [2][FCNT_MAX] at XCNT_STRIDE words
   unsigned* hcnt;          // attention heads' arrival counters, [HCNT_MAX] at HCNT_STRIDE words; zero between launches
   unsigned* qcnt;          // qkv tiles stored per query head [QCNT_KV] and per key / value head [QCNT_KV], same stride

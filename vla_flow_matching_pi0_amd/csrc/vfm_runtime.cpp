@@ -119,6 +119,7 @@ struct vfm_expert {
   // launch failed
   bool xcd_local = true;
   bool xcd_attn = true;                       // ... and the attention splits with their merge
+  bool attn_merge = true;                     // option "attn_merge": the persistent kernels' in-place merge
   unsigned* xcnt = nullptr;                   // [2][FCNT_MAX] counters, XCNT_STRIDE words apart
   unsigned* hcnt = nullptr;                   // [HCNT_MAX] attention head counters, HCNT_STRIDE words apart
   long long xl_plan = -1;
@@ -666,12 +667,19 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
     p.S_o = p.gp_s[1];
     p.S_down = p.gp_s[3];
   }
+  // the persistent kernel's in-place attention merge with counter-scoped
+  // attention start (every persistent kernel whose shapes its counters take)
+  p.merge = mode == 0 && x->attn_merge && (long)B * p.Hq <= vfm::HCNT_MAX && p.Hq <= vfm::QCNT_KV &&
+            p.Hkv <= vfm::QCNT_KV && p.d % (16 * p.gp_nt[0]) == 0 ? 1 : 0;
+  p.hcnt = x->hcnt;
+  p.qcnt = x->hcnt + (size_t)vfm::HCNT_MAX * vfm::HCNT_STRIDE;
+  // attention splits of a head on one XCD, in any persistent launch
+  p.xl = mode == 0 && x->xcd_local && x->xcd_attn && x->coop_grid % 8 == 0 ? 2 : 0;
   p.fuse = 0;
-  if (mode == 0 && x->can_fuse && x->fuse_norms) {
+  if (mode == 0 && x->can_fuse && x->fuse_norms && p.merge) {
     const long mt = (p.M + 63) / 64;
     const long go = (long)p.W / (16 * p.gp_nt[1]) * mt, gd = (long)p.W / (16 * p.gp_nt[3]) * mt;
-    if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX && (long)B * p.Hq <= vfm::HCNT_MAX && p.Hq <= vfm::QCNT_KV &&
-        p.Hkv <= vfm::QCNT_KV && p.d % (16 * p.gp_nt[0]) == 0) {
+    if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX) {
       p.fuse = 1;
       p.shw_q = x->shw_q; p.shw_g = x->shw_g; p.off_ssa = x->off_ssa; p.off_ssm = x->off_ssm; p.fcnt = x->fcnt;
       // XCD-local split sums: every unit of a column group on one XCD (the
@@ -680,11 +688,9 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
       // across a 32-bit wrap)
       const long ngo = (long)p.W / (16 * p.gp_nt[1]), ngd = (long)p.W / (16 * p.gp_nt[3]);
       auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
-      p.xl = x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) &&
-             pow2(p.gp_s[3]) ? (x->xcd_attn ? 3 : 1) : 0;
+      if (x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) && pow2(p.gp_s[3]))
+        p.xl |= 1;
       p.xcnt = x->xcnt;
-      p.hcnt = x->hcnt;
-      p.qcnt = x->hcnt + (size_t)vfm::HCNT_MAX * vfm::HCNT_STRIDE;
     }
   }
   p.qs = x->qs;
@@ -963,6 +969,13 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     if (e == hipSuccess && fp8_act(x)) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
   }
+  // the persistent kernel's attention arrival counters (every expert)
+  x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
+  if (!x->hcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
+  if (vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess) {
+    fail(VFM_E_HIP, "counter clear");
+    return bail(VFM_E_HIP);
+  }
   // norms folded into the persistent kernel's GEMMs: shift W tables (fp64
   // sums over the packed bf16 weights), sums-of-squares rows, split counters
   if (can_fold_norms(cfg)) {
@@ -971,14 +984,12 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->shw_g = (float*)x->dalloc((size_t)x->N * L * 2 * F * 4);
     x->fcnt = (unsigned*)x->dalloc((size_t)2 * vfm::FCNT_MAX * 4);
     x->xcnt = (unsigned*)x->dalloc((size_t)vfm::XCNT_WORDS * 4);
-    x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
-    if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt || !x->hcnt) {
+    if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt) {
       fail(VFM_E_OOM, "workspace allocation failed");
       return bail(VFM_E_OOM);
     }
     if (vfm::zero_words(x->fcnt, 2 * vfm::FCNT_MAX, s) != hipSuccess ||
         vfm::zero_words(x->xcnt, vfm::XCNT_WORDS, s) != hipSuccess ||
-        vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess ||
         shift_tables(x, L, W, Nq, F, n_norms, s) != hipSuccess) {
       fail(VFM_E_HIP, "shift projection tables");
       return bail(VFM_E_HIP);
@@ -1115,6 +1126,16 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     }
     return VFM_OK;
   }
+  if (k == "attn_merge") {
+    // the persistent kernels merge the attention key splits in the attention
+    // phase, whose units start on per-head counters (1, the default), or run
+    // a combine phase between device-wide barriers (0; the folded-norm
+    // kernel needs the in-place merge, so "0" also selects separate norms)
+    if (v == "1") x->attn_merge = true;
+    else if (v == "0") x->attn_merge = false;
+    else return fail(VFM_E_INVALID_ARG, "attn_merge must be 0 or 1");
+    return VFM_OK;
+  }
   if (k == "xcd_local") {
     // the fused kernel's o / down split sums through one XCD's L2 (1, the
     // default where the plan allows it) or through the device coherence point (0)
@@ -1202,7 +1223,7 @@ vfm_status vfm_denoise(vfm_expert* x, const float* noise, const float* state, fl
   if (mode == 0) {
     // one launch per call: the kernel's last workgroup clears the arrival
     // counters, and a failure raises the host-mapped word read by the checks
-    if (p.xl) {
+    if (p.xl & 1) {
       const int mt = (p.M + 63) / 64;
       const long long plan = (((long long)p.gp_s[1] * 64 + p.gp_s[3]) * 4096 + (long long)(p.W / (16 * p.gp_nt[1])) * mt) *
                                  4096 + (long long)(p.W / (16 * p.gp_nt[3])) * mt;
@@ -1385,9 +1406,9 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
   }
   if (n == "persistent_plan") {
     // int32 [fused norms (0 / 1), device-wide barriers per call, o splits,
-    // down splits, XCD-local split sums (0 / 1)] of the persistent kernel at
-    // the bound batch and prefix
-    if (bytes != 5 * 4) return fail(VFM_E_SHAPE, "'persistent_plan' needs 20 bytes");
+    // down splits, XCD-local split sums (0 / 1), in-place attention merge
+    // (0 / 1)] of the persistent kernel at the bound batch and prefix
+    if (bytes != 6 * 4) return fail(VFM_E_SHAPE, "'persistent_plan' needs 24 bytes");
     if (!x->prefix_k.bound) return fail(VFM_E_UNBOUND, "buffer 'prefix_k' is not bound");
     const int B = (int)x->prefix_k.shape[1], P = (int)x->prefix_k.shape[2];
     if (launch_mode_of(x, B, P) != 0) return fail(VFM_E_STATE, "the expert does not run the persistent kernel");
@@ -1396,10 +1417,11 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     if (st != VFM_OK) return st;
     int32_t* o = static_cast<int32_t*>(dst);
     o[0] = p.fuse;
-    o[1] = p.fuse ? 1 + x->N * (4 * x->L + 1) : 1 + x->N * (8 * x->L + 2 * x->pi0);
+    o[1] = p.fuse ? 1 + x->N * (4 * x->L + 1) : 1 + x->N * ((p.merge ? 6 : 8) * x->L + 2 * x->pi0);
     o[2] = p.S_o;
     o[3] = p.S_down;
-    o[4] = p.fuse ? p.xl : 0;
+    o[4] = p.fuse ? (p.xl & 1) : 0;
+    o[5] = p.merge;
     return VFM_OK;
   }
   if (n == "trace") {

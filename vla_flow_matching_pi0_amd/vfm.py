@@ -219,10 +219,10 @@ class Expert:
 
     def persistent_plan(self) -> dict:
         """The persistent kernel's plan at the bound batch and prefix (vfm_export "persistent_plan")."""
-        out = np.empty(5, dtype=np.int32)
+        out = np.empty(6, dtype=np.int32)
         _check(_lib.vfm_export(self._h, b"persistent_plan", out.ctypes.data, out.nbytes))
         return {"fused_norms": bool(out[0]), "barriers": int(out[1]), "o_splits": int(out[2]), "down_splits": int(out[3]),
-                "xcd_local": bool(out[4])}
+                "xcd_local": bool(out[4]), "attn_merge": bool(out[5])}
 
     def stream_debug(self, name: str, index: int = 0, nbytes: int = 0) -> np.ndarray:
         """Raw bytes of an internal buffer of the streaming kernel (diagnostics; see vfm_stream_debug)."""
