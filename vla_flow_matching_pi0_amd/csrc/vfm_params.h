@@ -82,12 +82,14 @@ struct VP {
   size_t off_ssm;          // ... before gate/up
   unsigned* fcnt;          // arrival counters: [2 (o, down)][FCNT_MAX]; zero between launches
   int xl;                  // bit 0: the o / down split units of a column group share an XCD (see ph_gemm);
-                           // bit 1: the attention splits of a head share one (attn_unit)
-  int merge;               // the persistent kernel merges the attention splits in place (see ph_attn)
+                           // bit 1: the attention splits of a head share one (attn_unit);
+                           // XL_MERGE: the separate-norm persistent kernel merges the attention splits in
+                           // place (see ph_attn; the folded-norm kernel always does)
   unsigned* xcnt;          // their XCD-local arrival counters, [2][FCNT_MAX] at XCNT_STRIDE words
   unsigned* hcnt;          // attention heads' arrival counters, [HCNT_MAX] at HCNT_STRIDE words; zero between launches
   unsigned* qcnt;          // qkv tiles stored per query head [QCNT_KV] and per key / value head [QCNT_KV], same stride
 };
+constexpr int XL_MERGE = 4;
 constexpr int HCNT_MAX = 1024;   // samples x query heads the folded attention merge takes
 constexpr int HCNT_STRIDE = 32;
 constexpr int QCNT_KV = 64;      // query heads the folded kernel takes (the kv counters follow)

@@ -981,7 +981,7 @@ __device__ __forceinline__ void ph_gemm(const VP&, int step, int layer, int wg, 
         }
       }
     }
-    if (WHICH == G_QKV && arrive) {
+    if (WHICH == G_QKV && (FUSE || arrive)) {
       // no barrier between qkv and attention (the persistent kernel's merged
       // attention): once its outputs are stored, the unit adds its tiles to
       // the counter of their head (q), or of their key / value head (k and v
@@ -1132,7 +1132,7 @@ __device__ __forceinline__ void combine_row(const VP& p, int layer, uint8_t* att
 
 // xl: XCD-ordered units (attn_unit) whose split outputs stay in the XCD's
 // L2 (write-back stores) for the XCD-local merge.
-// merge (the persistent kernel): the key splits of a head are merged in
+// MERGE (the persistent kernel): the key splits of a head are merged in
 // this phase instead of a combine phase behind a device-wide barrier, and
 // each unit starts once its head's qkv tiles are stored (counters instead of
 // the barrier after qkv). Each unit, once its split output is stored, adds 1 to its head's
@@ -1142,9 +1142,9 @@ __device__ __forceinline__ void combine_row(const VP& p, int layer, uint8_t* att
 // unit's share of the head's query rows (rows c, c + KS, ...). Every arrival
 // comes before any wait, so the waits cannot form a cycle. Returns false when
 // a wait gave up.
-template <typename T, int D, bool PRE = false, int WF = WF_NATIVE>
+template <typename T, int D, bool PRE = false, int WF = WF_NATIVE, bool MERGE = false>
 __device__ __forceinline__ bool ph_attn(const VP&, int step, int layer, int wg, int nwg,
-                                        const APre<T, D>& pre = APre<T, D>{}, bool xl = false, bool merge = false) {
+                                        const APre<T, D>& pre = APre<T, D>{}, bool xl = false) {
   const VP& p = vp_fresh();
   const int tid = tid_opaque();
   constexpr int E = MT<T>::E, KB = MT<T>::KB;
@@ -1174,7 +1174,7 @@ __device__ __forceinline__ bool ph_attn(const VP&, int step, int layer, int wg, 
     const int kvh = jh / group;
     int s0, s1;
     attn_split(p, c, s0, s1);
-    if (merge) {
+    if constexpr (MERGE) {
       // no barrier after qkv: wait for this head's query tiles (every
       // 64-row tile), and for a split of the chunk's own keys also for its
       // key / value head's tiles
@@ -1311,14 +1311,14 @@ __device__ __forceinline__ bool ph_attn(const VP&, int step, int layer, int wg, 
       }
     }
     }   // active
-    if (merge) {
+    if constexpr (MERGE) {
       __builtin_amdgcn_s_waitcnt(0);   // this wave's split output is stored
       __syncthreads();
       if (tid == 0)
         __hip_atomic_fetch_add(&p.hcnt[bh * HCNT_STRIDE], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (merge) {
+  if constexpr (MERGE) {
     // the counters count every arrival of the launch: this layer's target is
     // KS times the number of (step, layer) instances so far
     const unsigned target = (unsigned)((step * p.L + layer + 1) * KS);
@@ -2046,7 +2046,7 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   // XCD-local split sums (ph_gemm): only while every workgroup runs on XCD
   // blockIdx % 8; one that does not raises a word that every workgroup reads
   // after the first barrier, and the launch takes the device-scope path
-  if (p.xl && threadIdx.x == 0) {
+  if ((FUSE ? p.xl : (p.xl & 2)) && threadIdx.x == 0) {
     unsigned xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     if ((xcc & 15u) != (blockIdx.x & 7u))
@@ -2056,10 +2056,11 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
   if (p.pi0) VFM_BAR_PF(G_TMLP, 0);
   else if (p.L > 0) VFM_BAR_PF(G_QKV, 0);
   else VFM_BAR();
-  const bool xok = p.xl && ld_agent(&p.bar[BAR_XL_BAD]) == 0u;
-  const bool xl = FUSE && xok && (p.xl & 1);   // o / down split sums (folded norms only)
-  const bool xla = xok && (p.xl & 2);          // attention splits and their merge
-  const bool mg = FUSE || p.merge;             // merged attention, counters instead of two barriers
+  // o / down split sums (folded norms only), attention splits and their merge
+  const bool xl = FUSE && p.xl && ld_agent(&p.bar[BAR_XL_BAD]) == 0u;
+  const bool xla = FUSE ? xl && (p.xl & 2) : (p.xl & 2) && ld_agent(&p.bar[BAR_XL_BAD]) == 0u;
+  // merged attention, counters instead of two barriers (always with folded norms)
+  const bool mg = FUSE || (p.xl & XL_MERGE);
   for (int k = 0; k < p.N; ++k) {
     if (p.pi0) {
       // the action tokens' time-MLP output, then layer 0's norm
@@ -2077,16 +2078,16 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
       {
         APre<T, D> apre;
         if (mg) {
-          // dependency-scoped: attention units wait for their heads' qkv tiles
+          // dependency-scoped: attention units wait for their heads' qkv
+          // tiles, and merge the key splits in place
           AttnPrefetchHook<T, D>{p, l, wg, apre, xla}();
+          if (!ph_attn<T, D, true, WF, true>(p, k, l, wg, nwg, apre, xla)) return;
         } else {
           if (!grid_barrier(p.bar, epoch, p.trace, p.spin_limit, p.fail_epoch, p.herr, AttnPrefetchHook<T, D>{p, l, wg, apre, xla})) return;
+          ph_attn<T, D, true, WF, false>(p, k, l, wg, nwg, apre, xla);
+          VFM_BAR();
+          ph_combine<T, WF>(p, k, l, wg, nwg, xla);
         }
-        if (!ph_attn<T, D, true, WF>(p, k, l, wg, nwg, apre, xla, mg)) return;
-      }
-      if (!mg) {
-        VFM_BAR();
-        ph_combine<T, WF>(p, k, l, wg, nwg, xla);
       }
       VFM_BAR_PF(G_O, l);
       ph_gemm<T, G_O, true, WF, false, FUSE>(p, k, l, wg, nwg, pre, xl);
@@ -2125,8 +2126,8 @@ __global__ __launch_bounds__(NTH) void k_persistent(VP p) {
         for (int c = 0; c < no; ++c) __hip_atomic_store(&p.fcnt[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int c = 0; c < nd; ++c) __hip_atomic_store(&p.fcnt[FCNT_MAX + c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (p.xl) __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (FUSE || p.merge) {
+      if (FUSE || (p.xl & 2)) __hip_atomic_store(&p.bar[BAR_XL_BAD], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (FUSE || (p.xl & XL_MERGE)) {
         for (int c = 0; c < p.B * p.Hq; ++c)
           __hip_atomic_store(&p.hcnt[c * HCNT_STRIDE], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (int c = 0; c < 2 * QCNT_KV; ++c)

@@ -669,14 +669,15 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   }
   // the persistent kernel's in-place attention merge with counter-scoped
   // attention start (every persistent kernel whose shapes its counters take)
-  p.merge = mode == 0 && x->attn_merge && (long)B * p.Hq <= vfm::HCNT_MAX && p.Hq <= vfm::QCNT_KV &&
-            p.Hkv <= vfm::QCNT_KV && p.d % (16 * p.gp_nt[0]) == 0 ? 1 : 0;
+  const bool merge = mode == 0 && x->attn_merge && (long)B * p.Hq <= vfm::HCNT_MAX && p.Hq <= vfm::QCNT_KV &&
+                     p.Hkv <= vfm::QCNT_KV && p.d % (16 * p.gp_nt[0]) == 0;
   p.hcnt = x->hcnt;
   p.qcnt = x->hcnt + (size_t)vfm::HCNT_MAX * vfm::HCNT_STRIDE;
-  // attention splits of a head on one XCD, in any persistent launch
-  p.xl = mode == 0 && x->xcd_local && x->xcd_attn && x->coop_grid % 8 == 0 ? 2 : 0;
+  // separate-norm kernel: a head's attention splits on one XCD (bit 1) and
+  // the in-place merge (XL_MERGE)
+  p.xl = (mode == 0 && x->xcd_local && x->xcd_attn && x->coop_grid % 8 == 0 ? 2 : 0) | (merge ? vfm::XL_MERGE : 0);
   p.fuse = 0;
-  if (mode == 0 && x->can_fuse && x->fuse_norms && p.merge) {
+  if (mode == 0 && x->can_fuse && x->fuse_norms && merge) {
     const long mt = (p.M + 63) / 64;
     const long go = (long)p.W / (16 * p.gp_nt[1]) * mt, gd = (long)p.W / (16 * p.gp_nt[3]) * mt;
     if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX) {
@@ -686,10 +687,12 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
       // column-group count and the grid multiples of 8) and a power-of-two
       // split count (the never-cleared counters stay multiples of S, also
       // across a 32-bit wrap)
+      // (the folded-norm kernel: any non-zero p.xl selects the XCD-local sums, bit 1
+      // the attention placement too; it always merges in place)
       const long ngo = (long)p.W / (16 * p.gp_nt[1]), ngd = (long)p.W / (16 * p.gp_nt[3]);
       auto pow2 = [](int v) { return v > 0 && (v & (v - 1)) == 0; };
-      if (x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) && pow2(p.gp_s[3]))
-        p.xl |= 1;
+      p.xl = x->xcd_local && x->coop_grid % 8 == 0 && ngo % 8 == 0 && ngd % 8 == 0 && pow2(p.gp_s[1]) &&
+             pow2(p.gp_s[3]) ? (x->xcd_attn ? 3 : 1) : 0;
       p.xcnt = x->xcnt;
     }
   }
@@ -969,13 +972,6 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     if (e == hipSuccess && fp8_act(x)) e = vfm::prepare_kernels(vfm::KS_CAL, d, (int)x->lds);
     if (e != hipSuccess) { fail(VFM_E_HIP, "kernel attribute: %s", hipGetErrorString(e)); return bail(VFM_E_HIP); }
   }
-  // the persistent kernel's attention arrival counters (every expert)
-  x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
-  if (!x->hcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
-  if (vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess) {
-    fail(VFM_E_HIP, "counter clear");
-    return bail(VFM_E_HIP);
-  }
   // norms folded into the persistent kernel's GEMMs: shift W tables (fp64
   // sums over the packed bf16 weights), sums-of-squares rows, split counters
   if (can_fold_norms(cfg)) {
@@ -984,7 +980,8 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
     x->shw_g = (float*)x->dalloc((size_t)x->N * L * 2 * F * 4);
     x->fcnt = (unsigned*)x->dalloc((size_t)2 * vfm::FCNT_MAX * 4);
     x->xcnt = (unsigned*)x->dalloc((size_t)vfm::XCNT_WORDS * 4);
-    if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt) {
+    x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
+    if (!x->shw_q || !x->shw_g || !x->fcnt || !x->xcnt || !x->hcnt) {
       fail(VFM_E_OOM, "workspace allocation failed");
       return bail(VFM_E_OOM);
     }
@@ -995,6 +992,15 @@ vfm_status vfm_expert_create(const vfm_config* cfg, const vfm_tensor* weights, i
       return bail(VFM_E_HIP);
     }
     x->can_fuse = true;
+  } else {
+    x->hcnt = (unsigned*)x->dalloc((size_t)(vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE * 4);
+    if (!x->hcnt) { fail(VFM_E_OOM, "workspace allocation failed"); return bail(VFM_E_OOM); }
+  }
+  // the persistent kernel's attention arrival counters (every expert; for a
+  // folded-norm expert allocated with its tables above)
+  if (vfm::zero_words(x->hcnt, (vfm::HCNT_MAX + 2 * vfm::QCNT_KV) * vfm::HCNT_STRIDE, s) != hipSuccess) {
+    fail(VFM_E_HIP, "counter clear");
+    return bail(VFM_E_HIP);
   }
   // the streaming batch-1 kernel: bf16 pi0.5 experts whose shapes fit it
   if (x->kset == vfm::KS_BF16 && !x->pi0) {
@@ -1417,11 +1423,12 @@ vfm_status vfm_export(vfm_expert* x, const char* name, void* dst, size_t bytes) 
     if (st != VFM_OK) return st;
     int32_t* o = static_cast<int32_t*>(dst);
     o[0] = p.fuse;
-    o[1] = p.fuse ? 1 + x->N * (4 * x->L + 1) : 1 + x->N * ((p.merge ? 6 : 8) * x->L + 2 * x->pi0);
+    const bool merged = p.fuse || (p.xl & vfm::XL_MERGE);
+    o[1] = p.fuse ? 1 + x->N * (4 * x->L + 1) : 1 + x->N * ((merged ? 6 : 8) * x->L + 2 * x->pi0);
     o[2] = p.S_o;
     o[3] = p.S_down;
     o[4] = p.fuse ? (p.xl & 1) : 0;
-    o[5] = p.merge;
+    o[5] = merged ? 1 : 0;
     return VFM_OK;
   }
   if (n == "trace") {
