@@ -443,6 +443,9 @@ vfm_status vfm_prefix_run_noalloc(vfm_prefix* pre, const void* embeds, int32_t b
  *       units, every split has at least 1024 K and the tiles cover the
  *       padded token rows, or on the 128 x 128 tiles. Results agree to
  *       rounding (a different summation order).
+ *   "o_tiles": "auto" (default) or "full": the o projection on 128-token x
+ *       64-column tiles with half the K splits where 128 x 128 tiles would
+ *       split K, or on 128 x 128 tiles. Results agree to rounding.
  *   "qkv_tiles": "auto" (default) or "full": the fused QKV projection on
  *       128-token x 64-column tiles where 128 x 128 tiles would number at
  *       most 128 (half the compute units), or always on 128 x 128 tiles.

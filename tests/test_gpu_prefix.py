@@ -190,6 +190,33 @@ def test_qkv_tiles_bitwise_equal():
     assert np.array_equal(got["full"][0], got["auto"][0]) and np.array_equal(got["full"][1], got["auto"][1])
 
 
+def test_o_tiles_agree():
+    """The o projection on 128 x 64 tiles with 2 K splits (the default at the
+    Gemma-2B shape) and on 128 x 128 tiles with 4: both against the oracle
+    per layer, and against each other to 1e-3 (the partial sums added in
+    another grouping)."""
+    from vla_flow_matching_pi0_amd import vfm
+    cfg = PREFIX_CONFIGS["prefix_gemma2b_p560"].replace(num_layers=2, seed=75)
+    params, emb = make_prefix_inputs(cfg)
+    rk, rv = PO.prefix_kv(params, emb, cfg)
+    got = {}
+    for tiles in ("full", "auto"):
+        print(f"case prefix o tiles {tiles}", flush=True)
+        dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
+        pre = vfm.PrefixProducer(cfg, dev)
+        del dev
+        pre.set_option("o_tiles", tiles)
+        pre, k, v = run_producer(cfg, params, emb, producer=pre)
+        pre.close()
+        check_layers(k, v, rk, rv)
+        got[tiles] = (k, v)
+    for l in range(cfg.num_layers):
+        ek = rel_l2(got["auto"][0][l], got["full"][0][l])
+        ev = rel_l2(got["auto"][1][l], got["full"][1][l])
+        print(f"layer {l}: half vs full o tiles k {ek:.3e} v {ev:.3e}")
+        assert ek <= 1e-3 and ev <= 1e-3, l
+
+
 def test_prefix_option_is_validated():
     from vla_flow_matching_pi0_amd import vfm
     cfg = PREFIX_CONFIGS["prefix_tiny"]
@@ -197,7 +224,7 @@ def test_prefix_option_is_validated():
     dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in params.items()}
     pre = vfm.PrefixProducer(cfg, dev)
     try:
-        for key, val in (("gate_up_tiles", "huge"), ("down_tiles", "1"), ("qkv_tiles", "half"), ("no_such_option", "1")):
+        for key, val in (("gate_up_tiles", "huge"), ("down_tiles", "1"), ("qkv_tiles", "half"), ("o_tiles", "x"), ("no_such_option", "1")):
             with pytest.raises(vfm.VfmError) as e:
                 pre.set_option(key, val)
             assert e.value.name == "VFM_E_INVALID_ARG"

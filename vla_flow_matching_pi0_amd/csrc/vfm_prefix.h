@@ -33,6 +33,7 @@ struct GemmArgs {
   int N, K, M, Mpad, S;     // S: K splits (EPI_PART only)
   int bm;                   // EPI_PART: tokens per 256-column tile (part_plan), 0: 128 x 128 tiles
   int qkv_half;             // EPI_QKV: 128 x 64 tiles where 128 x 128 tiles would fill at most half the units
+  int part_half;            // EPI_PART with bm = 0: 128 x 64 tiles (the caller halves S)
   // EPI_PART: part[s][Mpad][N] fp32
   float* part;
   // EPI_GU: act packed [Mpad/16][N/2/32][64][16 B] (gate/up interleaved columns)

@@ -507,6 +507,9 @@ hipError_t prepare() {
   if ((e = hipFuncSetAttribute((const void*)k_gemm<EPI_QKV, 64>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE)) !=
       hipSuccess)
     return e;
+  if ((e = hipFuncSetAttribute((const void*)k_gemm<EPI_PART, 64>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE)) !=
+      hipSuccess)
+    return e;
   return hipFuncSetAttribute((const void*)k_gemm<EPI_QKV>, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
 }
 
@@ -554,6 +557,11 @@ hipError_t gemm(int epi, const GemmArgs& g, hipStream_t st, bool wide_gu) {
     // fewer 128 x 128 tiles than half the compute units: 128 x 64 tiles
     const int grid64 = (2 * total + 7) / 8 * 8;
     hipLaunchKernelGGL((k_gemm<EPI_QKV, 64>), dim3(grid64), dim3(256), 2 * STAGE, st, g);
+    return hipGetLastError();
+  }
+  if (epi == EPI_PART && g.part_half && g.N % 64 == 0) {
+    const int grid64 = (2 * total + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_gemm<EPI_PART, 64>), dim3(grid64), dim3(256), 2 * STAGE, st, g);
     return hipGetLastError();
   }
   switch (epi) {

@@ -43,6 +43,7 @@ struct vfm_prefix {
   bool wide_gu = true;       // option "gate_up_tiles"
   bool wide_down = true;     // option "down_tiles"
   bool half_qkv = true;      // option "qkv_tiles"
+  bool half_o = true;        // option "o_tiles"
 
   void* dalloc(size_t bytes) {
     void* p = nullptr;
@@ -316,7 +317,11 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
   const int M = B * P, Mpad = (int)round_up(M, pfx::TM), Ppad = (int)round_up(P, pfx::AK);
   const size_t kv_layer = (size_t)B * P * Hkv * d;
   const int MT = Mpad / pfx::TM;
-  const int S_o = plan_split(MT * (W / pfx::TN), Hq * d);
+  // o: 128 x 64 tiles with half the K splits where 128 x 128 tiles would
+  // split K (the same units, half the partial sums for the next norm)
+  int S_o = plan_split(MT * (W / pfx::TN), Hq * d);
+  const bool o_half = x->half_o && S_o > 1 && W % 64 == 0;
+  if (o_half) S_o /= 2;
   const pfx::PartPlan pd = pfx::part_plan(M, Mpad, W, F, plan_split(MT * (W / pfx::TN), F), x->wide_down);
   const int S_d = pd.S;
 
@@ -345,13 +350,13 @@ vfm_status run_pass(vfm_prefix* x, const PrefixWork& ws, const void* embeds, int
     if (last) break;
     aa.k = kl;
     PCHK(pfx::attention(d, aa, B, s));
-    ga.A = x->w_o[l]; ga.B = ws.attn; ga.N = W; ga.K = Hq * d; ga.S = S_o; ga.bm = 0;
+    ga.A = x->w_o[l]; ga.B = ws.attn; ga.N = W; ga.K = Hq * d; ga.S = S_o; ga.bm = 0; ga.part_half = o_half ? 1 : 0;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
     na.gain = x->g_mlp[l]; na.S = S_o;
     PCHK(pfx::norm(false, na, s));
     ga.A = x->w_gu[l]; ga.B = ws.xn; ga.N = 2 * F; ga.K = W; ga.S = 1;
     PCHK(pfx::gemm(pfx::EPI_GU, ga, s, x->wide_gu));
-    ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d; ga.bm = pd.bm;
+    ga.A = x->w_down[l]; ga.B = ws.act; ga.N = W; ga.K = F; ga.S = S_d; ga.bm = pd.bm; ga.part_half = 0;
     PCHK(pfx::gemm(pfx::EPI_PART, ga, s));
   }
   return VFM_OK;
@@ -418,6 +423,12 @@ vfm_status vfm_prefix_set_option(vfm_prefix* x, const char* key, const char* val
     if (v == "wide") x->wide_gu = true;
     else if (v == "narrow") x->wide_gu = false;
     else return report(VFM_E_INVALID_ARG, "gate_up_tiles must be 'wide' or 'narrow'");
+    return VFM_OK;
+  }
+  if (k == "o_tiles") {
+    if (v == "auto") x->half_o = true;
+    else if (v == "full") x->half_o = false;
+    else return report(VFM_E_INVALID_ARG, "o_tiles must be 'auto' or 'full'");
     return VFM_OK;
   }
   if (k == "qkv_tiles") {
