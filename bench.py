@@ -261,7 +261,7 @@ def phase_breakdown(t, nb, N, L, fused, pi0, merged=True):
         for l in range(1, L - 1):
             base = 1 + k * per_step + l * len(names) - (0 if fused else 1)
             for j, n in enumerate(names):
-                i = base + j + (0 if fused else 0)
+                i = base + j
                 if i + 1 > nb:
                     continue
                 out[n][0] += t[i + 1, 0] - t[i, 1]

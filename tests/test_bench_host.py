@@ -67,3 +67,52 @@ def test_auto_mode_resolution_matches_the_library_rule():
     assert bench.resolved_mode(CONFIGS["pi05_bf16_b32"], "auto") == "graph"
     assert bench.resolved_mode(CONFIGS["pi05_fp8_p816"], "auto") == "persistent"
     assert bench.resolved_mode(CONFIGS["pi05_bf16_b32"], "eager") == "eager"
+
+
+def _timeline(N, L, fused, merged, work, wait):
+    """(arrive, release) stamps of workgroup 0 for the persistent kernel's
+    phase sequence, each phase taking work[name] before its barrier and
+    wait[name] at it: the boundary, then per Euler step every layer's phases
+    (separate norms: layer l > 0 starts with rn_attn, layer 0's norm is in
+    the boundary) and the step boundary."""
+    import numpy as np
+    if fused:
+        layer = lambda l: ["qkv_attn", "o", "gu", "down"]
+    elif merged:
+        layer = lambda l: (["rn_attn"] if l else []) + ["qkv_attn", "o", "rn_mlp", "gu", "down"]
+    else:
+        layer = lambda l: (["rn_attn"] if l else []) + ["qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"]
+    seq = ["boundary"]
+    for _ in range(N):
+        for l in range(L):
+            seq += layer(l)
+        seq.append("boundary")
+    t = np.zeros((len(seq) + 1, 2))
+    now = 0.0
+    for i, name in enumerate(seq):
+        now += work.get(name, 1.0)
+        t[i + 1, 0] = now
+        now += wait.get(name, 0.5)
+        t[i + 1, 1] = now
+    return t, len(seq)
+
+
+@pytest.mark.parametrize("fused,merged", [(True, True), (False, True), (False, False)])
+def test_phase_breakdown_recovers_each_phase(fused, merged):
+    """bench.phase_breakdown reads a middle layer's (work, wait) per phase
+    from the barrier timeline: on a synthetic timeline with a distinct
+    duration per phase it returns those durations, for the folded-norm
+    kernel (4 barriers per layer + 1 per step), the separate-norm kernel
+    with the in-place merge (6 per layer) and with the combine phase (8)."""
+    N, L = 3, 5
+    names = (["qkv_attn", "o", "gu", "down"] if fused
+             else ["rn_attn", "qkv_attn", "o", "rn_mlp", "gu", "down"] if merged
+             else ["rn_attn", "qkv", "attn", "combine", "o", "rn_mlp", "gu", "down"])
+    work = {n: 2.0 + i for i, n in enumerate(names)}
+    wait = {n: 0.25 * (i + 1) for i, n in enumerate(names)}
+    t, nb = _timeline(N, L, fused, merged, work, wait)
+    assert nb == (1 + N * (4 * L + 1) if fused else 1 + N * ((6 if merged else 8) * L))
+    got = bench.phase_breakdown(t, nb, N, L, fused, 0, merged)
+    assert set(got) == set(names)
+    for n in names:
+        assert got[n] == [round(work[n], 2), round(wait[n], 2)], n
