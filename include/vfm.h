@@ -194,7 +194,7 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       up after a bounded spin and the next vfm_check / vfm_denoise
  *       reports VFM_E_HIP. Used where a tool cannot follow cooperative
  *       launches (kernel profilers).
- *   "fused_norms": "1" (default where it applies) or "0": the persistent
+ *   "fused_norms": "auto" (default), "1" or "0": the persistent
  *       kernel of a pi0.5 expert with bf16, W4A16 or W8A16 weights (width a
  *       multiple of 256, at most 1024; the shift W table is built from the
  *       weights the GEMMs multiply by)
@@ -209,7 +209,12 @@ vfm_status vfm_denoise(vfm_expert* ex, const float* noise, const float* state, f
  *       starts each attention unit once its head's qkv tiles are stored
  *       (per-head tile counters): four device-wide barriers per layer
  *       instead of eight. Results agree with "0" to bf16 rounding of the
- *       GEMM inputs. VFM_E_UNSUPPORTED for "1" on other experts.
+ *       GEMM inputs. "auto" folds for calls of at most 128 rows (batch
+ *       times rows per sample: pi0.5 batch 1 and 2), where the barriers
+ *       dominate; larger calls are faster with separate norm phases (the
+ *       split-sum exchanges and per-row scaling outweigh the barriers
+ *       saved), which "1" overrides. VFM_E_UNSUPPORTED for "1" on other
+ *       experts ("auto" then keeps separate norm phases).
  *   "attn_merge": "1" (default) or "0": every persistent kernel merges
  *       the attention key splits inside the attention phase (per-head
  *       arrival counters, one 128-byte line each) and starts each attention

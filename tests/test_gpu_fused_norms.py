@@ -107,6 +107,7 @@ def test_batch_change_between_fused_calls():
     cfg = CONFIGS["pi05_bf16_b1"].replace(num_layers=2, batch=4, prefix_len=40)
     params, pk, pv, noise, state = make_inputs(cfg)
     ex = gu.build_expert(cfg, params, "persistent", max_batch=4)
+    ex.set_option("fused_norms", "1")   # batch 4 (200 rows) folds only when asked to
     splits = []
     for b in (1, 4, 1):
         c = cfg.replace(batch=b)
@@ -156,6 +157,26 @@ def test_fused_plain_launch_and_trace():
     assert np.all(stamps >= 0) and np.all(np.diff(stamps) >= 0)
 
 
+def test_fused_norms_auto_folds_small_calls_only():
+    """The default ("auto") folds the norms for calls of at most 128 rows
+    (pi0.5 batch 1 and 2); larger calls run separate norm phases unless
+    "1" asks for the folded kernel."""
+    gu = _gu()
+    cfg = CONFIGS["pi05_bf16_b1"].replace(num_layers=2, batch=32, prefix_len=40)
+    params, pk, pv, noise, state = make_inputs(cfg)
+    ex = gu.build_expert(cfg, params, "persistent", max_batch=32)
+    got = {}
+    for b in (1, 2, 4, 32):
+        bufs = gu.bind_inputs(ex, cfg.replace(batch=b), pk[:, :b].copy(), pv[:, :b].copy(), noise[:b].copy(), state[:b].copy())
+        got[b] = ex.persistent_plan()["fused_norms"]
+    ex.set_option("fused_norms", "1")
+    forced = ex.persistent_plan()["fused_norms"]
+    ex.close()
+    print(f"auto fold by batch {got}, batch 32 with '1': {forced}")
+    assert got == {1: True, 2: True, 4: False, 32: False}
+    assert forced
+
+
 def test_fused_norms_option_is_validated():
     from vla_flow_matching_pi0_amd import vfm
     gu = _gu()
@@ -166,6 +187,7 @@ def test_fused_norms_option_is_validated():
         ex.set_option("fused_norms", "1")
     assert e.value.name == "VFM_E_UNSUPPORTED"
     ex.set_option("fused_norms", "0")
+    ex.set_option("fused_norms", "auto")
     with pytest.raises(vfm.VfmError) as e:
         ex.set_option("fused_norms", "yes")
     assert e.value.name == "VFM_E_INVALID_ARG"

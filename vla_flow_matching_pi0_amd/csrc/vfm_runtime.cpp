@@ -109,7 +109,9 @@ struct vfm_expert {
   int gemm_tiles = 0;        // large-M GEMMs: 0 auto, 1 128-column tiles only, 2 256-column tiles where they apply
   // norms folded into the persistent kernel's GEMMs (bf16 pi0.5 experts, W a multiple of 256 up to 1024)
   bool can_fuse = false;
-  bool fuse_norms = true;    // option "fused_norms"
+  // option "fused_norms": -1 auto (fold where the call has at most
+  // FOLD_AUTO_ROWS rows), 1 at any size, 0 never
+  int fuse_norms = -1;
   float *shw_q = nullptr, *shw_g = nullptr;   // [N][L][columns] shift W per step, layer and norm
   size_t off_ssa = 0, off_ssm = 0;            // slab offsets of the per-tile sums of squares [Mpad][W/16]
   unsigned* fcnt = nullptr;                   // [2][FCNT_MAX] split arrival counters
@@ -265,6 +267,10 @@ hipError_t shift_tables(vfm_expert* x, int L, int W, int Nq, int F, int n_norms,
   if (e == hipSuccess) e = vfm::sk::shift_proj_q(x->shw_g, x->w_gu.data(), L, W, 2 * F, x->mod, n_norms, 1, W, x->N, fmt, s);
   return e;
 }
+
+// fused_norms "auto": fold the norms into the GEMMs where the call has at
+// most this many rows (two 64-row tiles: batch 1 and 2 of pi0.5)
+constexpr long FOLD_AUTO_ROWS = 128;
 
 bool can_fold_norms(const vfm_config* c) {
   const int w = c->weight_precision;
@@ -677,7 +683,12 @@ vfm_status fill_vp(vfm_expert* x, VP& p, int B, int P, const float* noise, const
   // the in-place merge (XL_MERGE)
   p.xl = (mode == 0 && x->xcd_local && x->xcd_attn && x->coop_grid % 8 == 0 ? 2 : 0) | (merge ? vfm::XL_MERGE : 0);
   p.fuse = 0;
-  if (mode == 0 && x->can_fuse && x->fuse_norms && merge) {
+  // auto: the folded kernel saves four barriers per layer, which is what a
+  // call of one or two samples waits on; from four samples (200 rows) on
+  // the split-sum exchanges and the per-row scaling cost more than that
+  // (0.4 % slower at 4 samples, 5 % at 32)
+  const bool fold = x->fuse_norms > 0 || (x->fuse_norms < 0 && p.M <= FOLD_AUTO_ROWS);
+  if (mode == 0 && x->can_fuse && fold && merge) {
     const long mt = (p.M + 63) / 64;
     const long go = (long)p.W / (16 * p.gp_nt[1]) * mt, gd = (long)p.W / (16 * p.gp_nt[3]) * mt;
     if (go <= vfm::FCNT_MAX && gd <= vfm::FCNT_MAX) {
@@ -1119,16 +1130,19 @@ vfm_status vfm_set_option(vfm_expert* x, const char* key, const char* value) {
     return VFM_OK;
   }
   if (k == "fused_norms") {
-    // the persistent kernel with the norms folded into its GEMMs (1, the
-    // default where it applies) or with separate norm phases (0)
+    // the persistent kernel with the norms folded into its GEMMs: "auto"
+    // (default) where the call has at most FOLD_AUTO_ROWS rows, "1" at any
+    // size, "0" never (separate norm phases)
     if (v == "1") {
       if (!x->can_fuse)
         return fail(VFM_E_UNSUPPORTED, "fused_norms applies to pi0.5 experts with bf16, W4A16 or W8A16 weights and a width that is a multiple of 256 up to 1024");
-      x->fuse_norms = true;
+      x->fuse_norms = 1;
     } else if (v == "0") {
-      x->fuse_norms = false;
+      x->fuse_norms = 0;
+    } else if (v == "auto") {
+      x->fuse_norms = -1;
     } else {
-      return fail(VFM_E_INVALID_ARG, "fused_norms must be 0 or 1");
+      return fail(VFM_E_INVALID_ARG, "fused_norms must be 'auto', 0 or 1");
     }
     return VFM_OK;
   }
